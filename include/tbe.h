@@ -1,0 +1,180 @@
+/*
+ * tbe.h -- C ABI of the MI355X (gfx950) table-batched-embedding (TBE) library.
+ *
+ * One handle covers a set of T embedding tables that live in one flat device
+ * buffer, and runs the two halves of the TBE hot path on them:
+ *
+ *   tbe_forward          pooled lookup over all tables in one launch: every
+ *                        bag of row ids is gathered from its table and summed
+ *                        (or averaged), optionally scaled per lookup, with fp32
+ *                        accumulation whatever the storage dtype.
+ *                        kimbodo.com/?p=28372, "What Happened";
+ *                        "FBTriton Rewrites Table Batched Embedding"
+ *                        (kongchang.com), "Responsibilities of the forward and
+ *                        backward passes".
+ *   tbe_backward_update  the fused backward: lookups are linearized to
+ *                        (table, row) ids, sorted and run-length encoded, the
+ *                        upstream gradients of each run are added up (a
+ *                        streaming path for short runs, split accumulation for
+ *                        runs of 256 lookups or more) and every touched row
+ *                        receives exactly one optimizer update.
+ *                        kimbodo.com/?p=28372, "What Happened" and "Kimbodo
+ *                        Engineering Perspective".
+ *
+ * The batch format (flat ids + CSR offsets whose last entry is the id count)
+ * follows the example call in "Optimizing Recommendation Systems with FBTriton
+ * Table Batched Embeddings" (explore.n1n.ai), "Implementation Guide:
+ * Integrating TBE".
+ *
+ * Layouts (all row-major, no padding):
+ *   weights   one flat buffer of the storage dtype; table t starts at element
+ *             woff_t = sum_{t'<t} rows[t'] * dims[t'] and holds rows[t] rows
+ *             of dims[t] elements.
+ *   state     row-wise Adagrad only: fp32 [sum_t rows[t]], one value per table
+ *             row, indexed by the linear row id roff_t + row
+ *             (roff_t = sum_{t'<t} rows[t']).  Must start at 0.
+ *   bags      table-major: bag k = t*B + b, B bags per table.
+ *   indices   [num_indices] table-local row ids (int32 or int64).
+ *   offsets   [T*B + 1], same integer type as indices; bag k holds
+ *             indices[offsets[k] .. offsets[k+1]); offsets[0] = 0 and
+ *             offsets[T*B] = num_indices.
+ *   per_sample_weights  optional fp32 [num_indices].
+ *   output    fp32 [B, sum_t dims[t]]; table t fills columns
+ *             [doff_t, doff_t + dims[t]) with doff_t = sum_{t'<t} dims[t'].
+ *   grad_output  fp32, same layout as output.
+ *
+ * Ownership: every buffer is allocated and owned by the caller.  The weights
+ * and state pointers given to tbe_create are kept (not copied) and must
+ * outlive the handle.  The library allocates only a small per-handle device
+ * metadata block (in tbe_create) and frees it in tbe_destroy.
+ *
+ * Asynchrony: tbe_forward and tbe_backward_update enqueue work on the given
+ * HIP stream (a hipStream_t passed as void*, NULL = the null stream) and
+ * return without waiting, unless TBE_FLAG_VALIDATE is set.  Host-side argument
+ * checks happen first: on any error nothing is enqueued.  Device-side input
+ * preconditions (ids in range, offsets monotone and ending at num_indices) are
+ * not checked unless TBE_FLAG_VALIDATE is set; violating them is undefined.
+ *
+ * Threading: a handle may be used by one host thread at a time.  Two
+ * backward_update calls in flight on one handle race on the weights.
+ *
+ * No C++ exception crosses this interface.  Every function returns a
+ * tbe_status; tbe_status_string gives a static description.
+ */
+#ifndef TBE_H
+#define TBE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TBE_ABI_VERSION 1
+
+typedef struct tbe_handle tbe_handle;
+
+typedef enum {
+  TBE_OK = 0,
+  TBE_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size or enum, misaligned buffer */
+  TBE_ERR_UNSUPPORTED = 2,        /* valid request this build does not handle */
+  TBE_ERR_INDEX_OUT_OF_RANGE = 3, /* TBE_FLAG_VALIDATE found a bad id or offsets array */
+  TBE_ERR_WORKSPACE_TOO_SMALL = 4,
+  TBE_ERR_HIP = 5,                /* a HIP runtime call or kernel launch failed */
+  TBE_ERR_OUT_OF_MEMORY = 6       /* metadata allocation failed */
+} tbe_status;
+
+typedef enum { TBE_F32 = 0, TBE_F16 = 1, TBE_BF16 = 2 } tbe_dtype;       /* table storage */
+typedef enum { TBE_I32 = 0, TBE_I64 = 1 } tbe_index_dtype;                /* indices and offsets */
+typedef enum { TBE_POOL_SUM = 0, TBE_POOL_MEAN = 1 } tbe_pooling;
+typedef enum { TBE_OPT_SGD = 0, TBE_OPT_ROWWISE_ADAGRAD = 1 } tbe_optimizer;
+
+enum {
+  /* Check ids and offsets on the device before touching any output or
+   * weight; the call then waits for the stream and returns
+   * TBE_ERR_INDEX_OUT_OF_RANGE on a bad batch. */
+  TBE_FLAG_VALIDATE = 1u,
+  /* Never use the count-matrix (MFMA) forward for small tables. */
+  TBE_FLAG_NO_HISTOGRAM = 2u,
+  /* Use the count-matrix forward for every table; tbe_create fails with
+   * TBE_ERR_UNSUPPORTED if a table is not eligible. */
+  TBE_FLAG_FORCE_HISTOGRAM = 4u
+};
+
+typedef struct {
+  int32_t num_tables;      /* T >= 1 */
+  const int64_t* rows;     /* host [T], rows[t] >= 1, sum < 2^31 */
+  const int32_t* dims;     /* host [T], 1 <= dims[t] <= 1024 */
+  int32_t weight_dtype;    /* tbe_dtype */
+  int32_t pooling;         /* tbe_pooling */
+  int32_t optimizer;       /* tbe_optimizer */
+  uint32_t flags;          /* TBE_FLAG_* */
+} tbe_config;
+
+/* Optional output of tbe_backward_update: the grouping it computed.  Device
+ * buffers with room for num_indices entries; num_unique is one int32. */
+typedef struct {
+  int32_t* unique_ids;     /* ascending linear row ids roff_t + row */
+  int32_t* run_lengths;    /* lookups per unique id */
+  int32_t* num_unique;     /* U */
+} tbe_runs;
+
+/* Tuning / test knobs for tbe_set_option. */
+typedef enum {
+  /* Runs with at least this many lookups take the split-accumulation path
+   * (default 256).  Changes only the fp32 summation order. */
+  TBE_OPTION_LONG_RUN_THRESHOLD = 1,
+  /* 1: record HIP events between the stages of every call, readable with
+   * tbe_stage_times; 0 (default): off. */
+  TBE_OPTION_PROFILE = 2
+} tbe_option;
+
+/* Create a handle.  Validates the configuration (host only; nothing is
+ * allocated when it fails), computes the table layout and copies a small
+ * metadata block to the current device.  weights: device, flat, storage
+ * dtype, 16-byte aligned.  optim_state: device fp32 [sum rows], required for
+ * row-wise Adagrad, ignored (may be NULL) for SGD. */
+tbe_status tbe_create(const tbe_config* config, void* weights, float* optim_state,
+                      tbe_handle** out);
+
+/* Release the handle's metadata.  Waits for nothing; the caller must not
+ * destroy a handle whose work is still running.  NULL is a no-op. */
+void tbe_destroy(tbe_handle* handle);
+
+/* Pooled forward.  B >= 0 bags per table; num_indices >= 0.  B == 0 is a
+ * no-op; bags without ids produce zeros (also under mean pooling). */
+tbe_status tbe_forward(tbe_handle* handle, int32_t B, const void* indices, const void* offsets,
+                       int32_t index_dtype, int64_t num_indices,
+                       const float* per_sample_weights, float* output, void* stream);
+
+/* Bytes of device workspace tbe_backward_update needs for this batch shape. */
+tbe_status tbe_backward_workspace_size(const tbe_handle* handle, int32_t B, int64_t num_indices,
+                                       size_t* bytes);
+
+/* Fused backward + optimizer update of the handle's weights (and state).
+ * lr: learning rate; eps: Adagrad epsilon (ignored for SGD).  workspace:
+ * device, 256-byte aligned, at least tbe_backward_workspace_size bytes; its
+ * contents on entry do not matter.  runs: optional (NULL for none). */
+tbe_status tbe_backward_update(tbe_handle* handle, int32_t B, const void* indices,
+                               const void* offsets, int32_t index_dtype, int64_t num_indices,
+                               const float* per_sample_weights, const float* grad_output,
+                               float lr, float eps, void* workspace, size_t workspace_bytes,
+                               const tbe_runs* runs, void* stream);
+
+/* Set a tbe_option (see above). */
+tbe_status tbe_set_option(tbe_handle* handle, int32_t option, int64_t value);
+
+/* With TBE_OPTION_PROFILE on: waits for the last call's events and writes the
+ * duration in milliseconds of each of its stages to ms[0..*count) (at most
+ * capacity), and a static name for each to names (may be NULL). */
+tbe_status tbe_stage_times(tbe_handle* handle, float* ms, const char** names, int32_t capacity,
+                           int32_t* count);
+
+const char* tbe_status_string(tbe_status status);
+int32_t tbe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TBE_H */

@@ -1,0 +1,539 @@
+// api.hip -- host side of the C ABI declared in include/tbe.h: configuration
+// checks, table layout, per-call launch planning, workspace carving,
+// optional validation and profiling.  No exception leaves this file.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "common.hpp"
+#include "tbe.h"
+
+using namespace tbe;
+
+struct tbe_handle {
+  int32_t T = 0;
+  std::vector<int64_t> rows;
+  std::vector<int32_t> dims;
+  int32_t dtype = 0, pooling = 0, optimizer = 0;
+  uint32_t flags = 0;
+  void* weights = nullptr;
+  float* state = nullptr;
+  int64_t sum_rows = 0;
+  int32_t sum_dims = 0;
+  int32_t dmax = 0;
+  int32_t key_bits = 1;
+  bool fwd_vec = false;  // every row is a whole number of 16-byte chunks
+  bool bwd_vec = false;  // every dim is a multiple of 4 (16-byte gradient chunks)
+  int device = 0;
+  std::vector<TableMeta> meta_host;
+  TableMeta* meta = nullptr;     // device copy
+  uint32_t* flag = nullptr;      // device word for the validation kernel
+  int64_t long_threshold = 256;
+  // profiling
+  bool profile = false;
+  std::vector<hipEvent_t> events;
+  std::vector<const char*> stage_names;
+  int nrecorded = 0;
+};
+
+namespace {
+
+constexpr int kChunk = 256;       // lookups per level-1 partial of a long run
+constexpr int kSuperChunk = 32;   // level-1 partials per level-2 partial
+constexpr size_t kAlign = 256;
+
+int ceil_log2(int64_t x) {
+  int b = 0;
+  while ((int64_t{1} << b) < x) ++b;
+  return b;
+}
+
+int64_t next_pow2(int64_t x) { return int64_t{1} << ceil_log2(x < 1 ? 1 : x); }
+
+int storage_bytes(int dtype) { return dtype == TBE_F32 ? 4 : 2; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+tbe_status from_hip(hipError_t e) { return e == hipSuccess ? TBE_OK : TBE_ERR_HIP; }
+
+// --- profiling -------------------------------------------------------------
+
+void prof_begin(tbe_handle* h, hipStream_t s) {
+  if (!h->profile) return;
+  h->nrecorded = 0;
+  h->stage_names.clear();
+  if (h->events.empty()) {
+    h->events.resize(64);
+    for (auto& e : h->events) (void)hipEventCreate(&e);
+  }
+  (void)hipEventRecord(h->events[h->nrecorded++], s);
+}
+
+struct HookCtx {
+  tbe_handle* h;
+  hipStream_t s;
+};
+
+void prof_mark(void* ctx, const char* name) {
+  auto* c = static_cast<HookCtx*>(ctx);
+  tbe_handle* h = c->h;
+  if (!h->profile || h->nrecorded >= static_cast<int>(h->events.size())) return;
+  (void)hipEventRecord(h->events[h->nrecorded++], c->s);
+  h->stage_names.push_back(name);
+}
+
+// --- validation kernel -----------------------------------------------------
+
+template <typename IT>
+__global__ __launch_bounds__(kBlock) void validate_batch(const IT* idx, const IT* off,
+                                                         const TableMeta* meta, int32_t B,
+                                                         int64_t nbags, int64_t n,
+                                                         uint32_t* flag) {
+  const int64_t k = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  if (k > nbags) return;
+  bool bad = false;
+  if (k == 0 && off[0] != 0) bad = true;
+  if (k == nbags) {
+    if (static_cast<int64_t>(off[nbags]) != n) bad = true;
+  } else {
+    const int64_t lo = off[k], hi = off[k + 1];
+    if (hi < lo || lo < 0 || hi > n) {
+      bad = true;
+    } else {
+      const int64_t E = meta[k / B].rows;
+      for (int64_t i = lo; i < hi; ++i) {
+        const int64_t x = idx[i];
+        if (x < 0 || x >= E) {
+          bad = true;
+          break;
+        }
+      }
+    }
+  }
+  if (bad) atomicOr(flag, 1u);
+}
+
+__global__ void fill_u32(uint32_t* p, uint32_t v, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+tbe_status run_validation(tbe_handle* h, int32_t B, const void* indices, const void* offsets,
+                          int32_t index_dtype, int64_t n, hipStream_t s) {
+  const int64_t nbags = static_cast<int64_t>(h->T) * B;
+  hipLaunchKernelGGL(fill_u32, dim3(1), dim3(64), 0, s, h->flag, 0u, int64_t{1});
+  const unsigned blocks = static_cast<unsigned>((nbags + 1 + kBlock - 1) / kBlock);
+  if (index_dtype == TBE_I64)
+    hipLaunchKernelGGL(validate_batch<int64_t>, dim3(blocks), dim3(kBlock), 0, s,
+                       static_cast<const int64_t*>(indices), static_cast<const int64_t*>(offsets),
+                       h->meta, B, nbags, n, h->flag);
+  else
+    hipLaunchKernelGGL(validate_batch<int32_t>, dim3(blocks), dim3(kBlock), 0, s,
+                       static_cast<const int32_t*>(indices), static_cast<const int32_t*>(offsets),
+                       h->meta, B, nbags, n, h->flag);
+  if (hipGetLastError() != hipSuccess) return TBE_ERR_HIP;
+  uint32_t host_flag = 0;
+  if (hipMemcpyAsync(&host_flag, h->flag, sizeof(host_flag), hipMemcpyDeviceToHost, s) !=
+      hipSuccess)
+    return TBE_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return TBE_ERR_HIP;
+  return host_flag ? TBE_ERR_INDEX_OUT_OF_RANGE : TBE_OK;
+}
+
+tbe_status check_batch_args(const tbe_handle* h, int32_t B, const void* indices,
+                            const void* offsets, int32_t index_dtype, int64_t n) {
+  if (!h || B < 0 || n < 0) return TBE_ERR_INVALID_ARGUMENT;
+  if (index_dtype != TBE_I32 && index_dtype != TBE_I64) return TBE_ERR_INVALID_ARGUMENT;
+  if (B > 0 && !offsets) return TBE_ERR_INVALID_ARGUMENT;
+  if (n > 0 && !indices) return TBE_ERR_INVALID_ARGUMENT;
+  if (n > 0x7FFFFFFF - 1) return TBE_ERR_UNSUPPORTED;  // lookup ids are 32-bit on the device
+  if (static_cast<int64_t>(h->T) * B >= 0x7FFFFFFF) return TBE_ERR_UNSUPPORTED;
+  return TBE_OK;
+}
+
+// --- backward workspace layout ---------------------------------------------
+
+struct Carve {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off += (bytes + kAlign - 1) / kAlign * kAlign;
+    return o;
+  }
+};
+
+struct BwdPlan {
+  int64_t n = 0;
+  int sort_tiles = 0, rle_tiles = 0;
+  int64_t long_ub = 0, items1_ub = 0, items2_ub = 0;
+  int32_t pstride = 0;
+  int32_t nch = 1, gshift = 0;
+  bool vec = false;
+  size_t o_keys[2], o_vals[2], o_rec, o_hist, o_tot, o_rle, o_uniq, o_start, o_cnt, o_longs,
+      o_items1, o_items2, o_p1, o_p2;
+  size_t bytes = 0;
+};
+
+bool plan_backward(const tbe_handle* h, int64_t n, bool vec, BwdPlan* p) {
+  p->n = n;
+  p->vec = vec;
+  const int ve = vec ? 4 : 1;
+  const int64_t c = (h->dmax + ve - 1) / ve;  // chunks per gradient row
+  if (c <= kWave) {
+    p->nch = 1;
+    p->gshift = ceil_log2(next_pow2(c));
+  } else {
+    p->gshift = 6;
+    const int64_t sets = (c + kWave - 1) / kWave;
+    if (vec) {
+      if (sets > 4) return false;
+      p->nch = 4;
+    } else {
+      if (sets > 16) return false;
+      p->nch = 16;
+    }
+  }
+  p->pstride = static_cast<int32_t>((h->dmax + 3) / 4 * 4);
+  p->sort_tiles = static_cast<int>((n + kSortTile - 1) / kSortTile);
+  p->rle_tiles = static_cast<int>((n + kRleTile - 1) / kRleTile);
+  const int64_t thr = std::max<int64_t>(1, h->long_threshold);
+  p->long_ub = n / thr + 1;
+  p->items1_ub = n / kChunk + p->long_ub;
+  p->items2_ub = p->items1_ub / kSuperChunk + p->long_ub;
+  Carve cv;
+  for (int i = 0; i < 2; ++i) {
+    p->o_keys[i] = cv.take(4 * static_cast<size_t>(n));
+    p->o_vals[i] = cv.take(4 * static_cast<size_t>(n));
+  }
+  p->o_rec = cv.take(8 * static_cast<size_t>(n));
+  p->o_hist = cv.take(4 * static_cast<size_t>(kRadix) * std::max(1, p->sort_tiles));
+  p->o_tot = cv.take(4 * kRadix);
+  p->o_rle = cv.take(4 * static_cast<size_t>(std::max(1, p->rle_tiles)));
+  p->o_uniq = cv.take(4 * static_cast<size_t>(n));
+  p->o_start = cv.take(4 * static_cast<size_t>(n + 1));
+  p->o_cnt = cv.take(16);
+  p->o_longs = cv.take(16 * static_cast<size_t>(p->long_ub));
+  p->o_items1 = cv.take(8 * static_cast<size_t>(p->items1_ub));
+  p->o_items2 = cv.take(8 * static_cast<size_t>(p->items2_ub));
+  p->o_p1 = cv.take(4 * static_cast<size_t>(p->pstride) * p->items1_ub);
+  p->o_p2 = cv.take(4 * static_cast<size_t>(p->pstride) * p->items2_ub);
+  p->bytes = cv.off;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tbe_status_string(tbe_status status) {
+  switch (status) {
+    case TBE_OK: return "ok";
+    case TBE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case TBE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case TBE_ERR_INDEX_OUT_OF_RANGE: return "row id or offsets out of range";
+    case TBE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case TBE_ERR_HIP: return "HIP runtime error";
+    case TBE_ERR_OUT_OF_MEMORY: return "out of device memory";
+  }
+  return "unknown status";
+}
+
+int32_t tbe_abi_version(void) { return TBE_ABI_VERSION; }
+
+tbe_status tbe_create(const tbe_config* cfg, void* weights, float* optim_state, tbe_handle** out) {
+  if (!out) return TBE_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  if (!cfg || !weights || cfg->num_tables <= 0 || !cfg->rows || !cfg->dims)
+    return TBE_ERR_INVALID_ARGUMENT;
+  if (cfg->weight_dtype < TBE_F32 || cfg->weight_dtype > TBE_BF16) return TBE_ERR_INVALID_ARGUMENT;
+  if (cfg->pooling != TBE_POOL_SUM && cfg->pooling != TBE_POOL_MEAN)
+    return TBE_ERR_INVALID_ARGUMENT;
+  if (cfg->optimizer != TBE_OPT_SGD && cfg->optimizer != TBE_OPT_ROWWISE_ADAGRAD)
+    return TBE_ERR_INVALID_ARGUMENT;
+  if (cfg->optimizer == TBE_OPT_ROWWISE_ADAGRAD && !optim_state) return TBE_ERR_INVALID_ARGUMENT;
+  if (cfg->flags & ~7u) return TBE_ERR_INVALID_ARGUMENT;
+  if ((cfg->flags & TBE_FLAG_NO_HISTOGRAM) && (cfg->flags & TBE_FLAG_FORCE_HISTOGRAM))
+    return TBE_ERR_INVALID_ARGUMENT;
+  if (cfg->flags & TBE_FLAG_FORCE_HISTOGRAM) return TBE_ERR_UNSUPPORTED;
+  const int sb = storage_bytes(cfg->weight_dtype);
+  if (!aligned(weights, 16)) return TBE_ERR_INVALID_ARGUMENT;
+  int64_t sum_rows = 0, sum_dims = 0;
+  for (int t = 0; t < cfg->num_tables; ++t) {
+    if (cfg->rows[t] < 1 || cfg->dims[t] < 1 || cfg->dims[t] > kMaxDim)
+      return TBE_ERR_INVALID_ARGUMENT;
+    sum_rows += cfg->rows[t];
+    sum_dims += cfg->dims[t];
+    if (sum_rows > 0x7FFFFFFF || sum_dims > 0x7FFFFFFF) return TBE_ERR_UNSUPPORTED;
+  }
+
+  tbe_handle* h = nullptr;
+  try {
+    h = new tbe_handle();
+    h->T = cfg->num_tables;
+    h->rows.assign(cfg->rows, cfg->rows + h->T);
+    h->dims.assign(cfg->dims, cfg->dims + h->T);
+    h->dtype = cfg->weight_dtype;
+    h->pooling = cfg->pooling;
+    h->optimizer = cfg->optimizer;
+    h->flags = cfg->flags;
+    h->weights = weights;
+    h->state = cfg->optimizer == TBE_OPT_ROWWISE_ADAGRAD ? optim_state : nullptr;
+    h->sum_rows = sum_rows;
+    h->sum_dims = static_cast<int32_t>(sum_dims);
+    h->key_bits = std::max(1, ceil_log2(sum_rows));
+    h->fwd_vec = true;
+    h->bwd_vec = true;
+    for (int t = 0; t < h->T; ++t) {
+      h->dmax = std::max(h->dmax, h->dims[t]);
+      if ((h->dims[t] * sb) % 16 != 0) h->fwd_vec = false;
+      if (h->dims[t] % 4 != 0) h->bwd_vec = false;
+    }
+    const int fwd_ve = h->fwd_vec ? 16 / sb : 1;
+    h->meta_host.resize(h->T);
+    int64_t woff = 0, roff = 0, doff = 0;
+    for (int t = 0; t < h->T; ++t) {
+      TableMeta& m = h->meta_host[t];
+      std::memset(&m, 0, sizeof m);
+      m.woff = woff;
+      m.roff = static_cast<int32_t>(roff);
+      m.rows = static_cast<int32_t>(h->rows[t]);
+      m.dim = h->dims[t];
+      m.doff = static_cast<int32_t>(doff);
+      const int64_t chunks = (h->dims[t] + fwd_ve - 1) / fwd_ve;
+      m.fwd_gshift = ceil_log2(next_pow2(std::min<int64_t>(chunks, kWave)));
+      woff += h->rows[t] * h->dims[t];
+      roff += h->rows[t];
+      doff += h->dims[t];
+    }
+  } catch (...) {
+    delete h;
+    return TBE_ERR_OUT_OF_MEMORY;
+  }
+
+  if (hipGetDevice(&h->device) != hipSuccess) {
+    delete h;
+    return TBE_ERR_HIP;
+  }
+  const size_t meta_bytes = sizeof(TableMeta) * static_cast<size_t>(h->T);
+  const size_t flag_off = (meta_bytes + kAlign - 1) / kAlign * kAlign;
+  void* block = nullptr;
+  if (hipMalloc(&block, flag_off + kAlign) != hipSuccess) {
+    delete h;
+    return TBE_ERR_OUT_OF_MEMORY;
+  }
+  h->meta = static_cast<TableMeta*>(block);
+  h->flag = reinterpret_cast<uint32_t*>(static_cast<char*>(block) + flag_off);
+  if (hipMemcpy(h->meta, h->meta_host.data(), meta_bytes, hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(block);
+    delete h;
+    return TBE_ERR_HIP;
+  }
+  *out = h;
+  return TBE_OK;
+}
+
+void tbe_destroy(tbe_handle* h) {
+  if (!h) return;
+  for (auto& e : h->events) (void)hipEventDestroy(e);
+  if (h->meta) (void)hipFree(h->meta);
+  delete h;
+}
+
+tbe_status tbe_set_option(tbe_handle* h, int32_t option, int64_t value) {
+  if (!h) return TBE_ERR_INVALID_ARGUMENT;
+  switch (option) {
+    case TBE_OPTION_LONG_RUN_THRESHOLD:
+      if (value < 1) return TBE_ERR_INVALID_ARGUMENT;
+      h->long_threshold = value;
+      return TBE_OK;
+    case TBE_OPTION_PROFILE:
+      h->profile = value != 0;
+      return TBE_OK;
+  }
+  return TBE_ERR_INVALID_ARGUMENT;
+}
+
+tbe_status tbe_stage_times(tbe_handle* h, float* ms, const char** names, int32_t capacity,
+                           int32_t* count) {
+  if (!h || !count || (capacity > 0 && !ms)) return TBE_ERR_INVALID_ARGUMENT;
+  *count = 0;
+  if (!h->profile || h->nrecorded < 2) return TBE_OK;
+  if (hipEventSynchronize(h->events[h->nrecorded - 1]) != hipSuccess) return TBE_ERR_HIP;
+  const int n = std::min<int>(capacity, h->nrecorded - 1);
+  for (int i = 0; i < n; ++i) {
+    float t = 0.0f;
+    if (hipEventElapsedTime(&t, h->events[i], h->events[i + 1]) != hipSuccess) return TBE_ERR_HIP;
+    ms[i] = t;
+    if (names) names[i] = h->stage_names[i];
+  }
+  *count = n;
+  return TBE_OK;
+}
+
+tbe_status tbe_forward(tbe_handle* h, int32_t B, const void* indices, const void* offsets,
+                       int32_t index_dtype, int64_t n, const float* psw, float* output,
+                       void* stream) {
+  tbe_status st = check_batch_args(h, B, indices, offsets, index_dtype, n);
+  if (st != TBE_OK) return st;
+  if (B == 0) return TBE_OK;
+  if (!output || !aligned(output, 16)) return TBE_ERR_INVALID_ARGUMENT;
+  if (psw && !aligned(psw, 4)) return TBE_ERR_INVALID_ARGUMENT;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  try {
+    if (h->flags & TBE_FLAG_VALIDATE) {
+      st = run_validation(h, B, indices, offsets, index_dtype, n, s);
+      if (st != TBE_OK) return st;
+    }
+    HookCtx hc{h, s};
+    prof_begin(h, s);
+
+    // Sub-wave size: enough lane groups per bag that one round of row loads
+    // covers a mean-length bag.
+    const double mean_len = static_cast<double>(n) / (static_cast<double>(h->T) * B);
+    int lshift = 0;
+    while (lshift < 6 && (int64_t{kFwdUnroll} << lshift) < mean_len) ++lshift;
+    int64_t tiles = 1;
+    for (int t = 0; t < h->T; ++t) {
+      const int sw = std::min(6, h->meta_host[t].fwd_gshift + lshift);
+      const int64_t bags_per_block = int64_t{kWavesPerBlock} << (6 - sw);
+      tiles = std::max<int64_t>(tiles, (B + bags_per_block - 1) / bags_per_block);
+    }
+    ForwardLaunch a{};
+    a.weights = h->weights;
+    a.indices = indices;
+    a.offsets = offsets;
+    a.psw = psw;
+    a.out = output;
+    a.meta = h->meta;
+    a.T = h->T;
+    a.B = B;
+    a.sum_dims = h->sum_dims;
+    a.tiles_per_table = static_cast<int32_t>(tiles);
+    a.lshift = lshift;
+    a.mean = h->pooling == TBE_POOL_MEAN;
+    a.dtype = h->dtype;
+    a.index64 = index_dtype == TBE_I64;
+    a.vec = h->fwd_vec;
+    if (tiles * h->T > 0x7FFFFFFF) return TBE_ERR_UNSUPPORTED;
+    const hipError_t e = launch_forward_gather(a, s);
+    prof_mark(&hc, "forward_gather");
+    return from_hip(e);
+  } catch (...) {
+    return TBE_ERR_OUT_OF_MEMORY;
+  }
+}
+
+tbe_status tbe_backward_workspace_size(const tbe_handle* h, int32_t B, int64_t n, size_t* bytes) {
+  if (!h || !bytes || B < 0 || n < 0) return TBE_ERR_INVALID_ARGUMENT;
+  BwdPlan p;
+  if (!plan_backward(h, n, h->bwd_vec, &p)) return TBE_ERR_UNSUPPORTED;
+  *bytes = p.bytes;
+  return TBE_OK;
+}
+
+tbe_status tbe_backward_update(tbe_handle* h, int32_t B, const void* indices, const void* offsets,
+                               int32_t index_dtype, int64_t n, const float* psw,
+                               const float* grad_output, float lr, float eps, void* workspace,
+                               size_t workspace_bytes, const tbe_runs* runs, void* stream) {
+  tbe_status st = check_batch_args(h, B, indices, offsets, index_dtype, n);
+  if (st != TBE_OK) return st;
+  if (B > 0 && (!grad_output || !aligned(grad_output, 4))) return TBE_ERR_INVALID_ARGUMENT;
+  if (runs && (!runs->num_unique || (n > 0 && (!runs->unique_ids || !runs->run_lengths))))
+    return TBE_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(lr) || !std::isfinite(eps)) return TBE_ERR_INVALID_ARGUMENT;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  try {
+    if (B == 0 || n == 0) {
+      if (runs) {
+        hipLaunchKernelGGL(fill_u32, dim3(1), dim3(64), 0, s,
+                           reinterpret_cast<uint32_t*>(runs->num_unique), 0u, int64_t{1});
+        return from_hip(hipGetLastError());
+      }
+      return TBE_OK;
+    }
+    const bool vec = h->bwd_vec && aligned(grad_output, 16);
+    BwdPlan p;
+    if (!plan_backward(h, n, vec, &p)) return TBE_ERR_UNSUPPORTED;
+    if (!workspace || !aligned(workspace, kAlign)) return TBE_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < p.bytes) return TBE_ERR_WORKSPACE_TOO_SMALL;
+    if (h->flags & TBE_FLAG_VALIDATE) {
+      st = run_validation(h, B, indices, offsets, index_dtype, n, s);
+      if (st != TBE_OK) return st;
+    }
+    HookCtx hc{h, s};
+    prof_begin(h, s);
+
+    char* w = static_cast<char*>(workspace);
+    BackwardLaunch a{};
+    a.indices = indices;
+    a.offsets = offsets;
+    a.psw = psw;
+    a.grad = grad_output;
+    a.weights = h->weights;
+    a.state = h->state;
+    a.meta = h->meta;
+    a.num_indices = n;
+    a.num_bags = static_cast<int64_t>(h->T) * B;
+    a.T = h->T;
+    a.B = B;
+    a.sum_dims = h->sum_dims;
+    a.key_bits = h->key_bits;
+    a.mean = h->pooling == TBE_POOL_MEAN;
+    a.index64 = index_dtype == TBE_I64;
+    a.dtype = h->dtype;
+    a.adagrad = h->optimizer == TBE_OPT_ROWWISE_ADAGRAD;
+    a.use_rec = (psw != nullptr) || a.mean;
+    a.vec = vec;
+    a.nch = p.nch;
+    a.gshift = p.gshift;
+    a.pstride = p.pstride;
+    a.long_threshold = static_cast<int32_t>(std::min<int64_t>(h->long_threshold, 0x7FFFFFFF));
+    a.chunk = kChunk;
+    a.super_chunk = kSuperChunk;
+    a.lr = lr;
+    a.eps = eps;
+    if (runs) {
+      a.out_unique = runs->unique_ids;
+      a.out_lengths = runs->run_lengths;
+      a.out_num = runs->num_unique;
+    }
+    BackwardBuffers& b = a.buf;
+    for (int i = 0; i < 2; ++i) {
+      b.keys[i] = reinterpret_cast<uint32_t*>(w + p.o_keys[i]);
+      b.vals[i] = reinterpret_cast<uint32_t*>(w + p.o_vals[i]);
+    }
+    b.rec = reinterpret_cast<uint2*>(w + p.o_rec);
+    b.hist = reinterpret_cast<uint32_t*>(w + p.o_hist);
+    b.digit_totals = reinterpret_cast<uint32_t*>(w + p.o_tot);
+    b.rle_tiles = reinterpret_cast<uint32_t*>(w + p.o_rle);
+    b.unique_keys = reinterpret_cast<uint32_t*>(w + p.o_uniq);
+    b.run_start = reinterpret_cast<uint32_t*>(w + p.o_start);
+    b.counters = reinterpret_cast<uint32_t*>(w + p.o_cnt);
+    b.longs = reinterpret_cast<uint4*>(w + p.o_longs);
+    b.items1 = reinterpret_cast<uint2*>(w + p.o_items1);
+    b.items2 = reinterpret_cast<uint2*>(w + p.o_items2);
+    b.partial1 = reinterpret_cast<float*>(w + p.o_p1);
+    b.partial2 = reinterpret_cast<float*>(w + p.o_p2);
+
+    hipError_t e = launch_linearize(a, s);
+    if (e != hipSuccess) return TBE_ERR_HIP;
+    prof_mark(&hc, "linearize");
+    int sorted = 0;
+    e = launch_radix_sort(a, s, &sorted, h->profile ? prof_mark : nullptr, &hc);
+    if (e != hipSuccess) return TBE_ERR_HIP;
+    e = launch_run_length_encode(a, b.keys[sorted], s);
+    if (e != hipSuccess) return TBE_ERR_HIP;
+    prof_mark(&hc, "run_length_encode");
+    e = launch_segment_reduce_update(a, b.vals[sorted], s, h->profile ? prof_mark : nullptr, &hc);
+    return from_hip(e);
+  } catch (...) {
+    return TBE_ERR_OUT_OF_MEMORY;
+  }
+}
+
+}  // extern "C"

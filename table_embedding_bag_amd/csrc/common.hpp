@@ -1,0 +1,267 @@
+// common.hpp -- device helpers and internal launch interfaces of the gfx950
+// TBE library.  Everything here is internal; the public interface is tbe.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tbe {
+
+constexpr int kWave = 64;        // CDNA wavefront width
+constexpr int kBlock = 256;      // threads per workgroup for every kernel here
+constexpr int kWavesPerBlock = kBlock / kWave;
+
+// Storage dtype codes (same values as tbe_dtype).
+constexpr int kF32 = 0, kF16 = 1, kBF16 = 2;
+
+// Per-table metadata, computed once at handle creation and kept on the device.
+struct TableMeta {
+  int64_t woff;      // element offset of the table's row 0 in the flat weights
+  int32_t roff;      // linear row id of the table's row 0
+  int32_t rows;      // E_t
+  int32_t dim;       // D_t
+  int32_t doff;      // first output column of the table
+  int32_t fwd_gshift;  // log2(lanes that cover one row in the forward)
+  int32_t pad;
+};
+static_assert(sizeof(TableMeta) == 32, "TableMeta layout");
+
+// ---------------------------------------------------------------------------
+// Small device helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Number of set bits of m in lanes below this one.
+__device__ __forceinline__ uint32_t popc_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const uint32_t y = __shfl_up(x, d, kWave);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// Exclusive prefix sum over a 256-thread block; *total receives the sum.
+// scratch: 4 words of shared memory.  Contains barriers: call from all threads.
+__device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t x, uint32_t* scratch,
+                                                        uint32_t* total) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_inclusive_sum(x);
+  if (lane == kWave - 1) scratch[wave] = incl;
+  __syncthreads();
+  uint32_t base = 0, sum = 0;
+#pragma unroll
+  for (int w = 0; w < kWavesPerBlock; ++w) {
+    const uint32_t s = scratch[w];
+    base += (w < wave) ? s : 0u;
+    sum += s;
+  }
+  __syncthreads();
+  *total = sum;
+  return base + incl - x;
+}
+
+// Workgroups are handed to the 8 XCDs of the chip round robin.  Renumber them
+// so that each XCD works on one contiguous range of logical work items (and so
+// keeps that range's data in its own L2).
+__device__ __forceinline__ int xcd_contiguous_block(int bid, int nblocks) {
+  const int xcd = bid & 7, pos = bid >> 3;
+  const int q = nblocks >> 3, r = nblocks & 7;
+  return xcd * q + (xcd < r ? xcd : r) + pos;
+}
+
+// bf16 / fp16 widening (exact) and narrowing (round to nearest even).
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+__device__ __forceinline__ float f16_lo(uint32_t u) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(u & 0xFFFFu)));
+}
+__device__ __forceinline__ float f16_hi(uint32_t u) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(u >> 16)));
+}
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;  // NaN stays a quiet NaN
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;                   // ties to even
+}
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));  // v_cvt_f16_f32, RNE mode
+}
+
+template <int ST>
+struct StorageTraits;
+template <>
+struct StorageTraits<kF32> { static constexpr int bytes = 4; };
+template <>
+struct StorageTraits<kF16> { static constexpr int bytes = 2; };
+template <>
+struct StorageTraits<kBF16> { static constexpr int bytes = 2; };
+
+// Load VE consecutive stored elements starting at element e of base and widen
+// them to fp32.  VE * bytes is 16, 8, 4 or 2 and the address is aligned to it.
+template <int ST, int VE>
+__device__ __forceinline__ void load_widen(const void* base, int64_t e, float* out) {
+  if constexpr (ST == kF32) {
+    const float* p = static_cast<const float*>(base) + e;
+    if constexpr (VE == 4) {
+      const float4 v = *reinterpret_cast<const float4*>(p);
+      out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < VE; ++i) out[i] = p[i];
+    }
+  } else {
+    const uint16_t* p = static_cast<const uint16_t*>(base) + e;
+    if constexpr (VE == 8) {
+      const uint4 v = *reinterpret_cast<const uint4*>(p);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        out[2 * i] = (ST == kBF16) ? bf16_lo(w[i]) : f16_lo(w[i]);
+        out[2 * i + 1] = (ST == kBF16) ? bf16_hi(w[i]) : f16_hi(w[i]);
+      }
+    } else if constexpr (VE == 4) {
+      const uint2 v = *reinterpret_cast<const uint2*>(p);
+      out[0] = (ST == kBF16) ? bf16_lo(v.x) : f16_lo(v.x);
+      out[1] = (ST == kBF16) ? bf16_hi(v.x) : f16_hi(v.x);
+      out[2] = (ST == kBF16) ? bf16_lo(v.y) : f16_lo(v.y);
+      out[3] = (ST == kBF16) ? bf16_hi(v.y) : f16_hi(v.y);
+    } else {
+#pragma unroll
+      for (int i = 0; i < VE; ++i) {
+        const uint32_t u = p[i];
+        out[i] = (ST == kBF16) ? bf16_lo(u) : f16_lo(u);
+      }
+    }
+  }
+}
+
+// Narrow VE fp32 values to the storage dtype and store them at element e.
+template <int ST, int VE>
+__device__ __forceinline__ void narrow_store(void* base, int64_t e, const float* v) {
+  if constexpr (ST == kF32) {
+    float* p = static_cast<float*>(base) + e;
+    if constexpr (VE == 4) {
+      *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < VE; ++i) p[i] = v[i];
+    }
+  } else {
+    uint16_t* p = static_cast<uint16_t*>(base) + e;
+    auto cvt = [](float f) { return (ST == kBF16) ? f32_to_bf16_bits(f) : f32_to_f16_bits(f); };
+    if constexpr (VE == 4) {
+      *reinterpret_cast<uint2*>(p) =
+          make_uint2(cvt(v[0]) | (cvt(v[1]) << 16), cvt(v[2]) | (cvt(v[3]) << 16));
+    } else {
+#pragma unroll
+      for (int i = 0; i < VE; ++i) p[i] = static_cast<uint16_t>(cvt(v[i]));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launch interfaces (host side, implemented next to their kernels)
+// ---------------------------------------------------------------------------
+
+struct ForwardLaunch {
+  const void* weights;
+  const void* indices;
+  const void* offsets;
+  const float* psw;         // may be null
+  float* out;
+  const TableMeta* meta;
+  int32_t T, B, sum_dims;
+  int32_t tiles_per_table;  // workgroups per table
+  int32_t lshift;           // log2(rows in flight per bag per lane group)
+  int32_t mean;
+  int32_t dtype;            // storage dtype code
+  int32_t index64;          // indices/offsets are int64
+  int32_t vec;              // 16-byte row chunks (else one element per lane)
+};
+hipError_t launch_forward_gather(const ForwardLaunch& a, hipStream_t stream);
+
+// Device workspace of the backward, carved by the host.
+struct BackwardBuffers {
+  uint32_t* keys[2];
+  uint32_t* vals[2];
+  uint2* rec;               // per lookup {bag, coefficient bits} when needed, else null
+  uint32_t* hist;           // [256 * sort_tiles]
+  uint32_t* digit_totals;   // [256]
+  uint32_t* rle_tiles;      // [rle_tiles]
+  uint32_t* unique_keys;    // [N]
+  uint32_t* run_start;      // [N + 1]
+  uint32_t* counters;       // [4]: U, long runs, level-1 items, level-2 items
+  uint2* items1;            // {long run, chunk}
+  uint2* items2;            // {long run, super-chunk}
+  uint4* longs;             // {run, item1 base, item1 count, item2 base}
+  float* partial1;          // [items1 cap, pstride]
+  float* partial2;          // [items2 cap, pstride]
+};
+
+enum { kCntUnique = 0, kCntLong = 1, kCntItems1 = 2, kCntItems2 = 3 };
+
+struct BackwardLaunch {
+  const void* indices;
+  const void* offsets;
+  const float* psw;
+  const float* grad;
+  void* weights;
+  float* state;
+  const TableMeta* meta;
+  int64_t num_indices;
+  int64_t num_bags;
+  int32_t T, B, sum_dims;
+  int32_t key_bits;
+  int32_t mean, index64, dtype, adagrad;
+  int32_t use_rec;
+  int32_t vec;              // G_Y rows read as 16-byte chunks
+  int32_t nch;              // chunk sets per lane in the segment kernels (1, 4 or 16)
+  int32_t gshift;           // log2(lanes per gradient row) in the segment kernels
+  int32_t pstride;          // floats per partial row
+  int32_t long_threshold;   // runs at least this long use split accumulation
+  int32_t chunk;            // lookups per level-1 partial
+  int32_t super_chunk;      // level-1 partials per level-2 partial
+  float lr, eps;
+  int32_t* out_unique;      // optional run outputs
+  int32_t* out_lengths;
+  int32_t* out_num;
+  BackwardBuffers buf;
+};
+
+// Stage hooks let the host record profiling events between launches.
+typedef void (*StageHook)(void* ctx, const char* stage_name);
+
+hipError_t launch_linearize(const BackwardLaunch& a, hipStream_t stream);
+// Sorts buf.keys[0]/vals[0]; returns the index (0 or 1) of the buffer pair
+// that holds the sorted result.
+hipError_t launch_radix_sort(const BackwardLaunch& a, hipStream_t stream, int* result_buffer,
+                             StageHook hook, void* ctx);
+hipError_t launch_run_length_encode(const BackwardLaunch& a, const uint32_t* sorted_keys,
+                                    hipStream_t stream);
+hipError_t launch_segment_reduce_update(const BackwardLaunch& a, const uint32_t* sorted_vals,
+                                        hipStream_t stream, StageHook hook, void* ctx);
+
+// Row loads a forward lane group issues before it accumulates (shared by the
+// kernel and the host planner that sizes sub-waves from the mean bag length).
+constexpr int kFwdUnroll = 4;
+
+// Largest embedding dimension handled.
+constexpr int kMaxDim = 1024;
+
+// Tile sizes shared by the planner (workspace sizing) and the kernels.
+constexpr int kSortKeysPerThread = 8;
+constexpr int kSortTile = kBlock * kSortKeysPerThread;   // 2048 keys
+constexpr int kRleTile = 4096;
+constexpr int kRadixBits = 8;
+constexpr int kRadix = 1 << kRadixBits;
+
+}  // namespace tbe

@@ -1,0 +1,179 @@
+// forward.hip -- pooled multi-table lookup (the TBE forward) for gfx950.
+//
+// What it computes (kimbodo.com/?p=28372, "What Happened"; "FBTriton Rewrites
+// Table Batched Embedding", "Responsibilities of the forward and backward
+// passes"): for every bag k = t*B + b,
+//     Y[b, doff_t + d] = s_k * sum_{i in bag k} p_i * W_t[x_i, d]
+// with s_k = 1 (sum) or 1/L_k (mean; empty bags give 0), p_i the optional
+// per-sample weight, and fp32 accumulation whatever the storage dtype.  All
+// tables are covered by a single launch.
+//
+// Mapping onto CDNA4:
+//  * A lane group of Gs = 2^gshift lanes covers one table row: each lane loads
+//    one 16-byte chunk (4 fp32 or 8 fp16/bf16 elements), so a row read is one
+//    coalesced access.  Rows wider than 64 chunks are walked in chunk sets.
+//  * A bag is handled by a sub-wave of SW = Gs * 2^lshift lanes (at most the
+//    whole wave): its R = SW / Gs lane groups read R different rows of the bag
+//    per instruction and U instructions are issued before the first result
+//    is consumed, so a bag keeps R*U row reads in flight.  lshift is picked per
+//    call from the mean bag length so that one such round usually covers a
+//    bag.  Small rows and short bags therefore pack several bags per wave;
+//    wide rows or long bags get a whole wave per bag.
+//  * The bag's row ids are loaded once, one per lane of the sub-wave
+//    (coalesced), and broadcast to the lane groups with ds_bpermute.
+//  * At the end the R partial sums are folded with cross-lane adds and the
+//    first lane group writes the fp32 output with 16-byte stores.
+//  * Workgroups are renumbered so that every XCD works on a contiguous range
+//    of tables, which keeps each table's hot rows in one XCD's L2.
+#include "common.hpp"
+
+namespace tbe {
+namespace {
+
+constexpr int kUnroll = kFwdUnroll;
+
+template <typename IT>
+__device__ __forceinline__ int64_t ld_index(const void* p, int64_t i) {
+  return static_cast<int64_t>(static_cast<const IT*>(p)[i]);
+}
+
+// ST: storage dtype code; IT: index type; VEC: 16-byte chunks (else one
+// element per lane); PSW: per-sample weights present.
+template <int ST, typename IT, bool VEC, bool PSW>
+__global__ __launch_bounds__(kBlock) void fwd_gather_pool(ForwardLaunch a) {
+  constexpr int SB = StorageTraits<ST>::bytes;
+  constexpr int VE = VEC ? 16 / SB : 1;  // elements per lane chunk
+
+  const int logical = xcd_contiguous_block(blockIdx.x, gridDim.x);
+  const int t = logical / a.tiles_per_table;
+  const int tile = logical - t * a.tiles_per_table;
+  const TableMeta m = a.meta[t];
+
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int gshift = m.fwd_gshift;
+  const int swshift = min(6, gshift + a.lshift);
+  const int SW = 1 << swshift;                  // lanes per bag
+  const int Gs = 1 << gshift;                   // lanes per row
+  const int R = SW >> gshift;                   // rows per instruction per bag
+  const int sl = lane & (SW - 1);               // lane within the bag's sub-wave
+  const int g = sl >> gshift;                   // lane group within the sub-wave
+  const int gl = sl & (Gs - 1);                 // lane within the lane group
+  const int sub_base = lane & ~(SW - 1);
+
+  const int b = ((tile * kWavesPerBlock + wave) << (6 - swshift)) + (lane >> swshift);
+  const bool bag_ok = b < a.B;
+  const int64_t k = static_cast<int64_t>(t) * a.B + b;
+  int64_t start = 0, end = 0;
+  if (bag_ok) {
+    start = ld_index<IT>(a.offsets, k);
+    end = ld_index<IT>(a.offsets, k + 1);
+  }
+  const int D = m.dim;
+  const int C = VEC ? D / VE : D;               // chunks per row
+  const void* wbase = static_cast<const char*>(a.weights) + m.woff * SB;
+  float scale = 1.0f;
+  if (a.mean) scale = (end > start) ? 1.0f / static_cast<float>(end - start) : 0.0f;
+  float* orow = a.out + static_cast<int64_t>(b) * a.sum_dims + m.doff;
+
+  for (int cb = 0; cb < C; cb += Gs) {
+    const int chunk = cb + gl;
+    const bool lane_ok = chunk < C;
+    float acc[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) acc[e] = 0.0f;
+
+    for (int64_t j0 = start; j0 < end; j0 += SW) {
+      const int n = static_cast<int>(min(static_cast<int64_t>(SW), end - j0));
+      int my_row = 0;
+      float my_p = 1.0f;
+      if (sl < n) {
+        my_row = static_cast<int>(ld_index<IT>(a.indices, j0 + sl));
+        if constexpr (PSW) my_p = a.psw[j0 + sl];
+      }
+      for (int r = 0; r < n; r += R * kUnroll) {
+        float v[kUnroll][VE];
+        float p[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const int jj = r + u * R + g;
+          const int src = sub_base + min(jj, SW - 1);
+          const int row = __shfl(my_row, src, kWave);
+          p[u] = PSW ? __shfl(my_p, src, kWave) : 1.0f;
+          if (jj < n && lane_ok) {
+            load_widen<ST, VE>(wbase, static_cast<int64_t>(row) * D + chunk * VE, v[u]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < VE; ++e) v[u][e] = 0.0f;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+#pragma unroll
+          for (int e = 0; e < VE; ++e) {
+            if constexpr (PSW)
+              acc[e] = fmaf(p[u], v[u][e], acc[e]);
+            else
+              acc[e] += v[u][e];
+          }
+        }
+      }
+    }
+    // fold the R lane groups of the bag
+    for (int o = SW >> 1; o >= Gs; o >>= 1) {
+#pragma unroll
+      for (int e = 0; e < VE; ++e) acc[e] += __shfl_xor(acc[e], o, kWave);
+    }
+    if (bag_ok && g == 0 && lane_ok) {
+      float* dst = orow + chunk * VE;
+      if constexpr (VE % 4 == 0) {
+#pragma unroll
+        for (int e = 0; e < VE; e += 4)
+          *reinterpret_cast<float4*>(dst + e) =
+              make_float4(acc[e] * scale, acc[e + 1] * scale, acc[e + 2] * scale, acc[e + 3] * scale);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VE; ++e) dst[e] = acc[e] * scale;
+      }
+    }
+  }
+}
+
+template <int ST, typename IT>
+hipError_t dispatch_vec_psw(const ForwardLaunch& a, hipStream_t s, dim3 grid) {
+  if (a.vec) {
+    if (a.psw)
+      hipLaunchKernelGGL((fwd_gather_pool<ST, IT, true, true>), grid, dim3(kBlock), 0, s, a);
+    else
+      hipLaunchKernelGGL((fwd_gather_pool<ST, IT, true, false>), grid, dim3(kBlock), 0, s, a);
+  } else {
+    if (a.psw)
+      hipLaunchKernelGGL((fwd_gather_pool<ST, IT, false, true>), grid, dim3(kBlock), 0, s, a);
+    else
+      hipLaunchKernelGGL((fwd_gather_pool<ST, IT, false, false>), grid, dim3(kBlock), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <int ST>
+hipError_t dispatch_index(const ForwardLaunch& a, hipStream_t s, dim3 grid) {
+  return a.index64 ? dispatch_vec_psw<ST, int64_t>(a, s, grid)
+                   : dispatch_vec_psw<ST, int32_t>(a, s, grid);
+}
+
+}  // namespace
+
+hipError_t launch_forward_gather(const ForwardLaunch& a, hipStream_t stream) {
+  const int64_t blocks = static_cast<int64_t>(a.T) * a.tiles_per_table;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<unsigned>(blocks));
+  switch (a.dtype) {
+    case kF32: return dispatch_index<kF32>(a, stream, grid);
+    case kF16: return dispatch_index<kF16>(a, stream, grid);
+    case kBF16: return dispatch_index<kBF16>(a, stream, grid);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace tbe

@@ -1,0 +1,200 @@
+"""Shared parity machinery for the GPU tests: run the HIP library through its
+C ABI on seeded inputs and compare every result with the CPU reference.
+
+Comparison rules (tolerances relative to the absolute-sum scale, since sums of
+signed values may cancel):
+  forward       |Y - Y_ref| <= rtol * s_k * sum_i |p_i W[x_i, d]|
+                rtol = 1e-5 for fp32 storage, 1e-2 for fp16 / bf16 storage;
+                every storage dtype is also held to 1e-5, as both sides read the
+                same stored values and accumulate in fp32 or better.
+  runs          unique row ids, run lengths and their count: bit-exact.
+  fp32 weights  |W - W_ref| <= 1e-5 * (|W_old| + max_d |W_ref - W_old| over the row)
+  fp16 / bf16   within one unit in the last place of the storage dtype at W_ref.
+  state         |m - m_ref| <= 1e-5 * m_ref.
+  other rows    bit-identical weights and state.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+import torch
+
+import oracle
+import table_embedding_bag_amd as tbe
+import workloads
+
+DEV = "cuda"
+
+
+def code(spec):
+    return workloads.oracle_dtype(spec.dtype)
+
+
+def pool(spec):
+    return oracle.POOL_MEAN if spec.pooling == "mean" else oracle.POOL_SUM
+
+
+def opt(spec):
+    return oracle.OPT_ROWWISE_ADAGRAD if spec.optimizer == "rowwise_adagrad" else oracle.OPT_SGD
+
+
+def abs_bits(spec, W: np.ndarray) -> np.ndarray:
+    """|W| of raw storage bits (sign bit cleared)."""
+    if spec.dtype == "f32":
+        return np.abs(W)
+    return W & np.uint16(0x7FFF)
+
+
+def layout(spec):
+    rows = np.array(spec.rows, np.int64)
+    dims = np.array(spec.dims, np.int64)
+    return (np.concatenate([[0], np.cumsum(rows * dims)]), np.concatenate([[0], np.cumsum(rows)]),
+            np.concatenate([[0], np.cumsum(dims)]))
+
+
+@dataclasses.dataclass
+class Problem:
+    spec: workloads.Spec
+    batch: workloads.Batch
+    W: torch.Tensor                 # device weights (updated in place by the library)
+    state: Optional[torch.Tensor]
+    op: tbe.TBE
+    idx: torch.Tensor
+    off: torch.Tensor
+    psw: Optional[torch.Tensor]
+
+
+def make_problem(spec, seed=0, step=0, index_dtype=torch.int64, batch=None, flags=0) -> Problem:
+    batch = batch if batch is not None else workloads.batch(spec, seed=seed, step=step)
+    W = workloads.weights(spec, seed=seed, device=DEV)
+    state = torch.zeros(spec.sum_rows, dtype=torch.float32, device=DEV) \
+        if spec.optimizer == "rowwise_adagrad" else None
+    op = tbe.TBE(spec.rows, spec.dims, W, state, pooling=spec.pooling, optimizer=spec.optimizer,
+                 flags=flags)
+    return Problem(spec, batch, W, state, op, *to_device(batch, index_dtype))
+
+
+def to_device(batch, index_dtype=torch.int64):
+    idx = torch.from_numpy(batch.indices).to(DEV, index_dtype)
+    off = torch.from_numpy(batch.offsets).to(DEV, index_dtype)
+    psw = torch.from_numpy(batch.psw).to(DEV) if batch.psw is not None else None
+    return idx, off, psw
+
+
+def check_forward(pb: Problem, Y: torch.Tensor, W_host: np.ndarray, bag_sample=None):
+    """Compare the GPU output with the reference on all bags (or a sample of bag ids)."""
+    spec, batch = pb.spec, pb.batch
+    Yh = Y.cpu().numpy()
+    _, _, doff = layout(spec)
+    if bag_sample is None:
+        ref = oracle.forward(spec.rows, spec.dims, code(spec), pool(spec), W_host, spec.B,
+                             batch.indices, batch.offsets, batch.psw)
+        scale = oracle.forward(spec.rows, spec.dims, code(spec), pool(spec), abs_bits(spec, W_host),
+                               spec.B, batch.indices, batch.offsets,
+                               None if batch.psw is None else np.abs(batch.psw))
+        got = Yh
+    else:
+        ids = np.asarray(bag_sample, np.int64)
+        ref = np.concatenate(oracle.forward_bags(spec.rows, spec.dims, code(spec), pool(spec), W_host,
+                                                 spec.B, batch.indices, batch.offsets, batch.psw, ids))
+        scale = np.concatenate(oracle.forward_bags(
+            spec.rows, spec.dims, code(spec), pool(spec), abs_bits(spec, W_host), spec.B,
+            batch.indices, batch.offsets, None if batch.psw is None else np.abs(batch.psw), ids))
+        got = np.concatenate([Yh[k % spec.B, doff[k // spec.B]:doff[k // spec.B + 1]] for k in ids])
+    err = np.abs(got - ref)
+    rel = err / (scale + 1e-30)
+    rtol = 1e-5 if spec.dtype == "f32" else 1e-2
+    assert np.isfinite(got).all()
+    assert (err <= rtol * scale + 1e-30).all(), f"forward: max rel err {rel.max():.3e} > {rtol}"
+    assert (err <= 1e-5 * scale + 1e-30).all(), f"forward: max rel err {rel.max():.3e} > 1e-5"
+    return float(rel.max())
+
+
+def gpu_runs(pb: Problem, n):
+    u = torch.empty(max(n, 1), dtype=torch.int32, device=DEV)
+    c = torch.empty(max(n, 1), dtype=torch.int32, device=DEV)
+    k = torch.zeros(1, dtype=torch.int32, device=DEV)
+    return u, c, k
+
+
+def check_runs(pb: Problem, runs):
+    spec, batch = pb.spec, pb.batch
+    uniq, cnt = oracle.runs(spec.rows, spec.B, batch.indices, batch.offsets)
+    U = int(runs[2].item())
+    assert U == uniq.size, f"U {U} != {uniq.size}"
+    assert np.array_equal(runs[0][:U].cpu().numpy().astype(np.int64), uniq)
+    assert np.array_equal(runs[1][:U].cpu().numpy().astype(np.int64), cnt)
+    return uniq, cnt
+
+
+def ulp_distance(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
+    """Distance in units of the storage format between 16-bit codes (monotone ordering)."""
+    def ordered(x):
+        x = x.astype(np.int64)
+        return np.where(x & 0x8000, -(x & 0x7FFF), x)
+    return np.abs(ordered(a_bits) - ordered(b_bits))
+
+
+def rows_of(spec, flat, linear_ids):
+    """{table: [n_t, D_t] raw storage rows} of the given linear row ids, from a
+    flat host array or a flat device tensor (gathered on the device)."""
+    woff, roff, _ = layout(spec)
+    ids = np.asarray(linear_ids, np.int64)
+    tab = np.searchsorted(roff, ids, side="right") - 1
+    out = {}
+    for t in np.unique(tab):
+        D = spec.dims[t]
+        r = ids[tab == t] - roff[t]
+        el = woff[t] + r[:, None] * D + np.arange(D)[None, :]
+        if isinstance(flat, torch.Tensor):
+            out[int(t)] = workloads.storage_numpy(flat[torch.from_numpy(el.reshape(-1)).to(flat.device)]).reshape(-1, D)
+        else:
+            out[int(t)] = flat[el]
+    return out
+
+
+def check_update(spec, before: dict, ref: dict, gpu: dict, st_ref=None, st_gpu=None, ids=None):
+    """Compare updated rows (dicts from rows_of) and, for Adagrad, state values at ids."""
+    worst = 0.0
+    for t, f in ref.items():
+        g, o = gpu[t], before[t]
+        if spec.dtype == "f32":
+            tol = 1e-5 * (np.abs(o) + np.abs(f - o).max(axis=1, keepdims=True))
+            err = np.abs(g - f)
+            ratio = float((err / (tol + 1e-38)).max())
+            assert (err <= tol).all(), f"table {t}: weight err {ratio:.3f} x tol"
+            worst = max(worst, ratio)
+        else:
+            d = ulp_distance(g, f)
+            assert d.max() <= 1, f"table {t}: weights differ by {d.max()} ulp"
+            worst = max(worst, float(d.max()))
+    if st_ref is not None:
+        m, mr = st_gpu[ids], st_ref[ids]
+        assert (np.abs(m - mr) <= 1e-5 * mr + 1e-30).all(), "state mismatch"
+    return worst
+
+
+def run_step(pb: Problem, G: torch.Tensor, lr=None, eps=None, with_runs=True):
+    spec = pb.spec
+    runs = gpu_runs(pb, pb.batch.N) if with_runs else None
+    pb.op.backward_update(spec.B, pb.idx, pb.off, pb.psw, G,
+                          spec.lr if lr is None else lr, spec.eps if eps is None else eps, runs)
+    torch.cuda.synchronize()
+    return runs
+
+
+def reference_update(pb: Problem, W_host: np.ndarray, st_host, G_host, selected=None):
+    spec, batch = pb.spec, pb.batch
+    oracle.backward_update(spec.rows, spec.dims, code(spec), pool(spec), opt(spec), W_host, st_host,
+                           spec.B, batch.indices, batch.offsets, batch.psw, G_host,
+                           float(np.float32(spec.lr)), float(np.float32(spec.eps)), selected)
+
+
+def untouched_identical(spec, before: dict, gpu: dict, st_before=None, st_gpu=None, ids=None):
+    """Rows no lookup hit keep bit-identical weights (and state)."""
+    for t in before:
+        assert np.array_equal(before[t], gpu[t]), f"table {t}: an untouched row changed"
+    if st_before is not None:
+        assert np.array_equal(st_before[ids], st_gpu[ids]), "untouched state changed"

@@ -1,0 +1,83 @@
+"""The C ABI library loads, exports every entry point include/tbe.h declares,
+and rejects bad arguments on the host before touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import table_embedding_bag_amd as tbe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "tbe.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:tbe_status|void|const char\*|int32_t)\s+(tbe_\w+)\(", src, re.M)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(tbe.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(tbe.library_path())
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings():
+    assert tbe.tbe_abi_version() == 1
+    for s in range(7):
+        assert tbe.tbe_status_string(s)
+    assert tbe.tbe_status_string(0) == "ok"
+
+
+def _cfg(rows, dims, dtype=0, pooling=0, opt=0, flags=0):
+    T = len(rows)
+    r = (ctypes.c_int64 * T)(*rows)
+    d = (ctypes.c_int32 * T)(*dims)
+    return tbe._Config(T, r, d, dtype, pooling, opt, flags), (r, d)
+
+
+@pytest.mark.parametrize("case", ["null_weights", "no_tables", "zero_rows", "dim_too_big", "bad_dtype",
+                                  "bad_pooling", "bad_optimizer", "adagrad_without_state",
+                                  "unknown_flag", "conflicting_flags", "misaligned_weights"])
+def test_create_rejects_bad_configs_on_host(case):
+    lib = tbe.load()
+    rows, dims, kw, w, st = [10, 20], [8, 8], {}, 4096, None
+    if case == "no_tables":
+        rows, dims = [], []
+    elif case == "zero_rows":
+        rows = [10, 0]
+    elif case == "dim_too_big":
+        dims = [8, 4096]
+    elif case == "bad_dtype":
+        kw["dtype"] = 7
+    elif case == "bad_pooling":
+        kw["pooling"] = 3
+    elif case == "bad_optimizer":
+        kw["opt"] = 9
+    elif case == "adagrad_without_state":
+        kw["opt"] = 1
+    elif case == "unknown_flag":
+        kw["flags"] = 64
+    elif case == "conflicting_flags":
+        kw["flags"] = 6
+    elif case == "misaligned_weights":
+        w = 4096 + 4
+    if case == "null_weights":
+        w = None
+    cfg, keep = _cfg(rows, dims, **kw)
+    out = ctypes.c_void_p(123)
+    rc = lib.tbe_create(ctypes.byref(cfg), w, st, ctypes.byref(out))
+    assert rc == 1 and out.value is None
+
+
+def test_null_handle_calls_are_rejected():
+    lib = tbe.load()
+    n = ctypes.c_size_t(0)
+    assert lib.tbe_backward_workspace_size(None, 4, 10, ctypes.byref(n)) == 1
+    assert lib.tbe_forward(None, 4, None, None, 1, 0, None, None, None) == 1
+    assert lib.tbe_set_option(None, 1, 5) == 1
+    lib.tbe_destroy(None)

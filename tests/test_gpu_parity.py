@@ -1,0 +1,273 @@
+"""GPU parity of the HIP library (through its C ABI) against the CPU reference.
+
+Forward pooling over all tables with optional per-sample weights and fp32
+accumulation, and the fused backward (linearize, sort, run-length encode,
+segment reduce, one optimizer update per touched row): kimbodo.com/?p=28372,
+"What Happened" and "Kimbodo Engineering Perspective".  Comparison rules are
+documented in gpu_check.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import table_embedding_bag_amd as tbe
+import workloads
+from gpu_check import (Problem, check_forward, check_runs, check_update, layout, make_problem,
+                       reference_update, rows_of, run_step, to_device, untouched_identical)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def parity(spec, seed=0, steps=2, bag_sample=None, row_sample=None, index_dtype=torch.int64,
+           threshold=None, batches=None):
+    """Forward and backward_update for `steps` steps, each checked against the reference,
+    which advances its own copy of weights and state."""
+    _say(f"[parity] {spec.name} dtype={spec.dtype} seed={seed} thr={threshold}")
+    pb = make_problem(spec, seed=seed, index_dtype=index_dtype,
+                      batch=None if batches is None else batches[0])
+    if threshold is not None:
+        pb.op.set_option(tbe.OPTION_LONG_RUN_THRESHOLD, threshold)
+    W_host = workloads.storage_numpy(pb.W).copy()
+    st_host = np.zeros(spec.sum_rows, np.float32) if pb.state is not None else None
+    rng = np.random.default_rng(seed + 99)
+    report = {}
+    for step in range(steps):
+        if step > 0:
+            pb.batch = batches[step] if batches is not None else workloads.batch(spec, seed=seed, step=step)
+            pb.idx, pb.off, pb.psw = to_device(pb.batch, index_dtype)
+        nbags = spec.T * spec.B
+        sample = None
+        if bag_sample is not None and bag_sample < nbags:
+            sample = np.unique(np.concatenate([
+                rng.choice(nbags, bag_sample, replace=False),
+                np.arange(spec.T) * spec.B, np.arange(1, spec.T + 1) * spec.B - 1]))
+        Y = pb.op.forward(spec.B, pb.idx, pb.off, pb.psw)
+        torch.cuda.synchronize()
+        report[f"fwd{step}"] = check_forward(pb, Y, W_host, sample)
+        _say(f"  step {step}: forward ok (max rel {report[f'fwd{step}']:.2e})")
+
+        G = workloads.grad_output(spec, seed=seed, step=step, device="cuda")
+        runs = run_step(pb, G)
+        uniq, cnt = check_runs(pb, runs)
+        _say(f"  step {step}: runs ok (U={uniq.size}, max run {cnt.max() if cnt.size else 0})")
+        if row_sample is not None and uniq.size > row_sample:
+            hot = uniq[np.argsort(cnt)[-50:]]
+            sel = np.unique(np.concatenate([rng.choice(uniq, row_sample, replace=False), hot,
+                                            uniq[:5], uniq[-5:]]))
+        else:
+            sel = uniq
+        before = rows_of(spec, W_host, sel)
+        st_before = st_host.copy() if st_host is not None else None
+        reference_update(pb, W_host, st_host, G.cpu().numpy())
+        st_gpu = pb.state.cpu().numpy() if pb.state is not None else None
+        report[f"upd{step}"] = check_update(spec, before, rows_of(spec, W_host, sel),
+                                            rows_of(spec, pb.W, sel), st_host, st_gpu, sel)
+        # rows nobody looked up stay bit-identical
+        untouched = np.setdiff1d(np.arange(spec.sum_rows), uniq, assume_unique=True)
+        if untouched.size > 20000:
+            untouched = np.sort(rng.choice(untouched, 20000, replace=False))
+        if untouched.size:
+            untouched_identical(spec, rows_of(spec, W_host, untouched), rows_of(spec, pb.W, untouched),
+                                st_before, st_gpu, untouched)
+        _say(f"  step {step}: update ok (worst {report[f'upd{step}']:.3f})")
+    pb.op.close()
+    return report
+
+
+# --------------------------------------------------------------------------
+# the page's worked example and small unit cases
+# --------------------------------------------------------------------------
+
+def test_worked_example_bit_exact():
+    import json, os
+    ex = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")))
+    E, D = 16, 8
+    Wn = (np.arange(E)[:, None] + np.arange(D)[None, :] / 4.0).astype(np.float32)
+    W = torch.from_numpy(Wn.reshape(-1)).cuda()
+    op = tbe.TBE([E], [D], W)
+    idx = torch.tensor(ex["indices"], dtype=torch.int64, device="cuda")
+    off = torch.tensor(ex["offsets"], dtype=torch.int64, device="cuda")
+    Y = op.forward(len(ex["offsets"]) - 1, idx, off).cpu().numpy()
+    for b, bag in enumerate(ex["bags"]):
+        assert np.array_equal(Y[b], Wn[bag].sum(axis=0))
+    op.close()
+
+
+UNIT = [
+    workloads.custom([50, 7, 300], [8, 4, 16], "f32", B=33, lengths=("uniform_int", 0, 9), key=201),
+    workloads.custom([50, 7, 300], [8, 16, 32], "bf16", B=33, lengths=("uniform_int", 0, 9), key=202,
+                     optimizer="rowwise_adagrad"),
+    workloads.custom([20, 90], [64, 8], "f16", B=70, lengths=("uniform_int", 0, 40),
+                     index_dist=("zipf", 1.2), pooling="mean", optimizer="rowwise_adagrad", key=203),
+    workloads.custom([40, 13, 9], [4, 12, 64], "f32", B=65, lengths=("uniform_int", 0, 8), psw=True,
+                     key=204),
+    workloads.custom([40, 13, 9], [8, 24, 64], "bf16", B=65, lengths=("uniform_int", 0, 8), psw=True,
+                     pooling="mean", optimizer="rowwise_adagrad", key=205),
+    # dims that are not whole 16-byte chunks: one element per lane
+    workloads.custom([30, 11], [6, 3], "f32", B=17, lengths=("uniform_int", 0, 7), key=206,
+                     optimizer="rowwise_adagrad"),
+    workloads.custom([30, 11], [6, 10], "bf16", B=17, lengths=("uniform_int", 0, 7), key=207,
+                     psw=True, pooling="mean"),
+    # wide rows: chunk sets per lane in both directions
+    workloads.custom([100, 60], [512, 1024], "f32", B=9, lengths=("uniform_int", 1, 20), key=208,
+                     optimizer="rowwise_adagrad"),
+    workloads.custom([100, 60], [520, 96], "f16", B=9, lengths=("uniform_int", 1, 20), key=209),
+    workloads.custom([100], [300], "bf16", B=9, lengths=("uniform_int", 1, 20), key=210),
+    # long bags (a whole wave per bag, several index chunks)
+    workloads.custom([1000], [128], "f32", B=40, lengths=("uniform_int", 60, 300), key=211,
+                     index_dist=("zipf", 1.1), optimizer="rowwise_adagrad"),
+]
+
+
+@pytest.mark.parametrize("spec", UNIT, ids=lambda s: f"{s.key}-{s.dtype}-{s.pooling}-psw{int(s.psw)}-{s.optimizer}")
+def test_unit_parity(spec):
+    parity(spec, seed=1, steps=2)
+
+
+@pytest.mark.parametrize("spec", [UNIT[0], UNIT[4]], ids=["f32", "bf16-mean-psw"])
+def test_int32_indices(spec):
+    parity(spec, seed=2, steps=1, index_dtype=torch.int32)
+
+
+def _hand_batch(T, B, bags):
+    """bags: list (per table) of lists (per bag) of row ids."""
+    lens = [len(b) for tb in bags for b in tb]
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    idx = np.array([x for tb in bags for b in tb for x in b], dtype=np.int64)
+    return workloads.Batch(idx, off, None)
+
+
+def test_run_length_boundaries_and_long_runs():
+    # rows hit exactly 255 / 256 / 257 times straddle the long-run threshold; one row
+    # hit 20000 times needs more than 32 chunk partials (the two-level combine).
+    E, D, B = 64, 32, 400
+    rng = np.random.default_rng(3)
+    hits = [3] * 255 + [7] * 256 + [9] * 257 + [11] * 20000 + list(rng.integers(0, E, 3000))
+    hits = rng.permutation(np.array(hits))
+    per_bag = np.array_split(hits, B)
+    batch = _hand_batch(1, B, [[list(b) for b in per_bag]])
+    for opt in ("sgd", "rowwise_adagrad"):
+        spec = workloads.custom([E], [D], "f32", B=B, optimizer=opt, key=220)
+        for thr in (None, 1, 1 << 30):
+            parity(spec, seed=4, steps=1, threshold=thr, batches=[batch])
+
+
+def test_dyadic_sgd_is_bit_exact():
+    # with dyadic weights, gradients and learning rate every sum is exact in any order
+    E, D, B = 40, 16, 300
+    rng = np.random.default_rng(5)
+    spec = workloads.custom([E, E], [D, D], "f32", B=B, lengths=("uniform_int", 0, 12),
+                            index_dist=("zipf", 1.3), key=230, lr=0.25)
+    batch = workloads.batch(spec, seed=5)
+    Wn = (rng.integers(-64, 64, spec.num_weights) / 64.0).astype(np.float32)
+    Gn = (rng.integers(-8, 8, (B, spec.sum_dims)) / 8.0).astype(np.float32)
+    W = torch.from_numpy(Wn).cuda()
+    G = torch.from_numpy(Gn).cuda()
+    op = tbe.TBE(spec.rows, spec.dims, W)
+    idx, off, _ = to_device(batch)
+    Y = op.forward(B, idx, off).cpu().numpy()
+    Yr = oracle.forward(spec.rows, spec.dims, oracle.F32, oracle.POOL_SUM, Wn, B, batch.indices,
+                        batch.offsets)
+    assert np.array_equal(Y, Yr)
+    for thr in (1, 256, 1 << 30):
+        W.copy_(torch.from_numpy(Wn))
+        op.set_option(tbe.OPTION_LONG_RUN_THRESHOLD, thr)
+        op.backward_update(B, idx, off, None, G, 0.25)
+        Wr = Wn.copy()
+        oracle.backward_update(spec.rows, spec.dims, oracle.F32, oracle.POOL_SUM, oracle.OPT_SGD, Wr,
+                               None, B, batch.indices, batch.offsets, None, Gn, 0.25, 0.0)
+        assert np.array_equal(W.cpu().numpy(), Wr)
+    op.close()
+
+
+def test_empty_bags_and_empty_batch():
+    spec = workloads.custom([10, 10], [8, 8], "f32", B=5, optimizer="rowwise_adagrad", key=240,
+                            pooling="mean")
+    W = workloads.weights(spec, 0, "cuda")
+    W0 = W.clone()
+    st = torch.zeros(spec.sum_rows, device="cuda")
+    op = tbe.TBE(spec.rows, spec.dims, W, st, pooling="mean", optimizer="rowwise_adagrad")
+    # all bags empty
+    off = torch.zeros(2 * 5 + 1, dtype=torch.int64, device="cuda")
+    idx = torch.zeros(0, dtype=torch.int64, device="cuda")
+    Y = torch.full((5, 16), 7.0, device="cuda")
+    op.forward(5, idx, off, out=Y)
+    torch.cuda.synchronize()
+    assert (Y == 0).all()
+    G = torch.randn(5, 16, device="cuda")
+    runs = (torch.zeros(1, dtype=torch.int32, device="cuda"),
+            torch.zeros(1, dtype=torch.int32, device="cuda"),
+            torch.full((1,), 5, dtype=torch.int32, device="cuda"))
+    op.backward_update(5, idx, off, None, G, 0.1, runs=runs)
+    torch.cuda.synchronize()
+    assert int(runs[2].item()) == 0
+    assert torch.equal(W, W0) and (st == 0).all()
+    # B = 0 is a no-op
+    op.forward(0, idx, torch.zeros(1, dtype=torch.int64, device="cuda"), out=Y)
+    # one table all-empty, the other not
+    batch = _hand_batch(2, 5, [[[], [], [], [], []], [[1, 2], [], [3], [3, 3, 9], []]])
+    parity(spec, seed=0, steps=1, batches=[batch])
+    op.close()
+
+
+def test_validate_flag_rejects_bad_ids_without_touching_outputs():
+    spec = workloads.custom([10, 20], [8, 8], "f32", B=4, key=250)
+    W = workloads.weights(spec, 0, "cuda")
+    W0 = W.clone()
+    op = tbe.TBE(spec.rows, spec.dims, W, flags=tbe.FLAG_VALIDATE)
+    idx = torch.tensor([1, 2, 10, 3, 19, 0], dtype=torch.int64, device="cuda")  # 10 is out of table 0
+    off = torch.tensor([0, 2, 3, 3, 3, 4, 5, 6, 6], dtype=torch.int64, device="cuda")
+    Y = torch.full((4, 16), 3.0, device="cuda")
+    with pytest.raises(tbe.TBEError) as e:
+        op.forward(4, idx, off, out=Y)
+    assert e.value.status == 3
+    assert (Y == 3.0).all()
+    G = torch.ones(4, 16, device="cuda")
+    with pytest.raises(tbe.TBEError):
+        op.backward_update(4, idx, off, None, G, 0.1)
+    torch.cuda.synchronize()
+    assert torch.equal(W, W0)
+    idx[2] = 9
+    op.forward(4, idx, off, out=Y)   # valid now
+    bad_off = off.clone()
+    bad_off[-1] = 5                  # offsets do not end at the id count
+    with pytest.raises(tbe.TBEError):
+        op.forward(4, idx, bad_off, out=Y)
+    op.close()
+
+
+def test_backward_is_deterministic():
+    spec = workloads.config(2)
+    spec = workloads.custom(spec.rows[:2], spec.dims[:2], "f32", B=1024, lengths=("uniform_int", 1, 32),
+                            index_dist=("zipf", 1.3), optimizer="rowwise_adagrad", key=260)
+    batch = workloads.batch(spec, seed=7)
+    idx, off, _ = to_device(batch)
+    G = workloads.grad_output(spec, seed=7, device="cuda")
+    outs = []
+    for _ in range(2):
+        W = workloads.weights(spec, 7, "cuda")
+        st = torch.zeros(spec.sum_rows, device="cuda")
+        op = tbe.TBE(spec.rows, spec.dims, W, st, optimizer="rowwise_adagrad")
+        op.backward_update(spec.B, idx, off, None, G, 0.01)
+        torch.cuda.synchronize()
+        outs.append((W.clone(), st.clone()))
+        op.close()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+# --------------------------------------------------------------------------
+# the five benchmark workloads, two optimizer steps each
+# --------------------------------------------------------------------------
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_workload_parity(n):
+    spec = workloads.config(n)
+    big = n >= 3
+    parity(spec, seed=0, steps=2, bag_sample=20000 if big else None,
+           row_sample=50000 if big else None)

@@ -36,15 +36,20 @@ namespace {
 
 constexpr int kSegUnroll = 4;  // gradient rows in flight per lane group
 
-// Rows gathered by one lane: NCH chunk sets of VE floats.
+// The slice of a summed gradient row held by one lane: NCH chunk sets of VE
+// values.  Sums are kept in fp64: a run may add the same gradient row many
+// times over (a hot row hit repeatedly inside one bag), and fp32 rounding
+// errors of such correlated sums grow linearly.  The products c_i * g are
+// exact in fp64, so each add rounds once at 2^-53; the kernels stay bound by
+// memory traffic, not by the fp64 adds.
 template <int VE, int NCH>
 struct Acc {
-  float v[NCH][VE];
+  double v[NCH][VE];
   __device__ __forceinline__ void zero() {
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
 #pragma unroll
-      for (int e = 0; e < VE; ++e) v[c][e] = 0.0f;
+      for (int e = 0; e < VE; ++e) v[c][e] = 0.0;
   }
 };
 
@@ -110,7 +115,8 @@ __device__ __forceinline__ void gather_sum(const BackwardLaunch& a, const uint32
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
 #pragma unroll
-        for (int q = 0; q < VE; ++q) acc.v[c][q] = fmaf(coef[u], v[u][c][q], acc.v[c][q]);
+        for (int q = 0; q < VE; ++q)
+          acc.v[c][q] = fma(static_cast<double>(coef[u]), static_cast<double>(v[u][c][q]), acc.v[c][q]);
   }
 }
 
@@ -123,13 +129,13 @@ __device__ __forceinline__ void apply_update(const BackwardLaunch& a, const Tabl
   const int C = D / VE;
   float step = a.lr;
   if (a.adagrad) {
-    float ss = 0.0f;
+    double ss = 0.0;
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
 #pragma unroll
-      for (int q = 0; q < VE; ++q) ss = fmaf(acc.v[c][q], acc.v[c][q], ss);
+      for (int q = 0; q < VE; ++q) ss = fma(acc.v[c][q], acc.v[c][q], ss);
     for (int o = g.Gs >> 1; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, kWave);
-    const float mnew = a.state[key] + ss / static_cast<float>(D);
+    const float mnew = static_cast<float>(static_cast<double>(a.state[key]) + ss / D);
     if (g.gl == 0) a.state[key] = mnew;
     step = a.lr / (sqrtf(mnew) + a.eps);
   }
@@ -141,7 +147,7 @@ __device__ __forceinline__ void apply_update(const BackwardLaunch& a, const Tabl
       float w[VE];
       load_widen<ST, VE>(a.weights, row0 + chunk * VE, w);
 #pragma unroll
-      for (int q = 0; q < VE; ++q) w[q] = fmaf(-step, acc.v[c][q], w[q]);
+      for (int q = 0; q < VE; ++q) w[q] = fmaf(-step, static_cast<float>(acc.v[c][q]), w[q]);
       narrow_store<ST, VE>(a.weights, row0 + chunk * VE, w);
     }
   }
@@ -227,10 +233,11 @@ __device__ __forceinline__ void store_partial(float* dst, const GroupCtx& g, int
     if (chunk < C) {
       if constexpr (VE == 4)
         *reinterpret_cast<float4*>(dst + chunk * 4) =
-            make_float4(acc.v[c][0], acc.v[c][1], acc.v[c][2], acc.v[c][3]);
+            make_float4(static_cast<float>(acc.v[c][0]), static_cast<float>(acc.v[c][1]),
+                        static_cast<float>(acc.v[c][2]), static_cast<float>(acc.v[c][3]));
       else
 #pragma unroll
-        for (int q = 0; q < VE; ++q) dst[chunk * VE + q] = acc.v[c][q];
+        for (int q = 0; q < VE; ++q) dst[chunk * VE + q] = static_cast<float>(acc.v[c][q]);
     }
   }
 }
@@ -267,7 +274,7 @@ __device__ __forceinline__ void sum_partials(const float* part, int pstride, uin
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
 #pragma unroll
-        for (int q = 0; q < VE; ++q) acc.v[c][q] += v[u][c][q];
+        for (int q = 0; q < VE; ++q) acc.v[c][q] += static_cast<double>(v[u][c][q]);
   }
 }
 

@@ -83,8 +83,9 @@ def to_device(batch, index_dtype=torch.int64):
     return idx, off, psw
 
 
-def check_forward(pb: Problem, Y: torch.Tensor, W_host: np.ndarray, bag_sample=None):
-    """Compare the GPU output with the reference on all bags (or a sample of bag ids)."""
+def check_forward(pb: Problem, Y: torch.Tensor, W_host: np.ndarray, bag_sample=None, dev=None):
+    """Compare the GPU output with the reference on all bags (or a sample of bag ids).
+    dev: per linear row, the deviation the GPU's weights may carry from earlier steps."""
     spec, batch = pb.spec, pb.batch
     Yh = Y.cpu().numpy()
     _, _, doff = layout(spec)
@@ -95,6 +96,7 @@ def check_forward(pb: Problem, Y: torch.Tensor, W_host: np.ndarray, bag_sample=N
                                spec.B, batch.indices, batch.offsets,
                                None if batch.psw is None else np.abs(batch.psw))
         got = Yh
+        ids = np.arange(spec.T * spec.B)
     else:
         ids = np.asarray(bag_sample, np.int64)
         ref = np.concatenate(oracle.forward_bags(spec.rows, spec.dims, code(spec), pool(spec), W_host,
@@ -103,12 +105,20 @@ def check_forward(pb: Problem, Y: torch.Tensor, W_host: np.ndarray, bag_sample=N
             spec.rows, spec.dims, code(spec), pool(spec), abs_bits(spec, W_host), spec.B,
             batch.indices, batch.offsets, None if batch.psw is None else np.abs(batch.psw), ids))
         got = np.concatenate([Yh[k % spec.B, doff[k // spec.B]:doff[k // spec.B + 1]] for k in ids])
+    carried = 0.0
+    if dev is not None and dev.any():
+        per_bag = forward_deviation(spec, pb.batch, dev)
+        if bag_sample is None:
+            carried = np.concatenate([np.repeat(per_bag[t * spec.B:(t + 1) * spec.B, None],
+                                                spec.dims[t], axis=1) for t in range(spec.T)], axis=1)
+        else:
+            carried = np.concatenate([np.full(spec.dims[k // spec.B], per_bag[k]) for k in ids])
     err = np.abs(got - ref)
     rel = err / (scale + 1e-30)
     rtol = 1e-5 if spec.dtype == "f32" else 1e-2
     assert np.isfinite(got).all()
-    assert (err <= rtol * scale + 1e-30).all(), f"forward: max rel err {rel.max():.3e} > {rtol}"
-    assert (err <= 1e-5 * scale + 1e-30).all(), f"forward: max rel err {rel.max():.3e} > 1e-5"
+    assert (err <= rtol * scale + carried + 1e-30).all(), f"forward: max rel err {rel.max():.3e} > {rtol}"
+    assert (err <= 1e-5 * scale + carried + 1e-30).all(), f"forward: max rel err {rel.max():.3e} > 1e-5"
     return float(rel.max())
 
 
@@ -155,25 +165,82 @@ def rows_of(spec, flat, linear_ids):
     return out
 
 
-def check_update(spec, before: dict, ref: dict, gpu: dict, st_ref=None, st_gpu=None, ids=None):
-    """Compare updated rows (dicts from rows_of) and, for Adagrad, state values at ids."""
-    worst = 0.0
-    for t, f in ref.items():
-        g, o = gpu[t], before[t]
+def spacing(spec, bits: np.ndarray) -> np.ndarray:
+    """Gap between the stored value and the next code away from zero (fp16 / bf16)."""
+    dt = code(spec)
+    mag = (bits & np.uint16(0x7FFF)).astype(np.int64)
+    lo = np.minimum(mag, 0x7BFE if spec.dtype == "f16" else 0x7F7E)
+    return oracle.widen(dt, (lo + 1).astype(np.uint16)) - oracle.widen(dt, lo.astype(np.uint16))
+
+
+def update_allowance(spec, before: dict, after: dict) -> dict:
+    """Per element: how far the GPU's new weights may be from the reference's after
+    one update of these rows from identical inputs."""
+    out = {}
+    for t, f in after.items():
+        o = before[t]
         if spec.dtype == "f32":
-            tol = 1e-5 * (np.abs(o) + np.abs(f - o).max(axis=1, keepdims=True))
-            err = np.abs(g - f)
-            ratio = float((err / (tol + 1e-38)).max())
-            assert (err <= tol).all(), f"table {t}: weight err {ratio:.3f} x tol"
-            worst = max(worst, ratio)
+            out[t] = 1e-5 * (np.abs(o).astype(np.float64) + np.abs(f.astype(np.float64) - o).max(axis=1, keepdims=True))
         else:
-            d = ulp_distance(g, f)
-            assert d.max() <= 1, f"table {t}: weights differ by {d.max()} ulp"
-            worst = max(worst, float(d.max()))
+            out[t] = spacing(spec, f).reshape(f.shape)
+    return out
+
+
+def check_update(spec, ids, before: dict, ref: dict, gpu: dict, dev_old: np.ndarray,
+                 st_ref=None, st_gpu=None, counts=None):
+    """|W_gpu - W_ref| <= (allowed deviation carried in from earlier steps) + (one update's
+    allowance); state within 1e-5 relative.  ids: sorted linear ids of the compared rows."""
+    _, roff, _ = layout(spec)
+    worst = 0.0
+    allow = update_allowance(spec, before, ref)
+    tab = np.searchsorted(roff, ids, side="right") - 1
+    for t, f in ref.items():
+        lin = ids[tab == t]
+        g = gpu[t]
+        if spec.dtype == "f32":
+            err = np.abs(g.astype(np.float64) - f)
+        else:
+            dt = code(spec)
+            err = np.abs(oracle.widen(dt, g.reshape(-1)) - oracle.widen(dt, f.reshape(-1))).reshape(g.shape)
+        lim = dev_old[lin][:, None] + allow[t]
+        ratio = err / (lim + 1e-38)
+        if not (err <= lim).all():
+            bad = np.argsort(ratio.max(axis=1))[-5:]
+            msg = [f"table {t}: weight error up to {ratio.max():.3f} x allowed"]
+            for i in bad:
+                c = "" if counts is None else f" hits={counts.get(int(lin[i]), '?')}"
+                msg.append(f"  row {lin[i]}{c}: err {err[i].max():.3e} allowed {lim[i].min():.3e} "
+                           f"|W_ref| {np.abs(f[i].astype(np.float64)).max():.3e}")
+            raise AssertionError("\n".join(msg))
+        worst = max(worst, float(ratio.max()))
     if st_ref is not None:
         m, mr = st_gpu[ids], st_ref[ids]
         assert (np.abs(m - mr) <= 1e-5 * mr + 1e-30).all(), "state mismatch"
     return worst
+
+
+def carry_deviation(spec, dev: np.ndarray, ids, before: dict, after: dict) -> None:
+    """dev[row] += largest allowance of one update over the row (in place)."""
+    _, roff, _ = layout(spec)
+    tab = np.searchsorted(roff, ids, side="right") - 1
+    for t, a in update_allowance(spec, before, after).items():
+        lin = ids[tab == t]
+        dev[lin] += a.max(axis=1)
+
+
+def forward_deviation(spec, batch, dev: np.ndarray) -> np.ndarray:
+    """Per bag: s_k * sum_i |p_i| dev[row_i], the effect of allowed weight deviations."""
+    _, roff, _ = layout(spec)
+    nb = spec.T * spec.B
+    lens = np.diff(batch.offsets)
+    bag = np.repeat(np.arange(nb), lens)
+    lin = roff[bag // spec.B] + batch.indices
+    v = dev[lin] * (1.0 if batch.psw is None else np.abs(batch.psw.astype(np.float64)))
+    out = np.zeros(nb)
+    np.add.at(out, bag, v)
+    if spec.pooling == "mean":
+        out = np.where(lens > 0, out / np.maximum(lens, 1), 0.0)
+    return out
 
 
 def run_step(pb: Problem, G: torch.Tensor, lr=None, eps=None, with_runs=True):

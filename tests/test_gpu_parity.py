@@ -13,7 +13,7 @@ import torch
 import oracle
 import table_embedding_bag_amd as tbe
 import workloads
-from gpu_check import (Problem, check_forward, check_runs, check_update, layout, make_problem,
+from gpu_check import (carry_deviation, check_forward, check_runs, check_update, make_problem,
                        reference_update, rows_of, run_step, to_device, untouched_identical)
 
 pytestmark = pytest.mark.gpu
@@ -35,6 +35,7 @@ def parity(spec, seed=0, steps=2, bag_sample=None, row_sample=None, index_dtype=
     W_host = workloads.storage_numpy(pb.W).copy()
     st_host = np.zeros(spec.sum_rows, np.float32) if pb.state is not None else None
     rng = np.random.default_rng(seed + 99)
+    dev = np.zeros(spec.sum_rows)   # allowed |W_gpu - W_ref| per row, carried across steps
     report = {}
     for step in range(steps):
         if step > 0:
@@ -48,10 +49,17 @@ def parity(spec, seed=0, steps=2, bag_sample=None, row_sample=None, index_dtype=
                 np.arange(spec.T) * spec.B, np.arange(1, spec.T + 1) * spec.B - 1]))
         Y = pb.op.forward(spec.B, pb.idx, pb.off, pb.psw)
         torch.cuda.synchronize()
-        report[f"fwd{step}"] = check_forward(pb, Y, W_host, sample)
+        report[f"fwd{step}"] = check_forward(pb, Y, W_host, sample, dev)
         _say(f"  step {step}: forward ok (max rel {report[f'fwd{step}']:.2e})")
 
         G = workloads.grad_output(spec, seed=seed, step=step, device="cuda")
+        # rows this step leaves alone, as the GPU holds them before the step
+        ref_uniq, _ = oracle.runs(spec.rows, spec.B, pb.batch.indices, pb.batch.offsets)
+        untouched = np.setdiff1d(np.arange(spec.sum_rows), ref_uniq, assume_unique=True)
+        if untouched.size > 20000:
+            untouched = np.sort(rng.choice(untouched, 20000, replace=False))
+        gpu_before = rows_of(spec, pb.W, untouched)
+        gpu_st_before = pb.state.cpu().numpy() if pb.state is not None else None
         runs = run_step(pb, G)
         uniq, cnt = check_runs(pb, runs)
         _say(f"  step {step}: runs ok (U={uniq.size}, max run {cnt.max() if cnt.size else 0})")
@@ -61,22 +69,36 @@ def parity(spec, seed=0, steps=2, bag_sample=None, row_sample=None, index_dtype=
                                             uniq[:5], uniq[-5:]]))
         else:
             sel = uniq
-        before = rows_of(spec, W_host, sel)
-        st_before = st_host.copy() if st_host is not None else None
+        before_all = rows_of(spec, W_host, uniq)
         reference_update(pb, W_host, st_host, G.cpu().numpy())
+        after_all = rows_of(spec, W_host, uniq)
         st_gpu = pb.state.cpu().numpy() if pb.state is not None else None
-        report[f"upd{step}"] = check_update(spec, before, rows_of(spec, W_host, sel),
-                                            rows_of(spec, pb.W, sel), st_host, st_gpu, sel)
-        # rows nobody looked up stay bit-identical
-        untouched = np.setdiff1d(np.arange(spec.sum_rows), uniq, assume_unique=True)
-        if untouched.size > 20000:
-            untouched = np.sort(rng.choice(untouched, 20000, replace=False))
+        counts = dict(zip(uniq.tolist(), cnt.tolist()))
+        before_sel = before_all if sel is uniq else _subset(spec, before_all, uniq, sel)
+        report[f"upd{step}"] = check_update(spec, sel, before_sel,
+                                            rows_of(spec, W_host, sel), rows_of(spec, pb.W, sel), dev,
+                                            st_host, st_gpu, counts)
+        carry_deviation(spec, dev, uniq, before_all, after_all)
+        # rows nobody looked up in this step stay bit-identical
         if untouched.size:
-            untouched_identical(spec, rows_of(spec, W_host, untouched), rows_of(spec, pb.W, untouched),
-                                st_before, st_gpu, untouched)
+            untouched_identical(spec, gpu_before, rows_of(spec, pb.W, untouched),
+                                gpu_st_before, st_gpu, untouched)
         _say(f"  step {step}: update ok (worst {report[f'upd{step}']:.3f})")
     pb.op.close()
     return report
+
+
+def _subset(spec, rows: dict, ids, sel):
+    """Rows of `sel` (a sorted subset of sorted `ids`) out of a rows_of(ids) dict."""
+    from gpu_check import layout
+    _, roff, _ = layout(spec)
+    tab_ids = np.searchsorted(roff, ids, side="right") - 1
+    out = {}
+    for t in np.unique(np.searchsorted(roff, sel, side="right") - 1):
+        mine = ids[tab_ids == t]
+        want = sel[(sel >= roff[t]) & (sel < roff[t + 1])]
+        out[int(t)] = rows[int(t)][np.searchsorted(mine, want)]
+    return out
 
 
 # --------------------------------------------------------------------------

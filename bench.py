@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Benchmark of the TBE hot path on one MI355X: forward gather-pool plus the fused
+backward (linearize, radix sort, run-length encode, segment reduce, one row-wise
+Adagrad / SGD update per touched row), through the library's C ABI.
+
+A step is one forward and one backward_update over one batch of the workload.
+Four seeded batches (and upstream gradients) are generated up front, resident
+in HBM, and used in rotation.  Default workload: T=8 tables of 100,000 x 128
+fp32 rows, B=2048 bags per table, bag length uniform in 1..32, Zipf(1.05) row
+ids, sum pooling, row-wise Adagrad.
+
+Prints one JSON line:
+  value        fwd+bwd lookups per second (lookups of the K timed steps / time)
+  roofline     the dominant kernel: algorithmic bytes per launch / its average
+               duration (HIP events on the library's stream, second pass of the
+               same K steps), against the 8 TB/s HBM peak; traffic from the
+               committed rocprofv3 counter summary when it matches the current
+               kernel source, else null
+  cpu_baseline the CPU reference (fp64, OpenMP) timed on a bounded sample of
+               the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "TBE fwd+bwd lookups/sec and achieved HBM GB/s (% of peak) at 1 MI355X"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", type=int, default=2, help="benchmark workload 1..5")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU baseline")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="only run a plain device copy of known size (counter calibration)")
+    return p.parse_args()
+
+
+def copy_probe():
+    import torch
+    n = 1 << 28  # 1 GiB of fp32
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n,
+                      "launches": 5}))
+
+
+def row_stats(spec, batch):
+    """Runs of equal (table, row) ids: their lengths, from the batch itself."""
+    import numpy as np
+    roff = np.concatenate([[0], np.cumsum(spec.rows)])
+    bag = np.repeat(np.arange(spec.T * spec.B), np.diff(batch.offsets))
+    lin = roff[bag // spec.B] + batch.indices
+    uniq, cnt = np.unique(lin, return_counts=True)
+    tab = np.searchsorted(roff, uniq, side="right") - 1
+    return uniq, cnt, tab
+
+
+def algorithmic_bytes(spec, batch, long_threshold=256, chunk=256):
+    """Bytes the method itself must move, per kernel (one launch each), for one batch.
+
+    forward (per lookup)   row read D*s + id 8 (+ weight 4); (per bag) offset 8 + output 4*D
+    seg_short (per lookup) sorted value 4 + gradient row 4*D (+ record 8 with weights / mean)
+              (per row)    id + start 8 + row read and write 2*D*s (+ state read and write 8)
+    seg_partial            the same per lookup for long runs, + partial write 4*D per chunk
+    seg_finalize           partial reads 4*D per chunk + the per-row terms of long runs
+    """
+    import numpy as np
+    s = {"f32": 4, "f16": 2, "bf16": 2}[spec.dtype]
+    dims = np.array(spec.dims, np.int64)
+    lens = np.diff(batch.offsets)
+    bag_t = np.repeat(np.arange(spec.T), spec.B)
+    look_D = np.repeat(dims[bag_t], lens)
+    psw = 4 if spec.psw else 0
+    fwd = float((look_D * s + 8 + psw).sum() + (8 + 4 * dims[bag_t]).sum())
+    _, cnt, tab = row_stats(spec, batch)
+    D = dims[tab]
+    rec = 8 if (spec.psw or spec.pooling == "mean") else 0
+    state = 8 if spec.optimizer == "rowwise_adagrad" else 0
+    short = cnt < long_threshold
+    per_row = 8 + 2 * D * s + state
+    seg_short = float((cnt[short] * (4 + 4 * D[short] + rec) + per_row[short]).sum())
+    nch = -(-cnt[~short] // chunk)
+    seg_partial = float((cnt[~short] * (4 + 4 * D[~short] + rec) + nch * 4 * D[~short]).sum())
+    seg_final = float((nch * 4 * D[~short] + per_row[~short]).sum())
+    N, U, nbags = int(lens.sum()), int(cnt.size), spec.T * spec.B
+    # grouping front: linearize (ids 8 + offsets, key/value writes 8, record 8),
+    # per radix pass: digit counts read 4, scatter reads and writes key+value 16;
+    # run-length encoding: heads read 4, then keys read 4 + unique id/start writes 8 per run
+    front = {"linearize_kernel": float(N * (8 + 8 + rec) + 8 * nbags),
+             "radix_upsweep": float(4 * N), "radix_downsweep": float(16 * N),
+             "rle_count": float(4 * N), "rle_write": float(4 * N + 8 * U)}
+    return {"fwd_gather_pool": fwd, "seg_short": seg_short, "seg_partial": seg_partial,
+            "seg_finalize": seg_final, **front}, {"N": int(lens.sum()), "U": int(cnt.size),
+                                         "long_run_share": float(cnt[~short].sum() / max(1, cnt.sum())),
+                                         "max_run": int(cnt.max()) if cnt.size else 0}
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "table_embedding_bag_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel, workload_tag):
+    """HBM bytes per launch from profiles/<kernel>_<workload>_counters.txt, if it was
+    taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload_tag}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(spec, batch, W_host, grad_host, budget_s):
+    """The CPU reference as it stands (fp64, OpenMP over bags and rows): forward +
+    backward_update on the full first batch, repeated while within the budget."""
+    import numpy as np
+    import oracle
+    import workloads
+    dt = workloads.oracle_dtype(spec.dtype)
+    pool = oracle.POOL_MEAN if spec.pooling == "mean" else oracle.POOL_SUM
+    opt = oracle.OPT_ROWWISE_ADAGRAD if spec.optimizer == "rowwise_adagrad" else oracle.OPT_SGD
+    W = W_host.copy()
+    st = np.zeros(spec.sum_rows, np.float32)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(spec.rows, spec.dims, dt, pool, W, spec.B, batch.indices, batch.offsets,
+                       batch.psw)
+        oracle.backward_update(spec.rows, spec.dims, dt, pool, opt, W, st, spec.B, batch.indices,
+                               batch.offsets, batch.psw, grad_host, float(np.float32(spec.lr)),
+                               float(np.float32(spec.eps)))
+        reps += 1
+        el = time.perf_counter() - t0
+        if el > budget_s or reps >= 20:
+            break
+    return {"value": reps * batch.N / el, "unit": "lookups/s", "cores": oracle.get_threads(),
+            "kind": "oracle",
+            "sample": f"{reps} x one full batch ({batch.N} lookups): forward + backward_update, "
+                      f"fp64, {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
+
+    import numpy as np
+    import torch
+
+    import table_embedding_bag_amd as tbe
+    import workloads
+
+    torch.cuda.set_device(0)
+    spec = workloads.config(args.workload)
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    W = workloads.weights(spec, seed=0, device=dev)
+    W_host = workloads.storage_numpy(W).copy() if not args.no_cpu_baseline else None
+    state = torch.zeros(spec.sum_rows, dtype=torch.float32, device=dev) \
+        if spec.optimizer == "rowwise_adagrad" else None
+    op = tbe.TBE(spec.rows, spec.dims, W, state, pooling=spec.pooling, optimizer=spec.optimizer)
+    nrot = 4
+    host_batches = [workloads.batch(spec, seed=0, step=s) for s in range(nrot)]
+    batches = []
+    for hb in host_batches:
+        idx = torch.from_numpy(hb.indices).to(dev)
+        off = torch.from_numpy(hb.offsets).to(dev)
+        psw = torch.from_numpy(hb.psw).to(dev) if hb.psw is not None else None
+        batches.append((idx, off, psw, hb.N))
+    grads = [workloads.grad_output(spec, seed=0, step=s, device=dev) for s in range(nrot)]
+    Y = torch.empty((spec.B, spec.sum_dims), dtype=torch.float32, device=dev)
+    ws = max((op.workspace(spec.B, n) for (_, _, _, n) in batches), key=lambda t: t.numel())
+    torch.cuda.synchronize()
+    print(f"[bench] workload {args.workload} ready in {time.perf_counter() - t_gen:.1f}s",
+          file=sys.stderr, flush=True)
+
+    def step(i):
+        idx, off, psw, n = batches[i % nrot]
+        tbe.tbe_forward(op.handle, spec.B, idx, off, psw, Y)
+        tbe.tbe_backward_update(op.handle, spec.B, idx, off, psw, grads[i % nrot], spec.lr,
+                                spec.eps, ws)
+        return n
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, nothing else on the stream
+    lookups = 0
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        lookups += step(args.warmup + i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    print(f"[bench] timed {args.steps} steps in {elapsed * 1e3:.2f} ms", file=sys.stderr, flush=True)
+
+    # second pass over the same K steps with HIP events after every kernel
+    op.set_option(tbe.OPTION_PROFILE, 1)
+    tbe.tbe_stage_times(op.handle, capacity=1 << 16)  # drop anything earlier
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    stages = tbe.tbe_stage_times(op.handle, capacity=1 << 16)
+    op.set_option(tbe.OPTION_PROFILE, 0)
+    per_kernel = {}
+    for name, ms in stages:
+        tot, cnt = per_kernel.get(name, (0.0, 0))
+        per_kernel[name] = (tot + ms, cnt + 1)
+    avg_us = {k: 1e3 * t / c for k, (t, c) in per_kernel.items()}
+    steps_per_launch = {k: c / args.steps for k, (t, c) in per_kernel.items()}
+
+    # algorithmic bytes per launch (averaged over the rotated batches used)
+    alg = [algorithmic_bytes(spec, host_batches[(args.warmup + i) % nrot]) for i in range(nrot)]
+    alg_bytes = {k: float(np.mean([a[0][k] for a in alg])) for k in alg[0][0]}
+    stats = alg[0][1]
+    kernels = {}
+    for k, b in alg_bytes.items():
+        if k in avg_us:
+            kernels[k] = {"avg_us": round(avg_us[k], 2), "alg_bytes": b,
+                          "alg_GBps": round(b / (avg_us[k] * 1e-6) / 1e9, 1),
+                          "pct_of_peak": round(100 * b / (avg_us[k] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 1)}
+    dominant = max(avg_us, key=lambda k: avg_us[k] * steps_per_launch[k])
+    workload_tag = f"workload{args.workload}"
+    if dominant in alg_bytes:
+        achieved = alg_bytes[dominant] / (avg_us[dominant] * 1e-6) / 1e9
+        traffic = committed_traffic(dominant, workload_tag)
+        roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
+                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                    "traffic": traffic, "alg_bytes_per_launch": alg_bytes[dominant],
+                    "avg_launch_us": round(avg_us[dominant], 2)}
+    else:
+        roofline = {"bound": "hbm", "kernel": dominant, "achieved": None, "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": None, "traffic": None,
+                    "avg_launch_us": round(avg_us[dominant], 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU reference", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(spec, host_batches[0], W_host, grads[0].cpu().numpy(), args.cpu_seconds)
+
+    value = lookups / elapsed
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "lookups/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * elapsed / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "f16": "f16 storage, f32 accumulate",
+                  "bf16": "bf16 storage, f32 accumulate"}[spec.dtype],
+        "data": "synthetic (seeded generator, 4 rotated batches resident in HBM)",
+        "config": {"workload": spec.name, "tables": spec.T, "bags_per_table": spec.B,
+                   "lookups_per_step": stats["N"], "unique_rows_batch0": stats["U"],
+                   "long_run_share_batch0": round(stats["long_run_share"], 3),
+                   "max_run_batch0": stats["max_run"]},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "kernel_avg_us": {k: round(v, 2) for k, v in avg_us.items()},
+        "launches_per_step": {k: round(v, 2) for k, v in steps_per_launch.items()},
+        "profiled_ms_per_step": round(sum(ms for _, ms in stages) / args.steps, 4),
+    }
+    print(json.dumps(out))
+    op.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -203,7 +203,7 @@ def tbe_set_option(handle, option: int, value: int) -> None:
     _check(load().tbe_set_option(handle, option, int(value)), "tbe_set_option")
 
 
-def tbe_stage_times(handle, capacity: int = 64):
+def tbe_stage_times(handle, capacity: int = 1 << 16):
     """[(stage name, milliseconds)] of the last call (profiling option must be on)."""
     ms = (ctypes.c_float * capacity)()
     names = (ctypes.c_char_p * capacity)()

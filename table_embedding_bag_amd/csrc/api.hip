@@ -34,11 +34,11 @@ struct tbe_handle {
   TableMeta* meta = nullptr;     // device copy
   uint32_t* flag = nullptr;      // device word for the validation kernel
   int64_t long_threshold = 256;
-  // profiling
+  // profiling: events recorded at call starts (name == nullptr) and after
+  // each kernel (name of that kernel), kept until tbe_stage_times reads them.
   bool profile = false;
-  std::vector<hipEvent_t> events;
-  std::vector<const char*> stage_names;
-  int nrecorded = 0;
+  std::vector<hipEvent_t> pool;
+  std::vector<std::pair<hipEvent_t, const char*>> marks;
 };
 
 namespace {
@@ -63,16 +63,20 @@ tbe_status from_hip(hipError_t e) { return e == hipSuccess ? TBE_OK : TBE_ERR_HI
 
 // --- profiling -------------------------------------------------------------
 
-void prof_begin(tbe_handle* h, hipStream_t s) {
-  if (!h->profile) return;
-  h->nrecorded = 0;
-  h->stage_names.clear();
-  if (h->events.empty()) {
-    h->events.resize(64);
-    for (auto& e : h->events) (void)hipEventCreate(&e);
+constexpr size_t kMaxMarks = size_t{1} << 16;
+
+void prof_record(tbe_handle* h, hipStream_t s, const char* name) {
+  if (!h->profile || h->marks.size() >= kMaxMarks) return;
+  if (h->pool.size() <= h->marks.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return;
+    h->pool.push_back(e);
   }
-  (void)hipEventRecord(h->events[h->nrecorded++], s);
+  hipEvent_t e = h->pool[h->marks.size()];
+  if (hipEventRecord(e, s) == hipSuccess) h->marks.emplace_back(e, name);
 }
+
+void prof_begin(tbe_handle* h, hipStream_t s) { prof_record(h, s, nullptr); }
 
 struct HookCtx {
   tbe_handle* h;
@@ -81,10 +85,7 @@ struct HookCtx {
 
 void prof_mark(void* ctx, const char* name) {
   auto* c = static_cast<HookCtx*>(ctx);
-  tbe_handle* h = c->h;
-  if (!h->profile || h->nrecorded >= static_cast<int>(h->events.size())) return;
-  (void)hipEventRecord(h->events[h->nrecorded++], c->s);
-  h->stage_names.push_back(name);
+  prof_record(c->h, c->s, name);
 }
 
 // --- validation kernel -----------------------------------------------------
@@ -170,7 +171,7 @@ struct Carve {
 struct BwdPlan {
   int64_t n = 0;
   int sort_tiles = 0, rle_tiles = 0;
-  int64_t long_ub = 0, items1_ub = 0, items2_ub = 0;
+  int64_t long_ub = 0, chunks_ub = 0, items1_ub = 0, items2_ub = 0;
   int32_t pstride = 0;
   int32_t nch = 1, gshift = 0;
   bool vec = false;
@@ -201,10 +202,11 @@ bool plan_backward(const tbe_handle* h, int64_t n, bool vec, BwdPlan* p) {
   p->pstride = static_cast<int32_t>((h->dmax + 3) / 4 * 4);
   p->sort_tiles = static_cast<int>((n + kSortTile - 1) / kSortTile);
   p->rle_tiles = static_cast<int>((n + kRleTile - 1) / kRleTile);
-  const int64_t thr = std::max<int64_t>(1, h->long_threshold);
-  p->long_ub = n / thr + 1;
-  p->items1_ub = n / kChunk + p->long_ub;
-  p->items2_ub = p->items1_ub / kSuperChunk + p->long_ub;
+  const SegmentBounds ub = segment_bounds(n, h->long_threshold, kChunk, kSuperChunk, p->gshift);
+  p->long_ub = ub.longs;
+  p->chunks_ub = ub.chunks;
+  p->items1_ub = ub.items1;
+  p->items2_ub = ub.items2;
   Carve cv;
   for (int i = 0; i < 2; ++i) {
     p->o_keys[i] = cv.take(4 * static_cast<size_t>(n));
@@ -216,11 +218,11 @@ bool plan_backward(const tbe_handle* h, int64_t n, bool vec, BwdPlan* p) {
   p->o_rle = cv.take(4 * static_cast<size_t>(std::max(1, p->rle_tiles)));
   p->o_uniq = cv.take(4 * static_cast<size_t>(n));
   p->o_start = cv.take(4 * static_cast<size_t>(n + 1));
-  p->o_cnt = cv.take(16);
+  p->o_cnt = cv.take(4 * kNumCounters);
   p->o_longs = cv.take(16 * static_cast<size_t>(p->long_ub));
   p->o_items1 = cv.take(8 * static_cast<size_t>(p->items1_ub));
   p->o_items2 = cv.take(8 * static_cast<size_t>(p->items2_ub));
-  p->o_p1 = cv.take(4 * static_cast<size_t>(p->pstride) * p->items1_ub);
+  p->o_p1 = cv.take(4 * static_cast<size_t>(p->pstride) * p->chunks_ub);
   p->o_p2 = cv.take(4 * static_cast<size_t>(p->pstride) * p->items2_ub);
   p->bytes = cv.off;
   return true;
@@ -339,7 +341,7 @@ tbe_status tbe_create(const tbe_config* cfg, void* weights, float* optim_state, 
 
 void tbe_destroy(tbe_handle* h) {
   if (!h) return;
-  for (auto& e : h->events) (void)hipEventDestroy(e);
+  for (auto& e : h->pool) (void)hipEventDestroy(e);
   if (h->meta) (void)hipFree(h->meta);
   delete h;
 }
@@ -362,15 +364,19 @@ tbe_status tbe_stage_times(tbe_handle* h, float* ms, const char** names, int32_t
                            int32_t* count) {
   if (!h || !count || (capacity > 0 && !ms)) return TBE_ERR_INVALID_ARGUMENT;
   *count = 0;
-  if (!h->profile || h->nrecorded < 2) return TBE_OK;
-  if (hipEventSynchronize(h->events[h->nrecorded - 1]) != hipSuccess) return TBE_ERR_HIP;
-  const int n = std::min<int>(capacity, h->nrecorded - 1);
-  for (int i = 0; i < n; ++i) {
+  if (h->marks.empty()) return TBE_OK;
+  if (hipEventSynchronize(h->marks.back().first) != hipSuccess) return TBE_ERR_HIP;
+  int n = 0;
+  for (size_t i = 1; i < h->marks.size() && n < capacity; ++i) {
+    if (!h->marks[i].second) continue;  // start of the next call
     float t = 0.0f;
-    if (hipEventElapsedTime(&t, h->events[i], h->events[i + 1]) != hipSuccess) return TBE_ERR_HIP;
-    ms[i] = t;
-    if (names) names[i] = h->stage_names[i];
+    if (hipEventElapsedTime(&t, h->marks[i - 1].first, h->marks[i].first) != hipSuccess)
+      return TBE_ERR_HIP;
+    ms[n] = t;
+    if (names) names[n] = h->marks[i].second;
+    ++n;
   }
+  h->marks.clear();
   *count = n;
   return TBE_OK;
 }
@@ -421,7 +427,7 @@ tbe_status tbe_forward(tbe_handle* h, int32_t B, const void* indices, const void
     a.vec = h->fwd_vec;
     if (tiles * h->T > 0x7FFFFFFF) return TBE_ERR_UNSUPPORTED;
     const hipError_t e = launch_forward_gather(a, s);
-    prof_mark(&hc, "forward_gather");
+    prof_mark(&hc, "fwd_gather_pool");
     return from_hip(e);
   } catch (...) {
     return TBE_ERR_OUT_OF_MEMORY;
@@ -522,13 +528,12 @@ tbe_status tbe_backward_update(tbe_handle* h, int32_t B, const void* indices, co
 
     hipError_t e = launch_linearize(a, s);
     if (e != hipSuccess) return TBE_ERR_HIP;
-    prof_mark(&hc, "linearize");
+    prof_mark(&hc, "linearize_kernel");
     int sorted = 0;
     e = launch_radix_sort(a, s, &sorted, h->profile ? prof_mark : nullptr, &hc);
     if (e != hipSuccess) return TBE_ERR_HIP;
-    e = launch_run_length_encode(a, b.keys[sorted], s);
+    e = launch_run_length_encode(a, b.keys[sorted], s, h->profile ? prof_mark : nullptr, &hc);
     if (e != hipSuccess) return TBE_ERR_HIP;
-    prof_mark(&hc, "run_length_encode");
     e = launch_segment_reduce_update(a, b.vals[sorted], s, h->profile ? prof_mark : nullptr, &hc);
     return from_hip(e);
   } catch (...) {

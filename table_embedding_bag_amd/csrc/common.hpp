@@ -199,15 +199,24 @@ struct BackwardBuffers {
   uint32_t* rle_tiles;      // [rle_tiles]
   uint32_t* unique_keys;    // [N]
   uint32_t* run_start;      // [N + 1]
-  uint32_t* counters;       // [4]: U, long runs, level-1 items, level-2 items
-  uint2* items1;            // {long run, chunk}
+  uint32_t* counters;       // [kNumCounters]
+  uint2* items1;            // workgroup items: {run, medium flag} or {long run, chunk}
   uint2* items2;            // {long run, super-chunk}
-  uint4* longs;             // {run, item1 base, item1 count, item2 base}
-  float* partial1;          // [items1 cap, pstride]
+  uint4* longs;             // {run, first chunk partial, chunk count, first level-2 partial}
+  float* partial1;          // [chunks cap, pstride]
   float* partial2;          // [items2 cap, pstride]
 };
 
-enum { kCntUnique = 0, kCntLong = 1, kCntItems1 = 2, kCntItems2 = 3 };
+// Device counters of the backward, zeroed by the linearize kernel.
+enum { kCntUnique = 0, kCntLong = 1, kCntItems1 = 2, kCntItems2 = 3, kCntChunks = 4,
+       kNumCounters = 8 };
+
+// Upper bounds of the segment work lists for a batch of n lookups.
+struct SegmentBounds {
+  int64_t longs, chunks, items1, items2;
+};
+SegmentBounds segment_bounds(int64_t n, int64_t long_threshold, int chunk, int super_chunk,
+                             int gshift);
 
 struct BackwardLaunch {
   const void* indices;
@@ -246,7 +255,7 @@ hipError_t launch_linearize(const BackwardLaunch& a, hipStream_t stream);
 hipError_t launch_radix_sort(const BackwardLaunch& a, hipStream_t stream, int* result_buffer,
                              StageHook hook, void* ctx);
 hipError_t launch_run_length_encode(const BackwardLaunch& a, const uint32_t* sorted_keys,
-                                    hipStream_t stream);
+                                    hipStream_t stream, StageHook hook, void* ctx);
 hipError_t launch_segment_reduce_update(const BackwardLaunch& a, const uint32_t* sorted_vals,
                                         hipStream_t stream, StageHook hook, void* ctx);
 

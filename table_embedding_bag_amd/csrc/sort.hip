@@ -39,7 +39,7 @@ __global__ __launch_bounds__(kBlock) void linearize_kernel(BackwardLaunch a) {
   __shared__ float s_scale[kBlock];
 
   const int tid = threadIdx.x;
-  if (blockIdx.x == 0 && tid < 4) a.buf.counters[tid] = 0u;
+  if (blockIdx.x == 0 && tid < kNumCounters) a.buf.counters[tid] = 0u;
 
   const int64_t k0 = static_cast<int64_t>(blockIdx.x) * kBlock;
   const int nb = static_cast<int>(min(static_cast<int64_t>(kBlock), a.num_bags - k0));
@@ -296,30 +296,35 @@ hipError_t launch_radix_sort(const BackwardLaunch& a, hipStream_t stream, int* r
   for (int shift = 0; shift < a.key_bits; shift += kRadixBits) {
     hipLaunchKernelGGL(radix_upsweep, dim3(ntiles), dim3(kBlock), 0, stream, a.buf.keys[cur], n,
                        shift, a.buf.hist, ntiles);
+    if (hook) hook(ctx, "radix_upsweep");
     hipLaunchKernelGGL(radix_scan, dim3(kRadix), dim3(kBlock), 0, stream, a.buf.hist, ntiles,
                        a.buf.digit_totals);
+    if (hook) hook(ctx, "radix_scan");
     hipLaunchKernelGGL(radix_downsweep, dim3(ntiles), dim3(kBlock), 0, stream, a.buf.keys[cur],
                        a.buf.vals[cur], a.buf.keys[cur ^ 1], a.buf.vals[cur ^ 1], n, shift,
                        a.buf.hist, a.buf.digit_totals, ntiles);
+    if (hook) hook(ctx, "radix_downsweep");
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     cur ^= 1;
-    if (hook) hook(ctx, "sort_pass");
   }
   *result_buffer = cur;
   return hipSuccess;
 }
 
 hipError_t launch_run_length_encode(const BackwardLaunch& a, const uint32_t* sorted_keys,
-                                    hipStream_t stream) {
+                                    hipStream_t stream, StageHook hook, void* ctx) {
   const int64_t n = a.num_indices;
   const int ntiles = static_cast<int>((n + kRleTile - 1) / kRleTile);
   hipLaunchKernelGGL(rle_count, dim3(ntiles), dim3(kBlock), 0, stream, sorted_keys, n,
                      a.buf.rle_tiles);
+  if (hook) hook(ctx, "rle_count");
   hipLaunchKernelGGL(rle_scan, dim3(1), dim3(kBlock), 0, stream, a.buf.rle_tiles, ntiles,
                      a.buf.counters, a.buf.run_start, n);
+  if (hook) hook(ctx, "rle_scan");
   hipLaunchKernelGGL(rle_write, dim3(ntiles), dim3(kBlock), 0, stream, sorted_keys, n,
                      a.buf.rle_tiles, a.buf.unique_keys, a.buf.run_start);
+  if (hook) hook(ctx, "rle_write");
   return hipGetLastError();
 }
 

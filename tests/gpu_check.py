@@ -173,16 +173,30 @@ def spacing(spec, bits: np.ndarray) -> np.ndarray:
     return oracle.widen(dt, (lo + 1).astype(np.uint16)) - oracle.widen(dt, lo.astype(np.uint16))
 
 
+def values(spec, rows: np.ndarray) -> np.ndarray:
+    """Stored rows as float64 values."""
+    if spec.dtype == "f32":
+        return rows.astype(np.float64)
+    return oracle.widen(code(spec), rows.reshape(-1)).reshape(rows.shape)
+
+
 def update_allowance(spec, before: dict, after: dict) -> dict:
     """Per element: how far the GPU's new weights may be from the reference's after
-    one update of these rows from identical inputs."""
+    one update of these rows from identical inputs.
+
+    The update is computed in fp32 on the GPU and in fp64 by the reference, so
+    both differ by fp32-level rounding of W_old - step * Gamma, bounded by
+    1e-5 * (|W_old| + max over the row of |W_new - W_old|); fp16 / bf16 storage
+    adds one rounding to the storage grid (one unit in the last place at the
+    reference value).  Where the new value nearly cancels, the storage grid is
+    much finer than the fp32-level term, so a 'one ulp' bound alone is wrong."""
     out = {}
     for t, f in after.items():
-        o = before[t]
-        if spec.dtype == "f32":
-            out[t] = 1e-5 * (np.abs(o).astype(np.float64) + np.abs(f.astype(np.float64) - o).max(axis=1, keepdims=True))
-        else:
-            out[t] = spacing(spec, f).reshape(f.shape)
+        o, fv = values(spec, before[t]), values(spec, f)
+        a = 1e-5 * (np.abs(o) + np.abs(fv - o).max(axis=1, keepdims=True))
+        if spec.dtype != "f32":
+            a = a + spacing(spec, f).reshape(f.shape)
+        out[t] = a
     return out
 
 
@@ -197,20 +211,18 @@ def check_update(spec, ids, before: dict, ref: dict, gpu: dict, dev_old: np.ndar
     for t, f in ref.items():
         lin = ids[tab == t]
         g = gpu[t]
-        if spec.dtype == "f32":
-            err = np.abs(g.astype(np.float64) - f)
-        else:
-            dt = code(spec)
-            err = np.abs(oracle.widen(dt, g.reshape(-1)) - oracle.widen(dt, f.reshape(-1))).reshape(g.shape)
+        fv, gv = values(spec, f), values(spec, g)
+        err = np.abs(gv - fv)
         lim = dev_old[lin][:, None] + allow[t]
         ratio = err / (lim + 1e-38)
         if not (err <= lim).all():
-            bad = np.argsort(ratio.max(axis=1))[-5:]
+            worst_rows = np.argsort(ratio.max(axis=1))[-5:]
             msg = [f"table {t}: weight error up to {ratio.max():.3f} x allowed"]
-            for i in bad:
+            for i in worst_rows:
+                d = int(np.argmax(ratio[i]))
                 c = "" if counts is None else f" hits={counts.get(int(lin[i]), '?')}"
-                msg.append(f"  row {lin[i]}{c}: err {err[i].max():.3e} allowed {lim[i].min():.3e} "
-                           f"|W_ref| {np.abs(f[i].astype(np.float64)).max():.3e}")
+                msg.append(f"  row {lin[i]}{c} col {d}: gpu {gv[i, d]:.6e} ref {fv[i, d]:.6e} "
+                           f"err {err[i, d]:.3e} allowed {lim[i, d]:.3e}")
             raise AssertionError("\n".join(msg))
         worst = max(worst, float(ratio.max()))
     if st_ref is not None:

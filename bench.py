@@ -71,14 +71,24 @@ def row_stats(spec, batch):
     return uniq, cnt, tab
 
 
-def algorithmic_bytes(spec, batch, long_threshold=256, chunk=256):
+def group_lanes(spec):
+    """Lanes per gradient row in the segment kernels (longest run a lane group takes alone)."""
+    ve = 4 if all(d % 4 == 0 for d in spec.dims) else 1
+    c = -(-max(spec.dims) // ve)
+    return min(64, 1 << (c - 1).bit_length())
+
+
+def algorithmic_bytes(spec, batch, long_threshold=256, chunk=256, super_chunk=32):
     """Bytes the method itself must move, per kernel (one launch each), for one batch.
 
-    forward (per lookup)   row read D*s + id 8 (+ weight 4); (per bag) offset 8 + output 4*D
-    seg_short (per lookup) sorted value 4 + gradient row 4*D (+ record 8 with weights / mean)
-              (per row)    id + start 8 + row read and write 2*D*s (+ state read and write 8)
-    seg_partial            the same per lookup for long runs, + partial write 4*D per chunk
-    seg_finalize           partial reads 4*D per chunk + the per-row terms of long runs
+    forward (per lookup)  row read D*s + id 8 (+ weight 4); (per bag) offset 8 + output 4*D
+    segment (per lookup)  sorted value 4 + gradient row 4*D (+ record 8 with weights / mean)
+            (per row)     id + run bounds 12 + row read and write 2*D*s (+ state read/write 8)
+      seg_short           runs a lane group takes alone (at most Gs lookups)
+      seg_wg              longer runs below the long-run threshold, and the lookups of long
+                          runs (+ one 4*D partial write per 256-lookup chunk)
+      seg_reduce2         32 partial reads + 1 write per level-2 partial (runs of > 32 chunks)
+      seg_finalize        partial reads + the per-row terms of long runs
     """
     import numpy as np
     s = {"f32": 4, "f16": 2, "bf16": 2}[spec.dtype]
@@ -92,12 +102,19 @@ def algorithmic_bytes(spec, batch, long_threshold=256, chunk=256):
     D = dims[tab]
     rec = 8 if (spec.psw or spec.pooling == "mean") else 0
     state = 8 if spec.optimizer == "rowwise_adagrad" else 0
-    short = cnt < long_threshold
-    per_row = 8 + 2 * D * s + state
-    seg_short = float((cnt[short] * (4 + 4 * D[short] + rec) + per_row[short]).sum())
-    nch = -(-cnt[~short] // chunk)
-    seg_partial = float((cnt[~short] * (4 + 4 * D[~short] + rec) + nch * 4 * D[~short]).sum())
-    seg_final = float((nch * 4 * D[~short] + per_row[~short]).sum())
+    gs = group_lanes(spec)
+    per_look = 4 + 4 * D + rec
+    per_row = 12 + 2 * D * s + state
+    short = cnt <= gs
+    long_ = cnt >= long_threshold
+    medium = ~short & ~long_
+    nch = -(-cnt // chunk)
+    n2 = np.where(nch > super_chunk, -(-nch // super_chunk), 0)
+    seg_short = float((cnt[short] * per_look[short] + per_row[short]).sum())
+    seg_wg = float((cnt[medium] * per_look[medium] + per_row[medium]).sum()
+                   + (cnt[long_] * per_look[long_] + nch[long_] * 4 * D[long_]).sum())
+    seg_r2 = float((nch[long_ & (n2 > 0)] * 4 * D[long_ & (n2 > 0)] + n2[long_] * 4 * D[long_]).sum())
+    seg_final = float((np.where(n2 > 0, n2, nch)[long_] * 4 * D[long_] + per_row[long_]).sum())
     N, U, nbags = int(lens.sum()), int(cnt.size), spec.T * spec.B
     # grouping front: linearize (ids 8 + offsets, key/value writes 8, record 8),
     # per radix pass: digit counts read 4, scatter reads and writes key+value 16;
@@ -105,9 +122,9 @@ def algorithmic_bytes(spec, batch, long_threshold=256, chunk=256):
     front = {"linearize_kernel": float(N * (8 + 8 + rec) + 8 * nbags),
              "radix_upsweep": float(4 * N), "radix_downsweep": float(16 * N),
              "rle_count": float(4 * N), "rle_write": float(4 * N + 8 * U)}
-    return {"fwd_gather_pool": fwd, "seg_short": seg_short, "seg_partial": seg_partial,
-            "seg_finalize": seg_final, **front}, {"N": int(lens.sum()), "U": int(cnt.size),
-                                         "long_run_share": float(cnt[~short].sum() / max(1, cnt.sum())),
+    return {"fwd_gather_pool": fwd, "seg_short": seg_short, "seg_wg": seg_wg,
+            "seg_reduce2": seg_r2, "seg_finalize": seg_final, **front}, {"N": int(lens.sum()), "U": int(cnt.size),
+                                         "long_run_share": float(cnt[long_].sum() / max(1, cnt.sum())),
                                          "max_run": int(cnt.max()) if cnt.size else 0}
 
 
@@ -252,6 +269,13 @@ def main():
             kernels[k] = {"avg_us": round(avg_us[k], 2), "alg_bytes": b,
                           "alg_GBps": round(b / (avg_us[k] * 1e-6) / 1e9, 1),
                           "pct_of_peak": round(100 * b / (avg_us[k] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 1)}
+    # the whole segment reduce + update (all of its kernels, one launch each per step)
+    seg_names = [k for k in ("seg_short", "seg_wg", "seg_reduce2", "seg_finalize") if k in avg_us]
+    if seg_names:
+        sb, su = sum(alg_bytes[k] for k in seg_names), sum(avg_us[k] for k in seg_names)
+        kernels["segment_reduce_update"] = {
+            "avg_us": round(su, 2), "alg_bytes": sb, "alg_GBps": round(sb / (su * 1e-6) / 1e9, 1),
+            "pct_of_peak": round(100 * sb / (su * 1e-6) / 1e9 / HBM_PEAK_GBPS, 1)}
     dominant = max(avg_us, key=lambda k: avg_us[k] * steps_per_launch[k])
     workload_tag = f"workload{args.workload}"
     if dominant in alg_bytes:

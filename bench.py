@@ -113,7 +113,8 @@ def algorithmic_bytes(spec, batch, long_threshold=256, chunk=256, super_chunk=32
     seg_short = float((cnt[short] * per_look[short] + per_row[short]).sum())
     seg_wg = float((cnt[medium] * per_look[medium] + per_row[medium]).sum()
                    + (cnt[long_] * per_look[long_] + nch[long_] * 4 * D[long_]).sum())
-    seg_r2 = float((nch[long_ & (n2 > 0)] * 4 * D[long_ & (n2 > 0)] + n2[long_] * 4 * D[long_]).sum())
+    two = long_ & (n2 > 0)
+    seg_r2 = float(((nch[two] + n2[two]) * 4 * D[two]).sum())
     seg_final = float((np.where(n2 > 0, n2, nch)[long_] * 4 * D[long_] + per_row[long_]).sum())
     N, U, nbags = int(lens.sum()), int(cnt.size), spec.T * spec.B
     # grouping front: linearize (ids 8 + offsets, key/value writes 8, record 8),

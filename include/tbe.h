@@ -34,7 +34,7 @@
  *             row, indexed by the linear row id roff_t + row
  *             (roff_t = sum_{t'<t} rows[t']).  Must start at 0.
  *   bags      table-major: bag k = t*B + b, B bags per table.
- *   indices   [num_indices] table-local row ids (int32 or int64).
+ *   indices   [num_indices] table-local row ids (int32 or int64); num_indices < 2^30.
  *   offsets   [T*B + 1], same integer type as indices; bag k holds
  *             indices[offsets[k] .. offsets[k+1]); offsets[0] = 0 and
  *             offsets[T*B] = num_indices.

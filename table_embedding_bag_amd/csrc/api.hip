@@ -152,7 +152,8 @@ tbe_status check_batch_args(const tbe_handle* h, int32_t B, const void* indices,
   if (index_dtype != TBE_I32 && index_dtype != TBE_I64) return TBE_ERR_INVALID_ARGUMENT;
   if (B > 0 && !offsets) return TBE_ERR_INVALID_ARGUMENT;
   if (n > 0 && !indices) return TBE_ERR_INVALID_ARGUMENT;
-  if (n > 0x7FFFFFFF - 1) return TBE_ERR_UNSUPPORTED;  // lookup ids are 32-bit on the device
+  // lookup ids and the sort's chained counts are 30-bit on the device
+  if (n >= (int64_t{1} << 30)) return TBE_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(h->T) * B >= 0x7FFFFFFF) return TBE_ERR_UNSUPPORTED;
   return TBE_OK;
 }
@@ -175,8 +176,10 @@ struct BwdPlan {
   int32_t pstride = 0;
   int32_t nch = 1, gshift = 0;
   bool vec = false;
-  size_t o_keys[2], o_vals[2], o_rec, o_hist, o_tot, o_rle, o_uniq, o_start, o_cnt, o_longs,
-      o_items1, o_items2, o_p1, o_p2;
+  int passes = 1;
+  int64_t zero_words = 0;
+  size_t o_keys[2], o_vals[2], o_rec, o_zero, o_uniq, o_start, o_longs, o_items1, o_items2, o_p1,
+      o_p2;
   size_t bytes = 0;
 };
 
@@ -200,8 +203,12 @@ bool plan_backward(const tbe_handle* h, int64_t n, bool vec, BwdPlan* p) {
     }
   }
   p->pstride = static_cast<int32_t>((h->dmax + 3) / 4 * 4);
-  p->sort_tiles = static_cast<int>((n + kSortTile - 1) / kSortTile);
+  const int64_t sort_tile = static_cast<int64_t>(kBlock) * sort_keys_per_thread(n);
+  p->sort_tiles = static_cast<int>((n + sort_tile - 1) / sort_tile);
   p->rle_tiles = static_cast<int>((n + kRleTile - 1) / kRleTile);
+  p->passes = (h->key_bits + kRadixBits - 1) / kRadixBits;
+  p->zero_words = kNumCounters + kNumTickets + int64_t{kMaxRadixPasses} * kRadix +
+                  int64_t{p->passes} * p->sort_tiles * kRadix + p->rle_tiles;
   const SegmentBounds ub = segment_bounds(n, h->long_threshold, kChunk, kSuperChunk, p->gshift);
   p->long_ub = ub.longs;
   p->chunks_ub = ub.chunks;
@@ -213,12 +220,9 @@ bool plan_backward(const tbe_handle* h, int64_t n, bool vec, BwdPlan* p) {
     p->o_vals[i] = cv.take(4 * static_cast<size_t>(n));
   }
   p->o_rec = cv.take(8 * static_cast<size_t>(n));
-  p->o_hist = cv.take(4 * static_cast<size_t>(kRadix) * std::max(1, p->sort_tiles));
-  p->o_tot = cv.take(4 * kRadix);
-  p->o_rle = cv.take(4 * static_cast<size_t>(std::max(1, p->rle_tiles)));
+  p->o_zero = cv.take(4 * static_cast<size_t>(p->zero_words));
   p->o_uniq = cv.take(4 * static_cast<size_t>(n));
   p->o_start = cv.take(4 * static_cast<size_t>(n + 1));
-  p->o_cnt = cv.take(4 * kNumCounters);
   p->o_longs = cv.take(16 * static_cast<size_t>(p->long_ub));
   p->o_items1 = cv.take(8 * static_cast<size_t>(p->items1_ub));
   p->o_items2 = cv.take(8 * static_cast<size_t>(p->items2_ub));
@@ -514,12 +518,14 @@ tbe_status tbe_backward_update(tbe_handle* h, int32_t B, const void* indices, co
       b.vals[i] = reinterpret_cast<uint32_t*>(w + p.o_vals[i]);
     }
     b.rec = reinterpret_cast<uint2*>(w + p.o_rec);
-    b.hist = reinterpret_cast<uint32_t*>(w + p.o_hist);
-    b.digit_totals = reinterpret_cast<uint32_t*>(w + p.o_tot);
-    b.rle_tiles = reinterpret_cast<uint32_t*>(w + p.o_rle);
+    b.counters = reinterpret_cast<uint32_t*>(w + p.o_zero);
+    b.tickets = b.counters + kNumCounters;
+    b.digit_hist = b.tickets + kNumTickets;
+    b.sort_status = b.digit_hist + kMaxRadixPasses * kRadix;
+    b.rle_status = b.sort_status + static_cast<int64_t>(p.passes) * p.sort_tiles * kRadix;
+    b.zero_words = p.zero_words;
     b.unique_keys = reinterpret_cast<uint32_t*>(w + p.o_uniq);
     b.run_start = reinterpret_cast<uint32_t*>(w + p.o_start);
-    b.counters = reinterpret_cast<uint32_t*>(w + p.o_cnt);
     b.longs = reinterpret_cast<uint4*>(w + p.o_longs);
     b.items1 = reinterpret_cast<uint2*>(w + p.o_items1);
     b.items2 = reinterpret_cast<uint2*>(w + p.o_items2);

@@ -194,12 +194,17 @@ struct BackwardBuffers {
   uint32_t* keys[2];
   uint32_t* vals[2];
   uint2* rec;               // per lookup {bag, coefficient bits} when needed, else null
-  uint32_t* hist;           // [256 * sort_tiles]
-  uint32_t* digit_totals;   // [256]
-  uint32_t* rle_tiles;      // [rle_tiles]
+  // One contiguous region zeroed at the start of every backward call:
+  //   counters [kNumCounters], tickets [kNumTickets], digit_hist [kMaxRadixPasses][256],
+  //   sort_status [passes][sort tiles][256], rle_status [rle tiles]
+  uint32_t* counters;
+  uint32_t* tickets;        // tile tickets: one per radix pass, then the RLE's
+  uint32_t* digit_hist;     // digit counts of every radix pass
+  uint32_t* sort_status;    // look-back status words of the radix passes
+  uint32_t* rle_status;     // look-back status words of the RLE
+  int64_t zero_words;       // size of the zeroed region, in 32-bit words
   uint32_t* unique_keys;    // [N]
   uint32_t* run_start;      // [N + 1]
-  uint32_t* counters;       // [kNumCounters]
   uint2* items1;            // workgroup items: {run, medium flag} or {long run, chunk}
   uint2* items2;            // {long run, super-chunk}
   uint4* longs;             // {run, first chunk partial, chunk count, first level-2 partial}
@@ -207,9 +212,15 @@ struct BackwardBuffers {
   float* partial2;          // [items2 cap, pstride]
 };
 
-// Device counters of the backward, zeroed by the linearize kernel.
+// Device counters of the backward (zeroed at the start of every call).
+// kCntError is raised if a look-back wait ever gives up (results then invalid).
 enum { kCntUnique = 0, kCntLong = 1, kCntItems1 = 2, kCntItems2 = 3, kCntChunks = 4,
-       kNumCounters = 8 };
+       kCntError = 5, kNumCounters = 8 };
+constexpr int kMaxRadixPasses = 4;       // 32-bit keys, 8-bit digits
+constexpr int kNumTickets = 8;           // kMaxRadixPasses radix passes + the RLE
+
+// Keys per thread of a radix tile for a batch of n lookups (8 or 16).
+int sort_keys_per_thread(int64_t n);
 
 // Upper bounds of the segment work lists for a batch of n lookups.
 struct SegmentBounds {
@@ -267,8 +278,6 @@ constexpr int kFwdUnroll = 4;
 constexpr int kMaxDim = 1024;
 
 // Tile sizes shared by the planner (workspace sizing) and the kernels.
-constexpr int kSortKeysPerThread = 8;
-constexpr int kSortTile = kBlock * kSortKeysPerThread;   // 2048 keys
 constexpr int kRleTile = 4096;
 constexpr int kRadixBits = 8;
 constexpr int kRadix = 1 << kRadixBits;

@@ -191,20 +191,104 @@ __device__ __forceinline__ GroupIds group_ids(const BackwardLaunch& a) {
   return r;
 }
 
+// Table metadata staged in LDS (handles with at most kLdsTables tables), so
+// that a run's table follows from its row id without a dependent global load.
+constexpr int kLdsTables = 256;
+
+__device__ __forceinline__ void stage_meta(const BackwardLaunch& a, TableMeta* s_meta) {
+  if (a.T <= kLdsTables)
+    for (int i = threadIdx.x; i < a.T; i += kBlock) s_meta[i] = a.meta[i];
+  __syncthreads();
+}
+
+// Table of linear row id `key`: the last t with roff_t <= key.
+__device__ __forceinline__ int table_of_key(const BackwardLaunch& a, const TableMeta* s_meta,
+                                            uint32_t key) {
+  int lo = 0, hi = a.T;
+  if (a.T <= kLdsTables) {
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (static_cast<uint32_t>(s_meta[mid].roff) <= key) lo = mid; else hi = mid;
+    }
+  } else {
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (static_cast<uint32_t>(a.meta[mid].roff) <= key) lo = mid; else hi = mid;
+    }
+  }
+  return lo;
+}
+
+__device__ __forceinline__ TableMeta meta_of(const BackwardLaunch& a, const TableMeta* s_meta,
+                                             int t) {
+  return a.T <= kLdsTables ? s_meta[t] : a.meta[t];
+}
+
+// Short runs (at most Gs lookups): one lane group per run, grid-stride over
+// runs.  Most runs have one to three lookups, so the per-run instruction
+// count is what matters here: the next run's bounds are loaded while the
+// current one is processed, every lane prefetches one lookup, the row to
+// update and its state are loaded before the gradient rows arrive, the gather
+// is unrolled to the run's length (2, 4 or 8 rows in flight) and sums are
+// kept in fp32 (at most Gs terms: error below Gs * 2^-24 of the sum of
+// magnitudes; longer runs are summed in fp64 by the kernels below).
+template <int U, int VE, int NCH, bool REC>
+__device__ __forceinline__ void gather_short(const BackwardLaunch& a, const TableMeta& m,
+                                             int64_t tb, int leader, int gl, int Gs, int len,
+                                             uint32_t my_bag, float my_coef,
+                                             float (&acc)[NCH][VE]) {
+  for (int j = 0; j < len; j += U) {
+    float v[U][NCH][VE];
+    float cf[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int jj = j + u;
+      const int src = leader + min(jj, Gs - 1);
+      const uint32_t bag = __shfl(my_bag, src, kWave);
+      cf[u] = jj < len ? __shfl(my_coef, src, kWave) : 0.0f;
+      load_grad<VE, NCH>(a, m, static_cast<int64_t>(bag) - tb, gl, Gs, jj < len, v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int q = 0; q < VE; ++q) acc[c][q] = fmaf(cf[u], v[u][c][q], acc[c][q]);
+  }
+}
+
 template <int ST, int VE, int NCH, bool REC>
 __global__ __launch_bounds__(kBlock) void seg_short(BackwardLaunch a, const uint32_t* sorted_vals) {
+  __shared__ TableMeta s_meta[kLdsTables];
   const GroupIds id = group_ids(a);
   const int Gs = id.g.Gs, gl = id.g.gl;
   const int leader = lane_id() & ~(Gs - 1);
+  const bool failed = a.buf.counters[kCntError] != 0u;  // a look-back wait gave up earlier
   const uint32_t U = a.buf.counters[kCntUnique];
-  if (a.out_num && id.gid == 0 && gl == 0) *a.out_num = static_cast<int32_t>(U);
-  for (uint32_t r = id.gid; r < U; r += id.ngroups) {
-    const int64_t s = a.buf.run_start[r], e = a.buf.run_start[r + 1];
-    const int64_t len = e - s;
-    const uint32_t key = a.buf.unique_keys[r];
+  if (a.out_num && id.gid == 0 && gl == 0) *a.out_num = failed ? -1 : static_cast<int32_t>(U);
+  if (failed) return;
+  stage_meta(a, s_meta);
+  uint32_t r = id.gid;
+  int64_t ns = 0, ne = 0;
+  uint32_t nkey = 0;
+  if (r < U) {
+    ns = a.buf.run_start[r];
+    ne = a.buf.run_start[r + 1];
+    nkey = a.buf.unique_keys[r];
+  }
+  for (; r < U; r += id.ngroups) {
+    const int64_t s = ns, e = ne;
+    const uint32_t key = nkey;
+    const uint32_t rn = r + id.ngroups;
+    if (rn < U) {
+      ns = a.buf.run_start[rn];
+      ne = a.buf.run_start[rn + 1];
+      nkey = a.buf.unique_keys[rn];
+    }
+    const int len = static_cast<int>(e - s);
     if (a.out_unique && gl == 0) {
       a.out_unique[r] = static_cast<int32_t>(key);
-      a.out_lengths[r] = static_cast<int32_t>(len);
+      a.out_lengths[r] = len;
     }
     if (len > Gs) {
       // queue: a medium run as one workgroup item, a long run as its chunks
@@ -232,31 +316,51 @@ __global__ __launch_bounds__(kBlock) void seg_short(BackwardLaunch a, const uint
       }
       continue;
     }
-    // short run: every lane prefetches one lookup, then the group gathers
     uint32_t my_bag = 0;
     float my_coef = 0.0f;
     if (gl < len) lookup_of<REC>(a, sorted_vals[s + gl], &my_bag, &my_coef);
-    const int t = static_cast<int>(__shfl(my_bag, leader, kWave) / static_cast<uint32_t>(a.B));
-    const TableMeta m = a.meta[t];
+    const int t = table_of_key(a, s_meta, key);
+    const TableMeta m = meta_of(a, s_meta, t);
     const int64_t tb = static_cast<int64_t>(t) * a.B;
-    Acc<VE, NCH> acc;
-    acc.zero();
-    constexpr int kU = group_unroll<VE, NCH>();
-    for (int j = 0; j < len; j += kU) {
-      float v[kU][NCH][VE];
-      float cf[kU];
+    const int64_t row0 = m.woff + static_cast<int64_t>(key - static_cast<uint32_t>(m.roff)) * m.dim;
+    const int C = m.dim / VE;
+    float w[NCH][VE];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int jj = j + u;
-        const int src = leader + min(jj, Gs - 1);
-        const uint32_t bag = __shfl(my_bag, src, kWave);
-        cf[u] = __shfl(my_coef, src, kWave);
-        load_grad<VE, NCH>(a, m, static_cast<int64_t>(bag) - tb, gl, Gs, jj < len, v[u]);
-      }
+    for (int c = 0; c < NCH; ++c)
+      if (c * Gs + gl < C) load_widen<ST, VE>(a.weights, row0 + (c * Gs + gl) * VE, w[c]);
+    const float m_old = a.adagrad ? a.state[key] : 0.0f;
+    float acc[NCH][VE];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) accumulate<VE, NCH>(acc, (j + u < len) ? cf[u] : 0.0f, v[u]);
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int q = 0; q < VE; ++q) acc[c][q] = 0.0f;
+    if (len <= 2)
+      gather_short<2, VE, NCH, REC>(a, m, tb, leader, gl, Gs, len, my_bag, my_coef, acc);
+    else if (len <= 4)
+      gather_short<4, VE, NCH, REC>(a, m, tb, leader, gl, Gs, len, my_bag, my_coef, acc);
+    else
+      gather_short<group_unroll<VE, NCH>(), VE, NCH, REC>(a, m, tb, leader, gl, Gs, len, my_bag,
+                                                           my_coef, acc);
+    float step = a.lr;
+    if (a.adagrad) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int q = 0; q < VE; ++q) ss = fmaf(acc[c][q], acc[c][q], ss);
+      for (int o = Gs >> 1; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, kWave);
+      const float mnew = m_old + ss / static_cast<float>(m.dim);
+      if (gl == 0) a.state[key] = mnew;
+      step = a.lr / (sqrtf(mnew) + a.eps);
     }
-    group_update<ST, VE, NCH>(a, m, key, id.g, acc);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      if (c * Gs + gl < C) {
+#pragma unroll
+        for (int q = 0; q < VE; ++q) w[c][q] = fmaf(-step, acc[c][q], w[c][q]);
+        narrow_store<ST, VE>(a.weights, row0 + (c * Gs + gl) * VE, w[c]);
+      }
+    }
   }
 }
 
@@ -275,6 +379,7 @@ __device__ __forceinline__ double block_sum(double x, double* scratch) {
 
 template <int ST, int VE, int NCH, bool REC>
 __global__ __launch_bounds__(kBlock) void seg_wg(BackwardLaunch a, const uint32_t* sorted_vals) {
+  if (a.buf.counters[kCntError] != 0u) return;  // a look-back wait gave up earlier
   constexpr int NV = VE * NCH;                 // values per lane
   constexpr int kElemsPerThread = kMaxDim / kBlock;
   __shared__ uint32_t s_bag[kBlock];
@@ -433,6 +538,7 @@ __device__ __forceinline__ void store_partial(float* dst, const GroupCtx& g, int
 
 template <int VE, int NCH, bool REC>
 __global__ __launch_bounds__(kBlock) void seg_reduce2(BackwardLaunch a, const uint32_t* sorted_vals) {
+  if (a.buf.counters[kCntError] != 0u) return;  // a look-back wait gave up earlier
   const GroupIds id = group_ids(a);
   const uint32_t n = a.buf.counters[kCntItems2];
   for (uint32_t j = id.gid; j < n; j += id.ngroups) {
@@ -451,6 +557,7 @@ __global__ __launch_bounds__(kBlock) void seg_reduce2(BackwardLaunch a, const ui
 
 template <int ST, int VE, int NCH, bool REC>
 __global__ __launch_bounds__(kBlock) void seg_finalize(BackwardLaunch a, const uint32_t* sorted_vals) {
+  if (a.buf.counters[kCntError] != 0u) return;  // a look-back wait gave up earlier
   const GroupIds id = group_ids(a);
   const uint32_t n = a.buf.counters[kCntLong];
   for (uint32_t li = id.gid; li < n; li += id.ngroups) {

@@ -6,43 +6,75 @@
 // so that each row gets one optimizer update; "Kimbodo Engineering
 // Perspective": the grouping is a transpose, a sort and a run-length encoding.
 //
+//   init        zeroes the device counters, digit histograms and the status
+//               words the passes below chain through.
 //   linearize   key_i = roff_t + x_i (one 32-bit id space over all tables),
-//               value_i = bag id k (plain sums) or lookup id i, with a side
-//               record {k, p_i * s_k} when the lookup carries a coefficient.
-//   radix sort  stable least-significant-digit radix sort of (key, value) on
-//               ceil(log2(sum E_t)) bits, 8 bits per pass.  Each pass is
-//               three kernels: per-tile digit counts, a per-digit scan over
-//               tiles, and a scatter that ranks every key of a 2048-key tile in
-//               LDS (wave-level match of equal digits through ballots, per-wave
-//               digit counters in LDS) and writes the tile out bucket by
-//               bucket so that the global stores are coalesced.
-//   RLE         run heads (key differs from its predecessor), a scan of head
-//               counts over 4096-key tiles, then unique ids and run starts.
-//               The number of runs U stays on the device.
+//               value_i = bag id k (plain sums) or lookup id i with a side
+//               record {k, p_i * s_k} when lookups carry a coefficient.  It
+//               also counts the digits of every radix pass (these counts do not
+//               depend on the order of the keys), so no pass needs a counting
+//               kernel of its own.
+//   radix pass  one kernel per 8-bit digit of a stable LSD radix sort on
+//               ceil(log2(sum E_t)) bits.  A tile of 256*KPT keys is ranked in
+//               LDS (equal digits matched within a wave through 8 ballots,
+//               per-wave digit counters), its digit counts are published and
+//               the tile's offset within every digit bucket is found by a
+//               decoupled look-back over the tiles before it; the tile is then
+//               written bucket by bucket so global stores are coalesced.
+//   RLE         one kernel: run heads of a 4096-key tile, a look-back over
+//               the head counts of earlier tiles, then unique ids and run
+//               starts.  The number of runs U stays on the device.
+//
+// Tiles are numbered by an atomic ticket taken when a workgroup starts, so a
+// tile only waits for tiles that are already running and that publish their
+// counts before they wait themselves.  Every wait is bounded: past a spin
+// limit the workgroup raises an error flag and stops waiting, so no wave can
+// hang.
 #include "common.hpp"
 
 namespace tbe {
 namespace {
+
+constexpr uint32_t kFlagAgg = 1u << 30;     // status word: this tile's own count
+constexpr uint32_t kFlagIncl = 2u << 30;    // status word: count up to and including this tile
+constexpr uint32_t kValueMask = (1u << 30) - 1u;
+constexpr uint32_t kSpinLimit = 1u << 20;   // polls before a waiting tile gives up
+constexpr int kLookDepth = 32;              // status words read at once per digit
+constexpr int kLinBags = 64;                // bags per linearize workgroup
 
 template <typename IT>
 __device__ __forceinline__ int64_t ld_index(const void* p, int64_t i) {
   return static_cast<int64_t>(static_cast<const IT*>(p)[i]);
 }
 
-// One workgroup per 256 consecutive bags.  The bags' offsets are staged in
-// LDS; the workgroup then walks all of their lookups with consecutive threads
-// on consecutive lookups and finds each lookup's bag by binary search in LDS.
+__device__ __forceinline__ uint32_t ld_status(uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_status(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ __launch_bounds__(kBlock) void init_workspace(uint32_t* words, int64_t nwords) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < nwords;
+       i += static_cast<int64_t>(gridDim.x) * kBlock)
+    words[i] = 0u;
+}
+
+// One workgroup per 64 consecutive bags.  The bags' offsets are staged in LDS;
+// the workgroup then walks all of their lookups with consecutive threads on
+// consecutive lookups and finds each lookup's bag by binary search in LDS.
 template <typename IT>
 __global__ __launch_bounds__(kBlock) void linearize_kernel(BackwardLaunch a) {
-  __shared__ int64_t s_off[kBlock + 1];
-  __shared__ uint32_t s_roff[kBlock];
-  __shared__ float s_scale[kBlock];
+  __shared__ int64_t s_off[kLinBags + 1];
+  __shared__ uint32_t s_roff[kLinBags];
+  __shared__ float s_scale[kLinBags];
+  __shared__ uint32_t s_hist[kMaxRadixPasses * kRadix];
 
   const int tid = threadIdx.x;
-  if (blockIdx.x == 0 && tid < kNumCounters) a.buf.counters[tid] = 0u;
-
-  const int64_t k0 = static_cast<int64_t>(blockIdx.x) * kBlock;
-  const int nb = static_cast<int>(min(static_cast<int64_t>(kBlock), a.num_bags - k0));
+  const int passes = (a.key_bits + kRadixBits - 1) / kRadixBits;
+  for (int i = tid; i < passes * kRadix; i += kBlock) s_hist[i] = 0u;
+  const int64_t k0 = static_cast<int64_t>(blockIdx.x) * kLinBags;
+  const int nb = static_cast<int>(min(static_cast<int64_t>(kLinBags), a.num_bags - k0));
   if (tid < nb) {
     const int64_t k = k0 + tid;
     const int64_t lo = ld_index<IT>(a.offsets, k);
@@ -57,8 +89,7 @@ __global__ __launch_bounds__(kBlock) void linearize_kernel(BackwardLaunch a) {
 
   const int64_t p0 = s_off[0], p1 = s_off[nb];
   for (int64_t p = p0 + tid; p < p1; p += kBlock) {
-    // bag slot s with s_off[s] <= p < s_off[s + 1]
-    int lo = 0, hi = nb;
+    int lo = 0, hi = nb;  // bag slot s with s_off[s] <= p < s_off[s + 1]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (s_off[mid] <= p)
@@ -76,74 +107,78 @@ __global__ __launch_bounds__(kBlock) void linearize_kernel(BackwardLaunch a) {
     } else {
       a.buf.vals[0][p] = bag;
     }
+    for (int q = 0; q < passes; ++q)
+      atomicAdd(&s_hist[q * kRadix + ((key >> (q * kRadixBits)) & (kRadix - 1))], 1u);
   }
+  __syncthreads();
+  for (int i = tid; i < passes * kRadix; i += kBlock)
+    if (s_hist[i]) atomicAdd(&a.buf.digit_hist[i], s_hist[i]);
 }
 
-// Per-tile digit counts, stored digit-major: hist[d * ntiles + tile].
-__global__ __launch_bounds__(kBlock) void radix_upsweep(const uint32_t* __restrict__ keys,
-                                                        int64_t n, int shift, uint32_t* hist,
-                                                        int ntiles) {
-  __shared__ uint32_t h[kRadix];
-  const int tid = threadIdx.x;
-  h[tid] = 0u;
-  __syncthreads();
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * kSortTile;
+// Count of digit d in all tiles before `tile` (decoupled look-back, one digit
+// per thread, kLookDepth status words in flight).
+__device__ uint32_t lookback_digit(uint32_t* status, int tile, int d, uint32_t* err) {
+  uint32_t excl = 0;
+  int j = tile - 1;
+  uint32_t spins = 0;
+  while (true) {
+    uint32_t w[kLookDepth];
 #pragma unroll
-  for (int i = 0; i < kSortKeysPerThread; ++i) {
-    const int64_t p = base + i * kBlock + tid;
-    if (p < n) atomicAdd(&h[(keys[p] >> shift) & (kRadix - 1)], 1u);
+    for (int k = 0; k < kLookDepth; ++k)
+      w[k] = (j - k >= 0) ? ld_status(status + static_cast<int64_t>(j - k) * kRadix + d) : kFlagIncl;
+    bool stop = false, done = false;
+    int used = 0;
+#pragma unroll
+    for (int k = 0; k < kLookDepth; ++k) {
+      if (!stop) {
+        const uint32_t f = w[k] & ~kValueMask;
+        if (f == 0) {
+          stop = true;  // not published yet: poll again from here
+        } else {
+          excl += w[k] & kValueMask;
+          ++used;
+          if (f == kFlagIncl) stop = done = true;
+        }
+      }
+    }
+    if (done) return excl;
+    j -= used;
+    if (used == 0) {
+      if (++spins > kSpinLimit) {
+        atomicOr(err, 1u);
+        return excl;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
   }
-  __syncthreads();
-  hist[static_cast<int64_t>(tid) * ntiles + blockIdx.x] = h[tid];
 }
 
-// One workgroup per digit: exclusive scan of that digit's per-tile counts
-// (in place) and the digit's total.
-__global__ __launch_bounds__(kBlock) void radix_scan(uint32_t* hist, int ntiles,
-                                                     uint32_t* totals) {
-  __shared__ uint32_t scratch[kWavesPerBlock];
-  uint32_t* row = hist + static_cast<int64_t>(blockIdx.x) * ntiles;
-  uint32_t carry = 0;
-  for (int base = 0; base < ntiles; base += kBlock) {
-    const int i = base + threadIdx.x;
-    const uint32_t v = (i < ntiles) ? row[i] : 0u;
-    uint32_t total;
-    const uint32_t excl = block_exclusive_sum(v, scratch, &total);
-    if (i < ntiles) row[i] = carry + excl;
-    carry += total;
-  }
-  if (threadIdx.x == 0) totals[blockIdx.x] = carry;
-}
-
-// Stable scatter of one 2048-key tile.  Wave w owns tile positions
-// [w*512, (w+1)*512) and ranks them in 8 rounds of 64 consecutive keys; the
-// rank of a key is (keys with its digit in earlier waves) + (in earlier rounds
-// of its wave) + (in lower lanes of its round), which preserves input order.
-__global__ __launch_bounds__(kBlock) void radix_downsweep(
+// One LSD pass on digit (key >> shift) & 255.
+template <int KPT>
+__global__ __launch_bounds__(kBlock) void radix_pass(
     const uint32_t* __restrict__ kin, const uint32_t* __restrict__ vin, uint32_t* __restrict__ kout,
-    uint32_t* __restrict__ vout, int64_t n, int shift, const uint32_t* __restrict__ hist,
-    const uint32_t* __restrict__ totals, int ntiles) {
-  constexpr int KPT = kSortKeysPerThread;
-  __shared__ uint32_t s_k[kSortTile];
-  __shared__ uint32_t s_v[kSortTile];
+    uint32_t* __restrict__ vout, int64_t n, int shift, const uint32_t* __restrict__ totals,
+    uint32_t* status, uint32_t* ticket, uint32_t* err) {
+  constexpr int TS = kBlock * KPT;
+  __shared__ uint32_t s_k[TS];
+  __shared__ uint32_t s_v[TS];
   __shared__ uint32_t s_cnt[kWavesPerBlock][kRadix];
   __shared__ uint32_t s_dstart[kRadix];
   __shared__ uint32_t s_gbase[kRadix];
   __shared__ uint32_t scratch[kWavesPerBlock];
+  __shared__ uint32_t s_tile;
 
+  if (*err != 0u) return;  // an earlier pass gave up waiting: nothing here is valid
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const int tile = blockIdx.x;
-  const int64_t base = static_cast<int64_t>(tile) * kSortTile;
+  if (tid == 0) s_tile = atomicAdd(ticket, 1u);
+  for (int i = tid; i < kWavesPerBlock * kRadix; i += kBlock) (&s_cnt[0][0])[i] = 0u;
+  __syncthreads();
+  const int tile = static_cast<int>(s_tile);
+  const int64_t base = static_cast<int64_t>(tile) * TS;
   const uint32_t dmask = kRadix - 1;
 
-  for (int i = tid; i < kWavesPerBlock * kRadix; i += kBlock) (&s_cnt[0][0])[i] = 0u;
-  {
-    uint32_t total;
-    const uint32_t dbase = block_exclusive_sum(totals[tid], scratch, &total);
-    s_gbase[tid] = dbase + hist[static_cast<int64_t>(tid) * ntiles + tile];
-  }
-  __syncthreads();
-
+  // rank: wave w owns tile positions [w*64*KPT, (w+1)*64*KPT), ranked in KPT
+  // rounds of 64 consecutive keys, so equal digits keep their input order
   const int64_t seg = base + static_cast<int64_t>(wave) * (kWave * KPT);
   uint32_t key[KPT], val[KPT], rank[KPT];
 #pragma unroll
@@ -171,16 +206,28 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep(
     if (ok && below == 0) s_cnt[wave][d] = pre + cnt;
   }
   __syncthreads();
-  {
-    const uint32_t c0 = s_cnt[0][tid], c1 = s_cnt[1][tid], c2 = s_cnt[2][tid], c3 = s_cnt[3][tid];
-    s_cnt[0][tid] = 0u;
-    s_cnt[1][tid] = c0;
-    s_cnt[2][tid] = c0 + c1;
-    s_cnt[3][tid] = c0 + c1 + c2;
-    uint32_t total;
-    s_dstart[tid] = block_exclusive_sum(c0 + c1 + c2 + c3, scratch, &total);
+
+  // per digit (thread tid owns digit tid): wave offsets, tile-local bucket
+  // starts, and the tile's offset inside the global bucket
+  const uint32_t c0 = s_cnt[0][tid], c1 = s_cnt[1][tid], c2 = s_cnt[2][tid], c3 = s_cnt[3][tid];
+  const uint32_t mine = c0 + c1 + c2 + c3;
+  s_cnt[0][tid] = 0u;
+  s_cnt[1][tid] = c0;
+  s_cnt[2][tid] = c0 + c1;
+  s_cnt[3][tid] = c0 + c1 + c2;
+  uint32_t total;
+  s_dstart[tid] = block_exclusive_sum(mine, scratch, &total);
+  uint32_t* my_status = status + static_cast<int64_t>(tile) * kRadix + tid;
+  st_status(my_status, (tile == 0 ? kFlagIncl : kFlagAgg) | mine);
+  uint32_t before = 0;
+  if (tile > 0) {
+    before = lookback_digit(status, tile, tid, err);
+    st_status(my_status, kFlagIncl | ((before + mine) & kValueMask));
   }
+  const uint32_t dbase = block_exclusive_sum(totals[tid], scratch, &total);
+  s_gbase[tid] = dbase + before;
   __syncthreads();
+
 #pragma unroll
   for (int r = 0; r < KPT; ++r) {
     const bool ok = (seg + r * kWave + lane) < n;
@@ -192,62 +239,69 @@ __global__ __launch_bounds__(kBlock) void radix_downsweep(
     }
   }
   __syncthreads();
-  const int tile_n = static_cast<int>(min(static_cast<int64_t>(kSortTile), n - base));
+  const int tile_n = static_cast<int>(min(static_cast<int64_t>(TS), n - base));
   for (int i = tid; i < tile_n; i += kBlock) {
     const uint32_t k = s_k[i];
     const uint32_t d = (k >> shift) & dmask;
     const uint32_t gp = s_gbase[d] + (static_cast<uint32_t>(i) - s_dstart[d]);
-    kout[gp] = k;
-    vout[gp] = s_v[i];
+    if (gp < static_cast<uint64_t>(n)) {  // always true unless a look-back gave up
+      kout[gp] = k;
+      vout[gp] = s_v[i];
+    }
   }
 }
 
-// Run heads per 4096-key tile.
-__global__ __launch_bounds__(kBlock) void rle_count(const uint32_t* __restrict__ keys, int64_t n,
-                                                    uint32_t* tile_heads) {
-  __shared__ uint32_t scratch[kWavesPerBlock];
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * kRleTile;
-  uint32_t c = 0;
-  for (int i = 0; i < kRleTile / kBlock; ++i) {
-    const int64_t p = base + i * kBlock + threadIdx.x;
-    if (p < n) c += (p == 0 || keys[p] != keys[p - 1]) ? 1u : 0u;
-  }
-  uint32_t total;
-  block_exclusive_sum(c, scratch, &total);
-  if (threadIdx.x == 0) tile_heads[blockIdx.x] = total;
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+  for (int o = kWave >> 1; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
 }
 
-// One workgroup: exclusive scan of the per-tile head counts; U = total.
-__global__ __launch_bounds__(kBlock) void rle_scan(uint32_t* tile_heads, int ntiles,
-                                                   uint32_t* counters, uint32_t* run_start,
-                                                   int64_t n) {
-  __shared__ uint32_t scratch[kWavesPerBlock];
-  uint32_t carry = 0;
-  for (int base = 0; base < ntiles; base += kBlock) {
-    const int i = base + threadIdx.x;
-    const uint32_t v = (i < ntiles) ? tile_heads[i] : 0u;
-    uint32_t total;
-    const uint32_t excl = block_exclusive_sum(v, scratch, &total);
-    if (i < ntiles) tile_heads[i] = carry + excl;
-    carry += total;
-  }
-  if (threadIdx.x == 0) {
-    counters[kCntUnique] = carry;
-    run_start[carry] = static_cast<uint32_t>(n);
+// Sum of the values of all tiles before `tile` (one status word per tile; a
+// whole wave reads 64 predecessors at once).
+__device__ uint32_t lookback_wave(uint32_t* status, int tile, uint32_t* err) {
+  const int lane = lane_id();
+  uint32_t excl = 0;
+  int j = tile - 1;
+  uint32_t spins = 0;
+  while (true) {
+    const int idx = j - lane;
+    const uint32_t w = idx >= 0 ? ld_status(status + idx) : kFlagIncl;
+    const uint32_t f = w & ~kValueMask;
+    const uint64_t not_ready = __ballot(f == 0);
+    const uint64_t incl = __ballot(f == kFlagIncl);
+    const int first_nr = not_ready ? __builtin_ctzll(not_ready) : kWave;
+    const int first_in = incl ? __builtin_ctzll(incl) : kWave;
+    const int take = first_in < first_nr ? first_in + 1 : first_nr;
+    excl += wave_sum_u32(lane < take ? (w & kValueMask) : 0u);
+    if (first_in < first_nr) return excl;
+    j -= take;
+    if (take == 0) {
+      if (++spins > kSpinLimit) {
+        if (lane == 0) atomicOr(err, 1u);
+        return excl;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
   }
 }
 
-// Unique ids and run starts.  The tile (plus the key before it) is staged in
-// LDS; each thread then owns 16 consecutive positions so that run ids follow
-// position order.
-__global__ __launch_bounds__(kBlock) void rle_write(const uint32_t* __restrict__ keys, int64_t n,
-                                                    const uint32_t* __restrict__ tile_base,
-                                                    uint32_t* unique_keys, uint32_t* run_start) {
+// Run heads of a 4096-key tile (staged in LDS with the key before it); each
+// thread owns 16 consecutive positions so run ids follow position order.
+__global__ __launch_bounds__(kBlock) void rle_kernel(const uint32_t* __restrict__ keys, int64_t n,
+                                                     int ntiles, uint32_t* status, uint32_t* ticket,
+                                                     uint32_t* counters, uint32_t* unique_keys,
+                                                     uint32_t* run_start) {
   constexpr int PER = kRleTile / kBlock;
   __shared__ uint32_t s_k[kRleTile + 1];
   __shared__ uint32_t scratch[kWavesPerBlock];
+  __shared__ uint32_t s_tile, s_base;
+  if (counters[kCntError] != 0u) return;  // the sort gave up waiting: nothing here is valid
   const int tid = threadIdx.x;
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * kRleTile;
+  if (tid == 0) s_tile = atomicAdd(ticket, 1u);
+  __syncthreads();
+  const int tile = static_cast<int>(s_tile);
+  const int64_t base = static_cast<int64_t>(tile) * kRleTile;
   for (int i = tid; i < kRleTile + 1; i += kBlock) {
     const int64_t p = base - 1 + i;
     s_k[i] = (p >= 0 && p < n) ? keys[p] : 0u;
@@ -261,14 +315,33 @@ __global__ __launch_bounds__(kBlock) void rle_write(const uint32_t* __restrict__
     if (p < n && (p == 0 || s_k[i + 1] != s_k[i])) ++c;
   }
   uint32_t total;
-  uint32_t r = tile_base[blockIdx.x] + block_exclusive_sum(c, scratch, &total);
+  uint32_t r = block_exclusive_sum(c, scratch, &total);
+  if (tid < kWave) {
+    if (tid == 0) st_status(status + tile, (tile == 0 ? kFlagIncl : kFlagAgg) | total);
+    uint32_t before = 0;
+    if (tile > 0) before = lookback_wave(status, tile, counters + kCntError);
+    if (tid == 0) {
+      if (tile > 0) st_status(status + tile, kFlagIncl | ((before + total) & kValueMask));
+      s_base = before;
+      if (tile == ntiles - 1) {
+        // U <= n always, unless a look-back gave up; keep every index in range regardless
+        const uint32_t U = min(before + total, static_cast<uint32_t>(n));
+        counters[kCntUnique] = U;
+        run_start[U] = static_cast<uint32_t>(n);
+      }
+    }
+  }
+  __syncthreads();
+  r += s_base;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int i = tid * PER + j;
     const int64_t p = base + i;
     if (p < n && (p == 0 || s_k[i + 1] != s_k[i])) {
-      unique_keys[r] = s_k[i + 1];
-      run_start[r] = static_cast<uint32_t>(p);
+      if (r < static_cast<uint64_t>(n)) {
+        unique_keys[r] = s_k[i + 1];
+        run_start[r] = static_cast<uint32_t>(p);
+      }
       ++r;
     }
   }
@@ -276,9 +349,16 @@ __global__ __launch_bounds__(kBlock) void rle_write(const uint32_t* __restrict__
 
 }  // namespace
 
+int sort_keys_per_thread(int64_t n) { return n <= (int64_t{1} << 21) ? 8 : 16; }
+
 hipError_t launch_linearize(const BackwardLaunch& a, hipStream_t stream) {
-  const int64_t blocks = (a.num_bags + kBlock - 1) / kBlock;
-  if (blocks <= 0) return hipSuccess;
+  // zero the counters, histograms and look-back status words first
+  int64_t zblocks = (a.buf.zero_words + kBlock - 1) / kBlock;
+  if (zblocks > 1024) zblocks = 1024;
+  hipLaunchKernelGGL(init_workspace, dim3(static_cast<unsigned>(zblocks > 0 ? zblocks : 1)),
+                     dim3(kBlock), 0, stream, a.buf.counters, a.buf.zero_words);
+  const int64_t blocks = (a.num_bags + kLinBags - 1) / kLinBags;
+  if (blocks <= 0) return hipGetLastError();
   if (a.index64)
     hipLaunchKernelGGL(linearize_kernel<int64_t>, dim3(static_cast<unsigned>(blocks)),
                        dim3(kBlock), 0, stream, a);
@@ -291,19 +371,23 @@ hipError_t launch_linearize(const BackwardLaunch& a, hipStream_t stream) {
 hipError_t launch_radix_sort(const BackwardLaunch& a, hipStream_t stream, int* result_buffer,
                              StageHook hook, void* ctx) {
   const int64_t n = a.num_indices;
-  const int ntiles = static_cast<int>((n + kSortTile - 1) / kSortTile);
-  int cur = 0;
-  for (int shift = 0; shift < a.key_bits; shift += kRadixBits) {
-    hipLaunchKernelGGL(radix_upsweep, dim3(ntiles), dim3(kBlock), 0, stream, a.buf.keys[cur], n,
-                       shift, a.buf.hist, ntiles);
-    if (hook) hook(ctx, "radix_upsweep");
-    hipLaunchKernelGGL(radix_scan, dim3(kRadix), dim3(kBlock), 0, stream, a.buf.hist, ntiles,
-                       a.buf.digit_totals);
-    if (hook) hook(ctx, "radix_scan");
-    hipLaunchKernelGGL(radix_downsweep, dim3(ntiles), dim3(kBlock), 0, stream, a.buf.keys[cur],
-                       a.buf.vals[cur], a.buf.keys[cur ^ 1], a.buf.vals[cur ^ 1], n, shift,
-                       a.buf.hist, a.buf.digit_totals, ntiles);
-    if (hook) hook(ctx, "radix_downsweep");
+  const int kpt = sort_keys_per_thread(n);
+  const int64_t ts = static_cast<int64_t>(kBlock) * kpt;
+  const int ntiles = static_cast<int>((n + ts - 1) / ts);
+  int cur = 0, pass = 0;
+  for (int shift = 0; shift < a.key_bits; shift += kRadixBits, ++pass) {
+    uint32_t* status = a.buf.sort_status + static_cast<int64_t>(pass) * ntiles * kRadix;
+    const uint32_t* totals = a.buf.digit_hist + pass * kRadix;
+    uint32_t* ticket = a.buf.tickets + pass;
+    if (kpt == 8)
+      hipLaunchKernelGGL(radix_pass<8>, dim3(ntiles), dim3(kBlock), 0, stream, a.buf.keys[cur],
+                         a.buf.vals[cur], a.buf.keys[cur ^ 1], a.buf.vals[cur ^ 1], n, shift, totals,
+                         status, ticket, a.buf.counters + kCntError);
+    else
+      hipLaunchKernelGGL(radix_pass<16>, dim3(ntiles), dim3(kBlock), 0, stream, a.buf.keys[cur],
+                         a.buf.vals[cur], a.buf.keys[cur ^ 1], a.buf.vals[cur ^ 1], n, shift, totals,
+                         status, ticket, a.buf.counters + kCntError);
+    if (hook) hook(ctx, "radix_pass");
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     cur ^= 1;
@@ -316,15 +400,10 @@ hipError_t launch_run_length_encode(const BackwardLaunch& a, const uint32_t* sor
                                     hipStream_t stream, StageHook hook, void* ctx) {
   const int64_t n = a.num_indices;
   const int ntiles = static_cast<int>((n + kRleTile - 1) / kRleTile);
-  hipLaunchKernelGGL(rle_count, dim3(ntiles), dim3(kBlock), 0, stream, sorted_keys, n,
-                     a.buf.rle_tiles);
-  if (hook) hook(ctx, "rle_count");
-  hipLaunchKernelGGL(rle_scan, dim3(1), dim3(kBlock), 0, stream, a.buf.rle_tiles, ntiles,
-                     a.buf.counters, a.buf.run_start, n);
-  if (hook) hook(ctx, "rle_scan");
-  hipLaunchKernelGGL(rle_write, dim3(ntiles), dim3(kBlock), 0, stream, sorted_keys, n,
-                     a.buf.rle_tiles, a.buf.unique_keys, a.buf.run_start);
-  if (hook) hook(ctx, "rle_write");
+  hipLaunchKernelGGL(rle_kernel, dim3(ntiles), dim3(kBlock), 0, stream, sorted_keys, n, ntiles,
+                     a.buf.rle_status, a.buf.tickets + kMaxRadixPasses, a.buf.counters,
+                     a.buf.unique_keys, a.buf.run_start);
+  if (hook) hook(ctx, "rle_kernel");
   return hipGetLastError();
 }
 

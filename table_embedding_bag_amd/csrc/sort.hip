@@ -25,9 +25,10 @@
 //               the head counts of earlier tiles, then unique ids and run
 //               starts.  The number of runs U stays on the device.
 //
-// Tiles are numbered by an atomic ticket taken when a workgroup starts, so a
-// tile only waits for tiles that are already running and that publish their
-// counts before they wait themselves.  Every wait is bounded: past a spin
+// A tile only waits for tiles numbered before it, which publish their counts
+// before they wait themselves.  When the grid is small enough to be resident
+// all at once, tiles are numbered by workgroup id; otherwise by an atomic
+// ticket taken when a workgroup starts, so every tile waited for is running.  Every wait is bounded: past a spin
 // limit the workgroup raises an error flag and stops waiting, so no wave can
 // hang.
 #include "common.hpp"
@@ -39,8 +40,9 @@ constexpr uint32_t kFlagAgg = 1u << 30;     // status word: this tile's own coun
 constexpr uint32_t kFlagIncl = 2u << 30;    // status word: count up to and including this tile
 constexpr uint32_t kValueMask = (1u << 30) - 1u;
 constexpr uint32_t kSpinLimit = 1u << 20;   // polls before a waiting tile gives up
-constexpr int kLookDepth = 32;              // status words read at once per digit
+constexpr int kLookDepth = 16;              // status words read at once per digit
 constexpr int kLinBags = 64;                // bags per linearize workgroup
+constexpr int kResidentTiles = 256;         // grids this small are resident all at once
 
 template <typename IT>
 __device__ __forceinline__ int64_t ld_index(const void* p, int64_t i) {
@@ -168,9 +170,11 @@ __global__ __launch_bounds__(kBlock) void radix_pass(
   __shared__ uint32_t scratch[kWavesPerBlock];
   __shared__ uint32_t s_tile;
 
-  if (*err != 0u) return;  // an earlier pass gave up waiting: nothing here is valid
+  // (no early exit on an earlier failure: every write below is clamped in range,
+  // and a failed call is reported by the kernels after the sort)
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  if (tid == 0) s_tile = atomicAdd(ticket, 1u);
+  const uint32_t my_total = totals[tid];  // issued with the key loads below
+  if (tid == 0) s_tile = ticket ? atomicAdd(ticket, 1u) : blockIdx.x;
   for (int i = tid; i < kWavesPerBlock * kRadix; i += kBlock) (&s_cnt[0][0])[i] = 0u;
   __syncthreads();
   const int tile = static_cast<int>(s_tile);
@@ -224,7 +228,7 @@ __global__ __launch_bounds__(kBlock) void radix_pass(
     before = lookback_digit(status, tile, tid, err);
     st_status(my_status, kFlagIncl | ((before + mine) & kValueMask));
   }
-  const uint32_t dbase = block_exclusive_sum(totals[tid], scratch, &total);
+  const uint32_t dbase = block_exclusive_sum(my_total, scratch, &total);
   s_gbase[tid] = dbase + before;
   __syncthreads();
 
@@ -296,9 +300,8 @@ __global__ __launch_bounds__(kBlock) void rle_kernel(const uint32_t* __restrict_
   __shared__ uint32_t s_k[kRleTile + 1];
   __shared__ uint32_t scratch[kWavesPerBlock];
   __shared__ uint32_t s_tile, s_base;
-  if (counters[kCntError] != 0u) return;  // the sort gave up waiting: nothing here is valid
-  const int tid = threadIdx.x;
-  if (tid == 0) s_tile = atomicAdd(ticket, 1u);
+  const int tid = threadIdx.x;  // every write below is clamped in range
+  if (tid == 0) s_tile = ticket ? atomicAdd(ticket, 1u) : blockIdx.x;
   __syncthreads();
   const int tile = static_cast<int>(s_tile);
   const int64_t base = static_cast<int64_t>(tile) * kRleTile;
@@ -349,7 +352,7 @@ __global__ __launch_bounds__(kBlock) void rle_kernel(const uint32_t* __restrict_
 
 }  // namespace
 
-int sort_keys_per_thread(int64_t n) { return n <= (int64_t{1} << 21) ? 8 : 16; }
+int sort_keys_per_thread(int64_t n) { return n <= (int64_t{1} << 17) ? 8 : 16; }
 
 hipError_t launch_linearize(const BackwardLaunch& a, hipStream_t stream) {
   // zero the counters, histograms and look-back status words first
@@ -378,7 +381,7 @@ hipError_t launch_radix_sort(const BackwardLaunch& a, hipStream_t stream, int* r
   for (int shift = 0; shift < a.key_bits; shift += kRadixBits, ++pass) {
     uint32_t* status = a.buf.sort_status + static_cast<int64_t>(pass) * ntiles * kRadix;
     const uint32_t* totals = a.buf.digit_hist + pass * kRadix;
-    uint32_t* ticket = a.buf.tickets + pass;
+    uint32_t* ticket = ntiles <= kResidentTiles ? nullptr : a.buf.tickets + pass;
     if (kpt == 8)
       hipLaunchKernelGGL(radix_pass<8>, dim3(ntiles), dim3(kBlock), 0, stream, a.buf.keys[cur],
                          a.buf.vals[cur], a.buf.keys[cur ^ 1], a.buf.vals[cur ^ 1], n, shift, totals,
@@ -401,7 +404,9 @@ hipError_t launch_run_length_encode(const BackwardLaunch& a, const uint32_t* sor
   const int64_t n = a.num_indices;
   const int ntiles = static_cast<int>((n + kRleTile - 1) / kRleTile);
   hipLaunchKernelGGL(rle_kernel, dim3(ntiles), dim3(kBlock), 0, stream, sorted_keys, n, ntiles,
-                     a.buf.rle_status, a.buf.tickets + kMaxRadixPasses, a.buf.counters,
+                     a.buf.rle_status,
+                     ntiles <= kResidentTiles ? nullptr : a.buf.tickets + kMaxRadixPasses,
+                     a.buf.counters,
                      a.buf.unique_keys, a.buf.run_start);
   if (hook) hook(ctx, "rle_kernel");
   return hipGetLastError();

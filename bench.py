@@ -117,12 +117,11 @@ def algorithmic_bytes(spec, batch, long_threshold=256, chunk=256, super_chunk=32
     seg_r2 = float(((nch[two] + n2[two]) * 4 * D[two]).sum())
     seg_final = float((np.where(n2 > 0, n2, nch)[long_] * 4 * D[long_] + per_row[long_]).sum())
     N, U, nbags = int(lens.sum()), int(cnt.size), spec.T * spec.B
-    # grouping front: linearize (ids 8 + offsets, key/value writes 8, record 8),
-    # per radix pass: digit counts read 4, scatter reads and writes key+value 16;
-    # run-length encoding: heads read 4, then keys read 4 + unique id/start writes 8 per run
+    # grouping front: workspace clear (a few KB), linearize (ids 8 + offsets, key/value
+    # writes 8, record 8), per radix pass the key+value read and scatter 16 per lookup,
+    # run-length encoding keys read 4 + unique id/start writes 8 per run
     front = {"linearize_kernel": float(N * (8 + 8 + rec) + 8 * nbags),
-             "radix_upsweep": float(4 * N), "radix_downsweep": float(16 * N),
-             "rle_count": float(4 * N), "rle_write": float(4 * N + 8 * U)}
+             "radix_pass": float(16 * N), "rle_kernel": float(4 * N + 8 * U)}
     return {"fwd_gather_pool": fwd, "seg_short": seg_short, "seg_wg": seg_wg,
             "seg_reduce2": seg_r2, "seg_finalize": seg_final, **front}, {"N": int(lens.sum()), "U": int(cnt.size),
                                          "long_run_share": float(cnt[long_].sum() / max(1, cnt.sum())),

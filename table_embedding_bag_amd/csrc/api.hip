@@ -33,6 +33,15 @@ struct tbe_handle {
   std::vector<TableMeta> meta_host;
   TableMeta* meta = nullptr;     // device copy
   uint32_t* flag = nullptr;      // device word for the validation kernel
+  // count-matrix forward: eligible tables (device list), the other tables
+  // (device list for the gather kernel) and the transposed-table buffer
+  std::vector<HistTable> hist_host;
+  std::vector<int32_t> gather_host;
+  HistTable* hist = nullptr;
+  int32_t* gather_list = nullptr;
+  uint16_t* wt = nullptr;
+  int32_t hist_etiles = 0, hist_dtiles = 0;
+  int64_t wt_elems = 0;
   int64_t long_threshold = 256;
   // profiling: events recorded at call starts (name == nullptr) and after
   // each kernel (name of that kernel), kept until tbe_stage_times reads them.
@@ -265,7 +274,6 @@ tbe_status tbe_create(const tbe_config* cfg, void* weights, float* optim_state, 
   if (cfg->flags & ~7u) return TBE_ERR_INVALID_ARGUMENT;
   if ((cfg->flags & TBE_FLAG_NO_HISTOGRAM) && (cfg->flags & TBE_FLAG_FORCE_HISTOGRAM))
     return TBE_ERR_INVALID_ARGUMENT;
-  if (cfg->flags & TBE_FLAG_FORCE_HISTOGRAM) return TBE_ERR_UNSUPPORTED;
   const int sb = storage_bytes(cfg->weight_dtype);
   if (!aligned(weights, 16)) return TBE_ERR_INVALID_ARGUMENT;
   int64_t sum_rows = 0, sum_dims = 0;
@@ -316,6 +324,32 @@ tbe_status tbe_create(const tbe_config* cfg, void* weights, float* optim_state, 
       roff += h->rows[t];
       doff += h->dims[t];
     }
+    // count-matrix forward eligibility (16-bit storage, small tables, dims in
+    // 16-column MFMA tiles, 16-byte aligned rows)
+    int64_t wt_off = 0;
+    const bool use_hist = h->dtype != TBE_F32 && !(h->flags & TBE_FLAG_NO_HISTOGRAM);
+    for (int t = 0; t < h->T; ++t) {
+      const TableMeta& m = h->meta_host[t];
+      const bool ok = use_hist && m.rows <= kHistMaxRows && m.dim <= kHistMaxDim &&
+                      m.dim % 16 == 0 && m.woff % 8 == 0;
+      if (!ok) {
+        if (h->flags & TBE_FLAG_FORCE_HISTOGRAM) {
+          delete h;
+          return TBE_ERR_UNSUPPORTED;
+        }
+        h->gather_host.push_back(t);
+        continue;
+      }
+      HistTable ht{};
+      ht.table = t;
+      ht.epad = (m.rows + kHistKc - 1) / kHistKc * kHistKc;
+      ht.wt_off = wt_off;
+      wt_off += static_cast<int64_t>(ht.epad) * m.dim;
+      h->hist_host.push_back(ht);
+      h->hist_etiles = std::max(h->hist_etiles, ht.epad / 64);
+      h->hist_dtiles = std::max(h->hist_dtiles, (m.dim + 63) / 64);
+    }
+    h->wt_elems = wt_off;
   } catch (...) {
     delete h;
     return TBE_ERR_OUT_OF_MEMORY;
@@ -325,19 +359,41 @@ tbe_status tbe_create(const tbe_config* cfg, void* weights, float* optim_state, 
     delete h;
     return TBE_ERR_HIP;
   }
+  // one device block: table metadata | validation flag | count-matrix table
+  // list | gather table list
+  auto up = [](size_t x) { return (x + kAlign - 1) / kAlign * kAlign; };
   const size_t meta_bytes = sizeof(TableMeta) * static_cast<size_t>(h->T);
-  const size_t flag_off = (meta_bytes + kAlign - 1) / kAlign * kAlign;
+  const size_t flag_off = up(meta_bytes);
+  const size_t hist_off = flag_off + kAlign;
+  const size_t hist_bytes = sizeof(HistTable) * h->hist_host.size();
+  const size_t gather_off = hist_off + up(hist_bytes);
+  const size_t gather_bytes = sizeof(int32_t) * h->gather_host.size();
   void* block = nullptr;
-  if (hipMalloc(&block, flag_off + kAlign) != hipSuccess) {
+  if (hipMalloc(&block, gather_off + up(gather_bytes)) != hipSuccess) {
     delete h;
     return TBE_ERR_OUT_OF_MEMORY;
   }
+  char* base = static_cast<char*>(block);
   h->meta = static_cast<TableMeta*>(block);
-  h->flag = reinterpret_cast<uint32_t*>(static_cast<char*>(block) + flag_off);
-  if (hipMemcpy(h->meta, h->meta_host.data(), meta_bytes, hipMemcpyHostToDevice) != hipSuccess) {
+  h->flag = reinterpret_cast<uint32_t*>(base + flag_off);
+  h->hist = hist_bytes ? reinterpret_cast<HistTable*>(base + hist_off) : nullptr;
+  h->gather_list = gather_bytes ? reinterpret_cast<int32_t*>(base + gather_off) : nullptr;
+  bool ok = hipMemcpy(h->meta, h->meta_host.data(), meta_bytes, hipMemcpyHostToDevice) == hipSuccess;
+  if (ok && hist_bytes)
+    ok = hipMemcpy(h->hist, h->hist_host.data(), hist_bytes, hipMemcpyHostToDevice) == hipSuccess;
+  if (ok && gather_bytes)
+    ok = hipMemcpy(h->gather_list, h->gather_host.data(), gather_bytes, hipMemcpyHostToDevice) ==
+         hipSuccess;
+  if (!ok) {
     (void)hipFree(block);
     delete h;
     return TBE_ERR_HIP;
+  }
+  if (h->wt_elems > 0 &&
+      hipMalloc(reinterpret_cast<void**>(&h->wt), sizeof(uint16_t) * h->wt_elems) != hipSuccess) {
+    (void)hipFree(block);
+    delete h;
+    return TBE_ERR_OUT_OF_MEMORY;
   }
   *out = h;
   return TBE_OK;
@@ -347,6 +403,7 @@ void tbe_destroy(tbe_handle* h) {
   if (!h) return;
   for (auto& e : h->pool) (void)hipEventDestroy(e);
   if (h->meta) (void)hipFree(h->meta);
+  if (h->wt) (void)hipFree(h->wt);
   delete h;
 }
 
@@ -393,15 +450,10 @@ tbe_status tbe_forward(tbe_handle* h, int32_t B, const void* indices, const void
   if (B == 0) return TBE_OK;
   if (!output || !aligned(output, 16)) return TBE_ERR_INVALID_ARGUMENT;
   if (psw && !aligned(psw, 4)) return TBE_ERR_INVALID_ARGUMENT;
+  // per-sample weights rule out the count-matrix forward
+  if (psw && (h->flags & TBE_FLAG_FORCE_HISTOGRAM)) return TBE_ERR_UNSUPPORTED;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   try {
-    if (h->flags & TBE_FLAG_VALIDATE) {
-      st = run_validation(h, B, indices, offsets, index_dtype, n, s);
-      if (st != TBE_OK) return st;
-    }
-    HookCtx hc{h, s};
-    prof_begin(h, s);
-
     // Sub-wave size: enough lane groups per bag that one round of row loads
     // covers a mean-length bag.
     const double mean_len = static_cast<double>(n) / (static_cast<double>(h->T) * B);
@@ -413,14 +465,46 @@ tbe_status tbe_forward(tbe_handle* h, int32_t B, const void* indices, const void
       const int64_t bags_per_block = int64_t{kWavesPerBlock} << (6 - sw);
       tiles = std::max<int64_t>(tiles, (B + bags_per_block - 1) / bags_per_block);
     }
+    if (tiles * h->T > 0x7FFFFFFF) return TBE_ERR_UNSUPPORTED;
+    if (h->flags & TBE_FLAG_VALIDATE) {
+      st = run_validation(h, B, indices, offsets, index_dtype, n, s);
+      if (st != TBE_OK) return st;
+    }
+    HookCtx hc{h, s};
+    prof_begin(h, s);
+    // Count-matrix forward for the eligible tables unless lookups carry
+    // per-sample weights; the gather kernel covers every other table.
+    const bool hist = !psw && !h->hist_host.empty();
+    if (hist) {
+      HistLaunch ha{};
+      ha.weights = h->weights;
+      ha.indices = indices;
+      ha.offsets = offsets;
+      ha.out = output;
+      ha.meta = h->meta;
+      ha.list = h->hist;
+      ha.wt = h->wt;
+      ha.H = static_cast<int32_t>(h->hist_host.size());
+      ha.B = B;
+      ha.sum_dims = h->sum_dims;
+      ha.etiles = h->hist_etiles;
+      ha.dtiles = h->hist_dtiles;
+      ha.mean = h->pooling == TBE_POOL_MEAN;
+      ha.dtype = h->dtype;
+      ha.index64 = index_dtype == TBE_I64;
+      const hipError_t e = launch_forward_histogram(ha, s, h->profile ? prof_mark : nullptr, &hc);
+      if (e != hipSuccess) return from_hip(e);
+      if (h->gather_host.empty()) return TBE_OK;
+    }
     ForwardLaunch a{};
+    a.table_list = hist ? h->gather_list : nullptr;
     a.weights = h->weights;
     a.indices = indices;
     a.offsets = offsets;
     a.psw = psw;
     a.out = output;
     a.meta = h->meta;
-    a.T = h->T;
+    a.T = hist ? static_cast<int32_t>(h->gather_host.size()) : h->T;
     a.B = B;
     a.sum_dims = h->sum_dims;
     a.tiles_per_table = static_cast<int32_t>(tiles);
@@ -429,7 +513,6 @@ tbe_status tbe_forward(tbe_handle* h, int32_t B, const void* indices, const void
     a.dtype = h->dtype;
     a.index64 = index_dtype == TBE_I64;
     a.vec = h->fwd_vec;
-    if (tiles * h->T > 0x7FFFFFFF) return TBE_ERR_UNSUPPORTED;
     const hipError_t e = launch_forward_gather(a, s);
     prof_mark(&hc, "fwd_gather_pool");
     return from_hip(e);

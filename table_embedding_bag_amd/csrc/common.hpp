@@ -172,6 +172,9 @@ __device__ __forceinline__ void narrow_store(void* base, int64_t e, const float*
 // Launch interfaces (host side, implemented next to their kernels)
 // ---------------------------------------------------------------------------
 
+// Stage hooks let the host record profiling events between launches.
+typedef void (*StageHook)(void* ctx, const char* stage_name);
+
 struct ForwardLaunch {
   const void* weights;
   const void* indices;
@@ -186,8 +189,38 @@ struct ForwardLaunch {
   int32_t dtype;            // storage dtype code
   int32_t index64;          // indices/offsets are int64
   int32_t vec;              // 16-byte row chunks (else one element per lane)
+  const int32_t* table_list;  // tables to cover (T entries), or null for tables 0..T-1
 };
 hipError_t launch_forward_gather(const ForwardLaunch& a, hipStream_t stream);
+
+// Count-matrix forward of small 16-bit tables.  Each such table has a
+// transposed, zero-padded copy W^T[d][e] (e < epad, epad a multiple of
+// kHistKc) at element wt_off of a handle-owned buffer.
+constexpr int kHistKc = 64;        // table rows per K chunk
+constexpr int kHistMaxRows = 1024; // eligibility: E_t
+constexpr int kHistMaxDim = 256;   // eligibility: D_t (and a multiple of 16)
+struct HistTable {
+  int32_t table;
+  int32_t epad;
+  int64_t wt_off;
+};
+struct HistLaunch {
+  const void* weights;
+  const void* indices;
+  const void* offsets;
+  float* out;
+  const TableMeta* meta;
+  const HistTable* list;
+  uint16_t* wt;
+  int32_t H;                // tables in list
+  int32_t B, sum_dims;
+  int32_t etiles, dtiles;   // max over the listed tables of epad/64 and ceil(D/64)
+  int32_t mean;
+  int32_t dtype;            // kF16 or kBF16
+  int32_t index64;
+};
+hipError_t launch_forward_histogram(const HistLaunch& a, hipStream_t stream, StageHook hook,
+                                    void* ctx);
 
 // Device workspace of the backward, carved by the host.
 struct BackwardBuffers {
@@ -256,9 +289,6 @@ struct BackwardLaunch {
   int32_t* out_num;
   BackwardBuffers buf;
 };
-
-// Stage hooks let the host record profiling events between launches.
-typedef void (*StageHook)(void* ctx, const char* stage_name);
 
 hipError_t launch_linearize(const BackwardLaunch& a, hipStream_t stream);
 // Sorts buf.keys[0]/vals[0]; returns the index (0 or 1) of the buffer pair

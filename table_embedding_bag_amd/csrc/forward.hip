@@ -45,8 +45,9 @@ __global__ __launch_bounds__(kBlock) void fwd_gather_pool(ForwardLaunch a) {
   constexpr int VE = VEC ? 16 / SB : 1;  // elements per lane chunk
 
   const int logical = xcd_contiguous_block(blockIdx.x, gridDim.x);
-  const int t = logical / a.tiles_per_table;
-  const int tile = logical - t * a.tiles_per_table;
+  const int listed = logical / a.tiles_per_table;
+  const int tile = logical - listed * a.tiles_per_table;
+  const int t = a.table_list ? a.table_list[listed] : listed;
   const TableMeta m = a.meta[t];
 
   const int lane = lane_id();

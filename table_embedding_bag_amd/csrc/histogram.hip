@@ -1,0 +1,326 @@
+// histogram.hip -- count-matrix forward of small 16-bit tables on gfx950.
+//
+// kimbodo.com/?p=28372, "What Happened": next to the generic gather path
+// (which also takes per-sample weights), small tables that qualify are pooled
+// through a histogram and the matrix cores.  For such a table t the pooled
+// output of all bags is one dense product
+//     Y_t = diag(s) * C_t * W_t,   C_t[b, r] = #{i in bag (t, b) : x_i = r},
+// with s_k = 1 (sum) or 1/L_k (mean).  It equals the gather result exactly up
+// to fp32 rounding order: counts are small integers and the stored rows are
+// fp16/bf16, so every product C*W is exact in fp32.
+//
+// Eligible: fp16 or bf16 storage, E_t <= 1024, D_t <= 256 with D_t a multiple
+// of 16, no per-sample weights.  A bag longer than 256 lookups (bf16; 2048 for
+// fp16) could hold a count the 16-bit operand does not represent exactly; such
+// bags are left out of C and pooled by a plain gather loop in the same
+// workgroup.  Because C is dense, a NaN or infinity anywhere in W_t reaches
+// every bag of table t (0 * inf); the gather path does not have this property.
+//
+// Mapping onto CDNA4:
+//  * hist_transpose writes W_t^T[d][e] (zero for e >= E_t, up to a multiple of
+//    64 rows) to a handle-owned buffer, so that the MFMA's B operand -- eight
+//    consecutive K (= table row) values per lane -- is one 16-byte read.
+//  * fwd_histogram: a workgroup owns 256 bags x 64 output columns of one table
+//    (a wave owns 64 bags x 64 columns: 16 accumulators of
+//    v_mfma_f32_16x16x32_{bf16,f16}).  C never exists in HBM: the K range is
+//    walked in chunks of 64 table rows, and for each chunk the count tile
+//    [256 bags][64 rows] is built in LDS with packed 16-bit LDS atomic adds
+//    (+1 per lookup; the lookups of the workgroup are bucketed by chunk once),
+//    multiplied, then cleared again with -1 adds for the same lookups.
+//  * Chunks that no lookup of the workgroup touches are skipped (their
+//    product is zero).
+//  * Workgroups are renumbered so that every XCD works on a contiguous range
+//    of tables (each table's W^T stays in one XCD's L2).
+#include "common.hpp"
+
+namespace tbe {
+namespace {
+
+constexpr int kHB = 256;              // bags per workgroup (64 per wave)
+constexpr int kDB = 64;               // output columns per workgroup
+constexpr int kCS = kHistKc + 8;      // LDS row stride in 16-bit elements (bank spread)
+constexpr int kLookCap = 2048;        // lookups bucketed per batch
+constexpr int kMaxChunks = kHistMaxRows / kHistKc;
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+template <int ST>
+struct Mma;
+
+template <>
+struct Mma<kBF16> {
+  typedef __attribute__((ext_vector_type(8))) __bf16 v8;
+  typedef __attribute__((ext_vector_type(2))) __bf16 v2;
+  static constexpr int kCountCap = 256;  // largest integer n with all of 0..n exact
+  static __device__ __forceinline__ f32x4 mma(const uint4& a, const uint4& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8, a),
+                                                   __builtin_bit_cast(v8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ void lds_add(uint32_t* word, bool high, float v) {
+    const v2 x = high ? v2{static_cast<__bf16>(0.0f), static_cast<__bf16>(v)}
+                      : v2{static_cast<__bf16>(v), static_cast<__bf16>(0.0f)};
+    __builtin_amdgcn_ds_atomic_fadd_v2bf16(
+        (__attribute__((address_space(3))) v2*)(word), x);
+  }
+};
+
+template <>
+struct Mma<kF16> {
+  typedef __attribute__((ext_vector_type(8))) _Float16 v8;
+  typedef __attribute__((ext_vector_type(2))) _Float16 v2;
+  static constexpr int kCountCap = 2048;
+  static __device__ __forceinline__ f32x4 mma(const uint4& a, const uint4& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8, a),
+                                                  __builtin_bit_cast(v8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ void lds_add(uint32_t* word, bool high, float v) {
+    const v2 x = high ? v2{static_cast<_Float16>(0.0f), static_cast<_Float16>(v)}
+                      : v2{static_cast<_Float16>(v), static_cast<_Float16>(0.0f)};
+    __builtin_amdgcn_ds_atomic_fadd_v2f16(
+        (__attribute__((address_space(3))) v2*)(word), x);
+  }
+};
+
+template <typename IT>
+__device__ __forceinline__ int64_t ld_index(const void* p, int64_t i) {
+  return static_cast<int64_t>(static_cast<const IT*>(p)[i]);
+}
+
+// One workgroup per (listed table, 64-row e tile, 64-column d tile): a
+// 64 x 64 block of W_t goes through LDS and leaves as rows of W_t^T.
+__global__ __launch_bounds__(kBlock) void hist_transpose(HistLaunch a) {
+  __shared__ uint16_t s[64][66];
+  const int per_table = a.etiles * a.dtiles;
+  const int h = blockIdx.x / per_table;
+  const int rem = blockIdx.x - h * per_table;
+  const int et = rem / a.dtiles, dt = rem - et * a.dtiles;
+  const HistTable ht = a.list[h];
+  const TableMeta m = a.meta[ht.table];
+  const int e0 = et * 64, d0 = dt * 64;
+  if (e0 >= ht.epad || d0 >= m.dim) return;
+  const uint16_t* w = static_cast<const uint16_t*>(a.weights) + m.woff;
+  const int tid = threadIdx.x;
+  for (int idx = tid; idx < 64 * 8; idx += kBlock) {
+    const int r = idx >> 3, c8 = (idx & 7) * 8;
+    const int e = e0 + r, d = d0 + c8;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (e < m.rows && d < m.dim)
+      v = *reinterpret_cast<const uint4*>(w + static_cast<int64_t>(e) * m.dim + d);
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s[r][c8 + 2 * j] = static_cast<uint16_t>(u[j] & 0xFFFFu);
+      s[r][c8 + 2 * j + 1] = static_cast<uint16_t>(u[j] >> 16);
+    }
+  }
+  __syncthreads();
+  uint16_t* wt = a.wt + ht.wt_off;
+  for (int idx = tid; idx < 64 * 8; idx += kBlock) {
+    const int dr = idx >> 3, c8 = (idx & 7) * 8;
+    const int d = d0 + dr;
+    if (d >= m.dim) continue;
+    uint32_t u[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      u[j] = static_cast<uint32_t>(s[c8 + 2 * j][dr]) |
+             (static_cast<uint32_t>(s[c8 + 2 * j + 1][dr]) << 16);
+    *reinterpret_cast<uint4*>(wt + static_cast<int64_t>(d) * ht.epad + e0 + c8) =
+        make_uint4(u[0], u[1], u[2], u[3]);
+  }
+}
+
+template <int ST, typename IT>
+__global__ __launch_bounds__(kBlock) void fwd_histogram(HistLaunch a) {
+  using M = Mma<ST>;
+  __shared__ __align__(16) uint16_t s_c[kHB * kCS];     // count tile [bag][row in chunk]
+  __shared__ __align__(16) uint16_t s_w[kDB * kCS];     // W^T chunk [column][row in chunk]
+  __shared__ uint32_t s_look[kLookCap];                 // bucketed: slot << 16 | row in chunk
+  __shared__ int32_t s_off[kHB + 1];
+  __shared__ uint32_t s_cnt[kMaxChunks], s_start[kMaxChunks], s_fill[kMaxChunks];
+
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int logical = xcd_contiguous_block(blockIdx.x, gridDim.x);
+  const int tiles = (a.B + kHB - 1) / kHB;
+  const int per_table = tiles * a.dtiles;
+  const int h = logical / per_table;
+  const int rem = logical - h * per_table;
+  const int dt = rem / tiles, tile = rem - dt * tiles;
+  const HistTable ht = a.list[h];
+  const TableMeta m = a.meta[ht.table];
+  const int d0 = dt * kDB;
+  if (d0 >= m.dim) return;  // whole workgroup
+  const int NT = min(kDB, m.dim - d0) >> 4;  // 16-column MFMA tiles
+  const int b0 = tile * kHB;
+  const int nb = min(kHB, a.B - b0);
+  const int64_t k0 = static_cast<int64_t>(ht.table) * a.B + b0;
+
+  for (int i = tid; i <= nb; i += kBlock) s_off[i] = static_cast<int32_t>(ld_index<IT>(a.offsets, k0 + i));
+  {
+    uint4* c4 = reinterpret_cast<uint4*>(s_c);
+    for (int i = tid; i < kHB * kCS / 8; i += kBlock) c4[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  __syncthreads();
+
+  const int lo = s_off[0], hi = s_off[nb];
+  const int nchunks = ht.epad / kHistKc;
+  const uint16_t* wt = a.wt + ht.wt_off + static_cast<int64_t>(d0) * ht.epad;
+  uint32_t* cw = reinterpret_cast<uint32_t*>(s_c);
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int p0 = lo; p0 < hi; p0 += kLookCap) {
+    const int pn = min(kLookCap, hi - p0);
+    if (tid < kMaxChunks) s_cnt[tid] = 0u, s_fill[tid] = 0u;
+    __syncthreads();
+    // bag slot, row and chunk of this thread's lookups
+    constexpr int PER = kLookCap / kBlock;
+    uint32_t ent[PER];
+    int chk[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int q = tid + j * kBlock;
+      chk[j] = -1;
+      if (q < pn) {
+        const int p = p0 + q;
+        int l = 0, r = nb;  // slot with s_off[slot] <= p < s_off[slot + 1]
+        while (r - l > 1) {
+          const int mid = (l + r) >> 1;
+          if (s_off[mid] <= p) l = mid; else r = mid;
+        }
+        const int len = s_off[l + 1] - s_off[l];
+        const int64_t x = ld_index<IT>(a.indices, p);
+        if (len <= M::kCountCap && x >= 0 && x < ht.epad) {
+          chk[j] = static_cast<int>(x) / kHistKc;
+          ent[j] = (static_cast<uint32_t>(l) << 16) | static_cast<uint32_t>(x & (kHistKc - 1));
+          atomicAdd(&s_cnt[chk[j]], 1u);
+        }
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t run = 0;
+      for (int c = 0; c < nchunks; ++c) s_start[c] = run, run += s_cnt[c];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (chk[j] >= 0) s_look[s_start[chk[j]] + atomicAdd(&s_fill[chk[j]], 1u)] = ent[j];
+    __syncthreads();
+
+    for (int c = 0; c < nchunks; ++c) {
+      const int cn = static_cast<int>(s_cnt[c]);
+      if (cn == 0) continue;  // uniform: the chunk adds nothing
+      const int cs = static_cast<int>(s_start[c]);
+      for (int i = tid; i < cn; i += kBlock) {
+        const uint32_t e = s_look[cs + i];
+        const int el = static_cast<int>(e >> 16) * kCS + static_cast<int>(e & 0xFFFFu);
+        M::lds_add(cw + (el >> 1), el & 1, 1.0f);
+      }
+      // W^T rows d0 .. d0 + 16*NT, columns of chunk c
+      for (int i = tid; i < NT * 16 * 8; i += kBlock) {
+        const int r = i >> 3, c8 = (i & 7) * 8;
+        *reinterpret_cast<uint4*>(s_w + r * kCS + c8) = *reinterpret_cast<const uint4*>(
+            wt + static_cast<int64_t>(r) * ht.epad + c * kHistKc + c8);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int ks = 0; ks < kHistKc / 32; ++ks) {
+        const int col = ks * 32 + (lane >> 4) * 8;
+        uint4 af[4], bf[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          af[mt] = *reinterpret_cast<const uint4*>(s_c + (wave * 64 + mt * 16 + (lane & 15)) * kCS + col);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          if (nt < NT) bf[nt] = *reinterpret_cast<const uint4*>(s_w + (nt * 16 + (lane & 15)) * kCS + col);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          if (nt < NT) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) acc[mt][nt] = M::mma(af[mt], bf[nt], acc[mt][nt]);
+          }
+      }
+      __syncthreads();
+      for (int i = tid; i < cn; i += kBlock) {
+        const uint32_t e = s_look[cs + i];
+        const int el = static_cast<int>(e >> 16) * kCS + static_cast<int>(e & 0xFFFFu);
+        M::lds_add(cw + (el >> 1), el & 1, -1.0f);
+      }
+    }
+    __syncthreads();
+  }
+
+  // results: lane holds rows 4*(lane/16) + r of each 16 x 16 tile, column lane % 16
+  float* const out0 = a.out + static_cast<int64_t>(b0) * a.sum_dims + m.doff + d0;
+  float* const obase = out0 + (lane & 15);
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int slot = wave * 64 + mt * 16 + (lane >> 4) * 4 + r;
+      if (slot < nb) {
+        const int len = s_off[slot + 1] - s_off[slot];
+        if (len <= M::kCountCap) {
+          const float sc = a.mean ? (len > 0 ? 1.0f / static_cast<float>(len) : 0.0f) : 1.0f;
+          float* o = obase + static_cast<int64_t>(slot) * a.sum_dims;
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt)
+            if (nt < NT) o[nt * 16] = acc[mt][nt][r] * sc;
+        }
+      }
+    }
+  }
+
+  // bags too long for exact 16-bit counts: plain gather, one wave per bag
+  const uint16_t* w = static_cast<const uint16_t*>(a.weights) + m.woff;
+  const int DN = NT * 16;
+  for (int slot = wave; slot < nb; slot += kWavesPerBlock) {
+    const int s0 = s_off[slot], s1 = s_off[slot + 1];
+    if (s1 - s0 <= M::kCountCap) continue;
+    if (lane < DN) {
+      float sum = 0.0f;
+      for (int p = s0; p < s1; ++p) {
+        const int64_t x = ld_index<IT>(a.indices, p);
+        const uint32_t u = w[x * m.dim + d0 + lane];
+        sum += ST == kBF16 ? bf16_lo(u) : f16_lo(u);
+      }
+      const float sc = a.mean ? 1.0f / static_cast<float>(s1 - s0) : 1.0f;
+      out0[static_cast<int64_t>(slot) * a.sum_dims + lane] = sum * sc;
+    }
+  }
+}
+
+template <int ST>
+hipError_t dispatch(const HistLaunch& a, hipStream_t s, dim3 grid) {
+  if (a.index64)
+    hipLaunchKernelGGL((fwd_histogram<ST, int64_t>), grid, dim3(kBlock), 0, s, a);
+  else
+    hipLaunchKernelGGL((fwd_histogram<ST, int32_t>), grid, dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_forward_histogram(const HistLaunch& a, hipStream_t stream, StageHook hook,
+                                    void* ctx) {
+  if (a.H <= 0 || a.B <= 0) return hipSuccess;
+  const int64_t tgrid = static_cast<int64_t>(a.H) * a.etiles * a.dtiles;
+  const int64_t tiles = (a.B + kHB - 1) / kHB;
+  const int64_t fgrid = static_cast<int64_t>(a.H) * tiles * a.dtiles;
+  if (tgrid > 0x7FFFFFFF || fgrid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(hist_transpose, dim3(static_cast<unsigned>(tgrid)), dim3(kBlock), 0, stream, a);
+  if (hook) hook(ctx, "hist_transpose");
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid(static_cast<unsigned>(fgrid));
+  e = a.dtype == kBF16 ? dispatch<kBF16>(a, stream, grid)
+                       : (a.dtype == kF16 ? dispatch<kF16>(a, stream, grid) : hipErrorInvalidValue);
+  if (hook) hook(ctx, "fwd_histogram");
+  return e;
+}
+
+}  // namespace tbe

@@ -74,6 +74,20 @@ def test_create_rejects_bad_configs_on_host(case):
     assert rc == 1 and out.value is None
 
 
+@pytest.mark.parametrize("dtype,rows,dims", [(0, [10, 20], [16, 16]),     # fp32 storage
+                                             (2, [10, 2000], [16, 16]),   # a table over 1024 rows
+                                             (1, [10, 20], [16, 24]),     # a dim not in 16-column tiles
+                                             (2, [10, 20], [16, 512])])   # a dim over 256
+def test_forced_histogram_on_an_ineligible_table_is_unsupported(dtype, rows, dims):
+    """The count-matrix forward only takes small fp16/bf16 tables; forcing it on any other
+    table fails at create, before any device call."""
+    lib = tbe.load()
+    cfg, keep = _cfg(rows, dims, dtype=dtype, flags=tbe.FLAG_FORCE_HISTOGRAM)
+    out = ctypes.c_void_p(123)
+    assert lib.tbe_create(ctypes.byref(cfg), 4096, None, ctypes.byref(out)) == 2
+    assert out.value is None
+
+
 def test_null_handle_calls_are_rejected():
     lib = tbe.load()
     n = ctypes.c_size_t(0)

@@ -24,12 +24,12 @@ def _say(*a):
 
 
 def parity(spec, seed=0, steps=2, bag_sample=None, row_sample=None, index_dtype=torch.int64,
-           threshold=None, batches=None):
+           threshold=None, batches=None, flags=0):
     """Forward and backward_update for `steps` steps, each checked against the reference,
     which advances its own copy of weights and state."""
-    _say(f"[parity] {spec.name} dtype={spec.dtype} seed={seed} thr={threshold}")
+    _say(f"[parity] {spec.name} dtype={spec.dtype} seed={seed} thr={threshold} flags={flags}")
     pb = make_problem(spec, seed=seed, index_dtype=index_dtype,
-                      batch=None if batches is None else batches[0])
+                      batch=None if batches is None else batches[0], flags=flags)
     if threshold is not None:
         pb.op.set_option(tbe.OPTION_LONG_RUN_THRESHOLD, threshold)
     W_host = workloads.storage_numpy(pb.W).copy()

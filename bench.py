@@ -32,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA16_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16 matrix-core peak of the MI355X
 METRIC = "TBE fwd+bwd lookups/sec and achieved HBM GB/s (% of peak) at 1 MI355X"
 
 
@@ -43,6 +44,9 @@ def parse():
     p.add_argument("--workload", type=int, default=2, help="benchmark workload 1..5")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU baseline")
+    p.add_argument("--forward", choices=("auto", "gather", "histogram"), default="auto",
+                   help="auto: count-matrix forward for the tables that qualify; gather: never; "
+                        "histogram: force it (every table must qualify)")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain device copy of known size (counter calibration)")
     return p.parse_args()
@@ -78,7 +82,7 @@ def group_lanes(spec):
     return min(64, 1 << (c - 1).bit_length())
 
 
-def algorithmic_bytes(spec, batch, long_threshold=256, chunk=256, super_chunk=32):
+def algorithmic_bytes(spec, batch, long_threshold=256, chunk=256):
     """Bytes the method itself must move, per kernel (one launch each), for one batch.
 
     forward (per lookup)  row read D*s + id 8 (+ weight 4); (per bag) offset 8 + output 4*D
@@ -87,8 +91,7 @@ def algorithmic_bytes(spec, batch, long_threshold=256, chunk=256, super_chunk=32
       seg_short           runs a lane group takes alone (at most Gs lookups)
       seg_wg              longer runs below the long-run threshold, and the lookups of long
                           runs (+ one 4*D partial write per 256-lookup chunk)
-      seg_reduce2         32 partial reads + 1 write per level-2 partial (runs of > 32 chunks)
-      seg_finalize        partial reads + the per-row terms of long runs
+      seg_finalize        per long run: its chunk partials read, the row terms
     """
     import numpy as np
     s = {"f32": 4, "f16": 2, "bf16": 2}[spec.dtype]
@@ -109,21 +112,30 @@ def algorithmic_bytes(spec, batch, long_threshold=256, chunk=256, super_chunk=32
     long_ = cnt >= long_threshold
     medium = ~short & ~long_
     nch = -(-cnt // chunk)
-    n2 = np.where(nch > super_chunk, -(-nch // super_chunk), 0)
     seg_short = float((cnt[short] * per_look[short] + per_row[short]).sum())
     seg_wg = float((cnt[medium] * per_look[medium] + per_row[medium]).sum()
                    + (cnt[long_] * per_look[long_] + nch[long_] * 4 * D[long_]).sum())
-    two = long_ & (n2 > 0)
-    seg_r2 = float(((nch[two] + n2[two]) * 4 * D[two]).sum())
-    seg_final = float((np.where(n2 > 0, n2, nch)[long_] * 4 * D[long_] + per_row[long_]).sum())
+    seg_final = float((nch[long_] * 4 * D[long_] + per_row[long_]).sum())
     N, U, nbags = int(lens.sum()), int(cnt.size), spec.T * spec.B
     # grouping front: workspace clear (a few KB), linearize (ids 8 + offsets, key/value
     # writes 8, record 8), per radix pass the key+value read and scatter 16 per lookup,
     # run-length encoding keys read 4 + unique id/start writes 8 per run
     front = {"linearize_kernel": float(N * (8 + 8 + rec) + 8 * nbags),
              "radix_pass": float(16 * N), "rle_kernel": float(4 * N + 8 * U)}
-    return {"fwd_gather_pool": fwd, "seg_short": seg_short, "seg_wg": seg_wg,
-            "seg_reduce2": seg_r2, "seg_finalize": seg_final, **front}, {"N": int(lens.sum()), "U": int(cnt.size),
+    # count-matrix forward (tables that qualify): ids 8 + per bag offset 8 + output 4*D, one
+    # read of each table; the dense product does 2*B*E_t*D_t flops per table.  The W^T
+    # staging kernel reads each table and writes its transposed copy.
+    s16 = 2
+    hist = [t for t in range(spec.T) if spec.dtype != "f32" and spec.rows[t] <= 1024
+            and spec.dims[t] <= 256 and spec.dims[t] % 16 == 0]
+    hist_n = sum(int(lens[t * spec.B:(t + 1) * spec.B].sum()) for t in hist)
+    hist_bytes = float(8 * hist_n + sum(8 * spec.B + 4 * spec.B * spec.dims[t]
+                                        + s16 * spec.rows[t] * spec.dims[t] for t in hist))
+    hist_flops = float(sum(2 * spec.B * spec.rows[t] * spec.dims[t] for t in hist))
+    hist_t = float(sum(2 * s16 * spec.rows[t] * spec.dims[t] for t in hist))
+    return {"fwd_gather_pool": fwd, "fwd_histogram": hist_bytes, "hist_transpose": hist_t,
+            "fwd_histogram_flops": hist_flops, "seg_short": seg_short, "seg_wg": seg_wg,
+            "seg_finalize": seg_final, **front}, {"N": int(lens.sum()), "U": int(cnt.size),
                                          "long_run_share": float(cnt[long_].sum() / max(1, cnt.sum())),
                                          "max_run": int(cnt.max()) if cnt.size else 0}
 
@@ -208,7 +220,10 @@ def main():
     W_host = workloads.storage_numpy(W).copy() if not args.no_cpu_baseline else None
     state = torch.zeros(spec.sum_rows, dtype=torch.float32, device=dev) \
         if spec.optimizer == "rowwise_adagrad" else None
-    op = tbe.TBE(spec.rows, spec.dims, W, state, pooling=spec.pooling, optimizer=spec.optimizer)
+    fwd_flags = {"auto": 0, "gather": tbe.FLAG_NO_HISTOGRAM,
+                 "histogram": tbe.FLAG_FORCE_HISTOGRAM}[args.forward]
+    op = tbe.TBE(spec.rows, spec.dims, W, state, pooling=spec.pooling, optimizer=spec.optimizer,
+                 flags=fwd_flags)
     nrot = 4
     host_batches = [workloads.batch(spec, seed=0, step=s) for s in range(nrot)]
     batches = []
@@ -265,12 +280,20 @@ def main():
     stats = alg[0][1]
     kernels = {}
     for k, b in alg_bytes.items():
-        if k in avg_us:
+        if k == "fwd_histogram" and k in avg_us:
+            fl = alg_bytes["fwd_histogram_flops"]
+            kernels[k] = {"avg_us": round(avg_us[k], 2), "alg_bytes": b,
+                          "alg_GBps": round(b / (avg_us[k] * 1e-6) / 1e9, 1),
+                          "pct_of_peak": round(100 * b / (avg_us[k] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 1),
+                          "alg_flops": fl, "TFLOPs": round(fl / (avg_us[k] * 1e-6) / 1e12, 1),
+                          "pct_of_mfma_peak": round(100 * fl / (avg_us[k] * 1e-6) / 1e12
+                                                    / MFMA16_PEAK_TFLOPS, 1)}
+        elif k in avg_us:
             kernels[k] = {"avg_us": round(avg_us[k], 2), "alg_bytes": b,
                           "alg_GBps": round(b / (avg_us[k] * 1e-6) / 1e9, 1),
                           "pct_of_peak": round(100 * b / (avg_us[k] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 1)}
     # the whole segment reduce + update (all of its kernels, one launch each per step)
-    seg_names = [k for k in ("seg_short", "seg_wg", "seg_reduce2", "seg_finalize") if k in avg_us]
+    seg_names = [k for k in ("seg_short", "seg_wg", "seg_finalize") if k in avg_us]
     if seg_names:
         sb, su = sum(alg_bytes[k] for k in seg_names), sum(avg_us[k] for k in seg_names)
         kernels["segment_reduce_update"] = {
@@ -278,7 +301,15 @@ def main():
             "pct_of_peak": round(100 * sb / (su * 1e-6) / 1e9 / HBM_PEAK_GBPS, 1)}
     dominant = max(avg_us, key=lambda k: avg_us[k] * steps_per_launch[k])
     workload_tag = f"workload{args.workload}"
-    if dominant in alg_bytes:
+    if dominant == "fwd_histogram" and alg_bytes.get("fwd_histogram_flops"):
+        tflops = alg_bytes["fwd_histogram_flops"] / (avg_us[dominant] * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(tflops, 1),
+                    "peak": MFMA16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tflops / MFMA16_PEAK_TFLOPS, 4),
+                    "traffic": committed_traffic(dominant, f"workload{args.workload}"),
+                    "alg_flops_per_launch": alg_bytes["fwd_histogram_flops"],
+                    "avg_launch_us": round(avg_us[dominant], 2)}
+    elif dominant in alg_bytes:
         achieved = alg_bytes[dominant] / (avg_us[dominant] * 1e-6) / 1e9
         traffic = committed_traffic(dominant, workload_tag)
         roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
@@ -311,6 +342,7 @@ def main():
                   "bf16": "bf16 storage, f32 accumulate"}[spec.dtype],
         "data": "synthetic (seeded generator, 4 rotated batches resident in HBM)",
         "config": {"workload": spec.name, "tables": spec.T, "bags_per_table": spec.B,
+                   "forward": args.forward,
                    "lookups_per_step": stats["N"], "unique_rows_batch0": stats["U"],
                    "long_run_share_batch0": round(stats["long_run_share"], 3),
                    "max_run_batch0": stats["max_run"]},

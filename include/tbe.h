@@ -125,9 +125,9 @@ typedef enum {
   /* Runs with at least this many lookups take the split-accumulation path
    * (default 256).  Changes only the fp32 summation order. */
   TBE_OPTION_LONG_RUN_THRESHOLD = 1,
-  /* 1: record a HIP event before every call and after every kernel it
-   * launches, on the call's stream, readable with tbe_stage_times; 0
-   * (default): off. */
+  /* 1: every kernel the calls launch records its own start and end in a pair
+   * of HIP events (hipExtLaunchKernelGGL), readable with tbe_stage_times;
+   * 0 (default): off. */
   TBE_OPTION_PROFILE = 2
 } tbe_option;
 
@@ -168,8 +168,8 @@ tbe_status tbe_set_option(tbe_handle* handle, int32_t option, int64_t value);
 
 /* With TBE_OPTION_PROFILE on: waits for the recorded events, then writes, for
  * every kernel launched by the calls made since the last read (in launch
- * order, at most capacity), its duration in milliseconds (event to event on
- * the call's stream) to ms and the kernel's static name to names (may be
+ * order, at most capacity), its duration in milliseconds (from the kernel's
+ * start to its end, host gaps excluded) to ms and the kernel's static name to names (may be
  * NULL); *count receives the number written.  The recorded events are then
  * dropped. */
 tbe_status tbe_stage_times(tbe_handle* handle, float* ms, const char** names, int32_t capacity,

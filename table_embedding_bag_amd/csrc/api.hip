@@ -43,17 +43,17 @@ struct tbe_handle {
   int32_t hist_etiles = 0, hist_dtiles = 0;
   int64_t wt_elems = 0;
   int64_t long_threshold = 256;
-  // profiling: events recorded at call starts (name == nullptr) and after
-  // each kernel (name of that kernel), kept until tbe_stage_times reads them.
+  // profiling: pairs of events handed to timed kernel launches (start and end
+  // of that kernel), kept until tbe_stage_times reads them
   bool profile = false;
   std::vector<hipEvent_t> pool;
-  std::vector<std::pair<hipEvent_t, const char*>> marks;
+  std::vector<std::pair<size_t, const char*>> timed;  // start event index in pool, kernel name
+  size_t used = 0;
 };
 
 namespace {
 
 constexpr int kChunk = 256;       // lookups per level-1 partial of a long run
-constexpr int kSuperChunk = 32;   // level-1 partials per level-2 partial
 constexpr size_t kAlign = 256;
 
 int ceil_log2(int64_t x) {
@@ -74,27 +74,19 @@ tbe_status from_hip(hipError_t e) { return e == hipSuccess ? TBE_OK : TBE_ERR_HI
 
 constexpr size_t kMaxMarks = size_t{1} << 16;
 
-void prof_record(tbe_handle* h, hipStream_t s, const char* name) {
-  if (!h->profile || h->marks.size() >= kMaxMarks) return;
-  if (h->pool.size() <= h->marks.size()) {
+bool take_events(void* ctx, const char* name, hipEvent_t* start, hipEvent_t* stop) {
+  auto* h = static_cast<tbe_handle*>(ctx);
+  if (!h->profile || h->timed.size() >= kMaxMarks) return false;
+  while (h->pool.size() < h->used + 2) {
     hipEvent_t e;
-    if (hipEventCreate(&e) != hipSuccess) return;
+    if (hipEventCreate(&e) != hipSuccess) return false;
     h->pool.push_back(e);
   }
-  hipEvent_t e = h->pool[h->marks.size()];
-  if (hipEventRecord(e, s) == hipSuccess) h->marks.emplace_back(e, name);
-}
-
-void prof_begin(tbe_handle* h, hipStream_t s) { prof_record(h, s, nullptr); }
-
-struct HookCtx {
-  tbe_handle* h;
-  hipStream_t s;
-};
-
-void prof_mark(void* ctx, const char* name) {
-  auto* c = static_cast<HookCtx*>(ctx);
-  prof_record(c->h, c->s, name);
+  *start = h->pool[h->used];
+  *stop = h->pool[h->used + 1];
+  h->timed.emplace_back(h->used, name);
+  h->used += 2;
+  return true;
 }
 
 // --- validation kernel -----------------------------------------------------
@@ -181,14 +173,13 @@ struct Carve {
 struct BwdPlan {
   int64_t n = 0;
   int sort_tiles = 0, rle_tiles = 0;
-  int64_t long_ub = 0, chunks_ub = 0, items1_ub = 0, items2_ub = 0;
+  int64_t long_ub = 0, chunks_ub = 0, items1_ub = 0;
   int32_t pstride = 0;
   int32_t nch = 1, gshift = 0;
   bool vec = false;
   int passes = 1;
   int64_t zero_words = 0;
-  size_t o_keys[2], o_vals[2], o_rec, o_zero, o_uniq, o_start, o_longs, o_items1, o_items2, o_p1,
-      o_p2;
+  size_t o_keys[2], o_vals[2], o_rec, o_zero, o_uniq, o_start, o_longs, o_items1, o_p1;
   size_t bytes = 0;
 };
 
@@ -216,13 +207,12 @@ bool plan_backward(const tbe_handle* h, int64_t n, bool vec, BwdPlan* p) {
   p->sort_tiles = static_cast<int>((n + sort_tile - 1) / sort_tile);
   p->rle_tiles = static_cast<int>((n + kRleTile - 1) / kRleTile);
   p->passes = (h->key_bits + kRadixBits - 1) / kRadixBits;
-  p->zero_words = kNumCounters + kNumTickets + int64_t{kMaxRadixPasses} * kRadix +
-                  int64_t{p->passes} * p->sort_tiles * kRadix + p->rle_tiles;
-  const SegmentBounds ub = segment_bounds(n, h->long_threshold, kChunk, kSuperChunk, p->gshift);
+  const SegmentBounds ub = segment_bounds(n, h->long_threshold, kChunk, p->gshift);
   p->long_ub = ub.longs;
   p->chunks_ub = ub.chunks;
   p->items1_ub = ub.items1;
-  p->items2_ub = ub.items2;
+  p->zero_words = kNumCounters + kNumTickets + int64_t{kMaxRadixPasses} * kRadix +
+                  int64_t{p->passes} * p->sort_tiles * kRadix + p->rle_tiles;
   Carve cv;
   for (int i = 0; i < 2; ++i) {
     p->o_keys[i] = cv.take(4 * static_cast<size_t>(n));
@@ -234,9 +224,7 @@ bool plan_backward(const tbe_handle* h, int64_t n, bool vec, BwdPlan* p) {
   p->o_start = cv.take(4 * static_cast<size_t>(n + 1));
   p->o_longs = cv.take(16 * static_cast<size_t>(p->long_ub));
   p->o_items1 = cv.take(8 * static_cast<size_t>(p->items1_ub));
-  p->o_items2 = cv.take(8 * static_cast<size_t>(p->items2_ub));
   p->o_p1 = cv.take(4 * static_cast<size_t>(p->pstride) * p->chunks_ub);
-  p->o_p2 = cv.take(4 * static_cast<size_t>(p->pstride) * p->items2_ub);
   p->bytes = cv.off;
   return true;
 }
@@ -425,19 +413,19 @@ tbe_status tbe_stage_times(tbe_handle* h, float* ms, const char** names, int32_t
                            int32_t* count) {
   if (!h || !count || (capacity > 0 && !ms)) return TBE_ERR_INVALID_ARGUMENT;
   *count = 0;
-  if (h->marks.empty()) return TBE_OK;
-  if (hipEventSynchronize(h->marks.back().first) != hipSuccess) return TBE_ERR_HIP;
+  if (h->timed.empty()) return TBE_OK;
+  if (hipEventSynchronize(h->pool[h->timed.back().first + 1]) != hipSuccess) return TBE_ERR_HIP;
   int n = 0;
-  for (size_t i = 1; i < h->marks.size() && n < capacity; ++i) {
-    if (!h->marks[i].second) continue;  // start of the next call
+  for (size_t i = 0; i < h->timed.size() && n < capacity; ++i) {
     float t = 0.0f;
-    if (hipEventElapsedTime(&t, h->marks[i - 1].first, h->marks[i].first) != hipSuccess)
-      return TBE_ERR_HIP;
+    const size_t e = h->timed[i].first;
+    if (hipEventElapsedTime(&t, h->pool[e], h->pool[e + 1]) != hipSuccess) return TBE_ERR_HIP;
     ms[n] = t;
-    if (names) names[n] = h->marks[i].second;
+    if (names) names[n] = h->timed[i].second;
     ++n;
   }
-  h->marks.clear();
+  h->timed.clear();
+  h->used = 0;
   *count = n;
   return TBE_OK;
 }
@@ -470,8 +458,8 @@ tbe_status tbe_forward(tbe_handle* h, int32_t B, const void* indices, const void
       st = run_validation(h, B, indices, offsets, index_dtype, n, s);
       if (st != TBE_OK) return st;
     }
-    HookCtx hc{h, s};
-    prof_begin(h, s);
+    KernelTimer timer{h, take_events};
+    const KernelTimer* kt = h->profile ? &timer : nullptr;
     // Count-matrix forward for the eligible tables unless lookups carry
     // per-sample weights; the gather kernel covers every other table.
     const bool hist = !psw && !h->hist_host.empty();
@@ -492,7 +480,7 @@ tbe_status tbe_forward(tbe_handle* h, int32_t B, const void* indices, const void
       ha.mean = h->pooling == TBE_POOL_MEAN;
       ha.dtype = h->dtype;
       ha.index64 = index_dtype == TBE_I64;
-      const hipError_t e = launch_forward_histogram(ha, s, h->profile ? prof_mark : nullptr, &hc);
+      const hipError_t e = launch_forward_histogram(ha, s, kt);
       if (e != hipSuccess) return from_hip(e);
       if (h->gather_host.empty()) return TBE_OK;
     }
@@ -513,8 +501,7 @@ tbe_status tbe_forward(tbe_handle* h, int32_t B, const void* indices, const void
     a.dtype = h->dtype;
     a.index64 = index_dtype == TBE_I64;
     a.vec = h->fwd_vec;
-    const hipError_t e = launch_forward_gather(a, s);
-    prof_mark(&hc, "fwd_gather_pool");
+    const hipError_t e = launch_forward_gather(a, s, kt);
     return from_hip(e);
   } catch (...) {
     return TBE_ERR_OUT_OF_MEMORY;
@@ -558,8 +545,8 @@ tbe_status tbe_backward_update(tbe_handle* h, int32_t B, const void* indices, co
       st = run_validation(h, B, indices, offsets, index_dtype, n, s);
       if (st != TBE_OK) return st;
     }
-    HookCtx hc{h, s};
-    prof_begin(h, s);
+    KernelTimer timer{h, take_events};
+    const KernelTimer* kt = h->profile ? &timer : nullptr;
 
     char* w = static_cast<char*>(workspace);
     BackwardLaunch a{};
@@ -587,7 +574,6 @@ tbe_status tbe_backward_update(tbe_handle* h, int32_t B, const void* indices, co
     a.pstride = p.pstride;
     a.long_threshold = static_cast<int32_t>(std::min<int64_t>(h->long_threshold, 0x7FFFFFFF));
     a.chunk = kChunk;
-    a.super_chunk = kSuperChunk;
     a.lr = lr;
     a.eps = eps;
     if (runs) {
@@ -611,19 +597,16 @@ tbe_status tbe_backward_update(tbe_handle* h, int32_t B, const void* indices, co
     b.run_start = reinterpret_cast<uint32_t*>(w + p.o_start);
     b.longs = reinterpret_cast<uint4*>(w + p.o_longs);
     b.items1 = reinterpret_cast<uint2*>(w + p.o_items1);
-    b.items2 = reinterpret_cast<uint2*>(w + p.o_items2);
     b.partial1 = reinterpret_cast<float*>(w + p.o_p1);
-    b.partial2 = reinterpret_cast<float*>(w + p.o_p2);
 
-    hipError_t e = launch_linearize(a, s);
+    hipError_t e = launch_linearize(a, s, kt);
     if (e != hipSuccess) return TBE_ERR_HIP;
-    prof_mark(&hc, "linearize_kernel");
     int sorted = 0;
-    e = launch_radix_sort(a, s, &sorted, h->profile ? prof_mark : nullptr, &hc);
+    e = launch_radix_sort(a, s, &sorted, kt);
     if (e != hipSuccess) return TBE_ERR_HIP;
-    e = launch_run_length_encode(a, b.keys[sorted], s, h->profile ? prof_mark : nullptr, &hc);
+    e = launch_run_length_encode(a, b.keys[sorted], s, kt);
     if (e != hipSuccess) return TBE_ERR_HIP;
-    e = launch_segment_reduce_update(a, b.vals[sorted], s, h->profile ? prof_mark : nullptr, &hc);
+    e = launch_segment_reduce_update(a, b.vals[sorted], s, kt);
     return from_hip(e);
   } catch (...) {
     return TBE_ERR_OUT_OF_MEMORY;

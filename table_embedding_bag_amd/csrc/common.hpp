@@ -2,6 +2,7 @@
 // TBE library.  Everything here is internal; the public interface is tbe.h.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -172,8 +173,23 @@ __device__ __forceinline__ void narrow_store(void* base, int64_t e, const float*
 // Launch interfaces (host side, implemented next to their kernels)
 // ---------------------------------------------------------------------------
 
-// Stage hooks let the host record profiling events between launches.
-typedef void (*StageHook)(void* ctx, const char* stage_name);
+// Kernel timing for profiling: when a timer is given and hands out a pair of
+// events, the launch records the kernel's own start and end in them
+// (hipExtLaunchKernelGGL), so host gaps between launches are not counted.
+struct KernelTimer {
+  void* ctx;
+  bool (*take)(void* ctx, const char* kernel_name, hipEvent_t* start, hipEvent_t* stop);
+};
+
+template <typename... KArgs, typename... Args>
+inline void launch_timed(const KernelTimer* kt, const char* name, void (*kernel)(KArgs...),
+                         dim3 grid, dim3 block, uint32_t shmem, hipStream_t s, Args... args) {
+  hipEvent_t e0, e1;
+  if (kt && kt->take(kt->ctx, name, &e0, &e1))
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, e0, e1, 0u, static_cast<KArgs>(args)...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, shmem, s, static_cast<KArgs>(args)...);
+}
 
 struct ForwardLaunch {
   const void* weights;
@@ -191,7 +207,8 @@ struct ForwardLaunch {
   int32_t vec;              // 16-byte row chunks (else one element per lane)
   const int32_t* table_list;  // tables to cover (T entries), or null for tables 0..T-1
 };
-hipError_t launch_forward_gather(const ForwardLaunch& a, hipStream_t stream);
+hipError_t launch_forward_gather(const ForwardLaunch& a, hipStream_t stream,
+                                 const KernelTimer* kt);
 
 // Count-matrix forward of small 16-bit tables.  Each such table has a
 // transposed, zero-padded copy W^T[d][e] (e < epad, epad a multiple of
@@ -219,8 +236,8 @@ struct HistLaunch {
   int32_t dtype;            // kF16 or kBF16
   int32_t index64;
 };
-hipError_t launch_forward_histogram(const HistLaunch& a, hipStream_t stream, StageHook hook,
-                                    void* ctx);
+hipError_t launch_forward_histogram(const HistLaunch& a, hipStream_t stream,
+                                    const KernelTimer* kt);
 
 // Device workspace of the backward, carved by the host.
 struct BackwardBuffers {
@@ -239,15 +256,13 @@ struct BackwardBuffers {
   uint32_t* unique_keys;    // [N]
   uint32_t* run_start;      // [N + 1]
   uint2* items1;            // workgroup items: {run, medium flag} or {long run, chunk}
-  uint2* items2;            // {long run, super-chunk}
-  uint4* longs;             // {run, first chunk partial, chunk count, first level-2 partial}
+  uint4* longs;             // {run, first chunk partial, chunk count, 0}
   float* partial1;          // [chunks cap, pstride]
-  float* partial2;          // [items2 cap, pstride]
 };
 
 // Device counters of the backward (zeroed at the start of every call).
 // kCntError is raised if a look-back wait ever gives up (results then invalid).
-enum { kCntUnique = 0, kCntLong = 1, kCntItems1 = 2, kCntItems2 = 3, kCntChunks = 4,
+enum { kCntUnique = 0, kCntLong = 1, kCntItems1 = 2, kCntChunks = 4,
        kCntError = 5, kNumCounters = 8 };
 constexpr int kMaxRadixPasses = 4;       // 32-bit keys, 8-bit digits
 constexpr int kNumTickets = 8;           // kMaxRadixPasses radix passes + the RLE
@@ -257,10 +272,9 @@ int sort_keys_per_thread(int64_t n);
 
 // Upper bounds of the segment work lists for a batch of n lookups.
 struct SegmentBounds {
-  int64_t longs, chunks, items1, items2;
+  int64_t longs, chunks, items1;
 };
-SegmentBounds segment_bounds(int64_t n, int64_t long_threshold, int chunk, int super_chunk,
-                             int gshift);
+SegmentBounds segment_bounds(int64_t n, int64_t long_threshold, int chunk, int gshift);
 
 struct BackwardLaunch {
   const void* indices;
@@ -282,7 +296,6 @@ struct BackwardLaunch {
   int32_t pstride;          // floats per partial row
   int32_t long_threshold;   // runs at least this long use split accumulation
   int32_t chunk;            // lookups per level-1 partial
-  int32_t super_chunk;      // level-1 partials per level-2 partial
   float lr, eps;
   int32_t* out_unique;      // optional run outputs
   int32_t* out_lengths;
@@ -290,15 +303,15 @@ struct BackwardLaunch {
   BackwardBuffers buf;
 };
 
-hipError_t launch_linearize(const BackwardLaunch& a, hipStream_t stream);
+hipError_t launch_linearize(const BackwardLaunch& a, hipStream_t stream, const KernelTimer* kt);
 // Sorts buf.keys[0]/vals[0]; returns the index (0 or 1) of the buffer pair
 // that holds the sorted result.
 hipError_t launch_radix_sort(const BackwardLaunch& a, hipStream_t stream, int* result_buffer,
-                             StageHook hook, void* ctx);
+                             const KernelTimer* kt);
 hipError_t launch_run_length_encode(const BackwardLaunch& a, const uint32_t* sorted_keys,
-                                    hipStream_t stream, StageHook hook, void* ctx);
+                                    hipStream_t stream, const KernelTimer* kt);
 hipError_t launch_segment_reduce_update(const BackwardLaunch& a, const uint32_t* sorted_vals,
-                                        hipStream_t stream, StageHook hook, void* ctx);
+                                        hipStream_t stream, const KernelTimer* kt);
 
 // Row loads a forward lane group issues before it accumulates (shared by the
 // kernel and the host planner that sizes sub-waves from the mean bag length).

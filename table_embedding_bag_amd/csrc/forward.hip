@@ -141,38 +141,41 @@ __global__ __launch_bounds__(kBlock) void fwd_gather_pool(ForwardLaunch a) {
 }
 
 template <int ST, typename IT>
-hipError_t dispatch_vec_psw(const ForwardLaunch& a, hipStream_t s, dim3 grid) {
+hipError_t dispatch_vec_psw(const ForwardLaunch& a, hipStream_t s, dim3 grid,
+                            const KernelTimer* kt) {
   if (a.vec) {
     if (a.psw)
-      hipLaunchKernelGGL((fwd_gather_pool<ST, IT, true, true>), grid, dim3(kBlock), 0, s, a);
+      launch_timed(kt, "fwd_gather_pool", fwd_gather_pool<ST, IT, true, true>, grid, dim3(kBlock), 0, s, a);
     else
-      hipLaunchKernelGGL((fwd_gather_pool<ST, IT, true, false>), grid, dim3(kBlock), 0, s, a);
+      launch_timed(kt, "fwd_gather_pool", fwd_gather_pool<ST, IT, true, false>, grid, dim3(kBlock), 0, s, a);
   } else {
     if (a.psw)
-      hipLaunchKernelGGL((fwd_gather_pool<ST, IT, false, true>), grid, dim3(kBlock), 0, s, a);
+      launch_timed(kt, "fwd_gather_pool", fwd_gather_pool<ST, IT, false, true>, grid, dim3(kBlock), 0, s, a);
     else
-      hipLaunchKernelGGL((fwd_gather_pool<ST, IT, false, false>), grid, dim3(kBlock), 0, s, a);
+      launch_timed(kt, "fwd_gather_pool", fwd_gather_pool<ST, IT, false, false>, grid, dim3(kBlock), 0, s, a);
   }
   return hipGetLastError();
 }
 
 template <int ST>
-hipError_t dispatch_index(const ForwardLaunch& a, hipStream_t s, dim3 grid) {
-  return a.index64 ? dispatch_vec_psw<ST, int64_t>(a, s, grid)
-                   : dispatch_vec_psw<ST, int32_t>(a, s, grid);
+hipError_t dispatch_index(const ForwardLaunch& a, hipStream_t s, dim3 grid,
+                          const KernelTimer* kt) {
+  return a.index64 ? dispatch_vec_psw<ST, int64_t>(a, s, grid, kt)
+                   : dispatch_vec_psw<ST, int32_t>(a, s, grid, kt);
 }
 
 }  // namespace
 
-hipError_t launch_forward_gather(const ForwardLaunch& a, hipStream_t stream) {
+hipError_t launch_forward_gather(const ForwardLaunch& a, hipStream_t stream,
+                                 const KernelTimer* kt) {
   const int64_t blocks = static_cast<int64_t>(a.T) * a.tiles_per_table;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const dim3 grid(static_cast<unsigned>(blocks));
   switch (a.dtype) {
-    case kF32: return dispatch_index<kF32>(a, stream, grid);
-    case kF16: return dispatch_index<kF16>(a, stream, grid);
-    case kBF16: return dispatch_index<kBF16>(a, stream, grid);
+    case kF32: return dispatch_index<kF32>(a, stream, grid, kt);
+    case kF16: return dispatch_index<kF16>(a, stream, grid, kt);
+    case kBF16: return dispatch_index<kBF16>(a, stream, grid, kt);
     default: return hipErrorInvalidValue;
   }
 }

@@ -295,31 +295,30 @@ __global__ __launch_bounds__(kBlock) void fwd_histogram(HistLaunch a) {
 }
 
 template <int ST>
-hipError_t dispatch(const HistLaunch& a, hipStream_t s, dim3 grid) {
+hipError_t dispatch(const HistLaunch& a, hipStream_t s, dim3 grid, const KernelTimer* kt) {
   if (a.index64)
-    hipLaunchKernelGGL((fwd_histogram<ST, int64_t>), grid, dim3(kBlock), 0, s, a);
+    launch_timed(kt, "fwd_histogram", fwd_histogram<ST, int64_t>, grid, dim3(kBlock), 0, s, a);
   else
-    hipLaunchKernelGGL((fwd_histogram<ST, int32_t>), grid, dim3(kBlock), 0, s, a);
+    launch_timed(kt, "fwd_histogram", fwd_histogram<ST, int32_t>, grid, dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_forward_histogram(const HistLaunch& a, hipStream_t stream, StageHook hook,
-                                    void* ctx) {
+hipError_t launch_forward_histogram(const HistLaunch& a, hipStream_t stream,
+                                    const KernelTimer* kt) {
   if (a.H <= 0 || a.B <= 0) return hipSuccess;
   const int64_t tgrid = static_cast<int64_t>(a.H) * a.etiles * a.dtiles;
   const int64_t tiles = (a.B + kHB - 1) / kHB;
   const int64_t fgrid = static_cast<int64_t>(a.H) * tiles * a.dtiles;
   if (tgrid > 0x7FFFFFFF || fgrid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(hist_transpose, dim3(static_cast<unsigned>(tgrid)), dim3(kBlock), 0, stream, a);
-  if (hook) hook(ctx, "hist_transpose");
+  launch_timed(kt, "hist_transpose", hist_transpose, dim3(static_cast<unsigned>(tgrid)),
+               dim3(kBlock), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid(static_cast<unsigned>(fgrid));
-  e = a.dtype == kBF16 ? dispatch<kBF16>(a, stream, grid)
-                       : (a.dtype == kF16 ? dispatch<kF16>(a, stream, grid) : hipErrorInvalidValue);
-  if (hook) hook(ctx, "fwd_histogram");
+  e = a.dtype == kBF16 ? dispatch<kBF16>(a, stream, grid, kt)
+                       : (a.dtype == kF16 ? dispatch<kF16>(a, stream, grid, kt) : hipErrorInvalidValue);
   return e;
 }
 

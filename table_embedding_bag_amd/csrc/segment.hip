@@ -19,26 +19,28 @@
 // flight per run:
 //   seg_short     one lane group (Gs lanes = one gradient row of 16-byte
 //                 chunks) per run of at most Gs lookups: every lane prefetches
-//                 one lookup, the group then keeps 8 gradient rows in flight
-//                 and updates the row.  Most runs are this short.  Longer runs
-//                 are queued (atomic counters give each a contiguous range of
-//                 work items).
+//                 one lookup, the group gathers the run's gradient rows with 2
+//                 or 4 in flight (matched to the run's length), sums them in
+//                 fp32 and updates the row.  Most runs are this short.  Longer
+//                 runs are queued as workgroup items; each wave reserves its
+//                 queue slots with one atomic per counter.
 //   seg_wg        one workgroup per queued item: a medium run (shorter than the
 //                 long-run threshold, streamed in one pass and updated at once)
 //                 or a 256-lookup chunk of a long run (split accumulation: an
 //                 fp32 partial sum per chunk).  The workgroup stages 256 lookups
 //                 in LDS and its 256/Gs lane groups keep 4 rows each in flight;
 //                 the groups' sums are added in LDS in a fixed order.
-//   seg_reduce2   long runs with more than 32 chunks: sums of 32 consecutive
-//                 chunk partials.
-//   seg_finalize  per long run: its partials summed in chunk order, then the
-//                 update.
+//   seg_finalize  one workgroup per long run: its partials summed in a fixed
+//                 order, then the update.
 // Summation order never depends on scheduling (no float atomics), so results
-// are reproducible bit for bit.  Sums are kept in fp64: a run may add the same
-// gradient row many times over (a hot row hit repeatedly inside one bag), and
-// fp32 rounding errors of such correlated sums grow linearly; products c_i * g
-// are exact in fp64.  Every stage is its own kernel: no workgroup waits for
-// another.
+// are reproducible bit for bit.  Sums inside workgroup items are kept in fp64:
+// a run may add the same gradient row many times over (a hot row hit
+// repeatedly inside one bag), and fp32 rounding errors of such correlated sums
+// grow linearly; products c_i * g are exact in fp64.  Every stage is its own
+// kernel: no workgroup waits for another.  (Finishing a long run in the chunk
+// workgroup that completes it last would need a device-scope release per
+// chunk, which writes back the whole L2 of its XCD and costs far more than
+// one more small kernel.)
 #include "common.hpp"
 
 namespace tbe {
@@ -52,6 +54,12 @@ constexpr uint32_t kMediumItem = 0x80000000u;
 template <int VE, int NCH>
 constexpr int group_unroll() {
   return (32 / (VE * NCH)) < 1 ? 1 : ((32 / (VE * NCH)) > 8 ? 8 : 32 / (VE * NCH));
+}
+// Short runs keep at most 4 rows in flight: the registers saved buy more
+// resident waves, which hides more latency than a deeper unroll.
+template <int VE, int NCH>
+constexpr int short_unroll() {
+  return group_unroll<VE, NCH>() > 4 ? 4 : group_unroll<VE, NCH>();
 }
 template <int VE, int NCH>
 constexpr int wg_unroll() {
@@ -143,36 +151,6 @@ __device__ __forceinline__ float step_size(const BackwardLaunch& a, uint32_t key
   return a.lr / (sqrtf(mnew) + a.eps);
 }
 
-// Group-wide update of row `key` (this lane's chunks).
-template <int ST, int VE, int NCH>
-__device__ __forceinline__ void group_update(const BackwardLaunch& a, const TableMeta& m,
-                                             uint32_t key, const GroupCtx& g,
-                                             const Acc<VE, NCH>& acc) {
-  const int D = m.dim;
-  const int C = D / VE;
-  double ss = 0.0;
-  if (a.adagrad) {
-#pragma unroll
-    for (int c = 0; c < NCH; ++c)
-#pragma unroll
-      for (int q = 0; q < VE; ++q) ss = fma(acc.v[c][q], acc.v[c][q], ss);
-    for (int o = g.Gs >> 1; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, kWave);
-  }
-  const float step = step_size(a, key, ss, D, g.gl == 0);
-  const int64_t row0 = m.woff + static_cast<int64_t>(key - static_cast<uint32_t>(m.roff)) * D;
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const int chunk = c * g.Gs + g.gl;
-    if (chunk < C) {
-      float w[VE];
-      load_widen<ST, VE>(a.weights, row0 + chunk * VE, w);
-#pragma unroll
-      for (int q = 0; q < VE; ++q) w[q] = fmaf(-step, static_cast<float>(acc.v[c][q]), w[q]);
-      narrow_store<ST, VE>(a.weights, row0 + chunk * VE, w);
-    }
-  }
-}
-
 struct GroupIds {
   int gid, ngroups;
   GroupCtx g;
@@ -224,14 +202,30 @@ __device__ __forceinline__ TableMeta meta_of(const BackwardLaunch& a, const Tabl
   return a.T <= kLdsTables ? s_meta[t] : a.meta[t];
 }
 
+// Exclusive prefix sum over the 64 lanes of a wave (all lanes active); the
+// wave's total goes to *total.
+__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t* total) {
+  const int lane = lane_id();
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  *total = __shfl(x, kWave - 1, kWave);
+  return x - v;
+}
+
 // Short runs (at most Gs lookups): one lane group per run, grid-stride over
-// runs.  Most runs have one to three lookups, so the per-run instruction
-// count is what matters here: the next run's bounds are loaded while the
-// current one is processed, every lane prefetches one lookup, the row to
-// update and its state are loaded before the gradient rows arrive, the gather
-// is unrolled to the run's length (2, 4 or 8 rows in flight) and sums are
-// kept in fp32 (at most Gs terms: error below Gs * 2^-24 of the sum of
-// magnitudes; longer runs are summed in fp64 by the kernels below).
+// runs.  Most runs have one to three lookups and the kernel is bound by the
+// latency of its dependent loads (run bounds -> lookup -> gradient rows), so
+// it is kept lean enough for 7 resident waves per SIMD: every lane loads one
+// lookup, the row to update and its state are loaded before the gradient rows
+// arrive, the gather keeps 2 or 4 rows in flight (matched to the run's
+// length) and sums are kept in fp32 (at most Gs terms: error below
+// Gs * 2^-24 of the sum of magnitudes; longer runs are summed in fp64 by the
+// kernels below).  Loading the next run while working on the current one
+// costs more registers, hence resident waves, than it saves.
 template <int U, int VE, int NCH, bool REC>
 __device__ __forceinline__ void gather_short(const BackwardLaunch& a, const TableMeta& m,
                                              int64_t tb, int leader, int gl, int Gs, int len,
@@ -268,54 +262,58 @@ __global__ __launch_bounds__(kBlock) void seg_short(BackwardLaunch a, const uint
   if (a.out_num && id.gid == 0 && gl == 0) *a.out_num = failed ? -1 : static_cast<int32_t>(U);
   if (failed) return;
   stage_meta(a, s_meta);
+  // The loop runs the same number of times on every lane of a wave (groups
+  // past the last run idle), so the queueing below can use wave-wide scans.
+  const uint32_t wave_first = id.gid - static_cast<uint32_t>(lane_id() >> a.gshift);
+  const uint32_t ng = id.ngroups;
   uint32_t r = id.gid;
-  int64_t ns = 0, ne = 0;
-  uint32_t nkey = 0;
-  if (r < U) {
-    ns = a.buf.run_start[r];
-    ne = a.buf.run_start[r + 1];
-    nkey = a.buf.unique_keys[r];
-  }
-  for (; r < U; r += id.ngroups) {
-    const int64_t s = ns, e = ne;
-    const uint32_t key = nkey;
-    const uint32_t rn = r + id.ngroups;
-    if (rn < U) {
-      ns = a.buf.run_start[rn];
-      ne = a.buf.run_start[rn + 1];
-      nkey = a.buf.unique_keys[rn];
+  for (uint32_t rb = wave_first; rb < U; rb += ng, r += ng) {
+    const bool valid = r < U;
+    int64_t s = 0, e = 0;
+    uint32_t key = 0;
+    if (valid) {
+      s = a.buf.run_start[r];
+      e = a.buf.run_start[r + 1];
+      key = a.buf.unique_keys[r];
     }
-    const int len = static_cast<int>(e - s);
-    if (a.out_unique && gl == 0) {
+    const int len = valid ? static_cast<int>(e - s) : 0;
+    if (valid && a.out_unique && gl == 0) {
       a.out_unique[r] = static_cast<int32_t>(key);
       a.out_lengths[r] = len;
     }
-    if (len > Gs) {
-      // queue: a medium run as one workgroup item, a long run as its chunks
-      if (len >= a.long_threshold) {
-        const uint32_t n1 = static_cast<uint32_t>((len + a.chunk - 1) / a.chunk);
-        const uint32_t n2 = n1 > static_cast<uint32_t>(a.super_chunk)
-                                ? (n1 + a.super_chunk - 1) / a.super_chunk
-                                : 0u;
-        uint32_t li = 0, b1 = 0, b2 = 0, it = 0;
-        if (gl == 0) {
-          li = atomicAdd(&a.buf.counters[kCntLong], 1u);
-          b1 = atomicAdd(&a.buf.counters[kCntChunks], n1);
-          it = atomicAdd(&a.buf.counters[kCntItems1], n1);
-          if (n2) b2 = atomicAdd(&a.buf.counters[kCntItems2], n2);
-          a.buf.longs[li] = make_uint4(r, b1, n1, b2);
-        }
-        li = __shfl(li, leader, kWave);
-        b2 = __shfl(b2, leader, kWave);
-        it = __shfl(it, leader, kWave);
+    // Queue runs longer than Gs: a medium run as one workgroup item, a long
+    // run as its 256-lookup chunks.  Queue slots are reserved with one atomic
+    // per counter per wave (a wave-wide scan of the groups' needs), not per run.
+    if (__ballot(gl == 0 && len > Gs)) {
+      const bool is_long = len > Gs && len >= a.long_threshold;
+      const bool is_medium = len > Gs && !is_long;
+      const uint32_t n1 = is_long ? static_cast<uint32_t>((len + a.chunk - 1) / a.chunk) : 0u;
+      const bool ld = gl == 0;
+      uint32_t t_long, t_chunks, t_items1;
+      const uint32_t x_long = wave_excl_scan(ld && is_long ? 1u : 0u, &t_long);
+      const uint32_t x_chunks = wave_excl_scan(ld ? n1 : 0u, &t_chunks);
+      const uint32_t x_items1 = wave_excl_scan(ld ? (is_long ? n1 : (is_medium ? 1u : 0u)) : 0u,
+                                               &t_items1);
+      uint32_t base[3] = {0u, 0u, 0u};
+      if (lane_id() == 0) {
+        if (t_long) base[0] = atomicAdd(&a.buf.counters[kCntLong], t_long);
+        if (t_chunks) base[1] = atomicAdd(&a.buf.counters[kCntChunks], t_chunks);
+        if (t_items1) base[2] = atomicAdd(&a.buf.counters[kCntItems1], t_items1);
+      }
+#pragma unroll
+      for (int q = 0; q < 3; ++q) base[q] = __shfl(base[q], 0, kWave);
+      // every lane of a group takes its leader's slots
+      const uint32_t li = __shfl(base[0] + x_long, leader, kWave);
+      const uint32_t b1 = __shfl(base[1] + x_chunks, leader, kWave);
+      const uint32_t it = __shfl(base[2] + x_items1, leader, kWave);
+      if (is_long) {
+        if (ld) a.buf.longs[li] = make_uint4(r, b1, n1, 0u);
         for (uint32_t c = gl; c < n1; c += Gs) a.buf.items1[it + c] = make_uint2(li, c);
-        for (uint32_t c = gl; c < n2; c += Gs) a.buf.items2[b2 + c] = make_uint2(li, c);
-      } else if (gl == 0) {
-        const uint32_t it = atomicAdd(&a.buf.counters[kCntItems1], 1u);
+      } else if (is_medium && ld) {
         a.buf.items1[it] = make_uint2(r, kMediumItem);
       }
-      continue;
     }
+    if (!valid || len > Gs) continue;
     uint32_t my_bag = 0;
     float my_coef = 0.0f;
     if (gl < len) lookup_of<REC>(a, sorted_vals[s + gl], &my_bag, &my_coef);
@@ -339,7 +337,7 @@ __global__ __launch_bounds__(kBlock) void seg_short(BackwardLaunch a, const uint
     else if (len <= 4)
       gather_short<4, VE, NCH, REC>(a, m, tb, leader, gl, Gs, len, my_bag, my_coef, acc);
     else
-      gather_short<group_unroll<VE, NCH>(), VE, NCH, REC>(a, m, tb, leader, gl, Gs, len, my_bag,
+      gather_short<short_unroll<VE, NCH>(), VE, NCH, REC>(a, m, tb, leader, gl, Gs, len, my_bag,
                                                            my_coef, acc);
     float step = a.lr;
     if (a.adagrad) {
@@ -481,99 +479,106 @@ __global__ __launch_bounds__(kBlock) void seg_wg(BackwardLaunch a, const uint32_
   }
 }
 
-// acc += rows [first, first + count) of a partial buffer, in order.
-template <int VE, int NCH>
-__device__ __forceinline__ void sum_partials(const float* part, int pstride, uint32_t first,
-                                             uint32_t count, const GroupCtx& g, int C,
-                                             Acc<VE, NCH>& acc) {
-  constexpr int kU = group_unroll<VE, NCH>();
-  for (uint32_t j = 0; j < count; j += kU) {
-    float v[kU][NCH][VE];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const float* row = part + static_cast<int64_t>(first + j + u) * pstride;
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        const int chunk = c * g.Gs + g.gl;
-        if (j + u < count && chunk < C) {
-          if constexpr (VE == 4) {
-            const float4 x = *reinterpret_cast<const float4*>(row + chunk * 4);
-            v[u][c][0] = x.x; v[u][c][1] = x.y; v[u][c][2] = x.z; v[u][c][3] = x.w;
-          } else {
-#pragma unroll
-            for (int q = 0; q < VE; ++q) v[u][c][q] = row[chunk * VE + q];
-          }
-        } else {
-#pragma unroll
-          for (int q = 0; q < VE; ++q) v[u][c][q] = 0.0f;
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kU; ++u)
-#pragma unroll
-      for (int c = 0; c < NCH; ++c)
-#pragma unroll
-        for (int q = 0; q < VE; ++q) acc.v[c][q] += static_cast<double>(v[u][c][q]);
-  }
-}
-
-template <int VE, int NCH>
-__device__ __forceinline__ void store_partial(float* dst, const GroupCtx& g, int C,
-                                              const Acc<VE, NCH>& acc) {
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const int chunk = c * g.Gs + g.gl;
-    if (chunk < C) {
-      if constexpr (VE == 4)
-        *reinterpret_cast<float4*>(dst + chunk * 4) =
-            make_float4(static_cast<float>(acc.v[c][0]), static_cast<float>(acc.v[c][1]),
-                        static_cast<float>(acc.v[c][2]), static_cast<float>(acc.v[c][3]));
-      else
-#pragma unroll
-        for (int q = 0; q < VE; ++q) dst[chunk * VE + q] = static_cast<float>(acc.v[c][q]);
-    }
-  }
-}
-
-template <int VE, int NCH, bool REC>
-__global__ __launch_bounds__(kBlock) void seg_reduce2(BackwardLaunch a, const uint32_t* sorted_vals) {
-  if (a.buf.counters[kCntError] != 0u) return;  // a look-back wait gave up earlier
-  const GroupIds id = group_ids(a);
-  const uint32_t n = a.buf.counters[kCntItems2];
-  for (uint32_t j = id.gid; j < n; j += id.ngroups) {
-    const uint2 it = a.buf.items2[j];
-    const uint4 L = a.buf.longs[it.x];
-    const uint32_t c0 = it.y * a.super_chunk;
-    const uint32_t cnt = min(static_cast<uint32_t>(a.super_chunk), L.z - c0);
-    const int t = table_of_run<REC>(a, sorted_vals, a.buf.run_start[L.x]);
-    const int C = a.meta[t].dim / VE;
-    Acc<VE, NCH> acc;
-    acc.zero();
-    sum_partials<VE, NCH>(a.buf.partial1, a.pstride, L.y + c0, cnt, id.g, C, acc);
-    store_partial<VE, NCH>(a.buf.partial2 + static_cast<int64_t>(j) * a.pstride, id.g, C, acc);
-  }
-}
-
+// One workgroup per long run: its chunk partials are added up and the row
+// is updated.  The workgroup's 256/Gs lane groups take the partials in a
+// fixed interleaving (group j: chunks j, j + 256/Gs, ...), each summing in
+// fp64 in chunk order, and the groups' sums are then added in group order, so
+// the result does not depend on scheduling.  The row to update and its state
+// are loaded while the partials are in flight.
 template <int ST, int VE, int NCH, bool REC>
 __global__ __launch_bounds__(kBlock) void seg_finalize(BackwardLaunch a, const uint32_t* sorted_vals) {
   if (a.buf.counters[kCntError] != 0u) return;  // a look-back wait gave up earlier
-  const GroupIds id = group_ids(a);
+  constexpr int NV = VE * NCH;
+  constexpr int kElemsPerThread = kMaxDim / kBlock;
+  constexpr int kU = group_unroll<VE, NCH>();
+  __shared__ TableMeta s_meta[kLdsTables];
+  __shared__ double s_red[kBlock * NV];        // [group][row element]
+  __shared__ double s_scratch[kWavesPerBlock];
+  stage_meta(a, s_meta);
+  const int tid = threadIdx.x;
+  const int Gs = 1 << a.gshift;
+  const int ngroups = kBlock >> a.gshift;
+  const int g = tid >> a.gshift, gl = tid & (Gs - 1);
+  const int row_elems = Gs * NV;
   const uint32_t n = a.buf.counters[kCntLong];
-  for (uint32_t li = id.gid; li < n; li += id.ngroups) {
+  for (uint32_t li = blockIdx.x; li < n; li += gridDim.x) {
     const uint4 L = a.buf.longs[li];
-    const int t = table_of_run<REC>(a, sorted_vals, a.buf.run_start[L.x]);
-    const TableMeta m = a.meta[t];
-    const int C = m.dim / VE;
+    const uint32_t key = a.buf.unique_keys[L.x];
+    const TableMeta m = meta_of(a, s_meta, table_of_key(a, s_meta, key));
+    const int D = m.dim, C = D / VE;
+    const int64_t row0 = m.woff + static_cast<int64_t>(key - static_cast<uint32_t>(m.roff)) * D;
+    float w[kElemsPerThread];
+#pragma unroll
+    for (int k = 0; k < kElemsPerThread; ++k) {
+      const int d = tid + k * kBlock;
+      w[k] = 0.0f;
+      if (d < D) load_widen<ST, 1>(a.weights, row0 + d, &w[k]);
+    }
+    const float m_old = a.adagrad ? a.state[key] : 0.0f;
     Acc<VE, NCH> acc;
     acc.zero();
-    if (L.z > static_cast<uint32_t>(a.super_chunk)) {
-      const uint32_t n2 = (L.z + a.super_chunk - 1) / a.super_chunk;
-      sum_partials<VE, NCH>(a.buf.partial2, a.pstride, L.w, n2, id.g, C, acc);
-    } else {
-      sum_partials<VE, NCH>(a.buf.partial1, a.pstride, L.y, L.z, id.g, C, acc);
+    for (uint32_t c0 = g; c0 < L.z; c0 += static_cast<uint32_t>(ngroups * kU)) {
+      float v[kU][NCH][VE];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const uint32_t c = c0 + static_cast<uint32_t>(u * ngroups);
+        const float* row = a.buf.partial1 + static_cast<int64_t>(L.y + c) * a.pstride;
+#pragma unroll
+        for (int q = 0; q < NCH; ++q) {
+          const int chunk = q * Gs + gl;
+          if (c < L.z && chunk < C) {
+            if constexpr (VE == 4) {
+              const float4 x = *reinterpret_cast<const float4*>(row + chunk * 4);
+              v[u][q][0] = x.x; v[u][q][1] = x.y; v[u][q][2] = x.z; v[u][q][3] = x.w;
+            } else {
+#pragma unroll
+              for (int e = 0; e < VE; ++e) v[u][q][e] = row[chunk * VE + e];
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < VE; ++e) v[u][q][e] = 0.0f;
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+#pragma unroll
+        for (int q = 0; q < NCH; ++q)
+#pragma unroll
+          for (int e = 0; e < VE; ++e) acc.v[q][e] += static_cast<double>(v[u][q][e]);
     }
-    group_update<ST, VE, NCH>(a, m, a.buf.unique_keys[L.x], id.g, acc);
+#pragma unroll
+    for (int q = 0; q < NCH; ++q)
+#pragma unroll
+      for (int e = 0; e < VE; ++e) s_red[g * row_elems + (q * Gs + gl) * VE + e] = acc.v[q][e];
+    __syncthreads();
+    double gam[kElemsPerThread];
+    double ss = 0.0;
+#pragma unroll
+    for (int k = 0; k < kElemsPerThread; ++k) {
+      const int d = tid + k * kBlock;
+      double x = 0.0;
+      if (d < D)
+        for (int gg = 0; gg < ngroups; ++gg) x += s_red[gg * row_elems + d];
+      gam[k] = x;
+      ss = fma(x, x, ss);
+    }
+    float step = a.lr;
+    if (a.adagrad) {
+      ss = block_sum(ss, s_scratch);
+      const float mnew = static_cast<float>(static_cast<double>(m_old) + ss / D);
+      if (tid == 0) a.state[key] = mnew;
+      step = a.lr / (sqrtf(mnew) + a.eps);
+    }
+#pragma unroll
+    for (int k = 0; k < kElemsPerThread; ++k) {
+      const int d = tid + k * kBlock;
+      if (d < D) {
+        float x = fmaf(-step, static_cast<float>(gam[k]), w[k]);
+        narrow_store<ST, 1>(a.weights, row0 + d, &x);
+      }
+    }
+    __syncthreads();  // s_red is reused by the next run
   }
 }
 
@@ -589,48 +594,43 @@ int64_t blocks_for(int64_t items, int gshift) {
 
 template <int ST, int VE, int NCH, bool REC>
 hipError_t run_segments(const BackwardLaunch& a, const uint32_t* sorted_vals, hipStream_t s,
-                        StageHook hook, void* ctx) {
+                        const KernelTimer* kt) {
   const int64_t n = a.num_indices;
-  const SegmentBounds ub = segment_bounds(n, a.long_threshold, a.chunk, a.super_chunk, a.gshift);
-  hipLaunchKernelGGL((seg_short<ST, VE, NCH, REC>), dim3(blocks_for(n, a.gshift)), dim3(kBlock),
-                     0, s, a, sorted_vals);
-  if (hook) hook(ctx, "seg_short");
+  const SegmentBounds ub = segment_bounds(n, a.long_threshold, a.chunk, a.gshift);
+  launch_timed(kt, "seg_short", seg_short<ST, VE, NCH, REC>, dim3(blocks_for(n, a.gshift)),
+               dim3(kBlock), 0, s, a, sorted_vals);
   const int64_t wg = ub.items1 < kMaxSegBlocks ? (ub.items1 > 0 ? ub.items1 : 1) : kMaxSegBlocks;
-  hipLaunchKernelGGL((seg_wg<ST, VE, NCH, REC>), dim3(wg), dim3(kBlock), 0, s, a, sorted_vals);
-  if (hook) hook(ctx, "seg_wg");
-  hipLaunchKernelGGL((seg_reduce2<VE, NCH, REC>), dim3(blocks_for(ub.items2, a.gshift)),
-                     dim3(kBlock), 0, s, a, sorted_vals);
-  if (hook) hook(ctx, "seg_reduce2");
-  hipLaunchKernelGGL((seg_finalize<ST, VE, NCH, REC>), dim3(blocks_for(ub.longs, a.gshift)),
-                     dim3(kBlock), 0, s, a, sorted_vals);
-  if (hook) hook(ctx, "seg_finalize");
+  launch_timed(kt, "seg_wg", seg_wg<ST, VE, NCH, REC>, dim3(wg), dim3(kBlock), 0, s, a,
+               sorted_vals);
+  const int64_t fin = ub.longs < kMaxSegBlocks ? ub.longs : kMaxSegBlocks;
+  launch_timed(kt, "seg_finalize", seg_finalize<ST, VE, NCH, REC>, dim3(fin), dim3(kBlock), 0, s,
+               a, sorted_vals);
   return hipGetLastError();
 }
 
 template <int ST, int VE, int NCH>
-hipError_t dispatch_rec(const BackwardLaunch& a, const uint32_t* v, hipStream_t s, StageHook h,
-                        void* c) {
-  return a.use_rec ? run_segments<ST, VE, NCH, true>(a, v, s, h, c)
-                   : run_segments<ST, VE, NCH, false>(a, v, s, h, c);
+hipError_t dispatch_rec(const BackwardLaunch& a, const uint32_t* v, hipStream_t s,
+                        const KernelTimer* kt) {
+  return a.use_rec ? run_segments<ST, VE, NCH, true>(a, v, s, kt)
+                   : run_segments<ST, VE, NCH, false>(a, v, s, kt);
 }
 
 template <int ST>
-hipError_t dispatch_shape(const BackwardLaunch& a, const uint32_t* v, hipStream_t s, StageHook h,
-                          void* c) {
+hipError_t dispatch_shape(const BackwardLaunch& a, const uint32_t* v, hipStream_t s,
+                          const KernelTimer* kt) {
   if (a.vec) {
-    if (a.nch == 1) return dispatch_rec<ST, 4, 1>(a, v, s, h, c);
-    if (a.nch == 4) return dispatch_rec<ST, 4, 4>(a, v, s, h, c);
+    if (a.nch == 1) return dispatch_rec<ST, 4, 1>(a, v, s, kt);
+    if (a.nch == 4) return dispatch_rec<ST, 4, 4>(a, v, s, kt);
   } else {
-    if (a.nch == 1) return dispatch_rec<ST, 1, 1>(a, v, s, h, c);
-    if (a.nch == 16) return dispatch_rec<ST, 1, 16>(a, v, s, h, c);
+    if (a.nch == 1) return dispatch_rec<ST, 1, 1>(a, v, s, kt);
+    if (a.nch == 16) return dispatch_rec<ST, 1, 16>(a, v, s, kt);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-SegmentBounds segment_bounds(int64_t n, int64_t long_threshold, int chunk, int super_chunk,
-                             int gshift) {
+SegmentBounds segment_bounds(int64_t n, int64_t long_threshold, int chunk, int gshift) {
   SegmentBounds b;
   const int64_t thr = long_threshold > 0 ? long_threshold : 1;
   const int64_t group_max = int64_t{1} << gshift;  // longest run a lane group takes alone
@@ -638,16 +638,15 @@ SegmentBounds segment_bounds(int64_t n, int64_t long_threshold, int chunk, int s
   b.chunks = n / chunk + b.longs;
   // queued items: runs longer than group_max that are not long, plus long-run chunks
   b.items1 = n / (group_max + 1) + b.chunks + 1;
-  b.items2 = b.chunks / super_chunk + b.longs;
   return b;
 }
 
 hipError_t launch_segment_reduce_update(const BackwardLaunch& a, const uint32_t* sorted_vals,
-                                        hipStream_t stream, StageHook hook, void* ctx) {
+                                        hipStream_t stream, const KernelTimer* kt) {
   switch (a.dtype) {
-    case kF32: return dispatch_shape<kF32>(a, sorted_vals, stream, hook, ctx);
-    case kF16: return dispatch_shape<kF16>(a, sorted_vals, stream, hook, ctx);
-    case kBF16: return dispatch_shape<kBF16>(a, sorted_vals, stream, hook, ctx);
+    case kF32: return dispatch_shape<kF32>(a, sorted_vals, stream, kt);
+    case kF16: return dispatch_shape<kF16>(a, sorted_vals, stream, kt);
+    case kBF16: return dispatch_shape<kBF16>(a, sorted_vals, stream, kt);
     default: return hipErrorInvalidValue;
   }
 }

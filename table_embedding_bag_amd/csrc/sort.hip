@@ -41,7 +41,8 @@ constexpr uint32_t kFlagIncl = 2u << 30;    // status word: count up to and incl
 constexpr uint32_t kValueMask = (1u << 30) - 1u;
 constexpr uint32_t kSpinLimit = 1u << 20;   // polls before a waiting tile gives up
 constexpr int kLookDepth = 16;              // status words read at once per digit
-constexpr int kLinBags = 64;                // bags per linearize workgroup
+constexpr int kLinBags = 64;                // bags per linearize tile
+constexpr int64_t kLinMaxBlocks = 1024;     // linearize grid bound
 constexpr int kResidentTiles = 256;         // grids this small are resident all at once
 
 template <typename IT>
@@ -62,9 +63,12 @@ __global__ __launch_bounds__(kBlock) void init_workspace(uint32_t* words, int64_
     words[i] = 0u;
 }
 
-// One workgroup per 64 consecutive bags.  The bags' offsets are staged in LDS;
-// the workgroup then walks all of their lookups with consecutive threads on
-// consecutive lookups and finds each lookup's bag by binary search in LDS.
+// Workgroups stride over tiles of 64 consecutive bags.  A tile's offsets are
+// staged in LDS; the workgroup then walks all of its lookups with consecutive
+// threads on consecutive lookups and finds each lookup's bag by binary search
+// in LDS.  Digit counts are kept in LDS across the workgroup's tiles and
+// added to the global counts once at the end (a bounded grid keeps those
+// global atomics, all on the same few hundred words, few).
 template <typename IT>
 __global__ __launch_bounds__(kBlock) void linearize_kernel(BackwardLaunch a) {
   __shared__ int64_t s_off[kLinBags + 1];
@@ -75,42 +79,60 @@ __global__ __launch_bounds__(kBlock) void linearize_kernel(BackwardLaunch a) {
   const int tid = threadIdx.x;
   const int passes = (a.key_bits + kRadixBits - 1) / kRadixBits;
   for (int i = tid; i < passes * kRadix; i += kBlock) s_hist[i] = 0u;
-  const int64_t k0 = static_cast<int64_t>(blockIdx.x) * kLinBags;
-  const int nb = static_cast<int>(min(static_cast<int64_t>(kLinBags), a.num_bags - k0));
-  if (tid < nb) {
-    const int64_t k = k0 + tid;
-    const int64_t lo = ld_index<IT>(a.offsets, k);
-    const int64_t hi = ld_index<IT>(a.offsets, k + 1);
-    s_off[tid] = lo;
-    if (tid == nb - 1) s_off[nb] = hi;
-    const int t = static_cast<int>(k / a.B);
-    s_roff[tid] = static_cast<uint32_t>(a.meta[t].roff);
-    s_scale[tid] = a.mean ? ((hi > lo) ? 1.0f / static_cast<float>(hi - lo) : 0.0f) : 1.0f;
-  }
-  __syncthreads();
+  const int64_t ntiles = (a.num_bags + kLinBags - 1) / kLinBags;
+  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int64_t k0 = tile * kLinBags;
+    const int nb = static_cast<int>(min(static_cast<int64_t>(kLinBags), a.num_bags - k0));
+    __syncthreads();  // the previous tile's offsets are no longer read
+    if (tid < nb) {
+      const int64_t k = k0 + tid;
+      const int64_t lo = ld_index<IT>(a.offsets, k);
+      const int64_t hi = ld_index<IT>(a.offsets, k + 1);
+      s_off[tid] = lo;
+      if (tid == nb - 1) s_off[nb] = hi;
+      const int t = static_cast<int>(k / a.B);
+      s_roff[tid] = static_cast<uint32_t>(a.meta[t].roff);
+      s_scale[tid] = a.mean ? ((hi > lo) ? 1.0f / static_cast<float>(hi - lo) : 0.0f) : 1.0f;
+    }
+    __syncthreads();
 
-  const int64_t p0 = s_off[0], p1 = s_off[nb];
-  for (int64_t p = p0 + tid; p < p1; p += kBlock) {
-    int lo = 0, hi = nb;  // bag slot s with s_off[s] <= p < s_off[s + 1]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_off[mid] <= p)
-        lo = mid;
-      else
-        hi = mid;
+    const int64_t p0 = s_off[0], p1 = s_off[nb];
+    for (int64_t p = p0 + tid; p < p1; p += kBlock) {
+      int lo = 0, hi = nb;  // bag slot s with s_off[s] <= p < s_off[s + 1]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_off[mid] <= p)
+          lo = mid;
+        else
+          hi = mid;
+      }
+      const uint32_t key = s_roff[lo] + static_cast<uint32_t>(ld_index<IT>(a.indices, p));
+      a.buf.keys[0][p] = key;
+      const uint32_t bag = static_cast<uint32_t>(k0 + lo);
+      if (a.use_rec) {
+        a.buf.vals[0][p] = static_cast<uint32_t>(p);
+        const float coef = (a.psw ? a.psw[p] : 1.0f) * s_scale[lo];
+        a.buf.rec[p] = make_uint2(bag, __float_as_uint(coef));
+      } else {
+        a.buf.vals[0][p] = bag;
+      }
+      // digit counts: lanes holding the same digit are matched through 8
+      // ballots and only the lowest of them adds their number (the high digits
+      // of one table's keys take few values, so per-lane atomics would queue
+      // on a handful of LDS words)
+      const uint64_t active = __ballot(1);
+      for (int q = 0; q < passes; ++q) {
+        const uint32_t d = (key >> (q * kRadixBits)) & (kRadix - 1);
+        uint64_t peers = active;
+#pragma unroll
+        for (int bit = 0; bit < kRadixBits; ++bit) {
+          const bool set = (d >> bit) & 1u;
+          const uint64_t bal = __ballot(set);
+          peers &= set ? bal : ~bal;
+        }
+        if (popc_below(peers) == 0) atomicAdd(&s_hist[q * kRadix + d], __popcll(peers));
+      }
     }
-    const uint32_t key = s_roff[lo] + static_cast<uint32_t>(ld_index<IT>(a.indices, p));
-    a.buf.keys[0][p] = key;
-    const uint32_t bag = static_cast<uint32_t>(k0 + lo);
-    if (a.use_rec) {
-      a.buf.vals[0][p] = static_cast<uint32_t>(p);
-      const float coef = (a.psw ? a.psw[p] : 1.0f) * s_scale[lo];
-      a.buf.rec[p] = make_uint2(bag, __float_as_uint(coef));
-    } else {
-      a.buf.vals[0][p] = bag;
-    }
-    for (int q = 0; q < passes; ++q)
-      atomicAdd(&s_hist[q * kRadix + ((key >> (q * kRadixBits)) & (kRadix - 1))], 1u);
   }
   __syncthreads();
   for (int i = tid; i < passes * kRadix; i += kBlock)
@@ -354,25 +376,27 @@ __global__ __launch_bounds__(kBlock) void rle_kernel(const uint32_t* __restrict_
 
 int sort_keys_per_thread(int64_t n) { return n <= (int64_t{1} << 17) ? 8 : 16; }
 
-hipError_t launch_linearize(const BackwardLaunch& a, hipStream_t stream) {
+hipError_t launch_linearize(const BackwardLaunch& a, hipStream_t stream, const KernelTimer* kt) {
   // zero the counters, histograms and look-back status words first
   int64_t zblocks = (a.buf.zero_words + kBlock - 1) / kBlock;
   if (zblocks > 1024) zblocks = 1024;
-  hipLaunchKernelGGL(init_workspace, dim3(static_cast<unsigned>(zblocks > 0 ? zblocks : 1)),
-                     dim3(kBlock), 0, stream, a.buf.counters, a.buf.zero_words);
-  const int64_t blocks = (a.num_bags + kLinBags - 1) / kLinBags;
+  launch_timed(kt, "init_workspace", init_workspace,
+               dim3(static_cast<unsigned>(zblocks > 0 ? zblocks : 1)), dim3(kBlock), 0, stream,
+               a.buf.counters, a.buf.zero_words);
+  int64_t blocks = (a.num_bags + kLinBags - 1) / kLinBags;
   if (blocks <= 0) return hipGetLastError();
+  if (blocks > kLinMaxBlocks) blocks = kLinMaxBlocks;
   if (a.index64)
-    hipLaunchKernelGGL(linearize_kernel<int64_t>, dim3(static_cast<unsigned>(blocks)),
-                       dim3(kBlock), 0, stream, a);
+    launch_timed(kt, "linearize_kernel", linearize_kernel<int64_t>,
+                 dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, stream, a);
   else
-    hipLaunchKernelGGL(linearize_kernel<int32_t>, dim3(static_cast<unsigned>(blocks)),
-                       dim3(kBlock), 0, stream, a);
+    launch_timed(kt, "linearize_kernel", linearize_kernel<int32_t>,
+                 dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_radix_sort(const BackwardLaunch& a, hipStream_t stream, int* result_buffer,
-                             StageHook hook, void* ctx) {
+                             const KernelTimer* kt) {
   const int64_t n = a.num_indices;
   const int kpt = sort_keys_per_thread(n);
   const int64_t ts = static_cast<int64_t>(kBlock) * kpt;
@@ -383,14 +407,13 @@ hipError_t launch_radix_sort(const BackwardLaunch& a, hipStream_t stream, int* r
     const uint32_t* totals = a.buf.digit_hist + pass * kRadix;
     uint32_t* ticket = ntiles <= kResidentTiles ? nullptr : a.buf.tickets + pass;
     if (kpt == 8)
-      hipLaunchKernelGGL(radix_pass<8>, dim3(ntiles), dim3(kBlock), 0, stream, a.buf.keys[cur],
+      launch_timed(kt, "radix_pass", radix_pass<8>, dim3(ntiles), dim3(kBlock), 0, stream, a.buf.keys[cur],
                          a.buf.vals[cur], a.buf.keys[cur ^ 1], a.buf.vals[cur ^ 1], n, shift, totals,
                          status, ticket, a.buf.counters + kCntError);
     else
-      hipLaunchKernelGGL(radix_pass<16>, dim3(ntiles), dim3(kBlock), 0, stream, a.buf.keys[cur],
+      launch_timed(kt, "radix_pass", radix_pass<16>, dim3(ntiles), dim3(kBlock), 0, stream, a.buf.keys[cur],
                          a.buf.vals[cur], a.buf.keys[cur ^ 1], a.buf.vals[cur ^ 1], n, shift, totals,
                          status, ticket, a.buf.counters + kCntError);
-    if (hook) hook(ctx, "radix_pass");
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     cur ^= 1;
@@ -400,15 +423,14 @@ hipError_t launch_radix_sort(const BackwardLaunch& a, hipStream_t stream, int* r
 }
 
 hipError_t launch_run_length_encode(const BackwardLaunch& a, const uint32_t* sorted_keys,
-                                    hipStream_t stream, StageHook hook, void* ctx) {
+                                    hipStream_t stream, const KernelTimer* kt) {
   const int64_t n = a.num_indices;
   const int ntiles = static_cast<int>((n + kRleTile - 1) / kRleTile);
-  hipLaunchKernelGGL(rle_kernel, dim3(ntiles), dim3(kBlock), 0, stream, sorted_keys, n, ntiles,
+  launch_timed(kt, "rle_kernel", rle_kernel, dim3(ntiles), dim3(kBlock), 0, stream, sorted_keys, n, ntiles,
                      a.buf.rle_status,
                      ntiles <= kResidentTiles ? nullptr : a.buf.tickets + kMaxRadixPasses,
                      a.buf.counters,
                      a.buf.unique_keys, a.buf.run_start);
-  if (hook) hook(ctx, "rle_kernel");
   return hipGetLastError();
 }
 

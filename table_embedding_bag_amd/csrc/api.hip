@@ -177,7 +177,7 @@ struct BwdPlan {
   int32_t pstride = 0;
   int32_t nch = 1, gshift = 0;
   bool vec = false;
-  int passes = 1;
+  int passes = 1, slots = 256;
   int64_t zero_words = 0;
   size_t o_keys[2], o_vals[2], o_rec, o_zero, o_uniq, o_start, o_longs, o_items1, o_p1;
   size_t bytes = 0;
@@ -206,13 +206,14 @@ bool plan_backward(const tbe_handle* h, int64_t n, bool vec, BwdPlan* p) {
   const int64_t sort_tile = static_cast<int64_t>(kBlock) * sort_keys_per_thread(n);
   p->sort_tiles = static_cast<int>((n + sort_tile - 1) / sort_tile);
   p->rle_tiles = static_cast<int>((n + kRleTile - 1) / kRleTile);
-  p->passes = (h->key_bits + kRadixBits - 1) / kRadixBits;
+  p->passes = radix_passes(h->key_bits);
+  p->slots = radix_slots(radix_digit_bits(h->key_bits));
   const SegmentBounds ub = segment_bounds(n, h->long_threshold, kChunk, p->gshift);
   p->long_ub = ub.longs;
   p->chunks_ub = ub.chunks;
   p->items1_ub = ub.items1;
-  p->zero_words = kNumCounters + kNumTickets + int64_t{kMaxRadixPasses} * kRadix +
-                  int64_t{p->passes} * p->sort_tiles * kRadix + p->rle_tiles;
+  p->zero_words = kNumCounters + kNumTickets + int64_t{p->passes} * p->slots +
+                  int64_t{p->passes} * p->sort_tiles * p->slots + p->rle_tiles;
   Carve cv;
   for (int i = 0; i < 2; ++i) {
     p->o_keys[i] = cv.take(4 * static_cast<size_t>(n));
@@ -590,8 +591,8 @@ tbe_status tbe_backward_update(tbe_handle* h, int32_t B, const void* indices, co
     b.counters = reinterpret_cast<uint32_t*>(w + p.o_zero);
     b.tickets = b.counters + kNumCounters;
     b.digit_hist = b.tickets + kNumTickets;
-    b.sort_status = b.digit_hist + kMaxRadixPasses * kRadix;
-    b.rle_status = b.sort_status + static_cast<int64_t>(p.passes) * p.sort_tiles * kRadix;
+    b.sort_status = b.digit_hist + p.passes * p.slots;
+    b.rle_status = b.sort_status + static_cast<int64_t>(p.passes) * p.sort_tiles * p.slots;
     b.zero_words = p.zero_words;
     b.unique_keys = reinterpret_cast<uint32_t*>(w + p.o_uniq);
     b.run_start = reinterpret_cast<uint32_t*>(w + p.o_start);

@@ -245,8 +245,9 @@ struct BackwardBuffers {
   uint32_t* vals[2];
   uint2* rec;               // per lookup {bag, coefficient bits} when needed, else null
   // One contiguous region zeroed at the start of every backward call:
-  //   counters [kNumCounters], tickets [kNumTickets], digit_hist [kMaxRadixPasses][256],
-  //   sort_status [passes][sort tiles][256], rle_status [rle tiles]
+  //   counters [kNumCounters], tickets [kNumTickets], digit_hist [passes][slots],
+  //   sort_status [passes][sort tiles][slots], rle_status [rle tiles]
+  // (slots = radix_slots(digit bits))
   uint32_t* counters;
   uint32_t* tickets;        // tile tickets: one per radix pass, then the RLE's
   uint32_t* digit_hist;     // digit counts of every radix pass
@@ -260,11 +261,12 @@ struct BackwardBuffers {
   float* partial1;          // [chunks cap, pstride]
 };
 
-// Device counters of the backward (zeroed at the start of every call).
-// kCntError is raised if a look-back wait ever gives up (results then invalid).
-enum { kCntUnique = 0, kCntLong = 1, kCntItems1 = 2, kCntChunks = 4,
-       kCntError = 5, kNumCounters = 8 };
-constexpr int kMaxRadixPasses = 4;       // 32-bit keys, 8-bit digits
+// Device counters of the backward (zeroed at the start of every call), each
+// on a 128-byte line of its own so that atomics on different counters do not
+// queue behind each other.  kCntError is raised if a look-back wait ever
+// gives up (results then invalid).
+enum { kCntUnique = 0, kCntLong = 32, kCntItems1 = 64, kCntChunks = 96, kCntError = 128,
+       kNumCounters = 160 };
 constexpr int kNumTickets = 8;           // kMaxRadixPasses radix passes + the RLE
 
 // Keys per thread of a radix tile for a batch of n lookups (8 or 16).
@@ -322,7 +324,25 @@ constexpr int kMaxDim = 1024;
 
 // Tile sizes shared by the planner (workspace sizing) and the kernels.
 constexpr int kRleTile = 4096;
-constexpr int kRadixBits = 8;
-constexpr int kRadix = 1 << kRadixBits;
+
+// LSD radix sort plan for keys of key_bits bits: the fewest passes of at most
+// 8-bit digits, the bits split evenly over the passes.  Every per-pass table
+// (digit counts, look-back status words) has radix_slots(bits) entries: at
+// least 256, so that narrow digits keep one digit per thread.  (Wider digits
+// were measured slower on gfx950: a 10-bit pass costs about twice an 8-bit
+// one -- the look-back then covers 4 digits per thread -- so fewer passes do
+// not pay.)
+constexpr int kMaxRadixBits = 8;
+constexpr int kMaxRadixPasses = 4;  // 32-bit ids
+__host__ __device__ inline int radix_passes(int key_bits) {
+  return (key_bits + kMaxRadixBits - 1) / kMaxRadixBits;
+}
+__host__ __device__ inline int radix_digit_bits(int key_bits) {
+  const int p = radix_passes(key_bits);
+  return (key_bits + p - 1) / p;
+}
+__host__ __device__ inline int radix_slots(int digit_bits) {
+  return 1 << (digit_bits > 8 ? digit_bits : 8);
+}
 
 }  // namespace tbe

@@ -219,7 +219,7 @@ __device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t* total) 
 // Short runs (at most Gs lookups): one lane group per run, grid-stride over
 // runs.  Most runs have one to three lookups and the kernel is bound by the
 // latency of its dependent loads (run bounds -> lookup -> gradient rows), so
-// it is kept lean enough for 7 resident waves per SIMD: every lane loads one
+// it is kept lean (about 70 registers, 7 resident waves per SIMD): every lane loads one
 // lookup, the row to update and its state are loaded before the gradient rows
 // arrive, the gather keeps 2 or 4 rows in flight (matched to the run's
 // length) and sums are kept in fp32 (at most Gs terms: error below
@@ -283,7 +283,8 @@ __global__ __launch_bounds__(kBlock) void seg_short(BackwardLaunch a, const uint
     }
     // Queue runs longer than Gs: a medium run as one workgroup item, a long
     // run as its 256-lookup chunks.  Queue slots are reserved with one atomic
-    // per counter per wave (a wave-wide scan of the groups' needs), not per run.
+    // per counter per wave (a wave-wide scan of the groups' needs), not per
+    // run; the counters sit on separate cache lines.
     if (__ballot(gl == 0 && len > Gs)) {
       const bool is_long = len > Gs && len >= a.long_threshold;
       const bool is_medium = len > Gs && !is_long;

@@ -14,13 +14,15 @@
 //               also counts the digits of every radix pass (these counts do not
 //               depend on the order of the keys), so no pass needs a counting
 //               kernel of its own.
-//   radix pass  one kernel per 8-bit digit of a stable LSD radix sort on
-//               ceil(log2(sum E_t)) bits.  A tile of 256*KPT keys is ranked in
-//               LDS (equal digits matched within a wave through 8 ballots,
-//               per-wave digit counters), its digit counts are published and
-//               the tile's offset within every digit bucket is found by a
-//               decoupled look-back over the tiles before it; the tile is then
-//               written bucket by bucket so global stores are coalesced.
+//   radix pass  one kernel per digit of a stable LSD radix sort on
+//               ceil(log2(sum E_t)) bits, split evenly into the fewest digits
+//               of at most 8 bits.  A tile of 256*KPT keys is ranked in LDS
+//               (equal digits matched within a wave through one ballot per
+//               digit bit, per-wave digit counters), its digit counts are
+//               published and the tile's offset within every digit bucket is
+//               found by a decoupled look-back over the tiles before it; the
+//               tile is then written bucket by bucket so global stores are
+//               coalesced.
 //   RLE         one kernel: run heads of a 4096-key tile, a look-back over
 //               the head counts of earlier tiles, then unique ids and run
 //               starts.  The number of runs U stays on the device.
@@ -40,7 +42,6 @@ constexpr uint32_t kFlagAgg = 1u << 30;     // status word: this tile's own coun
 constexpr uint32_t kFlagIncl = 2u << 30;    // status word: count up to and including this tile
 constexpr uint32_t kValueMask = (1u << 30) - 1u;
 constexpr uint32_t kSpinLimit = 1u << 20;   // polls before a waiting tile gives up
-constexpr int kLookDepth = 16;              // status words read at once per digit
 constexpr int kLinBags = 64;                // bags per linearize tile
 constexpr int64_t kLinMaxBlocks = 1024;     // linearize grid bound
 constexpr int kResidentTiles = 256;         // grids this small are resident all at once
@@ -74,11 +75,14 @@ __global__ __launch_bounds__(kBlock) void linearize_kernel(BackwardLaunch a) {
   __shared__ int64_t s_off[kLinBags + 1];
   __shared__ uint32_t s_roff[kLinBags];
   __shared__ float s_scale[kLinBags];
-  __shared__ uint32_t s_hist[kMaxRadixPasses * kRadix];
+  __shared__ uint32_t s_hist[kMaxRadixPasses << kMaxRadixBits];
 
   const int tid = threadIdx.x;
-  const int passes = (a.key_bits + kRadixBits - 1) / kRadixBits;
-  for (int i = tid; i < passes * kRadix; i += kBlock) s_hist[i] = 0u;
+  const int passes = radix_passes(a.key_bits);
+  const int bits = radix_digit_bits(a.key_bits);
+  const int slots = radix_slots(bits);
+  const uint32_t dmask = (1u << bits) - 1u;
+  for (int i = tid; i < passes * slots; i += kBlock) s_hist[i] = 0u;
   const int64_t ntiles = (a.num_bags + kLinBags - 1) / kLinBags;
   for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     const int64_t k0 = tile * kLinBags;
@@ -122,86 +126,110 @@ __global__ __launch_bounds__(kBlock) void linearize_kernel(BackwardLaunch a) {
       // on a handful of LDS words)
       const uint64_t active = __ballot(1);
       for (int q = 0; q < passes; ++q) {
-        const uint32_t d = (key >> (q * kRadixBits)) & (kRadix - 1);
+        const uint32_t d = (key >> (q * bits)) & dmask;
         uint64_t peers = active;
 #pragma unroll
-        for (int bit = 0; bit < kRadixBits; ++bit) {
+        for (int bit = 0; bit < kMaxRadixBits; ++bit) {  // bits above `bits` are 0: no effect
           const bool set = (d >> bit) & 1u;
           const uint64_t bal = __ballot(set);
           peers &= set ? bal : ~bal;
         }
-        if (popc_below(peers) == 0) atomicAdd(&s_hist[q * kRadix + d], __popcll(peers));
+        if (popc_below(peers) == 0) atomicAdd(&s_hist[q * slots + d], __popcll(peers));
       }
     }
   }
   __syncthreads();
-  for (int i = tid; i < passes * kRadix; i += kBlock)
+  for (int i = tid; i < passes * slots; i += kBlock)
     if (s_hist[i]) atomicAdd(&a.buf.digit_hist[i], s_hist[i]);
 }
 
-// Count of digit d in all tiles before `tile` (decoupled look-back, one digit
-// per thread, kLookDepth status words in flight).
-__device__ uint32_t lookback_digit(uint32_t* status, int tile, int d, uint32_t* err) {
-  uint32_t excl = 0;
-  int j = tile - 1;
+// Counts of digits d0 .. d0 + DPT - 1 in all tiles before `tile` (decoupled
+// look-back; every digit keeps DEPTH status words in flight per round).
+// status rows have `slots` words per tile.
+template <int DPT, int DEPTH>
+__device__ void lookback_digits(uint32_t* status, int slots, int tile, int d0, uint32_t* err,
+                                uint32_t (&excl)[DPT]) {
+  int j[DPT];
+  bool done[DPT];
+#pragma unroll
+  for (int q = 0; q < DPT; ++q) excl[q] = 0u, j[q] = tile - 1, done[q] = false;
   uint32_t spins = 0;
   while (true) {
-    uint32_t w[kLookDepth];
+    uint32_t w[DPT][DEPTH];
 #pragma unroll
-    for (int k = 0; k < kLookDepth; ++k)
-      w[k] = (j - k >= 0) ? ld_status(status + static_cast<int64_t>(j - k) * kRadix + d) : kFlagIncl;
-    bool stop = false, done = false;
-    int used = 0;
+    for (int q = 0; q < DPT; ++q)
 #pragma unroll
-    for (int k = 0; k < kLookDepth; ++k) {
-      if (!stop) {
-        const uint32_t f = w[k] & ~kValueMask;
-        if (f == 0) {
-          stop = true;  // not published yet: poll again from here
-        } else {
-          excl += w[k] & kValueMask;
-          ++used;
-          if (f == kFlagIncl) stop = done = true;
+      for (int k = 0; k < DEPTH; ++k)
+        w[q][k] = (!done[q] && j[q] - k >= 0)
+                      ? ld_status(status + static_cast<int64_t>(j[q] - k) * slots + d0 + q)
+                      : kFlagIncl;
+    bool all_done = true, moved = false;
+#pragma unroll
+    for (int q = 0; q < DPT; ++q) {
+      if (done[q]) continue;
+      bool stop = false;
+      int used = 0;
+#pragma unroll
+      for (int k = 0; k < DEPTH; ++k) {
+        if (!stop) {
+          const uint32_t f = w[q][k] & ~kValueMask;
+          if (f == 0) {
+            stop = true;  // not published yet: poll again from here
+          } else {
+            excl[q] += w[q][k] & kValueMask;
+            ++used;
+            if (f == kFlagIncl) stop = done[q] = true;
+          }
         }
       }
+      j[q] -= used;
+      moved |= used > 0;
+      all_done &= done[q];
     }
-    if (done) return excl;
-    j -= used;
-    if (used == 0) {
+    if (all_done) return;
+    if (!moved) {
       if (++spins > kSpinLimit) {
         atomicOr(err, 1u);
-        return excl;
+        return;
       }
       __builtin_amdgcn_s_sleep(2);
     }
   }
 }
 
-// One LSD pass on digit (key >> shift) & 255.
-template <int KPT>
+// One LSD pass on the digit (key >> shift) & (2^bits - 1), bits <= RB.  A
+// tile of 256*KPT keys; thread tid owns the DPT = 2^RB / 256 consecutive
+// digits tid*DPT .. tid*DPT + DPT - 1 for counting, look-back and offsets.
+template <int KPT, int RB>
 __global__ __launch_bounds__(kBlock) void radix_pass(
     const uint32_t* __restrict__ kin, const uint32_t* __restrict__ vin, uint32_t* __restrict__ kout,
-    uint32_t* __restrict__ vout, int64_t n, int shift, const uint32_t* __restrict__ totals,
+    uint32_t* __restrict__ vout, int64_t n, int shift, int bits, const uint32_t* __restrict__ totals,
     uint32_t* status, uint32_t* ticket, uint32_t* err) {
   constexpr int TS = kBlock * KPT;
+  constexpr int RMAX = 1 << RB;
+  constexpr int DPT = RMAX / kBlock;
+  constexpr int DEPTH = DPT == 1 ? 16 : (DPT == 2 ? 8 : 4);
   __shared__ uint32_t s_k[TS];
   __shared__ uint32_t s_v[TS];
-  __shared__ uint32_t s_cnt[kWavesPerBlock][kRadix];
-  __shared__ uint32_t s_dstart[kRadix];
-  __shared__ uint32_t s_gbase[kRadix];
+  __shared__ uint32_t s_cnt[kWavesPerBlock][RMAX];
+  __shared__ uint32_t s_dstart[RMAX];
+  __shared__ uint32_t s_gbase[RMAX];
   __shared__ uint32_t scratch[kWavesPerBlock];
   __shared__ uint32_t s_tile;
 
   // (no early exit on an earlier failure: every write below is clamped in range,
   // and a failed call is reported by the kernels after the sort)
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const uint32_t my_total = totals[tid];  // issued with the key loads below
+  const int d0 = tid * DPT;
+  uint32_t my_total[DPT];  // issued with the key loads below
+#pragma unroll
+  for (int q = 0; q < DPT; ++q) my_total[q] = totals[d0 + q];
   if (tid == 0) s_tile = ticket ? atomicAdd(ticket, 1u) : blockIdx.x;
-  for (int i = tid; i < kWavesPerBlock * kRadix; i += kBlock) (&s_cnt[0][0])[i] = 0u;
+  for (int i = tid; i < kWavesPerBlock * RMAX; i += kBlock) (&s_cnt[0][0])[i] = 0u;
   __syncthreads();
   const int tile = static_cast<int>(s_tile);
   const int64_t base = static_cast<int64_t>(tile) * TS;
-  const uint32_t dmask = kRadix - 1;
+  const uint32_t dmask = (1u << bits) - 1u;
 
   // rank: wave w owns tile positions [w*64*KPT, (w+1)*64*KPT), ranked in KPT
   // rounds of 64 consecutive keys, so equal digits keep their input order
@@ -220,7 +248,7 @@ __global__ __launch_bounds__(kBlock) void radix_pass(
     const uint32_t d = (key[r] >> shift) & dmask;
     uint64_t peers = __ballot(ok);
 #pragma unroll
-    for (int bit = 0; bit < kRadixBits; ++bit) {
+    for (int bit = 0; bit < RB; ++bit) {  // bits above `bits` are 0 everywhere: no effect
       const bool set = (d >> bit) & 1u;
       const uint64_t bal = __ballot(set);
       peers &= set ? bal : ~bal;
@@ -233,25 +261,44 @@ __global__ __launch_bounds__(kBlock) void radix_pass(
   }
   __syncthreads();
 
-  // per digit (thread tid owns digit tid): wave offsets, tile-local bucket
-  // starts, and the tile's offset inside the global bucket
-  const uint32_t c0 = s_cnt[0][tid], c1 = s_cnt[1][tid], c2 = s_cnt[2][tid], c3 = s_cnt[3][tid];
-  const uint32_t mine = c0 + c1 + c2 + c3;
-  s_cnt[0][tid] = 0u;
-  s_cnt[1][tid] = c0;
-  s_cnt[2][tid] = c0 + c1;
-  s_cnt[3][tid] = c0 + c1 + c2;
-  uint32_t total;
-  s_dstart[tid] = block_exclusive_sum(mine, scratch, &total);
-  uint32_t* my_status = status + static_cast<int64_t>(tile) * kRadix + tid;
-  st_status(my_status, (tile == 0 ? kFlagIncl : kFlagAgg) | mine);
-  uint32_t before = 0;
-  if (tile > 0) {
-    before = lookback_digit(status, tile, tid, err);
-    st_status(my_status, kFlagIncl | ((before + mine) & kValueMask));
+  // per owned digit: wave offsets, tile-local bucket starts, and the tile's
+  // offset inside the global bucket
+  uint32_t mine[DPT], loc[DPT], tsum = 0;
+#pragma unroll
+  for (int q = 0; q < DPT; ++q) {
+    const int d = d0 + q;
+    const uint32_t c0 = s_cnt[0][d], c1 = s_cnt[1][d], c2 = s_cnt[2][d], c3 = s_cnt[3][d];
+    mine[q] = c0 + c1 + c2 + c3;
+    s_cnt[0][d] = 0u;
+    s_cnt[1][d] = c0;
+    s_cnt[2][d] = c0 + c1;
+    s_cnt[3][d] = c0 + c1 + c2;
+    loc[q] = tsum;
+    tsum += mine[q];
   }
-  const uint32_t dbase = block_exclusive_sum(my_total, scratch, &total);
-  s_gbase[tid] = dbase + before;
+  uint32_t total;
+  const uint32_t tbase = block_exclusive_sum(tsum, scratch, &total);
+  uint32_t* my_status = status + static_cast<int64_t>(tile) * RMAX + d0;
+#pragma unroll
+  for (int q = 0; q < DPT; ++q) {
+    s_dstart[d0 + q] = tbase + loc[q];
+    st_status(my_status + q, (tile == 0 ? kFlagIncl : kFlagAgg) | mine[q]);
+  }
+  uint32_t before[DPT];
+#pragma unroll
+  for (int q = 0; q < DPT; ++q) before[q] = 0u;
+  if (tile > 0) {
+    lookback_digits<DPT, DEPTH>(status, RMAX, tile, d0, err, before);
+#pragma unroll
+    for (int q = 0; q < DPT; ++q)
+      st_status(my_status + q, kFlagIncl | ((before[q] + mine[q]) & kValueMask));
+  }
+  uint32_t gsum = 0, gloc[DPT];
+#pragma unroll
+  for (int q = 0; q < DPT; ++q) gloc[q] = gsum, gsum += my_total[q];
+  const uint32_t gbase = block_exclusive_sum(gsum, scratch, &total);
+#pragma unroll
+  for (int q = 0; q < DPT; ++q) s_gbase[d0 + q] = gbase + gloc[q] + before[q];
   __syncthreads();
 
 #pragma unroll
@@ -374,7 +421,7 @@ __global__ __launch_bounds__(kBlock) void rle_kernel(const uint32_t* __restrict_
 
 }  // namespace
 
-int sort_keys_per_thread(int64_t n) { return n <= (int64_t{1} << 17) ? 8 : 16; }
+int sort_keys_per_thread(int64_t n) { return n <= (int64_t{1} << 20) ? 8 : 16; }
 
 hipError_t launch_linearize(const BackwardLaunch& a, hipStream_t stream, const KernelTimer* kt) {
   // zero the counters, histograms and look-back status words first
@@ -401,19 +448,23 @@ hipError_t launch_radix_sort(const BackwardLaunch& a, hipStream_t stream, int* r
   const int kpt = sort_keys_per_thread(n);
   const int64_t ts = static_cast<int64_t>(kBlock) * kpt;
   const int ntiles = static_cast<int>((n + ts - 1) / ts);
-  int cur = 0, pass = 0;
-  for (int shift = 0; shift < a.key_bits; shift += kRadixBits, ++pass) {
-    uint32_t* status = a.buf.sort_status + static_cast<int64_t>(pass) * ntiles * kRadix;
-    const uint32_t* totals = a.buf.digit_hist + pass * kRadix;
+  const int passes = radix_passes(a.key_bits), bits = radix_digit_bits(a.key_bits);
+  const int slots = radix_slots(bits);
+  int cur = 0;
+  for (int pass = 0; pass < passes; ++pass) {
+    uint32_t* status = a.buf.sort_status + static_cast<int64_t>(pass) * ntiles * slots;
+    const uint32_t* totals = a.buf.digit_hist + pass * slots;
     uint32_t* ticket = ntiles <= kResidentTiles ? nullptr : a.buf.tickets + pass;
     if (kpt == 8)
-      launch_timed(kt, "radix_pass", radix_pass<8>, dim3(ntiles), dim3(kBlock), 0, stream, a.buf.keys[cur],
-                         a.buf.vals[cur], a.buf.keys[cur ^ 1], a.buf.vals[cur ^ 1], n, shift, totals,
-                         status, ticket, a.buf.counters + kCntError);
+      launch_timed(kt, "radix_pass", radix_pass<8, kMaxRadixBits>, dim3(ntiles), dim3(kBlock), 0,
+                   stream, a.buf.keys[cur], a.buf.vals[cur], a.buf.keys[cur ^ 1],
+                   a.buf.vals[cur ^ 1], n, pass * bits, bits, totals, status, ticket,
+                   a.buf.counters + kCntError);
     else
-      launch_timed(kt, "radix_pass", radix_pass<16>, dim3(ntiles), dim3(kBlock), 0, stream, a.buf.keys[cur],
-                         a.buf.vals[cur], a.buf.keys[cur ^ 1], a.buf.vals[cur ^ 1], n, shift, totals,
-                         status, ticket, a.buf.counters + kCntError);
+      launch_timed(kt, "radix_pass", radix_pass<16, kMaxRadixBits>, dim3(ntiles), dim3(kBlock), 0,
+                   stream, a.buf.keys[cur], a.buf.vals[cur], a.buf.keys[cur ^ 1],
+                   a.buf.vals[cur ^ 1], n, pass * bits, bits, totals, status, ticket,
+                   a.buf.counters + kCntError);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     cur ^= 1;

@@ -44,9 +44,10 @@ def parse():
     p.add_argument("--workload", type=int, default=2, help="benchmark workload 1..5")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU baseline")
-    p.add_argument("--forward", choices=("auto", "gather", "histogram"), default="auto",
-                   help="auto: count-matrix forward for the tables that qualify; gather: never; "
-                        "histogram: force it (every table must qualify)")
+    p.add_argument("--forward", choices=("gather", "routed", "histogram"), default="gather",
+                   help="gather: the gather forward (the library default); routed: count-matrix "
+                        "forward for the tables that qualify; histogram: count-matrix forward "
+                        "for every table (all must qualify)")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain device copy of known size (counter calibration)")
     return p.parse_args()
@@ -220,7 +221,7 @@ def main():
     W_host = workloads.storage_numpy(W).copy() if not args.no_cpu_baseline else None
     state = torch.zeros(spec.sum_rows, dtype=torch.float32, device=dev) \
         if spec.optimizer == "rowwise_adagrad" else None
-    fwd_flags = {"auto": 0, "gather": tbe.FLAG_NO_HISTOGRAM,
+    fwd_flags = {"gather": 0, "routed": tbe.FLAG_HISTOGRAM,
                  "histogram": tbe.FLAG_FORCE_HISTOGRAM}[args.forward]
     op = tbe.TBE(spec.rows, spec.dims, W, state, pooling=spec.pooling, optimizer=spec.optimizer,
                  flags=fwd_flags)

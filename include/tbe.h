@@ -95,11 +95,19 @@ enum {
    * weight; the call then waits for the stream and returns
    * TBE_ERR_INDEX_OUT_OF_RANGE on a bad batch. */
   TBE_FLAG_VALIDATE = 1u,
-  /* Never use the count-matrix (MFMA) forward for small tables. */
+  /* Never use the count-matrix (MFMA) forward (the default: on MI355X the
+   * gather forward measured faster at every qualifying workload tried). */
   TBE_FLAG_NO_HISTOGRAM = 2u,
   /* Use the count-matrix forward for every table; tbe_create fails with
-   * TBE_ERR_UNSUPPORTED if a table is not eligible. */
-  TBE_FLAG_FORCE_HISTOGRAM = 4u
+   * TBE_ERR_UNSUPPORTED if a table does not qualify. */
+  TBE_FLAG_FORCE_HISTOGRAM = 4u,
+  /* Use the count-matrix forward for the tables that qualify and the gather
+   * forward for the others (per call: only when there are no per-sample
+   * weights).  Qualifying: fp16/bf16 storage, E_t <= 1024, D_t <= 256 and a
+   * multiple of 16, rows 16-byte aligned in the flat weights.  Source:
+   * kimbodo.com/?p=28372, "What Happened" (small tables that qualify use a
+   * histogram and tensor-core path). */
+  TBE_FLAG_HISTOGRAM = 8u
 };
 
 typedef struct {

@@ -21,7 +21,7 @@ __all__ = [
     "tbe_backward_workspace_size", "tbe_backward_update", "tbe_set_option", "tbe_stage_times",
     "tbe_status_string", "tbe_abi_version", "TBE",
     "F32", "F16", "BF16", "POOL_SUM", "POOL_MEAN", "OPT_SGD", "OPT_ROWWISE_ADAGRAD",
-    "FLAG_VALIDATE", "FLAG_NO_HISTOGRAM", "FLAG_FORCE_HISTOGRAM",
+    "FLAG_VALIDATE", "FLAG_NO_HISTOGRAM", "FLAG_FORCE_HISTOGRAM", "FLAG_HISTOGRAM",
     "OPTION_LONG_RUN_THRESHOLD", "OPTION_PROFILE", "EXPORTED_SYMBOLS",
 ]
 
@@ -29,7 +29,7 @@ F32, F16, BF16 = 0, 1, 2
 I32, I64 = 0, 1
 POOL_SUM, POOL_MEAN = 0, 1
 OPT_SGD, OPT_ROWWISE_ADAGRAD = 0, 1
-FLAG_VALIDATE, FLAG_NO_HISTOGRAM, FLAG_FORCE_HISTOGRAM = 1, 2, 4
+FLAG_VALIDATE, FLAG_NO_HISTOGRAM, FLAG_FORCE_HISTOGRAM, FLAG_HISTOGRAM = 1, 2, 4, 8
 OPTION_LONG_RUN_THRESHOLD, OPTION_PROFILE = 1, 2
 
 STATUS = {

@@ -260,8 +260,9 @@ tbe_status tbe_create(const tbe_config* cfg, void* weights, float* optim_state, 
   if (cfg->optimizer != TBE_OPT_SGD && cfg->optimizer != TBE_OPT_ROWWISE_ADAGRAD)
     return TBE_ERR_INVALID_ARGUMENT;
   if (cfg->optimizer == TBE_OPT_ROWWISE_ADAGRAD && !optim_state) return TBE_ERR_INVALID_ARGUMENT;
-  if (cfg->flags & ~7u) return TBE_ERR_INVALID_ARGUMENT;
-  if ((cfg->flags & TBE_FLAG_NO_HISTOGRAM) && (cfg->flags & TBE_FLAG_FORCE_HISTOGRAM))
+  if (cfg->flags & ~15u) return TBE_ERR_INVALID_ARGUMENT;
+  if ((cfg->flags & TBE_FLAG_NO_HISTOGRAM) &&
+      (cfg->flags & (TBE_FLAG_FORCE_HISTOGRAM | TBE_FLAG_HISTOGRAM)))
     return TBE_ERR_INVALID_ARGUMENT;
   const int sb = storage_bytes(cfg->weight_dtype);
   if (!aligned(weights, 16)) return TBE_ERR_INVALID_ARGUMENT;
@@ -316,7 +317,8 @@ tbe_status tbe_create(const tbe_config* cfg, void* weights, float* optim_state, 
     // count-matrix forward eligibility (16-bit storage, small tables, dims in
     // 16-column MFMA tiles, 16-byte aligned rows)
     int64_t wt_off = 0;
-    const bool use_hist = h->dtype != TBE_F32 && !(h->flags & TBE_FLAG_NO_HISTOGRAM);
+    const bool use_hist =
+        h->dtype != TBE_F32 && (h->flags & (TBE_FLAG_HISTOGRAM | TBE_FLAG_FORCE_HISTOGRAM));
     for (int t = 0; t < h->T; ++t) {
       const TableMeta& m = h->meta_host[t];
       const bool ok = use_hist && m.rows <= kHistMaxRows && m.dim <= kHistMaxDim &&

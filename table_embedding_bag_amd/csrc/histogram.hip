@@ -39,7 +39,8 @@ namespace {
 constexpr int kHB = 256;              // bags per workgroup (64 per wave)
 constexpr int kDB = 64;               // output columns per workgroup
 constexpr int kCS = kHistKc + 8;      // LDS row stride in 16-bit elements (bank spread)
-constexpr int kLookCap = 2048;        // lookups bucketed per batch
+constexpr int kRegIds = 8;            // row ids of a bag held in registers
+constexpr float kNoBag = -1.0f, kLongBag = -2.0f;
 constexpr int kMaxChunks = kHistMaxRows / kHistKc;
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
@@ -80,6 +81,19 @@ struct Mma<kF16> {
         (__attribute__((address_space(3))) v2*)(word), x);
   }
 };
+
+// Exclusive prefix sum over the 64 lanes of a wave; *total gets the sum.
+__device__ __forceinline__ uint32_t wave_excl(uint32_t v, uint32_t* total) {
+  const int lane = lane_id();
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  *total = __shfl(x, kWave - 1, kWave);
+  return x - v;
+}
 
 template <typename IT>
 __device__ __forceinline__ int64_t ld_index(const void* p, int64_t i) {
@@ -129,14 +143,46 @@ __global__ __launch_bounds__(kBlock) void hist_transpose(HistLaunch a) {
   }
 }
 
+// Adds v (+1 or -1) to the count rows of a wave's bags for the lookups that
+// fall in one chunk: entries {bag slot in wave << 8 | row in chunk}, listed
+// by chunk once per tile.
+template <typename M>
+__device__ __forceinline__ void add_listed(uint32_t* cw, const uint32_t* ent, int n, int row0,
+                                           float v) {
+  for (int e = lane_id(); e < n; e += kWave) {
+    const uint32_t q = ent[e];
+    const int el = (row0 + static_cast<int>(q >> 8)) * kCS + static_cast<int>(q & 0xFFu);
+    M::lds_add(cw + (el >> 1), el & 1, v);
+  }
+}
+
+// The same for the ids of this thread's bag beyond the first kRegIds (bags
+// longer than kRegIds only): they are re-read for every chunk.
+template <typename M, typename IT>
+__device__ __forceinline__ bool add_rest(const HistLaunch& a, uint32_t* cw, int row_base, int len,
+                                         int64_t p0, int k0, float v) {
+  bool any = false;
+  for (int j = kRegIds; j < len; ++j) {
+    const int64_t xj = ld_index<IT>(a.indices, p0 + j);
+    const uint64_t off = static_cast<uint64_t>(xj - k0);
+    if (off < static_cast<uint64_t>(kHistKc)) {
+      const int el = row_base + static_cast<int>(off);
+      M::lds_add(cw + (el >> 1), el & 1, v);
+      any = true;
+    }
+  }
+  return any;
+}
+
 template <int ST, typename IT>
 __global__ __launch_bounds__(kBlock) void fwd_histogram(HistLaunch a) {
   using M = Mma<ST>;
-  __shared__ __align__(16) uint16_t s_c[kHB * kCS];     // count tile [bag][row in chunk]
-  __shared__ __align__(16) uint16_t s_w[kDB * kCS];     // W^T chunk [column][row in chunk]
-  __shared__ uint32_t s_look[kLookCap];                 // bucketed: slot << 16 | row in chunk
-  __shared__ int32_t s_off[kHB + 1];
-  __shared__ uint32_t s_cnt[kMaxChunks], s_start[kMaxChunks], s_fill[kMaxChunks];
+  __shared__ __align__(16) uint16_t s_c[kHB * kCS];  // count rows [bag][row in chunk]
+  __shared__ float s_scale[kHB];  // output scale per bag; kNoBag: no bag, kLongBag: gathered
+  __shared__ uint32_t s_ent[kWavesPerBlock][kWave * kRegIds];  // per wave, by chunk
+  __shared__ uint32_t s_cnt[kWavesPerBlock][kMaxChunks];
+  __shared__ uint32_t s_fill[kWavesPerBlock][kMaxChunks];
+  __shared__ uint32_t s_start[kWavesPerBlock][kMaxChunks + 1];
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int logical = xcd_contiguous_block(blockIdx.x, gridDim.x);
@@ -152,106 +198,104 @@ __global__ __launch_bounds__(kBlock) void fwd_histogram(HistLaunch a) {
   const int NT = min(kDB, m.dim - d0) >> 4;  // 16-column MFMA tiles
   const int b0 = tile * kHB;
   const int nb = min(kHB, a.B - b0);
-  const int64_t k0 = static_cast<int64_t>(ht.table) * a.B + b0;
-
-  for (int i = tid; i <= nb; i += kBlock) s_off[i] = static_cast<int32_t>(ld_index<IT>(a.offsets, k0 + i));
-  {
-    uint4* c4 = reinterpret_cast<uint4*>(s_c);
-    for (int i = tid; i < kHB * kCS / 8; i += kBlock) c4[i] = make_uint4(0u, 0u, 0u, 0u);
-  }
-  __syncthreads();
-
-  const int lo = s_off[0], hi = s_off[nb];
   const int nchunks = ht.epad / kHistKc;
-  const uint16_t* wt = a.wt + ht.wt_off + static_cast<int64_t>(d0) * ht.epad;
   uint32_t* cw = reinterpret_cast<uint32_t*>(s_c);
 
+  // thread tid owns bag slot tid: its lookups, first kRegIds ids in registers
+  // (ids outside [0, epad) match no chunk)
+  int64_t p0 = 0;
+  int len = 0;
+  if (tid < nb) {
+    const int64_t k = static_cast<int64_t>(ht.table) * a.B + b0 + tid;
+    p0 = ld_index<IT>(a.offsets, k);
+    len = static_cast<int>(ld_index<IT>(a.offsets, k + 1) - p0);
+  }
+  const bool fallback = len > M::kCountCap;  // pooled by the gather loop below
+  int32_t x[kRegIds];
+#pragma unroll
+  for (int j = 0; j < kRegIds; ++j) {
+    int64_t v = -1;
+    if (j < len && !fallback) v = ld_index<IT>(a.indices, p0 + j);
+    x[j] = (v >= 0 && v < ht.epad) ? static_cast<int32_t>(v) : -kHistKc - 1;
+  }
+  const int my_len = fallback ? 0 : len;
+  s_scale[tid] = tid >= nb ? kNoBag
+                 : fallback ? kLongBag
+                            : (a.mean ? (len > 0 ? 1.0f / static_cast<float>(len) : 0.0f) : 1.0f);
+  // this thread's count row (rows of a wave's bags are used by that wave only)
+  {
+    uint4* c4 = reinterpret_cast<uint4*>(s_c + tid * kCS);
+#pragma unroll
+    for (int i = 0; i < kCS / 8; ++i) c4[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+
+  // list the wave's registered lookups by chunk: counts, offsets, then entries
+  if (lane < kMaxChunks) s_cnt[wave][lane] = 0u, s_fill[wave][lane] = 0u;
+#pragma unroll
+  for (int j = 0; j < kRegIds; ++j)
+    if (j < my_len && x[j] >= 0) atomicAdd(&s_cnt[wave][x[j] / kHistKc], 1u);
+  {
+    const uint32_t cnt = lane < kMaxChunks ? s_cnt[wave][lane] : 0u;
+    uint32_t tot;
+    const uint32_t st = wave_excl(cnt, &tot);
+    if (lane < kMaxChunks) s_start[wave][lane] = st;
+    if (lane == 0) s_start[wave][kMaxChunks] = tot;
+  }
+#pragma unroll
+  for (int j = 0; j < kRegIds; ++j)
+    if (j < my_len && x[j] >= 0) {
+      const int c = x[j] / kHistKc;
+      s_ent[wave][s_start[wave][c] + atomicAdd(&s_fill[wave][c], 1u)] =
+          (static_cast<uint32_t>(lane) << 8) | static_cast<uint32_t>(x[j] & (kHistKc - 1));
+    }
+  const bool rest = __any(my_len > kRegIds);  // some bag of the wave has ids beyond registers
+
+  // B operands (W^T) straight from L2 into registers, one chunk ahead:
+  // lane holds column n0 + (lane & 15), rows k0 + ks*32 + (lane >> 4)*8 .. +8
+  const uint16_t* wcol =
+      a.wt + ht.wt_off + static_cast<int64_t>(d0 + (lane & 15)) * ht.epad + (lane >> 4) * 8;
   f32x4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  for (int p0 = lo; p0 < hi; p0 += kLookCap) {
-    const int pn = min(kLookCap, hi - p0);
-    if (tid < kMaxChunks) s_cnt[tid] = 0u, s_fill[tid] = 0u;
-    __syncthreads();
-    // bag slot, row and chunk of this thread's lookups
-    constexpr int PER = kLookCap / kBlock;
-    uint32_t ent[PER];
-    int chk[PER];
+  const int row_base = tid * kCS;
+  __syncthreads();  // s_scale
+  for (int c = 0; c < nchunks; ++c) {
+    const int k0 = c * kHistKc;
+    uint4 bf[2][4];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int q = tid + j * kBlock;
-      chk[j] = -1;
-      if (q < pn) {
-        const int p = p0 + q;
-        int l = 0, r = nb;  // slot with s_off[slot] <= p < s_off[slot + 1]
-        while (r - l > 1) {
-          const int mid = (l + r) >> 1;
-          if (s_off[mid] <= p) l = mid; else r = mid;
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        bf[ks][nt] = nt < NT ? *reinterpret_cast<const uint4*>(
+                                   wcol + static_cast<int64_t>(nt * 16) * ht.epad + k0 + ks * 32)
+                             : make_uint4(0u, 0u, 0u, 0u);
+    // the wave's count rows for chunk c (LDS operations of one wave complete
+    // in order, so no barrier is needed before the reads below)
+    const int es = static_cast<int>(s_start[wave][c]);
+    const int en = static_cast<int>(s_start[wave][c + 1]) - es;
+    add_listed<M>(cw, s_ent[wave] + es, en, wave * 64, 1.0f);
+    bool extra = false;
+    if (rest) extra = __any(add_rest<M, IT>(a, cw, row_base, my_len, p0, k0, 1.0f));
+    if (en == 0 && !extra) continue;  // no lookup of this wave's bags in this chunk
+#pragma unroll
+    for (int ks = 0; ks < kHistKc / 32; ++ks) {
+      const int col = ks * 32 + (lane >> 4) * 8;
+      uint4 af[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        af[mt] = *reinterpret_cast<const uint4*>(s_c + (wave * 64 + mt * 16 + (lane & 15)) * kCS + col);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        if (nt < NT) {
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) acc[mt][nt] = M::mma(af[mt], bf[ks][nt], acc[mt][nt]);
         }
-        const int len = s_off[l + 1] - s_off[l];
-        const int64_t x = ld_index<IT>(a.indices, p);
-        if (len <= M::kCountCap && x >= 0 && x < ht.epad) {
-          chk[j] = static_cast<int>(x) / kHistKc;
-          ent[j] = (static_cast<uint32_t>(l) << 16) | static_cast<uint32_t>(x & (kHistKc - 1));
-          atomicAdd(&s_cnt[chk[j]], 1u);
-        }
-      }
     }
-    __syncthreads();
-    if (tid == 0) {
-      uint32_t run = 0;
-      for (int c = 0; c < nchunks; ++c) s_start[c] = run, run += s_cnt[c];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < PER; ++j)
-      if (chk[j] >= 0) s_look[s_start[chk[j]] + atomicAdd(&s_fill[chk[j]], 1u)] = ent[j];
-    __syncthreads();
-
-    for (int c = 0; c < nchunks; ++c) {
-      const int cn = static_cast<int>(s_cnt[c]);
-      if (cn == 0) continue;  // uniform: the chunk adds nothing
-      const int cs = static_cast<int>(s_start[c]);
-      for (int i = tid; i < cn; i += kBlock) {
-        const uint32_t e = s_look[cs + i];
-        const int el = static_cast<int>(e >> 16) * kCS + static_cast<int>(e & 0xFFFFu);
-        M::lds_add(cw + (el >> 1), el & 1, 1.0f);
-      }
-      // W^T rows d0 .. d0 + 16*NT, columns of chunk c
-      for (int i = tid; i < NT * 16 * 8; i += kBlock) {
-        const int r = i >> 3, c8 = (i & 7) * 8;
-        *reinterpret_cast<uint4*>(s_w + r * kCS + c8) = *reinterpret_cast<const uint4*>(
-            wt + static_cast<int64_t>(r) * ht.epad + c * kHistKc + c8);
-      }
-      __syncthreads();
-#pragma unroll
-      for (int ks = 0; ks < kHistKc / 32; ++ks) {
-        const int col = ks * 32 + (lane >> 4) * 8;
-        uint4 af[4], bf[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          af[mt] = *reinterpret_cast<const uint4*>(s_c + (wave * 64 + mt * 16 + (lane & 15)) * kCS + col);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          if (nt < NT) bf[nt] = *reinterpret_cast<const uint4*>(s_w + (nt * 16 + (lane & 15)) * kCS + col);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          if (nt < NT) {
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) acc[mt][nt] = M::mma(af[mt], bf[nt], acc[mt][nt]);
-          }
-      }
-      __syncthreads();
-      for (int i = tid; i < cn; i += kBlock) {
-        const uint32_t e = s_look[cs + i];
-        const int el = static_cast<int>(e >> 16) * kCS + static_cast<int>(e & 0xFFFFu);
-        M::lds_add(cw + (el >> 1), el & 1, -1.0f);
-      }
-    }
-    __syncthreads();
+    add_listed<M>(cw, s_ent[wave] + es, en, wave * 64, -1.0f);
+    if (extra) add_rest<M, IT>(a, cw, row_base, my_len, p0, k0, -1.0f);
   }
 
   // results: lane holds rows 4*(lane/16) + r of each 16 x 16 tile, column lane % 16
@@ -262,15 +306,12 @@ __global__ __launch_bounds__(kBlock) void fwd_histogram(HistLaunch a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int slot = wave * 64 + mt * 16 + (lane >> 4) * 4 + r;
-      if (slot < nb) {
-        const int len = s_off[slot + 1] - s_off[slot];
-        if (len <= M::kCountCap) {
-          const float sc = a.mean ? (len > 0 ? 1.0f / static_cast<float>(len) : 0.0f) : 1.0f;
-          float* o = obase + static_cast<int64_t>(slot) * a.sum_dims;
+      const float sc = s_scale[slot];
+      if (sc >= 0.0f) {
+        float* o = obase + static_cast<int64_t>(slot) * a.sum_dims;
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt)
-            if (nt < NT) o[nt * 16] = acc[mt][nt][r] * sc;
-        }
+        for (int nt = 0; nt < 4; ++nt)
+          if (nt < NT) o[nt * 16] = acc[mt][nt][r] * sc;
       }
     }
   }
@@ -279,13 +320,14 @@ __global__ __launch_bounds__(kBlock) void fwd_histogram(HistLaunch a) {
   const uint16_t* w = static_cast<const uint16_t*>(a.weights) + m.woff;
   const int DN = NT * 16;
   for (int slot = wave; slot < nb; slot += kWavesPerBlock) {
-    const int s0 = s_off[slot], s1 = s_off[slot + 1];
-    if (s1 - s0 <= M::kCountCap) continue;
+    if (s_scale[slot] != kLongBag) continue;
+    const int64_t kk = static_cast<int64_t>(ht.table) * a.B + b0 + slot;
+    const int64_t s0 = ld_index<IT>(a.offsets, kk), s1 = ld_index<IT>(a.offsets, kk + 1);
     if (lane < DN) {
       float sum = 0.0f;
-      for (int p = s0; p < s1; ++p) {
-        const int64_t x = ld_index<IT>(a.indices, p);
-        const uint32_t u = w[x * m.dim + d0 + lane];
+      for (int64_t p = s0; p < s1; ++p) {
+        const int64_t xr = ld_index<IT>(a.indices, p);
+        const uint32_t u = w[xr * m.dim + d0 + lane];
         sum += ST == kBF16 ? bf16_lo(u) : f16_lo(u);
       }
       const float sc = a.mean ? 1.0f / static_cast<float>(s1 - s0) : 1.0f;

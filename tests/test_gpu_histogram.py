@@ -47,12 +47,20 @@ def test_histogram_int32_indices():
     parity(HIST[0], seed=4, steps=1, index_dtype=torch.int32, flags=FORCE)
 
 
-def test_default_routing_mixes_both_forwards():
-    """Eligible tables (bf16, <= 1024 rows, dims in 16-column tiles) take the count-matrix
-    forward and the others the gather forward, in one call."""
+def test_routing_mixes_both_forwards():
+    """With TBE_FLAG_HISTOGRAM, qualifying tables (bf16, <= 1024 rows, dims in 16-column
+    tiles) take the count-matrix forward and the others the gather forward, in one call."""
     spec = workloads.custom([300, 5000, 64, 40], [32, 32, 24, 512], "bf16", B=130,
                             lengths=("uniform_int", 0, 10), key=306, optimizer="rowwise_adagrad")
-    parity(spec, seed=5, steps=2)
+    parity(spec, seed=5, steps=2, flags=tbe.FLAG_HISTOGRAM)
+
+
+def test_histogram_routing_with_weights_uses_gather():
+    """Per-sample weights rule the count-matrix forward out for the call (the counts would
+    no longer be integers): the routed handle pools such a batch with the gather forward."""
+    spec = workloads.custom([300, 64], [32, 64], "bf16", B=70, lengths=("uniform_int", 0, 10),
+                            psw=True, pooling="mean", key=307)
+    parity(spec, seed=8, steps=1, flags=tbe.FLAG_HISTOGRAM)
 
 
 def test_histogram_and_gather_agree():

@@ -3,16 +3,19 @@
 backward (linearize, radix sort, run-length encode, segment reduce, one row-wise
 Adagrad / SGD update per touched row), through the library's C ABI.
 
-A step is one forward and one backward_update over one batch of the workload.
-Four seeded batches (and upstream gradients) are generated up front, resident
-in HBM, and used in rotation.  Default workload: T=8 tables of 100,000 x 128
+A step is one forward and one backward_update over one batch of the workload
+(tbe_forward + tbe_backward_update; --grouped times tbe_forward_group, which
+runs the backward's grouping of the batch on a second stream beside the pooled
+lookup, + tbe_backward_update_grouped).  Four seeded batches (and
+upstream gradients) are generated up front, resident in HBM, and used in
+rotation.  Default workload: T=8 tables of 100,000 x 128
 fp32 rows, B=2048 bags per table, bag length uniform in 1..32, Zipf(1.05) row
 ids, sum pooling, row-wise Adagrad.
 
 Prints one JSON line:
   value        fwd+bwd lookups per second (lookups of the K timed steps / time)
   roofline     the dominant kernel: algorithmic bytes per launch / its average
-               duration (HIP events on the library's stream, second pass of the
+               duration (the kernel's own start/end events, second pass of the
                same K steps), against the 8 TB/s HBM peak; traffic from the
                committed rocprofv3 counter summary when it matches the current
                kernel source, else null
@@ -48,6 +51,10 @@ def parse():
                    help="gather: the gather forward (the library default); routed: count-matrix "
                         "forward for the tables that qualify; histogram: count-matrix forward "
                         "for every table (all must qualify)")
+    p.add_argument("--grouped", action="store_true",
+                   help="time tbe_forward_group + tbe_backward_update_grouped (the backward's "
+                        "grouping done during the forward, on a second stream beside the pooled "
+                        "lookup) instead of tbe_forward + tbe_backward_update")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain device copy of known size (counter calibration)")
     return p.parse_args()
@@ -242,9 +249,14 @@ def main():
 
     def step(i):
         idx, off, psw, n = batches[i % nrot]
-        tbe.tbe_forward(op.handle, spec.B, idx, off, psw, Y)
-        tbe.tbe_backward_update(op.handle, spec.B, idx, off, psw, grads[i % nrot], spec.lr,
-                                spec.eps, ws)
+        if not args.grouped:
+            tbe.tbe_forward(op.handle, spec.B, idx, off, psw, Y)
+            tbe.tbe_backward_update(op.handle, spec.B, idx, off, psw, grads[i % nrot], spec.lr,
+                                    spec.eps, ws)
+        else:
+            tbe.tbe_forward_group(op.handle, spec.B, idx, off, psw, Y, ws)
+            tbe.tbe_backward_update_grouped(op.handle, spec.B, idx, off, psw, grads[i % nrot],
+                                            spec.lr, spec.eps, ws)
         return n
 
     for i in range(args.warmup):
@@ -344,6 +356,8 @@ def main():
         "data": "synthetic (seeded generator, 4 rotated batches resident in HBM)",
         "config": {"workload": spec.name, "tables": spec.T, "bags_per_table": spec.B,
                    "forward": args.forward,
+                   "calls": "tbe_forward + tbe_backward_update" if not args.grouped
+                            else "tbe_forward_group + tbe_backward_update_grouped",
                    "lookups_per_step": stats["N"], "unique_rows_batch0": stats["U"],
                    "long_run_share_batch0": round(stats["long_run_share"], 3),
                    "max_run_batch0": stats["max_run"]},

@@ -171,15 +171,43 @@ tbe_status tbe_backward_update(tbe_handle* handle, int32_t B, const void* indice
                                float lr, float eps, void* workspace, size_t workspace_bytes,
                                const tbe_runs* runs, void* stream);
 
+/* Forward plus the backward's grouping of the same batch.  kimbodo.com/?p=28372,
+ * "Kimbodo Engineering Perspective": the transpose, sort and run-length
+ * encoding of the backward can be done during the forward (an option that is
+ * off by default there).  Runs tbe_forward on `stream` and, on a second
+ * stream of the handle that starts after the work already queued on `stream`,
+ * linearizes, sorts and run-length encodes the batch into `workspace`
+ * (sized by tbe_backward_workspace_size, 256-byte aligned); `stream` then
+ * waits for that work, so the call completes as one unit on `stream`.  The
+ * grouping does not read the weights, so it runs beside the pooled lookup.
+ * Arguments and errors as tbe_forward, plus TBE_ERR_WORKSPACE_TOO_SMALL.  The
+ * workspace must then go, unchanged and with the same batch (ids, offsets,
+ * per-sample weights, B, num_indices), to tbe_backward_update_grouped;
+ * anything else gives undefined results. */
+tbe_status tbe_forward_group(tbe_handle* handle, int32_t B, const void* indices,
+                             const void* offsets, int32_t index_dtype, int64_t num_indices,
+                             const float* per_sample_weights, float* output, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* tbe_backward_update without the grouping: uses the one a tbe_forward_group
+ * call on the same batch left in `workspace` (same arguments and errors as
+ * tbe_backward_update; the result is bit-identical). */
+tbe_status tbe_backward_update_grouped(tbe_handle* handle, int32_t B, const void* indices,
+                                       const void* offsets, int32_t index_dtype,
+                                       int64_t num_indices, const float* per_sample_weights,
+                                       const float* grad_output, float lr, float eps,
+                                       void* workspace, size_t workspace_bytes,
+                                       const tbe_runs* runs, void* stream);
+
 /* Set a tbe_option (see above). */
 tbe_status tbe_set_option(tbe_handle* handle, int32_t option, int64_t value);
 
 /* With TBE_OPTION_PROFILE on: waits for the recorded events, then writes, for
  * every kernel launched by the calls made since the last read (in launch
  * order, at most capacity), its duration in milliseconds (from the kernel's
- * start to its end, host gaps excluded) to ms and the kernel's static name to names (may be
- * NULL); *count receives the number written.  The recorded events are then
- * dropped. */
+ * start to its end, host gaps excluded) to ms and the kernel's static name to
+ * names (may be NULL); *count receives the number written.  The recorded
+ * events are then dropped. */
 tbe_status tbe_stage_times(tbe_handle* handle, float* ms, const char** names, int32_t capacity,
                            int32_t* count);
 

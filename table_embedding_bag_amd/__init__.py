@@ -18,7 +18,8 @@ from typing import Optional, Sequence
 
 __all__ = [
     "TBEError", "library_path", "load", "tbe_create", "tbe_destroy", "tbe_forward",
-    "tbe_backward_workspace_size", "tbe_backward_update", "tbe_set_option", "tbe_stage_times",
+    "tbe_backward_workspace_size", "tbe_backward_update", "tbe_forward_group",
+    "tbe_backward_update_grouped", "tbe_set_option", "tbe_stage_times",
     "tbe_status_string", "tbe_abi_version", "TBE",
     "F32", "F16", "BF16", "POOL_SUM", "POOL_MEAN", "OPT_SGD", "OPT_ROWWISE_ADAGRAD",
     "FLAG_VALIDATE", "FLAG_NO_HISTOGRAM", "FLAG_FORCE_HISTOGRAM", "FLAG_HISTOGRAM",
@@ -40,8 +41,8 @@ STATUS = {
 
 EXPORTED_SYMBOLS = (
     "tbe_create", "tbe_destroy", "tbe_forward", "tbe_backward_workspace_size",
-    "tbe_backward_update", "tbe_set_option", "tbe_stage_times", "tbe_status_string",
-    "tbe_abi_version",
+    "tbe_backward_update", "tbe_forward_group", "tbe_backward_update_grouped", "tbe_set_option",
+    "tbe_stage_times", "tbe_status_string", "tbe_abi_version",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -89,6 +90,8 @@ def load():
     lib.tbe_backward_workspace_size.argtypes = [P, i32, i64, ctypes.POINTER(ctypes.c_size_t)]
     lib.tbe_backward_update.argtypes = [P, i32, P, P, i32, i64, P, P, f32, f32, P,
                                         ctypes.c_size_t, ctypes.POINTER(_Runs), P]
+    lib.tbe_forward_group.argtypes = [P, i32, P, P, i32, i64, P, P, P, ctypes.c_size_t, P]
+    lib.tbe_backward_update_grouped.argtypes = lib.tbe_backward_update.argtypes
     lib.tbe_set_option.argtypes = [P, i32, i64]
     lib.tbe_stage_times.argtypes = [P, ctypes.POINTER(f32), ctypes.POINTER(ctypes.c_char_p), i32,
                                     ctypes.POINTER(i32)]
@@ -97,6 +100,7 @@ def load():
     lib.tbe_abi_version.argtypes = []
     lib.tbe_abi_version.restype = i32
     for name in ("tbe_create", "tbe_forward", "tbe_backward_workspace_size", "tbe_backward_update",
+                 "tbe_forward_group", "tbe_backward_update_grouped",
                  "tbe_set_option", "tbe_stage_times"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -199,6 +203,30 @@ def tbe_backward_update(handle, B: int, indices, offsets, per_sample_weights, gr
            "tbe_backward_update")
 
 
+def tbe_forward_group(handle, B: int, indices, offsets, per_sample_weights, output, workspace,
+                      stream=None) -> None:
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().tbe_forward_group(handle, B, _ptr(indices), _ptr(offsets),
+                                    _index_dtype(indices, offsets), indices.numel(),
+                                    _ptr(per_sample_weights), _ptr(output), _ptr(workspace), nbytes,
+                                    _stream(stream)),
+           "tbe_forward_group")
+
+
+def tbe_backward_update_grouped(handle, B: int, indices, offsets, per_sample_weights, grad_output,
+                                lr: float, eps: float, workspace, runs=None, stream=None) -> None:
+    r = None
+    if runs is not None:
+        r = ctypes.byref(_Runs(_ptr(runs[0]), _ptr(runs[1]), _ptr(runs[2])))
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().tbe_backward_update_grouped(handle, B, _ptr(indices), _ptr(offsets),
+                                              _index_dtype(indices, offsets), indices.numel(),
+                                              _ptr(per_sample_weights), _ptr(grad_output), float(lr),
+                                              float(eps), _ptr(workspace), nbytes, r,
+                                              _stream(stream)),
+           "tbe_backward_update_grouped")
+
+
 def tbe_set_option(handle, option: int, value: int) -> None:
     _check(load().tbe_set_option(handle, option, int(value)), "tbe_set_option")
 
@@ -254,6 +282,22 @@ class TBE:
         ws = self.workspace(B, indices.numel())
         tbe_backward_update(self.handle, B, indices, offsets, per_sample_weights, grad_output, lr,
                             eps, ws, runs)
+
+    def forward_group(self, B, indices, offsets, per_sample_weights=None, out=None):
+        """Forward plus the backward's grouping of this batch (kept in the handle's workspace
+        for backward_update_grouped)."""
+        import torch
+        if out is None:
+            out = torch.empty((B, self.sum_dims), dtype=torch.float32, device=self.weights.device)
+        ws = self.workspace(B, indices.numel())
+        tbe_forward_group(self.handle, B, indices, offsets, per_sample_weights, out, ws)
+        return out
+
+    def backward_update_grouped(self, B, indices, offsets, per_sample_weights, grad_output, lr,
+                                eps=1e-8, runs=None):
+        ws = self.workspace(B, indices.numel())
+        tbe_backward_update_grouped(self.handle, B, indices, offsets, per_sample_weights,
+                                    grad_output, lr, eps, ws, runs)
 
     def set_option(self, option, value):
         tbe_set_option(self.handle, option, value)

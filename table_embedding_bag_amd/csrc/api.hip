@@ -45,6 +45,10 @@ struct tbe_handle {
   int64_t long_threshold = 256;
   // profiling: pairs of events handed to timed kernel launches (start and end
   // of that kernel), kept until tbe_stage_times reads them
+  // second stream (and fork/join events) on which tbe_forward_group runs the
+  // backward grouping next to the pooled lookup; made on first use
+  hipStream_t side = nullptr;
+  hipEvent_t fork_ev = nullptr, join_ev = nullptr;
   bool profile = false;
   std::vector<hipEvent_t> pool;
   std::vector<std::pair<size_t, const char*>> timed;  // start event index in pool, kernel name
@@ -230,6 +234,119 @@ bool plan_backward(const tbe_handle* h, int64_t n, bool vec, BwdPlan* p) {
   return true;
 }
 
+// The launch description of a backward call on a planned workspace.
+void fill_backward(const tbe_handle* h, int32_t B, const void* indices, const void* offsets,
+                   int32_t index_dtype, int64_t n, const float* psw, const float* grad_output,
+                   float lr, float eps, void* workspace, const tbe_runs* runs, bool vec,
+                   const BwdPlan& p, BackwardLaunch* out) {
+  char* w = static_cast<char*>(workspace);
+  BackwardLaunch& a = *out;
+  a = BackwardLaunch{};
+  a.indices = indices;
+  a.offsets = offsets;
+  a.psw = psw;
+  a.grad = grad_output;
+  a.weights = h->weights;
+  a.state = h->state;
+  a.meta = h->meta;
+  a.num_indices = n;
+  a.num_bags = static_cast<int64_t>(h->T) * B;
+  a.T = h->T;
+  a.B = B;
+  a.sum_dims = h->sum_dims;
+  a.key_bits = h->key_bits;
+  a.mean = h->pooling == TBE_POOL_MEAN;
+  a.index64 = index_dtype == TBE_I64;
+  a.dtype = h->dtype;
+  a.adagrad = h->optimizer == TBE_OPT_ROWWISE_ADAGRAD;
+  a.use_rec = (psw != nullptr) || a.mean;
+  a.vec = vec;
+  a.nch = p.nch;
+  a.gshift = p.gshift;
+  a.pstride = p.pstride;
+  a.long_threshold = static_cast<int32_t>(std::min<int64_t>(h->long_threshold, 0x7FFFFFFF));
+  a.chunk = kChunk;
+  a.lr = lr;
+  a.eps = eps;
+  if (runs) {
+    a.out_unique = runs->unique_ids;
+    a.out_lengths = runs->run_lengths;
+    a.out_num = runs->num_unique;
+  }
+  BackwardBuffers& b = a.buf;
+  for (int i = 0; i < 2; ++i) {
+    b.keys[i] = reinterpret_cast<uint32_t*>(w + p.o_keys[i]);
+    b.vals[i] = reinterpret_cast<uint32_t*>(w + p.o_vals[i]);
+  }
+  b.rec = reinterpret_cast<uint2*>(w + p.o_rec);
+  b.counters = reinterpret_cast<uint32_t*>(w + p.o_zero);
+  b.tickets = b.counters + kNumCounters;
+  b.digit_hist = b.tickets + kNumTickets;
+  b.sort_status = b.digit_hist + p.passes * p.slots;
+  b.rle_status = b.sort_status + static_cast<int64_t>(p.passes) * p.sort_tiles * p.slots;
+  b.zero_words = p.zero_words;
+  b.unique_keys = reinterpret_cast<uint32_t*>(w + p.o_uniq);
+  b.run_start = reinterpret_cast<uint32_t*>(w + p.o_start);
+  b.longs = reinterpret_cast<uint4*>(w + p.o_longs);
+  b.items1 = reinterpret_cast<uint2*>(w + p.o_items1);
+  b.partial1 = reinterpret_cast<float*>(w + p.o_p1);
+}
+
+// The grouping (linearize, sort, run-length encoding) of a backward call.
+// The sorted pair ends in buffer passes % 2.
+hipError_t launch_front(const BackwardLaunch& a, hipStream_t s, const KernelTimer* kt) {
+  hipError_t e = launch_linearize(a, s, kt);
+  if (e != hipSuccess) return e;
+  int sorted = 0;
+  e = launch_radix_sort(a, s, &sorted, kt);
+  if (e != hipSuccess) return e;
+  return launch_run_length_encode(a, a.buf.keys[sorted], s, kt);
+}
+
+tbe_status backward_impl(tbe_handle* h, int32_t B, const void* indices, const void* offsets,
+                         int32_t index_dtype, int64_t n, const float* psw,
+                         const float* grad_output, float lr, float eps, void* workspace,
+                         size_t workspace_bytes, const tbe_runs* runs, hipStream_t s,
+                         bool with_front) {
+  tbe_status st = check_batch_args(h, B, indices, offsets, index_dtype, n);
+  if (st != TBE_OK) return st;
+  if (B > 0 && (!grad_output || !aligned(grad_output, 4))) return TBE_ERR_INVALID_ARGUMENT;
+  if (runs && (!runs->num_unique || (n > 0 && (!runs->unique_ids || !runs->run_lengths))))
+    return TBE_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(lr) || !std::isfinite(eps)) return TBE_ERR_INVALID_ARGUMENT;
+  try {
+    if (B == 0 || n == 0) {
+      if (runs) {
+        hipLaunchKernelGGL(fill_u32, dim3(1), dim3(64), 0, s,
+                           reinterpret_cast<uint32_t*>(runs->num_unique), 0u, int64_t{1});
+        return from_hip(hipGetLastError());
+      }
+      return TBE_OK;
+    }
+    const bool vec = h->bwd_vec && aligned(grad_output, 16);
+    BwdPlan p;
+    if (!plan_backward(h, n, vec, &p)) return TBE_ERR_UNSUPPORTED;
+    if (!workspace || !aligned(workspace, kAlign)) return TBE_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < p.bytes) return TBE_ERR_WORKSPACE_TOO_SMALL;
+    if (h->flags & TBE_FLAG_VALIDATE) {
+      st = run_validation(h, B, indices, offsets, index_dtype, n, s);
+      if (st != TBE_OK) return st;
+    }
+    KernelTimer timer{h, take_events};
+    const KernelTimer* kt = h->profile ? &timer : nullptr;
+    BackwardLaunch a;
+    fill_backward(h, B, indices, offsets, index_dtype, n, psw, grad_output, lr, eps, workspace,
+                  runs, vec, p, &a);
+    if (with_front) {
+      const hipError_t e = launch_front(a, s, kt);
+      if (e != hipSuccess) return TBE_ERR_HIP;
+    }
+    return from_hip(launch_segment_reduce_update(a, a.buf.vals[p.passes % 2], s, kt));
+  } catch (...) {
+    return TBE_ERR_OUT_OF_MEMORY;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -395,6 +512,9 @@ void tbe_destroy(tbe_handle* h) {
   for (auto& e : h->pool) (void)hipEventDestroy(e);
   if (h->meta) (void)hipFree(h->meta);
   if (h->wt) (void)hipFree(h->wt);
+  if (h->fork_ev) (void)hipEventDestroy(h->fork_ev);
+  if (h->join_ev) (void)hipEventDestroy(h->join_ev);
+  if (h->side) (void)hipStreamDestroy(h->side);
   delete h;
 }
 
@@ -523,94 +643,62 @@ tbe_status tbe_backward_update(tbe_handle* h, int32_t B, const void* indices, co
                                int32_t index_dtype, int64_t n, const float* psw,
                                const float* grad_output, float lr, float eps, void* workspace,
                                size_t workspace_bytes, const tbe_runs* runs, void* stream) {
+  return backward_impl(h, B, indices, offsets, index_dtype, n, psw, grad_output, lr, eps,
+                       workspace, workspace_bytes, runs, static_cast<hipStream_t>(stream), true);
+}
+
+tbe_status tbe_backward_update_grouped(tbe_handle* h, int32_t B, const void* indices,
+                                       const void* offsets, int32_t index_dtype, int64_t n,
+                                       const float* psw, const float* grad_output, float lr,
+                                       float eps, void* workspace, size_t workspace_bytes,
+                                       const tbe_runs* runs, void* stream) {
+  return backward_impl(h, B, indices, offsets, index_dtype, n, psw, grad_output, lr, eps,
+                       workspace, workspace_bytes, runs, static_cast<hipStream_t>(stream), false);
+}
+
+tbe_status tbe_forward_group(tbe_handle* h, int32_t B, const void* indices, const void* offsets,
+                             int32_t index_dtype, int64_t n, const float* psw, float* output,
+                             void* workspace, size_t workspace_bytes, void* stream) {
   tbe_status st = check_batch_args(h, B, indices, offsets, index_dtype, n);
   if (st != TBE_OK) return st;
-  if (B > 0 && (!grad_output || !aligned(grad_output, 4))) return TBE_ERR_INVALID_ARGUMENT;
-  if (runs && (!runs->num_unique || (n > 0 && (!runs->unique_ids || !runs->run_lengths))))
-    return TBE_ERR_INVALID_ARGUMENT;
-  if (!std::isfinite(lr) || !std::isfinite(eps)) return TBE_ERR_INVALID_ARGUMENT;
+  if (B == 0) return TBE_OK;
+  if (!output || !aligned(output, 16)) return TBE_ERR_INVALID_ARGUMENT;
+  if (psw && !aligned(psw, 4)) return TBE_ERR_INVALID_ARGUMENT;
+  if (psw && (h->flags & TBE_FLAG_FORCE_HISTOGRAM)) return TBE_ERR_UNSUPPORTED;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   try {
-    if (B == 0 || n == 0) {
-      if (runs) {
-        hipLaunchKernelGGL(fill_u32, dim3(1), dim3(64), 0, s,
-                           reinterpret_cast<uint32_t*>(runs->num_unique), 0u, int64_t{1});
-        return from_hip(hipGetLastError());
-      }
-      return TBE_OK;
-    }
-    const bool vec = h->bwd_vec && aligned(grad_output, 16);
     BwdPlan p;
-    if (!plan_backward(h, n, vec, &p)) return TBE_ERR_UNSUPPORTED;
-    if (!workspace || !aligned(workspace, kAlign)) return TBE_ERR_INVALID_ARGUMENT;
-    if (workspace_bytes < p.bytes) return TBE_ERR_WORKSPACE_TOO_SMALL;
-    if (h->flags & TBE_FLAG_VALIDATE) {
-      st = run_validation(h, B, indices, offsets, index_dtype, n, s);
-      if (st != TBE_OK) return st;
+    BackwardLaunch a{};
+    if (n > 0) {
+      if (!plan_backward(h, n, h->bwd_vec, &p)) return TBE_ERR_UNSUPPORTED;
+      if (!workspace || !aligned(workspace, kAlign)) return TBE_ERR_INVALID_ARGUMENT;
+      if (workspace_bytes < p.bytes) return TBE_ERR_WORKSPACE_TOO_SMALL;
+      fill_backward(h, B, indices, offsets, index_dtype, n, psw, nullptr, 0.0f, 0.0f, workspace,
+                    nullptr, h->bwd_vec, p, &a);
+      if (!h->side) {
+        if (hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess ||
+            hipEventCreateWithFlags(&h->fork_ev, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&h->join_ev, hipEventDisableTiming) != hipSuccess)
+          return TBE_ERR_HIP;
+      }
     }
+    // the pooled lookup (with its own checks and validation) on the caller's stream
+    st = tbe_forward(h, B, indices, offsets, index_dtype, n, psw, output, stream);
+    if (st != TBE_OK || n == 0) return st;
+    // the grouping on the second stream: it starts after the caller's earlier
+    // work (the batch may have been written just before) and the caller's
+    // stream waits for it, so the call completes as one unit on `stream`
     KernelTimer timer{h, take_events};
     const KernelTimer* kt = h->profile ? &timer : nullptr;
-
-    char* w = static_cast<char*>(workspace);
-    BackwardLaunch a{};
-    a.indices = indices;
-    a.offsets = offsets;
-    a.psw = psw;
-    a.grad = grad_output;
-    a.weights = h->weights;
-    a.state = h->state;
-    a.meta = h->meta;
-    a.num_indices = n;
-    a.num_bags = static_cast<int64_t>(h->T) * B;
-    a.T = h->T;
-    a.B = B;
-    a.sum_dims = h->sum_dims;
-    a.key_bits = h->key_bits;
-    a.mean = h->pooling == TBE_POOL_MEAN;
-    a.index64 = index_dtype == TBE_I64;
-    a.dtype = h->dtype;
-    a.adagrad = h->optimizer == TBE_OPT_ROWWISE_ADAGRAD;
-    a.use_rec = (psw != nullptr) || a.mean;
-    a.vec = vec;
-    a.nch = p.nch;
-    a.gshift = p.gshift;
-    a.pstride = p.pstride;
-    a.long_threshold = static_cast<int32_t>(std::min<int64_t>(h->long_threshold, 0x7FFFFFFF));
-    a.chunk = kChunk;
-    a.lr = lr;
-    a.eps = eps;
-    if (runs) {
-      a.out_unique = runs->unique_ids;
-      a.out_lengths = runs->run_lengths;
-      a.out_num = runs->num_unique;
-    }
-    BackwardBuffers& b = a.buf;
-    for (int i = 0; i < 2; ++i) {
-      b.keys[i] = reinterpret_cast<uint32_t*>(w + p.o_keys[i]);
-      b.vals[i] = reinterpret_cast<uint32_t*>(w + p.o_vals[i]);
-    }
-    b.rec = reinterpret_cast<uint2*>(w + p.o_rec);
-    b.counters = reinterpret_cast<uint32_t*>(w + p.o_zero);
-    b.tickets = b.counters + kNumCounters;
-    b.digit_hist = b.tickets + kNumTickets;
-    b.sort_status = b.digit_hist + p.passes * p.slots;
-    b.rle_status = b.sort_status + static_cast<int64_t>(p.passes) * p.sort_tiles * p.slots;
-    b.zero_words = p.zero_words;
-    b.unique_keys = reinterpret_cast<uint32_t*>(w + p.o_uniq);
-    b.run_start = reinterpret_cast<uint32_t*>(w + p.o_start);
-    b.longs = reinterpret_cast<uint4*>(w + p.o_longs);
-    b.items1 = reinterpret_cast<uint2*>(w + p.o_items1);
-    b.partial1 = reinterpret_cast<float*>(w + p.o_p1);
-
-    hipError_t e = launch_linearize(a, s, kt);
+    if (hipEventRecord(h->fork_ev, s) != hipSuccess ||
+        hipStreamWaitEvent(h->side, h->fork_ev, 0) != hipSuccess)
+      return TBE_ERR_HIP;
+    const hipError_t e = launch_front(a, h->side, kt);
     if (e != hipSuccess) return TBE_ERR_HIP;
-    int sorted = 0;
-    e = launch_radix_sort(a, s, &sorted, kt);
-    if (e != hipSuccess) return TBE_ERR_HIP;
-    e = launch_run_length_encode(a, b.keys[sorted], s, kt);
-    if (e != hipSuccess) return TBE_ERR_HIP;
-    e = launch_segment_reduce_update(a, b.vals[sorted], s, kt);
-    return from_hip(e);
+    if (hipEventRecord(h->join_ev, h->side) != hipSuccess ||
+        hipStreamWaitEvent(s, h->join_ev, 0) != hipSuccess)
+      return TBE_ERR_HIP;
+    return TBE_OK;
   } catch (...) {
     return TBE_ERR_OUT_OF_MEMORY;
   }

@@ -255,11 +255,14 @@ def forward_deviation(spec, batch, dev: np.ndarray) -> np.ndarray:
     return out
 
 
-def run_step(pb: Problem, G: torch.Tensor, lr=None, eps=None, with_runs=True):
+def run_step(pb: Problem, G: torch.Tensor, lr=None, eps=None, with_runs=True, grouped=False):
+    """backward_update of the problem's batch (grouped: the variant that reuses the grouping a
+    forward_group call left in the handle's workspace)."""
     spec = pb.spec
     runs = gpu_runs(pb, pb.batch.N) if with_runs else None
-    pb.op.backward_update(spec.B, pb.idx, pb.off, pb.psw, G,
-                          spec.lr if lr is None else lr, spec.eps if eps is None else eps, runs)
+    update = pb.op.backward_update_grouped if grouped else pb.op.backward_update
+    update(spec.B, pb.idx, pb.off, pb.psw, G, spec.lr if lr is None else lr,
+           spec.eps if eps is None else eps, runs)
     torch.cuda.synchronize()
     return runs
 

@@ -94,4 +94,7 @@ def test_null_handle_calls_are_rejected():
     assert lib.tbe_backward_workspace_size(None, 4, 10, ctypes.byref(n)) == 1
     assert lib.tbe_forward(None, 4, None, None, 1, 0, None, None, None) == 1
     assert lib.tbe_set_option(None, 1, 5) == 1
+    assert lib.tbe_forward_group(None, 4, None, None, 1, 0, None, None, None, 0, None) == 1
+    assert lib.tbe_backward_update_grouped(None, 4, None, None, 1, 0, None, None, 0.1, 0.0, None,
+                                           0, None, None) == 1
     lib.tbe_destroy(None)

@@ -24,7 +24,7 @@ def _say(*a):
 
 
 def parity(spec, seed=0, steps=2, bag_sample=None, row_sample=None, index_dtype=torch.int64,
-           threshold=None, batches=None, flags=0):
+           threshold=None, batches=None, flags=0, grouped=False):
     """Forward and backward_update for `steps` steps, each checked against the reference,
     which advances its own copy of weights and state."""
     _say(f"[parity] {spec.name} dtype={spec.dtype} seed={seed} thr={threshold} flags={flags}")
@@ -47,7 +47,10 @@ def parity(spec, seed=0, steps=2, bag_sample=None, row_sample=None, index_dtype=
             sample = np.unique(np.concatenate([
                 rng.choice(nbags, bag_sample, replace=False),
                 np.arange(spec.T) * spec.B, np.arange(1, spec.T + 1) * spec.B - 1]))
-        Y = pb.op.forward(spec.B, pb.idx, pb.off, pb.psw)
+        if grouped:
+            Y = pb.op.forward_group(spec.B, pb.idx, pb.off, pb.psw)
+        else:
+            Y = pb.op.forward(spec.B, pb.idx, pb.off, pb.psw)
         torch.cuda.synchronize()
         report[f"fwd{step}"] = check_forward(pb, Y, W_host, sample, dev)
         _say(f"  step {step}: forward ok (max rel {report[f'fwd{step}']:.2e})")
@@ -60,7 +63,7 @@ def parity(spec, seed=0, steps=2, bag_sample=None, row_sample=None, index_dtype=
             untouched = np.sort(rng.choice(untouched, 20000, replace=False))
         gpu_before = rows_of(spec, pb.W, untouched)
         gpu_st_before = pb.state.cpu().numpy() if pb.state is not None else None
-        runs = run_step(pb, G)
+        runs = run_step(pb, G, grouped=grouped)
         uniq, cnt = check_runs(pb, runs)
         _say(f"  step {step}: runs ok (U={uniq.size}, max run {cnt.max() if cnt.size else 0})")
         if row_sample is not None and uniq.size > row_sample:

@@ -207,7 +207,7 @@ bool plan_backward(const tbe_handle* h, int64_t n, bool vec, BwdPlan* p) {
     }
   }
   p->pstride = static_cast<int32_t>((h->dmax + 3) / 4 * 4);
-  const int64_t sort_tile = static_cast<int64_t>(kBlock) * sort_keys_per_thread(n);
+  const int64_t sort_tile = sort_tile_keys(n, h->key_bits);
   p->sort_tiles = static_cast<int>((n + sort_tile - 1) / sort_tile);
   p->rle_tiles = static_cast<int>((n + kRleTile - 1) / kRleTile);
   p->passes = radix_passes(h->key_bits);

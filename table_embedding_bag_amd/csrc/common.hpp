@@ -271,6 +271,8 @@ constexpr int kNumTickets = 8;           // kMaxRadixPasses radix passes + the R
 
 // Keys per thread of a radix tile for a batch of n lookups (8 or 16).
 int sort_keys_per_thread(int64_t n);
+// Keys per radix tile for a batch of n lookups sorted on key_bits bits.
+int sort_tile_keys(int64_t n, int key_bits);
 
 // Upper bounds of the segment work lists for a batch of n lookups.
 struct SegmentBounds {
@@ -326,14 +328,15 @@ constexpr int kMaxDim = 1024;
 constexpr int kRleTile = 4096;
 
 // LSD radix sort plan for keys of key_bits bits: the fewest passes of at most
-// 8-bit digits, the bits split evenly over the passes.  Every per-pass table
-// (digit counts, look-back status words) has radix_slots(bits) entries: at
-// least 256, so that narrow digits keep one digit per thread.  (Wider digits
-// were measured slower on gfx950: a 10-bit pass costs about twice an 8-bit
-// one -- the look-back then covers 4 digits per thread -- so fewer passes do
-// not pay.)
-constexpr int kMaxRadixBits = 8;
-constexpr int kMaxRadixPasses = 4;  // 32-bit ids
+// 10-bit digits, the bits split evenly over the passes.  Digits of up to 8
+// bits use 256-thread tiles (one digit per thread); 9- and 10-bit digits use
+// 1024-thread tiles of 4096 keys, again one digit per thread, so that the
+// look-back keeps 16 status words in flight per digit (with several digits
+// per thread a 10-bit pass measured twice as slow as an 8-bit one).  Every
+// per-pass table (digit counts, look-back status words) has radix_slots(bits)
+// entries.
+constexpr int kMaxRadixBits = 10;
+constexpr int kMaxRadixPasses = 4;  // ids of up to 31 bits: at most 4 passes
 __host__ __device__ inline int radix_passes(int key_bits) {
   return (key_bits + kMaxRadixBits - 1) / kMaxRadixBits;
 }
@@ -342,7 +345,7 @@ __host__ __device__ inline int radix_digit_bits(int key_bits) {
   return (key_bits + p - 1) / p;
 }
 __host__ __device__ inline int radix_slots(int digit_bits) {
-  return 1 << (digit_bits > 8 ? digit_bits : 8);
+  return digit_bits > 8 ? 1024 : 256;  // the wide pass has 1024 digit slots
 }
 
 }  // namespace tbe

@@ -16,13 +16,15 @@
 //               kernel of its own.
 //   radix pass  one kernel per digit of a stable LSD radix sort on
 //               ceil(log2(sum E_t)) bits, split evenly into the fewest digits
-//               of at most 8 bits.  A tile of 256*KPT keys is ranked in LDS
-//               (equal digits matched within a wave through one ballot per
-//               digit bit, per-wave digit counters), its digit counts are
-//               published and the tile's offset within every digit bucket is
-//               found by a decoupled look-back over the tiles before it; the
-//               tile is then written bucket by bucket so global stores are
-//               coalesced.
+//               of at most 10 bits (20-bit ids: two 10-bit passes).  A tile
+//               of keys is ranked in LDS (equal digits matched within a wave
+//               through one ballot per digit bit, per-wave digit counters),
+//               its digit counts are published and the tile's offset within
+//               every digit bucket is found by a decoupled look-back over the
+//               tiles before it; the tile is then written bucket by bucket so
+//               global stores are coalesced.  Up to 8-bit digits: 256 threads
+//               per tile; 9-10 bits: 1024 threads, so that every thread still
+//               looks back for one digit.
 //   RLE         one kernel: run heads of a 4096-key tile, a look-back over
 //               the head counts of earlier tiles, then unique ids and run
 //               starts.  The number of runs U stays on the device.
@@ -324,6 +326,122 @@ __global__ __launch_bounds__(kBlock) void radix_pass(
   }
 }
 
+// Exclusive prefix sum over a block of NW waves; *total receives the sum.
+template <int NW>
+__device__ __forceinline__ uint32_t block_excl_n(uint32_t x, uint32_t* scratch, uint32_t* total) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_inclusive_sum(x);
+  if (lane == kWave - 1) scratch[wave] = incl;
+  __syncthreads();
+  uint32_t base = 0, sum = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t s = scratch[w];
+    base += (w < wave) ? s : 0u;
+    sum += s;
+  }
+  __syncthreads();
+  *total = sum;
+  return base + incl - x;
+}
+
+// A pass on digits wider than 8 bits: 1024 threads, one digit per thread
+// (2^RB = 1024 digits), so the look-back keeps 16 status words in flight per
+// digit as in the 8-bit pass.
+template <int KPT, int RB>
+__global__ __launch_bounds__(1024) void radix_pass_wide(
+    const uint32_t* __restrict__ kin, const uint32_t* __restrict__ vin, uint32_t* __restrict__ kout,
+    uint32_t* __restrict__ vout, int64_t n, int shift, int bits, const uint32_t* __restrict__ totals,
+    uint32_t* status, uint32_t* ticket, uint32_t* err) {
+  constexpr int NT = 1024, NW = NT / kWave;
+  constexpr int TS = NT * KPT;
+  constexpr int RMAX = 1 << RB;
+  static_assert(RMAX == NT, "one digit per thread");
+  __shared__ uint32_t s_k[TS];
+  __shared__ uint32_t s_v[TS];
+  __shared__ uint32_t s_cnt[NW][RMAX];
+  __shared__ uint32_t s_dstart[RMAX];
+  __shared__ uint32_t s_gbase[RMAX];
+  __shared__ uint32_t scratch[NW];
+  __shared__ uint32_t s_tile;
+
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const uint32_t my_total = totals[tid];
+  if (tid == 0) s_tile = ticket ? atomicAdd(ticket, 1u) : blockIdx.x;
+  for (int i = tid; i < NW * RMAX; i += NT) (&s_cnt[0][0])[i] = 0u;
+  __syncthreads();
+  const int tile = static_cast<int>(s_tile);
+  const int64_t base = static_cast<int64_t>(tile) * TS;
+  const uint32_t dmask = (1u << bits) - 1u;
+  const int64_t seg = base + static_cast<int64_t>(wave) * (kWave * KPT);
+  uint32_t key[KPT], val[KPT], rank[KPT];
+#pragma unroll
+  for (int r = 0; r < KPT; ++r) {
+    const int64_t p = seg + r * kWave + lane;
+    const bool ok = p < n;
+    key[r] = ok ? kin[p] : 0u;
+    val[r] = ok ? vin[p] : 0u;
+  }
+#pragma unroll
+  for (int r = 0; r < KPT; ++r) {
+    const bool ok = (seg + r * kWave + lane) < n;
+    const uint32_t d = (key[r] >> shift) & dmask;
+    uint64_t peers = __ballot(ok);
+#pragma unroll
+    for (int bit = 0; bit < RB; ++bit) {
+      const bool set = (d >> bit) & 1u;
+      const uint64_t bal = __ballot(set);
+      peers &= set ? bal : ~bal;
+    }
+    const uint32_t below = popc_below(peers);
+    const uint32_t cnt = __popcll(peers);
+    const uint32_t pre = ok ? s_cnt[wave][d] : 0u;
+    rank[r] = pre + below;
+    if (ok && below == 0) s_cnt[wave][d] = pre + cnt;
+  }
+  __syncthreads();
+  uint32_t mine = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t c = s_cnt[w][tid];
+    s_cnt[w][tid] = mine;
+    mine += c;
+  }
+  uint32_t total;
+  s_dstart[tid] = block_excl_n<NW>(mine, scratch, &total);
+  uint32_t* my_status = status + static_cast<int64_t>(tile) * RMAX + tid;
+  st_status(my_status, (tile == 0 ? kFlagIncl : kFlagAgg) | mine);
+  uint32_t before[1] = {0u};
+  if (tile > 0) {
+    lookback_digits<1, 16>(status, RMAX, tile, tid, err, before);
+    st_status(my_status, kFlagIncl | ((before[0] + mine) & kValueMask));
+  }
+  const uint32_t gb = block_excl_n<NW>(my_total, scratch, &total);
+  s_gbase[tid] = gb + before[0];
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < KPT; ++r) {
+    const bool ok = (seg + r * kWave + lane) < n;
+    if (ok) {
+      const uint32_t d = (key[r] >> shift) & dmask;
+      const uint32_t lp = s_dstart[d] + s_cnt[wave][d] + rank[r];
+      s_k[lp] = key[r];
+      s_v[lp] = val[r];
+    }
+  }
+  __syncthreads();
+  const int tile_n = static_cast<int>(min(static_cast<int64_t>(TS), n - base));
+  for (int i = tid; i < tile_n; i += NT) {
+    const uint32_t k = s_k[i];
+    const uint32_t d = (k >> shift) & dmask;
+    const uint32_t gp = s_gbase[d] + (static_cast<uint32_t>(i) - s_dstart[d]);
+    if (gp < static_cast<uint64_t>(n)) {
+      kout[gp] = k;
+      vout[gp] = s_v[i];
+    }
+  }
+}
+
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
 #pragma unroll
   for (int o = kWave >> 1; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
@@ -422,6 +540,9 @@ __global__ __launch_bounds__(kBlock) void rle_kernel(const uint32_t* __restrict_
 }  // namespace
 
 int sort_keys_per_thread(int64_t n) { return n <= (int64_t{1} << 20) ? 8 : 16; }
+int sort_tile_keys(int64_t n, int key_bits) {
+  return radix_digit_bits(key_bits) > 8 ? 4096 : kBlock * sort_keys_per_thread(n);
+}
 
 hipError_t launch_linearize(const BackwardLaunch& a, hipStream_t stream, const KernelTimer* kt) {
   // zero the counters, histograms and look-back status words first
@@ -446,7 +567,7 @@ hipError_t launch_radix_sort(const BackwardLaunch& a, hipStream_t stream, int* r
                              const KernelTimer* kt) {
   const int64_t n = a.num_indices;
   const int kpt = sort_keys_per_thread(n);
-  const int64_t ts = static_cast<int64_t>(kBlock) * kpt;
+  const int64_t ts = sort_tile_keys(n, a.key_bits);
   const int ntiles = static_cast<int>((n + ts - 1) / ts);
   const int passes = radix_passes(a.key_bits), bits = radix_digit_bits(a.key_bits);
   const int slots = radix_slots(bits);
@@ -455,13 +576,18 @@ hipError_t launch_radix_sort(const BackwardLaunch& a, hipStream_t stream, int* r
     uint32_t* status = a.buf.sort_status + static_cast<int64_t>(pass) * ntiles * slots;
     const uint32_t* totals = a.buf.digit_hist + pass * slots;
     uint32_t* ticket = ntiles <= kResidentTiles ? nullptr : a.buf.tickets + pass;
-    if (kpt == 8)
-      launch_timed(kt, "radix_pass", radix_pass<8, kMaxRadixBits>, dim3(ntiles), dim3(kBlock), 0,
+    if (bits > 8)
+      launch_timed(kt, "radix_pass", radix_pass_wide<4, 10>, dim3(ntiles), dim3(1024), 0,
+                   stream, a.buf.keys[cur], a.buf.vals[cur], a.buf.keys[cur ^ 1],
+                   a.buf.vals[cur ^ 1], n, pass * bits, bits, totals, status, ticket,
+                   a.buf.counters + kCntError);
+    else if (kpt == 8)
+      launch_timed(kt, "radix_pass", radix_pass<8, 8>, dim3(ntiles), dim3(kBlock), 0,
                    stream, a.buf.keys[cur], a.buf.vals[cur], a.buf.keys[cur ^ 1],
                    a.buf.vals[cur ^ 1], n, pass * bits, bits, totals, status, ticket,
                    a.buf.counters + kCntError);
     else
-      launch_timed(kt, "radix_pass", radix_pass<16, kMaxRadixBits>, dim3(ntiles), dim3(kBlock), 0,
+      launch_timed(kt, "radix_pass", radix_pass<16, 8>, dim3(ntiles), dim3(kBlock), 0,
                    stream, a.buf.keys[cur], a.buf.vals[cur], a.buf.keys[cur ^ 1],
                    a.buf.vals[cur ^ 1], n, pass * bits, bits, totals, status, ticket,
                    a.buf.counters + kCntError);

@@ -44,7 +44,7 @@ constexpr uint32_t kFlagAgg = 1u << 30;     // status word: this tile's own coun
 constexpr uint32_t kFlagIncl = 2u << 30;    // status word: count up to and including this tile
 constexpr uint32_t kValueMask = (1u << 30) - 1u;
 constexpr uint32_t kSpinLimit = 1u << 20;   // polls before a waiting tile gives up
-constexpr int kLinBags = 64;                // bags per linearize tile
+constexpr int kLinBags = 128;               // bags per linearize tile
 constexpr int64_t kLinMaxBlocks = 1024;     // linearize grid bound
 constexpr int kResidentTiles = 256;         // grids this small are resident all at once
 
@@ -66,14 +66,14 @@ __global__ __launch_bounds__(kBlock) void init_workspace(uint32_t* words, int64_
     words[i] = 0u;
 }
 
-// Workgroups stride over tiles of 64 consecutive bags.  A tile's offsets are
-// staged in LDS; the workgroup then walks all of its lookups with consecutive
-// threads on consecutive lookups and finds each lookup's bag by binary search
-// in LDS.  Digit counts are kept in LDS across the workgroup's tiles and
+// Workgroups of 1024 threads stride over tiles of 128 consecutive bags.  A
+// tile's offsets are staged in LDS; the workgroup then walks all of its
+// lookups with consecutive threads on consecutive lookups and finds each
+// lookup's bag by binary search in LDS.  Digit counts are kept in LDS across the workgroup's tiles and
 // added to the global counts once at the end (a bounded grid keeps those
 // global atomics, all on the same few hundred words, few).
 template <typename IT>
-__global__ __launch_bounds__(kBlock) void linearize_kernel(BackwardLaunch a) {
+__global__ __launch_bounds__(1024) void linearize_kernel(BackwardLaunch a) {
   __shared__ int64_t s_off[kLinBags + 1];
   __shared__ uint32_t s_roff[kLinBags];
   __shared__ float s_scale[kLinBags];
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(kBlock) void linearize_kernel(BackwardLaunch a) {
   const int bits = radix_digit_bits(a.key_bits);
   const int slots = radix_slots(bits);
   const uint32_t dmask = (1u << bits) - 1u;
-  for (int i = tid; i < passes * slots; i += kBlock) s_hist[i] = 0u;
+  for (int i = tid; i < passes * slots; i += 1024) s_hist[i] = 0u;
   const int64_t ntiles = (a.num_bags + kLinBags - 1) / kLinBags;
   for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     const int64_t k0 = tile * kLinBags;
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(kBlock) void linearize_kernel(BackwardLaunch a) {
     __syncthreads();
 
     const int64_t p0 = s_off[0], p1 = s_off[nb];
-    for (int64_t p = p0 + tid; p < p1; p += kBlock) {
+    for (int64_t p = p0 + tid; p < p1; p += 1024) {
       int lo = 0, hi = nb;  // bag slot s with s_off[s] <= p < s_off[s + 1]
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -141,7 +141,7 @@ __global__ __launch_bounds__(kBlock) void linearize_kernel(BackwardLaunch a) {
     }
   }
   __syncthreads();
-  for (int i = tid; i < passes * slots; i += kBlock)
+  for (int i = tid; i < passes * slots; i += 1024)
     if (s_hist[i]) atomicAdd(&a.buf.digit_hist[i], s_hist[i]);
 }
 
@@ -477,22 +477,24 @@ __device__ uint32_t lookback_wave(uint32_t* status, int tile, uint32_t* err) {
   }
 }
 
-// Run heads of a 4096-key tile (staged in LDS with the key before it); each
-// thread owns 16 consecutive positions so run ids follow position order.
-__global__ __launch_bounds__(kBlock) void rle_kernel(const uint32_t* __restrict__ keys, int64_t n,
+// Run heads of a 4096-key tile (staged in LDS with the key before it), 1024
+// threads per tile; each thread owns 4 consecutive positions so run ids
+// follow position order.
+__global__ __launch_bounds__(1024) void rle_kernel(const uint32_t* __restrict__ keys, int64_t n,
                                                      int ntiles, uint32_t* status, uint32_t* ticket,
                                                      uint32_t* counters, uint32_t* unique_keys,
                                                      uint32_t* run_start) {
-  constexpr int PER = kRleTile / kBlock;
+  constexpr int NT = 1024;
+  constexpr int PER = kRleTile / NT;
   __shared__ uint32_t s_k[kRleTile + 1];
-  __shared__ uint32_t scratch[kWavesPerBlock];
+  __shared__ uint32_t scratch[NT / kWave];
   __shared__ uint32_t s_tile, s_base;
   const int tid = threadIdx.x;  // every write below is clamped in range
   if (tid == 0) s_tile = ticket ? atomicAdd(ticket, 1u) : blockIdx.x;
   __syncthreads();
   const int tile = static_cast<int>(s_tile);
   const int64_t base = static_cast<int64_t>(tile) * kRleTile;
-  for (int i = tid; i < kRleTile + 1; i += kBlock) {
+  for (int i = tid; i < kRleTile + 1; i += NT) {
     const int64_t p = base - 1 + i;
     s_k[i] = (p >= 0 && p < n) ? keys[p] : 0u;
   }
@@ -505,7 +507,7 @@ __global__ __launch_bounds__(kBlock) void rle_kernel(const uint32_t* __restrict_
     if (p < n && (p == 0 || s_k[i + 1] != s_k[i])) ++c;
   }
   uint32_t total;
-  uint32_t r = block_exclusive_sum(c, scratch, &total);
+  uint32_t r = block_excl_n<NT / kWave>(c, scratch, &total);
   if (tid < kWave) {
     if (tid == 0) st_status(status + tile, (tile == 0 ? kFlagIncl : kFlagAgg) | total);
     uint32_t before = 0;
@@ -556,10 +558,10 @@ hipError_t launch_linearize(const BackwardLaunch& a, hipStream_t stream, const K
   if (blocks > kLinMaxBlocks) blocks = kLinMaxBlocks;
   if (a.index64)
     launch_timed(kt, "linearize_kernel", linearize_kernel<int64_t>,
-                 dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, stream, a);
+                 dim3(static_cast<unsigned>(blocks)), dim3(1024), 0, stream, a);
   else
     launch_timed(kt, "linearize_kernel", linearize_kernel<int32_t>,
-                 dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, stream, a);
+                 dim3(static_cast<unsigned>(blocks)), dim3(1024), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -603,7 +605,7 @@ hipError_t launch_run_length_encode(const BackwardLaunch& a, const uint32_t* sor
                                     hipStream_t stream, const KernelTimer* kt) {
   const int64_t n = a.num_indices;
   const int ntiles = static_cast<int>((n + kRleTile - 1) / kRleTile);
-  launch_timed(kt, "rle_kernel", rle_kernel, dim3(ntiles), dim3(kBlock), 0, stream, sorted_keys, n, ntiles,
+  launch_timed(kt, "rle_kernel", rle_kernel, dim3(ntiles), dim3(1024), 0, stream, sorted_keys, n, ntiles,
                      a.buf.rle_status,
                      ntiles <= kResidentTiles ? nullptr : a.buf.tickets + kMaxRadixPasses,
                      a.buf.counters,

@@ -210,8 +210,8 @@ bool plan_backward(const tbe_handle* h, int64_t n, bool vec, BwdPlan* p) {
   const int64_t sort_tile = sort_tile_keys(n, h->key_bits);
   p->sort_tiles = static_cast<int>((n + sort_tile - 1) / sort_tile);
   p->rle_tiles = static_cast<int>((n + kRleTile - 1) / kRleTile);
-  p->passes = radix_passes(h->key_bits);
-  p->slots = radix_slots(radix_digit_bits(h->key_bits));
+  p->passes = radix_passes(h->key_bits, n);
+  p->slots = radix_slots(radix_digit_bits(h->key_bits, n));
   const SegmentBounds ub = segment_bounds(n, h->long_threshold, kChunk, p->gshift);
   p->long_ub = ub.longs;
   p->chunks_ub = ub.chunks;

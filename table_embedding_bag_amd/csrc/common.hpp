@@ -327,21 +327,25 @@ constexpr int kMaxDim = 1024;
 // Tile sizes shared by the planner (workspace sizing) and the kernels.
 constexpr int kRleTile = 4096;
 
-// LSD radix sort plan for keys of key_bits bits: the fewest passes of at most
-// 10-bit digits, the bits split evenly over the passes.  Digits of up to 8
-// bits use 256-thread tiles (one digit per thread); 9- and 10-bit digits use
-// 1024-thread tiles of 4096 keys, again one digit per thread, so that the
-// look-back keeps 16 status words in flight per digit (with several digits
-// per thread a 10-bit pass measured twice as slow as an 8-bit one).  Every
-// per-pass table (digit counts, look-back status words) has radix_slots(bits)
-// entries.
+// LSD radix sort plan for n keys of key_bits bits: the fewest passes of
+// digits of at most kMaxRadixBits bits, the bits split evenly over the
+// passes.  Digits of up to 8 bits use 256-thread tiles (one digit per
+// thread); 9- and 10-bit digits use 1024-thread tiles of 4096 keys, again one
+// digit per thread, so that the look-back keeps 16 status words in flight per
+// digit (with several digits per thread a 10-bit pass measured twice as slow
+// as an 8-bit one).  Wide digits pay only while a pass is bound by latency
+// (batches of up to 2^20 lookups); larger batches are bound by bandwidth and
+// sort with 8-bit digits.  Every per-pass table (digit counts, look-back
+// status words) has radix_slots(bits) entries.
 constexpr int kMaxRadixBits = 10;
 constexpr int kMaxRadixPasses = 4;  // ids of up to 31 bits: at most 4 passes
-__host__ __device__ inline int radix_passes(int key_bits) {
-  return (key_bits + kMaxRadixBits - 1) / kMaxRadixBits;
+constexpr int64_t kWideRadixMaxKeys = int64_t{1} << 20;
+__host__ __device__ inline int radix_passes(int key_bits, int64_t n) {
+  const int w = n <= kWideRadixMaxKeys ? kMaxRadixBits : 8;
+  return (key_bits + w - 1) / w;
 }
-__host__ __device__ inline int radix_digit_bits(int key_bits) {
-  const int p = radix_passes(key_bits);
+__host__ __device__ inline int radix_digit_bits(int key_bits, int64_t n) {
+  const int p = radix_passes(key_bits, n);
   return (key_bits + p - 1) / p;
 }
 __host__ __device__ inline int radix_slots(int digit_bits) {

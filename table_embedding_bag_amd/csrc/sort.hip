@@ -80,8 +80,8 @@ __global__ __launch_bounds__(1024) void linearize_kernel(BackwardLaunch a) {
   __shared__ uint32_t s_hist[kMaxRadixPasses << kMaxRadixBits];
 
   const int tid = threadIdx.x;
-  const int passes = radix_passes(a.key_bits);
-  const int bits = radix_digit_bits(a.key_bits);
+  const int passes = radix_passes(a.key_bits, a.num_indices);
+  const int bits = radix_digit_bits(a.key_bits, a.num_indices);
   const int slots = radix_slots(bits);
   const uint32_t dmask = (1u << bits) - 1u;
   for (int i = tid; i < passes * slots; i += 1024) s_hist[i] = 0u;
@@ -543,7 +543,7 @@ __global__ __launch_bounds__(1024) void rle_kernel(const uint32_t* __restrict__ 
 
 int sort_keys_per_thread(int64_t n) { return n <= (int64_t{1} << 20) ? 8 : 16; }
 int sort_tile_keys(int64_t n, int key_bits) {
-  return radix_digit_bits(key_bits) > 8 ? 4096 : kBlock * sort_keys_per_thread(n);
+  return radix_digit_bits(key_bits, n) > 8 ? 4096 : kBlock * sort_keys_per_thread(n);
 }
 
 hipError_t launch_linearize(const BackwardLaunch& a, hipStream_t stream, const KernelTimer* kt) {
@@ -571,7 +571,8 @@ hipError_t launch_radix_sort(const BackwardLaunch& a, hipStream_t stream, int* r
   const int kpt = sort_keys_per_thread(n);
   const int64_t ts = sort_tile_keys(n, a.key_bits);
   const int ntiles = static_cast<int>((n + ts - 1) / ts);
-  const int passes = radix_passes(a.key_bits), bits = radix_digit_bits(a.key_bits);
+  const int passes = radix_passes(a.key_bits, a.num_indices);
+  const int bits = radix_digit_bits(a.key_bits, a.num_indices);
   const int slots = radix_slots(bits);
   int cur = 0;
   for (int pass = 0; pass < passes; ++pass) {

@@ -59,6 +59,8 @@ def _load():
     lib.tbe_oracle_runs.restype = ctypes.c_int
     lib.tbe_oracle_dense_grad.argtypes = [i32, P, P, i32, i64, P, P, i64, P, P, P]
     lib.tbe_oracle_dense_grad.restype = ctypes.c_int
+    lib.tbe_oracle_psw_grad.argtypes = [i32, P, P, i32, i32, P, i64, P, P, i64, P, P]
+    lib.tbe_oracle_psw_grad.restype = ctypes.c_int
     lib.tbe_oracle_backward_update.argtypes = [i32, P, P, i32, i32, i32, P, P, i64, P, P, i64,
                                                P, P, f64, f64, i64, P]
     lib.tbe_oracle_backward_update.restype = ctypes.c_int
@@ -164,6 +166,18 @@ def dense_grad(rows, dims, pooling, B, indices, offsets, psw, grad_output):
     rc = _load().tbe_oracle_dense_grad(len(rows), _ptr(rows), _ptr(dims), pooling, B, _ptr(indices),
                                        _ptr(offsets), indices.size, _ptr(psw), _ptr(g), _ptr(out))
     _check(rc, "dense_grad")
+    return out
+
+
+def psw_grad(rows, dims, dtype, pooling, weights, B, indices, offsets, grad_output):
+    """dL/dp_i for every lookup (float64 [N])."""
+    rows, dims, indices, offsets = _i64(rows), _i32(dims), _i64(indices), _i64(offsets)
+    g = np.ascontiguousarray(grad_output, dtype=np.float32)
+    w = _storage_view(dtype, np.ascontiguousarray(weights))
+    out = np.empty(indices.size, dtype=np.float64)
+    rc = _load().tbe_oracle_psw_grad(len(rows), _ptr(rows), _ptr(dims), dtype, pooling, _ptr(w), B,
+                                     _ptr(indices), _ptr(offsets), indices.size, _ptr(g), _ptr(out))
+    _check(rc, "psw_grad")
     return out
 
 

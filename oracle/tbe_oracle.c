@@ -412,6 +412,43 @@ int tbe_oracle_dense_grad(int32_t T, const int64_t* rows, const int32_t* dims, i
   return rc;
 }
 
+/* Gradient of the loss with respect to every per-sample weight (the pages
+ * take per-sample weights in the forward: kimbodo.com/?p=28372, "What
+ * Happened").  The forward is linear in p_i,
+ * Y[b, doff_t + d] = s_k * sum_i p_i * W_t[x_i, d], so
+ * dL/dp_i = s_k * sum_d G[b, doff_t + d] * W_t[x_i, d].
+ * grad_psw: fp64 [num_indices]. */
+int tbe_oracle_psw_grad(int32_t T, const int64_t* rows, const int32_t* dims, int32_t dtype,
+                        int32_t pooling, const void* weights, int64_t B, const int64_t* indices,
+                        const int64_t* offsets, int64_t num_indices, const float* grad_output,
+                        double* grad_psw) {
+  layout_t L;
+  int rc = layout_init(&L, T, rows, dims);
+  if (rc == 0 && (!weights || (num_indices > 0 && (!grad_psw || !grad_output)))) rc = -1;
+  if (rc == 0) rc = check_batch(&L, B, indices, offsets, num_indices);
+  if (rc == 0) {
+    const int64_t nbags = (int64_t)T * B;
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t k = 0; k < nbags; ++k) {
+      const int64_t t = k / B, b = k % B;
+      const int64_t D = dims[t];
+      const int64_t begin = offsets[k], end = offsets[k + 1];
+      const double s = (pooling == ORACLE_POOL_MEAN && end > begin) ? 1.0 / (double)(end - begin)
+                                                                     : 1.0;
+      const float* g = grad_output + b * L.sum_dims + L.doff[t];
+      for (int64_t i = begin; i < end; ++i) {
+        const int64_t row = L.woff[t] + indices[i] * D;
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; ++d)
+          dot += (double)g[d] * tbe_oracle_widen(dtype, load_bits(dtype, weights, row + d));
+        grad_psw[i] = s * dot;
+      }
+    }
+  }
+  layout_free(&L);
+  return rc;
+}
+
 static int is_selected(int64_t key, int64_t n, const int64_t* sel) {
   int64_t lo = 0, hi = n;
   while (lo < hi) {

@@ -76,6 +76,14 @@ int tbe_oracle_dense_grad(int32_t T, const int64_t* rows, const int32_t* dims, i
                           int64_t num_indices, const float* per_sample_weights,
                           const float* grad_output, double* grad);
 
+/* dL/dp_i for every lookup: s_k * sum_d grad_output[b, doff_t + d] *
+ * W_t[x_i, d] (the forward is linear in the per-sample weights).
+ * grad_psw: fp64 [num_indices]. */
+int tbe_oracle_psw_grad(int32_t T, const int64_t* rows, const int32_t* dims, int32_t dtype,
+                        int32_t pooling, const void* weights, int64_t B, const int64_t* indices,
+                        const int64_t* offsets, int64_t num_indices, const float* grad_output,
+                        double* grad_psw);
+
 /* Backward with the fused optimizer: exactly one update per touched row.
  * weights (storage dtype) and state (fp32, one per table row, indexed by the
  * linear row id; may be NULL for SGD) are updated in place.

@@ -157,6 +157,18 @@ tbe_status tbe_forward(tbe_handle* handle, int32_t B, const void* indices, const
                        int32_t index_dtype, int64_t num_indices,
                        const float* per_sample_weights, float* output, void* stream);
 
+/* Gradient of the loss with respect to the per-sample weights: for every
+ * lookup i of bag k = (t, b), grad_psw[i] = s_k * <grad_output[b, doff_t :
+ * doff_t + D_t], W_t[x_i]>, with s_k = 1 (sum) or 1 / L_k (mean).  The pages
+ * take per-sample weights in the forward (kimbodo.com/?p=28372, "What
+ * Happened"); the forward is linear in them, which gives this gradient.  It
+ * reads the weights, so call it before tbe_backward_update changes them.
+ * grad_output: device fp32 [B, sum D]; grad_psw: device fp32 [num_indices],
+ * written.  Errors as tbe_forward. */
+tbe_status tbe_psw_grad(tbe_handle* handle, int32_t B, const void* indices, const void* offsets,
+                        int32_t index_dtype, int64_t num_indices, const float* grad_output,
+                        float* grad_psw, void* stream);
+
 /* Bytes of device workspace tbe_backward_update needs for this batch shape. */
 tbe_status tbe_backward_workspace_size(const tbe_handle* handle, int32_t B, int64_t num_indices,
                                        size_t* bytes);

@@ -19,7 +19,7 @@ from typing import Optional, Sequence
 __all__ = [
     "TBEError", "library_path", "load", "tbe_create", "tbe_destroy", "tbe_forward",
     "tbe_backward_workspace_size", "tbe_backward_update", "tbe_forward_group",
-    "tbe_backward_update_grouped", "tbe_set_option", "tbe_stage_times",
+    "tbe_backward_update_grouped", "tbe_psw_grad", "tbe_set_option", "tbe_stage_times",
     "tbe_status_string", "tbe_abi_version", "TBE",
     "F32", "F16", "BF16", "POOL_SUM", "POOL_MEAN", "OPT_SGD", "OPT_ROWWISE_ADAGRAD",
     "FLAG_VALIDATE", "FLAG_NO_HISTOGRAM", "FLAG_FORCE_HISTOGRAM", "FLAG_HISTOGRAM",
@@ -41,8 +41,8 @@ STATUS = {
 
 EXPORTED_SYMBOLS = (
     "tbe_create", "tbe_destroy", "tbe_forward", "tbe_backward_workspace_size",
-    "tbe_backward_update", "tbe_forward_group", "tbe_backward_update_grouped", "tbe_set_option",
-    "tbe_stage_times", "tbe_status_string", "tbe_abi_version",
+    "tbe_backward_update", "tbe_forward_group", "tbe_backward_update_grouped", "tbe_psw_grad",
+    "tbe_set_option", "tbe_stage_times", "tbe_status_string", "tbe_abi_version",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -92,6 +92,7 @@ def load():
                                         ctypes.c_size_t, ctypes.POINTER(_Runs), P]
     lib.tbe_forward_group.argtypes = [P, i32, P, P, i32, i64, P, P, P, ctypes.c_size_t, P]
     lib.tbe_backward_update_grouped.argtypes = lib.tbe_backward_update.argtypes
+    lib.tbe_psw_grad.argtypes = [P, i32, P, P, i32, i64, P, P, P]
     lib.tbe_set_option.argtypes = [P, i32, i64]
     lib.tbe_stage_times.argtypes = [P, ctypes.POINTER(f32), ctypes.POINTER(ctypes.c_char_p), i32,
                                     ctypes.POINTER(i32)]
@@ -100,7 +101,7 @@ def load():
     lib.tbe_abi_version.argtypes = []
     lib.tbe_abi_version.restype = i32
     for name in ("tbe_create", "tbe_forward", "tbe_backward_workspace_size", "tbe_backward_update",
-                 "tbe_forward_group", "tbe_backward_update_grouped",
+                 "tbe_forward_group", "tbe_backward_update_grouped", "tbe_psw_grad",
                  "tbe_set_option", "tbe_stage_times"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -227,6 +228,13 @@ def tbe_backward_update_grouped(handle, B: int, indices, offsets, per_sample_wei
            "tbe_backward_update_grouped")
 
 
+def tbe_psw_grad(handle, B: int, indices, offsets, grad_output, grad_psw, stream=None) -> None:
+    _check(load().tbe_psw_grad(handle, B, _ptr(indices), _ptr(offsets),
+                               _index_dtype(indices, offsets), indices.numel(), _ptr(grad_output),
+                               _ptr(grad_psw), _stream(stream)),
+           "tbe_psw_grad")
+
+
 def tbe_set_option(handle, option: int, value: int) -> None:
     _check(load().tbe_set_option(handle, option, int(value)), "tbe_set_option")
 
@@ -298,6 +306,14 @@ class TBE:
         ws = self.workspace(B, indices.numel())
         tbe_backward_update_grouped(self.handle, B, indices, offsets, per_sample_weights,
                                     grad_output, lr, eps, ws, runs)
+
+    def psw_grad(self, B, indices, offsets, grad_output, out=None):
+        """dL/dp for every lookup (fp32 [N]); call before backward_update changes the weights."""
+        import torch
+        if out is None:
+            out = torch.empty(indices.numel(), dtype=torch.float32, device=self.weights.device)
+        tbe_psw_grad(self.handle, B, indices, offsets, grad_output, out)
+        return out
 
     def set_option(self, option, value):
         tbe_set_option(self.handle, option, value)

@@ -631,6 +631,51 @@ tbe_status tbe_forward(tbe_handle* h, int32_t B, const void* indices, const void
   }
 }
 
+tbe_status tbe_psw_grad(tbe_handle* h, int32_t B, const void* indices, const void* offsets,
+                        int32_t index_dtype, int64_t n, const float* grad_output, float* grad_psw,
+                        void* stream) {
+  tbe_status st = check_batch_args(h, B, indices, offsets, index_dtype, n);
+  if (st != TBE_OK) return st;
+  if (B == 0 || n == 0) return TBE_OK;
+  if (!grad_output || !grad_psw || !aligned(grad_output, 4) || !aligned(grad_psw, 4))
+    return TBE_ERR_INVALID_ARGUMENT;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  try {
+    const double mean_len = static_cast<double>(n) / (static_cast<double>(h->T) * B);
+    int lshift = 0;
+    while (lshift < 6 && (int64_t{kFwdUnroll} << lshift) < mean_len) ++lshift;
+    int64_t tiles = 1;
+    for (int t = 0; t < h->T; ++t) {
+      const int sw = std::min(6, h->meta_host[t].fwd_gshift + lshift);
+      const int64_t bags_per_block = int64_t{kWavesPerBlock} << (6 - sw);
+      tiles = std::max<int64_t>(tiles, (B + bags_per_block - 1) / bags_per_block);
+    }
+    if (tiles * h->T > 0x7FFFFFFF) return TBE_ERR_UNSUPPORTED;
+    if (h->flags & TBE_FLAG_VALIDATE) {
+      st = run_validation(h, B, indices, offsets, index_dtype, n, s);
+      if (st != TBE_OK) return st;
+    }
+    KernelTimer timer{h, take_events};
+    ForwardLaunch a{};
+    a.weights = h->weights;
+    a.indices = indices;
+    a.offsets = offsets;
+    a.meta = h->meta;
+    a.T = h->T;
+    a.B = B;
+    a.sum_dims = h->sum_dims;
+    a.tiles_per_table = static_cast<int32_t>(tiles);
+    a.lshift = lshift;
+    a.mean = h->pooling == TBE_POOL_MEAN;
+    a.dtype = h->dtype;
+    a.index64 = index_dtype == TBE_I64;
+    a.vec = h->fwd_vec;
+    return from_hip(launch_psw_grad(a, grad_output, grad_psw, s, h->profile ? &timer : nullptr));
+  } catch (...) {
+    return TBE_ERR_OUT_OF_MEMORY;
+  }
+}
+
 tbe_status tbe_backward_workspace_size(const tbe_handle* h, int32_t B, int64_t n, size_t* bytes) {
   if (!h || !bytes || B < 0 || n < 0) return TBE_ERR_INVALID_ARGUMENT;
   BwdPlan p;

@@ -209,6 +209,9 @@ struct ForwardLaunch {
 };
 hipError_t launch_forward_gather(const ForwardLaunch& a, hipStream_t stream,
                                  const KernelTimer* kt);
+// dL/dp_i for every lookup (a.table_list must be null: all tables).
+hipError_t launch_psw_grad(const ForwardLaunch& a, const float* grad, float* gpsw,
+                           hipStream_t stream, const KernelTimer* kt);
 
 // Count-matrix forward of small 16-bit tables.  Each such table has a
 // transposed, zero-padded copy W^T[d][e] (e < epad, epad a multiple of

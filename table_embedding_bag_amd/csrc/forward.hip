@@ -140,6 +140,88 @@ __global__ __launch_bounds__(kBlock) void fwd_gather_pool(ForwardLaunch a) {
   }
 }
 
+// Gradient with respect to the per-sample weights: the forward is linear in
+// p_i, so dL/dp_i = s_k * <G[b, doff_t : doff_t + D_t], W_t[x_i]>.  Same lane
+// layout as the forward: a lane group covers a row in 16-byte chunks, a
+// sub-wave serves a bag, and each lane group computes the dot products of
+// kUnroll lookups at a time (the bag's gradient chunk is loaded once per
+// chunk set and shared by them), folded across the group's lanes.
+template <int ST, typename IT, bool VEC>
+__global__ __launch_bounds__(kBlock) void psw_grad(ForwardLaunch a, const float* __restrict__ grad,
+                                                   float* __restrict__ gpsw) {
+  constexpr int SB = StorageTraits<ST>::bytes;
+  constexpr int VE = VEC ? 16 / SB : 1;
+  const int logical = xcd_contiguous_block(blockIdx.x, gridDim.x);
+  const int t = logical / a.tiles_per_table;
+  const int tile = logical - t * a.tiles_per_table;
+  const TableMeta m = a.meta[t];
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int gshift = m.fwd_gshift;
+  const int swshift = min(6, gshift + a.lshift);
+  const int SW = 1 << swshift;
+  const int Gs = 1 << gshift;
+  const int R = SW >> gshift;
+  const int sl = lane & (SW - 1);
+  const int g = sl >> gshift;
+  const int gl = sl & (Gs - 1);
+  const int sub_base = lane & ~(SW - 1);
+  const int b = ((tile * kWavesPerBlock + wave) << (6 - swshift)) + (lane >> swshift);
+  const bool bag_ok = b < a.B;
+  const int64_t k = static_cast<int64_t>(t) * a.B + b;
+  int64_t start = 0, end = 0;
+  if (bag_ok) {
+    start = ld_index<IT>(a.offsets, k);
+    end = ld_index<IT>(a.offsets, k + 1);
+  }
+  const int D = m.dim;
+  const int C = VEC ? D / VE : D;
+  const void* wbase = static_cast<const char*>(a.weights) + m.woff * SB;
+  const float scale = (a.mean && end > start) ? 1.0f / static_cast<float>(end - start) : 1.0f;
+  const float* grow = grad + static_cast<int64_t>(b) * a.sum_dims + m.doff;
+  for (int64_t j0 = start; j0 < end; j0 += SW) {
+    const int n = static_cast<int>(min(static_cast<int64_t>(SW), end - j0));
+    int my_row = 0;
+    if (sl < n) my_row = static_cast<int>(ld_index<IT>(a.indices, j0 + sl));
+    for (int r = 0; r < n; r += R * kUnroll) {
+      float dot[kUnroll];
+      int rows[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        dot[u] = 0.0f;
+        rows[u] = __shfl(my_row, sub_base + min(r + u * R + g, SW - 1), kWave);
+      }
+      for (int cb = 0; cb < C; cb += Gs) {
+        const int chunk = cb + gl;
+        const bool lane_ok = chunk < C;
+        float gv[VE];
+#pragma unroll
+        for (int e = 0; e < VE; ++e) gv[e] = lane_ok ? grow[chunk * VE + e] : 0.0f;
+        float w[kUnroll][VE];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          if (r + u * R + g < n && lane_ok) {
+            load_widen<ST, VE>(wbase, static_cast<int64_t>(rows[u]) * D + chunk * VE, w[u]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < VE; ++e) w[u][e] = 0.0f;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+          for (int e = 0; e < VE; ++e) dot[u] = fmaf(w[u][e], gv[e], dot[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        for (int o = Gs >> 1; o >= 1; o >>= 1) dot[u] += __shfl_xor(dot[u], o, kWave);
+        const int jj = r + u * R + g;
+        if (gl == 0 && jj < n) gpsw[j0 + jj] = dot[u] * scale;
+      }
+    }
+  }
+}
+
 template <int ST, typename IT>
 hipError_t dispatch_vec_psw(const ForwardLaunch& a, hipStream_t s, dim3 grid,
                             const KernelTimer* kt) {
@@ -164,6 +246,24 @@ hipError_t dispatch_index(const ForwardLaunch& a, hipStream_t s, dim3 grid,
                    : dispatch_vec_psw<ST, int32_t>(a, s, grid, kt);
 }
 
+template <int ST, typename IT>
+void launch_psw(const ForwardLaunch& a, const float* grad, float* gpsw, hipStream_t s, dim3 grid,
+                const KernelTimer* kt) {
+  if (a.vec)
+    launch_timed(kt, "psw_grad", psw_grad<ST, IT, true>, grid, dim3(kBlock), 0, s, a, grad, gpsw);
+  else
+    launch_timed(kt, "psw_grad", psw_grad<ST, IT, false>, grid, dim3(kBlock), 0, s, a, grad, gpsw);
+}
+
+template <int ST>
+void launch_psw_index(const ForwardLaunch& a, const float* grad, float* gpsw, hipStream_t s,
+                      dim3 grid, const KernelTimer* kt) {
+  if (a.index64)
+    launch_psw<ST, int64_t>(a, grad, gpsw, s, grid, kt);
+  else
+    launch_psw<ST, int32_t>(a, grad, gpsw, s, grid, kt);
+}
+
 }  // namespace
 
 hipError_t launch_forward_gather(const ForwardLaunch& a, hipStream_t stream,
@@ -178,6 +278,25 @@ hipError_t launch_forward_gather(const ForwardLaunch& a, hipStream_t stream,
     case kBF16: return dispatch_index<kBF16>(a, stream, grid, kt);
     default: return hipErrorInvalidValue;
   }
+}
+
+}  // namespace tbe
+
+namespace tbe {
+
+hipError_t launch_psw_grad(const ForwardLaunch& a, const float* grad, float* gpsw,
+                           hipStream_t stream, const KernelTimer* kt) {
+  const int64_t blocks = static_cast<int64_t>(a.T) * a.tiles_per_table;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<unsigned>(blocks));
+  switch (a.dtype) {
+    case kF32: launch_psw_index<kF32>(a, grad, gpsw, stream, grid, kt); break;
+    case kF16: launch_psw_index<kF16>(a, grad, gpsw, stream, grid, kt); break;
+    case kBF16: launch_psw_index<kBF16>(a, grad, gpsw, stream, grid, kt); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace tbe

@@ -97,4 +97,5 @@ def test_null_handle_calls_are_rejected():
     assert lib.tbe_forward_group(None, 4, None, None, 1, 0, None, None, None, 0, None) == 1
     assert lib.tbe_backward_update_grouped(None, 4, None, None, 1, 0, None, None, 0.1, 0.0, None,
                                            0, None, None) == 1
+    assert lib.tbe_psw_grad(None, 4, None, None, 1, 0, None, None, None) == 1
     lib.tbe_destroy(None)

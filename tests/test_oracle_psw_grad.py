@@ -5,7 +5,7 @@ them: Y[b, doff_t + d] = s_k * sum_i p_i * W_t[x_i, d].  Hence
 dL/dp_i = s_k * <G[b, doff_t : doff_t + D_t], W_t[x_i]> for L = <G, Y>.
 
 Pins: torch autograd through embedding_bag in float64 (library), exact finite differences of
-<G, forward(p)> (the forward is linear in p, so a dyadic step is exact), the mean-pooling scale,
+<G, forward(p)> (the forward is linear in p, so only fp64 rounding remains), the mean-pooling scale,
 and an empty batch.
 """
 import numpy as np

@@ -669,7 +669,8 @@ tbe_status tbe_psw_grad(tbe_handle* h, int32_t B, const void* indices, const voi
     a.mean = h->pooling == TBE_POOL_MEAN;
     a.dtype = h->dtype;
     a.index64 = index_dtype == TBE_I64;
-    a.vec = h->fwd_vec;
+    // 16-byte row chunks of the weights need 16-byte aligned gradient rows too
+    a.vec = h->fwd_vec && aligned(grad_output, 16);
     return from_hip(launch_psw_grad(a, grad_output, grad_psw, s, h->profile ? &timer : nullptr));
   } catch (...) {
     return TBE_ERR_OUT_OF_MEMORY;

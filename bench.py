@@ -160,9 +160,13 @@ def kernel_source_hash():
 def committed_traffic(kernel, workload_tag):
     """HBM bytes per launch from profiles/<kernel>_<workload>_counters.txt, if it was
     taken on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload_tag}_counters.txt")
-    if not os.path.exists(path):
+    # a radix pass is timed as one stage whichever kernel variant ran it
+    names = {"radix_pass": ("radix_pass", "radix_pass_wide")}.get(kernel, (kernel,))
+    paths = [os.path.join(ROOT, "profiles", f"{k}_{workload_tag}_counters.txt") for k in names]
+    paths = [p for p in paths if os.path.exists(p)]
+    if not paths:
         return None
+    path = paths[0]
     kv = {}
     for line in open(path):
         if ":" in line and not line.startswith("#"):

@@ -191,7 +191,10 @@ tbe_status tbe_backward_update(tbe_handle* handle, int32_t B, const void* indice
  * linearizes, sorts and run-length encodes the batch into `workspace`
  * (sized by tbe_backward_workspace_size, 256-byte aligned); `stream` then
  * waits for that work, so the call completes as one unit on `stream`.  The
- * grouping does not read the weights, so it runs beside the pooled lookup.
+ * grouping does not read the weights, so it runs beside the pooled lookup
+ * (with TBE_FLAG_VALIDATE the ids are checked before either part is queued).
+ * The ordering between the two streams costs some microseconds, so on small
+ * batches the pair of grouped calls can be slower than the plain ones.
  * Arguments and errors as tbe_forward, plus TBE_ERR_WORKSPACE_TOO_SMALL.  The
  * workspace must then go, unchanged and with the same batch (ids, offsets,
  * per-sample weights, B, num_indices), to tbe_backward_update_grouped;

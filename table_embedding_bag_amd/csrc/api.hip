@@ -553,9 +553,13 @@ tbe_status tbe_stage_times(tbe_handle* h, float* ms, const char** names, int32_t
   return TBE_OK;
 }
 
-tbe_status tbe_forward(tbe_handle* h, int32_t B, const void* indices, const void* offsets,
-                       int32_t index_dtype, int64_t n, const float* psw, float* output,
-                       void* stream) {
+}  // extern "C"
+
+namespace {
+
+tbe_status forward_impl(tbe_handle* h, int32_t B, const void* indices, const void* offsets,
+                        int32_t index_dtype, int64_t n, const float* psw, float* output,
+                        hipStream_t s, bool validate) {
   tbe_status st = check_batch_args(h, B, indices, offsets, index_dtype, n);
   if (st != TBE_OK) return st;
   if (B == 0) return TBE_OK;
@@ -563,7 +567,6 @@ tbe_status tbe_forward(tbe_handle* h, int32_t B, const void* indices, const void
   if (psw && !aligned(psw, 4)) return TBE_ERR_INVALID_ARGUMENT;
   // per-sample weights rule out the count-matrix forward
   if (psw && (h->flags & TBE_FLAG_FORCE_HISTOGRAM)) return TBE_ERR_UNSUPPORTED;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
   try {
     // Sub-wave size: enough lane groups per bag that one round of row loads
     // covers a mean-length bag.
@@ -577,7 +580,7 @@ tbe_status tbe_forward(tbe_handle* h, int32_t B, const void* indices, const void
       tiles = std::max<int64_t>(tiles, (B + bags_per_block - 1) / bags_per_block);
     }
     if (tiles * h->T > 0x7FFFFFFF) return TBE_ERR_UNSUPPORTED;
-    if (h->flags & TBE_FLAG_VALIDATE) {
+    if (validate && (h->flags & TBE_FLAG_VALIDATE)) {
       st = run_validation(h, B, indices, offsets, index_dtype, n, s);
       if (st != TBE_OK) return st;
     }
@@ -629,6 +632,17 @@ tbe_status tbe_forward(tbe_handle* h, int32_t B, const void* indices, const void
   } catch (...) {
     return TBE_ERR_OUT_OF_MEMORY;
   }
+}
+
+}  // namespace
+
+extern "C" {
+
+tbe_status tbe_forward(tbe_handle* h, int32_t B, const void* indices, const void* offsets,
+                       int32_t index_dtype, int64_t n, const float* psw, float* output,
+                       void* stream) {
+  return forward_impl(h, B, indices, offsets, index_dtype, n, psw, output,
+                      static_cast<hipStream_t>(stream), true);
 }
 
 tbe_status tbe_psw_grad(tbe_handle* h, int32_t B, const void* indices, const void* offsets,
@@ -728,12 +742,16 @@ tbe_status tbe_forward_group(tbe_handle* h, int32_t B, const void* indices, cons
           return TBE_ERR_HIP;
       }
     }
-    // the pooled lookup (with its own checks and validation) on the caller's stream
-    st = tbe_forward(h, B, indices, offsets, index_dtype, n, psw, output, stream);
-    if (st != TBE_OK || n == 0) return st;
-    // the grouping on the second stream: it starts after the caller's earlier
-    // work (the batch may have been written just before) and the caller's
-    // stream waits for it, so the call completes as one unit on `stream`
+    if (n == 0) return tbe_forward(h, B, indices, offsets, index_dtype, n, psw, output, stream);
+    // ids are checked (when asked) before either half is enqueued
+    if (h->flags & TBE_FLAG_VALIDATE) {
+      st = run_validation(h, B, indices, offsets, index_dtype, n, s);
+      if (st != TBE_OK) return st;
+    }
+    // The grouping runs on the second stream next to the pooled lookup: it
+    // starts after the caller's earlier work (the batch may have been written
+    // just before), and the caller's stream waits for it, so the call
+    // completes as one unit on `stream`.
     KernelTimer timer{h, take_events};
     const KernelTimer* kt = h->profile ? &timer : nullptr;
     if (hipEventRecord(h->fork_ev, s) != hipSuccess ||
@@ -741,10 +759,12 @@ tbe_status tbe_forward_group(tbe_handle* h, int32_t B, const void* indices, cons
       return TBE_ERR_HIP;
     const hipError_t e = launch_front(a, h->side, kt);
     if (e != hipSuccess) return TBE_ERR_HIP;
+    st = forward_impl(h, B, indices, offsets, index_dtype, n, psw, output, s, false);
+    // join even when the forward failed, so that no work is left unordered
     if (hipEventRecord(h->join_ev, h->side) != hipSuccess ||
         hipStreamWaitEvent(s, h->join_ev, 0) != hipSuccess)
       return TBE_ERR_HIP;
-    return TBE_OK;
+    return st;
   } catch (...) {
     return TBE_ERR_OUT_OF_MEMORY;
   }

@@ -341,7 +341,8 @@ tbe_status backward_impl(tbe_handle* h, int32_t B, const void* indices, const vo
       const hipError_t e = launch_front(a, s, kt);
       if (e != hipSuccess) return TBE_ERR_HIP;
     }
-    return from_hip(launch_segment_reduce_update(a, a.buf.vals[p.passes % 2], s, kt));
+    return from_hip(launch_segment_reduce_update(a, a.buf.keys[p.passes % 2],
+                                                 a.buf.vals[p.passes % 2], s, kt));
   } catch (...) {
     return TBE_ERR_OUT_OF_MEMORY;
   }

@@ -259,8 +259,9 @@ struct BackwardBuffers {
   int64_t zero_words;       // size of the zeroed region, in 32-bit words
   uint32_t* unique_keys;    // [N]
   uint32_t* run_start;      // [N + 1]
-  uint2* items1;            // workgroup items: {run, medium flag} or {long run, chunk}
-  uint4* longs;             // {run, first chunk partial, chunk count, 0}
+  uint2* items1;            // workgroup items: {first position, medium flag | length}
+                            // or {long run, chunk}
+  uint4* longs;             // {first position, length, first chunk partial, chunk count}
   float* partial1;          // [chunks cap, pstride]
 };
 
@@ -317,8 +318,9 @@ hipError_t launch_radix_sort(const BackwardLaunch& a, hipStream_t stream, int* r
                              const KernelTimer* kt);
 hipError_t launch_run_length_encode(const BackwardLaunch& a, const uint32_t* sorted_keys,
                                     hipStream_t stream, const KernelTimer* kt);
-hipError_t launch_segment_reduce_update(const BackwardLaunch& a, const uint32_t* sorted_vals,
-                                        hipStream_t stream, const KernelTimer* kt);
+hipError_t launch_segment_reduce_update(const BackwardLaunch& a, const uint32_t* sorted_keys,
+                                        const uint32_t* sorted_vals, hipStream_t stream,
+                                        const KernelTimer* kt);
 
 // Row loads a forward lane group issues before it accumulates (shared by the
 // kernel and the host planner that sizes sub-waves from the mean bag length).

@@ -98,7 +98,9 @@ __device__ __forceinline__ void lookup_of(const BackwardLaunch& a, uint32_t val,
   }
 }
 
-// This lane's chunks of gradient row b of table m (zeros where absent).
+// This lane's chunks of gradient row b of table m (zeros where absent),
+// loads under a predicate: for the short-run gather, whose unroll already
+// matches the run's length.
 template <int VE, int NCH>
 __device__ __forceinline__ void load_grad(const BackwardLaunch& a, const TableMeta& m, int64_t b,
                                           int gl, int Gs, bool valid, float (&v)[NCH][VE]) {
@@ -118,6 +120,37 @@ __device__ __forceinline__ void load_grad(const BackwardLaunch& a, const TableMe
     } else {
 #pragma unroll
       for (int q = 0; q < VE; ++q) v[c][q] = 0.0f;
+    }
+  }
+}
+
+// The same, branch-free: absent chunks load from the start of G and are
+// zeroed after, so the loads of several rows stay in flight together (a load
+// under a branch whose other side writes the same registers is waited for at
+// once).  For the workgroup items, whose unrolled batches are mostly full.
+template <int VE, int NCH>
+__device__ __forceinline__ void load_grad_all(const BackwardLaunch& a, const TableMeta& m,
+                                              int64_t b, int gl, int Gs, bool valid,
+                                              float (&v)[NCH][VE]) {
+  const int64_t row = b * a.sum_dims + m.doff;
+  const int C = m.dim / VE;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int chunk = c * Gs + gl;
+    const bool ok = valid && chunk < C;
+    const float* src = a.grad + (ok ? row + chunk * VE : 0);
+    if constexpr (VE == 4) {
+      const float4 x = *reinterpret_cast<const float4*>(src);
+      v[c][0] = ok ? x.x : 0.0f;
+      v[c][1] = ok ? x.y : 0.0f;
+      v[c][2] = ok ? x.z : 0.0f;
+      v[c][3] = ok ? x.w : 0.0f;
+    } else {
+#pragma unroll
+      for (int q = 0; q < VE; ++q) {
+        const float x = src[q];
+        v[c][q] = ok ? x : 0.0f;
+      }
     }
   }
 }
@@ -307,11 +340,16 @@ __global__ __launch_bounds__(kBlock) void seg_short(BackwardLaunch a, const uint
       const uint32_t li = __shfl(base[0] + x_long, leader, kWave);
       const uint32_t b1 = __shfl(base[1] + x_chunks, leader, kWave);
       const uint32_t it = __shfl(base[2] + x_items1, leader, kWave);
+      // items carry the run's first position and length, so the workgroup
+      // kernels need no run-list lookup
       if (is_long) {
-        if (ld) a.buf.longs[li] = make_uint4(r, b1, n1, 0u);
+        if (ld)
+          a.buf.longs[li] =
+              make_uint4(static_cast<uint32_t>(s), static_cast<uint32_t>(len), b1, n1);
         for (uint32_t c = gl; c < n1; c += Gs) a.buf.items1[it + c] = make_uint2(li, c);
       } else if (is_medium && ld) {
-        a.buf.items1[it] = make_uint2(r, kMediumItem);
+        a.buf.items1[it] =
+            make_uint2(static_cast<uint32_t>(s), kMediumItem | static_cast<uint32_t>(len));
       }
     }
     if (!valid || len > Gs) continue;
@@ -377,7 +415,8 @@ __device__ __forceinline__ double block_sum(double x, double* scratch) {
 }
 
 template <int ST, int VE, int NCH, bool REC>
-__global__ __launch_bounds__(kBlock) void seg_wg(BackwardLaunch a, const uint32_t* sorted_vals) {
+__global__ __launch_bounds__(kBlock) void seg_wg(BackwardLaunch a, const uint32_t* __restrict__ keys,
+                                                 const uint32_t* __restrict__ sorted_vals) {
   if (a.buf.counters[kCntError] != 0u) return;  // a look-back wait gave up earlier
   constexpr int NV = VE * NCH;                 // values per lane
   constexpr int kElemsPerThread = kMaxDim / kBlock;
@@ -396,19 +435,16 @@ __global__ __launch_bounds__(kBlock) void seg_wg(BackwardLaunch a, const uint32_
   for (uint32_t item = blockIdx.x; item < n; item += gridDim.x) {
     const uint2 it = a.buf.items1[item];
     const bool medium = (it.y & kMediumItem) != 0;
-    uint32_t r, slot = 0;
+    uint32_t slot = 0;
     int64_t s, e;
-    if (medium) {
-      r = it.x;
-      s = a.buf.run_start[r];
-      e = a.buf.run_start[r + 1];
-    } else {
+    if (medium) {  // {first position, medium flag | length}
+      s = it.x;
+      e = s + (it.y & ~kMediumItem);
+    } else {       // {long run, chunk}
       const uint4 L = a.buf.longs[it.x];
-      r = L.x;
-      const int64_t rs = a.buf.run_start[r], re = a.buf.run_start[r + 1];
-      s = rs + static_cast<int64_t>(it.y) * a.chunk;
-      e = min(re, s + a.chunk);
-      slot = L.y + it.y;
+      s = static_cast<int64_t>(L.x) + static_cast<int64_t>(it.y) * a.chunk;
+      e = min(static_cast<int64_t>(L.x) + L.y, s + a.chunk);
+      slot = L.z + it.y;
     }
     const int t = table_of_run<REC>(a, sorted_vals, s);
     const TableMeta m = a.meta[t];
@@ -430,7 +466,7 @@ __global__ __launch_bounds__(kBlock) void seg_wg(BackwardLaunch a, const uint32_
           const bool ok = jj < nb;
           const uint32_t bag = ok ? s_bag[jj] : static_cast<uint32_t>(tb);
           cf[u] = ok ? s_coef[jj] : 0.0f;
-          load_grad<VE, NCH>(a, m, static_cast<int64_t>(bag) - tb, gl, Gs, ok, v[u]);
+          load_grad_all<VE, NCH>(a, m, static_cast<int64_t>(bag) - tb, gl, Gs, ok, v[u]);
         }
 #pragma unroll
         for (int u = 0; u < kU; ++u) accumulate<VE, NCH>(acc, cf[u], v[u]);
@@ -455,7 +491,7 @@ __global__ __launch_bounds__(kBlock) void seg_wg(BackwardLaunch a, const uint32_
       ss = fma(x, x, ss);
     }
     if (medium) {
-      const uint32_t key = a.buf.unique_keys[r];
+      const uint32_t key = keys[s];
       if (a.adagrad) ss = block_sum(ss, s_scratch);
       const float step = step_size(a, key, ss, D, tid == 0);
       const int64_t row0 = m.woff + static_cast<int64_t>(key - static_cast<uint32_t>(m.roff)) * D;
@@ -487,7 +523,8 @@ __global__ __launch_bounds__(kBlock) void seg_wg(BackwardLaunch a, const uint32_
 // the result does not depend on scheduling.  The row to update and its state
 // are loaded while the partials are in flight.
 template <int ST, int VE, int NCH, bool REC>
-__global__ __launch_bounds__(kBlock) void seg_finalize(BackwardLaunch a, const uint32_t* sorted_vals) {
+__global__ __launch_bounds__(kBlock) void seg_finalize(BackwardLaunch a,
+                                                       const uint32_t* __restrict__ keys) {
   if (a.buf.counters[kCntError] != 0u) return;  // a look-back wait gave up earlier
   constexpr int NV = VE * NCH;
   constexpr int kElemsPerThread = kMaxDim / kBlock;
@@ -503,8 +540,8 @@ __global__ __launch_bounds__(kBlock) void seg_finalize(BackwardLaunch a, const u
   const int row_elems = Gs * NV;
   const uint32_t n = a.buf.counters[kCntLong];
   for (uint32_t li = blockIdx.x; li < n; li += gridDim.x) {
-    const uint4 L = a.buf.longs[li];
-    const uint32_t key = a.buf.unique_keys[L.x];
+    const uint4 L = a.buf.longs[li];  // {first position, length, first partial, chunks}
+    const uint32_t key = keys[L.x];
     const TableMeta m = meta_of(a, s_meta, table_of_key(a, s_meta, key));
     const int D = m.dim, C = D / VE;
     const int64_t row0 = m.woff + static_cast<int64_t>(key - static_cast<uint32_t>(m.roff)) * D;
@@ -518,16 +555,16 @@ __global__ __launch_bounds__(kBlock) void seg_finalize(BackwardLaunch a, const u
     const float m_old = a.adagrad ? a.state[key] : 0.0f;
     Acc<VE, NCH> acc;
     acc.zero();
-    for (uint32_t c0 = g; c0 < L.z; c0 += static_cast<uint32_t>(ngroups * kU)) {
+    for (uint32_t c0 = g; c0 < L.w; c0 += static_cast<uint32_t>(ngroups * kU)) {
       float v[kU][NCH][VE];
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const uint32_t c = c0 + static_cast<uint32_t>(u * ngroups);
-        const float* row = a.buf.partial1 + static_cast<int64_t>(L.y + c) * a.pstride;
+        const float* row = a.buf.partial1 + static_cast<int64_t>(L.z + c) * a.pstride;
 #pragma unroll
         for (int q = 0; q < NCH; ++q) {
           const int chunk = q * Gs + gl;
-          if (c < L.z && chunk < C) {
+          if (c < L.w && chunk < C) {
             if constexpr (VE == 4) {
               const float4 x = *reinterpret_cast<const float4*>(row + chunk * 4);
               v[u][q][0] = x.x; v[u][q][1] = x.y; v[u][q][2] = x.z; v[u][q][3] = x.w;
@@ -594,37 +631,37 @@ int64_t blocks_for(int64_t items, int gshift) {
 }
 
 template <int ST, int VE, int NCH, bool REC>
-hipError_t run_segments(const BackwardLaunch& a, const uint32_t* sorted_vals, hipStream_t s,
-                        const KernelTimer* kt) {
+hipError_t run_segments(const BackwardLaunch& a, const uint32_t* keys, const uint32_t* sorted_vals,
+                        hipStream_t s, const KernelTimer* kt) {
   const int64_t n = a.num_indices;
   const SegmentBounds ub = segment_bounds(n, a.long_threshold, a.chunk, a.gshift);
   launch_timed(kt, "seg_short", seg_short<ST, VE, NCH, REC>, dim3(blocks_for(n, a.gshift)),
                dim3(kBlock), 0, s, a, sorted_vals);
   const int64_t wg = ub.items1 < kMaxSegBlocks ? (ub.items1 > 0 ? ub.items1 : 1) : kMaxSegBlocks;
-  launch_timed(kt, "seg_wg", seg_wg<ST, VE, NCH, REC>, dim3(wg), dim3(kBlock), 0, s, a,
+  launch_timed(kt, "seg_wg", seg_wg<ST, VE, NCH, REC>, dim3(wg), dim3(kBlock), 0, s, a, keys,
                sorted_vals);
   const int64_t fin = ub.longs < kMaxSegBlocks ? ub.longs : kMaxSegBlocks;
   launch_timed(kt, "seg_finalize", seg_finalize<ST, VE, NCH, REC>, dim3(fin), dim3(kBlock), 0, s,
-               a, sorted_vals);
+               a, keys);
   return hipGetLastError();
 }
 
 template <int ST, int VE, int NCH>
-hipError_t dispatch_rec(const BackwardLaunch& a, const uint32_t* v, hipStream_t s,
-                        const KernelTimer* kt) {
-  return a.use_rec ? run_segments<ST, VE, NCH, true>(a, v, s, kt)
-                   : run_segments<ST, VE, NCH, false>(a, v, s, kt);
+hipError_t dispatch_rec(const BackwardLaunch& a, const uint32_t* k, const uint32_t* v,
+                        hipStream_t s, const KernelTimer* kt) {
+  return a.use_rec ? run_segments<ST, VE, NCH, true>(a, k, v, s, kt)
+                   : run_segments<ST, VE, NCH, false>(a, k, v, s, kt);
 }
 
 template <int ST>
-hipError_t dispatch_shape(const BackwardLaunch& a, const uint32_t* v, hipStream_t s,
-                          const KernelTimer* kt) {
+hipError_t dispatch_shape(const BackwardLaunch& a, const uint32_t* k, const uint32_t* v,
+                          hipStream_t s, const KernelTimer* kt) {
   if (a.vec) {
-    if (a.nch == 1) return dispatch_rec<ST, 4, 1>(a, v, s, kt);
-    if (a.nch == 4) return dispatch_rec<ST, 4, 4>(a, v, s, kt);
+    if (a.nch == 1) return dispatch_rec<ST, 4, 1>(a, k, v, s, kt);
+    if (a.nch == 4) return dispatch_rec<ST, 4, 4>(a, k, v, s, kt);
   } else {
-    if (a.nch == 1) return dispatch_rec<ST, 1, 1>(a, v, s, kt);
-    if (a.nch == 16) return dispatch_rec<ST, 1, 16>(a, v, s, kt);
+    if (a.nch == 1) return dispatch_rec<ST, 1, 1>(a, k, v, s, kt);
+    if (a.nch == 16) return dispatch_rec<ST, 1, 16>(a, k, v, s, kt);
   }
   return hipErrorInvalidValue;
 }
@@ -642,12 +679,13 @@ SegmentBounds segment_bounds(int64_t n, int64_t long_threshold, int chunk, int g
   return b;
 }
 
-hipError_t launch_segment_reduce_update(const BackwardLaunch& a, const uint32_t* sorted_vals,
-                                        hipStream_t stream, const KernelTimer* kt) {
+hipError_t launch_segment_reduce_update(const BackwardLaunch& a, const uint32_t* sorted_keys,
+                                        const uint32_t* sorted_vals, hipStream_t stream,
+                                        const KernelTimer* kt) {
   switch (a.dtype) {
-    case kF32: return dispatch_shape<kF32>(a, sorted_vals, stream, kt);
-    case kF16: return dispatch_shape<kF16>(a, sorted_vals, stream, kt);
-    case kBF16: return dispatch_shape<kBF16>(a, sorted_vals, stream, kt);
+    case kF32: return dispatch_shape<kF32>(a, sorted_keys, sorted_vals, stream, kt);
+    case kF16: return dispatch_shape<kF16>(a, sorted_keys, sorted_vals, stream, kt);
+    case kBF16: return dispatch_shape<kBF16>(a, sorted_keys, sorted_vals, stream, kt);
     default: return hipErrorInvalidValue;
   }
 }

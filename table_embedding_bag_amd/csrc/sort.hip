@@ -199,6 +199,39 @@ __device__ void lookback_digits(uint32_t* status, int slots, int tile, int d0, u
   }
 }
 
+// Lanes of the wave (among those with ok) whose digit d equals this lane's.
+// Each lane sets its bit in the LDS slot chosen by the low 8 bits of d and
+// reads the slot back; lanes that share the slot but differ in the digit's
+// higher bits (at most RB - 8 of them) are removed with one ballot per bit.
+// The slot is cleared again for the next round.  Replaces RB ballots per
+// round by one LDS atomic, one read and RB - 8 ballots: used for 9- and
+// 10-bit digits (for 8-bit digits the LDS round trip costs more than the
+// ballots it saves).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int RB>
+__device__ __forceinline__ uint64_t match_digit(uint64_t* s_slots, uint32_t d, bool ok) {
+  uint64_t* slot = s_slots + (d & 255u);
+  if (ok)
+    __hip_atomic_fetch_or(slot, uint64_t{1} << lane_id(), __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_WAVEFRONT);
+  wave_lds_sync();
+  uint64_t peers = ok ? __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT) : 0u;
+  wave_lds_sync();
+  if (ok) __hip_atomic_store(slot, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+#pragma unroll
+  for (int bit = 8; bit < RB; ++bit) {
+    const bool set = (d >> bit) & 1u;
+    const uint64_t bal = __ballot(set);
+    peers &= set ? bal : ~bal;
+  }
+  return peers;
+}
+
 // One LSD pass on the digit (key >> shift) & (2^bits - 1), bits <= RB.  A
 // tile of 256*KPT keys; thread tid owns the DPT = 2^RB / 256 consecutive
 // digits tid*DPT .. tid*DPT + DPT - 1 for counting, look-back and offsets.
@@ -360,6 +393,7 @@ __global__ __launch_bounds__(1024) void radix_pass_wide(
   __shared__ uint32_t s_k[TS];
   __shared__ uint32_t s_v[TS];
   __shared__ uint32_t s_cnt[NW][RMAX];
+  __shared__ uint64_t s_slots[NW][256];
   __shared__ uint32_t s_dstart[RMAX];
   __shared__ uint32_t s_gbase[RMAX];
   __shared__ uint32_t scratch[NW];
@@ -369,6 +403,7 @@ __global__ __launch_bounds__(1024) void radix_pass_wide(
   const uint32_t my_total = totals[tid];
   if (tid == 0) s_tile = ticket ? atomicAdd(ticket, 1u) : blockIdx.x;
   for (int i = tid; i < NW * RMAX; i += NT) (&s_cnt[0][0])[i] = 0u;
+  for (int i = tid; i < NW * 256; i += NT) (&s_slots[0][0])[i] = 0u;
   __syncthreads();
   const int tile = static_cast<int>(s_tile);
   const int64_t base = static_cast<int64_t>(tile) * TS;
@@ -386,13 +421,7 @@ __global__ __launch_bounds__(1024) void radix_pass_wide(
   for (int r = 0; r < KPT; ++r) {
     const bool ok = (seg + r * kWave + lane) < n;
     const uint32_t d = (key[r] >> shift) & dmask;
-    uint64_t peers = __ballot(ok);
-#pragma unroll
-    for (int bit = 0; bit < RB; ++bit) {
-      const bool set = (d >> bit) & 1u;
-      const uint64_t bal = __ballot(set);
-      peers &= set ? bal : ~bal;
-    }
+    const uint64_t peers = match_digit<RB>(s_slots[wave], d, ok);
     const uint32_t below = popc_below(peers);
     const uint32_t cnt = __popcll(peers);
     const uint32_t pre = ok ? s_cnt[wave][d] : 0u;

@@ -429,23 +429,28 @@ __global__ __launch_bounds__(1024) void radix_pass_wide(
     if (ok && below == 0) s_cnt[wave][d] = pre + cnt;
   }
   __syncthreads();
+  // this digit's count per wave (all read before any is rewritten: one LDS
+  // round trip), then the waves' offsets inside the tile's bucket
+  uint32_t c[NW];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) c[w] = s_cnt[w][tid];
   uint32_t mine = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
-    const uint32_t c = s_cnt[w][tid];
     s_cnt[w][tid] = mine;
-    mine += c;
+    mine += c[w];
   }
   uint32_t total;
   s_dstart[tid] = block_excl_n<NW>(mine, scratch, &total);
   uint32_t* my_status = status + static_cast<int64_t>(tile) * RMAX + tid;
   st_status(my_status, (tile == 0 ? kFlagIncl : kFlagAgg) | mine);
+  // the bucket's global start does not depend on the look-back
+  const uint32_t gb = block_excl_n<NW>(my_total, scratch, &total);
   uint32_t before[1] = {0u};
   if (tile > 0) {
     lookback_digits<1, 16>(status, RMAX, tile, tid, err, before);
     st_status(my_status, kFlagIncl | ((before[0] + mine) & kValueMask));
   }
-  const uint32_t gb = block_excl_n<NW>(my_total, scratch, &total);
   s_gbase[tid] = gb + before[0];
   __syncthreads();
 #pragma unroll

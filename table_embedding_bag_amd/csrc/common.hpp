@@ -262,6 +262,7 @@ struct BackwardBuffers {
   uint2* items1;            // workgroup items: {first position, medium flag | length}
                             // or {long run, chunk}
   uint4* longs;             // {first position, length, first chunk partial, chunk count}
+  uint32_t* long_keys;      // row id of each long run (loaded with its list entry)
   float* partial1;          // [chunks cap, pstride]
 };
 

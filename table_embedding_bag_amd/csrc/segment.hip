@@ -343,9 +343,11 @@ __global__ __launch_bounds__(kBlock) void seg_short(BackwardLaunch a, const uint
       // items carry the run's first position and length, so the workgroup
       // kernels need no run-list lookup
       if (is_long) {
-        if (ld)
+        if (ld) {
           a.buf.longs[li] =
               make_uint4(static_cast<uint32_t>(s), static_cast<uint32_t>(len), b1, n1);
+          a.buf.long_keys[li] = key;
+        }
         for (uint32_t c = gl; c < n1; c += Gs) a.buf.items1[it + c] = make_uint2(li, c);
       } else if (is_medium && ld) {
         a.buf.items1[it] =
@@ -523,8 +525,7 @@ __global__ __launch_bounds__(kBlock) void seg_wg(BackwardLaunch a, const uint32_
 // the result does not depend on scheduling.  The row to update and its state
 // are loaded while the partials are in flight.
 template <int ST, int VE, int NCH, bool REC>
-__global__ __launch_bounds__(kBlock) void seg_finalize(BackwardLaunch a,
-                                                       const uint32_t* __restrict__ keys) {
+__global__ __launch_bounds__(kBlock) void seg_finalize(BackwardLaunch a) {
   if (a.buf.counters[kCntError] != 0u) return;  // a look-back wait gave up earlier
   constexpr int NV = VE * NCH;
   constexpr int kElemsPerThread = kMaxDim / kBlock;
@@ -541,7 +542,7 @@ __global__ __launch_bounds__(kBlock) void seg_finalize(BackwardLaunch a,
   const uint32_t n = a.buf.counters[kCntLong];
   for (uint32_t li = blockIdx.x; li < n; li += gridDim.x) {
     const uint4 L = a.buf.longs[li];  // {first position, length, first partial, chunks}
-    const uint32_t key = keys[L.x];
+    const uint32_t key = a.buf.long_keys[li];
     const TableMeta m = meta_of(a, s_meta, table_of_key(a, s_meta, key));
     const int D = m.dim, C = D / VE;
     const int64_t row0 = m.woff + static_cast<int64_t>(key - static_cast<uint32_t>(m.roff)) * D;
@@ -642,7 +643,7 @@ hipError_t run_segments(const BackwardLaunch& a, const uint32_t* keys, const uin
                sorted_vals);
   const int64_t fin = ub.longs < kMaxSegBlocks ? ub.longs : kMaxSegBlocks;
   launch_timed(kt, "seg_finalize", seg_finalize<ST, VE, NCH, REC>, dim3(fin), dim3(kBlock), 0, s,
-               a, keys);
+               a);
   return hipGetLastError();
 }
 

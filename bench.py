@@ -3,10 +3,12 @@
 backward (linearize, radix sort, run-length encode, segment reduce, one row-wise
 Adagrad / SGD update per touched row), through the library's C ABI.
 
-A step is one forward and one backward_update over one batch of the workload
-(tbe_forward + tbe_backward_update; --grouped times tbe_forward_group, which
-runs the backward's grouping of the batch on a second stream beside the pooled
-lookup, + tbe_backward_update_grouped).  Four seeded batches (and
+A step is one forward and one backward update over one batch of the workload:
+tbe_forward_group (the pooled lookup, with the backward's linearize step in the
+same launch, then the sort and run-length encoding of the batch) +
+tbe_backward_update_grouped (segment reduce and update).  --plain times
+tbe_forward + tbe_backward_update instead (same results, bit for bit).  Four
+seeded batches (and
 upstream gradients) are generated up front, resident in HBM, and used in
 rotation.  Default workload: T=8 tables of 100,000 x 128
 fp32 rows, B=2048 bags per table, bag length uniform in 1..32, Zipf(1.05) row
@@ -51,10 +53,10 @@ def parse():
                    help="gather: the gather forward (the library default); routed: count-matrix "
                         "forward for the tables that qualify; histogram: count-matrix forward "
                         "for every table (all must qualify)")
-    p.add_argument("--grouped", action="store_true",
-                   help="time tbe_forward_group + tbe_backward_update_grouped (the backward's "
-                        "grouping done during the forward, on a second stream beside the pooled "
-                        "lookup) instead of tbe_forward + tbe_backward_update")
+    p.add_argument("--plain", action="store_true",
+                   help="time tbe_forward + tbe_backward_update instead of the grouped pair "
+                        "tbe_forward_group + tbe_backward_update_grouped (the backward's "
+                        "grouping done with the forward)")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain device copy of known size (counter calibration)")
     return p.parse_args()
@@ -90,10 +92,19 @@ def group_lanes(spec):
     return min(64, 1 << (c - 1).bit_length())
 
 
-def algorithmic_bytes(spec, batch, long_threshold=256, chunk=256):
+def hist_tables(spec):
+    """Tables the count-matrix forward takes when routed: 16-bit storage, at most 1024 rows,
+    dims a multiple of 16 up to 256."""
+    return [t for t in range(spec.T) if spec.dtype != "f32" and spec.rows[t] <= 1024
+            and spec.dims[t] <= 256 and spec.dims[t] % 16 == 0]
+
+
+def algorithmic_bytes(spec, batch, gather_tables=None, long_threshold=256, chunk=256):
     """Bytes the method itself must move, per kernel (one launch each), for one batch.
 
     forward (per lookup)  row read D*s + id 8 (+ weight 4); (per bag) offset 8 + output 4*D
+                          (gather kernel: the tables in gather_tables, default all)
+    fwd_linearize         the gather forward's bytes plus the linearize step's
     segment (per lookup)  sorted value 4 + gradient row 4*D (+ record 8 with weights / mean)
             (per row)     id + run bounds 12 + row read and write 2*D*s (+ state read/write 8)
       seg_short           runs a lane group takes alone (at most Gs lookups)
@@ -108,7 +119,9 @@ def algorithmic_bytes(spec, batch, long_threshold=256, chunk=256):
     bag_t = np.repeat(np.arange(spec.T), spec.B)
     look_D = np.repeat(dims[bag_t], lens)
     psw = 4 if spec.psw else 0
-    fwd = float((look_D * s + 8 + psw).sum() + (8 + 4 * dims[bag_t]).sum())
+    gt = np.ones(spec.T, bool) if gather_tables is None else np.isin(np.arange(spec.T), gather_tables)
+    look_g = np.repeat(gt[bag_t], lens)
+    fwd = float((look_D * s + 8 + psw)[look_g].sum() + (8 + 4 * dims[bag_t])[gt[bag_t]].sum())
     _, cnt, tab = row_stats(spec, batch)
     D = dims[tab]
     rec = 8 if (spec.psw or spec.pooling == "mean") else 0
@@ -134,14 +147,14 @@ def algorithmic_bytes(spec, batch, long_threshold=256, chunk=256):
     # read of each table; the dense product does 2*B*E_t*D_t flops per table.  The W^T
     # staging kernel reads each table and writes its transposed copy.
     s16 = 2
-    hist = [t for t in range(spec.T) if spec.dtype != "f32" and spec.rows[t] <= 1024
-            and spec.dims[t] <= 256 and spec.dims[t] % 16 == 0]
+    hist = hist_tables(spec)
     hist_n = sum(int(lens[t * spec.B:(t + 1) * spec.B].sum()) for t in hist)
     hist_bytes = float(8 * hist_n + sum(8 * spec.B + 4 * spec.B * spec.dims[t]
                                         + s16 * spec.rows[t] * spec.dims[t] for t in hist))
     hist_flops = float(sum(2 * spec.B * spec.rows[t] * spec.dims[t] for t in hist))
     hist_t = float(sum(2 * s16 * spec.rows[t] * spec.dims[t] for t in hist))
-    return {"fwd_gather_pool": fwd, "fwd_histogram": hist_bytes, "hist_transpose": hist_t,
+    return {"fwd_gather_pool": fwd, "fwd_linearize": fwd + front["linearize_kernel"],
+            "fwd_histogram": hist_bytes, "hist_transpose": hist_t,
             "fwd_histogram_flops": hist_flops, "seg_short": seg_short, "seg_wg": seg_wg,
             "seg_finalize": seg_final, **front}, {"N": int(lens.sum()), "U": int(cnt.size),
                                          "long_run_share": float(cnt[long_].sum() / max(1, cnt.sum())),
@@ -253,7 +266,7 @@ def main():
 
     def step(i):
         idx, off, psw, n = batches[i % nrot]
-        if not args.grouped:
+        if args.plain:
             tbe.tbe_forward(op.handle, spec.B, idx, off, psw, Y)
             tbe.tbe_backward_update(op.handle, spec.B, idx, off, psw, grads[i % nrot], spec.lr,
                                     spec.eps, ws)
@@ -292,7 +305,10 @@ def main():
     steps_per_launch = {k: c / args.steps for k, (t, c) in per_kernel.items()}
 
     # algorithmic bytes per launch (averaged over the rotated batches used)
-    alg = [algorithmic_bytes(spec, host_batches[(args.warmup + i) % nrot]) for i in range(nrot)]
+    routed = [] if args.forward == "gather" else hist_tables(spec)
+    gather = [t for t in range(spec.T) if t not in routed]
+    alg = [algorithmic_bytes(spec, host_batches[(args.warmup + i) % nrot], gather)
+           for i in range(nrot)]
     alg_bytes = {k: float(np.mean([a[0][k] for a in alg])) for k in alg[0][0]}
     stats = alg[0][1]
     kernels = {}
@@ -360,7 +376,7 @@ def main():
         "data": "synthetic (seeded generator, 4 rotated batches resident in HBM)",
         "config": {"workload": spec.name, "tables": spec.T, "bags_per_table": spec.B,
                    "forward": args.forward,
-                   "calls": "tbe_forward + tbe_backward_update" if not args.grouped
+                   "calls": "tbe_forward + tbe_backward_update" if args.plain
                             else "tbe_forward_group + tbe_backward_update_grouped",
                    "lookups_per_step": stats["N"], "unique_rows_batch0": stats["U"],
                    "long_run_share_batch0": round(stats["long_run_share"], 3),

@@ -186,19 +186,17 @@ tbe_status tbe_backward_update(tbe_handle* handle, int32_t B, const void* indice
 /* Forward plus the backward's grouping of the same batch.  kimbodo.com/?p=28372,
  * "Kimbodo Engineering Perspective": the transpose, sort and run-length
  * encoding of the backward can be done during the forward (an option that is
- * off by default there).  Runs tbe_forward on `stream` and, on a second
- * stream of the handle that starts after the work already queued on `stream`,
- * linearizes, sorts and run-length encodes the batch into `workspace`
- * (sized by tbe_backward_workspace_size, 256-byte aligned); `stream` then
- * waits for that work, so the call completes as one unit on `stream`.  The
- * grouping does not read the weights, so it runs beside the pooled lookup
- * (with TBE_FLAG_VALIDATE the ids are checked before either part is queued).
- * The ordering between the two streams costs some microseconds, so on small
- * batches the pair of grouped calls can be slower than the plain ones.
- * Arguments and errors as tbe_forward, plus TBE_ERR_WORKSPACE_TOO_SMALL.  The
- * workspace must then go, unchanged and with the same batch (ids, offsets,
- * per-sample weights, B, num_indices), to tbe_backward_update_grouped;
- * anything else gives undefined results. */
+ * off by default there).  On `stream`: the workspace is cleared, one launch
+ * pools the batch (as tbe_forward) and also linearizes it, the linearize
+ * workgroups running beside the pooled lookup; then the sort and the
+ * run-length encoding of the batch follow, into `workspace` (sized by
+ * tbe_backward_workspace_size, 256-byte aligned).  With TBE_FLAG_VALIDATE the
+ * ids are checked before anything is queued.  Arguments and errors as
+ * tbe_forward, plus TBE_ERR_WORKSPACE_TOO_SMALL.  The workspace must then go,
+ * unchanged and with the same batch (ids, offsets, per-sample weights, B,
+ * num_indices), to tbe_backward_update_grouped; anything else gives undefined
+ * results.  The pair gives the same output, weights and state as tbe_forward
+ * + tbe_backward_update, bit for bit. */
 tbe_status tbe_forward_group(tbe_handle* handle, int32_t B, const void* indices,
                              const void* offsets, int32_t index_dtype, int64_t num_indices,
                              const float* per_sample_weights, float* output, void* workspace,

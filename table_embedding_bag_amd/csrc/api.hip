@@ -45,10 +45,6 @@ struct tbe_handle {
   int64_t long_threshold = 256;
   // profiling: pairs of events handed to timed kernel launches (start and end
   // of that kernel), kept until tbe_stage_times reads them
-  // second stream (and fork/join events) on which tbe_forward_group runs the
-  // backward grouping next to the pooled lookup; made on first use
-  hipStream_t side = nullptr;
-  hipEvent_t fork_ev = nullptr, join_ev = nullptr;
   bool profile = false;
   std::vector<hipEvent_t> pool;
   std::vector<std::pair<size_t, const char*>> timed;  // start event index in pool, kernel name
@@ -516,9 +512,6 @@ void tbe_destroy(tbe_handle* h) {
   for (auto& e : h->pool) (void)hipEventDestroy(e);
   if (h->meta) (void)hipFree(h->meta);
   if (h->wt) (void)hipFree(h->wt);
-  if (h->fork_ev) (void)hipEventDestroy(h->fork_ev);
-  if (h->join_ev) (void)hipEventDestroy(h->join_ev);
-  if (h->side) (void)hipStreamDestroy(h->side);
   delete h;
 }
 
@@ -561,9 +554,11 @@ tbe_status tbe_stage_times(tbe_handle* h, float* ms, const char** names, int32_t
 
 namespace {
 
+// The pooled lookup; with fuse set, the gather kernel also linearizes that
+// backward batch (its workspace already zeroed).
 tbe_status forward_impl(tbe_handle* h, int32_t B, const void* indices, const void* offsets,
                         int32_t index_dtype, int64_t n, const float* psw, float* output,
-                        hipStream_t s, bool validate) {
+                        hipStream_t s, bool validate, const BackwardLaunch* fuse = nullptr) {
   tbe_status st = check_batch_args(h, B, indices, offsets, index_dtype, n);
   if (st != TBE_OK) return st;
   if (B == 0) return TBE_OK;
@@ -612,7 +607,7 @@ tbe_status forward_impl(tbe_handle* h, int32_t B, const void* indices, const voi
       ha.index64 = index_dtype == TBE_I64;
       const hipError_t e = launch_forward_histogram(ha, s, kt);
       if (e != hipSuccess) return from_hip(e);
-      if (h->gather_host.empty()) return TBE_OK;
+      if (h->gather_host.empty() && !fuse) return TBE_OK;
     }
     ForwardLaunch a{};
     a.table_list = hist ? h->gather_list : nullptr;
@@ -631,7 +626,8 @@ tbe_status forward_impl(tbe_handle* h, int32_t B, const void* indices, const voi
     a.dtype = h->dtype;
     a.index64 = index_dtype == TBE_I64;
     a.vec = h->fwd_vec;
-    const hipError_t e = launch_forward_gather(a, s, kt);
+    const hipError_t e =
+        fuse ? launch_forward_linearize(a, *fuse, s, kt) : launch_forward_gather(a, s, kt);
     return from_hip(e);
   } catch (...) {
     return TBE_ERR_OUT_OF_MEMORY;
@@ -729,46 +725,31 @@ tbe_status tbe_forward_group(tbe_handle* h, int32_t B, const void* indices, cons
   if (!output || !aligned(output, 16)) return TBE_ERR_INVALID_ARGUMENT;
   if (psw && !aligned(psw, 4)) return TBE_ERR_INVALID_ARGUMENT;
   if (psw && (h->flags & TBE_FLAG_FORCE_HISTOGRAM)) return TBE_ERR_UNSUPPORTED;
+  if (n == 0) return tbe_forward(h, B, indices, offsets, index_dtype, n, psw, output, stream);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   try {
     BwdPlan p;
+    if (!plan_backward(h, n, h->bwd_vec, &p)) return TBE_ERR_UNSUPPORTED;
+    if (!workspace || !aligned(workspace, kAlign)) return TBE_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < p.bytes) return TBE_ERR_WORKSPACE_TOO_SMALL;
     BackwardLaunch a{};
-    if (n > 0) {
-      if (!plan_backward(h, n, h->bwd_vec, &p)) return TBE_ERR_UNSUPPORTED;
-      if (!workspace || !aligned(workspace, kAlign)) return TBE_ERR_INVALID_ARGUMENT;
-      if (workspace_bytes < p.bytes) return TBE_ERR_WORKSPACE_TOO_SMALL;
-      fill_backward(h, B, indices, offsets, index_dtype, n, psw, nullptr, 0.0f, 0.0f, workspace,
-                    nullptr, h->bwd_vec, p, &a);
-      if (!h->side) {
-        if (hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess ||
-            hipEventCreateWithFlags(&h->fork_ev, hipEventDisableTiming) != hipSuccess ||
-            hipEventCreateWithFlags(&h->join_ev, hipEventDisableTiming) != hipSuccess)
-          return TBE_ERR_HIP;
-      }
-    }
-    if (n == 0) return tbe_forward(h, B, indices, offsets, index_dtype, n, psw, output, stream);
-    // ids are checked (when asked) before either half is enqueued
+    fill_backward(h, B, indices, offsets, index_dtype, n, psw, nullptr, 0.0f, 0.0f, workspace,
+                  nullptr, h->bwd_vec, p, &a);
+    // ids are checked (when asked) before anything is enqueued
     if (h->flags & TBE_FLAG_VALIDATE) {
       st = run_validation(h, B, indices, offsets, index_dtype, n, s);
       if (st != TBE_OK) return st;
     }
-    // The grouping runs on the second stream next to the pooled lookup: it
-    // starts after the caller's earlier work (the batch may have been written
-    // just before), and the caller's stream waits for it, so the call
-    // completes as one unit on `stream`.
     KernelTimer timer{h, take_events};
     const KernelTimer* kt = h->profile ? &timer : nullptr;
-    if (hipEventRecord(h->fork_ev, s) != hipSuccess ||
-        hipStreamWaitEvent(h->side, h->fork_ev, 0) != hipSuccess)
-      return TBE_ERR_HIP;
-    const hipError_t e = launch_front(a, h->side, kt);
-    if (e != hipSuccess) return TBE_ERR_HIP;
-    st = forward_impl(h, B, indices, offsets, index_dtype, n, psw, output, s, false);
-    // join even when the forward failed, so that no work is left unordered
-    if (hipEventRecord(h->join_ev, h->side) != hipSuccess ||
-        hipStreamWaitEvent(s, h->join_ev, 0) != hipSuccess)
-      return TBE_ERR_HIP;
-    return st;
+    // workspace clear; the pooled lookup with the linearize step in the same
+    // launch; then the sort and the run-length encoding
+    if (launch_init_workspace(a, s, kt) != hipSuccess) return TBE_ERR_HIP;
+    st = forward_impl(h, B, indices, offsets, index_dtype, n, psw, output, s, false, &a);
+    if (st != TBE_OK) return st;
+    int sorted = 0;
+    if (launch_radix_sort(a, s, &sorted, kt) != hipSuccess) return TBE_ERR_HIP;
+    return from_hip(launch_run_length_encode(a, a.buf.keys[sorted], s, kt));
   } catch (...) {
     return TBE_ERR_OUT_OF_MEMORY;
   }

@@ -26,6 +26,7 @@
 //  * Workgroups are renumbered so that every XCD works on a contiguous range
 //    of tables, which keeps each table's hot rows in one XCD's L2.
 #include "common.hpp"
+#include "linearize.hpp"
 
 namespace tbe {
 namespace {
@@ -37,21 +38,22 @@ __device__ __forceinline__ int64_t ld_index(const void* p, int64_t i) {
   return static_cast<int64_t>(static_cast<const IT*>(p)[i]);
 }
 
-// ST: storage dtype code; IT: index type; VEC: 16-byte chunks (else one
-// element per lane); PSW: per-sample weights present.
+// One tile (kWavesPerBlock waves' worth of bags of one table) of the pooled
+// lookup.  ST: storage dtype code; IT: index type; VEC: 16-byte chunks (else
+// one element per lane); PSW: per-sample weights present.  logical numbers
+// the tiles table after table; wave is the wave's index inside the tile.
 template <int ST, typename IT, bool VEC, bool PSW>
-__global__ __launch_bounds__(kBlock) void fwd_gather_pool(ForwardLaunch a) {
+__device__ __forceinline__ void fwd_tile(const ForwardLaunch& a, int logical, int wave) {
   constexpr int SB = StorageTraits<ST>::bytes;
   constexpr int VE = VEC ? 16 / SB : 1;  // elements per lane chunk
 
-  const int logical = xcd_contiguous_block(blockIdx.x, gridDim.x);
+  if (logical >= a.T * a.tiles_per_table) return;
   const int listed = logical / a.tiles_per_table;
   const int tile = logical - listed * a.tiles_per_table;
   const int t = a.table_list ? a.table_list[listed] : listed;
   const TableMeta m = a.meta[t];
 
   const int lane = lane_id();
-  const int wave = threadIdx.x >> 6;
   const int gshift = m.fwd_gshift;
   const int swshift = min(6, gshift + a.lshift);
   const int SW = 1 << swshift;                  // lanes per bag
@@ -140,12 +142,33 @@ __global__ __launch_bounds__(kBlock) void fwd_gather_pool(ForwardLaunch a) {
   }
 }
 
-// Gradient with respect to the per-sample weights: the forward is linear in
-// p_i, so dL/dp_i = s_k * <G[b, doff_t : doff_t + D_t], W_t[x_i]>.  Same lane
-// layout as the forward: a lane group covers a row in 16-byte chunks, a
-// sub-wave serves a bag, and each lane group computes the dot products of
-// kUnroll lookups at a time (the bag's gradient chunk is loaded once per
-// chunk set and shared by them), folded across the group's lanes.
+template <int ST, typename IT, bool VEC, bool PSW>
+__global__ __launch_bounds__(kBlock) void fwd_gather_pool(ForwardLaunch a) {
+  fwd_tile<ST, IT, VEC, PSW>(a, xcd_contiguous_block(blockIdx.x, gridDim.x), threadIdx.x >> 6);
+}
+
+// The pooled lookup and the linearize step of the backward's grouping in one
+// launch (kimbodo.com/?p=28372, "Kimbodo Engineering Perspective": the
+// grouping can be done during the forward).  The first lin_blocks workgroups
+// linearize; each later workgroup takes kLinThreads / kBlock consecutive
+// forward tiles.  The two kinds share no data, so the linearize workgroups,
+// which wait on memory most of the time, run beside the bandwidth-bound
+// forward instead of after it.  lin_blocks is a multiple of 8, so the forward
+// workgroups keep the XCD-contiguous numbering of the stand-alone kernel.
+template <int ST, typename IT, bool VEC, bool PSW>
+__global__ __launch_bounds__(kLinThreads) void fwd_linearize(ForwardLaunch f, BackwardLaunch b,
+                                                             int lin_blocks) {
+  const int bid = static_cast<int>(blockIdx.x);
+  if (bid < lin_blocks) {
+    linearize_tiles<IT>(b, bid, lin_blocks);
+    return;
+  }
+  constexpr int kPer = kLinThreads / kBlock;
+  const int logical = xcd_contiguous_block(bid - lin_blocks, static_cast<int>(gridDim.x) - lin_blocks);
+  fwd_tile<ST, IT, VEC, PSW>(f, logical * kPer + static_cast<int>(threadIdx.x) / kBlock,
+                             (static_cast<int>(threadIdx.x) % kBlock) >> 6);
+}
+
 // Sums v[0..3] of each lookup over the Gs lanes of a lane group (Gs >= 4, a
 // power of two): two exchange steps leave every lane with one of the four
 // partial sums (lookup 2*[gl & Gs/2] + [gl & Gs/4]), a butterfly over the
@@ -167,6 +190,12 @@ __device__ __forceinline__ float group_sum4(const float (&v)[4], int gl, int Gs,
   return x;
 }
 
+// Gradient with respect to the per-sample weights: the forward is linear in
+// p_i, so dL/dp_i = s_k * <G[b, doff_t : doff_t + D_t], W_t[x_i]>.  Same lane
+// layout as the forward: a lane group covers a row in 16-byte chunks, a
+// sub-wave serves a bag, and each lane group computes the dot products of
+// kUnroll lookups at a time (the bag's gradient chunk is loaded once per
+// chunk set and shared by them), folded across the group's lanes.
 template <int ST, typename IT, bool VEC>
 __global__ __launch_bounds__(kBlock) void psw_grad(ForwardLaunch a, const float* __restrict__ grad,
                                                    float* __restrict__ gpsw) {
@@ -289,6 +318,31 @@ hipError_t dispatch_index(const ForwardLaunch& a, hipStream_t s, dim3 grid,
 }
 
 template <int ST, typename IT>
+hipError_t launch_fused(const ForwardLaunch& f, const BackwardLaunch& b, int lin, hipStream_t s,
+                        dim3 grid, const KernelTimer* kt) {
+  const dim3 block(kLinThreads);
+  if (f.vec) {
+    if (f.psw)
+      launch_timed(kt, "fwd_linearize", fwd_linearize<ST, IT, true, true>, grid, block, 0, s, f, b, lin);
+    else
+      launch_timed(kt, "fwd_linearize", fwd_linearize<ST, IT, true, false>, grid, block, 0, s, f, b, lin);
+  } else {
+    if (f.psw)
+      launch_timed(kt, "fwd_linearize", fwd_linearize<ST, IT, false, true>, grid, block, 0, s, f, b, lin);
+    else
+      launch_timed(kt, "fwd_linearize", fwd_linearize<ST, IT, false, false>, grid, block, 0, s, f, b, lin);
+  }
+  return hipGetLastError();
+}
+
+template <int ST>
+hipError_t launch_fused_index(const ForwardLaunch& f, const BackwardLaunch& b, int lin,
+                              hipStream_t s, dim3 grid, const KernelTimer* kt) {
+  return f.index64 ? launch_fused<ST, int64_t>(f, b, lin, s, grid, kt)
+                   : launch_fused<ST, int32_t>(f, b, lin, s, grid, kt);
+}
+
+template <int ST, typename IT>
 void launch_psw(const ForwardLaunch& a, const float* grad, float* gpsw, hipStream_t s, dim3 grid,
                 const KernelTimer* kt) {
   if (a.vec)
@@ -318,6 +372,24 @@ hipError_t launch_forward_gather(const ForwardLaunch& a, hipStream_t stream,
     case kF32: return dispatch_index<kF32>(a, stream, grid, kt);
     case kF16: return dispatch_index<kF16>(a, stream, grid, kt);
     case kBF16: return dispatch_index<kBF16>(a, stream, grid, kt);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_forward_linearize(const ForwardLaunch& f, const BackwardLaunch& b,
+                                    hipStream_t stream, const KernelTimer* kt) {
+  if (f.index64 != b.index64) return hipErrorInvalidValue;
+  const int64_t tiles = static_cast<int64_t>(f.T) * f.tiles_per_table;
+  constexpr int kPer = kLinThreads / kBlock;
+  // linearize workgroups first, rounded up to a multiple of the 8 XCDs
+  const int64_t lin = (linearize_blocks(b.num_bags) + 7) / 8 * 8;
+  const int64_t blocks = lin + (tiles + kPer - 1) / kPer;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<unsigned>(blocks));
+  switch (f.dtype) {
+    case kF32: return launch_fused_index<kF32>(f, b, static_cast<int>(lin), stream, grid, kt);
+    case kF16: return launch_fused_index<kF16>(f, b, static_cast<int>(lin), stream, grid, kt);
+    case kBF16: return launch_fused_index<kBF16>(f, b, static_cast<int>(lin), stream, grid, kt);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,0 +1,115 @@
+// linearize.hpp -- the linearize step of the TBE backward's grouping, shared
+// by the stand-alone linearize kernel (sort.hip) and the forward kernel that
+// also linearizes the batch it pools (forward.hip).
+//
+// kimbodo.com/?p=28372, "Kimbodo Engineering Perspective": the grouping starts
+// with a transpose of the batch into (table, row) ids.  Here
+//   key_i = roff_t + x_i (one 32-bit id space over all tables),
+//   value_i = bag id k (plain sums), or lookup id i with a side record
+//             {k, p_i * s_k} when lookups carry a coefficient,
+// and the digits of every radix pass are counted on the way (the counts do not
+// depend on the order of the keys, so no pass needs a counting kernel).
+#pragma once
+
+#include "common.hpp"
+
+namespace tbe {
+
+constexpr int kLinBags = 128;               // bags per linearize tile
+constexpr int64_t kLinMaxBlocks = 1024;     // linearize grid bound
+constexpr int kLinThreads = 1024;           // threads per linearize workgroup
+
+// Workgroups of the linearize step: one per tile of bags, at most kLinMaxBlocks.
+inline int64_t linearize_blocks(int64_t num_bags) {
+  const int64_t b = (num_bags + kLinBags - 1) / kLinBags;
+  return b < 1 ? 1 : (b < kLinMaxBlocks ? b : kLinMaxBlocks);
+}
+
+template <typename IT>
+__device__ __forceinline__ int64_t lin_index(const void* p, int64_t i) {
+  return static_cast<int64_t>(static_cast<const IT*>(p)[i]);
+}
+
+// A workgroup of kLinThreads threads takes tiles first, first + stride, ... of
+// kLinBags consecutive bags.  A tile's offsets are staged in LDS; the
+// workgroup then walks all of its lookups with consecutive threads on
+// consecutive lookups and finds each lookup's bag by binary search in LDS.
+// Digit counts are kept in LDS across the workgroup's tiles and added to the
+// global counts once at the end (a bounded grid keeps those global atomics,
+// all on the same few hundred words, few).  The digit counts must be zero
+// before the first workgroup starts.
+template <typename IT>
+__device__ __forceinline__ void linearize_tiles(const BackwardLaunch& a, int64_t first,
+                                                int64_t stride) {
+  __shared__ int64_t s_off[kLinBags + 1];
+  __shared__ uint32_t s_roff[kLinBags];
+  __shared__ float s_scale[kLinBags];
+  __shared__ uint32_t s_hist[kMaxRadixPasses << kMaxRadixBits];
+
+  const int tid = threadIdx.x;
+  const int passes = radix_passes(a.key_bits, a.num_indices);
+  const int bits = radix_digit_bits(a.key_bits, a.num_indices);
+  const int slots = radix_slots(bits);
+  const uint32_t dmask = (1u << bits) - 1u;
+  for (int i = tid; i < passes * slots; i += kLinThreads) s_hist[i] = 0u;
+  const int64_t ntiles = (a.num_bags + kLinBags - 1) / kLinBags;
+  for (int64_t tile = first; tile < ntiles; tile += stride) {
+    const int64_t k0 = tile * kLinBags;
+    const int nb = static_cast<int>(min(static_cast<int64_t>(kLinBags), a.num_bags - k0));
+    __syncthreads();  // the previous tile's offsets are no longer read
+    if (tid < nb) {
+      const int64_t k = k0 + tid;
+      const int64_t lo = lin_index<IT>(a.offsets, k);
+      const int64_t hi = lin_index<IT>(a.offsets, k + 1);
+      s_off[tid] = lo;
+      if (tid == nb - 1) s_off[nb] = hi;
+      const int t = static_cast<int>(k / a.B);
+      s_roff[tid] = static_cast<uint32_t>(a.meta[t].roff);
+      s_scale[tid] = a.mean ? ((hi > lo) ? 1.0f / static_cast<float>(hi - lo) : 0.0f) : 1.0f;
+    }
+    __syncthreads();
+
+    const int64_t p0 = s_off[0], p1 = s_off[nb];
+    for (int64_t p = p0 + tid; p < p1; p += kLinThreads) {
+      int lo = 0, hi = nb;  // bag slot s with s_off[s] <= p < s_off[s + 1]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_off[mid] <= p)
+          lo = mid;
+        else
+          hi = mid;
+      }
+      const uint32_t key = s_roff[lo] + static_cast<uint32_t>(lin_index<IT>(a.indices, p));
+      a.buf.keys[0][p] = key;
+      const uint32_t bag = static_cast<uint32_t>(k0 + lo);
+      if (a.use_rec) {
+        a.buf.vals[0][p] = static_cast<uint32_t>(p);
+        const float coef = (a.psw ? a.psw[p] : 1.0f) * s_scale[lo];
+        a.buf.rec[p] = make_uint2(bag, __float_as_uint(coef));
+      } else {
+        a.buf.vals[0][p] = bag;
+      }
+      // digit counts: lanes holding the same digit are matched through 8
+      // ballots and only the lowest of them adds their number (the high digits
+      // of one table's keys take few values, so per-lane atomics would queue
+      // on a handful of LDS words)
+      const uint64_t active = __ballot(1);
+      for (int q = 0; q < passes; ++q) {
+        const uint32_t d = (key >> (q * bits)) & dmask;
+        uint64_t peers = active;
+#pragma unroll
+        for (int bit = 0; bit < kMaxRadixBits; ++bit) {  // bits above `bits` are 0: no effect
+          const bool set = (d >> bit) & 1u;
+          const uint64_t bal = __ballot(set);
+          peers &= set ? bal : ~bal;
+        }
+        if (popc_below(peers) == 0) atomicAdd(&s_hist[q * slots + d], __popcll(peers));
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < passes * slots; i += kLinThreads)
+    if (s_hist[i]) atomicAdd(&a.buf.digit_hist[i], s_hist[i]);
+}
+
+}  // namespace tbe

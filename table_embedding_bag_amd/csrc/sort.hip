@@ -36,6 +36,7 @@
 // limit the workgroup raises an error flag and stops waiting, so no wave can
 // hang.
 #include "common.hpp"
+#include "linearize.hpp"
 
 namespace tbe {
 namespace {
@@ -44,8 +45,6 @@ constexpr uint32_t kFlagAgg = 1u << 30;     // status word: this tile's own coun
 constexpr uint32_t kFlagIncl = 2u << 30;    // status word: count up to and including this tile
 constexpr uint32_t kValueMask = (1u << 30) - 1u;
 constexpr uint32_t kSpinLimit = 1u << 20;   // polls before a waiting tile gives up
-constexpr int kLinBags = 128;               // bags per linearize tile
-constexpr int64_t kLinMaxBlocks = 1024;     // linearize grid bound
 constexpr int kResidentTiles = 256;         // grids this small are resident all at once
 
 template <typename IT>
@@ -66,83 +65,9 @@ __global__ __launch_bounds__(kBlock) void init_workspace(uint32_t* words, int64_
     words[i] = 0u;
 }
 
-// Workgroups of 1024 threads stride over tiles of 128 consecutive bags.  A
-// tile's offsets are staged in LDS; the workgroup then walks all of its
-// lookups with consecutive threads on consecutive lookups and finds each
-// lookup's bag by binary search in LDS.  Digit counts are kept in LDS across the workgroup's tiles and
-// added to the global counts once at the end (a bounded grid keeps those
-// global atomics, all on the same few hundred words, few).
 template <typename IT>
-__global__ __launch_bounds__(1024) void linearize_kernel(BackwardLaunch a) {
-  __shared__ int64_t s_off[kLinBags + 1];
-  __shared__ uint32_t s_roff[kLinBags];
-  __shared__ float s_scale[kLinBags];
-  __shared__ uint32_t s_hist[kMaxRadixPasses << kMaxRadixBits];
-
-  const int tid = threadIdx.x;
-  const int passes = radix_passes(a.key_bits, a.num_indices);
-  const int bits = radix_digit_bits(a.key_bits, a.num_indices);
-  const int slots = radix_slots(bits);
-  const uint32_t dmask = (1u << bits) - 1u;
-  for (int i = tid; i < passes * slots; i += 1024) s_hist[i] = 0u;
-  const int64_t ntiles = (a.num_bags + kLinBags - 1) / kLinBags;
-  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const int64_t k0 = tile * kLinBags;
-    const int nb = static_cast<int>(min(static_cast<int64_t>(kLinBags), a.num_bags - k0));
-    __syncthreads();  // the previous tile's offsets are no longer read
-    if (tid < nb) {
-      const int64_t k = k0 + tid;
-      const int64_t lo = ld_index<IT>(a.offsets, k);
-      const int64_t hi = ld_index<IT>(a.offsets, k + 1);
-      s_off[tid] = lo;
-      if (tid == nb - 1) s_off[nb] = hi;
-      const int t = static_cast<int>(k / a.B);
-      s_roff[tid] = static_cast<uint32_t>(a.meta[t].roff);
-      s_scale[tid] = a.mean ? ((hi > lo) ? 1.0f / static_cast<float>(hi - lo) : 0.0f) : 1.0f;
-    }
-    __syncthreads();
-
-    const int64_t p0 = s_off[0], p1 = s_off[nb];
-    for (int64_t p = p0 + tid; p < p1; p += 1024) {
-      int lo = 0, hi = nb;  // bag slot s with s_off[s] <= p < s_off[s + 1]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (s_off[mid] <= p)
-          lo = mid;
-        else
-          hi = mid;
-      }
-      const uint32_t key = s_roff[lo] + static_cast<uint32_t>(ld_index<IT>(a.indices, p));
-      a.buf.keys[0][p] = key;
-      const uint32_t bag = static_cast<uint32_t>(k0 + lo);
-      if (a.use_rec) {
-        a.buf.vals[0][p] = static_cast<uint32_t>(p);
-        const float coef = (a.psw ? a.psw[p] : 1.0f) * s_scale[lo];
-        a.buf.rec[p] = make_uint2(bag, __float_as_uint(coef));
-      } else {
-        a.buf.vals[0][p] = bag;
-      }
-      // digit counts: lanes holding the same digit are matched through 8
-      // ballots and only the lowest of them adds their number (the high digits
-      // of one table's keys take few values, so per-lane atomics would queue
-      // on a handful of LDS words)
-      const uint64_t active = __ballot(1);
-      for (int q = 0; q < passes; ++q) {
-        const uint32_t d = (key >> (q * bits)) & dmask;
-        uint64_t peers = active;
-#pragma unroll
-        for (int bit = 0; bit < kMaxRadixBits; ++bit) {  // bits above `bits` are 0: no effect
-          const bool set = (d >> bit) & 1u;
-          const uint64_t bal = __ballot(set);
-          peers &= set ? bal : ~bal;
-        }
-        if (popc_below(peers) == 0) atomicAdd(&s_hist[q * slots + d], __popcll(peers));
-      }
-    }
-  }
-  __syncthreads();
-  for (int i = tid; i < passes * slots; i += 1024)
-    if (s_hist[i]) atomicAdd(&a.buf.digit_hist[i], s_hist[i]);
+__global__ __launch_bounds__(kLinThreads) void linearize_kernel(BackwardLaunch a) {
+  linearize_tiles<IT>(a, blockIdx.x, gridDim.x);
 }
 
 // Counts of digits d0 .. d0 + DPT - 1 in all tiles before `tile` (decoupled
@@ -580,22 +505,27 @@ int sort_tile_keys(int64_t n, int key_bits) {
   return radix_digit_bits(key_bits, n) > 8 ? 4096 : kBlock * sort_keys_per_thread(n);
 }
 
-hipError_t launch_linearize(const BackwardLaunch& a, hipStream_t stream, const KernelTimer* kt) {
-  // zero the counters, histograms and look-back status words first
+hipError_t launch_init_workspace(const BackwardLaunch& a, hipStream_t stream,
+                                 const KernelTimer* kt) {
+  // the counters, histograms and look-back status words the later kernels chain through
   int64_t zblocks = (a.buf.zero_words + kBlock - 1) / kBlock;
   if (zblocks > 1024) zblocks = 1024;
   launch_timed(kt, "init_workspace", init_workspace,
                dim3(static_cast<unsigned>(zblocks > 0 ? zblocks : 1)), dim3(kBlock), 0, stream,
                a.buf.counters, a.buf.zero_words);
-  int64_t blocks = (a.num_bags + kLinBags - 1) / kLinBags;
-  if (blocks <= 0) return hipGetLastError();
-  if (blocks > kLinMaxBlocks) blocks = kLinMaxBlocks;
+  return hipGetLastError();
+}
+
+hipError_t launch_linearize(const BackwardLaunch& a, hipStream_t stream, const KernelTimer* kt) {
+  const hipError_t e = launch_init_workspace(a, stream, kt);
+  if (e != hipSuccess || a.num_bags <= 0) return e;
+  const dim3 grid(static_cast<unsigned>(linearize_blocks(a.num_bags)));
   if (a.index64)
-    launch_timed(kt, "linearize_kernel", linearize_kernel<int64_t>,
-                 dim3(static_cast<unsigned>(blocks)), dim3(1024), 0, stream, a);
+    launch_timed(kt, "linearize_kernel", linearize_kernel<int64_t>, grid, dim3(kLinThreads), 0,
+                 stream, a);
   else
-    launch_timed(kt, "linearize_kernel", linearize_kernel<int32_t>,
-                 dim3(static_cast<unsigned>(blocks)), dim3(1024), 0, stream, a);
+    launch_timed(kt, "linearize_kernel", linearize_kernel<int32_t>, grid, dim3(kLinThreads), 0,
+                 stream, a);
   return hipGetLastError();
 }
 

@@ -24,6 +24,47 @@ def test_grouped_workload2_parity():
     parity(workloads.config(2), seed=0, steps=2, bag_sample=3000, row_sample=3000, grouped=True)
 
 
+def test_grouped_int32_ids():
+    parity(UNIT[4], seed=12, steps=2, index_dtype=torch.int32, grouped=True)
+
+
+def _grouped_vs_plain(spec, seed, steps, flags=0, index_dtype=torch.int64):
+    """Two handles on identical weights and state: one with the plain calls, one with
+    forward_group + backward_update_grouped.  Outputs, weights and state must be
+    identical after every step."""
+    a = make_problem(spec, seed=seed, flags=flags)
+    b = make_problem(spec, seed=seed, flags=flags)
+    for step in range(steps):
+        batch = workloads.batch(spec, seed=seed, step=step)
+        idx, off, psw = to_device(batch, index_dtype)
+        G = workloads.grad_output(spec, seed=seed, step=step, device="cuda")
+        ya = a.op.forward(spec.B, idx, off, psw)
+        yb = b.op.forward_group(spec.B, idx, off, psw)
+        a.op.backward_update(spec.B, idx, off, psw, G, spec.lr, spec.eps)
+        b.op.backward_update_grouped(spec.B, idx, off, psw, G, spec.lr, spec.eps)
+        torch.cuda.synchronize()
+        assert torch.equal(ya, yb), f"step {step}: forward"
+        assert torch.equal(a.W, b.W), f"step {step}: weights"
+        if a.state is not None:
+            assert torch.equal(a.state, b.state), f"step {step}: state"
+    a.op.close()
+    b.op.close()
+
+
+@pytest.mark.parametrize("every_table", [False, True], ids=["mixed", "all-routed"])
+def test_grouped_with_count_matrix_routing(every_table):
+    """Tables routed to the count-matrix forward are pooled by their own kernel; the fused
+    launch then pools only the others (none when every table is routed) and still
+    linearizes the whole batch."""
+    if every_table:
+        spec = workloads.custom([64, 700, 1000], [64, 32, 16], "bf16", B=257,
+                                lengths=("uniform_int", 0, 30), key=420)
+    else:
+        spec = workloads.custom([64, 5000, 1000], [64, 32, 48], "bf16", B=257,
+                                lengths=("uniform_int", 0, 30), key=421)
+    _grouped_vs_plain(spec, seed=13, steps=2, flags=tbe.FLAG_HISTOGRAM)
+
+
 @pytest.mark.parametrize("n", [2, 4])
 def test_grouped_matches_plain_bit_for_bit(n):
     """Two handles on identical weights and state, three steps each: one with the plain

@@ -186,10 +186,11 @@ tbe_status tbe_backward_update(tbe_handle* handle, int32_t B, const void* indice
 /* Forward plus the backward's grouping of the same batch.  kimbodo.com/?p=28372,
  * "Kimbodo Engineering Perspective": the transpose, sort and run-length
  * encoding of the backward can be done during the forward (an option that is
- * off by default there).  On `stream`: the workspace is cleared, one launch
- * pools the batch (as tbe_forward) and also linearizes it, the linearize
- * workgroups running beside the pooled lookup; then the sort and the
- * run-length encoding of the batch follow, into `workspace` (sized by
+ * off by default there).  On `stream`: the workspace is cleared, the batch
+ * is pooled (as tbe_forward) and linearized (for batches of at most 2^20
+ * lookups in one launch, the linearize workgroups running beside the pooled
+ * lookup; one after the other above that); then the sort and the run-length
+ * encoding of the batch follow, into `workspace` (sized by
  * tbe_backward_workspace_size, 256-byte aligned).  With TBE_FLAG_VALIDATE the
  * ids are checked before anything is queued.  Arguments and errors as
  * tbe_forward, plus TBE_ERR_WORKSPACE_TOO_SMALL.  The workspace must then go,

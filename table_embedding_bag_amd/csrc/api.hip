@@ -743,10 +743,14 @@ tbe_status tbe_forward_group(tbe_handle* h, int32_t B, const void* indices, cons
     KernelTimer timer{h, take_events};
     const KernelTimer* kt = h->profile ? &timer : nullptr;
     // workspace clear; the pooled lookup with the linearize step in the same
-    // launch; then the sort and the run-length encoding
+    // launch (the two one after the other for large batches); then the sort
+    // and the run-length encoding
     if (launch_init_workspace(a, s, kt) != hipSuccess) return TBE_ERR_HIP;
-    st = forward_impl(h, B, indices, offsets, index_dtype, n, psw, output, s, false, &a);
+    const bool fused = n <= kFusedMaxLookups;
+    st = forward_impl(h, B, indices, offsets, index_dtype, n, psw, output, s, false,
+                      fused ? &a : nullptr);
     if (st != TBE_OK) return st;
+    if (!fused && launch_linearize_kernel(a, s, kt) != hipSuccess) return TBE_ERR_HIP;
     int sorted = 0;
     if (launch_radix_sort(a, s, &sorted, kt) != hipSuccess) return TBE_ERR_HIP;
     return from_hip(launch_run_length_encode(a, a.buf.keys[sorted], s, kt));

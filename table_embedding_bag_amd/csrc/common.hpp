@@ -315,10 +315,15 @@ struct BackwardLaunch {
 // Zeroes the workspace's counters, digit counts and look-back status words.
 hipError_t launch_init_workspace(const BackwardLaunch& a, hipStream_t stream,
                                  const KernelTimer* kt);
+// The linearize kernel alone (workspace zeroed before).
+hipError_t launch_linearize_kernel(const BackwardLaunch& a, hipStream_t stream,
+                                   const KernelTimer* kt);
 // launch_init_workspace, then the linearize kernel.
 hipError_t launch_linearize(const BackwardLaunch& a, hipStream_t stream, const KernelTimer* kt);
 // One launch that pools the gather tables of f (as launch_forward_gather) and
-// linearizes the batch of b (its workspace zeroed before).
+// linearizes the batch of b (its workspace zeroed before); for batches of at
+// most kFusedMaxLookups lookups.
+constexpr int64_t kFusedMaxLookups = int64_t{1} << 20;
 hipError_t launch_forward_linearize(const ForwardLaunch& f, const BackwardLaunch& b,
                                     hipStream_t stream, const KernelTimer* kt);
 // Sorts buf.keys[0]/vals[0]; returns the index (0 or 1) of the buffer pair

@@ -25,6 +25,8 @@
 //    first lane group writes the fp32 output with 16-byte stores.
 //  * Workgroups are renumbered so that every XCD works on a contiguous range
 //    of tables, which keeps each table's hot rows in one XCD's L2.
+#include <algorithm>
+
 #include "common.hpp"
 #include "linearize.hpp"
 
@@ -149,22 +151,33 @@ __global__ __launch_bounds__(kBlock) void fwd_gather_pool(ForwardLaunch a) {
 
 // The pooled lookup and the linearize step of the backward's grouping in one
 // launch (kimbodo.com/?p=28372, "Kimbodo Engineering Perspective": the
-// grouping can be done during the forward).  The first lin_blocks workgroups
-// linearize; each later workgroup takes kLinThreads / kBlock consecutive
-// forward tiles.  The two kinds share no data, so the linearize workgroups,
+// grouping can be done during the forward).  Workgroups of kFusedThreads
+// threads: the first lin_blocks linearize (kFusedK lookups in flight per
+// thread, at most kFusedLinCap workgroups, each striding over tiles of bags);
+// every later workgroup takes kFusedThreads / kBlock consecutive tiles of the
+// pooled lookup.  The two kinds share no data, so the linearize workgroups,
 // which wait on memory most of the time, run beside the bandwidth-bound
-// forward instead of after it.  lin_blocks is a multiple of 8, so the forward
+// forward instead of after it.  Used for batches of at most
+// kFusedMaxLookups lookups: on larger ones the linearize workgroups fill the
+// chip before the forward's start and the two kernels one after the other
+// are faster (measured: 512 threads, two lookups in flight per thread, best of
+// 256-1024 threads and 1-8 lookups on the workload of 270k lookups).  lin_blocks is a multiple of 8, so the forward
 // workgroups keep the XCD-contiguous numbering of the stand-alone kernel.
+constexpr int kFusedThreads = 512;
+constexpr int kFusedK = 2;
+constexpr int64_t kFusedLinCap = 1024;
+
 template <int ST, typename IT, bool VEC, bool PSW>
-__global__ __launch_bounds__(kLinThreads) void fwd_linearize(ForwardLaunch f, BackwardLaunch b,
-                                                             int lin_blocks) {
+__global__ __launch_bounds__(kFusedThreads) void fwd_linearize(ForwardLaunch f, BackwardLaunch b,
+                                                               int lin_blocks) {
   const int bid = static_cast<int>(blockIdx.x);
   if (bid < lin_blocks) {
-    linearize_tiles<IT>(b, bid, lin_blocks);
+    linearize_tiles<IT, kFusedThreads, kFusedK>(b, bid, lin_blocks);
     return;
   }
-  constexpr int kPer = kLinThreads / kBlock;
-  const int logical = xcd_contiguous_block(bid - lin_blocks, static_cast<int>(gridDim.x) - lin_blocks);
+  constexpr int kPer = kFusedThreads / kBlock;
+  const int logical =
+      xcd_contiguous_block(bid - lin_blocks, static_cast<int>(gridDim.x) - lin_blocks);
   fwd_tile<ST, IT, VEC, PSW>(f, logical * kPer + static_cast<int>(threadIdx.x) / kBlock,
                              (static_cast<int>(threadIdx.x) % kBlock) >> 6);
 }
@@ -320,7 +333,7 @@ hipError_t dispatch_index(const ForwardLaunch& a, hipStream_t s, dim3 grid,
 template <int ST, typename IT>
 hipError_t launch_fused(const ForwardLaunch& f, const BackwardLaunch& b, int lin, hipStream_t s,
                         dim3 grid, const KernelTimer* kt) {
-  const dim3 block(kLinThreads);
+  const dim3 block(kFusedThreads);
   if (f.vec) {
     if (f.psw)
       launch_timed(kt, "fwd_linearize", fwd_linearize<ST, IT, true, true>, grid, block, 0, s, f, b, lin);
@@ -380,9 +393,9 @@ hipError_t launch_forward_linearize(const ForwardLaunch& f, const BackwardLaunch
                                     hipStream_t stream, const KernelTimer* kt) {
   if (f.index64 != b.index64) return hipErrorInvalidValue;
   const int64_t tiles = static_cast<int64_t>(f.T) * f.tiles_per_table;
-  constexpr int kPer = kLinThreads / kBlock;
+  constexpr int kPer = kFusedThreads / kBlock;
   // linearize workgroups first, rounded up to a multiple of the 8 XCDs
-  const int64_t lin = (linearize_blocks(b.num_bags) + 7) / 8 * 8;
+  const int64_t lin = (std::min(linearize_blocks(b.num_bags), kFusedLinCap) + 7) / 8 * 8;
   const int64_t blocks = lin + (tiles + kPer - 1) / kPer;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const dim3 grid(static_cast<unsigned>(blocks));

@@ -30,17 +30,20 @@ __device__ __forceinline__ int64_t lin_index(const void* p, int64_t i) {
   return static_cast<int64_t>(static_cast<const IT*>(p)[i]);
 }
 
-// A workgroup of kLinThreads threads takes tiles first, first + stride, ... of
+// A workgroup of NT threads takes tiles first, first + stride, ... of
 // kLinBags consecutive bags.  A tile's offsets are staged in LDS; the
-// workgroup then walks all of its lookups with consecutive threads on
-// consecutive lookups and finds each lookup's bag by binary search in LDS.
-// Digit counts are kept in LDS across the workgroup's tiles and added to the
-// global counts once at the end (a bounded grid keeps those global atomics,
-// all on the same few hundred words, few).  The digit counts must be zero
-// before the first workgroup starts.
-template <typename IT>
+// workgroup then walks the tile's lookups NT * K at a time, each thread
+// taking K positions (consecutive threads on consecutive lookups): the bags
+// are found by binary search in LDS and all K row ids are loaded before any
+// is used, so a thread keeps K loads in flight.  Digit counts are kept in LDS
+// across the workgroup's tiles and added to the global counts once at the end
+// (a bounded grid keeps those global atomics, all on the same few hundred
+// words, few).  The global digit counts must be zero before the first
+// workgroup starts.
+template <typename IT, int NT, int K>
 __device__ __forceinline__ void linearize_tiles(const BackwardLaunch& a, int64_t first,
                                                 int64_t stride) {
+  static_assert(NT >= kLinBags, "one thread per bag stages the offsets");
   __shared__ int64_t s_off[kLinBags + 1];
   __shared__ uint32_t s_roff[kLinBags];
   __shared__ float s_scale[kLinBags];
@@ -51,7 +54,7 @@ __device__ __forceinline__ void linearize_tiles(const BackwardLaunch& a, int64_t
   const int bits = radix_digit_bits(a.key_bits, a.num_indices);
   const int slots = radix_slots(bits);
   const uint32_t dmask = (1u << bits) - 1u;
-  for (int i = tid; i < passes * slots; i += kLinThreads) s_hist[i] = 0u;
+  for (int i = tid; i < passes * slots; i += NT) s_hist[i] = 0u;
   const int64_t ntiles = (a.num_bags + kLinBags - 1) / kLinBags;
   for (int64_t tile = first; tile < ntiles; tile += stride) {
     const int64_t k0 = tile * kLinBags;
@@ -70,45 +73,68 @@ __device__ __forceinline__ void linearize_tiles(const BackwardLaunch& a, int64_t
     __syncthreads();
 
     const int64_t p0 = s_off[0], p1 = s_off[nb];
-    for (int64_t p = p0 + tid; p < p1; p += kLinThreads) {
-      int lo = 0, hi = nb;  // bag slot s with s_off[s] <= p < s_off[s + 1]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (s_off[mid] <= p)
-          lo = mid;
-        else
-          hi = mid;
-      }
-      const uint32_t key = s_roff[lo] + static_cast<uint32_t>(lin_index<IT>(a.indices, p));
-      a.buf.keys[0][p] = key;
-      const uint32_t bag = static_cast<uint32_t>(k0 + lo);
-      if (a.use_rec) {
-        a.buf.vals[0][p] = static_cast<uint32_t>(p);
-        const float coef = (a.psw ? a.psw[p] : 1.0f) * s_scale[lo];
-        a.buf.rec[p] = make_uint2(bag, __float_as_uint(coef));
-      } else {
-        a.buf.vals[0][p] = bag;
-      }
-      // digit counts: lanes holding the same digit are matched through 8
-      // ballots and only the lowest of them adds their number (the high digits
-      // of one table's keys take few values, so per-lane atomics would queue
-      // on a handful of LDS words)
-      const uint64_t active = __ballot(1);
-      for (int q = 0; q < passes; ++q) {
-        const uint32_t d = (key >> (q * bits)) & dmask;
-        uint64_t peers = active;
+    for (int64_t base = p0; base < p1; base += static_cast<int64_t>(NT) * K) {
+      int slot[K];
+      bool ok[K];
+      int64_t x[K];
+      float pw[K];
 #pragma unroll
-        for (int bit = 0; bit < kMaxRadixBits; ++bit) {  // bits above `bits` are 0: no effect
-          const bool set = (d >> bit) & 1u;
-          const uint64_t bal = __ballot(set);
-          peers &= set ? bal : ~bal;
+      for (int k = 0; k < K; ++k) {
+        const int64_t p = base + tid + static_cast<int64_t>(NT) * k;
+        ok[k] = p < p1;
+        int lo = 0, hi = nb;  // bag slot s with s_off[s] <= p < s_off[s + 1]
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (s_off[mid] <= p)
+            lo = mid;
+          else
+            hi = mid;
         }
-        if (popc_below(peers) == 0) atomicAdd(&s_hist[q * slots + d], __popcll(peers));
+        slot[k] = lo;
+      }
+      // every load of the batch is issued before any is used (positions past
+      // the tile read its last lookup instead)
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int64_t p = ok[k] ? base + tid + static_cast<int64_t>(NT) * k : p1 - 1;
+        x[k] = lin_index<IT>(a.indices, p);
+        pw[k] = a.psw ? a.psw[p] : 1.0f;
+      }
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int64_t p = base + tid + static_cast<int64_t>(NT) * k;
+        const uint32_t key = s_roff[slot[k]] + static_cast<uint32_t>(x[k]);
+        const uint32_t bag = static_cast<uint32_t>(k0 + slot[k]);
+        if (ok[k]) {
+          a.buf.keys[0][p] = key;
+          if (a.use_rec) {
+            a.buf.vals[0][p] = static_cast<uint32_t>(p);
+            a.buf.rec[p] = make_uint2(bag, __float_as_uint(pw[k] * s_scale[slot[k]]));
+          } else {
+            a.buf.vals[0][p] = bag;
+          }
+        }
+        // digit counts: lanes holding the same digit are matched through one
+        // ballot per digit bit and only the lowest of them adds their number
+        // (the high digits of one table's keys take few values, so per-lane
+        // atomics would queue on a handful of LDS words)
+        const uint64_t active = __ballot(ok[k]);
+        if (active == 0) continue;
+        for (int q = 0; q < passes; ++q) {
+          const uint32_t d = (key >> (q * bits)) & dmask;
+          uint64_t peers = active;
+          for (int bit = 0; bit < bits; ++bit) {
+            const bool set = (d >> bit) & 1u;
+            const uint64_t bal = __ballot(set);
+            peers &= set ? bal : ~bal;
+          }
+          if (ok[k] && popc_below(peers) == 0) atomicAdd(&s_hist[q * slots + d], __popcll(peers));
+        }
       }
     }
   }
   __syncthreads();
-  for (int i = tid; i < passes * slots; i += kLinThreads)
+  for (int i = tid; i < passes * slots; i += NT)
     if (s_hist[i]) atomicAdd(&a.buf.digit_hist[i], s_hist[i]);
 }
 

@@ -65,9 +65,11 @@ __global__ __launch_bounds__(kBlock) void init_workspace(uint32_t* words, int64_
     words[i] = 0u;
 }
 
-template <typename IT>
+// K lookups in flight per thread: 2 when a tile holds more lookups than the
+// workgroup has threads, else 1 (short bags would leave half the slots idle).
+template <typename IT, int K>
 __global__ __launch_bounds__(kLinThreads) void linearize_kernel(BackwardLaunch a) {
-  linearize_tiles<IT>(a, blockIdx.x, gridDim.x);
+  linearize_tiles<IT, kLinThreads, K>(a, blockIdx.x, gridDim.x);
 }
 
 // Counts of digits d0 .. d0 + DPT - 1 in all tiles before `tile` (decoupled
@@ -518,14 +520,31 @@ hipError_t launch_init_workspace(const BackwardLaunch& a, hipStream_t stream,
 
 hipError_t launch_linearize(const BackwardLaunch& a, hipStream_t stream, const KernelTimer* kt) {
   const hipError_t e = launch_init_workspace(a, stream, kt);
-  if (e != hipSuccess || a.num_bags <= 0) return e;
+  if (e != hipSuccess) return e;
+  return launch_linearize_kernel(a, stream, kt);
+}
+
+hipError_t launch_linearize_kernel(const BackwardLaunch& a, hipStream_t stream,
+                                   const KernelTimer* kt) {
+  if (a.num_bags <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(linearize_blocks(a.num_bags)));
-  if (a.index64)
-    launch_timed(kt, "linearize_kernel", linearize_kernel<int64_t>, grid, dim3(kLinThreads), 0,
-                 stream, a);
-  else
-    launch_timed(kt, "linearize_kernel", linearize_kernel<int32_t>, grid, dim3(kLinThreads), 0,
-                 stream, a);
+  const int64_t tiles = (a.num_bags + kLinBags - 1) / kLinBags;
+  const bool deep = a.num_indices > tiles * kLinThreads;
+  if (a.index64) {
+    if (deep)
+      launch_timed(kt, "linearize_kernel", linearize_kernel<int64_t, 2>, grid, dim3(kLinThreads),
+                   0, stream, a);
+    else
+      launch_timed(kt, "linearize_kernel", linearize_kernel<int64_t, 1>, grid, dim3(kLinThreads),
+                   0, stream, a);
+  } else {
+    if (deep)
+      launch_timed(kt, "linearize_kernel", linearize_kernel<int32_t, 2>, grid, dim3(kLinThreads),
+                   0, stream, a);
+    else
+      launch_timed(kt, "linearize_kernel", linearize_kernel<int32_t, 1>, grid, dim3(kLinThreads),
+                   0, stream, a);
+  }
   return hipGetLastError();
 }
 

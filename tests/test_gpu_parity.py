@@ -159,6 +159,27 @@ def test_int32_indices(spec):
     parity(spec, seed=2, steps=1, index_dtype=torch.int32)
 
 
+# more tables than the segment kernels stage in LDS (256): table metadata is then read from
+# global memory
+_rng = np.random.default_rng(301)
+MANY = [
+    workloads.custom(_rng.integers(3, 60, 300), [(4, 8, 16, 12)[t % 4] for t in range(300)], "f32",
+                     B=7, lengths=("uniform_int", 0, 6), pooling="mean", psw=True,
+                     optimizer="rowwise_adagrad", key=301),
+    workloads.custom(_rng.integers(3, 60, 270), [(8, 16, 32)[t % 3] for t in range(270)], "bf16",
+                     B=5, lengths=("uniform_int", 0, 9), index_dist=("zipf", 1.3), key=302),
+]
+
+
+@pytest.mark.parametrize("spec", MANY, ids=["300-f32-mean-psw-adagrad", "270-bf16-sum-sgd"])
+def test_many_tables(spec):
+    parity(spec, seed=3, steps=2)
+
+
+def test_many_tables_grouped():
+    parity(MANY[0], seed=4, steps=2, grouped=True)
+
+
 def _hand_batch(T, B, bags):
     """bags: list (per table) of lists (per bag) of row ids."""
     lens = [len(b) for tb in bags for b in tb]

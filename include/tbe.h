@@ -136,7 +136,17 @@ typedef enum {
   /* 1: every kernel the calls launch records its own start and end in a pair
    * of HIP events (hipExtLaunchKernelGGL), readable with tbe_stage_times;
    * 0 (default): off. */
-  TBE_OPTION_PROFILE = 2
+  TBE_OPTION_PROFILE = 2,
+  /* How the backward groups lookups by (table, row) id ("Kimbodo Engineering
+   * Perspective": transpose, sort, run-length encoding).
+   * 0 (default): when the batch sorts in two radix digits (at most 2^20
+   *    lookups, ids of 11 to 20 bits), one pass on the high digit and then a
+   *    bucket-local sort with the run-length encoding in the same kernel;
+   *    otherwise as 1.
+   * 1: LSD radix passes, then a separate run-length-encoding kernel.
+   * Both give the same order (stable on the id), so results are bit-identical.
+   * Other values: TBE_ERR_INVALID_ARGUMENT. */
+  TBE_OPTION_SORT = 3
 } tbe_option;
 
 /* Create a handle.  Validates the configuration (host only; nothing is

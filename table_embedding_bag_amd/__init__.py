@@ -23,7 +23,7 @@ __all__ = [
     "tbe_status_string", "tbe_abi_version", "TBE",
     "F32", "F16", "BF16", "POOL_SUM", "POOL_MEAN", "OPT_SGD", "OPT_ROWWISE_ADAGRAD",
     "FLAG_VALIDATE", "FLAG_NO_HISTOGRAM", "FLAG_FORCE_HISTOGRAM", "FLAG_HISTOGRAM",
-    "OPTION_LONG_RUN_THRESHOLD", "OPTION_PROFILE", "EXPORTED_SYMBOLS",
+    "OPTION_LONG_RUN_THRESHOLD", "OPTION_PROFILE", "OPTION_SORT", "EXPORTED_SYMBOLS",
 ]
 
 F32, F16, BF16 = 0, 1, 2
@@ -31,7 +31,7 @@ I32, I64 = 0, 1
 POOL_SUM, POOL_MEAN = 0, 1
 OPT_SGD, OPT_ROWWISE_ADAGRAD = 0, 1
 FLAG_VALIDATE, FLAG_NO_HISTOGRAM, FLAG_FORCE_HISTOGRAM, FLAG_HISTOGRAM = 1, 2, 4, 8
-OPTION_LONG_RUN_THRESHOLD, OPTION_PROFILE = 1, 2
+OPTION_LONG_RUN_THRESHOLD, OPTION_PROFILE, OPTION_SORT = 1, 2, 3
 
 STATUS = {
     0: "TBE_OK", 1: "TBE_ERR_INVALID_ARGUMENT", 2: "TBE_ERR_UNSUPPORTED",

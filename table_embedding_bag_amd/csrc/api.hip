@@ -43,6 +43,7 @@ struct tbe_handle {
   int32_t hist_etiles = 0, hist_dtiles = 0;
   int64_t wt_elems = 0;
   int64_t long_threshold = 256;
+  bool bucket_sort = true;  // TBE_OPTION_SORT
   // profiling: pairs of events handed to timed kernel launches (start and end
   // of that kernel), kept until tbe_stage_times reads them
   bool profile = false;
@@ -206,7 +207,9 @@ bool plan_backward(const tbe_handle* h, int64_t n, bool vec, BwdPlan* p) {
   p->pstride = static_cast<int32_t>((h->dmax + 3) / 4 * 4);
   const int64_t sort_tile = sort_tile_keys(n, h->key_bits);
   p->sort_tiles = static_cast<int>((n + sort_tile - 1) / sort_tile);
-  p->rle_tiles = static_cast<int>((n + kRleTile - 1) / kRleTile);
+  // look-back status words of the RLE kernel, or those of the bucket-local
+  // sort's windows followed by the windows' 4-word range records
+  p->rle_tiles = 5 * static_cast<int>((n + kBucketWindow - 1) / kBucketWindow) + 4;
   p->passes = radix_passes(h->key_bits, n);
   p->slots = radix_slots(radix_digit_bits(h->key_bits, n));
   const SegmentBounds ub = segment_bounds(n, h->long_threshold, kChunk, p->gshift);
@@ -263,6 +266,7 @@ void fill_backward(const tbe_handle* h, int32_t B, const void* indices, const vo
   a.gshift = p.gshift;
   a.pstride = p.pstride;
   a.long_threshold = static_cast<int32_t>(std::min<int64_t>(h->long_threshold, 0x7FFFFFFF));
+  a.bucket_sort = h->bucket_sort ? 1 : 0;
   a.chunk = kChunk;
   a.lr = lr;
   a.eps = eps;
@@ -296,10 +300,7 @@ void fill_backward(const tbe_handle* h, int32_t B, const void* indices, const vo
 hipError_t launch_front(const BackwardLaunch& a, hipStream_t s, const KernelTimer* kt) {
   hipError_t e = launch_linearize(a, s, kt);
   if (e != hipSuccess) return e;
-  int sorted = 0;
-  e = launch_radix_sort(a, s, &sorted, kt);
-  if (e != hipSuccess) return e;
-  return launch_run_length_encode(a, a.buf.keys[sorted], s, kt);
+  return launch_sort_encode(a, s, kt);
 }
 
 tbe_status backward_impl(tbe_handle* h, int32_t B, const void* indices, const void* offsets,
@@ -524,6 +525,10 @@ tbe_status tbe_set_option(tbe_handle* h, int32_t option, int64_t value) {
       return TBE_OK;
     case TBE_OPTION_PROFILE:
       h->profile = value != 0;
+      return TBE_OK;
+    case TBE_OPTION_SORT:
+      if (value != 0 && value != 1) return TBE_ERR_INVALID_ARGUMENT;
+      h->bucket_sort = value == 0;
       return TBE_OK;
   }
   return TBE_ERR_INVALID_ARGUMENT;
@@ -751,9 +756,7 @@ tbe_status tbe_forward_group(tbe_handle* h, int32_t B, const void* indices, cons
                       fused ? &a : nullptr);
     if (st != TBE_OK) return st;
     if (!fused && launch_linearize_kernel(a, s, kt) != hipSuccess) return TBE_ERR_HIP;
-    int sorted = 0;
-    if (launch_radix_sort(a, s, &sorted, kt) != hipSuccess) return TBE_ERR_HIP;
-    return from_hip(launch_run_length_encode(a, a.buf.keys[sorted], s, kt));
+    return from_hip(launch_sort_encode(a, s, kt));
   } catch (...) {
     return TBE_ERR_OUT_OF_MEMORY;
   }

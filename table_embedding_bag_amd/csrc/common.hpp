@@ -305,6 +305,7 @@ struct BackwardLaunch {
   int32_t pstride;          // floats per partial row
   int32_t long_threshold;   // runs at least this long use split accumulation
   int32_t chunk;            // lookups per level-1 partial
+  int32_t bucket_sort;      // two-digit ids: high-digit pass + bucket-local sort and RLE
   float lr, eps;
   int32_t* out_unique;      // optional run outputs
   int32_t* out_lengths;
@@ -332,6 +333,12 @@ hipError_t launch_radix_sort(const BackwardLaunch& a, hipStream_t stream, int* r
                              const KernelTimer* kt);
 hipError_t launch_run_length_encode(const BackwardLaunch& a, const uint32_t* sorted_keys,
                                     hipStream_t stream, const KernelTimer* kt);
+// Sort and run-length encoding of the linearized batch in buf.keys[0] /
+// buf.vals[0]: for ids of two radix digits (and a.bucket_sort), a pass on the
+// high digit and the bucket-local sort with its run-length encoding; else the
+// LSD passes and the RLE kernel.  Either way the sorted pair ends in buffer
+// radix_passes() % 2 and the order is the same (stable on the id).
+hipError_t launch_sort_encode(const BackwardLaunch& a, hipStream_t stream, const KernelTimer* kt);
 hipError_t launch_segment_reduce_update(const BackwardLaunch& a, const uint32_t* sorted_keys,
                                         const uint32_t* sorted_vals, hipStream_t stream,
                                         const KernelTimer* kt);
@@ -345,6 +352,9 @@ constexpr int kMaxDim = 1024;
 
 // Tile sizes shared by the planner (workspace sizing) and the kernels.
 constexpr int kRleTile = 4096;
+// Sorted positions per window of the bucket-local sort: a window takes the
+// buckets of the high digit that start inside it.
+constexpr int kBucketWindow = 2048;
 
 // LSD radix sort plan for n keys of key_bits bits: the fewest passes of
 // digits of at most kMaxRadixBits bits, the bits split evenly over the

@@ -159,6 +159,20 @@ __device__ __forceinline__ uint64_t match_digit(uint64_t* s_slots, uint32_t d, b
   return peers;
 }
 
+// Window range records of the bucket-local sort: bucket d of the high digit
+// (sorted positions [start, start + count)) belongs to window start /
+// kBucketWindow.  A record is {~first start, end, ~first bucket, last bucket +
+// 1}, built with atomic maxima on a zeroed record, so 0 in the last word
+// means the window starts no bucket.
+__device__ __forceinline__ void record_window(uint32_t* wtable, uint32_t start, uint32_t count,
+                                              uint32_t d) {
+  uint32_t* w = wtable + 4 * (start / kBucketWindow);
+  atomicMax(w + 0, ~start);
+  atomicMax(w + 1, start + count);
+  atomicMax(w + 2, ~d);
+  atomicMax(w + 3, d + 1u);
+}
+
 // One LSD pass on the digit (key >> shift) & (2^bits - 1), bits <= RB.  A
 // tile of 256*KPT keys; thread tid owns the DPT = 2^RB / 256 consecutive
 // digits tid*DPT .. tid*DPT + DPT - 1 for counting, look-back and offsets.
@@ -166,7 +180,7 @@ template <int KPT, int RB>
 __global__ __launch_bounds__(kBlock) void radix_pass(
     const uint32_t* __restrict__ kin, const uint32_t* __restrict__ vin, uint32_t* __restrict__ kout,
     uint32_t* __restrict__ vout, int64_t n, int shift, int bits, const uint32_t* __restrict__ totals,
-    uint32_t* status, uint32_t* ticket, uint32_t* err) {
+    uint32_t* status, uint32_t* ticket, uint32_t* err, uint32_t* wtable) {
   constexpr int TS = kBlock * KPT;
   constexpr int RMAX = 1 << RB;
   constexpr int DPT = RMAX / kBlock;
@@ -261,6 +275,13 @@ __global__ __launch_bounds__(kBlock) void radix_pass(
   const uint32_t gbase = block_exclusive_sum(gsum, scratch, &total);
 #pragma unroll
   for (int q = 0; q < DPT; ++q) s_gbase[d0 + q] = gbase + gloc[q] + before[q];
+  if (wtable) {  // every tile knows all bucket starts; digit d is recorded by tile d % tiles
+    const int ntiles = static_cast<int>((n + TS - 1) / TS);
+#pragma unroll
+    for (int q = 0; q < DPT; ++q)
+      if (my_total[q] > 0 && (d0 + q) % ntiles == tile)
+        record_window(wtable, gbase + gloc[q], my_total[q], d0 + q);
+  }
   __syncthreads();
 
 #pragma unroll
@@ -312,7 +333,7 @@ template <int KPT, int RB>
 __global__ __launch_bounds__(1024) void radix_pass_wide(
     const uint32_t* __restrict__ kin, const uint32_t* __restrict__ vin, uint32_t* __restrict__ kout,
     uint32_t* __restrict__ vout, int64_t n, int shift, int bits, const uint32_t* __restrict__ totals,
-    uint32_t* status, uint32_t* ticket, uint32_t* err) {
+    uint32_t* status, uint32_t* ticket, uint32_t* err, uint32_t* wtable) {
   constexpr int NT = 1024, NW = NT / kWave;
   constexpr int TS = NT * KPT;
   constexpr int RMAX = 1 << RB;
@@ -373,6 +394,9 @@ __global__ __launch_bounds__(1024) void radix_pass_wide(
   st_status(my_status, (tile == 0 ? kFlagIncl : kFlagAgg) | mine);
   // the bucket's global start does not depend on the look-back
   const uint32_t gb = block_excl_n<NW>(my_total, scratch, &total);
+  // every tile knows all bucket starts; digit d is recorded by tile d % tiles
+  if (wtable && my_total > 0 && tid % static_cast<int>((n + TS - 1) / TS) == tile)
+    record_window(wtable, gb, my_total, tid);
   uint32_t before[1] = {0u};
   if (tile > 0) {
     lookback_digits<1, 16>(status, RMAX, tile, tid, err, before);
@@ -500,6 +524,320 @@ __global__ __launch_bounds__(1024) void rle_kernel(const uint32_t* __restrict__ 
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Ids of two digits: one look-back pass on the HIGH digit, then a
+// bucket-local sort and run-length encoding.
+//
+// After a stable pass on the high digit every bucket holds whole runs (equal
+// ids share their high digit), so the rest of the sort and the run heads are
+// local to a bucket.  A window of kBucketWindow sorted positions takes the
+// buckets that start inside it (each bucket belongs to exactly one window);
+// its range of whole buckets is sorted in LDS by two stable counting passes
+// (low digit, then bucket), which leaves the ids in the order of the two LSD
+// passes (stable on the full id).  The range's run heads are counted, the
+// range's first run id comes from a look-back over the earlier windows' run
+// counts, and unique ids and run starts are written.  This replaces the
+// second look-back pass and the RLE kernel.  Ranges longer than kBucketCap
+// (a bucket of more than kBucketCap - kBucketWindow lookups) are sorted
+// bucket by bucket in chunks of kBucketCap through global memory.
+
+constexpr int kBucketThreads = 1024;
+constexpr int kBucketWaves = kBucketThreads / kWave;
+constexpr int kBucketKpt = 8;
+constexpr int kBucketCap = kBucketThreads * kBucketKpt;
+constexpr int64_t kBucketMeanMax = 1024;  // largest mean bucket the path is used for
+
+// One stable counting pass in LDS over elements held in registers: wave w
+// holds relative positions [w*64*rr, (w+1)*64*rr), round r of lane l position
+// q = w*64*rr + r*64 + l, and the elements with qlo <= q < qhi take part
+// (qhi - qlo <= kBucketCap); digit(key) < 1024.  Afterwards s_k/s_v hold
+// those elements in digit order (position order among equal digits) at
+// 0 .. qhi - qlo - 1, and s_dstart[d] is the first position of digit d.
+// s_cnt must be zero on entry and is zero again on return (after a barrier of
+// the caller).
+template <typename Digit>
+__device__ __forceinline__ void lds_counting_pass(const uint32_t (&key)[kBucketKpt],
+                                                  const uint32_t (&val)[kBucketKpt], int rr,
+                                                  int qlo, int qhi, Digit digit, uint32_t* s_k,
+                                                  uint32_t* s_v,
+                                                  uint16_t (*s_cnt)[kBucketThreads],
+                                                  uint64_t (*s_slots)[256], uint32_t* s_dstart,
+                                                  uint32_t* scratch) {
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int wseg = wave * kWave * rr;
+  uint32_t rank[kBucketKpt];
+#pragma unroll
+  for (int r = 0; r < kBucketKpt; ++r) {
+    rank[r] = 0u;
+    if (r < rr) {
+      const int q = wseg + r * kWave + lane;
+      const bool ok = q >= qlo && q < qhi;
+      const uint32_t d = ok ? digit(key[r]) : 0u;
+      const uint64_t peers = match_digit<10>(s_slots[wave], d, ok);
+      const uint32_t below = popc_below(peers);
+      const uint32_t pre = ok ? static_cast<uint32_t>(s_cnt[wave][d]) : 0u;
+      rank[r] = pre + below;
+      if (ok && below == 0) s_cnt[wave][d] = static_cast<uint16_t>(pre + __popcll(peers));
+    }
+  }
+  __syncthreads();
+  // digit tid: the waves' offsets inside the digit, then the digit's start
+  // (waves past the last element hold no counts)
+  const int nwa = (qhi + kWave * rr - 1) / (kWave * rr);
+  uint32_t c[kBucketWaves];
+#pragma unroll
+  for (int w = 0; w < kBucketWaves; ++w) c[w] = w < nwa ? s_cnt[w][tid] : 0u;
+  uint32_t mine = 0;
+#pragma unroll
+  for (int w = 0; w < kBucketWaves; ++w) {
+    if (w < nwa) s_cnt[w][tid] = static_cast<uint16_t>(mine);
+    mine += c[w];
+  }
+  uint32_t total;
+  s_dstart[tid] = block_excl_n<kBucketWaves>(mine, scratch, &total);
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kBucketKpt; ++r) {
+    const int q = wseg + r * kWave + lane;
+    if (r < rr && q >= qlo && q < qhi) {
+      const uint32_t d = digit(key[r]);
+      const uint32_t lp = s_dstart[d] + s_cnt[wave][d] + rank[r];
+      s_k[lp] = key[r];
+      s_v[lp] = val[r];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kBucketWaves; ++w)
+    if (w < nwa) s_cnt[w][tid] = 0;
+}
+
+// Load positions [start, start + len) (len <= kBucketCap) into registers in
+// the layout of lds_counting_pass.
+__device__ __forceinline__ void load_range(const uint32_t* kin, const uint32_t* vin, int64_t start,
+                                           int len, int rr, uint32_t (&key)[kBucketKpt],
+                                           uint32_t (&val)[kBucketKpt]) {
+  const int wseg = (threadIdx.x >> 6) * kWave * rr;
+#pragma unroll
+  for (int r = 0; r < kBucketKpt; ++r) {
+    const int p = wseg + r * kWave + lane_id();
+    const bool ok = r < rr && p < len;
+    key[r] = ok ? kin[start + p] : 0u;
+    val[r] = ok ? vin[start + p] : 0u;
+  }
+}
+
+__global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
+    const uint32_t* __restrict__ kin, const uint32_t* __restrict__ vin, uint32_t* kout,
+    uint32_t* vout, int64_t n, int lbits, int nbuckets, const uint32_t* __restrict__ htotals,
+    const uint32_t* __restrict__ wtable, int ntiles, uint32_t* status, uint32_t* ticket,
+    uint32_t* counters, uint32_t* unique_keys, uint32_t* run_start) {
+  constexpr int NT = kBucketThreads, NW = kBucketWaves, CAP = kBucketCap;
+  __shared__ uint32_t s_k[CAP];
+  __shared__ uint32_t s_v[CAP];
+  __shared__ uint16_t s_cnt[NW][NT];
+  __shared__ uint64_t s_slots[NW][256];
+  __shared__ uint32_t s_bstart[NT + 1];  // long ranges: bucket starts in the sorted order
+  __shared__ uint32_t s_dstart[NT];
+  __shared__ uint32_t s_dbase[NT];       // long ranges: digit starts inside the bucket
+  __shared__ uint32_t s_run[NT];         // long ranges: digit positions used so far
+  __shared__ uint32_t scratch[NW];
+  __shared__ uint32_t s_tile, s_base;
+
+  const int tid = threadIdx.x, wave = tid >> 6;
+  int tile = static_cast<int>(blockIdx.x);
+  if (ticket) {
+    if (tid == 0) s_tile = atomicAdd(ticket, 1u);
+    __syncthreads();
+    tile = static_cast<int>(s_tile);
+  }
+  // The window's range record and its first CAP sorted positions are loaded
+  // together; a range starts inside the window, so it usually lies within
+  // them.  Wave w loads positions w0 + [w*64*KPT, (w+1)*64*KPT).
+  const int64_t w0 = static_cast<int64_t>(tile) * kBucketWindow;
+  const uint4 rec = *reinterpret_cast<const uint4*>(wtable + 4 * static_cast<int64_t>(tile));
+  uint32_t key[kBucketKpt], val[kBucketKpt];
+#pragma unroll
+  for (int r = 0; r < kBucketKpt; ++r) {
+    const int64_t p = w0 + wave * kWave * kBucketKpt + r * kWave + lane_id();
+    key[r] = p < n ? kin[p] : 0u;
+    val[r] = p < n ? vin[p] : 0u;
+  }
+#pragma unroll
+  for (int w = 0; w < NW; ++w) s_cnt[w][tid] = 0;
+  for (int i = tid; i < NW * 256; i += NT) (&s_slots[0][0])[i] = 0u;
+  const bool empty = rec.w == 0u;
+  const int64_t start = empty ? 0 : static_cast<int64_t>(~rec.x);
+  const int64_t len64 = empty ? 0 : static_cast<int64_t>(rec.y) - start;
+  const uint32_t hf = ~rec.z, hl = rec.w - 1u;
+  const uint32_t lmask = (1u << lbits) - 1u;
+  const auto low = [lmask](uint32_t k) { return k & lmask; };
+
+  uint32_t my_heads = 0;  // run heads among this thread's positions
+  int rr = 0;             // positions per thread in the sorted range
+  if (len64 <= CAP) {
+    const int len = static_cast<int>(len64);
+    rr = (len + NT - 1) / NT;
+    if (len > 0) {
+      if (start + len <= w0 + CAP) {
+        // the range's positions go to LDS in order, then back in the layout
+        // of lds_counting_pass
+#pragma unroll
+        for (int r = 0; r < kBucketKpt; ++r) {
+          const int64_t q = w0 + wave * kWave * kBucketKpt + r * kWave + lane_id() - start;
+          if (q >= 0 && q < len) {
+            s_k[q] = key[r];
+            s_v[q] = val[r];
+          }
+        }
+        __syncthreads();
+        const int wseg = wave * kWave * rr;
+#pragma unroll
+        for (int r = 0; r < kBucketKpt; ++r) {
+          const int q = wseg + r * kWave + lane_id();
+          if (r < rr && q < len) {
+            key[r] = s_k[q];
+            val[r] = s_v[q];
+          }
+        }
+      } else {
+        load_range(kin, vin, start, len, rr, key, val);
+      }
+      __syncthreads();
+      lds_counting_pass(key, val, rr, 0, len, low, s_k, s_v, s_cnt, s_slots, s_dstart, scratch);
+      if (hl > hf) {  // several buckets: a stable pass on the bucket restores their order
+        const int wseg = wave * kWave * rr;
+#pragma unroll
+        for (int r = 0; r < kBucketKpt; ++r) {
+          const int p = wseg + r * kWave + lane_id();
+          if (r < rr && p < len) {
+            key[r] = s_k[p];
+            val[r] = s_v[p];
+          }
+        }
+        __syncthreads();
+        const uint32_t hmask = static_cast<uint32_t>(nbuckets) - 1u;
+        const auto bucket = [lbits, hf, hmask](uint32_t k) { return ((k >> lbits) & hmask) - hf; };
+        lds_counting_pass(key, val, rr, 0, len, bucket, s_k, s_v, s_cnt, s_slots, s_dstart,
+                          scratch);
+      }
+      // the sorted range goes out before the look-back (it does not depend on it)
+      for (int i = tid; i < len; i += NT) {
+        kout[start + i] = s_k[i];
+        vout[start + i] = s_v[i];
+      }
+      // a range starts a bucket, so its first position is always a run head
+      for (int j = 0; j < rr; ++j) {
+        const int i = tid * rr + j;
+        if (i < len && (i == 0 || s_k[i] != s_k[i - 1])) ++my_heads;
+      }
+    }
+  } else {
+    // long range: bucket by bucket, chunks of CAP positions in order
+    {
+      const uint32_t my_count = tid < nbuckets ? htotals[tid] : 0u;
+      uint32_t tot;
+      s_bstart[tid] = block_excl_n<NW>(my_count, scratch, &tot);
+      if (tid == 0) s_bstart[NT] = tot;
+      __syncthreads();
+    }
+    for (uint32_t h = hf; h <= hl; ++h) {
+      const uint32_t bs = s_bstart[h];
+      const uint32_t bn = s_bstart[h + 1] - bs;
+      if (bn == 0) continue;
+      s_dbase[tid] = 0u;
+      __syncthreads();
+      for (uint32_t i = tid; i < bn; i += NT) atomicAdd(&s_dbase[kin[bs + i] & lmask], 1u);
+      __syncthreads();
+      const uint32_t hc = s_dbase[tid];
+      uint32_t t2;
+      const uint32_t dbase = block_excl_n<NW>(hc, scratch, &t2);
+      s_dbase[tid] = dbase;
+      s_run[tid] = 0u;
+      __syncthreads();
+      for (uint32_t c0 = 0; c0 < bn; c0 += CAP) {
+        const int clen = static_cast<int>(min(static_cast<uint32_t>(CAP), bn - c0));
+        const int crr = (clen + NT - 1) / NT;
+        load_range(kin, vin, static_cast<int64_t>(bs) + c0, clen, crr, key, val);
+        lds_counting_pass(key, val, crr, 0, clen, low, s_k, s_v, s_cnt, s_slots, s_dstart,
+                          scratch);
+        for (int i = tid; i < clen; i += NT) {
+          const uint32_t k = s_k[i];
+          const uint32_t d = k & lmask;
+          const uint32_t gp = bs + s_dbase[d] + s_run[d] + (static_cast<uint32_t>(i) - s_dstart[d]);
+          if (gp < static_cast<uint64_t>(n)) {
+            kout[gp] = k;
+            vout[gp] = s_v[i];
+          }
+        }
+        __syncthreads();
+        const uint32_t next = tid + 1 < NT ? s_dstart[tid + 1] : static_cast<uint32_t>(clen);
+        s_run[tid] += next - s_dstart[tid];
+        __syncthreads();
+      }
+    }
+    __threadfence_block();
+    __syncthreads();
+    for (int64_t i = tid; i < len64; i += NT) {
+      const uint32_t k = kout[start + i];
+      if (i == 0 || k != kout[start + i - 1]) ++my_heads;
+    }
+  }
+
+  // run ids: this window's first one from the look-back over earlier windows
+  uint32_t htotal;
+  const uint32_t hex = block_excl_n<NW>(my_heads, scratch, &htotal);
+  if (tid < kWave) {
+    if (tid == 0) st_status(status + tile, (tile == 0 ? kFlagIncl : kFlagAgg) | htotal);
+    uint32_t before = 0;
+    if (tile > 0) before = lookback_wave(status, tile, counters + kCntError);
+    if (tid == 0) {
+      if (tile > 0) st_status(status + tile, kFlagIncl | ((before + htotal) & kValueMask));
+      s_base = before;
+      if (tile == ntiles - 1) {
+        // U <= n always, unless a look-back gave up; keep every index in range regardless
+        const uint32_t U = min(before + htotal, static_cast<uint32_t>(n));
+        counters[kCntUnique] = U;
+        run_start[U] = static_cast<uint32_t>(n);
+      }
+    }
+  }
+  __syncthreads();
+  if (len64 <= CAP) {
+    uint32_t r = s_base + hex;
+    const int len = static_cast<int>(len64);
+    for (int j = 0; j < rr; ++j) {
+      const int i = tid * rr + j;
+      if (i < len && (i == 0 || s_k[i] != s_k[i - 1])) {
+        if (r < static_cast<uint64_t>(n)) {
+          unique_keys[r] = s_k[i];
+          run_start[r] = static_cast<uint32_t>(start + i);
+        }
+        ++r;
+      }
+    }
+  } else {
+    uint32_t r0 = s_base;
+    for (int64_t c0 = 0; c0 < len64; c0 += NT) {
+      const int64_t i = c0 + tid;
+      uint32_t k = 0;
+      bool head = false;
+      if (i < len64) {
+        k = kout[start + i];
+        head = i == 0 || k != kout[start + i - 1];
+      }
+      uint32_t t3;
+      const uint32_t ex = block_excl_n<NW>(head ? 1u : 0u, scratch, &t3);
+      if (head && r0 + ex < static_cast<uint64_t>(n)) {
+        unique_keys[r0 + ex] = k;
+        run_start[r0 + ex] = static_cast<uint32_t>(start + i);
+      }
+      r0 += t3;
+    }
+  }
+}
+
 }  // namespace
 
 int sort_keys_per_thread(int64_t n) { return n <= (int64_t{1} << 20) ? 8 : 16; }
@@ -548,41 +886,84 @@ hipError_t launch_linearize_kernel(const BackwardLaunch& a, hipStream_t stream,
   return hipGetLastError();
 }
 
-hipError_t launch_radix_sort(const BackwardLaunch& a, hipStream_t stream, int* result_buffer,
-                             const KernelTimer* kt) {
+// One look-back pass over keys/values (kin, vin) -> (kout, vout) on the digit
+// (key >> shift) & (2^bits - 1), whose counts are `totals`; `pass` selects the
+// pass's status words and ticket.  With wtable, the pass also records the
+// window ranges of the bucket-local sort.
+hipError_t launch_pass(const BackwardLaunch& a, int pass, int shift, const uint32_t* totals,
+                       const uint32_t* kin, const uint32_t* vin, uint32_t* kout, uint32_t* vout,
+                       uint32_t* wtable, hipStream_t stream, const KernelTimer* kt) {
   const int64_t n = a.num_indices;
   const int kpt = sort_keys_per_thread(n);
   const int64_t ts = sort_tile_keys(n, a.key_bits);
   const int ntiles = static_cast<int>((n + ts - 1) / ts);
+  const int bits = radix_digit_bits(a.key_bits, n);
+  const int slots = radix_slots(bits);
+  uint32_t* status = a.buf.sort_status + static_cast<int64_t>(pass) * ntiles * slots;
+  uint32_t* ticket = ntiles <= kResidentTiles ? nullptr : a.buf.tickets + pass;
+  if (bits > 8)
+    launch_timed(kt, "radix_pass", radix_pass_wide<4, 10>, dim3(ntiles), dim3(1024), 0, stream,
+                 kin, vin, kout, vout, n, shift, bits, totals, status, ticket,
+                 a.buf.counters + kCntError, wtable);
+  else if (kpt == 8)
+    launch_timed(kt, "radix_pass", radix_pass<8, 8>, dim3(ntiles), dim3(kBlock), 0, stream, kin,
+                 vin, kout, vout, n, shift, bits, totals, status, ticket,
+                 a.buf.counters + kCntError, wtable);
+  else
+    launch_timed(kt, "radix_pass", radix_pass<16, 8>, dim3(ntiles), dim3(kBlock), 0, stream, kin,
+                 vin, kout, vout, n, shift, bits, totals, status, ticket,
+                 a.buf.counters + kCntError, wtable);
+  return hipGetLastError();
+}
+
+hipError_t launch_radix_sort(const BackwardLaunch& a, hipStream_t stream, int* result_buffer,
+                             const KernelTimer* kt) {
   const int passes = radix_passes(a.key_bits, a.num_indices);
   const int bits = radix_digit_bits(a.key_bits, a.num_indices);
   const int slots = radix_slots(bits);
   int cur = 0;
   for (int pass = 0; pass < passes; ++pass) {
-    uint32_t* status = a.buf.sort_status + static_cast<int64_t>(pass) * ntiles * slots;
-    const uint32_t* totals = a.buf.digit_hist + pass * slots;
-    uint32_t* ticket = ntiles <= kResidentTiles ? nullptr : a.buf.tickets + pass;
-    if (bits > 8)
-      launch_timed(kt, "radix_pass", radix_pass_wide<4, 10>, dim3(ntiles), dim3(1024), 0,
-                   stream, a.buf.keys[cur], a.buf.vals[cur], a.buf.keys[cur ^ 1],
-                   a.buf.vals[cur ^ 1], n, pass * bits, bits, totals, status, ticket,
-                   a.buf.counters + kCntError);
-    else if (kpt == 8)
-      launch_timed(kt, "radix_pass", radix_pass<8, 8>, dim3(ntiles), dim3(kBlock), 0,
-                   stream, a.buf.keys[cur], a.buf.vals[cur], a.buf.keys[cur ^ 1],
-                   a.buf.vals[cur ^ 1], n, pass * bits, bits, totals, status, ticket,
-                   a.buf.counters + kCntError);
-    else
-      launch_timed(kt, "radix_pass", radix_pass<16, 8>, dim3(ntiles), dim3(kBlock), 0,
-                   stream, a.buf.keys[cur], a.buf.vals[cur], a.buf.keys[cur ^ 1],
-                   a.buf.vals[cur ^ 1], n, pass * bits, bits, totals, status, ticket,
-                   a.buf.counters + kCntError);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e =
+        launch_pass(a, pass, pass * bits, a.buf.digit_hist + pass * slots, a.buf.keys[cur],
+                    a.buf.vals[cur], a.buf.keys[cur ^ 1], a.buf.vals[cur ^ 1], nullptr, stream,
+                    kt);
     if (e != hipSuccess) return e;
     cur ^= 1;
   }
   *result_buffer = cur;
   return hipSuccess;
+}
+
+hipError_t launch_sort_encode(const BackwardLaunch& a, hipStream_t stream, const KernelTimer* kt) {
+  const int64_t n = a.num_indices;
+  if (n <= 0) return hipSuccess;
+  const int passes = radix_passes(a.key_bits, n);
+  const int bits = radix_digit_bits(a.key_bits, n);
+  // two digits, and buckets of the high digit short on average (they are
+  // sorted in LDS; a bucket longer than kBucketCap - kBucketWindow takes the
+  // slower chunked path)
+  const bool bucket = a.bucket_sort && passes == 2 && n <= kWideRadixMaxKeys &&
+                      (n >> (a.key_bits - bits)) <= kBucketMeanMax;
+  if (!bucket) {
+    int sorted = 0;
+    const hipError_t e = launch_radix_sort(a, stream, &sorted, kt);
+    if (e != hipSuccess) return e;
+    return launch_run_length_encode(a, a.buf.keys[sorted], stream, kt);
+  }
+  const uint32_t* htotals = a.buf.digit_hist + radix_slots(bits);  // counts of the high digit
+  // look-back status words of the windows, then their range records
+  const int windows = static_cast<int>((n + kBucketWindow - 1) / kBucketWindow);
+  uint32_t* wstatus = a.buf.rle_status;
+  uint32_t* wtable = a.buf.rle_status + ((windows + 3) & ~3);  // 16-byte records
+  hipError_t e = launch_pass(a, 0, bits, htotals, a.buf.keys[0], a.buf.vals[0], a.buf.keys[1],
+                             a.buf.vals[1], wtable, stream, kt);
+  if (e != hipSuccess) return e;
+  launch_timed(kt, "bucket_sort_rle", bucket_sort_rle, dim3(windows), dim3(kBucketThreads), 0,
+               stream, a.buf.keys[1], a.buf.vals[1], a.buf.keys[0], a.buf.vals[0], n, bits,
+               1 << bits, htotals, wtable, windows, wstatus,
+               windows <= kResidentTiles ? nullptr : a.buf.tickets + kMaxRadixPasses,
+               a.buf.counters, a.buf.unique_keys, a.buf.run_start);
+  return hipGetLastError();
 }
 
 hipError_t launch_run_length_encode(const BackwardLaunch& a, const uint32_t* sorted_keys,

@@ -181,7 +181,8 @@ struct BwdPlan {
   int passes = 1, slots = 256;
   int64_t zero_words = 0;
   size_t o_keys[2], o_vals[2], o_rec, o_zero, o_uniq, o_start, o_longs, o_long_keys, o_items1,
-      o_p1;
+      o_p1, o_truns;
+  bool per_table = false;
   size_t bytes = 0;
 };
 
@@ -231,6 +232,12 @@ bool plan_backward(const tbe_handle* h, int64_t n, bool vec, BwdPlan* p) {
   p->o_long_keys = cv.take(4 * static_cast<size_t>(p->long_ub));
   p->o_items1 = cv.take(8 * static_cast<size_t>(p->items1_ub));
   p->o_p1 = cv.take(4 * static_cast<size_t>(p->pstride) * p->chunks_ub);
+  p->o_truns = cv.take(4 * static_cast<size_t>(h->T + 1));
+  // short runs in lane groups of each table's own width, when some table's
+  // rows are narrower than the widest (metadata staged in LDS)
+  if (h->T <= kSegLdsTables)
+    for (int t = 0; t < h->T; ++t)
+      if (((h->meta_host[t].bwd_gshift >> (vec ? 0 : 8)) & 0xFF) < p->gshift) p->per_table = true;
   p->bytes = cv.off;
   return true;
 }
@@ -264,6 +271,7 @@ void fill_backward(const tbe_handle* h, int32_t B, const void* indices, const vo
   a.vec = vec;
   a.nch = p.nch;
   a.gshift = p.gshift;
+  a.per_table = p.per_table ? 1 : 0;
   a.pstride = p.pstride;
   a.long_threshold = static_cast<int32_t>(std::min<int64_t>(h->long_threshold, 0x7FFFFFFF));
   a.bucket_sort = h->bucket_sort ? 1 : 0;
@@ -293,6 +301,7 @@ void fill_backward(const tbe_handle* h, int32_t B, const void* indices, const vo
   b.long_keys = reinterpret_cast<uint32_t*>(w + p.o_long_keys);
   b.items1 = reinterpret_cast<uint2*>(w + p.o_items1);
   b.partial1 = reinterpret_cast<float*>(w + p.o_p1);
+  b.table_runs = reinterpret_cast<uint32_t*>(w + p.o_truns);
 }
 
 // The grouping (linearize, sort, run-length encoding) of a backward call.
@@ -428,6 +437,9 @@ tbe_status tbe_create(const tbe_config* cfg, void* weights, float* optim_state, 
       m.doff = static_cast<int32_t>(doff);
       const int64_t chunks = (h->dims[t] + fwd_ve - 1) / fwd_ve;
       m.fwd_gshift = ceil_log2(next_pow2(std::min<int64_t>(chunks, kWave)));
+      const int64_t gchunks4 = (h->dims[t] + 3) / 4, gchunks1 = h->dims[t];
+      m.bwd_gshift = ceil_log2(next_pow2(std::min<int64_t>(gchunks4, kWave))) |
+                     (ceil_log2(next_pow2(std::min<int64_t>(gchunks1, kWave))) << 8);
       woff += h->rows[t] * h->dims[t];
       roff += h->rows[t];
       doff += h->dims[t];

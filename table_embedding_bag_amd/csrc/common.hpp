@@ -23,7 +23,9 @@ struct TableMeta {
   int32_t dim;       // D_t
   int32_t doff;      // first output column of the table
   int32_t fwd_gshift;  // log2(lanes that cover one row in the forward)
-  int32_t pad;
+  // log2(lanes that cover one fp32 gradient row in the backward's short-run
+  // kernel): bits 0-7 with 16-byte chunks, bits 8-15 with one value per lane
+  int32_t bwd_gshift;
 };
 static_assert(sizeof(TableMeta) == 32, "TableMeta layout");
 
@@ -259,6 +261,7 @@ struct BackwardBuffers {
   int64_t zero_words;       // size of the zeroed region, in 32-bit words
   uint32_t* unique_keys;    // [N]
   uint32_t* run_start;      // [N + 1]
+  uint32_t* table_runs;     // [T + 1]: first run id of each table (per-table lane groups)
   uint2* items1;            // workgroup items: {first position, medium flag | length}
                             // or {long run, chunk}
   uint4* longs;             // {first position, length, first chunk partial, chunk count}
@@ -302,6 +305,7 @@ struct BackwardLaunch {
   int32_t vec;              // G_Y rows read as 16-byte chunks
   int32_t nch;              // chunk sets per lane in the segment kernels (1, 4 or 16)
   int32_t gshift;           // log2(lanes per gradient row) in the segment kernels
+  int32_t per_table;        // short runs use each table's own lane-group width
   int32_t pstride;          // floats per partial row
   int32_t long_threshold;   // runs at least this long use split accumulation
   int32_t chunk;            // lookups per level-1 partial
@@ -346,6 +350,10 @@ hipError_t launch_segment_reduce_update(const BackwardLaunch& a, const uint32_t*
 // Row loads a forward lane group issues before it accumulates (shared by the
 // kernel and the host planner that sizes sub-waves from the mean bag length).
 constexpr int kFwdUnroll = 4;
+
+// Tables whose metadata the segment kernels stage in LDS; handles with more
+// tables read it from global memory and use one lane-group width for all.
+constexpr int kSegLdsTables = 256;
 
 // Largest embedding dimension handled.
 constexpr int kMaxDim = 1024;

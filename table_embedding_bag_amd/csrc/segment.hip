@@ -204,7 +204,7 @@ __device__ __forceinline__ GroupIds group_ids(const BackwardLaunch& a) {
 
 // Table metadata staged in LDS (handles with at most kLdsTables tables), so
 // that a run's table follows from its row id without a dependent global load.
-constexpr int kLdsTables = 256;
+constexpr int kLdsTables = kSegLdsTables;
 
 __device__ __forceinline__ void stage_meta(const BackwardLaunch& a, TableMeta* s_meta) {
   if (a.T <= kLdsTables)
@@ -284,123 +284,219 @@ __device__ __forceinline__ void gather_short(const BackwardLaunch& a, const Tabl
   }
 }
 
-template <int ST, int VE, int NCH, bool REC>
-__global__ __launch_bounds__(kBlock) void seg_short(BackwardLaunch a, const uint32_t* sorted_vals) {
-  __shared__ TableMeta s_meta[kLdsTables];
-  const GroupIds id = group_ids(a);
-  const int Gs = id.g.Gs, gl = id.g.gl;
-  const int leader = lane_id() & ~(Gs - 1);
-  const bool failed = a.buf.counters[kCntError] != 0u;  // a look-back wait gave up earlier
-  const uint32_t U = a.buf.counters[kCntUnique];
-  if (a.out_num && id.gid == 0 && gl == 0) *a.out_num = failed ? -1 : static_cast<int32_t>(U);
-  if (failed) return;
-  stage_meta(a, s_meta);
-  // The loop runs the same number of times on every lane of a wave (groups
-  // past the last run idle), so the queueing below can use wave-wide scans.
-  const uint32_t wave_first = id.gid - static_cast<uint32_t>(lane_id() >> a.gshift);
-  const uint32_t ng = id.ngroups;
-  uint32_t r = id.gid;
-  for (uint32_t rb = wave_first; rb < U; rb += ng, r += ng) {
-    const bool valid = r < U;
-    int64_t s = 0, e = 0;
-    uint32_t key = 0;
-    if (valid) {
-      s = a.buf.run_start[r];
-      e = a.buf.run_start[r + 1];
-      key = a.buf.unique_keys[r];
+// One run per lane group of Gs lanes (Gs = 2^k <= 64, groups aligned within
+// the wave), called by every lane of the wave together.  Runs longer than Gq
+// lookups are queued as workgroup items; shorter ones are gathered here in
+// batches of Gs lookups (one batch when Gs = Gq).  t is the run's table, or
+// -1 to find it from the row id.
+template <int ST, int VE, int NCH, bool REC, bool PT>
+__device__ __forceinline__ void short_run(const BackwardLaunch& a, const uint32_t* sorted_vals,
+                                          const TableMeta* s_meta, uint32_t r, bool valid,
+                                          int t_known, int Gs, int gl, int leader, int Gq) {
+  int64_t s = 0, e = 0;
+  uint32_t key = 0;
+  if (valid) {
+    s = a.buf.run_start[r];
+    e = a.buf.run_start[r + 1];
+    key = a.buf.unique_keys[r];
+  }
+  const int len = valid ? static_cast<int>(e - s) : 0;
+  if (valid && a.out_unique && gl == 0) {
+    a.out_unique[r] = static_cast<int32_t>(key);
+    a.out_lengths[r] = len;
+  }
+  // Queue runs longer than Gq: a medium run as one workgroup item, a long
+  // run as its 256-lookup chunks.  Queue slots are reserved with one atomic
+  // per counter per wave (a wave-wide scan of the groups' needs), not per
+  // run; the counters sit on separate cache lines.
+  if (__ballot(gl == 0 && len > Gq)) {
+    const bool is_long = len > Gq && len >= a.long_threshold;
+    const bool is_medium = len > Gq && !is_long;
+    const uint32_t n1 = is_long ? static_cast<uint32_t>((len + a.chunk - 1) / a.chunk) : 0u;
+    const bool ld = gl == 0;
+    uint32_t t_long, t_chunks, t_items1;
+    const uint32_t x_long = wave_excl_scan(ld && is_long ? 1u : 0u, &t_long);
+    const uint32_t x_chunks = wave_excl_scan(ld ? n1 : 0u, &t_chunks);
+    const uint32_t x_items1 = wave_excl_scan(ld ? (is_long ? n1 : (is_medium ? 1u : 0u)) : 0u,
+                                             &t_items1);
+    uint32_t base[3] = {0u, 0u, 0u};
+    if (lane_id() == 0) {
+      if (t_long) base[0] = atomicAdd(&a.buf.counters[kCntLong], t_long);
+      if (t_chunks) base[1] = atomicAdd(&a.buf.counters[kCntChunks], t_chunks);
+      if (t_items1) base[2] = atomicAdd(&a.buf.counters[kCntItems1], t_items1);
     }
-    const int len = valid ? static_cast<int>(e - s) : 0;
-    if (valid && a.out_unique && gl == 0) {
-      a.out_unique[r] = static_cast<int32_t>(key);
-      a.out_lengths[r] = len;
-    }
-    // Queue runs longer than Gs: a medium run as one workgroup item, a long
-    // run as its 256-lookup chunks.  Queue slots are reserved with one atomic
-    // per counter per wave (a wave-wide scan of the groups' needs), not per
-    // run; the counters sit on separate cache lines.
-    if (__ballot(gl == 0 && len > Gs)) {
-      const bool is_long = len > Gs && len >= a.long_threshold;
-      const bool is_medium = len > Gs && !is_long;
-      const uint32_t n1 = is_long ? static_cast<uint32_t>((len + a.chunk - 1) / a.chunk) : 0u;
-      const bool ld = gl == 0;
-      uint32_t t_long, t_chunks, t_items1;
-      const uint32_t x_long = wave_excl_scan(ld && is_long ? 1u : 0u, &t_long);
-      const uint32_t x_chunks = wave_excl_scan(ld ? n1 : 0u, &t_chunks);
-      const uint32_t x_items1 = wave_excl_scan(ld ? (is_long ? n1 : (is_medium ? 1u : 0u)) : 0u,
-                                               &t_items1);
-      uint32_t base[3] = {0u, 0u, 0u};
-      if (lane_id() == 0) {
-        if (t_long) base[0] = atomicAdd(&a.buf.counters[kCntLong], t_long);
-        if (t_chunks) base[1] = atomicAdd(&a.buf.counters[kCntChunks], t_chunks);
-        if (t_items1) base[2] = atomicAdd(&a.buf.counters[kCntItems1], t_items1);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) base[q] = __shfl(base[q], 0, kWave);
+    // every lane of a group takes its leader's slots
+    const uint32_t li = __shfl(base[0] + x_long, leader, kWave);
+    const uint32_t b1 = __shfl(base[1] + x_chunks, leader, kWave);
+    const uint32_t it = __shfl(base[2] + x_items1, leader, kWave);
+    // items carry the run's first position and length, so the workgroup
+    // kernels need no run-list lookup
+    if (is_long) {
+      if (ld) {
+        a.buf.longs[li] =
+            make_uint4(static_cast<uint32_t>(s), static_cast<uint32_t>(len), b1, n1);
+        a.buf.long_keys[li] = key;
       }
-#pragma unroll
-      for (int q = 0; q < 3; ++q) base[q] = __shfl(base[q], 0, kWave);
-      // every lane of a group takes its leader's slots
-      const uint32_t li = __shfl(base[0] + x_long, leader, kWave);
-      const uint32_t b1 = __shfl(base[1] + x_chunks, leader, kWave);
-      const uint32_t it = __shfl(base[2] + x_items1, leader, kWave);
-      // items carry the run's first position and length, so the workgroup
-      // kernels need no run-list lookup
-      if (is_long) {
-        if (ld) {
-          a.buf.longs[li] =
-              make_uint4(static_cast<uint32_t>(s), static_cast<uint32_t>(len), b1, n1);
-          a.buf.long_keys[li] = key;
-        }
-        for (uint32_t c = gl; c < n1; c += Gs) a.buf.items1[it + c] = make_uint2(li, c);
-      } else if (is_medium && ld) {
-        a.buf.items1[it] =
-            make_uint2(static_cast<uint32_t>(s), kMediumItem | static_cast<uint32_t>(len));
-      }
-    }
-    if (!valid || len > Gs) continue;
-    uint32_t my_bag = 0;
-    float my_coef = 0.0f;
-    if (gl < len) lookup_of<REC>(a, sorted_vals[s + gl], &my_bag, &my_coef);
-    const int t = table_of_key(a, s_meta, key);
-    const TableMeta m = meta_of(a, s_meta, t);
-    const int64_t tb = static_cast<int64_t>(t) * a.B;
-    const int64_t row0 = m.woff + static_cast<int64_t>(key - static_cast<uint32_t>(m.roff)) * m.dim;
-    const int C = m.dim / VE;
-    float w[NCH][VE];
-#pragma unroll
-    for (int c = 0; c < NCH; ++c)
-      if (c * Gs + gl < C) load_widen<ST, VE>(a.weights, row0 + (c * Gs + gl) * VE, w[c]);
-    const float m_old = a.adagrad ? a.state[key] : 0.0f;
-    float acc[NCH][VE];
-#pragma unroll
-    for (int c = 0; c < NCH; ++c)
-#pragma unroll
-      for (int q = 0; q < VE; ++q) acc[c][q] = 0.0f;
-    if (len <= 2)
-      gather_short<2, VE, NCH, REC>(a, m, tb, leader, gl, Gs, len, my_bag, my_coef, acc);
-    else if (len <= 4)
-      gather_short<4, VE, NCH, REC>(a, m, tb, leader, gl, Gs, len, my_bag, my_coef, acc);
-    else
-      gather_short<short_unroll<VE, NCH>(), VE, NCH, REC>(a, m, tb, leader, gl, Gs, len, my_bag,
-                                                           my_coef, acc);
-    float step = a.lr;
-    if (a.adagrad) {
-      float ss = 0.0f;
-#pragma unroll
-      for (int c = 0; c < NCH; ++c)
-#pragma unroll
-        for (int q = 0; q < VE; ++q) ss = fmaf(acc[c][q], acc[c][q], ss);
-      for (int o = Gs >> 1; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, kWave);
-      const float mnew = m_old + ss / static_cast<float>(m.dim);
-      if (gl == 0) a.state[key] = mnew;
-      step = a.lr / (sqrtf(mnew) + a.eps);
-    }
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      if (c * Gs + gl < C) {
-#pragma unroll
-        for (int q = 0; q < VE; ++q) w[c][q] = fmaf(-step, acc[c][q], w[c][q]);
-        narrow_store<ST, VE>(a.weights, row0 + (c * Gs + gl) * VE, w[c]);
-      }
+      for (uint32_t c = gl; c < n1; c += Gs) a.buf.items1[it + c] = make_uint2(li, c);
+    } else if (is_medium && ld) {
+      a.buf.items1[it] =
+          make_uint2(static_cast<uint32_t>(s), kMediumItem | static_cast<uint32_t>(len));
     }
   }
+  if (!valid || len > Gq) return;
+  uint32_t my_bag = 0;
+  float my_coef = 0.0f;
+  if (gl < len) lookup_of<REC>(a, sorted_vals[s + gl], &my_bag, &my_coef);
+  const int t = t_known >= 0 ? t_known : table_of_key(a, s_meta, key);
+  const TableMeta m = meta_of(a, s_meta, t);
+  const int64_t tb = static_cast<int64_t>(t) * a.B;
+  const int64_t row0 = m.woff + static_cast<int64_t>(key - static_cast<uint32_t>(m.roff)) * m.dim;
+  const int C = m.dim / VE;
+  float w[NCH][VE];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+    if (c * Gs + gl < C) load_widen<ST, VE>(a.weights, row0 + (c * Gs + gl) * VE, w[c]);
+  const float m_old = a.adagrad ? a.state[key] : 0.0f;
+  float acc[NCH][VE];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int q = 0; q < VE; ++q) acc[c][q] = 0.0f;
+  for (int b0 = 0;;) {
+    const int blen = PT ? min(Gs, len - b0) : len;
+    if (blen <= 2)
+      gather_short<2, VE, NCH, REC>(a, m, tb, leader, gl, Gs, blen, my_bag, my_coef, acc);
+    else if (blen <= 4)
+      gather_short<4, VE, NCH, REC>(a, m, tb, leader, gl, Gs, blen, my_bag, my_coef, acc);
+    else
+      gather_short<short_unroll<VE, NCH>(), VE, NCH, REC>(a, m, tb, leader, gl, Gs, blen,
+                                                           my_bag, my_coef, acc);
+    if constexpr (!PT) break;  // Gs = Gq: one batch
+    b0 += Gs;
+    if (b0 >= len) break;
+    my_bag = 0;
+    my_coef = 0.0f;
+    if (gl < len - b0) lookup_of<REC>(a, sorted_vals[s + b0 + gl], &my_bag, &my_coef);
+  }
+  float step = a.lr;
+  if (a.adagrad) {
+    float ss = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int q = 0; q < VE; ++q) ss = fmaf(acc[c][q], acc[c][q], ss);
+    for (int o = Gs >> 1; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, kWave);
+    const float mnew = m_old + ss / static_cast<float>(m.dim);
+    if (gl == 0) a.state[key] = mnew;
+    step = a.lr / (sqrtf(mnew) + a.eps);
+  }
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    if (c * Gs + gl < C) {
+#pragma unroll
+      for (int q = 0; q < VE; ++q) w[c][q] = fmaf(-step, acc[c][q], w[c][q]);
+      narrow_store<ST, VE>(a.weights, row0 + (c * Gs + gl) * VE, w[c]);
+    }
+  }
+}
+
+// log2 of the lane-group width of table m's gradient rows.
+template <int VE>
+__device__ __forceinline__ int table_gshift(const TableMeta& m) {
+  return (m.bwd_gshift >> (VE == 4 ? 0 : 8)) & 0xFF;
+}
+
+// Short runs.  Uniform mode: one lane group of Gs = 2^gshift lanes per run
+// (the widest table's row), grid-stride over runs.  Per-table mode (tables of
+// different widths, metadata in LDS): a wave takes a task of 64 / Gs_t
+// consecutive runs of one table t in lane groups of that table's own width,
+// so narrow tables fill the wave; tasks are numbered table after table from
+// the tables' first run ids (table_run_starts).  Either way the loop runs the
+// same number of times on every lane of a wave (groups past the last run
+// idle), so the queueing in short_run can use wave-wide scans.
+template <int ST, int VE, int NCH, bool REC, bool PT>
+__global__ __launch_bounds__(kBlock) void seg_short(BackwardLaunch a, const uint32_t* sorted_vals) {
+  __shared__ TableMeta s_meta[kLdsTables];
+  const bool failed = a.buf.counters[kCntError] != 0u;  // a look-back wait gave up earlier
+  const uint32_t U = a.buf.counters[kCntUnique];
+  if (a.out_num && blockIdx.x == 0 && threadIdx.x == 0) *a.out_num = failed ? -1 : static_cast<int32_t>(U);
+  if (failed) return;
+  stage_meta(a, s_meta);
+  const int Gq = 1 << a.gshift;
+  const int lane = lane_id();
+  if constexpr (!PT) {
+    const GroupIds id = group_ids(a);
+    const int leader = lane & ~(Gq - 1);
+    const uint32_t wave_first = id.gid - static_cast<uint32_t>(lane >> a.gshift);
+    const uint32_t ng = id.ngroups;
+    uint32_t r = id.gid;
+    for (uint32_t rb = wave_first; rb < U; rb += ng, r += ng)
+      short_run<ST, VE, NCH, REC, false>(a, sorted_vals, s_meta, r, r < U, -1, Gq, id.g.gl,
+                                         leader, Gq);
+    return;
+  }
+  __shared__ uint32_t s_task[kLdsTables + 1];    // tasks before table t
+  __shared__ uint32_t s_ustart[kLdsTables + 1];  // first run of table t
+  __shared__ uint32_t s_scr[kWavesPerBlock];
+  const int tid = threadIdx.x;
+  uint32_t my_tasks = 0;
+  if (tid < a.T) {
+    const uint32_t u0 = a.buf.table_runs[tid], u1 = a.buf.table_runs[tid + 1];
+    s_ustart[tid] = u0;
+    if (tid == a.T - 1) s_ustart[a.T] = u1;
+    const int gsh = table_gshift<VE>(s_meta[tid]);
+    my_tasks = (u1 - u0 + (kWave >> gsh) - 1) >> (6 - gsh);
+  }
+  uint32_t ntasks;
+  const uint32_t before = block_exclusive_sum(my_tasks, s_scr, &ntasks);
+  if (tid < a.T) s_task[tid] = before;
+  if (tid == 0) s_task[a.T] = ntasks;
+  __syncthreads();
+  const uint32_t nwaves = gridDim.x * kWavesPerBlock;
+  for (uint32_t k = blockIdx.x * kWavesPerBlock + (tid >> 6); k < ntasks; k += nwaves) {
+    int lo = 0, hi = a.T;  // the table of task k: s_task[lo] <= k < s_task[lo + 1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_task[mid] <= k) lo = mid; else hi = mid;
+    }
+    const int gsh = table_gshift<VE>(s_meta[lo]);
+    const int Gs = 1 << gsh;
+    const uint32_t r = s_ustart[lo] + ((k - s_task[lo]) << (6 - gsh)) + (lane >> gsh);
+    short_run<ST, VE, NCH, REC, true>(a, sorted_vals, s_meta, r, r < s_ustart[lo + 1], lo, Gs,
+                                      lane & (Gs - 1), lane & ~(Gs - 1), Gq);
+  }
+}
+
+// First run id of every table: the lower bound of the table's first row id in
+// the sorted unique ids, by a 256-way search (three rounds cover 2^24 runs).
+// One workgroup per table; workgroup T writes U.
+__global__ __launch_bounds__(kBlock) void table_run_starts(BackwardLaunch a) {
+  const int t = blockIdx.x;
+  const uint32_t U = a.buf.counters[kCntUnique];
+  if (t == a.T) {
+    if (threadIdx.x == 0) a.buf.table_runs[t] = U;
+    return;
+  }
+  const uint32_t target = static_cast<uint32_t>(a.meta[t].roff);
+  uint32_t lo = 0, hi = U;  // the answer lies in [lo, hi]
+  while (lo < hi) {
+    const uint32_t span = hi - lo;
+    const uint32_t step = (span + kBlock - 1) / kBlock;
+    const uint32_t p = lo + threadIdx.x * step;
+    const bool below = p < hi && a.buf.unique_keys[p] < target;
+    const uint32_t c = static_cast<uint32_t>(__syncthreads_count(below));
+    if (step == 1 || c == 0) {
+      lo += c * step;  // step 1: exact; c = 0: unique_keys[lo] >= target
+      break;
+    }
+    // unique_keys[lo + (c-1)*step] < target <= unique_keys[lo + c*step] (or hi)
+    const uint32_t nlo = lo + (c - 1) * step + 1;
+    hi = min(hi, lo + c * step);
+    lo = nlo;
+  }
+  if (threadIdx.x == 0) a.buf.table_runs[t] = min(lo, U);
 }
 
 // Sum of a double over the 256 threads of a block (every thread gets it).
@@ -636,8 +732,14 @@ hipError_t run_segments(const BackwardLaunch& a, const uint32_t* keys, const uin
                         hipStream_t s, const KernelTimer* kt) {
   const int64_t n = a.num_indices;
   const SegmentBounds ub = segment_bounds(n, a.long_threshold, a.chunk, a.gshift);
-  launch_timed(kt, "seg_short", seg_short<ST, VE, NCH, REC>, dim3(blocks_for(n, a.gshift)),
-               dim3(kBlock), 0, s, a, sorted_vals);
+  if (a.per_table) {
+    launch_timed(kt, "table_run_starts", table_run_starts, dim3(a.T + 1), dim3(kBlock), 0, s, a);
+    launch_timed(kt, "seg_short", seg_short<ST, VE, NCH, REC, true>,
+                 dim3(blocks_for(n, a.gshift)), dim3(kBlock), 0, s, a, sorted_vals);
+  } else {
+    launch_timed(kt, "seg_short", seg_short<ST, VE, NCH, REC, false>,
+                 dim3(blocks_for(n, a.gshift)), dim3(kBlock), 0, s, a, sorted_vals);
+  }
   const int64_t wg = ub.items1 < kMaxSegBlocks ? (ub.items1 > 0 ? ub.items1 : 1) : kMaxSegBlocks;
   launch_timed(kt, "seg_wg", seg_wg<ST, VE, NCH, REC>, dim3(wg), dim3(kBlock), 0, s, a, keys,
                sorted_vals);

@@ -524,10 +524,6 @@ __global__ __launch_bounds__(kBlock) void seg_wg(BackwardLaunch a, const uint32_
   __shared__ double s_scratch[kWavesPerBlock];
 
   const int tid = threadIdx.x;
-  const int Gs = 1 << a.gshift;
-  const int ngroups = kBlock >> a.gshift;
-  const int g = tid >> a.gshift, gl = tid & (Gs - 1);
-  const int row_elems = Gs * NV;               // elements per group row in s_red (>= D)
   const uint32_t n = a.buf.counters[kCntItems1];
 
   for (uint32_t item = blockIdx.x; item < n; item += gridDim.x) {
@@ -547,6 +543,13 @@ __global__ __launch_bounds__(kBlock) void seg_wg(BackwardLaunch a, const uint32_
     const int t = table_of_run<REC>(a, sorted_vals, s);
     const TableMeta m = a.meta[t];
     const int64_t tb = static_cast<int64_t>(t) * a.B;
+    // lane groups of the table's own width when tables differ in width, so
+    // narrow rows keep more lookups in flight
+    const int gsh = a.per_table ? table_gshift<VE>(m) : a.gshift;
+    const int Gs = 1 << gsh;
+    const int ngroups = kBlock >> gsh;
+    const int g = tid >> gsh, gl = tid & (Gs - 1);
+    const int row_elems = Gs * NV;             // elements per group row in s_red (>= D)
     Acc<VE, NCH> acc;
     acc.zero();
     for (int64_t base = s; base < e; base += kBlock) {

@@ -180,8 +180,8 @@ struct BwdPlan {
   bool vec = false;
   int passes = 1, slots = 256;
   int64_t zero_words = 0;
-  size_t o_keys[2], o_vals[2], o_rec, o_zero, o_uniq, o_start, o_longs, o_long_keys, o_items1,
-      o_p1, o_truns;
+  size_t o_keys[2], o_vals[2], o_rec, o_zero, o_uniq, o_start, o_first, o_longs, o_long_keys,
+      o_items1, o_p1, o_truns;
   bool per_table = false;
   size_t bytes = 0;
 };
@@ -228,6 +228,7 @@ bool plan_backward(const tbe_handle* h, int64_t n, bool vec, BwdPlan* p) {
   p->o_zero = cv.take(4 * static_cast<size_t>(p->zero_words));
   p->o_uniq = cv.take(4 * static_cast<size_t>(n));
   p->o_start = cv.take(4 * static_cast<size_t>(n + 1));
+  p->o_first = cv.take(4 * static_cast<size_t>(n));
   p->o_longs = cv.take(16 * static_cast<size_t>(p->long_ub));
   p->o_long_keys = cv.take(4 * static_cast<size_t>(p->long_ub));
   p->o_items1 = cv.take(8 * static_cast<size_t>(p->items1_ub));
@@ -297,6 +298,7 @@ void fill_backward(const tbe_handle* h, int32_t B, const void* indices, const vo
   b.zero_words = p.zero_words;
   b.unique_keys = reinterpret_cast<uint32_t*>(w + p.o_uniq);
   b.run_start = reinterpret_cast<uint32_t*>(w + p.o_start);
+  b.run_first = reinterpret_cast<uint32_t*>(w + p.o_first);
   b.longs = reinterpret_cast<uint4*>(w + p.o_longs);
   b.long_keys = reinterpret_cast<uint32_t*>(w + p.o_long_keys);
   b.items1 = reinterpret_cast<uint2*>(w + p.o_items1);

@@ -261,6 +261,7 @@ struct BackwardBuffers {
   int64_t zero_words;       // size of the zeroed region, in 32-bit words
   uint32_t* unique_keys;    // [N]
   uint32_t* run_start;      // [N + 1]
+  uint32_t* run_first;      // [N]: sorted value of each run's first lookup
   uint32_t* table_runs;     // [T + 1]: first run id of each table (per-table lane groups)
   uint2* items1;            // workgroup items: {first position, medium flag | length}
                             // or {long run, chunk}
@@ -336,7 +337,8 @@ hipError_t launch_forward_linearize(const ForwardLaunch& f, const BackwardLaunch
 hipError_t launch_radix_sort(const BackwardLaunch& a, hipStream_t stream, int* result_buffer,
                              const KernelTimer* kt);
 hipError_t launch_run_length_encode(const BackwardLaunch& a, const uint32_t* sorted_keys,
-                                    hipStream_t stream, const KernelTimer* kt);
+                                    const uint32_t* sorted_vals, hipStream_t stream,
+                                    const KernelTimer* kt);
 // Sort and run-length encoding of the linearized batch in buf.keys[0] /
 // buf.vals[0]: for ids of two radix digits (and a.bucket_sort), a pass on the
 // high digit and the bucket-local sort with its run-length encoding; else the

@@ -465,10 +465,11 @@ __device__ uint32_t lookback_wave(uint32_t* status, int tile, uint32_t* err) {
 // Run heads of a 4096-key tile (staged in LDS with the key before it), 1024
 // threads per tile; each thread owns 4 consecutive positions so run ids
 // follow position order.
-__global__ __launch_bounds__(1024) void rle_kernel(const uint32_t* __restrict__ keys, int64_t n,
+__global__ __launch_bounds__(1024) void rle_kernel(const uint32_t* __restrict__ keys,
+                                                     const uint32_t* __restrict__ vals, int64_t n,
                                                      int ntiles, uint32_t* status, uint32_t* ticket,
                                                      uint32_t* counters, uint32_t* unique_keys,
-                                                     uint32_t* run_start) {
+                                                     uint32_t* run_start, uint32_t* run_first) {
   constexpr int NT = 1024;
   constexpr int PER = kRleTile / NT;
   __shared__ uint32_t s_k[kRleTile + 1];
@@ -518,6 +519,7 @@ __global__ __launch_bounds__(1024) void rle_kernel(const uint32_t* __restrict__ 
       if (r < static_cast<uint64_t>(n)) {
         unique_keys[r] = s_k[i + 1];
         run_start[r] = static_cast<uint32_t>(p);
+        run_first[r] = vals[p];
       }
       ++r;
     }
@@ -632,7 +634,7 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
     const uint32_t* __restrict__ kin, const uint32_t* __restrict__ vin, uint32_t* kout,
     uint32_t* vout, int64_t n, int lbits, int nbuckets, const uint32_t* __restrict__ htotals,
     const uint32_t* __restrict__ wtable, int ntiles, uint32_t* status, uint32_t* ticket,
-    uint32_t* counters, uint32_t* unique_keys, uint32_t* run_start) {
+    uint32_t* counters, uint32_t* unique_keys, uint32_t* run_start, uint32_t* run_first) {
   constexpr int NT = kBucketThreads, NW = kBucketWaves, CAP = kBucketCap;
   __shared__ uint32_t s_k[CAP];
   __shared__ uint32_t s_v[CAP];
@@ -813,6 +815,7 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
         if (r < static_cast<uint64_t>(n)) {
           unique_keys[r] = s_k[i];
           run_start[r] = static_cast<uint32_t>(start + i);
+          run_first[r] = s_v[i];
         }
         ++r;
       }
@@ -832,6 +835,7 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
       if (head && r0 + ex < static_cast<uint64_t>(n)) {
         unique_keys[r0 + ex] = k;
         run_start[r0 + ex] = static_cast<uint32_t>(start + i);
+        run_first[r0 + ex] = vout[start + i];
       }
       r0 += t3;
     }
@@ -948,7 +952,7 @@ hipError_t launch_sort_encode(const BackwardLaunch& a, hipStream_t stream, const
     int sorted = 0;
     const hipError_t e = launch_radix_sort(a, stream, &sorted, kt);
     if (e != hipSuccess) return e;
-    return launch_run_length_encode(a, a.buf.keys[sorted], stream, kt);
+    return launch_run_length_encode(a, a.buf.keys[sorted], a.buf.vals[sorted], stream, kt);
   }
   const uint32_t* htotals = a.buf.digit_hist + radix_slots(bits);  // counts of the high digit
   // look-back status words of the windows, then their range records
@@ -962,19 +966,19 @@ hipError_t launch_sort_encode(const BackwardLaunch& a, hipStream_t stream, const
                stream, a.buf.keys[1], a.buf.vals[1], a.buf.keys[0], a.buf.vals[0], n, bits,
                1 << bits, htotals, wtable, windows, wstatus,
                windows <= kResidentTiles ? nullptr : a.buf.tickets + kMaxRadixPasses,
-               a.buf.counters, a.buf.unique_keys, a.buf.run_start);
+               a.buf.counters, a.buf.unique_keys, a.buf.run_start, a.buf.run_first);
   return hipGetLastError();
 }
 
 hipError_t launch_run_length_encode(const BackwardLaunch& a, const uint32_t* sorted_keys,
-                                    hipStream_t stream, const KernelTimer* kt) {
+                                    const uint32_t* sorted_vals, hipStream_t stream,
+                                    const KernelTimer* kt) {
   const int64_t n = a.num_indices;
   const int ntiles = static_cast<int>((n + kRleTile - 1) / kRleTile);
-  launch_timed(kt, "rle_kernel", rle_kernel, dim3(ntiles), dim3(1024), 0, stream, sorted_keys, n, ntiles,
-                     a.buf.rle_status,
-                     ntiles <= kResidentTiles ? nullptr : a.buf.tickets + kMaxRadixPasses,
-                     a.buf.counters,
-                     a.buf.unique_keys, a.buf.run_start);
+  launch_timed(kt, "rle_kernel", rle_kernel, dim3(ntiles), dim3(1024), 0, stream, sorted_keys,
+               sorted_vals, n, ntiles, a.buf.rle_status,
+               ntiles <= kResidentTiles ? nullptr : a.buf.tickets + kMaxRadixPasses,
+               a.buf.counters, a.buf.unique_keys, a.buf.run_start, a.buf.run_first);
   return hipGetLastError();
 }
 

@@ -142,21 +142,32 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 template <int RB>
 __device__ __forceinline__ uint64_t match_digit(uint64_t* s_slots, uint32_t d, bool ok) {
+  // Lanes holding the first active lane's digit are matched by one ballot: a
+  // hot row fills whole rounds with one digit, and atomics of all of its
+  // lanes on one slot would be serialised.  The other lanes use the slots.
+  const uint64_t act = __ballot(ok);
+  if (act == 0) return 0;
+  const uint32_t d0 = static_cast<uint32_t>(
+      __builtin_amdgcn_readlane(static_cast<int>(d), __builtin_ctzll(act)));
+  const bool same = ok && d == d0;
+  const uint64_t m0 = __ballot(same);
+  if (m0 == act) return same ? m0 : 0u;
+  const bool rest = ok && !same;
   uint64_t* slot = s_slots + (d & 255u);
-  if (ok)
+  if (rest)
     __hip_atomic_fetch_or(slot, uint64_t{1} << lane_id(), __ATOMIC_RELAXED,
                           __HIP_MEMORY_SCOPE_WAVEFRONT);
   wave_lds_sync();
-  uint64_t peers = ok ? __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT) : 0u;
+  uint64_t peers = rest ? __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT) : 0u;
   wave_lds_sync();
-  if (ok) __hip_atomic_store(slot, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+  if (rest) __hip_atomic_store(slot, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
 #pragma unroll
   for (int bit = 8; bit < RB; ++bit) {
     const bool set = (d >> bit) & 1u;
     const uint64_t bal = __ballot(set);
     peers &= set ? bal : ~bal;
   }
-  return peers;
+  return same ? m0 : peers;
 }
 
 // Window range records of the bucket-local sort: bucket d of the high digit

@@ -105,3 +105,72 @@ def test_hot_buckets_parity():
 def test_17bit_parity_grouped():
     _, spec, _ = CASES[3]
     parity(spec, seed=9, steps=2, grouped=True, bag_sample=2000, row_sample=3000)
+
+
+def _per_table_batches():
+    """Tables of different widths (short runs in per-table lane groups) where some tables get
+    no lookup at all: the first and last table, one in the middle; one table whose lookups
+    are a single row (one long run); and a batch whose runs all sit in one table."""
+    rng = np.random.default_rng(41)
+    T, B = 5, 96
+    # table 0: empty; table 1: random; table 2: empty; table 3: one row 700 times; table 4: empty
+    bags = [[[] for _ in range(B)] for _ in range(T)]
+    for b in range(B):
+        bags[1][b] = list(rng.integers(0, 300, rng.integers(0, 12)))
+    hot = np.array_split(np.full(700, 17), B)
+    for b in range(B):
+        bags[3][b] = list(hot[b])
+    only = [[[] for _ in range(B)] for _ in range(T)]
+    for b in range(B):
+        only[2][b] = list(rng.integers(0, 800, rng.integers(1, 9)))
+    return _hand_batch(T, B, bags), _hand_batch(T, B, only)
+
+
+@pytest.mark.parametrize("opt", ["sgd", "rowwise_adagrad"])
+def test_per_table_groups_with_empty_tables(opt):
+    spec = workloads.custom([500, 300, 800, 200, 64], [32, 256, 64, 128, 16], "bf16", B=96,
+                            optimizer=opt, key=240)
+    b1, b2 = _per_table_batches()
+    parity(spec, seed=10, steps=2, batches=[b1, b2])
+
+
+def test_sort_option_is_checked():
+    spec = workloads.config(1)
+    pb = make_problem(spec, seed=0)
+    with pytest.raises(tbe.TBEError):
+        pb.op.set_option(tbe.OPTION_SORT, 2)
+    pb.op.set_option(tbe.OPTION_SORT, 1)
+    pb.op.set_option(tbe.OPTION_SORT, 0)
+    pb.op.close()
+
+
+def _uniform_batch(E, B, n, seed):
+    """One table, n uniform ids spread over B bags (ragged)."""
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(0, E, n)
+    cuts = np.sort(rng.integers(0, n + 1, B - 1))
+    off = np.concatenate([[0], cuts, [n]]).astype(np.int64)
+    return workloads.Batch(ids.astype(np.int64), off, None)
+
+
+@pytest.mark.parametrize("E,n", [(1 << 20, 1 << 20), (1 << 20, (1 << 20) + 1),
+                                 ((1 << 20) + 1, 1 << 19)],
+                         ids=["20bit-2^20-lookups", "20bit-2^20+1-lookups", "21bit-ids"])
+def test_path_boundaries(E, n):
+    """Both sides of the bucket path's limits: 2^20 lookups (bucket path) and one more (LSD
+    passes and the RLE kernel); ids of 20 bits (two digits) and of 21 bits (three LSD
+    passes).  Runs bit-exact and sampled updates against the reference."""
+    spec = workloads.custom([E], [16], "f32", B=4096, optimizer="rowwise_adagrad", key=250)
+    batch = _uniform_batch(E, 4096, n, 51)
+    pb = make_problem(spec, seed=11, batch=batch)
+    pb.op.set_option(tbe.OPTION_PROFILE, 1)
+    G = workloads.grad_output(spec, seed=11, step=0, device="cuda")
+    runs = gpu_runs(pb, n)
+    pb.op.backward_update(spec.B, pb.idx, pb.off, None, G, spec.lr, spec.eps, runs)
+    torch.cuda.synchronize()
+    used = _stages(pb.op)
+    bucket = E == (1 << 20) and n <= (1 << 20)
+    assert ("bucket_sort_rle" in used) == bucket, used
+    assert ("rle_kernel" in used) == (not bucket), used
+    pb.op.close()
+    parity(spec, seed=12, steps=1, batches=[batch], bag_sample=500, row_sample=2000)

@@ -5,8 +5,9 @@ Adagrad / SGD update per touched row), through the library's C ABI.
 
 A step is one forward and one backward update over one batch of the workload:
 tbe_forward_group (the pooled lookup, with the backward's linearize step in the
-same launch, then the sort and run-length encoding of the batch) +
-tbe_backward_update_grouped (segment reduce and update).  --plain times
+same launch, then the sort and run-length encoding of the batch, which also
+queues the longer runs) + tbe_backward_update_grouped (segment reduce and
+update: short runs and queued items in one launch, then the long-run finish).  --plain times
 tbe_forward + tbe_backward_update instead (same results, bit for bit).  Four
 seeded batches (and
 upstream gradients) are generated up front, resident in HBM, and used in
@@ -110,7 +111,13 @@ def algorithmic_bytes(spec, batch, gather_tables=None, long_threshold=256, chunk
       seg_short           runs a lane group takes alone (at most Gs lookups)
       seg_wg              longer runs below the long-run threshold, and the lookups of long
                           runs (+ one 4*D partial write per 256-lookup chunk)
+      seg_fused           seg_short and seg_wg in one launch (batches whose run-length
+                          encoding queued the longer runs)
       seg_finalize        per long run: its chunk partials read, the row terms
+    grouping front: linearize, radix passes (key+value read and scatter 16 per lookup),
+    bucket_sort_rle (key+value read and final write 16 per lookup; unique id, start and
+    first value 12 per run), rle_kernel (keys 4 per lookup; per run 12 written, first
+    value read 4)
     """
     import numpy as np
     s = {"f32": 4, "f16": 2, "bf16": 2}[spec.dtype]
@@ -142,7 +149,8 @@ def algorithmic_bytes(spec, batch, gather_tables=None, long_threshold=256, chunk
     # writes 8, record 8), per radix pass the key+value read and scatter 16 per lookup,
     # run-length encoding keys read 4 + unique id/start writes 8 per run
     front = {"linearize_kernel": float(N * (8 + 8 + rec) + 8 * nbags),
-             "radix_pass": float(16 * N), "rle_kernel": float(4 * N + 8 * U)}
+             "radix_pass": float(16 * N), "rle_kernel": float(4 * N + 16 * U),
+             "bucket_sort_rle": float(16 * N + 12 * U)}
     # count-matrix forward (tables that qualify): ids 8 + per bag offset 8 + output 4*D, one
     # read of each table; the dense product does 2*B*E_t*D_t flops per table.  The W^T
     # staging kernel reads each table and writes its transposed copy.
@@ -156,6 +164,7 @@ def algorithmic_bytes(spec, batch, gather_tables=None, long_threshold=256, chunk
     return {"fwd_gather_pool": fwd, "fwd_linearize": fwd + front["linearize_kernel"],
             "fwd_histogram": hist_bytes, "hist_transpose": hist_t,
             "fwd_histogram_flops": hist_flops, "seg_short": seg_short, "seg_wg": seg_wg,
+            "seg_fused": seg_short + seg_wg,
             "seg_finalize": seg_final, **front}, {"N": int(lens.sum()), "U": int(cnt.size),
                                          "long_run_share": float(cnt[long_].sum() / max(1, cnt.sum())),
                                          "max_run": int(cnt.max()) if cnt.size else 0}
@@ -326,7 +335,7 @@ def main():
                           "alg_GBps": round(b / (avg_us[k] * 1e-6) / 1e9, 1),
                           "pct_of_peak": round(100 * b / (avg_us[k] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 1)}
     # the whole segment reduce + update (all of its kernels, one launch each per step)
-    seg_names = [k for k in ("seg_short", "seg_wg", "seg_finalize") if k in avg_us]
+    seg_names = [k for k in ("seg_short", "seg_wg", "seg_fused", "seg_finalize") if k in avg_us]
     if seg_names:
         sb, su = sum(alg_bytes[k] for k in seg_names), sum(avg_us[k] for k in seg_names)
         kernels["segment_reduce_update"] = {

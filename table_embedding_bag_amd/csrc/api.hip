@@ -44,6 +44,9 @@ struct tbe_handle {
   int64_t wt_elems = 0;
   int64_t long_threshold = 256;
   bool bucket_sort = true;  // TBE_OPTION_SORT
+  // whether the last tbe_forward_group's run-length encoding queued the longer
+  // runs (its tbe_backward_update_grouped must not queue them again)
+  bool grouped_queued = false;
   // profiling: pairs of events handed to timed kernel launches (start and end
   // of that kernel), kept until tbe_stage_times reads them
   bool profile = false;
@@ -177,6 +180,8 @@ struct BwdPlan {
   int64_t long_ub = 0, chunks_ub = 0, items1_ub = 0;
   int32_t pstride = 0;
   int32_t nch = 1, gshift = 0;
+  int32_t short_max = 1;  // longest short run: the lane group with 16-byte chunks if every
+                          // dim allows them (the same for a forward_group and its backward)
   bool vec = false;
   int passes = 1, slots = 256;
   int64_t zero_words = 0;
@@ -213,7 +218,12 @@ bool plan_backward(const tbe_handle* h, int64_t n, bool vec, BwdPlan* p) {
   p->rle_tiles = 5 * static_cast<int>((n + kBucketWindow - 1) / kBucketWindow) + 4;
   p->passes = radix_passes(h->key_bits, n);
   p->slots = radix_slots(radix_digit_bits(h->key_bits, n));
-  const SegmentBounds ub = segment_bounds(n, h->long_threshold, kChunk, p->gshift);
+  {
+    const int ve_h = h->bwd_vec ? 4 : 1;
+    const int64_t ch = (h->dmax + ve_h - 1) / ve_h;
+    p->short_max = 1 << (ch <= kWave ? ceil_log2(next_pow2(ch)) : 6);
+  }
+  const SegmentBounds ub = segment_bounds(n, h->long_threshold, kChunk, p->short_max);
   p->long_ub = ub.longs;
   p->chunks_ub = ub.chunks;
   p->items1_ub = ub.items1;
@@ -272,6 +282,7 @@ void fill_backward(const tbe_handle* h, int32_t B, const void* indices, const vo
   a.vec = vec;
   a.nch = p.nch;
   a.gshift = p.gshift;
+  a.short_max = p.short_max;
   a.per_table = p.per_table ? 1 : 0;
   a.pstride = p.pstride;
   a.long_threshold = static_cast<int32_t>(std::min<int64_t>(h->long_threshold, 0x7FFFFFFF));
@@ -348,6 +359,7 @@ tbe_status backward_impl(tbe_handle* h, int32_t B, const void* indices, const vo
     BackwardLaunch a;
     fill_backward(h, B, indices, offsets, index_dtype, n, psw, grad_output, lr, eps, workspace,
                   runs, vec, p, &a);
+    a.front_queued = (with_front ? uses_bucket_sort(a) : h->grouped_queued) ? 1 : 0;
     if (with_front) {
       const hipError_t e = launch_front(a, s, kt);
       if (e != hipSuccess) return TBE_ERR_HIP;
@@ -770,6 +782,7 @@ tbe_status tbe_forward_group(tbe_handle* h, int32_t B, const void* indices, cons
                       fused ? &a : nullptr);
     if (st != TBE_OK) return st;
     if (!fused && launch_linearize_kernel(a, s, kt) != hipSuccess) return TBE_ERR_HIP;
+    h->grouped_queued = uses_bucket_sort(a);
     return from_hip(launch_sort_encode(a, s, kt));
   } catch (...) {
     return TBE_ERR_OUT_OF_MEMORY;

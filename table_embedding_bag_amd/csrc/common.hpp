@@ -276,6 +276,22 @@ struct BackwardBuffers {
 // gives up (results then invalid).
 enum { kCntUnique = 0, kCntLong = 32, kCntItems1 = 64, kCntChunks = 96, kCntError = 128,
        kNumCounters = 160 };
+
+// Workgroup items of the segment kernels: {first position, kMediumItem | length}
+// for a medium run, {long run, chunk} for a 256-lookup chunk of a long run.
+constexpr uint32_t kMediumItem = 0x80000000u;
+
+// Where a run-length encoder that sees whole runs queues those longer than
+// short_max lookups (medium runs and the chunks of long runs), so that the
+// segment kernels need not queue them.
+struct RunQueue {
+  uint2* items1;
+  uint4* longs;            // {first position, length, first partial, chunks}
+  uint32_t* long_keys;
+  int32_t short_max;
+  int32_t long_threshold;
+  int32_t chunk;
+};
 constexpr int kNumTickets = 8;           // kMaxRadixPasses radix passes + the RLE
 
 // Keys per thread of a radix tile for a batch of n lookups (8 or 16).
@@ -287,7 +303,7 @@ int sort_tile_keys(int64_t n, int key_bits);
 struct SegmentBounds {
   int64_t longs, chunks, items1;
 };
-SegmentBounds segment_bounds(int64_t n, int64_t long_threshold, int chunk, int gshift);
+SegmentBounds segment_bounds(int64_t n, int64_t long_threshold, int chunk, int short_max);
 
 struct BackwardLaunch {
   const void* indices;
@@ -307,6 +323,8 @@ struct BackwardLaunch {
   int32_t nch;              // chunk sets per lane in the segment kernels (1, 4 or 16)
   int32_t gshift;           // log2(lanes per gradient row) in the segment kernels
   int32_t per_table;        // short runs use each table's own lane-group width
+  int32_t short_max;        // runs of at most this many lookups are short (a lane group's)
+  int32_t front_queued;     // the run-length encoder queued the longer runs
   int32_t pstride;          // floats per partial row
   int32_t long_threshold;   // runs at least this long use split accumulation
   int32_t chunk;            // lookups per level-1 partial
@@ -345,6 +363,9 @@ hipError_t launch_run_length_encode(const BackwardLaunch& a, const uint32_t* sor
 // LSD passes and the RLE kernel.  Either way the sorted pair ends in buffer
 // radix_passes() % 2 and the order is the same (stable on the id).
 hipError_t launch_sort_encode(const BackwardLaunch& a, hipStream_t stream, const KernelTimer* kt);
+// True when the grouping of this launch's batch takes the bucket-local sort
+// (whose run-length encoding also queues the longer runs).
+bool uses_bucket_sort(const BackwardLaunch& a);
 hipError_t launch_segment_reduce_update(const BackwardLaunch& a, const uint32_t* sorted_keys,
                                         const uint32_t* sorted_vals, hipStream_t stream,
                                         const KernelTimer* kt);

@@ -46,7 +46,6 @@
 namespace tbe {
 namespace {
 
-constexpr uint32_t kMediumItem = 0x80000000u;
 
 // Gradient rows kept in flight per lane group: 8 in seg_short (4 inside a
 // workgroup item) for rows of one 16-byte chunk per lane, fewer when a lane
@@ -189,14 +188,15 @@ struct GroupIds {
   GroupCtx g;
 };
 
-__device__ __forceinline__ GroupIds group_ids(const BackwardLaunch& a) {
+__device__ __forceinline__ GroupIds group_ids(const BackwardLaunch& a, uint32_t bid,
+                                              uint32_t nblk) {
   GroupIds r;
   const int Gs = 1 << a.gshift;
   const int per_wave = kWave >> a.gshift;
   const int lane = lane_id();
-  const int wave_global = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int wave_global = bid * kWavesPerBlock + (threadIdx.x >> 6);
   r.gid = wave_global * per_wave + (lane >> a.gshift);
-  r.ngroups = gridDim.x * kWavesPerBlock * per_wave;
+  r.ngroups = nblk * kWavesPerBlock * per_wave;
   r.g.gl = lane & (Gs - 1);
   r.g.Gs = Gs;
   return r;
@@ -286,9 +286,10 @@ __device__ __forceinline__ void gather_short(const BackwardLaunch& a, const Tabl
 
 // One run per lane group of Gs lanes (Gs = 2^k <= 64, groups aligned within
 // the wave), called by every lane of the wave together.  Runs longer than Gq
-// lookups are queued as workgroup items; shorter ones are gathered here in
-// batches of Gs lookups (one batch when Gs = Gq).  t is the run's table, or
-// -1 to find it from the row id.
+// lookups are queued as workgroup items (unless the run-length encoder queued
+// them already); shorter ones are gathered here in batches of Gs lookups (one
+// batch when Gs >= Gq).  t is the run's table, or -1 to find it from the row
+// id.
 template <int ST, int VE, int NCH, bool REC, bool PT>
 __device__ __forceinline__ void short_run(const BackwardLaunch& a, const uint32_t* sorted_vals,
                                           const TableMeta* s_meta, uint32_t r, bool valid,
@@ -310,7 +311,7 @@ __device__ __forceinline__ void short_run(const BackwardLaunch& a, const uint32_
   // run as its 256-lookup chunks.  Queue slots are reserved with one atomic
   // per counter per wave (a wave-wide scan of the groups' needs), not per
   // run; the counters sit on separate cache lines.
-  if (__ballot(gl == 0 && len > Gq)) {
+  if (!a.front_queued && __ballot(gl == 0 && len > Gq)) {
     const bool is_long = len > Gq && len >= a.long_threshold;
     const bool is_medium = len > Gq && !is_long;
     const uint32_t n1 = is_long ? static_cast<uint32_t>((len + a.chunk - 1) / a.chunk) : 0u;
@@ -420,23 +421,25 @@ __device__ __forceinline__ int table_gshift(const TableMeta& m) {
 // same number of times on every lane of a wave (groups past the last run
 // idle), so the queueing in short_run can use wave-wide scans.
 template <int ST, int VE, int NCH, bool REC, bool PT>
-__global__ __launch_bounds__(kBlock) void seg_short(BackwardLaunch a, const uint32_t* sorted_vals) {
+__device__ __forceinline__ void short_runs(const BackwardLaunch& a, const uint32_t* sorted_vals,
+                                           uint32_t bid, uint32_t nblk) {
   __shared__ TableMeta s_meta[kLdsTables];
   const bool failed = a.buf.counters[kCntError] != 0u;  // a look-back wait gave up earlier
   const uint32_t U = a.buf.counters[kCntUnique];
-  if (a.out_num && blockIdx.x == 0 && threadIdx.x == 0) *a.out_num = failed ? -1 : static_cast<int32_t>(U);
+  if (a.out_num && bid == 0 && threadIdx.x == 0) *a.out_num = failed ? -1 : static_cast<int32_t>(U);
   if (failed) return;
   stage_meta(a, s_meta);
-  const int Gq = 1 << a.gshift;
+  const int Gq = a.short_max;
   const int lane = lane_id();
   if constexpr (!PT) {
-    const GroupIds id = group_ids(a);
-    const int leader = lane & ~(Gq - 1);
+    const GroupIds id = group_ids(a, bid, nblk);
+    const int Gs = 1 << a.gshift;  // >= Gq
+    const int leader = lane & ~(Gs - 1);
     const uint32_t wave_first = id.gid - static_cast<uint32_t>(lane >> a.gshift);
     const uint32_t ng = id.ngroups;
     uint32_t r = id.gid;
     for (uint32_t rb = wave_first; rb < U; rb += ng, r += ng)
-      short_run<ST, VE, NCH, REC, false>(a, sorted_vals, s_meta, r, r < U, -1, Gq, id.g.gl,
+      short_run<ST, VE, NCH, REC, false>(a, sorted_vals, s_meta, r, r < U, -1, Gs, id.g.gl,
                                          leader, Gq);
     return;
   }
@@ -457,8 +460,8 @@ __global__ __launch_bounds__(kBlock) void seg_short(BackwardLaunch a, const uint
   if (tid < a.T) s_task[tid] = before;
   if (tid == 0) s_task[a.T] = ntasks;
   __syncthreads();
-  const uint32_t nwaves = gridDim.x * kWavesPerBlock;
-  for (uint32_t k = blockIdx.x * kWavesPerBlock + (tid >> 6); k < ntasks; k += nwaves) {
+  const uint32_t nwaves = nblk * kWavesPerBlock;
+  for (uint32_t k = bid * kWavesPerBlock + (tid >> 6); k < ntasks; k += nwaves) {
     int lo = 0, hi = a.T;  // the table of task k: s_task[lo] <= k < s_task[lo + 1]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -470,6 +473,11 @@ __global__ __launch_bounds__(kBlock) void seg_short(BackwardLaunch a, const uint
     short_run<ST, VE, NCH, REC, true>(a, sorted_vals, s_meta, r, r < s_ustart[lo + 1], lo, Gs,
                                       lane & (Gs - 1), lane & ~(Gs - 1), Gq);
   }
+}
+
+template <int ST, int VE, int NCH, bool REC, bool PT>
+__global__ __launch_bounds__(kBlock) void seg_short(BackwardLaunch a, const uint32_t* sorted_vals) {
+  short_runs<ST, VE, NCH, REC, PT>(a, sorted_vals, blockIdx.x, gridDim.x);
 }
 
 // First run id of every table: the lower bound of the table's first row id in
@@ -516,8 +524,9 @@ __device__ __forceinline__ double block_sum(double x, double* scratch) {
 }
 
 template <int ST, int VE, int NCH, bool REC>
-__global__ __launch_bounds__(kBlock) void seg_wg(BackwardLaunch a, const uint32_t* __restrict__ keys,
-                                                 const uint32_t* __restrict__ sorted_vals) {
+__device__ __forceinline__ void wg_items(const BackwardLaunch& a, const uint32_t* __restrict__ keys,
+                                         const uint32_t* __restrict__ sorted_vals, uint32_t bid,
+                                         uint32_t nblk) {
   if (a.buf.counters[kCntError] != 0u) return;  // a look-back wait gave up earlier
   constexpr int NV = VE * NCH;                 // values per lane
   constexpr int kElemsPerThread = kMaxDim / kBlock;
@@ -529,7 +538,7 @@ __global__ __launch_bounds__(kBlock) void seg_wg(BackwardLaunch a, const uint32_
   const int tid = threadIdx.x;
   const uint32_t n = a.buf.counters[kCntItems1];
 
-  for (uint32_t item = blockIdx.x; item < n; item += gridDim.x) {
+  for (uint32_t item = bid; item < n; item += nblk) {
     const uint2 it = a.buf.items1[item];
     const bool medium = (it.y & kMediumItem) != 0;
     uint32_t slot = 0;
@@ -618,6 +627,28 @@ __global__ __launch_bounds__(kBlock) void seg_wg(BackwardLaunch a, const uint32_
       }
     }
   }
+}
+
+template <int ST, int VE, int NCH, bool REC>
+__global__ __launch_bounds__(kBlock) void seg_wg(BackwardLaunch a, const uint32_t* __restrict__ keys,
+                                                 const uint32_t* __restrict__ sorted_vals) {
+  wg_items<ST, VE, NCH, REC>(a, keys, sorted_vals, blockIdx.x, gridDim.x);
+}
+
+// Short runs and workgroup items in one launch, for batches whose run-length
+// encoding queued the items already: the first item_blocks workgroups take
+// the items (bandwidth-bound row gathers), the others the short runs (bound
+// by the latency of their dependent loads), so the two overlap.
+template <int ST, int VE, int NCH, bool REC, bool PT>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(7))) void seg_fused(
+    BackwardLaunch a, const uint32_t* keys,
+                                                    const uint32_t* sorted_vals,
+                                                    uint32_t item_blocks) {
+  if (blockIdx.x < item_blocks)
+    wg_items<ST, VE, NCH, REC>(a, keys, sorted_vals, blockIdx.x, item_blocks);
+  else
+    short_runs<ST, VE, NCH, REC, PT>(a, sorted_vals, blockIdx.x - item_blocks,
+                                     gridDim.x - item_blocks);
 }
 
 // One workgroup per long run: its chunk partials are added up and the row
@@ -733,22 +764,37 @@ int64_t blocks_for(int64_t items, int gshift) {
   return b < kMaxSegBlocks ? b : kMaxSegBlocks;
 }
 
+// Workgroups of the fused launch that take the queued items.
+constexpr int64_t kFusedItemBlocks = 512;
+
 template <int ST, int VE, int NCH, bool REC>
 hipError_t run_segments(const BackwardLaunch& a, const uint32_t* keys, const uint32_t* sorted_vals,
                         hipStream_t s, const KernelTimer* kt) {
   const int64_t n = a.num_indices;
-  const SegmentBounds ub = segment_bounds(n, a.long_threshold, a.chunk, a.gshift);
-  if (a.per_table) {
+  const SegmentBounds ub = segment_bounds(n, a.long_threshold, a.chunk, a.short_max);
+  if (a.per_table)
     launch_timed(kt, "table_run_starts", table_run_starts, dim3(a.T + 1), dim3(kBlock), 0, s, a);
-    launch_timed(kt, "seg_short", seg_short<ST, VE, NCH, REC, true>,
-                 dim3(blocks_for(n, a.gshift)), dim3(kBlock), 0, s, a, sorted_vals);
+  const int64_t short_blocks = blocks_for(n, a.gshift);
+  if (a.front_queued) {
+    const int64_t ib = ub.items1 < kFusedItemBlocks ? ub.items1 : kFusedItemBlocks;
+    const dim3 grid(static_cast<unsigned>(ib + short_blocks));
+    if (a.per_table)
+      launch_timed(kt, "seg_fused", seg_fused<ST, VE, NCH, REC, true>, grid, dim3(kBlock), 0, s,
+                   a, keys, sorted_vals, static_cast<uint32_t>(ib));
+    else
+      launch_timed(kt, "seg_fused", seg_fused<ST, VE, NCH, REC, false>, grid, dim3(kBlock), 0, s,
+                   a, keys, sorted_vals, static_cast<uint32_t>(ib));
   } else {
-    launch_timed(kt, "seg_short", seg_short<ST, VE, NCH, REC, false>,
-                 dim3(blocks_for(n, a.gshift)), dim3(kBlock), 0, s, a, sorted_vals);
+    if (a.per_table)
+      launch_timed(kt, "seg_short", seg_short<ST, VE, NCH, REC, true>, dim3(short_blocks),
+                   dim3(kBlock), 0, s, a, sorted_vals);
+    else
+      launch_timed(kt, "seg_short", seg_short<ST, VE, NCH, REC, false>, dim3(short_blocks),
+                   dim3(kBlock), 0, s, a, sorted_vals);
+    const int64_t wg = ub.items1 < kMaxSegBlocks ? (ub.items1 > 0 ? ub.items1 : 1) : kMaxSegBlocks;
+    launch_timed(kt, "seg_wg", seg_wg<ST, VE, NCH, REC>, dim3(wg), dim3(kBlock), 0, s, a, keys,
+                 sorted_vals);
   }
-  const int64_t wg = ub.items1 < kMaxSegBlocks ? (ub.items1 > 0 ? ub.items1 : 1) : kMaxSegBlocks;
-  launch_timed(kt, "seg_wg", seg_wg<ST, VE, NCH, REC>, dim3(wg), dim3(kBlock), 0, s, a, keys,
-               sorted_vals);
   const int64_t fin = ub.longs < kMaxSegBlocks ? ub.longs : kMaxSegBlocks;
   launch_timed(kt, "seg_finalize", seg_finalize<ST, VE, NCH, REC>, dim3(fin), dim3(kBlock), 0, s,
                a);
@@ -777,10 +823,10 @@ hipError_t dispatch_shape(const BackwardLaunch& a, const uint32_t* k, const uint
 
 }  // namespace
 
-SegmentBounds segment_bounds(int64_t n, int64_t long_threshold, int chunk, int gshift) {
+SegmentBounds segment_bounds(int64_t n, int64_t long_threshold, int chunk, int short_max) {
   SegmentBounds b;
   const int64_t thr = long_threshold > 0 ? long_threshold : 1;
-  const int64_t group_max = int64_t{1} << gshift;  // longest run a lane group takes alone
+  const int64_t group_max = short_max;  // longest run a lane group takes
   b.longs = n / thr + 1;
   b.chunks = n / chunk + b.longs;
   // queued items: runs longer than group_max that are not long, plus long-run chunks

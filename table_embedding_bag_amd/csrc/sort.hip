@@ -641,11 +641,31 @@ __device__ __forceinline__ void load_range(const uint32_t* kin, const uint32_t* 
   }
 }
 
+// Queue a run of len > q.short_max lookups starting at sorted position s:
+// one medium item, or the long-run record and one item per 256-lookup chunk.
+// Only a small share of runs is this long, so each is queued on its own.
+__device__ __forceinline__ void queue_run(const RunQueue& q, uint32_t* counters, uint32_t s,
+                                          uint32_t len, uint32_t key) {
+  if (len >= static_cast<uint32_t>(q.long_threshold)) {
+    const uint32_t n1 = (len + q.chunk - 1) / q.chunk;
+    const uint32_t li = atomicAdd(&counters[kCntLong], 1u);
+    const uint32_t b1 = atomicAdd(&counters[kCntChunks], n1);
+    const uint32_t it = atomicAdd(&counters[kCntItems1], n1);
+    q.longs[li] = make_uint4(s, len, b1, n1);
+    q.long_keys[li] = key;
+    for (uint32_t c = 0; c < n1; ++c) q.items1[it + c] = make_uint2(li, c);
+  } else {
+    const uint32_t it = atomicAdd(&counters[kCntItems1], 1u);
+    q.items1[it] = make_uint2(s, kMediumItem | len);
+  }
+}
+
 __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
     const uint32_t* __restrict__ kin, const uint32_t* __restrict__ vin, uint32_t* kout,
     uint32_t* vout, int64_t n, int lbits, int nbuckets, const uint32_t* __restrict__ htotals,
     const uint32_t* __restrict__ wtable, int ntiles, uint32_t* status, uint32_t* ticket,
-    uint32_t* counters, uint32_t* unique_keys, uint32_t* run_start, uint32_t* run_first) {
+    uint32_t* counters, uint32_t* unique_keys, uint32_t* run_start, uint32_t* run_first,
+    RunQueue q) {
   constexpr int NT = kBucketThreads, NW = kBucketWaves, CAP = kBucketCap;
   __shared__ uint32_t s_k[CAP];
   __shared__ uint32_t s_v[CAP];
@@ -657,6 +677,7 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
   __shared__ uint32_t s_run[NT];         // long ranges: digit positions used so far
   __shared__ uint32_t scratch[NW];
   __shared__ uint32_t s_tile, s_base;
+  __shared__ uint32_t s_qbase[3];        // queue slots: items, long runs, chunks
 
   const int tid = threadIdx.x, wave = tid >> 6;
   int tile = static_cast<int>(blockIdx.x);
@@ -801,8 +822,49 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
   // run ids: this window's first one from the look-back over earlier windows
   uint32_t htotal;
   const uint32_t hex = block_excl_n<NW>(my_heads, scratch, &htotal);
+  // the window's run count goes out at once; the look-back comes later
+  if (tid == 0) st_status(status + tile, (tile == 0 ? kFlagIncl : kFlagAgg) | htotal);
+  // in-LDS ranges: head positions by run id inside the range (the count
+  // buffer is free now), so every run knows where it ends; then the queue
+  // slots the runs longer than q.short_max need: items, and long runs packed
+  // with their chunks (long runs << 16 | chunks; a range holds fewer than 2^16)
+  uint32_t* s_hpos = reinterpret_cast<uint32_t*>(&s_cnt[0][0]);
+  const int len_l = len64 <= CAP ? static_cast<int>(len64) : 0;
+  {
+    uint32_t lr = hex;
+    for (int j = 0; j < rr; ++j) {
+      const int i = tid * rr + j;
+      if (i < len_l && (i == 0 || s_k[i] != s_k[i - 1])) s_hpos[lr++] = static_cast<uint32_t>(i);
+    }
+  }
+  __syncthreads();
+  const auto run_len = [&](uint32_t lr, int i) {
+    return (lr + 1 < htotal ? s_hpos[lr + 1] : static_cast<uint32_t>(len_l)) -
+           static_cast<uint32_t>(i);
+  };
+  uint32_t need_items = 0, need_lc = 0;
+  if (q.short_max > 0) {
+    uint32_t lr = hex;
+    for (int j = 0; j < rr; ++j) {
+      const int i = tid * rr + j;
+      if (i < len_l && (i == 0 || s_k[i] != s_k[i - 1])) {
+        const uint32_t rl = run_len(lr++, i);
+        if (rl > static_cast<uint32_t>(q.short_max)) {
+          if (rl >= static_cast<uint32_t>(q.long_threshold)) {
+            const uint32_t n1 = (rl + q.chunk - 1) / q.chunk;
+            need_items += n1;
+            need_lc += (1u << 16) + n1;
+          } else {
+            need_items += 1;
+          }
+        }
+      }
+    }
+  }
+  uint32_t t_items, t_lc;
+  const uint32_t x_items = block_excl_n<NW>(need_items, scratch, &t_items);
+  const uint32_t x_lc = block_excl_n<NW>(need_lc, scratch, &t_lc);
   if (tid < kWave) {
-    if (tid == 0) st_status(status + tile, (tile == 0 ? kFlagIncl : kFlagAgg) | htotal);
     uint32_t before = 0;
     if (tile > 0) before = lookback_wave(status, tile, counters + kCntError);
     if (tid == 0) {
@@ -815,20 +877,43 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
         run_start[U] = static_cast<uint32_t>(n);
       }
     }
+  } else if (tid == kWave && (t_items | t_lc) != 0u) {
+    // the window's queue slots, reserved while wave 0 looks back
+    s_qbase[0] = t_items ? atomicAdd(&counters[kCntItems1], t_items) : 0u;
+    s_qbase[1] = (t_lc >> 16) ? atomicAdd(&counters[kCntLong], t_lc >> 16) : 0u;
+    s_qbase[2] = (t_lc & 0xFFFFu) ? atomicAdd(&counters[kCntChunks], t_lc & 0xFFFFu) : 0u;
   }
   __syncthreads();
   if (len64 <= CAP) {
-    uint32_t r = s_base + hex;
-    const int len = static_cast<int>(len64);
+    uint32_t lr = hex;
+    uint32_t it = s_qbase[0] + x_items;
+    uint32_t li = s_qbase[1] + (x_lc >> 16);
+    uint32_t b1 = s_qbase[2] + (x_lc & 0xFFFFu);
     for (int j = 0; j < rr; ++j) {
       const int i = tid * rr + j;
-      if (i < len && (i == 0 || s_k[i] != s_k[i - 1])) {
+      if (i < len_l && (i == 0 || s_k[i] != s_k[i - 1])) {
+        const uint32_t r = s_base + lr;
+        const uint32_t rl = run_len(lr, i);
+        const uint32_t ps = static_cast<uint32_t>(start + i);
         if (r < static_cast<uint64_t>(n)) {
           unique_keys[r] = s_k[i];
-          run_start[r] = static_cast<uint32_t>(start + i);
+          run_start[r] = ps;
           run_first[r] = s_v[i];
         }
-        ++r;
+        if (q.short_max > 0 && rl > static_cast<uint32_t>(q.short_max)) {
+          if (rl >= static_cast<uint32_t>(q.long_threshold)) {
+            const uint32_t n1 = (rl + q.chunk - 1) / q.chunk;
+            q.longs[li] = make_uint4(ps, rl, b1, n1);
+            q.long_keys[li] = s_k[i];
+            for (uint32_t c = 0; c < n1; ++c) q.items1[it + c] = make_uint2(li, c);
+            ++li;
+            b1 += n1;
+            it += n1;
+          } else {
+            q.items1[it++] = make_uint2(ps, kMediumItem | rl);
+          }
+        }
+        ++lr;
       }
     }
   } else {
@@ -849,6 +934,20 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
         run_first[r0 + ex] = vout[start + i];
       }
       r0 += t3;
+    }
+    if (q.short_max > 0) {
+      // run lengths from the run starts just written (the range's last run
+      // ends with the range)
+      __threadfence_block();
+      __syncthreads();
+      for (uint32_t lr = tid; lr < htotal; lr += NT) {
+        const uint32_t r = s_base + lr;
+        if (r + 1 >= static_cast<uint64_t>(n) + 1) break;
+        const uint32_t s0 = run_start[r];
+        const uint32_t e0 = lr + 1 < htotal ? run_start[r + 1] : static_cast<uint32_t>(start + len64);
+        if (e0 - s0 > static_cast<uint32_t>(q.short_max))
+          queue_run(q, counters, s0, e0 - s0, unique_keys[r]);
+      }
     }
   }
 }
@@ -949,22 +1048,27 @@ hipError_t launch_radix_sort(const BackwardLaunch& a, hipStream_t stream, int* r
   return hipSuccess;
 }
 
+// Two digits, and buckets of the high digit short on average (they are sorted
+// in LDS; a bucket longer than kBucketCap - kBucketWindow takes the slower
+// chunked path).
+bool uses_bucket_sort(const BackwardLaunch& a) {
+  const int64_t n = a.num_indices;
+  const int passes = radix_passes(a.key_bits, n);
+  const int bits = radix_digit_bits(a.key_bits, n);
+  return a.bucket_sort && n > 0 && passes == 2 && n <= kWideRadixMaxKeys &&
+         (n >> (a.key_bits - bits)) <= kBucketMeanMax;
+}
+
 hipError_t launch_sort_encode(const BackwardLaunch& a, hipStream_t stream, const KernelTimer* kt) {
   const int64_t n = a.num_indices;
   if (n <= 0) return hipSuccess;
-  const int passes = radix_passes(a.key_bits, n);
-  const int bits = radix_digit_bits(a.key_bits, n);
-  // two digits, and buckets of the high digit short on average (they are
-  // sorted in LDS; a bucket longer than kBucketCap - kBucketWindow takes the
-  // slower chunked path)
-  const bool bucket = a.bucket_sort && passes == 2 && n <= kWideRadixMaxKeys &&
-                      (n >> (a.key_bits - bits)) <= kBucketMeanMax;
-  if (!bucket) {
+  if (!uses_bucket_sort(a)) {
     int sorted = 0;
     const hipError_t e = launch_radix_sort(a, stream, &sorted, kt);
     if (e != hipSuccess) return e;
     return launch_run_length_encode(a, a.buf.keys[sorted], a.buf.vals[sorted], stream, kt);
   }
+  const int bits = radix_digit_bits(a.key_bits, n);
   const uint32_t* htotals = a.buf.digit_hist + radix_slots(bits);  // counts of the high digit
   // look-back status words of the windows, then their range records
   const int windows = static_cast<int>((n + kBucketWindow - 1) / kBucketWindow);
@@ -977,7 +1081,9 @@ hipError_t launch_sort_encode(const BackwardLaunch& a, hipStream_t stream, const
                stream, a.buf.keys[1], a.buf.vals[1], a.buf.keys[0], a.buf.vals[0], n, bits,
                1 << bits, htotals, wtable, windows, wstatus,
                windows <= kResidentTiles ? nullptr : a.buf.tickets + kMaxRadixPasses,
-               a.buf.counters, a.buf.unique_keys, a.buf.run_start, a.buf.run_first);
+               a.buf.counters, a.buf.unique_keys, a.buf.run_start, a.buf.run_first,
+               RunQueue{a.buf.items1, a.buf.longs, a.buf.long_keys, a.short_max,
+                        a.long_threshold, a.chunk});
   return hipGetLastError();
 }
 

@@ -108,16 +108,15 @@ def algorithmic_bytes(spec, batch, gather_tables=None, long_threshold=256, chunk
     fwd_linearize         the gather forward's bytes plus the linearize step's
     segment (per lookup)  sorted value 4 + gradient row 4*D (+ record 8 with weights / mean)
             (per row)     id + run bounds 12 + row read and write 2*D*s (+ state read/write 8)
-      seg_short           runs a lane group takes alone (at most Gs lookups)
-      seg_wg              longer runs below the long-run threshold, and the lookups of long
-                          runs (+ one 4*D partial write per 256-lookup chunk)
-      seg_fused           seg_short and seg_wg in one launch (batches whose run-length
-                          encoding queued the longer runs)
+      seg_fused           short runs (at most Gs lookups, one lane group each) and the
+                          queued items: longer runs below the long-run threshold, and the
+                          lookups of long runs (+ one 4*D partial write per 256-lookup
+                          chunk), in one launch
       seg_finalize        per long run: its chunk partials read, the row terms
     grouping front: linearize, radix passes (key+value read and scatter 16 per lookup),
     bucket_sort_rle (key+value read and final write 16 per lookup; unique id, start and
     first value 12 per run), rle_kernel (keys 4 per lookup; per run 12 written, first
-    value read 4)
+    value read 4), queue_runs (run bounds 8 per run)
     """
     import numpy as np
     s = {"f32": 4, "f16": 2, "bf16": 2}[spec.dtype]
@@ -150,7 +149,9 @@ def algorithmic_bytes(spec, batch, gather_tables=None, long_threshold=256, chunk
     # run-length encoding keys read 4 + unique id/start writes 8 per run
     front = {"linearize_kernel": float(N * (8 + 8 + rec) + 8 * nbags),
              "radix_pass": float(16 * N), "rle_kernel": float(4 * N + 16 * U),
-             "bucket_sort_rle": float(16 * N + 12 * U)}
+             "bucket_sort_rle": float(16 * N + 12 * U),
+             # run bounds read 8 per run (the few queued runs' entries are not counted)
+             "queue_runs": float(8 * U)}
     # count-matrix forward (tables that qualify): ids 8 + per bag offset 8 + output 4*D, one
     # read of each table; the dense product does 2*B*E_t*D_t flops per table.  The W^T
     # staging kernel reads each table and writes its transposed copy.

@@ -16,20 +16,24 @@
 //
 // The cost of a run is the latency of its dependent loads (sorted position ->
 // bag -> gradient row), so the work is shaped to keep many gradient rows in
-// flight per run:
-//   seg_short     one lane group (Gs lanes = one gradient row of 16-byte
-//                 chunks) per run of at most Gs lookups: every lane prefetches
-//                 one lookup, the group gathers the run's gradient rows with 2
-//                 or 4 in flight (matched to the run's length), sums them in
-//                 fp32 and updates the row.  Most runs are this short.  Longer
-//                 runs are queued as workgroup items; each wave reserves its
-//                 queue slots with one atomic per counter.
-//   seg_wg        one workgroup per queued item: a medium run (shorter than the
+// flight per run.  Runs longer than a lane group takes (short_max lookups) are
+// queued as workgroup items before the reduce: by the bucket-local run-length
+// encoder, which sees whole runs, or else by queue_runs (one lane per run).
+//   seg_fused     every workgroup first takes its share of the queued items,
+//                 then its share of the short runs, so bandwidth-bound and
+//                 latency-bound work overlap across the chip:
+//     items       one workgroup per item: a medium run (shorter than the
 //                 long-run threshold, streamed in one pass and updated at once)
 //                 or a 256-lookup chunk of a long run (split accumulation: an
 //                 fp32 partial sum per chunk).  The workgroup stages 256 lookups
 //                 in LDS and its 256/Gs lane groups keep 4 rows each in flight;
 //                 the groups' sums are added in LDS in a fixed order.
+//     short runs  one lane group (Gs lanes = one gradient row of 16-byte
+//                 chunks; per table when tables differ in width) per run: every
+//                 lane prefetches one lookup, the group gathers the run's
+//                 gradient rows with 2 or 4 in flight (matched to the run's
+//                 length), sums them in fp32 and updates the row.  Most runs
+//                 are this short.
 //   seg_finalize  one workgroup per long run: its partials summed in a fixed
 //                 order, then the update.
 // Summation order never depends on scheduling (no float atomics), so results
@@ -47,7 +51,7 @@ namespace tbe {
 namespace {
 
 
-// Gradient rows kept in flight per lane group: 8 in seg_short (4 inside a
+// Gradient rows kept in flight per lane group: 8 for short runs (4 inside a
 // workgroup item) for rows of one 16-byte chunk per lane, fewer when a lane
 // holds several chunks, so that registers stay below 128 per lane.
 template <int VE, int NCH>
@@ -286,10 +290,10 @@ __device__ __forceinline__ void gather_short(const BackwardLaunch& a, const Tabl
 
 // One run per lane group of Gs lanes (Gs = 2^k <= 64, groups aligned within
 // the wave), called by every lane of the wave together.  Runs longer than Gq
-// lookups are queued as workgroup items (unless the run-length encoder queued
-// them already); shorter ones are gathered here in batches of Gs lookups (one
-// batch when Gs >= Gq).  t is the run's table, or -1 to find it from the row
-// id.
+// lookups were queued as workgroup items (by the run-length encoder or
+// queue_runs) and are skipped; shorter ones are gathered here in batches of Gs
+// lookups (one batch when Gs >= Gq).  t is the run's table, or -1 to find it
+// from the row id.
 template <int ST, int VE, int NCH, bool REC, bool PT>
 __device__ __forceinline__ void short_run(const BackwardLaunch& a, const uint32_t* sorted_vals,
                                           const TableMeta* s_meta, uint32_t r, bool valid,
@@ -306,46 +310,6 @@ __device__ __forceinline__ void short_run(const BackwardLaunch& a, const uint32_
   if (valid && a.out_unique && gl == 0) {
     a.out_unique[r] = static_cast<int32_t>(key);
     a.out_lengths[r] = len;
-  }
-  // Queue runs longer than Gq: a medium run as one workgroup item, a long
-  // run as its 256-lookup chunks.  Queue slots are reserved with one atomic
-  // per counter per wave (a wave-wide scan of the groups' needs), not per
-  // run; the counters sit on separate cache lines.
-  if (!a.front_queued && __ballot(gl == 0 && len > Gq)) {
-    const bool is_long = len > Gq && len >= a.long_threshold;
-    const bool is_medium = len > Gq && !is_long;
-    const uint32_t n1 = is_long ? static_cast<uint32_t>((len + a.chunk - 1) / a.chunk) : 0u;
-    const bool ld = gl == 0;
-    uint32_t t_long, t_chunks, t_items1;
-    const uint32_t x_long = wave_excl_scan(ld && is_long ? 1u : 0u, &t_long);
-    const uint32_t x_chunks = wave_excl_scan(ld ? n1 : 0u, &t_chunks);
-    const uint32_t x_items1 = wave_excl_scan(ld ? (is_long ? n1 : (is_medium ? 1u : 0u)) : 0u,
-                                             &t_items1);
-    uint32_t base[3] = {0u, 0u, 0u};
-    if (lane_id() == 0) {
-      if (t_long) base[0] = atomicAdd(&a.buf.counters[kCntLong], t_long);
-      if (t_chunks) base[1] = atomicAdd(&a.buf.counters[kCntChunks], t_chunks);
-      if (t_items1) base[2] = atomicAdd(&a.buf.counters[kCntItems1], t_items1);
-    }
-#pragma unroll
-    for (int q = 0; q < 3; ++q) base[q] = __shfl(base[q], 0, kWave);
-    // every lane of a group takes its leader's slots
-    const uint32_t li = __shfl(base[0] + x_long, leader, kWave);
-    const uint32_t b1 = __shfl(base[1] + x_chunks, leader, kWave);
-    const uint32_t it = __shfl(base[2] + x_items1, leader, kWave);
-    // items carry the run's first position and length, so the workgroup
-    // kernels need no run-list lookup
-    if (is_long) {
-      if (ld) {
-        a.buf.longs[li] =
-            make_uint4(static_cast<uint32_t>(s), static_cast<uint32_t>(len), b1, n1);
-        a.buf.long_keys[li] = key;
-      }
-      for (uint32_t c = gl; c < n1; c += Gs) a.buf.items1[it + c] = make_uint2(li, c);
-    } else if (is_medium && ld) {
-      a.buf.items1[it] =
-          make_uint2(static_cast<uint32_t>(s), kMediumItem | static_cast<uint32_t>(len));
-    }
   }
   if (!valid || len > Gq) return;
   uint32_t my_bag = 0;
@@ -475,10 +439,6 @@ __device__ __forceinline__ void short_runs(const BackwardLaunch& a, const uint32
   }
 }
 
-template <int ST, int VE, int NCH, bool REC, bool PT>
-__global__ __launch_bounds__(kBlock) void seg_short(BackwardLaunch a, const uint32_t* sorted_vals) {
-  short_runs<ST, VE, NCH, REC, PT>(a, sorted_vals, blockIdx.x, gridDim.x);
-}
 
 // First run id of every table: the lower bound of the table's first row id in
 // the sorted unique ids, by a 256-way search (three rounds cover 2^24 runs).
@@ -629,26 +589,115 @@ __device__ __forceinline__ void wg_items(const BackwardLaunch& a, const uint32_t
   }
 }
 
-template <int ST, int VE, int NCH, bool REC>
-__global__ __launch_bounds__(kBlock) void seg_wg(BackwardLaunch a, const uint32_t* __restrict__ keys,
-                                                 const uint32_t* __restrict__ sorted_vals) {
-  wg_items<ST, VE, NCH, REC>(a, keys, sorted_vals, blockIdx.x, gridDim.x);
+// Queue the runs longer than a.short_max lookups when the run-length encoder
+// did not (it cannot see whole runs in the LSD path).  A workgroup takes 1024
+// runs at a time (4 per thread, strided so loads coalesce) and reserves the
+// slots they need with one atomic per counter: queue slots are few, but
+// reserving them per wave put tens of thousands of same-address atomics in a
+// row (60 us on 1 M runs; 16 runs per thread left too few workgroups).  Items carry the run's first position and length, so the workgroup
+// code needs no run-list lookup.
+constexpr int kQueueRunsPerThread = 4;
+// Long runs with more chunks than this have their chunk items written by the
+// whole workgroup (a run of 271k lookups has over a thousand).
+constexpr uint32_t kQueueOwnChunks = 16;
+
+__global__ __launch_bounds__(kBlock) void queue_runs(BackwardLaunch a) {
+  __shared__ uint32_t s_scr[kWavesPerBlock];
+  __shared__ uint32_t s_base[3];
+  __shared__ uint4 s_big[kBlock];  // {long run, first item, chunks}
+  __shared__ uint32_t s_nbig;
+  if (threadIdx.x == 0) s_nbig = 0u;
+  if (a.buf.counters[kCntError] != 0u) return;  // a look-back wait gave up earlier
+  const uint32_t U = a.buf.counters[kCntUnique];
+  constexpr uint32_t kRuns = kBlock * kQueueRunsPerThread;
+  for (uint32_t r0 = blockIdx.x * kRuns; r0 < U; r0 += gridDim.x * kRuns) {
+    uint32_t st[kQueueRunsPerThread], ln[kQueueRunsPerThread];
+    uint32_t n_items = 0, n_long = 0, n_chunks = 0, n_big = 0;
+#pragma unroll
+    for (int j = 0; j < kQueueRunsPerThread; ++j) {
+      const uint32_t r = r0 + j * kBlock + threadIdx.x;
+      st[j] = 0u;
+      ln[j] = 0u;
+      if (r < U) {
+        st[j] = a.buf.run_start[r];
+        ln[j] = a.buf.run_start[r + 1] - st[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kQueueRunsPerThread; ++j) {
+      if (ln[j] > static_cast<uint32_t>(a.short_max)) {
+        if (ln[j] >= static_cast<uint32_t>(a.long_threshold)) {
+          const uint32_t n1 = (ln[j] + a.chunk - 1) / a.chunk;
+          ++n_long;
+          n_chunks += n1;
+          n_items += n1;
+          n_big += n1 > kQueueOwnChunks ? 1u : 0u;
+        } else {
+          ++n_items;
+        }
+      }
+    }
+    uint32_t t_items, t_long, t_chunks;
+    uint32_t x_items = block_exclusive_sum(n_items, s_scr, &t_items);
+    uint32_t x_long = block_exclusive_sum(n_long, s_scr, &t_long);
+    uint32_t x_chunks = block_exclusive_sum(n_chunks, s_scr, &t_chunks);
+    if (t_items == 0u) continue;  // the same on every thread
+    if (threadIdx.x == 0) {
+      s_base[0] = atomicAdd(&a.buf.counters[kCntItems1], t_items);
+      s_base[1] = t_long ? atomicAdd(&a.buf.counters[kCntLong], t_long) : 0u;
+      s_base[2] = t_chunks ? atomicAdd(&a.buf.counters[kCntChunks], t_chunks) : 0u;
+    }
+    __syncthreads();
+    x_items += s_base[0];
+    x_long += s_base[1];
+    x_chunks += s_base[2];
+    __syncthreads();  // s_base is reused by the next round
+    const bool any_big = __syncthreads_or(n_big != 0u);
+#pragma unroll
+    for (int j = 0; j < kQueueRunsPerThread; ++j) {
+      if (ln[j] > static_cast<uint32_t>(a.short_max)) {
+        if (ln[j] >= static_cast<uint32_t>(a.long_threshold)) {
+          const uint32_t r = r0 + j * kBlock + threadIdx.x;
+          const uint32_t n1 = (ln[j] + a.chunk - 1) / a.chunk;
+          a.buf.longs[x_long] = make_uint4(st[j], ln[j], x_chunks, n1);
+          a.buf.long_keys[x_long] = a.buf.unique_keys[r];
+          if (n1 <= kQueueOwnChunks)
+            for (uint32_t c = 0; c < n1; ++c) a.buf.items1[x_items + c] = make_uint2(x_long, c);
+          else
+            s_big[atomicAdd(&s_nbig, 1u)] = make_uint4(x_long, x_items, n1, 0u);
+          ++x_long;
+          x_chunks += n1;
+          x_items += n1;
+        } else {
+          a.buf.items1[x_items++] = make_uint2(st[j], kMediumItem | ln[j]);
+        }
+      }
+      if (any_big) {  // the same on every thread; at most one entry per thread per round
+        __syncthreads();
+        const uint32_t m = s_nbig;
+        for (uint32_t e = 0; e < m; ++e) {
+          const uint4 b = s_big[e];
+          for (uint32_t c = threadIdx.x; c < b.z; c += kBlock)
+            a.buf.items1[b.y + c] = make_uint2(b.x, c);
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) s_nbig = 0u;
+        __syncthreads();
+      }
+    }
+  }
 }
 
-// Short runs and workgroup items in one launch, for batches whose run-length
-// encoding queued the items already: the first item_blocks workgroups take
-// the items (bandwidth-bound row gathers), the others the short runs (bound
-// by the latency of their dependent loads), so the two overlap.
+// The segment reduce of short runs and of the queued workgroup items in one
+// launch: every workgroup first takes its share of the items (medium runs and
+// 256-lookup chunks of long runs: bandwidth-bound row gathers), then its share
+// of the short runs (bound by the latency of their dependent loads), so the
+// two overlap across the chip.
 template <int ST, int VE, int NCH, bool REC, bool PT>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(7))) void seg_fused(
-    BackwardLaunch a, const uint32_t* keys,
-                                                    const uint32_t* sorted_vals,
-                                                    uint32_t item_blocks) {
-  if (blockIdx.x < item_blocks)
-    wg_items<ST, VE, NCH, REC>(a, keys, sorted_vals, blockIdx.x, item_blocks);
-  else
-    short_runs<ST, VE, NCH, REC, PT>(a, sorted_vals, blockIdx.x - item_blocks,
-                                     gridDim.x - item_blocks);
+    BackwardLaunch a, const uint32_t* keys, const uint32_t* sorted_vals) {
+  wg_items<ST, VE, NCH, REC>(a, keys, sorted_vals, blockIdx.x, gridDim.x);
+  short_runs<ST, VE, NCH, REC, PT>(a, sorted_vals, blockIdx.x, gridDim.x);
 }
 
 // One workgroup per long run: its chunk partials are added up and the row
@@ -764,37 +813,27 @@ int64_t blocks_for(int64_t items, int gshift) {
   return b < kMaxSegBlocks ? b : kMaxSegBlocks;
 }
 
-// Workgroups of the fused launch that take the queued items.
-constexpr int64_t kFusedItemBlocks = 512;
-
 template <int ST, int VE, int NCH, bool REC>
 hipError_t run_segments(const BackwardLaunch& a, const uint32_t* keys, const uint32_t* sorted_vals,
                         hipStream_t s, const KernelTimer* kt) {
   const int64_t n = a.num_indices;
   const SegmentBounds ub = segment_bounds(n, a.long_threshold, a.chunk, a.short_max);
+  if (!a.front_queued) {
+    const int64_t per = int64_t{kBlock} * kQueueRunsPerThread;
+    const int64_t qb = (n + per - 1) / per;  // U <= n runs
+    launch_timed(kt, "queue_runs", queue_runs, dim3(static_cast<unsigned>(qb < 1024 ? qb : 1024)),
+                 dim3(kBlock), 0, s, a);
+  }
   if (a.per_table)
     launch_timed(kt, "table_run_starts", table_run_starts, dim3(a.T + 1), dim3(kBlock), 0, s, a);
-  const int64_t short_blocks = blocks_for(n, a.gshift);
-  if (a.front_queued) {
-    const int64_t ib = ub.items1 < kFusedItemBlocks ? ub.items1 : kFusedItemBlocks;
-    const dim3 grid(static_cast<unsigned>(ib + short_blocks));
-    if (a.per_table)
-      launch_timed(kt, "seg_fused", seg_fused<ST, VE, NCH, REC, true>, grid, dim3(kBlock), 0, s,
-                   a, keys, sorted_vals, static_cast<uint32_t>(ib));
-    else
-      launch_timed(kt, "seg_fused", seg_fused<ST, VE, NCH, REC, false>, grid, dim3(kBlock), 0, s,
-                   a, keys, sorted_vals, static_cast<uint32_t>(ib));
-  } else {
-    if (a.per_table)
-      launch_timed(kt, "seg_short", seg_short<ST, VE, NCH, REC, true>, dim3(short_blocks),
-                   dim3(kBlock), 0, s, a, sorted_vals);
-    else
-      launch_timed(kt, "seg_short", seg_short<ST, VE, NCH, REC, false>, dim3(short_blocks),
-                   dim3(kBlock), 0, s, a, sorted_vals);
-    const int64_t wg = ub.items1 < kMaxSegBlocks ? (ub.items1 > 0 ? ub.items1 : 1) : kMaxSegBlocks;
-    launch_timed(kt, "seg_wg", seg_wg<ST, VE, NCH, REC>, dim3(wg), dim3(kBlock), 0, s, a, keys,
-                 sorted_vals);
-  }
+  int64_t blocks = blocks_for(n, a.gshift);
+  if (ub.items1 > blocks) blocks = ub.items1 < kMaxSegBlocks ? ub.items1 : kMaxSegBlocks;
+  if (a.per_table)
+    launch_timed(kt, "seg_fused", seg_fused<ST, VE, NCH, REC, true>, dim3(blocks), dim3(kBlock),
+                 0, s, a, keys, sorted_vals);
+  else
+    launch_timed(kt, "seg_fused", seg_fused<ST, VE, NCH, REC, false>, dim3(blocks), dim3(kBlock),
+                 0, s, a, keys, sorted_vals);
   const int64_t fin = ub.longs < kMaxSegBlocks ? ub.longs : kMaxSegBlocks;
   launch_timed(kt, "seg_finalize", seg_finalize<ST, VE, NCH, REC>, dim3(fin), dim3(kBlock), 0, s,
                a);

@@ -294,7 +294,7 @@ struct RunQueue {
 };
 constexpr int kNumTickets = 8;           // kMaxRadixPasses radix passes + the RLE
 
-// Keys per thread of a radix tile for a batch of n lookups (8 or 16).
+// Keys per thread of a radix tile for a batch of n lookups (8 or 32).
 int sort_keys_per_thread(int64_t n);
 // Keys per radix tile for a batch of n lookups sorted on key_bits bits.
 int sort_tile_keys(int64_t n, int key_bits);

@@ -954,7 +954,11 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
 
 }  // namespace
 
-int sort_keys_per_thread(int64_t n) { return n <= (int64_t{1} << 20) ? 8 : 16; }
+// Larger batches use 8192-key tiles: a tile's keys spread over every bucket of
+// an 8-bit digit, and 32 keys per bucket make the scatter write whole 128-byte
+// lines (16-key tiles left half lines shared with the next tile, usually on
+// another XCD: workload 5's first pass took 323 us against 138 us).
+int sort_keys_per_thread(int64_t n) { return n <= (int64_t{1} << 20) ? 8 : 32; }
 int sort_tile_keys(int64_t n, int key_bits) {
   return radix_digit_bits(key_bits, n) > 8 ? 4096 : kBlock * sort_keys_per_thread(n);
 }
@@ -1024,7 +1028,7 @@ hipError_t launch_pass(const BackwardLaunch& a, int pass, int shift, const uint3
                  vin, kout, vout, n, shift, bits, totals, status, ticket,
                  a.buf.counters + kCntError, wtable);
   else
-    launch_timed(kt, "radix_pass", radix_pass<16, 8>, dim3(ntiles), dim3(kBlock), 0, stream, kin,
+    launch_timed(kt, "radix_pass", radix_pass<32, 8>, dim3(ntiles), dim3(kBlock), 0, stream, kin,
                  vin, kout, vout, n, shift, bits, totals, status, ticket,
                  a.buf.counters + kCntError, wtable);
   return hipGetLastError();

@@ -382,7 +382,7 @@ constexpr int kSegLdsTables = 256;
 constexpr int kMaxDim = 1024;
 
 // Tile sizes shared by the planner (workspace sizing) and the kernels.
-constexpr int kRleTile = 4096;
+constexpr int kRleTile = 8192;
 // Sorted positions per window of the bucket-local sort: a window takes the
 // buckets of the high digit that start inside it.
 constexpr int kBucketWindow = 2048;

@@ -25,7 +25,7 @@
 //               global stores are coalesced.  Up to 8-bit digits: 256 threads
 //               per tile; 9-10 bits: 1024 threads, so that every thread still
 //               looks back for one digit.
-//   RLE         one kernel: run heads of a 4096-key tile, a look-back over
+//   RLE         one kernel: run heads of an 8192-key tile, a look-back over
 //               the head counts of earlier tiles, then unique ids and run
 //               starts.  The number of runs U stays on the device.
 //
@@ -473,8 +473,8 @@ __device__ uint32_t lookback_wave(uint32_t* status, int tile, uint32_t* err) {
   }
 }
 
-// Run heads of a 4096-key tile (staged in LDS with the key before it), 1024
-// threads per tile; each thread owns 4 consecutive positions so run ids
+// Run heads of an 8192-key tile (staged in LDS with the key before it), 1024
+// threads per tile; each thread owns 8 consecutive positions so run ids
 // follow position order.
 __global__ __launch_bounds__(1024) void rle_kernel(const uint32_t* __restrict__ keys,
                                                      const uint32_t* __restrict__ vals, int64_t n,

@@ -700,8 +700,87 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(7))) voi
   short_runs<ST, VE, NCH, REC, PT>(a, sorted_vals, blockIdx.x, gridDim.x);
 }
 
-// One workgroup per long run: its chunk partials are added up and the row
-// is updated.  The workgroup's 256/Gs lane groups take the partials in a
+// Long runs of at most this many chunks (one round of partial loads in
+// flight) are finished by one lane group each; longer ones by a whole
+// workgroup, whose groups load their partials side by side (with up to 16
+// chunks per group, workload 2's finish took 8.4 us against 4.8).
+constexpr uint32_t kFinGroupChunks = 4;
+
+// A long run finished by one lane group: each lane adds its columns of the
+// run's chunk partials in chunk order (fp64), the group reduces the squared
+// norm with shuffles, and the row is updated.  Called by the whole group.
+template <int ST, int VE, int NCH>
+__device__ __forceinline__ void finish_long_in_group(const BackwardLaunch& a,
+                                                     const TableMeta* s_meta, const uint4& L,
+                                                     uint32_t key, int Gs, int gl) {
+  constexpr int kU = VE * NCH >= 16 ? 1 : 4;  // partial rows in flight
+  const TableMeta m = meta_of(a, s_meta, table_of_key(a, s_meta, key));
+  const int D = m.dim, C = D / VE;
+  const int64_t row0 = m.woff + static_cast<int64_t>(key - static_cast<uint32_t>(m.roff)) * D;
+  float w[NCH][VE];
+#pragma unroll
+  for (int q = 0; q < NCH; ++q)
+    if (q * Gs + gl < C) load_widen<ST, VE>(a.weights, row0 + (q * Gs + gl) * VE, w[q]);
+  const float m_old = a.adagrad ? a.state[key] : 0.0f;
+  double acc[NCH][VE];
+#pragma unroll
+  for (int q = 0; q < NCH; ++q)
+#pragma unroll
+    for (int e = 0; e < VE; ++e) acc[q][e] = 0.0;
+  for (uint32_t c0 = 0; c0 < L.w; c0 += kU) {
+    float v[kU][NCH][VE];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const uint32_t c = c0 + u;
+      const float* row = a.buf.partial1 + static_cast<int64_t>(L.z + c) * a.pstride;
+#pragma unroll
+      for (int q = 0; q < NCH; ++q) {
+        const int chunk = q * Gs + gl;
+        if (c < L.w && chunk < C) {
+          if constexpr (VE == 4) {
+            const float4 x = *reinterpret_cast<const float4*>(row + chunk * 4);
+            v[u][q][0] = x.x; v[u][q][1] = x.y; v[u][q][2] = x.z; v[u][q][3] = x.w;
+          } else {
+#pragma unroll
+            for (int e = 0; e < VE; ++e) v[u][q][e] = row[chunk * VE + e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < VE; ++e) v[u][q][e] = 0.0f;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int q = 0; q < NCH; ++q)
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc[q][e] += static_cast<double>(v[u][q][e]);
+  }
+  float step = a.lr;
+  if (a.adagrad) {
+    double ss = 0.0;
+#pragma unroll
+    for (int q = 0; q < NCH; ++q)
+#pragma unroll
+      for (int e = 0; e < VE; ++e) ss = fma(acc[q][e], acc[q][e], ss);
+    for (int o = Gs >> 1; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, kWave);
+    const float mnew = static_cast<float>(static_cast<double>(m_old) + ss / D);
+    if (gl == 0) a.state[key] = mnew;
+    step = a.lr / (sqrtf(mnew) + a.eps);
+  }
+#pragma unroll
+  for (int q = 0; q < NCH; ++q) {
+    if (q * Gs + gl < C) {
+#pragma unroll
+      for (int e = 0; e < VE; ++e) w[q][e] = fmaf(-step, static_cast<float>(acc[q][e]), w[q][e]);
+      narrow_store<ST, VE>(a.weights, row0 + (q * Gs + gl) * VE, w[q]);
+    }
+  }
+}
+
+// Long runs of more chunks: one workgroup per long run: its chunk partials
+// are added up and the row is updated.  The workgroup's 256/Gs lane groups take the partials in a
 // fixed interleaving (group j: chunks j, j + 256/Gs, ...), each summing in
 // fp64 in chunk order, and the groups' sums are then added in group order, so
 // the result does not depend on scheduling.  The row to update and its state
@@ -722,8 +801,26 @@ __global__ __launch_bounds__(kBlock) void seg_finalize(BackwardLaunch a) {
   const int g = tid >> a.gshift, gl = tid & (Gs - 1);
   const int row_elems = Gs * NV;
   const uint32_t n = a.buf.counters[kCntLong];
+  {
+    // runs of few chunks: one lane group each (the loop runs the same number
+    // of times on every lane of a wave).  Groups are numbered from the last
+    // workgroup down, so that the workgroups finishing the longer runs below
+    // (from the first up) do not also take these first.
+    const GroupIds id = group_ids(a, gridDim.x - 1 - blockIdx.x, gridDim.x);
+    const uint32_t wave_first = id.gid - static_cast<uint32_t>(lane_id() >> a.gshift);
+    uint32_t r = id.gid;
+    for (uint32_t rb = wave_first; rb < n; rb += id.ngroups, r += id.ngroups) {
+      if (r < n) {
+        const uint4 L = a.buf.longs[r];
+        const uint32_t key = a.buf.long_keys[r];
+        if (L.w <= kFinGroupChunks)  // the same on every lane of the group
+          finish_long_in_group<ST, VE, NCH>(a, s_meta, L, key, id.g.Gs, id.g.gl);
+      }
+    }
+  }
   for (uint32_t li = blockIdx.x; li < n; li += gridDim.x) {
     const uint4 L = a.buf.longs[li];  // {first position, length, first partial, chunks}
+    if (L.w <= kFinGroupChunks) continue;  // finished above (the same on every thread)
     const uint32_t key = a.buf.long_keys[li];
     const TableMeta m = meta_of(a, s_meta, table_of_key(a, s_meta, key));
     const int D = m.dim, C = D / VE;

@@ -67,9 +67,9 @@ __global__ __launch_bounds__(kBlock) void init_workspace(uint32_t* words, int64_
 
 // K lookups in flight per thread: 2 when a tile holds more lookups than the
 // workgroup has threads, else 1 (short bags would leave half the slots idle).
-template <typename IT, int K>
+template <typename IT, int K, int BAGS>
 __global__ __launch_bounds__(kLinThreads) void linearize_kernel(BackwardLaunch a) {
-  linearize_tiles<IT, kLinThreads, K>(a, blockIdx.x, gridDim.x);
+  linearize_tiles<IT, kLinThreads, K, BAGS>(a, blockIdx.x, gridDim.x);
 }
 
 // Counts of digits d0 .. d0 + DPT - 1 in all tiles before `tile` (decoupled
@@ -957,7 +957,8 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
 // Larger batches use 8192-key tiles: a tile's keys spread over every bucket of
 // an 8-bit digit, and 32 keys per bucket make the scatter write whole 128-byte
 // lines (16-key tiles left half lines shared with the next tile, usually on
-// another XCD: workload 5's first pass took 323 us against 138 us).
+// another XCD: the first pass over 16.8 M uniform 16-bit ids took 323 us
+// against 138 us).
 int sort_keys_per_thread(int64_t n) { return n <= (int64_t{1} << 20) ? 8 : 32; }
 int sort_tile_keys(int64_t n, int key_bits) {
   return radix_digit_bits(key_bits, n) > 8 ? 4096 : kBlock * sort_keys_per_thread(n);
@@ -980,28 +981,36 @@ hipError_t launch_linearize(const BackwardLaunch& a, hipStream_t stream, const K
   return launch_linearize_kernel(a, stream, kt);
 }
 
-hipError_t launch_linearize_kernel(const BackwardLaunch& a, hipStream_t stream,
-                                   const KernelTimer* kt) {
-  if (a.num_bags <= 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>(linearize_blocks(a.num_bags)));
-  const int64_t tiles = (a.num_bags + kLinBags - 1) / kLinBags;
+template <int BAGS>
+hipError_t launch_linearize_bags(const BackwardLaunch& a, hipStream_t stream,
+                                 const KernelTimer* kt) {
+  const dim3 grid(static_cast<unsigned>(linearize_blocks(a.num_bags, BAGS)));
+  const int64_t tiles = (a.num_bags + BAGS - 1) / BAGS;
   const bool deep = a.num_indices > tiles * kLinThreads;
   if (a.index64) {
     if (deep)
-      launch_timed(kt, "linearize_kernel", linearize_kernel<int64_t, 2>, grid, dim3(kLinThreads),
-                   0, stream, a);
+      launch_timed(kt, "linearize_kernel", linearize_kernel<int64_t, 2, BAGS>, grid,
+                   dim3(kLinThreads), 0, stream, a);
     else
-      launch_timed(kt, "linearize_kernel", linearize_kernel<int64_t, 1>, grid, dim3(kLinThreads),
-                   0, stream, a);
+      launch_timed(kt, "linearize_kernel", linearize_kernel<int64_t, 1, BAGS>, grid,
+                   dim3(kLinThreads), 0, stream, a);
   } else {
     if (deep)
-      launch_timed(kt, "linearize_kernel", linearize_kernel<int32_t, 2>, grid, dim3(kLinThreads),
-                   0, stream, a);
+      launch_timed(kt, "linearize_kernel", linearize_kernel<int32_t, 2, BAGS>, grid,
+                   dim3(kLinThreads), 0, stream, a);
     else
-      launch_timed(kt, "linearize_kernel", linearize_kernel<int32_t, 1>, grid, dim3(kLinThreads),
-                   0, stream, a);
+      launch_timed(kt, "linearize_kernel", linearize_kernel<int32_t, 1, BAGS>, grid,
+                   dim3(kLinThreads), 0, stream, a);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_linearize_kernel(const BackwardLaunch& a, hipStream_t stream,
+                                   const KernelTimer* kt) {
+  if (a.num_bags <= 0) return hipSuccess;
+  return a.num_bags > int64_t{kLinBags} * kLinMaxBlocks
+             ? launch_linearize_bags<kLinBagsLarge>(a, stream, kt)
+             : launch_linearize_bags<kLinBags>(a, stream, kt);
 }
 
 // One look-back pass over keys/values (kin, vin) -> (kout, vout) on the digit

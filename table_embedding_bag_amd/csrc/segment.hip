@@ -901,14 +901,22 @@ __global__ __launch_bounds__(kBlock) void seg_finalize(BackwardLaunch a) {
   }
 }
 
-// Upper bound of concurrently useful workgroups for the grid-stride kernels.
-constexpr int64_t kMaxSegBlocks = 4096;
+// Grid bounds of seg_fused.  Large batches take more workgroups than fit at
+// once, so that the dispatcher keeps refilling the chip as workgroups with few
+// items finish (5.2 M lookups: 570 -> 485 us against 4096; 32768 was slower
+// again); batches of at most 2^20 lookups are faster with 4096 (0.7 us at
+// 270k lookups).
+constexpr int64_t kMaxSegBlocks = 16384;
+constexpr int64_t kMaxSegBlocksSmall = 4096;
+// Grid bound of seg_finalize (a larger grid slowed the finish of many short
+// long runs: 16.8 M lookups in 39k long runs, 35 -> 48 us at 32768).
+constexpr int64_t kMaxFinBlocks = 4096;
 
-int64_t blocks_for(int64_t items, int gshift) {
+int64_t blocks_for(int64_t items, int gshift, int64_t cap) {
   const int64_t per_block = static_cast<int64_t>(kWavesPerBlock) * (kWave >> gshift);
   int64_t b = (items + per_block - 1) / per_block;
   if (b < 1) b = 1;
-  return b < kMaxSegBlocks ? b : kMaxSegBlocks;
+  return b < cap ? b : cap;
 }
 
 template <int ST, int VE, int NCH, bool REC>
@@ -924,15 +932,16 @@ hipError_t run_segments(const BackwardLaunch& a, const uint32_t* keys, const uin
   }
   if (a.per_table)
     launch_timed(kt, "table_run_starts", table_run_starts, dim3(a.T + 1), dim3(kBlock), 0, s, a);
-  int64_t blocks = blocks_for(n, a.gshift);
-  if (ub.items1 > blocks) blocks = ub.items1 < kMaxSegBlocks ? ub.items1 : kMaxSegBlocks;
+  const int64_t cap = n > (int64_t{1} << 20) ? kMaxSegBlocks : kMaxSegBlocksSmall;
+  int64_t blocks = blocks_for(n, a.gshift, cap);
+  if (ub.items1 > blocks) blocks = ub.items1 < cap ? ub.items1 : cap;
   if (a.per_table)
     launch_timed(kt, "seg_fused", seg_fused<ST, VE, NCH, REC, true>, dim3(blocks), dim3(kBlock),
                  0, s, a, keys, sorted_vals);
   else
     launch_timed(kt, "seg_fused", seg_fused<ST, VE, NCH, REC, false>, dim3(blocks), dim3(kBlock),
                  0, s, a, keys, sorted_vals);
-  const int64_t fin = ub.longs < kMaxSegBlocks ? ub.longs : kMaxSegBlocks;
+  const int64_t fin = ub.longs < kMaxFinBlocks ? ub.longs : kMaxFinBlocks;
   launch_timed(kt, "seg_finalize", seg_finalize<ST, VE, NCH, REC>, dim3(fin), dim3(kBlock), 0, s,
                a);
   return hipGetLastError();

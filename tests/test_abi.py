@@ -20,6 +20,16 @@ def test_header_and_binding_agree():
     assert _declared() == sorted(tbe.EXPORTED_SYMBOLS)
 
 
+def test_header_constants_match_the_binding():
+    """Every TBE_FLAG_* / TBE_OPTION_* value the header defines is the binding's constant of
+    the same name (a mismatch would pass the wrong option or flag through the ABI)."""
+    src = open(os.path.join(ROOT, "include", "tbe.h")).read()
+    found = re.findall(r"\bTBE_((?:FLAG|OPTION)_\w+)\s*=\s*(\d+)u?", src)
+    assert found
+    for name, value in found:
+        assert getattr(tbe, name) == int(value), name
+
+
 def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(tbe.library_path())
     for name in _declared():

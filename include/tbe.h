@@ -107,7 +107,16 @@ enum {
    * multiple of 16, rows 16-byte aligned in the flat weights.  Source:
    * kimbodo.com/?p=28372, "What Happened" (small tables that qualify use a
    * histogram and tensor-core path). */
-  TBE_FLAG_HISTOGRAM = 8u
+  TBE_FLAG_HISTOGRAM = 8u,
+  /* Skew balancing (off by default): a bag of more than 2048 lookups pools its
+   * first 2048 in the forward's own pass and its other 2048-lookup segments
+   * in parallel waves, whose sums are then added to the bag's output in
+   * segment order (deterministic; the fp32 rounding order differs from the
+   * unsplit sum).  The handle allocates a scratch for the segment sums at
+   * creation (about 64 MB); a call whose lookups could need more segments
+   * than it holds pools its bags unsplit.  Source: kimbodo.com/?p=28372,
+   * "Kimbodo Engineering Perspective" (load imbalance across lookups). */
+  TBE_FLAG_SPLIT_BAGS = 16u
 };
 
 typedef struct {

@@ -23,6 +23,7 @@ __all__ = [
     "tbe_status_string", "tbe_abi_version", "TBE",
     "F32", "F16", "BF16", "POOL_SUM", "POOL_MEAN", "OPT_SGD", "OPT_ROWWISE_ADAGRAD",
     "FLAG_VALIDATE", "FLAG_NO_HISTOGRAM", "FLAG_FORCE_HISTOGRAM", "FLAG_HISTOGRAM",
+    "FLAG_SPLIT_BAGS",
     "OPTION_LONG_RUN_THRESHOLD", "OPTION_PROFILE", "OPTION_SORT", "EXPORTED_SYMBOLS",
 ]
 
@@ -31,6 +32,7 @@ I32, I64 = 0, 1
 POOL_SUM, POOL_MEAN = 0, 1
 OPT_SGD, OPT_ROWWISE_ADAGRAD = 0, 1
 FLAG_VALIDATE, FLAG_NO_HISTOGRAM, FLAG_FORCE_HISTOGRAM, FLAG_HISTOGRAM = 1, 2, 4, 8
+FLAG_SPLIT_BAGS = 16
 OPTION_LONG_RUN_THRESHOLD, OPTION_PROFILE, OPTION_SORT = 1, 2, 3
 
 STATUS = {

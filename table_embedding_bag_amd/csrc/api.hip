@@ -44,6 +44,11 @@ struct tbe_handle {
   int64_t wt_elems = 0;
   int64_t long_threshold = 256;
   bool bucket_sort = true;  // TBE_OPTION_SORT
+  // TBE_FLAG_SPLIT_BAGS scratch: counters, segment list, split-bag list and
+  // segment sums for at most split_cap segments of split_pstride floats
+  char* split = nullptr;
+  int64_t split_cap = 0;
+  int32_t split_pstride = 0;
   // whether the last tbe_forward_group's run-length encoding queued the longer
   // runs (its tbe_backward_update_grouped must not queue them again)
   bool grouped_queued = false;
@@ -173,6 +178,17 @@ struct Carve {
     return o;
   }
 };
+
+// Skew balancing (TBE_FLAG_SPLIT_BAGS): bags longer than kSplitLen lookups
+// are pooled in segments of kSplitLen.
+constexpr int32_t kSplitLen = 2048;
+constexpr int64_t kSplitMaxSegments = 65536;
+constexpr int64_t kSplitScratchBytes = int64_t{64} << 20;
+
+// Scratch layout: counters (256 bytes), segment list, split-bag list, sums.
+size_t split_bytes(int64_t cap, int32_t pstride) {
+  return 256 + static_cast<size_t>(cap) * (8 + 16 + 4 * static_cast<size_t>(pstride));
+}
 
 struct BwdPlan {
   int64_t n = 0;
@@ -401,7 +417,7 @@ tbe_status tbe_create(const tbe_config* cfg, void* weights, float* optim_state, 
   if (cfg->optimizer != TBE_OPT_SGD && cfg->optimizer != TBE_OPT_ROWWISE_ADAGRAD)
     return TBE_ERR_INVALID_ARGUMENT;
   if (cfg->optimizer == TBE_OPT_ROWWISE_ADAGRAD && !optim_state) return TBE_ERR_INVALID_ARGUMENT;
-  if (cfg->flags & ~15u) return TBE_ERR_INVALID_ARGUMENT;
+  if (cfg->flags & ~31u) return TBE_ERR_INVALID_ARGUMENT;
   if ((cfg->flags & TBE_FLAG_NO_HISTOGRAM) &&
       (cfg->flags & (TBE_FLAG_FORCE_HISTOGRAM | TBE_FLAG_HISTOGRAM)))
     return TBE_ERR_INVALID_ARGUMENT;
@@ -530,6 +546,19 @@ tbe_status tbe_create(const tbe_config* cfg, void* weights, float* optim_state, 
     delete h;
     return TBE_ERR_OUT_OF_MEMORY;
   }
+  if (h->flags & TBE_FLAG_SPLIT_BAGS) {
+    h->split_pstride = (h->dmax + 3) / 4 * 4;
+    h->split_cap = std::min<int64_t>(kSplitMaxSegments,
+                                     kSplitScratchBytes / (4 * int64_t{h->split_pstride})) /
+                   16 * 16;  // keeps the 16-byte split-bag records aligned
+    if (hipMalloc(reinterpret_cast<void**>(&h->split), split_bytes(h->split_cap, h->split_pstride)) !=
+        hipSuccess) {
+      if (h->wt) (void)hipFree(h->wt);
+      (void)hipFree(block);
+      delete h;
+      return TBE_ERR_OUT_OF_MEMORY;
+    }
+  }
   *out = h;
   return TBE_OK;
 }
@@ -539,6 +568,7 @@ void tbe_destroy(tbe_handle* h) {
   for (auto& e : h->pool) (void)hipEventDestroy(e);
   if (h->meta) (void)hipFree(h->meta);
   if (h->wt) (void)hipFree(h->wt);
+  if (h->split) (void)hipFree(h->split);
   delete h;
 }
 
@@ -657,8 +687,21 @@ tbe_status forward_impl(tbe_handle* h, int32_t B, const void* indices, const voi
     a.dtype = h->dtype;
     a.index64 = index_dtype == TBE_I64;
     a.vec = h->fwd_vec;
-    const hipError_t e =
+    // bags split only when every possible segment fits the scratch (at most
+    // n / kSplitLen segments after the first ones)
+    const bool split = h->split && n > kSplitLen && n / kSplitLen + 1 <= h->split_cap;
+    if (split) {
+      a.split_len = kSplitLen;
+      a.split_ctr = reinterpret_cast<uint32_t*>(h->split);
+      a.split_seg = reinterpret_cast<uint2*>(h->split + 256);
+      a.split_long = reinterpret_cast<uint4*>(h->split + 256 + 8 * h->split_cap);
+      a.split_part = reinterpret_cast<float*>(h->split + 256 + 24 * h->split_cap);
+      a.split_pstride = h->split_pstride;
+      hipLaunchKernelGGL(fill_u32, dim3(1), dim3(64), 0, s, a.split_ctr, 0u, int64_t{2});
+    }
+    hipError_t e =
         fuse ? launch_forward_linearize(a, *fuse, s, kt) : launch_forward_gather(a, s, kt);
+    if (e == hipSuccess && split) e = launch_forward_split(a, n, s, kt);
     return from_hip(e);
   } catch (...) {
     return TBE_ERR_OUT_OF_MEMORY;

@@ -208,7 +208,20 @@ struct ForwardLaunch {
   int32_t index64;          // indices/offsets are int64
   int32_t vec;              // 16-byte row chunks (else one element per lane)
   const int32_t* table_list;  // tables to cover (T entries), or null for tables 0..T-1
+  // Bags longer than split_len lookups (0: none) pool only their first
+  // split_len lookups here; the rest is queued as segments of split_len for
+  // launch_forward_split (host-checked: the segments always fit).
+  int32_t split_len;
+  uint32_t* split_ctr;      // [2]: segments queued, long bags queued (zeroed per call)
+  uint2* split_seg;         // {bag, segment index >= 1}
+  uint4* split_long;        // {bag, first segment slot, segments, 0}
+  float* split_part;        // [segments][split_pstride] scaled segment sums
+  int32_t split_pstride;
 };
+// Segment sums of the bags split by the pooled lookup, then their addition to
+// the output in segment order.
+hipError_t launch_forward_split(const ForwardLaunch& a, int64_t num_indices, hipStream_t stream,
+                                const KernelTimer* kt);
 hipError_t launch_forward_gather(const ForwardLaunch& a, hipStream_t stream,
                                  const KernelTimer* kt);
 // dL/dp_i for every lookup (a.table_list must be null: all tables).

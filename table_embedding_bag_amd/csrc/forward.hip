@@ -80,6 +80,20 @@ __device__ __forceinline__ void fwd_tile(const ForwardLaunch& a, int logical, in
   float scale = 1.0f;
   if (a.mean) scale = (end > start) ? 1.0f / static_cast<float>(end - start) : 0.0f;
   float* orow = a.out + static_cast<int64_t>(b) * a.sum_dims + m.doff;
+  if (a.split_len > 0 && end - start > a.split_len) {  // the same on the bag's sub-wave
+    // a long bag: this sub-wave pools its first split_len lookups and its
+    // first lane queues the other segments (slots always fit: host-checked)
+    if (sl == 0) {
+      const int64_t L = end - start;
+      const uint32_t nseg = static_cast<uint32_t>((L - 1) / a.split_len);  // segments after the first
+      const uint32_t base = atomicAdd(&a.split_ctr[0], nseg);
+      const uint32_t li = atomicAdd(&a.split_ctr[1], 1u);
+      a.split_long[li] = make_uint4(static_cast<uint32_t>(k), base, nseg, 0u);
+      for (uint32_t j = 0; j < nseg; ++j)
+        a.split_seg[base + j] = make_uint2(static_cast<uint32_t>(k), j + 1);
+    }
+    end = start + a.split_len;
+  }
 
   for (int cb = 0; cb < C; cb += Gs) {
     const int chunk = cb + gl;
@@ -147,6 +161,102 @@ __device__ __forceinline__ void fwd_tile(const ForwardLaunch& a, int logical, in
 template <int ST, typename IT, bool VEC, bool PSW>
 __global__ __launch_bounds__(kBlock) void fwd_gather_pool(ForwardLaunch a) {
   fwd_tile<ST, IT, VEC, PSW>(a, xcd_contiguous_block(blockIdx.x, gridDim.x), threadIdx.x >> 6);
+}
+
+// Segments of split bags (skew balancing: kimbodo.com/?p=28372, "Kimbodo
+// Engineering Perspective", names load imbalance across lookups as a risk):
+// one wave per queued segment pools its up to split_len lookups with lane
+// groups as the pooled lookup does and writes the scaled sum.
+template <int ST, typename IT, bool VEC, bool PSW>
+__global__ __launch_bounds__(kBlock) void fwd_split_segments(ForwardLaunch a) {
+  constexpr int SB = StorageTraits<ST>::bytes;
+  constexpr int VE = VEC ? 16 / SB : 1;
+  const uint32_t nseg = a.split_ctr[0];
+  const int lane = lane_id();
+  for (uint32_t si = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6); si < nseg;
+       si += gridDim.x * kWavesPerBlock) {
+    const uint2 sd = a.split_seg[si];
+    const int64_t k = sd.x;
+    const int t = static_cast<int>(k / a.B);
+    const TableMeta m = a.meta[t];
+    const int gshift = m.fwd_gshift;
+    const int Gs = 1 << gshift, R = kWave >> gshift;
+    const int g = lane >> gshift, gl = lane & (Gs - 1);
+    const int64_t b0 = ld_index<IT>(a.offsets, k), b1 = ld_index<IT>(a.offsets, k + 1);
+    const int64_t start = b0 + static_cast<int64_t>(sd.y) * a.split_len;
+    const int64_t end = min(b1, start + a.split_len);
+    const float scale = a.mean ? 1.0f / static_cast<float>(b1 - b0) : 1.0f;
+    const int D = m.dim;
+    const int C = VEC ? D / VE : D;
+    const void* wbase = static_cast<const char*>(a.weights) + m.woff * SB;
+    float* dst_row = a.split_part + static_cast<int64_t>(si) * a.split_pstride;
+    for (int cb = 0; cb < C; cb += Gs) {
+      const int chunk = cb + gl;
+      const bool lane_ok = chunk < C;
+      float acc[VE];
+#pragma unroll
+      for (int e = 0; e < VE; ++e) acc[e] = 0.0f;
+      for (int64_t j0 = start; j0 < end; j0 += kWave) {
+        const int n = static_cast<int>(min(static_cast<int64_t>(kWave), end - j0));
+        int my_row = 0;
+        float my_p = 1.0f;
+        if (lane < n) {
+          my_row = static_cast<int>(ld_index<IT>(a.indices, j0 + lane));
+          if constexpr (PSW) my_p = a.psw[j0 + lane];
+        }
+        for (int r = 0; r < n; r += R * kUnroll) {
+          float v[kUnroll][VE];
+          float p[kUnroll];
+#pragma unroll
+          for (int u = 0; u < kUnroll; ++u) {
+            const int jj = r + u * R + g;
+            const int src = min(jj, kWave - 1);
+            const int row = __shfl(my_row, src, kWave);
+            p[u] = PSW ? __shfl(my_p, src, kWave) : 1.0f;
+            if (jj < n && lane_ok) {
+              load_widen<ST, VE>(wbase, static_cast<int64_t>(row) * D + chunk * VE, v[u]);
+            } else {
+#pragma unroll
+              for (int e = 0; e < VE; ++e) v[u][e] = 0.0f;
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+            for (int e = 0; e < VE; ++e) acc[e] = PSW ? fmaf(p[u], v[u][e], acc[e]) : acc[e] + v[u][e];
+        }
+      }
+      for (int o = kWave >> 1; o >= Gs; o >>= 1) {
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc[e] += __shfl_xor(acc[e], o, kWave);
+      }
+      if (g == 0 && lane_ok) {
+#pragma unroll
+        for (int e = 0; e < VE; ++e) dst_row[chunk * VE + e] = acc[e] * scale;
+      }
+    }
+  }
+}
+
+// Adds each split bag's segment sums to its output row, in segment order (the
+// result does not depend on scheduling).  One wave per split bag.
+__global__ __launch_bounds__(kBlock) void fwd_split_combine(ForwardLaunch a) {
+  const uint32_t nlong = a.split_ctr[1];
+  for (uint32_t li = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6); li < nlong;
+       li += gridDim.x * kWavesPerBlock) {
+    const uint4 L = a.split_long[li];  // {bag, first segment slot, segments, 0}
+    const int64_t k = L.x;
+    const int t = static_cast<int>(k / a.B);
+    const int64_t b = k - static_cast<int64_t>(t) * a.B;
+    const TableMeta m = a.meta[t];
+    float* orow = a.out + b * a.sum_dims + m.doff;
+    for (int d = lane_id(); d < m.dim; d += kWave) {
+      float y = orow[d];
+      for (uint32_t j = 0; j < L.z; ++j)
+        y += a.split_part[static_cast<int64_t>(L.y + j) * a.split_pstride + d];
+      orow[d] = y;
+    }
+  }
 }
 
 // The pooled lookup and the linearize step of the backward's grouping in one
@@ -387,6 +497,52 @@ hipError_t launch_forward_gather(const ForwardLaunch& a, hipStream_t stream,
     case kBF16: return dispatch_index<kBF16>(a, stream, grid, kt);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <int ST, typename IT>
+void launch_split_segments(const ForwardLaunch& a, hipStream_t s, dim3 grid,
+                           const KernelTimer* kt) {
+  if (a.vec) {
+    if (a.psw)
+      launch_timed(kt, "fwd_split_segments", fwd_split_segments<ST, IT, true, true>, grid,
+                   dim3(kBlock), 0, s, a);
+    else
+      launch_timed(kt, "fwd_split_segments", fwd_split_segments<ST, IT, true, false>, grid,
+                   dim3(kBlock), 0, s, a);
+  } else {
+    if (a.psw)
+      launch_timed(kt, "fwd_split_segments", fwd_split_segments<ST, IT, false, true>, grid,
+                   dim3(kBlock), 0, s, a);
+    else
+      launch_timed(kt, "fwd_split_segments", fwd_split_segments<ST, IT, false, false>, grid,
+                   dim3(kBlock), 0, s, a);
+  }
+}
+
+template <int ST>
+void launch_split_index(const ForwardLaunch& a, hipStream_t s, dim3 grid, const KernelTimer* kt) {
+  if (a.index64)
+    launch_split_segments<ST, int64_t>(a, s, grid, kt);
+  else
+    launch_split_segments<ST, int32_t>(a, s, grid, kt);
+}
+
+hipError_t launch_forward_split(const ForwardLaunch& a, int64_t num_indices, hipStream_t stream,
+                                const KernelTimer* kt) {
+  // at most num_indices / split_len segments after the first ones, and as
+  // many split bags
+  const int64_t segs = num_indices / a.split_len + 1;
+  int64_t blocks = (segs + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (blocks > 4096) blocks = 4096;
+  const dim3 grid(static_cast<unsigned>(blocks));
+  switch (a.dtype) {
+    case kF32: launch_split_index<kF32>(a, stream, grid, kt); break;
+    case kF16: launch_split_index<kF16>(a, stream, grid, kt); break;
+    case kBF16: launch_split_index<kBF16>(a, stream, grid, kt); break;
+    default: return hipErrorInvalidValue;
+  }
+  launch_timed(kt, "fwd_split_combine", fwd_split_combine, grid, dim3(kBlock), 0, stream, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_forward_linearize(const ForwardLaunch& f, const BackwardLaunch& b,

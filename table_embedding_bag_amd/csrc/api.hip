@@ -181,8 +181,8 @@ struct Carve {
 
 // Skew balancing (TBE_FLAG_SPLIT_BAGS): bags longer than kSplitLen lookups
 // are pooled in segments of kSplitLen.
-constexpr int32_t kSplitLen = 2048;
-constexpr int64_t kSplitMaxSegments = 65536;
+constexpr int32_t kSplitLen = 256;
+constexpr int64_t kSplitMaxSegments = int64_t{1} << 18;
 constexpr int64_t kSplitScratchBytes = int64_t{64} << 20;
 
 // Scratch layout: counters (256 bytes), segment list, split-bag list, sums.

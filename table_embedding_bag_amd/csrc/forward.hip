@@ -240,6 +240,7 @@ __global__ __launch_bounds__(kBlock) void fwd_split_segments(ForwardLaunch a) {
 
 // Adds each split bag's segment sums to its output row, in segment order (the
 // result does not depend on scheduling).  One wave per split bag.
+constexpr int kCombineBatch = 16;
 __global__ __launch_bounds__(kBlock) void fwd_split_combine(ForwardLaunch a) {
   const uint32_t nlong = a.split_ctr[1];
   for (uint32_t li = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6); li < nlong;
@@ -250,10 +251,20 @@ __global__ __launch_bounds__(kBlock) void fwd_split_combine(ForwardLaunch a) {
     const int64_t b = k - static_cast<int64_t>(t) * a.B;
     const TableMeta m = a.meta[t];
     float* orow = a.out + b * a.sum_dims + m.doff;
+    const int64_t ps = a.split_pstride;
     for (int d = lane_id(); d < m.dim; d += kWave) {
+      const float* p = a.split_part + static_cast<int64_t>(L.y) * ps + d;
       float y = orow[d];
-      for (uint32_t j = 0; j < L.z; ++j)
-        y += a.split_part[static_cast<int64_t>(L.y + j) * a.split_pstride + d];
+      uint32_t j = 0;
+      // kCombineBatch loads in flight, then added in segment order
+      for (; j + kCombineBatch <= L.z; j += kCombineBatch) {
+        float v[kCombineBatch];
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u) v[u] = p[static_cast<int64_t>(j + u) * ps];
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u) y += v[u];
+      }
+      for (; j < L.z; ++j) y += p[static_cast<int64_t>(j) * ps];
       orow[d] = y;
     }
   }

@@ -244,7 +244,8 @@ bool plan_backward(const tbe_handle* h, int64_t n, bool vec, BwdPlan* p) {
   p->chunks_ub = ub.chunks;
   p->items1_ub = ub.items1;
   p->zero_words = kNumCounters + kNumTickets + int64_t{p->passes} * p->slots +
-                  int64_t{p->passes} * p->sort_tiles * p->slots + p->rle_tiles;
+                  int64_t{p->passes} * p->sort_tiles * p->slots + p->rle_tiles +
+                  p->chunks_ub / kFinPiece + 1;
   Carve cv;
   for (int i = 0; i < 2; ++i) {
     p->o_keys[i] = cv.take(4 * static_cast<size_t>(n));
@@ -322,6 +323,7 @@ void fill_backward(const tbe_handle* h, int32_t B, const void* indices, const vo
   b.digit_hist = b.tickets + kNumTickets;
   b.sort_status = b.digit_hist + p.passes * p.slots;
   b.rle_status = b.sort_status + static_cast<int64_t>(p.passes) * p.sort_tiles * p.slots;
+  b.piece_tickets = b.rle_status + p.rle_tiles;
   b.zero_words = p.zero_words;
   b.unique_keys = reinterpret_cast<uint32_t*>(w + p.o_uniq);
   b.run_start = reinterpret_cast<uint32_t*>(w + p.o_start);

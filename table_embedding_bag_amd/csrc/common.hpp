@@ -264,13 +264,16 @@ struct BackwardBuffers {
   uint2* rec;               // per lookup {bag, coefficient bits} when needed, else null
   // One contiguous region zeroed at the start of every backward call:
   //   counters [kNumCounters], tickets [kNumTickets], digit_hist [passes][slots],
-  //   sort_status [passes][sort tiles][slots], rle_status [rle tiles]
+  //   sort_status [passes][sort tiles][slots], rle_status [rle tiles],
+  //   piece_tickets [chunks cap / kFinPiece + 1]
   // (slots = radix_slots(digit bits))
   uint32_t* counters;
   uint32_t* tickets;        // tile tickets: one per radix pass, then the RLE's
   uint32_t* digit_hist;     // digit counts of every radix pass
   uint32_t* sort_status;    // look-back status words of the radix passes
   uint32_t* rle_status;     // look-back status words of the RLE
+  uint32_t* piece_tickets;  // finished chunks of each piece of a very long run, by the piece's
+                            // first partial slot / kFinPiece (reset by the piece's last chunk)
   int64_t zero_words;       // size of the zeroed region, in 32-bit words
   uint32_t* unique_keys;    // [N]
   uint32_t* run_start;      // [N + 1]
@@ -289,6 +292,14 @@ struct BackwardBuffers {
 // gives up (results then invalid).
 enum { kCntUnique = 0, kCntLong = 32, kCntItems1 = 64, kCntChunks = 96, kCntError = 128,
        kNumCounters = 160 };
+
+// A long run of at least kFinPieceMin chunks has its chunk partials added in
+// pieces of kFinPiece chunks (the last piece takes the remainder, so every
+// piece has at least kFinPiece); each piece's sum is left as doubles in its
+// first two partial slots.  Piece starts are thus at least kFinPiece slots
+// apart, and first slot / kFinPiece numbers them.
+constexpr uint32_t kFinPiece = 64;
+constexpr uint32_t kFinPieceMin = 2 * kFinPiece;
 
 // Workgroup items of the segment kernels: {first position, kMediumItem | length}
 // for a medium run, {long run, chunk} for a 256-lookup chunk of a long run.

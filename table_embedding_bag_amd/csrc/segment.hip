@@ -780,6 +780,96 @@ __device__ __forceinline__ void finish_long_in_group(const BackwardLaunch& a,
   }
 }
 
+// A long run of at least kFinPieceMin chunks is finished in pieces of
+// kFinPiece chunk partials (the last piece takes the remainder) by as many
+// workgroups: each adds its piece's partials in chunk order (fp64) and leaves
+// the sum, as doubles, over the piece's first two slots; the workgroup that
+// finishes the run's last piece (a ticket per run) adds the piece sums in
+// piece order and updates the row.  So a row hit hundreds of thousands of
+// times is not finished by one workgroup reading every partial, and the result
+// does not depend on which workgroup came last.  piece = {long run, piece}.
+template <int ST>
+__device__ __forceinline__ void finish_piece(const BackwardLaunch& a, const TableMeta* s_meta,
+                                             uint2 piece, double* s_sum, double* s_scratch,
+                                             uint32_t* s_last) {
+  constexpr int kBatch = 8;  // partial loads in flight per thread
+  const int tid = threadIdx.x;
+  const uint4 L = a.buf.longs[piece.x];
+  const uint32_t key = a.buf.long_keys[piece.x];
+  const TableMeta m = meta_of(a, s_meta, table_of_key(a, s_meta, key));
+  const int D = m.dim;
+  const int64_t ps = a.pstride;
+  const uint32_t np = L.w / kFinPiece;
+  const uint32_t j = piece.y;
+  const uint32_t cnt = j == np - 1 ? L.w - j * kFinPiece : kFinPiece;
+  float* first = a.buf.partial1 + static_cast<int64_t>(L.z + j * kFinPiece) * ps;
+  // H thread sets (all threads when D < kBlock): set h adds chunks h, h + H, ...
+  // in order; the sets' sums are then added in set order
+  const int H = D < kBlock ? kBlock / D : 1;
+  for (int e = tid; e < H * D; e += kBlock) {
+    const int h = e / D, d = e - h * D;
+    double x = 0.0;
+    uint32_t q = static_cast<uint32_t>(h);
+    for (; q + (kBatch - 1) * H < cnt; q += kBatch * H) {
+      float v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) v[u] = first[static_cast<int64_t>(q + u * H) * ps + d];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) x += static_cast<double>(v[u]);
+    }
+    for (; q < cnt; q += H) x += static_cast<double>(first[static_cast<int64_t>(q) * ps + d]);
+    s_sum[e] = x;
+  }
+  __syncthreads();  // every read of the first two slots is done
+  for (int d = tid; d < D; d += kBlock) {
+    double x = 0.0;
+    for (int h = 0; h < H; ++h) x += s_sum[h * D + d];
+    reinterpret_cast<double*>(first)[d] = x;
+  }
+  __threadfence();  // the piece sum is visible to the other workgroups
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t* ticket = a.buf.piece_tickets + L.z / kFinPiece;
+    const bool last = atomicAdd(ticket, 1u) == np - 1;
+    if (last) atomicExch(ticket, 0u);  // ready for the next call on this workspace
+    *s_last = last ? 1u : 0u;
+  }
+  __syncthreads();
+  if (*s_last == 0u) return;  // the same on every thread
+  __threadfence();            // the other pieces' sums are seen
+  const int64_t row0 = m.woff + static_cast<int64_t>(key - static_cast<uint32_t>(m.roff)) * D;
+  const int64_t pstep = static_cast<int64_t>(kFinPiece) * ps;
+  const double* p0 = reinterpret_cast<const double*>(a.buf.partial1 + static_cast<int64_t>(L.z) * ps);
+  double ss = 0.0;
+  for (int d = tid; d < D; d += kBlock) {
+    double x = 0.0;
+    uint32_t p = 0;
+    for (; p + kBatch <= np; p += kBatch) {
+      double v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) v[u] = p0[(p + u) * (pstep / 2) + d];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) x += v[u];
+    }
+    for (; p < np; ++p) x += p0[p * (pstep / 2) + d];
+    s_sum[d] = x;
+    ss = fma(x, x, ss);
+  }
+  float step = a.lr;
+  if (a.adagrad) {
+    ss = block_sum(ss, s_scratch);
+    const float mnew = static_cast<float>(static_cast<double>(a.state[key]) + ss / D);
+    if (tid == 0) a.state[key] = mnew;
+    step = a.lr / (sqrtf(mnew) + a.eps);
+  }
+  for (int d = tid; d < D; d += kBlock) {
+    float w;
+    load_widen<ST, 1>(a.weights, row0 + d, &w);
+    w = fmaf(-step, static_cast<float>(s_sum[d]), w);
+    narrow_store<ST, 1>(a.weights, row0 + d, &w);
+  }
+}
+
 // Long runs of more chunks: one workgroup per long run: its chunk partials
 // are added up and the row is updated.  The workgroup's 256/Gs lane groups take the partials in a
 // fixed interleaving (group j: chunks j, j + 256/Gs, ...), each summing in
@@ -803,6 +893,34 @@ __global__ __launch_bounds__(kBlock) void seg_finalize(BackwardLaunch a) {
   const int row_elems = Gs * NV;
   const uint32_t n = a.buf.counters[kCntLong];
   {
+    // the pieces of runs of at least kFinPieceMin chunks: the workgroups scan
+    // the item list for the first chunk of each piece, 256 adjacent items each
+    // (interleaving the items over the workgroups, so that a run's pieces go
+    // to different ones, was slower: 34 -> 42 us on 4.2 M lookups)
+    __shared__ uint32_t s_np, s_last;
+    __shared__ uint2 s_piece[kBlock];
+    const uint32_t nitems = a.buf.counters[kCntItems1];
+    for (uint32_t base = blockIdx.x * kBlock; base < nitems; base += gridDim.x * kBlock) {
+      if (tid == 0) s_np = 0u;
+      __syncthreads();
+      const uint32_t item = base + static_cast<uint32_t>(tid);
+      if (item < nitems) {
+        const uint2 it = a.buf.items1[item];
+        if (!(it.y & kMediumItem) && it.y % kFinPiece == 0u) {
+          const uint32_t w = a.buf.longs[it.x].w;
+          if (w >= kFinPieceMin && it.y / kFinPiece < w / kFinPiece)
+            s_piece[atomicAdd(&s_np, 1u)] = make_uint2(it.x, it.y / kFinPiece);
+        }
+      }
+      __syncthreads();
+      const uint32_t np = s_np;
+      for (uint32_t q = 0; q < np; ++q) {
+        finish_piece<ST>(a, s_meta, s_piece[q], s_red, s_scratch, &s_last);
+        __syncthreads();  // s_red, s_scratch and s_last are reused
+      }
+    }
+  }
+  {
     // runs of few chunks: one lane group each (the loop runs the same number
     // of times on every lane of a wave).  Groups are numbered from the last
     // workgroup down, so that the workgroups finishing the longer runs below
@@ -821,7 +939,8 @@ __global__ __launch_bounds__(kBlock) void seg_finalize(BackwardLaunch a) {
   }
   for (uint32_t li = blockIdx.x; li < n; li += gridDim.x) {
     const uint4 L = a.buf.longs[li];  // {first position, length, first partial, chunks}
-    if (L.w <= kFinGroupChunks) continue;  // finished above (the same on every thread)
+    // finished above (the same on every thread)
+    if (L.w <= kFinGroupChunks || L.w >= kFinPieceMin) continue;
     const uint32_t key = a.buf.long_keys[li];
     const TableMeta m = meta_of(a, s_meta, table_of_key(a, s_meta, key));
     const int D = m.dim, C = D / VE;

@@ -203,6 +203,35 @@ def test_run_length_boundaries_and_long_runs():
             parity(spec, seed=4, steps=1, threshold=thr, batches=[batch])
 
 
+@pytest.mark.parametrize("dtype,D", [("f32", 32), ("bf16", 128)])
+def test_very_long_runs_finish_in_pieces(dtype, D):
+    # Runs of at least 128 chunk partials (32 768 lookups) are finished in pieces of 64
+    # chunks, the last taking the remainder: rows hit 32 512 times (127 chunks, one
+    # workgroup), 32 768 (two pieces of 64), 33 000 (64 + 65) and 50 000 times
+    # (64 + 64 + 68).  Two steps on one handle, plain and grouped calls, and the same
+    # result bit for bit on a second handle.
+    E, B = 64, 512
+    rng = np.random.default_rng(7)
+    hits = [5] * 32512 + [13] * 32768 + [21] * 33000 + [29] * 50000 + list(rng.integers(0, E, 4000))
+    batches = []
+    for step in range(2):
+        h = rng.permutation(np.array(hits))
+        batches.append(_hand_batch(1, B, [[list(b) for b in np.array_split(h, B)]]))
+    for opt in ("sgd", "rowwise_adagrad"):
+        spec = workloads.custom([E], [D], dtype, B=B, optimizer=opt, key=225)
+        parity(spec, seed=6, steps=2, batches=batches)
+    parity(spec, seed=6, steps=2, batches=batches, grouped=True)
+    a = make_problem(spec, seed=8, batch=batches[0])
+    b = make_problem(spec, seed=8, batch=batches[0])
+    G = workloads.grad_output(spec, seed=8, step=0, device="cuda")
+    for pb in (a, b):
+        pb.op.backward_update(B, pb.idx, pb.off, None, G, spec.lr, spec.eps)
+    torch.cuda.synchronize()
+    assert torch.equal(a.W, b.W) and torch.equal(a.state, b.state)
+    a.op.close()
+    b.op.close()
+
+
 def test_dyadic_sgd_is_bit_exact():
     # with dyadic weights, gradients and learning rate every sum is exact in any order
     E, D, B = 40, 16, 300

@@ -289,9 +289,10 @@ struct BackwardBuffers {
 // Device counters of the backward (zeroed at the start of every call), each
 // on a 128-byte line of its own so that atomics on different counters do not
 // queue behind each other.  kCntError is raised if a look-back wait ever
-// gives up (results then invalid).
+// gives up (results then invalid); kCntPieced once a long run of at least
+// kFinPieceMin chunks is queued.
 enum { kCntUnique = 0, kCntLong = 32, kCntItems1 = 64, kCntChunks = 96, kCntError = 128,
-       kNumCounters = 160 };
+       kCntPieced = 160, kNumCounters = 192 };
 
 // A long run of at least kFinPieceMin chunks has its chunk partials added in
 // pieces of kFinPiece chunks (the last piece takes the remainder, so every

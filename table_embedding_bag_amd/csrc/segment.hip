@@ -661,6 +661,7 @@ __global__ __launch_bounds__(kBlock) void queue_runs(BackwardLaunch a) {
           const uint32_t n1 = (ln[j] + a.chunk - 1) / a.chunk;
           a.buf.longs[x_long] = make_uint4(st[j], ln[j], x_chunks, n1);
           a.buf.long_keys[x_long] = a.buf.unique_keys[r];
+          if (n1 >= kFinPieceMin) atomicOr(&a.buf.counters[kCntPieced], 1u);
           if (n1 <= kQueueOwnChunks)
             for (uint32_t c = 0; c < n1; ++c) a.buf.items1[x_items + c] = make_uint2(x_long, c);
           else
@@ -892,7 +893,7 @@ __global__ __launch_bounds__(kBlock) void seg_finalize(BackwardLaunch a) {
   const int g = tid >> a.gshift, gl = tid & (Gs - 1);
   const int row_elems = Gs * NV;
   const uint32_t n = a.buf.counters[kCntLong];
-  {
+  if (a.buf.counters[kCntPieced] != 0u) {
     // the pieces of runs of at least kFinPieceMin chunks: the workgroups scan
     // the item list for the first chunk of each piece, 256 adjacent items each
     // (interleaving the items over the workgroups, so that a run's pieces go

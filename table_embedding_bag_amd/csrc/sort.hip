@@ -653,6 +653,7 @@ __device__ __forceinline__ void queue_run(const RunQueue& q, uint32_t* counters,
     const uint32_t it = atomicAdd(&counters[kCntItems1], n1);
     q.longs[li] = make_uint4(s, len, b1, n1);
     q.long_keys[li] = key;
+    if (n1 >= kFinPieceMin) atomicOr(&counters[kCntPieced], 1u);
     for (uint32_t c = 0; c < n1; ++c) q.items1[it + c] = make_uint2(li, c);
   } else {
     const uint32_t it = atomicAdd(&counters[kCntItems1], 1u);
@@ -905,6 +906,7 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
             const uint32_t n1 = (rl + q.chunk - 1) / q.chunk;
             q.longs[li] = make_uint4(ps, rl, b1, n1);
             q.long_keys[li] = s_k[i];
+            if (n1 >= kFinPieceMin) atomicOr(&counters[kCntPieced], 1u);
             for (uint32_t c = 0; c < n1; ++c) q.items1[it + c] = make_uint2(li, c);
             ++li;
             b1 += n1;

@@ -20,7 +20,7 @@ def test_grouped_parity(spec):
     parity(spec, seed=11, steps=2, grouped=True)
 
 
-def test_grouped_workload2_parity():
+def test_grouped_parity_8_tables_100k_rows_zipf():
     parity(workloads.config(2), seed=0, steps=2, bag_sample=3000, row_sample=3000, grouped=True)
 
 

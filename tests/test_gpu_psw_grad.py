@@ -48,7 +48,7 @@ def test_psw_grad_int32_indices():
 
 
 @pytest.mark.timeout(600)
-def test_psw_grad_workload3():
+def test_psw_grad_32_mixed_bf16_tables():
     """Mixed dims 32..256, bf16, mean pooling with weights: the workload that trains them."""
     _check(workloads.config(3), seed=0)
 

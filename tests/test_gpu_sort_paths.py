@@ -42,8 +42,8 @@ _HOT = {5: 9000, 600: 30000, 199_999: 12000, 77_777: 300}
 
 def _cases():
     return [
-        ("workload1", workloads.config(1), None),
-        ("workload2", workloads.config(2), None),
+        ("tiny-2x1000", workloads.config(1), None),
+        ("8x100k-zipf", workloads.config(2), None),
         ("hot-buckets", workloads.custom([_E_HOT], [64], "f32", B=512,
                                          optimizer="rowwise_adagrad", key=230),
          [_hot_batch(_E_HOT, 512, _HOT, 100_000, 31)]),

@@ -5,7 +5,7 @@ per-sample weights, table values and upstream gradients.  It holds none of
 the arithmetic of the method itself (no pooling, no grouping, no update), so
 the GPU library and the CPU reference can both consume its output.
 
-Recipe (the readings behind each choice are listed in the design doc):
+Recipe (where the sources leave a choice open, the plainest reading is taken):
 
 * Host draws use numpy PCG64 with ``SeedSequence(seed, spawn_key=(workload,
   table, purpose, step))``, so every (table, purpose, step) has its own stream

@@ -56,7 +56,9 @@
  * not checked unless TBE_FLAG_VALIDATE is set; violating them is undefined.
  *
  * Threading: a handle may be used by one host thread at a time.  Two
- * backward_update calls in flight on one handle race on the weights.
+ * backward_update calls in flight on one handle race on the weights; with
+ * TBE_FLAG_SPLIT_BAGS, two forward calls in flight on one handle (on
+ * different streams) race on the handle's segment-sum scratch.
  *
  * No C++ exception crosses this interface.  Every function returns a
  * tbe_status; tbe_status_string gives a static description.

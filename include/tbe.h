@@ -110,8 +110,8 @@ enum {
    * kimbodo.com/?p=28372, "What Happened" (small tables that qualify use a
    * histogram and tensor-core path). */
   TBE_FLAG_HISTOGRAM = 8u,
-  /* Skew balancing (off by default): a bag of more than 256 lookups pools its
-   * first 256 in the forward's own pass and its other 256-lookup segments
+  /* Skew balancing (off by default): a bag of more than 128 lookups pools its
+   * first 128 in the forward's own pass and its other 128-lookup segments
    * in parallel waves, whose sums are then added to the bag's output in
    * segment order (deterministic; the fp32 rounding order differs from the
    * unsplit sum).  The handle allocates a scratch for the segment sums at

@@ -181,7 +181,7 @@ struct Carve {
 
 // Skew balancing (TBE_FLAG_SPLIT_BAGS): bags longer than kSplitLen lookups
 // are pooled in segments of kSplitLen.
-constexpr int32_t kSplitLen = 256;
+constexpr int32_t kSplitLen = 128;
 constexpr int64_t kSplitMaxSegments = int64_t{1} << 18;
 constexpr int64_t kSplitScratchBytes = int64_t{64} << 20;
 

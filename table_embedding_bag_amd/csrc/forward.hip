@@ -238,35 +238,49 @@ __global__ __launch_bounds__(kBlock) void fwd_split_segments(ForwardLaunch a) {
   }
 }
 
-// Adds each split bag's segment sums to its output row, in segment order (the
-// result does not depend on scheduling).  One wave per split bag.
+// Adds each split bag's segment sums to its output row.  One workgroup per
+// split bag: wave w adds the w-th quarter of the bag's segments in segment
+// order, and the quarters are then added to the row in wave order (the result
+// does not depend on scheduling).
 constexpr int kCombineBatch = 16;
 __global__ __launch_bounds__(kBlock) void fwd_split_combine(ForwardLaunch a) {
+  __shared__ float s_q[kWavesPerBlock][kMaxDim];
   const uint32_t nlong = a.split_ctr[1];
-  for (uint32_t li = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6); li < nlong;
-       li += gridDim.x * kWavesPerBlock) {
+  const uint32_t wave = threadIdx.x >> 6;
+  const int64_t ps = a.split_pstride;
+  for (uint32_t li = blockIdx.x; li < nlong; li += gridDim.x) {
     const uint4 L = a.split_long[li];  // {bag, first segment slot, segments, 0}
     const int64_t k = L.x;
     const int t = static_cast<int>(k / a.B);
     const int64_t b = k - static_cast<int64_t>(t) * a.B;
     const TableMeta m = a.meta[t];
     float* orow = a.out + b * a.sum_dims + m.doff;
-    const int64_t ps = a.split_pstride;
+    const uint32_t per = (L.z + kWavesPerBlock - 1) / kWavesPerBlock;
+    const uint32_t j0 = min(L.z, wave * per);
+    const uint32_t nj = min(L.z, j0 + per) - j0;
     for (int d = lane_id(); d < m.dim; d += kWave) {
-      const float* p = a.split_part + static_cast<int64_t>(L.y) * ps + d;
-      float y = orow[d];
+      const float* p = a.split_part + static_cast<int64_t>(L.y + j0) * ps + d;
+      float y = 0.0f;
       uint32_t j = 0;
       // kCombineBatch loads in flight, then added in segment order
-      for (; j + kCombineBatch <= L.z; j += kCombineBatch) {
+      for (; j + kCombineBatch <= nj; j += kCombineBatch) {
         float v[kCombineBatch];
 #pragma unroll
         for (int u = 0; u < kCombineBatch; ++u) v[u] = p[static_cast<int64_t>(j + u) * ps];
 #pragma unroll
         for (int u = 0; u < kCombineBatch; ++u) y += v[u];
       }
-      for (; j < L.z; ++j) y += p[static_cast<int64_t>(j) * ps];
+      for (; j < nj; ++j) y += p[static_cast<int64_t>(j) * ps];
+      s_q[wave][d] = y;
+    }
+    __syncthreads();
+    for (int d = static_cast<int>(threadIdx.x); d < m.dim; d += kBlock) {
+      float y = orow[d];
+#pragma unroll
+      for (int w = 0; w < kWavesPerBlock; ++w) y += s_q[w][d];
       orow[d] = y;
     }
+    __syncthreads();  // s_q is reused by the next split bag
   }
 }
 
@@ -552,7 +566,9 @@ hipError_t launch_forward_split(const ForwardLaunch& a, int64_t num_indices, hip
     case kBF16: launch_split_index<kBF16>(a, stream, grid, kt); break;
     default: return hipErrorInvalidValue;
   }
-  launch_timed(kt, "fwd_split_combine", fwd_split_combine, grid, dim3(kBlock), 0, stream, a);
+  // one workgroup per split bag
+  const dim3 cgrid(static_cast<unsigned>(segs < 4096 ? segs : 4096));
+  launch_timed(kt, "fwd_split_combine", fwd_split_combine, cgrid, dim3(kBlock), 0, stream, a);
   return hipGetLastError();
 }
 

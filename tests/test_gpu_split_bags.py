@@ -1,6 +1,6 @@
 """Skew balancing in the forward (TBE_FLAG_SPLIT_BAGS; kimbodo.com/?p=28372, "Kimbodo
-Engineering Perspective": load imbalance across lookups is a risk).  Bags of more than 256
-lookups are pooled in 256-lookup segments by parallel waves and the segment sums added in
+Engineering Perspective": load imbalance across lookups is a risk).  Bags of more than 128
+lookups are pooled in 128-lookup segments by parallel waves and the segment sums added in
 order: the pooled output must match the CPU reference within the forward tolerance, for sum and
 mean pooling, with and without per-sample weights, int64 and int32 ids, plain and grouped
 calls; the backward is unchanged."""
@@ -18,8 +18,8 @@ pytestmark = pytest.mark.gpu
 
 B = 48
 # (table, bag) -> length: one long bag per table, one just over and one exactly at the
-# 256-lookup segment length, one a whole number of segments plus one
-LONG = {(0, 3): 50000, (0, 10): 257, (0, 11): 256, (1, 20): 9000, (1, 47): 4097}
+# 128-lookup segment length, one a whole number of segments plus one
+LONG = {(0, 3): 50000, (0, 10): 129, (0, 11): 128, (1, 20): 9000, (1, 47): 4097}
 
 
 def _skewed_batch(rows, seed):

@@ -52,7 +52,8 @@ def _cfg(rows, dims, dtype=0, pooling=0, opt=0, flags=0):
 
 @pytest.mark.parametrize("case", ["null_weights", "no_tables", "zero_rows", "dim_too_big", "bad_dtype",
                                   "bad_pooling", "bad_optimizer", "adagrad_without_state",
-                                  "unknown_flag", "conflicting_flags", "misaligned_weights"])
+                                  "unknown_flag", "lowest_unknown_flag", "conflicting_flags",
+                                  "misaligned_weights"])
 def test_create_rejects_bad_configs_on_host(case):
     lib = tbe.load()
     rows, dims, kw, w, st = [10, 20], [8, 8], {}, 4096, None
@@ -72,6 +73,8 @@ def test_create_rejects_bad_configs_on_host(case):
         kw["opt"] = 1
     elif case == "unknown_flag":
         kw["flags"] = 64
+    elif case == "lowest_unknown_flag":
+        kw["flags"] = tbe.FLAG_SPLIT_BAGS << 1
     elif case == "conflicting_flags":
         kw["flags"] = 6
     elif case == "misaligned_weights":

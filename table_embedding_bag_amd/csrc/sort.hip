@@ -59,10 +59,12 @@ __device__ __forceinline__ void st_status(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__global__ __launch_bounds__(kBlock) void init_workspace(uint32_t* words, int64_t nwords) {
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < nwords;
+// 16-byte stores: the zeroed region starts 256-byte aligned and its carve is
+// rounded up to 256 bytes, so nvec = ceil(words / 4) stays inside it.
+__global__ __launch_bounds__(kBlock) void init_workspace(uint4* words, int64_t nvec) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < nvec;
        i += static_cast<int64_t>(gridDim.x) * kBlock)
-    words[i] = 0u;
+    words[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // K lookups in flight per thread: 2 when a tile holds more lookups than the
@@ -969,11 +971,12 @@ int sort_tile_keys(int64_t n, int key_bits) {
 hipError_t launch_init_workspace(const BackwardLaunch& a, hipStream_t stream,
                                  const KernelTimer* kt) {
   // the counters, histograms and look-back status words the later kernels chain through
-  int64_t zblocks = (a.buf.zero_words + kBlock - 1) / kBlock;
+  const int64_t nvec = (a.buf.zero_words + 3) / 4;
+  int64_t zblocks = (nvec + kBlock - 1) / kBlock;
   if (zblocks > 1024) zblocks = 1024;
   launch_timed(kt, "init_workspace", init_workspace,
                dim3(static_cast<unsigned>(zblocks > 0 ? zblocks : 1)), dim3(kBlock), 0, stream,
-               a.buf.counters, a.buf.zero_words);
+               reinterpret_cast<uint4*>(a.buf.counters), nvec);
   return hipGetLastError();
 }
 

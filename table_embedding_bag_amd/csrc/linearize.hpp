@@ -79,6 +79,13 @@ __device__ __forceinline__ void linearize_tiles(const BackwardLaunch& a, int64_t
     __syncthreads();
 
     const int64_t p0 = s_off[0], p1 = s_off[nb];
+    // A tile whose lookups are nb times its first bag's length most likely
+    // has equally long bags: there the slot interpolated from the position is
+    // exact (it is checked before it is used) and the binary search is
+    // skipped.  Bags of 8 lookups: 121 -> 107 us on 16.8 M lookups; trying it
+    // on every tile cost 4 us on 5.2 M lookups of Poisson lengths.
+    const bool even = p1 - p0 == static_cast<int64_t>(nb) * (s_off[1] - p0);
+    const float per = even && p1 > p0 ? static_cast<float>(nb) / static_cast<float>(p1 - p0) : 0.0f;
     for (int64_t base = p0; base < p1; base += static_cast<int64_t>(NT) * K) {
       int slot[K];
       bool ok[K];
@@ -88,15 +95,22 @@ __device__ __forceinline__ void linearize_tiles(const BackwardLaunch& a, int64_t
       for (int k = 0; k < K; ++k) {
         const int64_t p = base + tid + static_cast<int64_t>(NT) * k;
         ok[k] = p < p1;
-        int lo = 0, hi = nb;  // bag slot s with s_off[s] <= p < s_off[s + 1]
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (s_off[mid] <= p)
-            lo = mid;
-          else
-            hi = mid;
+        // bag slot s with s_off[s] <= p < s_off[s + 1]
+        int g = static_cast<int>(static_cast<float>(p - p0) * per);
+        g = g < 0 ? 0 : (g > nb - 1 ? nb - 1 : g);
+        if (even && s_off[g] <= p && p < s_off[g + 1]) {
+          slot[k] = g;
+        } else {
+          int lo = 0, hi = nb;
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_off[mid] <= p)
+              lo = mid;
+            else
+              hi = mid;
+          }
+          slot[k] = lo;
         }
-        slot[k] = lo;
       }
       // every load of the batch is issued before any is used (positions past
       // the tile read its last lookup instead)

@@ -232,6 +232,21 @@ def test_very_long_runs_finish_in_pieces(dtype, D):
     b.op.close()
 
 
+@pytest.mark.parametrize("cycle", [(2, 0, 4, 2), (2, 1, 3, 2), (8,)], ids=["with-empty", "uneven", "even"])
+def test_linearize_tiles_whose_lengths_sum_evenly(cycle):
+    # Bag lengths cycling (2, 0, 4, 2) or (2, 1, 3, 2) make every tile of 128 bags hold
+    # 128 times its first bag's length although the bags differ (so the interpolated bag
+    # slot is often wrong and must be caught); (8,) is the truly even case.
+    T, B, E = 2, 1024, 300
+    rng = np.random.default_rng(9)
+    bags = [[list(rng.integers(0, E, cycle[b % len(cycle)])) for b in range(B)] for t in range(T)]
+    batch = _hand_batch(T, B, bags)
+    spec = workloads.custom([E, E], [32, 32], "f32", B=B, optimizer="rowwise_adagrad", key=226)
+    parity(spec, seed=10, steps=1, batches=[batch])
+    parity(spec, seed=10, steps=1, batches=[batch], grouped=True)
+    parity(spec, seed=10, steps=1, batches=[batch], index_dtype=torch.int32)
+
+
 def test_dyadic_sgd_is_bit_exact():
     # with dyadic weights, gradients and learning rate every sum is exact in any order
     E, D, B = 40, 16, 300

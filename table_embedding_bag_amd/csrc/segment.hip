@@ -895,17 +895,19 @@ __global__ __launch_bounds__(kBlock) void seg_finalize(BackwardLaunch a) {
   const uint32_t n = a.buf.counters[kCntLong];
   if (a.buf.counters[kCntPieced] != 0u) {
     // the pieces of runs of at least kFinPieceMin chunks: the workgroups scan
-    // the item list for the first chunk of each piece, 256 adjacent items each
-    // (interleaving the items over the workgroups, so that a run's pieces go
-    // to different ones, was slower: 34 -> 42 us on 4.2 M lookups)
+    // the item list for the first chunk of each piece, kFinPiece adjacent items
+    // each, so one workgroup meets at most one piece of a run (pieces are
+    // kFinPiece items apart).  Interleaving the items over the workgroups was
+    // slower (34 -> 42 us on 4.2 M lookups): the pieces then sit in
+    // high-numbered workgroups, which start last.
     __shared__ uint32_t s_np, s_last;
-    __shared__ uint2 s_piece[kBlock];
+    __shared__ uint2 s_piece[kFinPiece];
     const uint32_t nitems = a.buf.counters[kCntItems1];
-    for (uint32_t base = blockIdx.x * kBlock; base < nitems; base += gridDim.x * kBlock) {
+    for (uint32_t base = blockIdx.x * kFinPiece; base < nitems; base += gridDim.x * kFinPiece) {
       if (tid == 0) s_np = 0u;
       __syncthreads();
       const uint32_t item = base + static_cast<uint32_t>(tid);
-      if (item < nitems) {
+      if (tid < static_cast<int>(kFinPiece) && item < nitems) {
         const uint2 it = a.buf.items1[item];
         if (!(it.y & kMediumItem) && it.y % kFinPiece == 0u) {
           const uint32_t w = a.buf.longs[it.x].w;

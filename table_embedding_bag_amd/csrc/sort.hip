@@ -493,9 +493,18 @@ __global__ __launch_bounds__(1024) void rle_kernel(const uint32_t* __restrict__ 
   __syncthreads();
   const int tile = static_cast<int>(s_tile);
   const int64_t base = static_cast<int64_t>(tile) * kRleTile;
-  for (int i = tid; i < kRleTile + 1; i += NT) {
-    const int64_t p = base - 1 + i;
-    s_k[i] = (p >= 0 && p < n) ? keys[p] : 0u;
+  {
+    // s_k[i] = keys[base - 1 + i]; the PER loads of a thread are all issued
+    // before any is stored
+    uint32_t v[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int64_t p = base + j * NT + tid;
+      v[j] = p < n ? keys[p] : 0u;
+    }
+    if (tid == 0) s_k[0] = (base > 0 && base - 1 < n) ? keys[base - 1] : 0u;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) s_k[1 + j * NT + tid] = v[j];
   }
   __syncthreads();
   uint32_t c = 0;

@@ -39,7 +39,9 @@
  *                             W_r <- W_r - lr * Gamma_r / (sqrt(m_r) + eps)
  *  The pages name no optimizer; SGD and the row-wise Adagrad above (state
  *  updated before it is used, eps outside the square root, mean over the row)
- *  are the plainest readings and are documented as readings.
+ *  are the plainest readings and are documented as readings.  On rows of one
+ *  column the row-wise Adagrad is plain Adagrad, and the tests pin it there
+ *  against torch.optim.Adagrad (update order, place of eps).
  *
  *  Storage conversions follow the IEEE-754 binary16 definition and the
  *  bfloat16 definition (the upper half of an IEEE binary32).

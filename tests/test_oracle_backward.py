@@ -10,7 +10,10 @@ plain SGD and row-wise Adagrad are readings, pinned here by their closed forms.
 
 Pins: numpy unique / bincount (library), the dense transpose product A^T G
 (brute force), central finite differences of <G, forward(W)>, the duplicate
-invariant, closed forms of both optimizers, untouched rows.
+invariant, closed forms of both optimizers, untouched rows, and
+torch.optim.Adagrad on one-column tables (where row-wise Adagrad is plain
+Adagrad), which fixes the update order and where eps sits.  The mean over the
+row for wider rows stays a reading.
 """
 import numpy as np
 import pytest
@@ -245,6 +248,92 @@ def test_rowwise_adagrad_closed_form_two_steps():
                     # from zero state: rms of the step equals lr * rho / (rho + eps)
                     assert abs(np.sqrt(np.mean(want ** 2)) - LR * rho / (rho + EPS)) <= 1e-12
 
+
+def _torch_bag_loss(spec, batch, G, params, torch):
+    """<G, forward(W)> through torch's own embedding_bag (sum pooling), one table at a time."""
+    loss = 0.0
+    for t in range(spec.T):
+        lo, hi = int(batch.offsets[t * spec.B]), int(batch.offsets[(t + 1) * spec.B])
+        off = torch.from_numpy(batch.offsets[t * spec.B:(t + 1) * spec.B + 1] - lo)
+        idx = torch.from_numpy(batch.indices[lo:hi])
+        p = None if batch.psw is None else torch.from_numpy(batch.psw[lo:hi].astype(np.float64))
+        Y = torch.nn.functional.embedding_bag(idx, params[t], off, mode="sum", per_sample_weights=p,
+                                              include_last_offset=True)
+        loss = loss + (Y * torch.from_numpy(G[:, t:t + 1].astype(np.float64))).sum()
+    return loss
+
+
+@pytest.mark.parametrize("psw", [False, True], ids=["plain", "weighted"])
+def test_rowwise_adagrad_at_dim_one_is_torch_adagrad(psw):
+    # With one column per row, the row-wise Adagrad reading (state += mean over the row of
+    # Gamma^2, then W -= lr * Gamma / (sqrt(state) + eps) with the updated state, state from
+    # 0) is plain Adagrad, which torch.optim.Adagrad implements independently (lr_decay 0,
+    # weight_decay 0, initial accumulator 0).  eps = 0.25 is large enough to tell
+    # sqrt(m) + eps from sqrt(m + eps) by several percent, and the state is used after its
+    # update (the other order divides the first step by eps alone).  Duplicate rows inside a
+    # batch and rows left out of some steps are both present.  Each step starts torch from
+    # the oracle's weights and state (both fp32-representable) and runs it in fp64; the
+    # oracle rounds its fp64 result once to fp32, so the two agree to one fp32 rounding.
+    import torch
+    lr, eps = 0.05, 0.25
+    spec = workloads.custom([40, 9], [1, 1], "f32", B=16, lengths=("uniform_int", 0, 6),
+                            index_dist=("zipf", 1.4), psw=psw, optimizer="rowwise_adagrad",
+                            key=280, lr=lr, eps=eps)
+    roff = np.concatenate([[0], np.cumsum(spec.rows)])
+
+    def params_from(W):
+        return [torch.nn.Parameter(torch.from_numpy(W[roff[t]:roff[t + 1]].astype(np.float64))
+                                   .reshape(-1, 1)) for t in range(spec.T)]
+
+    def adagrad(params):
+        return torch.optim.Adagrad(params, lr=lr, lr_decay=0, weight_decay=0,
+                                   initial_accumulator_value=0, eps=eps)
+
+    def flat(ts):
+        return np.concatenate([t.detach().numpy().reshape(-1) for t in ts])
+
+    W = _np_weights(spec, seed=21)
+    st = np.zeros(spec.sum_rows, np.float32)
+    chain = params_from(W)          # a torch-only trajectory over every step, never resynchronised
+    chain_opt = adagrad(chain)
+    skipped_rows_seen = False
+    for step in range(4):
+        batch = workloads.batch(spec, seed=21, step=step)
+        G = _np_grad(spec, seed=21, step=step)
+        params = params_from(W)
+        opt = adagrad(params)
+        for t, p in enumerate(params):
+            opt.state[p]["sum"].copy_(torch.from_numpy(st[roff[t]:roff[t + 1]].astype(np.float64))
+                                      .reshape(-1, 1))
+        _torch_bag_loss(spec, batch, G, params, torch).backward()
+        gamma = flat([p.grad for p in params])
+        opt.step()
+        _torch_bag_loss(spec, batch, G, chain, torch).backward()
+        chain_opt.step()
+        chain_opt.zero_grad()
+
+        W_before, st_before = W.copy(), st.copy()
+        _update(spec, W, st, batch, G)
+        uniq, cnt = oracle.runs(spec.rows, spec.B, batch.indices, batch.offsets)
+        assert (cnt > 1).any()                                   # duplicates in this batch
+        untouched = np.setdiff1d(np.arange(spec.sum_rows), uniq)
+        skipped_rows_seen |= bool((st_before[untouched] > 0).any())
+        assert np.array_equal(W[untouched], W_before[untouched])
+        assert np.array_equal(st[untouched], st_before[untouched])
+
+        w_t, m_t = flat(params), flat([opt.state[p]["sum"] for p in params])
+        assert np.all(np.abs(W - w_t) <= 2.0 ** -23 * np.abs(w_t)), f"weights, step {step}"
+        assert np.all(np.abs(st - m_t) <= 2.0 ** -23 * m_t), f"state, step {step}"
+        # fp32 rounding of the stored weights and state, carried over the steps
+        assert np.all(np.abs(W - flat(chain)) <= 1e-6 * (np.abs(flat(chain)) + lr))
+        # the readings rejected for the pages' silence land far outside that bound
+        w0, g, m0, m1 = W_before[uniq].astype(np.float64), gamma[uniq], st_before[uniq], m_t[uniq]
+        eps_inside = w0 - lr * g / np.sqrt(m1 + eps)
+        state_after_use = w0 - lr * g / (np.sqrt(m0) + eps)
+        for alt in (eps_inside, state_after_use):
+            far = np.abs(alt - w_t[uniq]) > 1e3 * 2.0 ** -23 * np.abs(w_t[uniq])
+            assert far.mean() > 0.5
+    assert skipped_rows_seen                                     # some row with state sat out a step
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_low_precision_update_rounds_once_to_nearest(dtype):

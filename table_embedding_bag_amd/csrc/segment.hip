@@ -178,11 +178,13 @@ __device__ __forceinline__ int table_of_run(const BackwardLaunch& a, const uint3
 }
 
 // Row-wise optimizer step size for a row whose summed gradient has squared
-// norm ss; updates the state (one lane writes it).
-__device__ __forceinline__ float step_size(const BackwardLaunch& a, uint32_t key, double ss, int D,
-                                           bool writer) {
+// norm ss and whose state was m_old; updates the state (one lane writes it).
+// Every thread must have read m_old before a barrier that the writer passes
+// before its store, else a late reader sees the new state.
+__device__ __forceinline__ float step_size(const BackwardLaunch& a, uint32_t key, float m_old,
+                                           double ss, int D, bool writer) {
   if (!a.adagrad) return a.lr;
-  const float mnew = static_cast<float>(static_cast<double>(a.state[key]) + ss / D);
+  const float mnew = static_cast<float>(static_cast<double>(m_old) + ss / D);
   if (writer) a.state[key] = mnew;
   return a.lr / (sqrtf(mnew) + a.eps);
 }
@@ -390,7 +392,10 @@ __device__ __forceinline__ void short_runs(const BackwardLaunch& a, const uint32
   __shared__ TableMeta s_meta[kLdsTables];
   const bool failed = a.buf.counters[kCntError] != 0u;  // a look-back wait gave up earlier
   const uint32_t U = a.buf.counters[kCntUnique];
-  if (a.out_num && bid == 0 && threadIdx.x == 0) *a.out_num = failed ? -1 : static_cast<int32_t>(U);
+  if (bid == 0 && threadIdx.x == 0) {
+    if (a.out_num) *a.out_num = failed ? -1 : static_cast<int32_t>(U);
+    if (failed && a.error_mark) atomicOr(a.error_mark, 1u);  // read by tbe_check_device_status
+  }
   if (failed) return;
   stage_meta(a, s_meta);
   const int Gq = a.short_max;
@@ -565,8 +570,11 @@ __device__ __forceinline__ void wg_items(const BackwardLaunch& a, const uint32_t
     }
     if (medium) {
       const uint32_t key = keys[s];
+      // read by every thread before block_sum's barriers, so no thread sees
+      // the state thread 0 writes after them
+      const float m_old = a.adagrad ? a.state[key] : 0.0f;
       if (a.adagrad) ss = block_sum(ss, s_scratch);
-      const float step = step_size(a, key, ss, D, tid == 0);
+      const float step = step_size(a, key, m_old, ss, D, tid == 0);
       const int64_t row0 = m.woff + static_cast<int64_t>(key - static_cast<uint32_t>(m.roff)) * D;
 #pragma unroll
       for (int k = 0; k < kElemsPerThread; ++k) {
@@ -838,6 +846,9 @@ __device__ __forceinline__ void finish_piece(const BackwardLaunch& a, const Tabl
   __syncthreads();
   if (*s_last == 0u) return;  // the same on every thread
   __threadfence();            // the other pieces' sums are seen
+  // read by every thread before block_sum's barriers (thread 0 writes the new
+  // state after them)
+  const float m_old = a.adagrad ? a.state[key] : 0.0f;
   const int64_t row0 = m.woff + static_cast<int64_t>(key - static_cast<uint32_t>(m.roff)) * D;
   const int64_t pstep = static_cast<int64_t>(kFinPiece) * ps;
   const double* p0 = reinterpret_cast<const double*>(a.buf.partial1 + static_cast<int64_t>(L.z) * ps);
@@ -859,9 +870,7 @@ __device__ __forceinline__ void finish_piece(const BackwardLaunch& a, const Tabl
   float step = a.lr;
   if (a.adagrad) {
     ss = block_sum(ss, s_scratch);
-    const float mnew = static_cast<float>(static_cast<double>(a.state[key]) + ss / D);
-    if (tid == 0) a.state[key] = mnew;
-    step = a.lr / (sqrtf(mnew) + a.eps);
+    step = step_size(a, key, m_old, ss, D, tid == 0);
   }
   for (int d = tid; d < D; d += kBlock) {
     float w;

@@ -84,7 +84,9 @@ typedef enum {
   TBE_ERR_INDEX_OUT_OF_RANGE = 3, /* TBE_FLAG_VALIDATE found a bad id or offsets array */
   TBE_ERR_WORKSPACE_TOO_SMALL = 4,
   TBE_ERR_HIP = 5,                /* a HIP runtime call or kernel launch failed */
-  TBE_ERR_OUT_OF_MEMORY = 6       /* metadata allocation failed */
+  TBE_ERR_OUT_OF_MEMORY = 6,      /* metadata allocation failed */
+  TBE_ERR_DEVICE_WAIT = 7         /* a device-side wait gave up: that backward update was
+                                     skipped (see tbe_check_device_status) */
 } tbe_status;
 
 typedef enum { TBE_F32 = 0, TBE_F16 = 1, TBE_BF16 = 2 } tbe_dtype;       /* table storage */
@@ -157,7 +159,15 @@ typedef enum {
    * 1: LSD radix passes, then a separate run-length-encoding kernel.
    * Both give the same order (stable on the id), so results are bit-identical.
    * Other values: TBE_ERR_INVALID_ARGUMENT. */
-  TBE_OPTION_SORT = 3
+  TBE_OPTION_SORT = 3,
+  /* Polls a workgroup of the backward's grouping makes while it waits for an
+   * earlier one (the sort's and the run-length encoding's look-backs) before
+   * it gives up (default 2^20, far beyond any wait seen; 0 to 2^31 - 1).  A
+   * wait that gives up never faults or hangs: the call finishes, updates no
+   * weight and no state, reports num_unique = -1 in its runs, and marks the
+   * handle (tbe_check_device_status).  0 makes every such wait give up at
+   * once, which only serves to test that path. */
+  TBE_OPTION_SPIN_LIMIT = 4
 } tbe_option;
 
 /* Create a handle.  Validates the configuration (host only; nothing is
@@ -214,11 +224,15 @@ tbe_status tbe_backward_update(tbe_handle* handle, int32_t B, const void* indice
  * encoding of the batch follow, into `workspace` (sized by
  * tbe_backward_workspace_size, 256-byte aligned).  With TBE_FLAG_VALIDATE the
  * ids are checked before anything is queued.  Arguments and errors as
- * tbe_forward, plus TBE_ERR_WORKSPACE_TOO_SMALL.  The workspace must then go,
- * unchanged and with the same batch (ids, offsets, per-sample weights, B,
- * num_indices), to tbe_backward_update_grouped; anything else gives undefined
- * results.  The pair gives the same output, weights and state as tbe_forward
- * + tbe_backward_update, bit for bit. */
+ * tbe_forward, plus TBE_ERR_WORKSPACE_TOO_SMALL.  The handle records the call
+ * by its workspace (up to 64 such records, oldest dropped first), so several
+ * forward_group calls on different workspaces may precede their backward
+ * calls.  The workspace must then go, unchanged and with the same batch
+ * buffers (ids, offsets, per-sample weights, B, num_indices, index dtype), to
+ * one tbe_backward_update_grouped call; the long-run threshold and sort
+ * options in force at this call are the ones used there.  The pair gives the
+ * same output, weights and state as tbe_forward + tbe_backward_update, bit
+ * for bit. */
 tbe_status tbe_forward_group(tbe_handle* handle, int32_t B, const void* indices,
                              const void* offsets, int32_t index_dtype, int64_t num_indices,
                              const float* per_sample_weights, float* output, void* workspace,
@@ -226,13 +240,26 @@ tbe_status tbe_forward_group(tbe_handle* handle, int32_t B, const void* indices,
 
 /* tbe_backward_update without the grouping: uses the one a tbe_forward_group
  * call on the same batch left in `workspace` (same arguments and errors as
- * tbe_backward_update; the result is bit-identical). */
+ * tbe_backward_update; the result is bit-identical).  Returns
+ * TBE_ERR_INVALID_ARGUMENT, with nothing enqueued, when the handle holds no
+ * grouping of this workspace, or when its batch buffers, B, num_indices or
+ * index dtype differ from that forward_group call's.  Each grouping serves one
+ * backward call; a plain tbe_backward_update or a new tbe_forward_group on the
+ * same workspace discards it. */
 tbe_status tbe_backward_update_grouped(tbe_handle* handle, int32_t B, const void* indices,
                                        const void* offsets, int32_t index_dtype,
                                        int64_t num_indices, const float* per_sample_weights,
                                        const float* grad_output, float lr, float eps,
                                        void* workspace, size_t workspace_bytes,
                                        const tbe_runs* runs, void* stream);
+
+/* Device-side failures of backward calls since the last check.  Waits for
+ * `stream` (all work queued on it, hipStream_t as void*), then reads and
+ * clears the handle's mark: TBE_ERR_DEVICE_WAIT if a backward call's wait gave
+ * up since the last check (TBE_OPTION_SPIN_LIMIT; that call left weights and
+ * state untouched), else TBE_OK.  With TBE_FLAG_VALIDATE every backward call
+ * makes this check itself before it returns. */
+tbe_status tbe_check_device_status(tbe_handle* handle, void* stream);
 
 /* Set a tbe_option (see above). */
 tbe_status tbe_set_option(tbe_handle* handle, int32_t option, int64_t value);

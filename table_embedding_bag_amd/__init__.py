@@ -20,11 +20,12 @@ __all__ = [
     "TBEError", "library_path", "load", "tbe_create", "tbe_destroy", "tbe_forward",
     "tbe_backward_workspace_size", "tbe_backward_update", "tbe_forward_group",
     "tbe_backward_update_grouped", "tbe_psw_grad", "tbe_set_option", "tbe_stage_times",
-    "tbe_status_string", "tbe_abi_version", "TBE",
+    "tbe_status_string", "tbe_abi_version", "tbe_check_device_status", "TBE",
     "F32", "F16", "BF16", "POOL_SUM", "POOL_MEAN", "OPT_SGD", "OPT_ROWWISE_ADAGRAD",
     "FLAG_VALIDATE", "FLAG_NO_HISTOGRAM", "FLAG_FORCE_HISTOGRAM", "FLAG_HISTOGRAM",
     "FLAG_SPLIT_BAGS",
-    "OPTION_LONG_RUN_THRESHOLD", "OPTION_PROFILE", "OPTION_SORT", "EXPORTED_SYMBOLS",
+    "OPTION_LONG_RUN_THRESHOLD", "OPTION_PROFILE", "OPTION_SORT", "OPTION_SPIN_LIMIT",
+    "EXPORTED_SYMBOLS",
 ]
 
 F32, F16, BF16 = 0, 1, 2
@@ -33,18 +34,19 @@ POOL_SUM, POOL_MEAN = 0, 1
 OPT_SGD, OPT_ROWWISE_ADAGRAD = 0, 1
 FLAG_VALIDATE, FLAG_NO_HISTOGRAM, FLAG_FORCE_HISTOGRAM, FLAG_HISTOGRAM = 1, 2, 4, 8
 FLAG_SPLIT_BAGS = 16
-OPTION_LONG_RUN_THRESHOLD, OPTION_PROFILE, OPTION_SORT = 1, 2, 3
+OPTION_LONG_RUN_THRESHOLD, OPTION_PROFILE, OPTION_SORT, OPTION_SPIN_LIMIT = 1, 2, 3, 4
 
 STATUS = {
     0: "TBE_OK", 1: "TBE_ERR_INVALID_ARGUMENT", 2: "TBE_ERR_UNSUPPORTED",
     3: "TBE_ERR_INDEX_OUT_OF_RANGE", 4: "TBE_ERR_WORKSPACE_TOO_SMALL", 5: "TBE_ERR_HIP",
-    6: "TBE_ERR_OUT_OF_MEMORY",
+    6: "TBE_ERR_OUT_OF_MEMORY", 7: "TBE_ERR_DEVICE_WAIT",
 }
 
 EXPORTED_SYMBOLS = (
     "tbe_create", "tbe_destroy", "tbe_forward", "tbe_backward_workspace_size",
     "tbe_backward_update", "tbe_forward_group", "tbe_backward_update_grouped", "tbe_psw_grad",
     "tbe_set_option", "tbe_stage_times", "tbe_status_string", "tbe_abi_version",
+    "tbe_check_device_status",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -96,6 +98,7 @@ def load():
     lib.tbe_backward_update_grouped.argtypes = lib.tbe_backward_update.argtypes
     lib.tbe_psw_grad.argtypes = [P, i32, P, P, i32, i64, P, P, P]
     lib.tbe_set_option.argtypes = [P, i32, i64]
+    lib.tbe_check_device_status.argtypes = [P, P]
     lib.tbe_stage_times.argtypes = [P, ctypes.POINTER(f32), ctypes.POINTER(ctypes.c_char_p), i32,
                                     ctypes.POINTER(i32)]
     lib.tbe_status_string.argtypes = [ctypes.c_int]
@@ -104,7 +107,7 @@ def load():
     lib.tbe_abi_version.restype = i32
     for name in ("tbe_create", "tbe_forward", "tbe_backward_workspace_size", "tbe_backward_update",
                  "tbe_forward_group", "tbe_backward_update_grouped", "tbe_psw_grad",
-                 "tbe_set_option", "tbe_stage_times"):
+                 "tbe_set_option", "tbe_stage_times", "tbe_check_device_status"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -237,6 +240,12 @@ def tbe_psw_grad(handle, B: int, indices, offsets, grad_output, grad_psw, stream
            "tbe_psw_grad")
 
 
+def tbe_check_device_status(handle, stream=None) -> None:
+    """Waits for the stream; raises TBEError (TBE_ERR_DEVICE_WAIT) if a backward call since
+    the last check skipped its update because a device-side wait gave up."""
+    _check(load().tbe_check_device_status(handle, _stream(stream)), "tbe_check_device_status")
+
+
 def tbe_set_option(handle, option: int, value: int) -> None:
     _check(load().tbe_set_option(handle, option, int(value)), "tbe_set_option")
 
@@ -319,6 +328,9 @@ class TBE:
 
     def set_option(self, option, value):
         tbe_set_option(self.handle, option, value)
+
+    def check_device_status(self):
+        tbe_check_device_status(self.handle)
 
     def stage_times(self):
         return tbe_stage_times(self.handle)

@@ -15,6 +15,20 @@
 
 using namespace tbe;
 
+// What a tbe_forward_group call left in a workspace, for the
+// tbe_backward_update_grouped call that must follow it on the same batch.
+struct GroupRecord {
+  const void* workspace;
+  const void* indices;
+  const void* offsets;
+  const float* psw;
+  int32_t B, index_dtype;
+  int64_t n;
+  int64_t long_threshold;  // the handle's option when the grouping was made
+  bool bucket_sort;
+  bool queued;             // its run-length encoding queued the longer runs
+};
+
 struct tbe_handle {
   int32_t T = 0;
   std::vector<int64_t> rows;
@@ -33,6 +47,8 @@ struct tbe_handle {
   std::vector<TableMeta> meta_host;
   TableMeta* meta = nullptr;     // device copy
   uint32_t* flag = nullptr;      // device word for the validation kernel
+  uint32_t* error_mark = nullptr;  // device word: a backward call's wait gave up (sticky)
+  uint32_t spin_limit = 1u << 20;  // TBE_OPTION_SPIN_LIMIT
   // count-matrix forward: eligible tables (device list), the other tables
   // (device list for the gather kernel) and the transposed-table buffer
   std::vector<HistTable> hist_host;
@@ -49,9 +65,8 @@ struct tbe_handle {
   char* split = nullptr;
   int64_t split_cap = 0;
   int32_t split_pstride = 0;
-  // whether the last tbe_forward_group's run-length encoding queued the longer
-  // runs (its tbe_backward_update_grouped must not queue them again)
-  bool grouped_queued = false;
+  // groupings made by tbe_forward_group and not yet used, by workspace
+  std::vector<GroupRecord> groups;
   // profiling: pairs of events handed to timed kernel launches (start and end
   // of that kernel), kept until tbe_stage_times reads them
   bool profile = false;
@@ -207,7 +222,7 @@ struct BwdPlan {
   size_t bytes = 0;
 };
 
-bool plan_backward(const tbe_handle* h, int64_t n, bool vec, BwdPlan* p) {
+bool plan_backward(const tbe_handle* h, int64_t n, bool vec, int64_t long_threshold, BwdPlan* p) {
   p->n = n;
   p->vec = vec;
   const int ve = vec ? 4 : 1;
@@ -239,7 +254,7 @@ bool plan_backward(const tbe_handle* h, int64_t n, bool vec, BwdPlan* p) {
     const int64_t ch = (h->dmax + ve_h - 1) / ve_h;
     p->short_max = 1 << (ch <= kWave ? ceil_log2(next_pow2(ch)) : 6);
   }
-  const SegmentBounds ub = segment_bounds(n, h->long_threshold, kChunk, p->short_max);
+  const SegmentBounds ub = segment_bounds(n, long_threshold, kChunk, p->short_max);
   p->long_ub = ub.longs;
   p->chunks_ub = ub.chunks;
   p->items1_ub = ub.items1;
@@ -274,7 +289,8 @@ bool plan_backward(const tbe_handle* h, int64_t n, bool vec, BwdPlan* p) {
 void fill_backward(const tbe_handle* h, int32_t B, const void* indices, const void* offsets,
                    int32_t index_dtype, int64_t n, const float* psw, const float* grad_output,
                    float lr, float eps, void* workspace, const tbe_runs* runs, bool vec,
-                   const BwdPlan& p, BackwardLaunch* out) {
+                   int64_t long_threshold, bool bucket_sort, const BwdPlan& p,
+                   BackwardLaunch* out) {
   char* w = static_cast<char*>(workspace);
   BackwardLaunch& a = *out;
   a = BackwardLaunch{};
@@ -302,8 +318,10 @@ void fill_backward(const tbe_handle* h, int32_t B, const void* indices, const vo
   a.short_max = p.short_max;
   a.per_table = p.per_table ? 1 : 0;
   a.pstride = p.pstride;
-  a.long_threshold = static_cast<int32_t>(std::min<int64_t>(h->long_threshold, 0x7FFFFFFF));
-  a.bucket_sort = h->bucket_sort ? 1 : 0;
+  a.long_threshold = static_cast<int32_t>(std::min<int64_t>(long_threshold, 0x7FFFFFFF));
+  a.bucket_sort = bucket_sort ? 1 : 0;
+  a.spin_limit = h->spin_limit;
+  a.error_mark = h->error_mark;
   a.chunk = kChunk;
   a.lr = lr;
   a.eps = eps;
@@ -343,6 +361,25 @@ hipError_t launch_front(const BackwardLaunch& a, hipStream_t s, const KernelTime
   return launch_sort_encode(a, s, kt);
 }
 
+// Reads and clears the handle's error mark once the stream's work is done.
+tbe_status check_error_mark(tbe_handle* h, hipStream_t s) {
+  uint32_t mark = 0;
+  if (hipMemcpyAsync(&mark, h->error_mark, sizeof mark, hipMemcpyDeviceToHost, s) != hipSuccess)
+    return TBE_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return TBE_ERR_HIP;
+  if (mark == 0u) return TBE_OK;
+  hipLaunchKernelGGL(fill_u32, dim3(1), dim3(64), 0, s, h->error_mark, 0u, int64_t{1});
+  if (hipGetLastError() != hipSuccess) return TBE_ERR_HIP;
+  return TBE_ERR_DEVICE_WAIT;
+}
+
+constexpr size_t kMaxGroupRecords = 64;
+
+std::vector<GroupRecord>::iterator find_group(tbe_handle* h, const void* workspace) {
+  return std::find_if(h->groups.begin(), h->groups.end(),
+                      [&](const GroupRecord& g) { return g.workspace == workspace; });
+}
+
 tbe_status backward_impl(tbe_handle* h, int32_t B, const void* indices, const void* offsets,
                          int32_t index_dtype, int64_t n, const float* psw,
                          const float* grad_output, float lr, float eps, void* workspace,
@@ -364,26 +401,44 @@ tbe_status backward_impl(tbe_handle* h, int32_t B, const void* indices, const vo
       return TBE_OK;
     }
     const bool vec = h->bwd_vec && aligned(grad_output, 16);
-    BwdPlan p;
-    if (!plan_backward(h, n, vec, &p)) return TBE_ERR_UNSUPPORTED;
     if (!workspace || !aligned(workspace, kAlign)) return TBE_ERR_INVALID_ARGUMENT;
+    // the grouped variant takes the grouping that tbe_forward_group made of this
+    // very batch in this workspace, with the options in force at that time
+    int64_t threshold = h->long_threshold;
+    bool bucket_sort = h->bucket_sort, queued = false;
+    auto rec = find_group(h, workspace);
+    if (!with_front) {
+      if (rec == h->groups.end() || rec->indices != indices || rec->offsets != offsets ||
+          rec->psw != psw || rec->B != B || rec->n != n || rec->index_dtype != index_dtype)
+        return TBE_ERR_INVALID_ARGUMENT;
+      threshold = rec->long_threshold;
+      bucket_sort = rec->bucket_sort;
+      queued = rec->queued;
+    }
+    BwdPlan p;
+    if (!plan_backward(h, n, vec, threshold, &p)) return TBE_ERR_UNSUPPORTED;
     if (workspace_bytes < p.bytes) return TBE_ERR_WORKSPACE_TOO_SMALL;
     if (h->flags & TBE_FLAG_VALIDATE) {
       st = run_validation(h, B, indices, offsets, index_dtype, n, s);
       if (st != TBE_OK) return st;
     }
+    // from here on the workspace is this call's: a grouping left in it is used
+    // (grouped) or overwritten (plain)
+    if (rec != h->groups.end()) h->groups.erase(rec);
     KernelTimer timer{h, take_events};
     const KernelTimer* kt = h->profile ? &timer : nullptr;
     BackwardLaunch a;
     fill_backward(h, B, indices, offsets, index_dtype, n, psw, grad_output, lr, eps, workspace,
-                  runs, vec, p, &a);
-    a.front_queued = (with_front ? uses_bucket_sort(a) : h->grouped_queued) ? 1 : 0;
+                  runs, vec, threshold, bucket_sort, p, &a);
+    a.front_queued = (with_front ? uses_bucket_sort(a) : queued) ? 1 : 0;
     if (with_front) {
       const hipError_t e = launch_front(a, s, kt);
       if (e != hipSuccess) return TBE_ERR_HIP;
     }
-    return from_hip(launch_segment_reduce_update(a, a.buf.keys[p.passes % 2],
-                                                 a.buf.vals[p.passes % 2], s, kt));
+    st = from_hip(launch_segment_reduce_update(a, a.buf.keys[p.passes % 2],
+                                               a.buf.vals[p.passes % 2], s, kt));
+    if (st == TBE_OK && (h->flags & TBE_FLAG_VALIDATE)) st = check_error_mark(h, s);
+    return st;
   } catch (...) {
     return TBE_ERR_OUT_OF_MEMORY;
   }
@@ -402,6 +457,7 @@ const char* tbe_status_string(tbe_status status) {
     case TBE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case TBE_ERR_HIP: return "HIP runtime error";
     case TBE_ERR_OUT_OF_MEMORY: return "out of device memory";
+    case TBE_ERR_DEVICE_WAIT: return "a device-side wait gave up; that backward update was skipped";
   }
   return "unknown status";
 }
@@ -529,9 +585,12 @@ tbe_status tbe_create(const tbe_config* cfg, void* weights, float* optim_state, 
   char* base = static_cast<char*>(block);
   h->meta = static_cast<TableMeta*>(block);
   h->flag = reinterpret_cast<uint32_t*>(base + flag_off);
+  h->error_mark = reinterpret_cast<uint32_t*>(base + flag_off + 128);
   h->hist = hist_bytes ? reinterpret_cast<HistTable*>(base + hist_off) : nullptr;
   h->gather_list = gather_bytes ? reinterpret_cast<int32_t*>(base + gather_off) : nullptr;
-  bool ok = hipMemcpy(h->meta, h->meta_host.data(), meta_bytes, hipMemcpyHostToDevice) == hipSuccess;
+  bool ok = hipMemset(block, 0, gather_off + up(gather_bytes)) == hipSuccess;
+  if (ok)
+    ok = hipMemcpy(h->meta, h->meta_host.data(), meta_bytes, hipMemcpyHostToDevice) == hipSuccess;
   if (ok && hist_bytes)
     ok = hipMemcpy(h->hist, h->hist_host.data(), hist_bytes, hipMemcpyHostToDevice) == hipSuccess;
   if (ok && gather_bytes)
@@ -588,8 +647,17 @@ tbe_status tbe_set_option(tbe_handle* h, int32_t option, int64_t value) {
       if (value != 0 && value != 1) return TBE_ERR_INVALID_ARGUMENT;
       h->bucket_sort = value == 0;
       return TBE_OK;
+    case TBE_OPTION_SPIN_LIMIT:
+      if (value < 0 || value > 0x7FFFFFFF) return TBE_ERR_INVALID_ARGUMENT;
+      h->spin_limit = static_cast<uint32_t>(value);
+      return TBE_OK;
   }
   return TBE_ERR_INVALID_ARGUMENT;
+}
+
+tbe_status tbe_check_device_status(tbe_handle* h, void* stream) {
+  if (!h) return TBE_ERR_INVALID_ARGUMENT;
+  return check_error_mark(h, static_cast<hipStream_t>(stream));
 }
 
 tbe_status tbe_stage_times(tbe_handle* h, float* ms, const char** names, int32_t capacity,
@@ -770,7 +838,7 @@ tbe_status tbe_psw_grad(tbe_handle* h, int32_t B, const void* indices, const voi
 tbe_status tbe_backward_workspace_size(const tbe_handle* h, int32_t B, int64_t n, size_t* bytes) {
   if (!h || !bytes || B < 0 || n < 0) return TBE_ERR_INVALID_ARGUMENT;
   BwdPlan p;
-  if (!plan_backward(h, n, h->bwd_vec, &p)) return TBE_ERR_UNSUPPORTED;
+  if (!plan_backward(h, n, h->bwd_vec, h->long_threshold, &p)) return TBE_ERR_UNSUPPORTED;
   *bytes = p.bytes;
   return TBE_OK;
 }
@@ -805,12 +873,12 @@ tbe_status tbe_forward_group(tbe_handle* h, int32_t B, const void* indices, cons
   const hipStream_t s = static_cast<hipStream_t>(stream);
   try {
     BwdPlan p;
-    if (!plan_backward(h, n, h->bwd_vec, &p)) return TBE_ERR_UNSUPPORTED;
+    if (!plan_backward(h, n, h->bwd_vec, h->long_threshold, &p)) return TBE_ERR_UNSUPPORTED;
     if (!workspace || !aligned(workspace, kAlign)) return TBE_ERR_INVALID_ARGUMENT;
     if (workspace_bytes < p.bytes) return TBE_ERR_WORKSPACE_TOO_SMALL;
     BackwardLaunch a{};
     fill_backward(h, B, indices, offsets, index_dtype, n, psw, nullptr, 0.0f, 0.0f, workspace,
-                  nullptr, h->bwd_vec, p, &a);
+                  nullptr, h->bwd_vec, h->long_threshold, h->bucket_sort, p, &a);
     // ids are checked (when asked) before anything is enqueued
     if (h->flags & TBE_FLAG_VALIDATE) {
       st = run_validation(h, B, indices, offsets, index_dtype, n, s);
@@ -821,14 +889,20 @@ tbe_status tbe_forward_group(tbe_handle* h, int32_t B, const void* indices, cons
     // workspace clear; the pooled lookup with the linearize step in the same
     // launch (the two one after the other for large batches); then the sort
     // and the run-length encoding
+    // a grouping this workspace held before is overwritten from here on
+    auto old = find_group(h, workspace);
+    if (old != h->groups.end()) h->groups.erase(old);
     if (launch_init_workspace(a, s, kt) != hipSuccess) return TBE_ERR_HIP;
     const bool fused = n <= kFusedMaxLookups;
     st = forward_impl(h, B, indices, offsets, index_dtype, n, psw, output, s, false,
                       fused ? &a : nullptr);
     if (st != TBE_OK) return st;
     if (!fused && launch_linearize_kernel(a, s, kt) != hipSuccess) return TBE_ERR_HIP;
-    h->grouped_queued = uses_bucket_sort(a);
-    return from_hip(launch_sort_encode(a, s, kt));
+    if (launch_sort_encode(a, s, kt) != hipSuccess) return TBE_ERR_HIP;
+    if (h->groups.size() >= kMaxGroupRecords) h->groups.erase(h->groups.begin());
+    h->groups.push_back(GroupRecord{workspace, indices, offsets, psw, B, index_dtype, n,
+                                    h->long_threshold, h->bucket_sort, uses_bucket_sort(a)});
+    return TBE_OK;
   } catch (...) {
     return TBE_ERR_OUT_OF_MEMORY;
   }

@@ -330,6 +330,14 @@ struct SegmentBounds {
 };
 SegmentBounds segment_bounds(int64_t n, int64_t long_threshold, int chunk, int short_max);
 
+// A bounded wait of one workgroup for another: past `limit` empty polls it
+// raises *err and stops waiting (limit 0: it gives up at once; the host sets
+// that only to test that a failed call is reported).
+struct WaitCtl {
+  uint32_t* err;
+  uint32_t limit;
+};
+
 struct BackwardLaunch {
   const void* indices;
   const void* offsets;
@@ -354,6 +362,8 @@ struct BackwardLaunch {
   int32_t long_threshold;   // runs at least this long use split accumulation
   int32_t chunk;            // lookups per level-1 partial
   int32_t bucket_sort;      // two-digit ids: high-digit pass + bucket-local sort and RLE
+  uint32_t spin_limit;      // polls before a waiting workgroup gives up
+  uint32_t* error_mark;     // handle's device word: set when a call gave up (sticky)
   float lr, eps;
   int32_t* out_unique;      // optional run outputs
   int32_t* out_lengths;

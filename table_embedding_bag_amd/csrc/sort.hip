@@ -32,9 +32,10 @@
 // A tile only waits for tiles numbered before it, which publish their counts
 // before they wait themselves.  When the grid is small enough to be resident
 // all at once, tiles are numbered by workgroup id; otherwise by an atomic
-// ticket taken when a workgroup starts, so every tile waited for is running.  Every wait is bounded: past a spin
-// limit the workgroup raises an error flag and stops waiting, so no wave can
-// hang.
+// ticket taken when a workgroup starts, so every tile waited for is running.
+// Every wait is bounded: past a spin limit (set per handle) the workgroup
+// raises an error flag and stops waiting, so no wave can hang; the segment
+// kernels then update nothing and the handle is marked.
 #include "common.hpp"
 #include "linearize.hpp"
 
@@ -44,7 +45,6 @@ namespace {
 constexpr uint32_t kFlagAgg = 1u << 30;     // status word: this tile's own count
 constexpr uint32_t kFlagIncl = 2u << 30;    // status word: count up to and including this tile
 constexpr uint32_t kValueMask = (1u << 30) - 1u;
-constexpr uint32_t kSpinLimit = 1u << 20;   // polls before a waiting tile gives up
 constexpr int kResidentTiles = 256;         // grids this small are resident all at once
 
 template <typename IT>
@@ -76,14 +76,19 @@ __global__ __launch_bounds__(kLinThreads) void linearize_kernel(BackwardLaunch a
 
 // Counts of digits d0 .. d0 + DPT - 1 in all tiles before `tile` (decoupled
 // look-back; every digit keeps DEPTH status words in flight per round).
-// status rows have `slots` words per tile.
+// status rows have `slots` words per tile.  A wait that gives up leaves excl
+// at most the true count, so every position derived from it stays in range.
 template <int DPT, int DEPTH>
-__device__ void lookback_digits(uint32_t* status, int slots, int tile, int d0, uint32_t* err,
+__device__ void lookback_digits(uint32_t* status, int slots, int tile, int d0, WaitCtl wait,
                                 uint32_t (&excl)[DPT]) {
   int j[DPT];
   bool done[DPT];
 #pragma unroll
   for (int q = 0; q < DPT; ++q) excl[q] = 0u, j[q] = tile - 1, done[q] = false;
+  if (wait.limit == 0u) {
+    atomicOr(wait.err, 1u);
+    return;
+  }
   uint32_t spins = 0;
   while (true) {
     uint32_t w[DPT][DEPTH];
@@ -119,8 +124,8 @@ __device__ void lookback_digits(uint32_t* status, int slots, int tile, int d0, u
     }
     if (all_done) return;
     if (!moved) {
-      if (++spins > kSpinLimit) {
-        atomicOr(err, 1u);
+      if (++spins > wait.limit) {
+        atomicOr(wait.err, 1u);
         return;
       }
       __builtin_amdgcn_s_sleep(2);
@@ -193,7 +198,7 @@ template <int KPT, int RB>
 __global__ __launch_bounds__(kBlock) void radix_pass(
     const uint32_t* __restrict__ kin, const uint32_t* __restrict__ vin, uint32_t* __restrict__ kout,
     uint32_t* __restrict__ vout, int64_t n, int shift, int bits, const uint32_t* __restrict__ totals,
-    uint32_t* status, uint32_t* ticket, uint32_t* err, uint32_t* wtable) {
+    uint32_t* status, uint32_t* ticket, WaitCtl wait, uint32_t* wtable) {
   constexpr int TS = kBlock * KPT;
   constexpr int RMAX = 1 << RB;
   constexpr int DPT = RMAX / kBlock;
@@ -277,7 +282,7 @@ __global__ __launch_bounds__(kBlock) void radix_pass(
 #pragma unroll
   for (int q = 0; q < DPT; ++q) before[q] = 0u;
   if (tile > 0) {
-    lookback_digits<DPT, DEPTH>(status, RMAX, tile, d0, err, before);
+    lookback_digits<DPT, DEPTH>(status, RMAX, tile, d0, wait, before);
 #pragma unroll
     for (int q = 0; q < DPT; ++q)
       st_status(my_status + q, kFlagIncl | ((before[q] + mine[q]) & kValueMask));
@@ -346,7 +351,7 @@ template <int KPT, int RB>
 __global__ __launch_bounds__(1024) void radix_pass_wide(
     const uint32_t* __restrict__ kin, const uint32_t* __restrict__ vin, uint32_t* __restrict__ kout,
     uint32_t* __restrict__ vout, int64_t n, int shift, int bits, const uint32_t* __restrict__ totals,
-    uint32_t* status, uint32_t* ticket, uint32_t* err, uint32_t* wtable) {
+    uint32_t* status, uint32_t* ticket, WaitCtl wait, uint32_t* wtable) {
   constexpr int NT = 1024, NW = NT / kWave;
   constexpr int TS = NT * KPT;
   constexpr int RMAX = 1 << RB;
@@ -412,7 +417,7 @@ __global__ __launch_bounds__(1024) void radix_pass_wide(
     record_window(wtable, gb, my_total, tid);
   uint32_t before[1] = {0u};
   if (tile > 0) {
-    lookback_digits<1, 16>(status, RMAX, tile, tid, err, before);
+    lookback_digits<1, 16>(status, RMAX, tile, tid, wait, before);
     st_status(my_status, kFlagIncl | ((before[0] + mine) & kValueMask));
   }
   s_gbase[tid] = gb + before[0];
@@ -447,11 +452,16 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
 }
 
 // Sum of the values of all tiles before `tile` (one status word per tile; a
-// whole wave reads 64 predecessors at once).
-__device__ uint32_t lookback_wave(uint32_t* status, int tile, uint32_t* err) {
+// whole wave reads 64 predecessors at once).  A wait that gives up returns at
+// most the true sum.
+__device__ uint32_t lookback_wave(uint32_t* status, int tile, WaitCtl wait) {
   const int lane = lane_id();
   uint32_t excl = 0;
   int j = tile - 1;
+  if (wait.limit == 0u) {
+    if (lane == 0) atomicOr(wait.err, 1u);
+    return 0u;
+  }
   uint32_t spins = 0;
   while (true) {
     const int idx = j - lane;
@@ -466,8 +476,8 @@ __device__ uint32_t lookback_wave(uint32_t* status, int tile, uint32_t* err) {
     if (first_in < first_nr) return excl;
     j -= take;
     if (take == 0) {
-      if (++spins > kSpinLimit) {
-        if (lane == 0) atomicOr(err, 1u);
+      if (++spins > wait.limit) {
+        if (lane == 0) atomicOr(wait.err, 1u);
         return excl;
       }
       __builtin_amdgcn_s_sleep(2);
@@ -482,7 +492,8 @@ __global__ __launch_bounds__(1024) void rle_kernel(const uint32_t* __restrict__ 
                                                      const uint32_t* __restrict__ vals, int64_t n,
                                                      int ntiles, uint32_t* status, uint32_t* ticket,
                                                      uint32_t* counters, uint32_t* unique_keys,
-                                                     uint32_t* run_start, uint32_t* run_first) {
+                                                     uint32_t* run_start, uint32_t* run_first,
+                                                     uint32_t spin_limit) {
   constexpr int NT = 1024;
   constexpr int PER = kRleTile / NT;
   __shared__ uint32_t s_k[kRleTile + 1];
@@ -519,7 +530,7 @@ __global__ __launch_bounds__(1024) void rle_kernel(const uint32_t* __restrict__ 
   if (tid < kWave) {
     if (tid == 0) st_status(status + tile, (tile == 0 ? kFlagIncl : kFlagAgg) | total);
     uint32_t before = 0;
-    if (tile > 0) before = lookback_wave(status, tile, counters + kCntError);
+    if (tile > 0) before = lookback_wave(status, tile, WaitCtl{counters + kCntError, spin_limit});
     if (tid == 0) {
       if (tile > 0) st_status(status + tile, kFlagIncl | ((before + total) & kValueMask));
       s_base = before;
@@ -677,7 +688,7 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
     uint32_t* vout, int64_t n, int lbits, int nbuckets, const uint32_t* __restrict__ htotals,
     const uint32_t* __restrict__ wtable, int ntiles, uint32_t* status, uint32_t* ticket,
     uint32_t* counters, uint32_t* unique_keys, uint32_t* run_start, uint32_t* run_first,
-    RunQueue q) {
+    RunQueue q, uint32_t spin_limit) {
   constexpr int NT = kBucketThreads, NW = kBucketWaves, CAP = kBucketCap;
   __shared__ uint32_t s_k[CAP];
   __shared__ uint32_t s_v[CAP];
@@ -763,8 +774,14 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
           }
         }
         __syncthreads();
+        // a key's bucket lies in [hf, hl]; the clamp only matters for a batch
+        // whose pass on the high digit gave up a wait (its output then holds
+        // stale positions), and keeps the LDS counters in range
         const uint32_t hmask = static_cast<uint32_t>(nbuckets) - 1u;
-        const auto bucket = [lbits, hf, hmask](uint32_t k) { return ((k >> lbits) & hmask) - hf; };
+        const uint32_t hspan = hl - hf;
+        const auto bucket = [lbits, hf, hmask, hspan](uint32_t k) {
+          return min(((k >> lbits) & hmask) - hf, hspan);
+        };
         lds_counting_pass(key, val, rr, 0, len, bucket, s_k, s_v, s_cnt, s_slots, s_dstart,
                           scratch);
       }
@@ -878,7 +895,7 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
   const uint32_t x_lc = block_excl_n<NW>(need_lc, scratch, &t_lc);
   if (tid < kWave) {
     uint32_t before = 0;
-    if (tile > 0) before = lookback_wave(status, tile, counters + kCntError);
+    if (tile > 0) before = lookback_wave(status, tile, WaitCtl{counters + kCntError, spin_limit});
     if (tid == 0) {
       if (tile > 0) st_status(status + tile, kFlagIncl | ((before + htotal) & kValueMask));
       s_base = before;
@@ -1045,15 +1062,15 @@ hipError_t launch_pass(const BackwardLaunch& a, int pass, int shift, const uint3
   if (bits > 8)
     launch_timed(kt, "radix_pass", radix_pass_wide<4, 10>, dim3(ntiles), dim3(1024), 0, stream,
                  kin, vin, kout, vout, n, shift, bits, totals, status, ticket,
-                 a.buf.counters + kCntError, wtable);
+                 WaitCtl{a.buf.counters + kCntError, a.spin_limit}, wtable);
   else if (kpt == 8)
     launch_timed(kt, "radix_pass", radix_pass<8, 8>, dim3(ntiles), dim3(kBlock), 0, stream, kin,
                  vin, kout, vout, n, shift, bits, totals, status, ticket,
-                 a.buf.counters + kCntError, wtable);
+                 WaitCtl{a.buf.counters + kCntError, a.spin_limit}, wtable);
   else
     launch_timed(kt, "radix_pass", radix_pass<32, 8>, dim3(ntiles), dim3(kBlock), 0, stream, kin,
                  vin, kout, vout, n, shift, bits, totals, status, ticket,
-                 a.buf.counters + kCntError, wtable);
+                 WaitCtl{a.buf.counters + kCntError, a.spin_limit}, wtable);
   return hipGetLastError();
 }
 
@@ -1110,7 +1127,8 @@ hipError_t launch_sort_encode(const BackwardLaunch& a, hipStream_t stream, const
                windows <= kResidentTiles ? nullptr : a.buf.tickets + kMaxRadixPasses,
                a.buf.counters, a.buf.unique_keys, a.buf.run_start, a.buf.run_first,
                RunQueue{a.buf.items1, a.buf.longs, a.buf.long_keys, a.short_max,
-                        a.long_threshold, a.chunk});
+                        a.long_threshold, a.chunk},
+               a.spin_limit);
   return hipGetLastError();
 }
 
@@ -1122,7 +1140,7 @@ hipError_t launch_run_length_encode(const BackwardLaunch& a, const uint32_t* sor
   launch_timed(kt, "rle_kernel", rle_kernel, dim3(ntiles), dim3(1024), 0, stream, sorted_keys,
                sorted_vals, n, ntiles, a.buf.rle_status,
                ntiles <= kResidentTiles ? nullptr : a.buf.tickets + kMaxRadixPasses,
-               a.buf.counters, a.buf.unique_keys, a.buf.run_start, a.buf.run_first);
+               a.buf.counters, a.buf.unique_keys, a.buf.run_start, a.buf.run_first, a.spin_limit);
   return hipGetLastError();
 }
 

@@ -115,3 +115,11 @@ def test_forced_histogram_rejects_per_sample_weights():
     with pytest.raises(tbe.TBEError, match="UNSUPPORTED"):
         pb.op.forward(spec.B, pb.idx, pb.off, psw)
     pb.op.close()
+
+
+@pytest.mark.timeout(900)
+def test_count_matrix_forward_on_the_64_small_tables_at_full_size():
+    """Every table of the many-small-tables batch (64 bf16 tables of 64..1024 rows, dim 64,
+    B = 32768 bags of 8 uniform lookups: 16.8 M lookups) through the count-matrix forward,
+    two steps with the backward in between; sampled bags and rows."""
+    parity(workloads.config(5), seed=0, steps=2, bag_sample=20000, row_sample=50000, flags=FORCE)

@@ -13,8 +13,9 @@ import torch
 import oracle
 import table_embedding_bag_amd as tbe
 import workloads
-from gpu_check import (carry_deviation, check_forward, check_runs, check_update, make_problem,
-                       reference_update, rows_of, run_step, to_device, untouched_identical)
+from gpu_check import (carry_deviation, check_forward, check_runs, check_update, guarded_empty,
+                       make_problem, reference_update, rows_of, run_step, to_device,
+                       untouched_identical)
 
 pytestmark = pytest.mark.gpu
 
@@ -47,11 +48,13 @@ def parity(spec, seed=0, steps=2, bag_sample=None, row_sample=None, index_dtype=
             sample = np.unique(np.concatenate([
                 rng.choice(nbags, bag_sample, replace=False),
                 np.arange(spec.T) * spec.B, np.arange(1, spec.T + 1) * spec.B - 1]))
+        ybuf, Y = guarded_empty((spec.B, spec.sum_dims), torch.float32)
         if grouped:
-            Y = pb.op.forward_group(spec.B, pb.idx, pb.off, pb.psw)
+            pb.op.forward_group(spec.B, pb.idx, pb.off, pb.psw, out=Y)
         else:
-            Y = pb.op.forward(spec.B, pb.idx, pb.off, pb.psw)
+            pb.op.forward(spec.B, pb.idx, pb.off, pb.psw, out=Y)
         torch.cuda.synchronize()
+        pb.check_guards(ybuf)
         report[f"fwd{step}"] = check_forward(pb, Y, W_host, sample, dev)
         _say(f"  step {step}: forward ok (max rel {report[f'fwd{step}']:.2e})")
 
@@ -86,6 +89,7 @@ def parity(spec, seed=0, steps=2, bag_sample=None, row_sample=None, index_dtype=
         if untouched.size:
             untouched_identical(spec, gpu_before, rows_of(spec, pb.W, untouched),
                                 gpu_st_before, st_gpu, untouched)
+        pb.check_guards()
         _say(f"  step {step}: update ok (worst {report[f'upd{step}']:.3f})")
     pb.op.close()
     return report

@@ -4,6 +4,11 @@ TEST INFRASTRUCTURE ONLY: tests, the smoke check and the benchmark's CPU
 baseline use this to check the GPU library.  The product package never
 imports it.  All arithmetic is fp64; see ``tbe_oracle.c`` for what each
 function computes and which page passage it follows.
+
+``build_timed`` compiles the same source with fp32 accumulators for the
+benchmark's CPU baseline only (``-O3 -march=native``, so it is built on the
+host that runs it); every function below takes ``lib=`` to run on it.  The
+fp64 build is the only one the tests compare against.
 """
 from __future__ import annotations
 
@@ -34,13 +39,33 @@ def build() -> str:
     return _LIB
 
 
+def build_timed(path: str) -> str:
+    """Compile the fp32-accumulator timing build of the oracle to ``path``, tuned for the
+    CPU this runs on (CPU baseline only; never a parity reference)."""
+    tmp = path + ".tmp"
+    subprocess.check_call(
+        ["gcc", "-O3", "-march=native", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+         "-DORACLE_ACC=float", "-o", tmp, _SRC, "-lm"])
+    os.replace(tmp, path)
+    return path
+
+
+def load_timed(path: str):
+    """The timing build at ``path`` (see build_timed), for the ``lib=`` argument."""
+    return _bind(ctypes.CDLL(path))
+
+
 def _load():
     global _lib
     if _lib is not None:
         return _lib
     if not os.path.exists(_LIB):
         build()
-    lib = ctypes.CDLL(_LIB)
+    _lib = _bind(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def _bind(lib):
     P = ctypes.c_void_p
     i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
     lib.tbe_oracle_widen.argtypes = [i32, ctypes.c_uint32]
@@ -68,7 +93,6 @@ def _load():
     lib.tbe_oracle_set_threads.restype = None
     lib.tbe_oracle_get_threads.argtypes = []
     lib.tbe_oracle_get_threads.restype = i32
-    _lib = lib
     return lib
 
 
@@ -120,12 +144,13 @@ def narrow(dtype: int, x: np.ndarray) -> np.ndarray:
     return out
 
 
-def forward(rows, dims, dtype, pooling, weights, B, indices, offsets, psw=None):
+def forward(rows, dims, dtype, pooling, weights, B, indices, offsets, psw=None, lib=None):
     """Y [B, sum(dims)] float64."""
     rows, dims, indices, offsets, psw = _i64(rows), _i32(dims), _i64(indices), _i64(offsets), _f32(psw)
     w = _storage_view(dtype, weights)
     out = np.empty((B, int(dims.sum())), dtype=np.float64)
-    rc = _load().tbe_oracle_forward(len(rows), _ptr(rows), _ptr(dims), dtype, pooling, _ptr(w), B,
+    rc = (lib or _load()).tbe_oracle_forward(len(rows), _ptr(rows), _ptr(dims), dtype, pooling,
+                                             _ptr(w), B,
                                     _ptr(indices), _ptr(offsets), indices.size, _ptr(psw), _ptr(out))
     _check(rc, "forward")
     return out
@@ -182,7 +207,7 @@ def psw_grad(rows, dims, dtype, pooling, weights, B, indices, offsets, grad_outp
 
 
 def backward_update(rows, dims, dtype, pooling, optimizer, weights, state, B, indices, offsets,
-                    psw, grad_output, lr, eps, selected_rows=None):
+                    psw, grad_output, lr, eps, selected_rows=None, lib=None):
     """Apply one optimizer step in place on ``weights`` (storage dtype) and ``state`` (fp32)."""
     rows, dims, indices, offsets, psw = _i64(rows), _i32(dims), _i64(indices), _i64(offsets), _f32(psw)
     g = np.ascontiguousarray(grad_output, dtype=np.float32)
@@ -195,16 +220,17 @@ def backward_update(rows, dims, dtype, pooling, optimizer, weights, state, B, in
     nsel = 0 if sel is None else sel.size
     if sel is not None and nsel == 0:
         return
-    rc = _load().tbe_oracle_backward_update(len(rows), _ptr(rows), _ptr(dims), dtype, pooling,
+    rc = (lib or _load()).tbe_oracle_backward_update(len(rows), _ptr(rows), _ptr(dims), dtype,
+                                                     pooling,
                                             optimizer, _ptr(w), _ptr(state), B, _ptr(indices),
                                             _ptr(offsets), indices.size, _ptr(psw), _ptr(g),
                                             float(lr), float(eps), nsel, _ptr(sel))
     _check(rc, "backward_update")
 
 
-def set_threads(n: int) -> None:
-    _load().tbe_oracle_set_threads(int(n))
+def set_threads(n: int, lib=None) -> None:
+    (lib or _load()).tbe_oracle_set_threads(int(n))
 
 
-def get_threads() -> int:
-    return int(_load().tbe_oracle_get_threads())
+def get_threads(lib=None) -> int:
+    return int((lib or _load()).tbe_oracle_get_threads())

@@ -55,6 +55,16 @@
 #include <omp.h>
 #endif
 
+/* Accumulator of the sums and of the update.  The default, double, is the
+ * parity reference the tests compare against.  The same source compiled with
+ * -DORACLE_ACC=float is the timing build (fp32 sums, as a plain CPU
+ * implementation would run); it is timed as a CPU baseline and never used as
+ * a reference. */
+#ifndef ORACLE_ACC
+#define ORACLE_ACC double
+#endif
+typedef ORACLE_ACC acc_t;
+
 /* ------------------------------------------------------------------------ */
 /* Storage conversions                                                       */
 /* ------------------------------------------------------------------------ */
@@ -210,23 +220,23 @@ static int check_batch(const layout_t* L, int64_t B, const int64_t* indices,
 /* Forward                                                                   */
 /* ------------------------------------------------------------------------ */
 
-/* Pool one bag into out[0 .. dims[t]). */
+/* Pool one bag into out[0 .. dims[t]): every column summed over the bag's
+ * lookups in index order, then divided by the bag length for mean pooling. */
 static void pool_bag(const layout_t* L, int32_t dtype, int32_t pooling, const void* weights,
                      int64_t B, const int64_t* indices, const int64_t* offsets,
                      const float* psw, int64_t k, double* out) {
   const int64_t t = k / B;
   const int64_t D = L->dims[t];
   const int64_t begin = offsets[k], end = offsets[k + 1];
-  for (int64_t d = 0; d < D; ++d) out[d] = 0.0;
-  for (int64_t i = begin; i < end; ++i) {
-    const double p = psw ? (double)psw[i] : 1.0;
-    const int64_t row = L->woff[t] + indices[i] * D;
-    for (int64_t d = 0; d < D; ++d)
-      out[d] += p * tbe_oracle_widen(dtype, load_bits(dtype, weights, row + d));
-  }
-  if (pooling == ORACLE_POOL_MEAN && end > begin) {
-    const double len = (double)(end - begin);
-    for (int64_t d = 0; d < D; ++d) out[d] /= len;
+  for (int64_t d = 0; d < D; ++d) {
+    acc_t acc = 0;
+    for (int64_t i = begin; i < end; ++i) {
+      const acc_t p = psw ? (acc_t)psw[i] : (acc_t)1;
+      const int64_t e = L->woff[t] + indices[i] * D + d;
+      acc += p * (acc_t)tbe_oracle_widen(dtype, load_bits(dtype, weights, e));
+    }
+    if (pooling == ORACLE_POOL_MEAN && end > begin) acc /= (acc_t)(end - begin);
+    out[d] = (double)acc;
   }
 }
 
@@ -358,18 +368,21 @@ static int32_t table_of_key(const layout_t* L, int64_t key) {
   return t;
 }
 
-/* Gamma of the run e[begin..end) (all with the same key), in lookup order. */
+/* Gamma of the run e[begin..end) (all with the same key): every column summed
+ * over the run's lookups in lookup order. */
 static void run_gradient(const layout_t* L, int32_t pooling, int64_t B, const int64_t* offsets,
                          const float* psw, const float* grad_output, const entry_t* e,
                          int64_t begin, int64_t end, int32_t t, double* gamma) {
   const int64_t D = L->dims[t];
-  for (int64_t d = 0; d < D; ++d) gamma[d] = 0.0;
-  for (int64_t j = begin; j < end; ++j) {
-    const int64_t k = e[j].bag, b = k % B;
-    double coef = psw ? (double)psw[e[j].lookup] : 1.0;
-    if (pooling == ORACLE_POOL_MEAN) coef /= (double)(offsets[k + 1] - offsets[k]);
-    const float* g = grad_output + b * L->sum_dims + L->doff[t];
-    for (int64_t d = 0; d < D; ++d) gamma[d] += coef * (double)g[d];
+  for (int64_t d = 0; d < D; ++d) {
+    acc_t acc = 0;
+    for (int64_t j = begin; j < end; ++j) {
+      const int64_t k = e[j].bag, b = k % B;
+      acc_t coef = psw ? (acc_t)psw[e[j].lookup] : (acc_t)1;
+      if (pooling == ORACLE_POOL_MEAN) coef /= (acc_t)(offsets[k + 1] - offsets[k]);
+      acc += coef * (acc_t)grad_output[b * L->sum_dims + L->doff[t] + d];
+    }
+    gamma[d] = (double)acc;
   }
 }
 
@@ -498,17 +511,18 @@ int tbe_oracle_backward_update(int32_t T, const int64_t* rows, const int32_t* di
           run_gradient(&L, pooling, B, offsets, psw, grad_output, e, starts[r], starts[r + 1], t,
                        gamma);
           const int64_t row = L.woff[t] + (key - L.roff[t]) * D;
-          double step = lr; /* SGD: W <- W - lr * Gamma */
+          acc_t step = (acc_t)lr; /* SGD: W <- W - lr * Gamma */
           if (optimizer == ORACLE_OPT_ROWWISE_ADAGRAD) {
-            double sq = 0.0;
-            for (int64_t d = 0; d < D; ++d) sq += gamma[d] * gamma[d];
-            const double m = (double)state[key] + sq / (double)D;
+            acc_t sq = 0;
+            for (int64_t d = 0; d < D; ++d) sq += (acc_t)gamma[d] * (acc_t)gamma[d];
+            const acc_t m = (acc_t)state[key] + sq / (acc_t)D;
             state[key] = (float)m;
-            step = lr / (sqrt(m) + eps);
+            step = (acc_t)lr / ((acc_t)sqrt((double)m) + (acc_t)eps);
           }
           for (int64_t d = 0; d < D; ++d) {
-            const double w = tbe_oracle_widen(dtype, load_bits(dtype, weights, row + d));
-            store_bits(dtype, weights, row + d, tbe_oracle_narrow(dtype, w - step * gamma[d]));
+            const acc_t w = (acc_t)tbe_oracle_widen(dtype, load_bits(dtype, weights, row + d));
+            const acc_t w_new = w - step * (acc_t)gamma[d];
+            store_bits(dtype, weights, row + d, tbe_oracle_narrow(dtype, (double)w_new));
           }
         }
         free(gamma);

@@ -232,3 +232,27 @@ def test_invalid_batches_are_rejected(bad):
     W = np.zeros(40, dtype=np.float32)
     with pytest.raises(ValueError):
         oracle.forward([10], [4], oracle.F32, oracle.POOL_SUM, W, 2, idx, off)
+
+
+def test_timing_build_agrees_with_the_reference_to_fp32_rounding(tmp_path):
+    """The CPU-baseline build (same source, fp32 accumulators) computes the same thing:
+    its forward and its update agree with the fp64 reference to fp32 rounding.  It is only
+    ever timed; parity always uses the fp64 build."""
+    lib = oracle.load_timed(oracle.build_timed(str(tmp_path / "libtbe_oracle_f32.so")))
+    spec = workloads.custom([300, 41], [16, 8], "f32", B=64, lengths=("uniform_int", 0, 20),
+                            index_dist=("zipf", 1.2), optimizer="rowwise_adagrad", psw=True)
+    batch = workloads.batch(spec, seed=3)
+    W = workloads.storage_numpy(workloads.weights(spec, 3)).copy()
+    G = workloads.grad_output(spec, 3).numpy()
+    args = (spec.rows, spec.dims, oracle.F32, oracle.POOL_SUM)
+    Y64 = oracle.forward(*args, W, spec.B, batch.indices, batch.offsets, batch.psw)
+    Y32 = oracle.forward(*args, W, spec.B, batch.indices, batch.offsets, batch.psw, lib=lib)
+    scale = oracle.forward(*args, np.abs(W), spec.B, batch.indices, batch.offsets, np.abs(batch.psw))
+    assert (np.abs(Y32 - Y64) <= 1e-5 * scale + 1e-30).all()
+    W64, W32 = W.copy(), W.copy()
+    s64, s32 = np.zeros(spec.sum_rows, np.float32), np.zeros(spec.sum_rows, np.float32)
+    for Wx, sx, lb in ((W64, s64, None), (W32, s32, lib)):
+        oracle.backward_update(*args, oracle.OPT_ROWWISE_ADAGRAD, Wx, sx, spec.B, batch.indices,
+                               batch.offsets, batch.psw, G, 0.01, 1e-8, lib=lb)
+    assert np.allclose(s32, s64, rtol=1e-5, atol=0)
+    assert np.all(np.abs(W32 - W64) <= 1e-5 * (np.abs(W) + 0.01))

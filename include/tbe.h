@@ -214,6 +214,27 @@ tbe_status tbe_backward_update(tbe_handle* handle, int32_t B, const void* indice
                                float lr, float eps, void* workspace, size_t workspace_bytes,
                                const tbe_runs* runs, void* stream);
 
+/* tbe_backward_update for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, bit for bit, with the workspace
+ * taken from a static device array of TBE_STATIC_SCRATCH_BYTES inside the
+ * library (one per GPU, held until the process ends) instead of a caller
+ * buffer.  Allocates nothing, neither device nor host memory, and records no
+ * kernel timings (TBE_OPTION_PROFILE does not apply).  A batch whose
+ * tbe_backward_workspace_size exceeds TBE_STATIC_SCRATCH_BYTES gets
+ * TBE_ERR_WORKSPACE_TOO_SMALL with nothing enqueued.  Every call on one GPU,
+ * from any handle, uses that GPU's one array: calls that overlap in time on
+ * one GPU (several streams, or host threads) race on it and give undefined
+ * results; calls ordered on one stream are fine.  Other arguments and errors
+ * as tbe_backward_update; TBE_ERR_HIP if the array's address could not be
+ * found. */
+#define TBE_STATIC_SCRATCH_BYTES (64u << 20)
+tbe_status tbe_backward_update_no_alloc(tbe_handle* handle, int32_t B, const void* indices,
+                                        const void* offsets, int32_t index_dtype,
+                                        int64_t num_indices, const float* per_sample_weights,
+                                        const float* grad_output, float lr, float eps,
+                                        const tbe_runs* runs, void* stream);
+
 /* Forward plus the backward's grouping of the same batch.  kimbodo.com/?p=28372,
  * "Kimbodo Engineering Perspective": the transpose, sort and run-length
  * encoding of the backward can be done during the forward (an option that is

@@ -20,7 +20,8 @@ __all__ = [
     "TBEError", "library_path", "load", "tbe_create", "tbe_destroy", "tbe_forward",
     "tbe_backward_workspace_size", "tbe_backward_update", "tbe_forward_group",
     "tbe_backward_update_grouped", "tbe_psw_grad", "tbe_set_option", "tbe_stage_times",
-    "tbe_status_string", "tbe_abi_version", "tbe_check_device_status", "TBE",
+    "tbe_status_string", "tbe_abi_version", "tbe_check_device_status",
+    "tbe_backward_update_no_alloc", "STATIC_SCRATCH_BYTES", "TBE",
     "F32", "F16", "BF16", "POOL_SUM", "POOL_MEAN", "OPT_SGD", "OPT_ROWWISE_ADAGRAD",
     "FLAG_VALIDATE", "FLAG_NO_HISTOGRAM", "FLAG_FORCE_HISTOGRAM", "FLAG_HISTOGRAM",
     "FLAG_SPLIT_BAGS",
@@ -35,6 +36,7 @@ OPT_SGD, OPT_ROWWISE_ADAGRAD = 0, 1
 FLAG_VALIDATE, FLAG_NO_HISTOGRAM, FLAG_FORCE_HISTOGRAM, FLAG_HISTOGRAM = 1, 2, 4, 8
 FLAG_SPLIT_BAGS = 16
 OPTION_LONG_RUN_THRESHOLD, OPTION_PROFILE, OPTION_SORT, OPTION_SPIN_LIMIT = 1, 2, 3, 4
+STATIC_SCRATCH_BYTES = 64 << 20   # TBE_STATIC_SCRATCH_BYTES
 
 STATUS = {
     0: "TBE_OK", 1: "TBE_ERR_INVALID_ARGUMENT", 2: "TBE_ERR_UNSUPPORTED",
@@ -46,7 +48,7 @@ EXPORTED_SYMBOLS = (
     "tbe_create", "tbe_destroy", "tbe_forward", "tbe_backward_workspace_size",
     "tbe_backward_update", "tbe_forward_group", "tbe_backward_update_grouped", "tbe_psw_grad",
     "tbe_set_option", "tbe_stage_times", "tbe_status_string", "tbe_abi_version",
-    "tbe_check_device_status",
+    "tbe_check_device_status", "tbe_backward_update_no_alloc",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -96,6 +98,8 @@ def load():
                                         ctypes.c_size_t, ctypes.POINTER(_Runs), P]
     lib.tbe_forward_group.argtypes = [P, i32, P, P, i32, i64, P, P, P, ctypes.c_size_t, P]
     lib.tbe_backward_update_grouped.argtypes = lib.tbe_backward_update.argtypes
+    lib.tbe_backward_update_no_alloc.argtypes = [P, i32, P, P, i32, i64, P, P, f32, f32,
+                                                 ctypes.POINTER(_Runs), P]
     lib.tbe_psw_grad.argtypes = [P, i32, P, P, i32, i64, P, P, P]
     lib.tbe_set_option.argtypes = [P, i32, i64]
     lib.tbe_check_device_status.argtypes = [P, P]
@@ -107,7 +111,8 @@ def load():
     lib.tbe_abi_version.restype = i32
     for name in ("tbe_create", "tbe_forward", "tbe_backward_workspace_size", "tbe_backward_update",
                  "tbe_forward_group", "tbe_backward_update_grouped", "tbe_psw_grad",
-                 "tbe_set_option", "tbe_stage_times", "tbe_check_device_status"):
+                 "tbe_set_option", "tbe_stage_times", "tbe_check_device_status",
+                 "tbe_backward_update_no_alloc"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -207,6 +212,20 @@ def tbe_backward_update(handle, B: int, indices, offsets, per_sample_weights, gr
                                       _ptr(per_sample_weights), _ptr(grad_output), float(lr),
                                       float(eps), _ptr(workspace), nbytes, r, _stream(stream)),
            "tbe_backward_update")
+
+
+def tbe_backward_update_no_alloc(handle, B: int, indices, offsets, per_sample_weights,
+                                 grad_output, lr: float, eps: float, runs=None,
+                                 stream=None) -> None:
+    """tbe_backward_update on the library's static device scratch (no workspace argument)."""
+    r = None
+    if runs is not None:
+        r = ctypes.byref(_Runs(_ptr(runs[0]), _ptr(runs[1]), _ptr(runs[2])))
+    _check(load().tbe_backward_update_no_alloc(handle, B, _ptr(indices), _ptr(offsets),
+                                               _index_dtype(indices, offsets), indices.numel(),
+                                               _ptr(per_sample_weights), _ptr(grad_output),
+                                               float(lr), float(eps), r, _stream(stream)),
+           "tbe_backward_update_no_alloc")
 
 
 def tbe_forward_group(handle, B: int, indices, offsets, per_sample_weights, output, workspace,

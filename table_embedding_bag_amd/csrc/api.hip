@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -14,6 +15,13 @@
 #include "tbe.h"
 
 using namespace tbe;
+
+// The workspace of tbe_backward_update_no_alloc, for callers that cannot
+// allocate: one copy per GPU the library runs on, held until the process
+// ends.  In host code this name stands for the array, not for its device
+// address: kernels and copies get the address that hipGetSymbolAddress
+// returns for the current device (static_scratch_address below).
+static __device__ __align__(256) unsigned char scratch[TBE_STATIC_SCRATCH_BYTES];
 
 // What a tbe_forward_group call left in a workspace, for the
 // tbe_backward_update_grouped call that must follow it on the same batch.
@@ -49,6 +57,7 @@ struct tbe_handle {
   uint32_t* flag = nullptr;      // device word for the validation kernel
   uint32_t* error_mark = nullptr;  // device word: a backward call's wait gave up (sticky)
   uint32_t spin_limit = 1u << 20;  // TBE_OPTION_SPIN_LIMIT
+  void* static_scratch = nullptr;  // device address of `scratch` on this handle's device
   // count-matrix forward: eligible tables (device list), the other tables
   // (device list for the gather kernel) and the transposed-table buffer
   std::vector<HistTable> hist_host;
@@ -76,6 +85,22 @@ struct tbe_handle {
 };
 
 namespace {
+
+// Device address of `scratch` on each device, looked up once per device (with
+// that device current) by the first tbe_create on it.
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mutex;
+void* g_scratch_address[kMaxDevices] = {};
+
+void* static_scratch_address(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_address[device]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess) g_scratch_address[device] = p;
+  }
+  return g_scratch_address[device];
+}
 
 constexpr int kChunk = 256;       // lookups per level-1 partial of a long run
 constexpr size_t kAlign = 256;
@@ -384,7 +409,7 @@ tbe_status backward_impl(tbe_handle* h, int32_t B, const void* indices, const vo
                          int32_t index_dtype, int64_t n, const float* psw,
                          const float* grad_output, float lr, float eps, void* workspace,
                          size_t workspace_bytes, const tbe_runs* runs, hipStream_t s,
-                         bool with_front) {
+                         bool with_front, bool timed = true) {
   tbe_status st = check_batch_args(h, B, indices, offsets, index_dtype, n);
   if (st != TBE_OK) return st;
   if (B > 0 && (!grad_output || !aligned(grad_output, 4))) return TBE_ERR_INVALID_ARGUMENT;
@@ -426,7 +451,7 @@ tbe_status backward_impl(tbe_handle* h, int32_t B, const void* indices, const vo
     // (grouped) or overwritten (plain)
     if (rec != h->groups.end()) h->groups.erase(rec);
     KernelTimer timer{h, take_events};
-    const KernelTimer* kt = h->profile ? &timer : nullptr;
+    const KernelTimer* kt = (h->profile && timed) ? &timer : nullptr;
     BackwardLaunch a;
     fill_backward(h, B, indices, offsets, index_dtype, n, psw, grad_output, lr, eps, workspace,
                   runs, vec, threshold, bucket_sort, p, &a);
@@ -568,6 +593,9 @@ tbe_status tbe_create(const tbe_config* cfg, void* weights, float* optim_state, 
     delete h;
     return TBE_ERR_HIP;
   }
+  // null if the lookup fails: only tbe_backward_update_no_alloc needs it, and
+  // it then returns TBE_ERR_HIP
+  h->static_scratch = static_scratch_address(h->device);
   // one device block: table metadata | validation flag | count-matrix table
   // list | gather table list
   auto up = [](size_t x) { return (x + kAlign - 1) / kAlign * kAlign; };
@@ -849,6 +877,20 @@ tbe_status tbe_backward_update(tbe_handle* h, int32_t B, const void* indices, co
                                size_t workspace_bytes, const tbe_runs* runs, void* stream) {
   return backward_impl(h, B, indices, offsets, index_dtype, n, psw, grad_output, lr, eps,
                        workspace, workspace_bytes, runs, static_cast<hipStream_t>(stream), true);
+}
+
+tbe_status tbe_backward_update_no_alloc(tbe_handle* h, int32_t B, const void* indices,
+                                        const void* offsets, int32_t index_dtype, int64_t n,
+                                        const float* psw, const float* grad_output, float lr,
+                                        float eps, const tbe_runs* runs, void* stream) {
+  if (!h) return TBE_ERR_INVALID_ARGUMENT;
+  if (!h->static_scratch) return TBE_ERR_HIP;
+  // the same kernels as tbe_backward_update on the device's static scratch (a
+  // batch that needs more gets TBE_ERR_WORKSPACE_TOO_SMALL); no kernel timing,
+  // whose events would be created on demand
+  return backward_impl(h, B, indices, offsets, index_dtype, n, psw, grad_output, lr, eps,
+                       h->static_scratch, TBE_STATIC_SCRATCH_BYTES, runs,
+                       static_cast<hipStream_t>(stream), true, false);
 }
 
 tbe_status tbe_backward_update_grouped(tbe_handle* h, int32_t B, const void* indices,

@@ -30,6 +30,12 @@ def test_header_constants_match_the_binding():
         assert getattr(tbe, name) == int(value), name
 
 
+def test_static_scratch_size_matches_the_binding():
+    src = open(os.path.join(ROOT, "include", "tbe.h")).read()
+    m = re.search(r"#define TBE_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == tbe.STATIC_SCRATCH_BYTES
+
+
 def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(tbe.library_path())
     for name in _declared():
@@ -112,4 +118,6 @@ def test_null_handle_calls_are_rejected():
                                            0, None, None) == 1
     assert lib.tbe_psw_grad(None, 4, None, None, 1, 0, None, None, None) == 1
     assert lib.tbe_check_device_status(None, None) == 1
+    assert lib.tbe_backward_update_no_alloc(None, 4, None, None, 1, 0, None, None, 0.1, 0.0,
+                                            None, None) == 1
     lib.tbe_destroy(None)

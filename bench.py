@@ -185,12 +185,34 @@ def algorithmic_bytes(spec, batch, gather_tables=None, long_threshold=256, chunk
                                          "max_run": int(cnt.max()) if cnt.size else 0}
 
 
-def kernel_source_hash():
-    h = hashlib.sha256()
+# source file of every kernel (the launch shapes are set next to the kernels)
+KERNEL_FILE = {
+    "fwd_gather_pool": "forward.hip", "fwd_linearize": "forward.hip", "psw_grad": "forward.hip",
+    "fwd_split_segments": "forward.hip", "fwd_split_combine": "forward.hip",
+    "fwd_histogram": "histogram.hip", "hist_transpose": "histogram.hip",
+    "init_workspace": "sort.hip", "linearize_kernel": "sort.hip", "radix_pass": "sort.hip",
+    "radix_pass_wide": "sort.hip", "bucket_sort_rle": "sort.hip", "rle_kernel": "sort.hip",
+    "queue_runs": "segment.hip", "table_run_starts": "segment.hip", "seg_fused": "segment.hip",
+    "seg_finalize": "segment.hip",
+}
+
+
+def kernel_source_hash(kernel):
+    """Hash of the kernel's source file and of the headers it includes (transitively): a
+    counter summary holds for the kernel while this is unchanged."""
     csrc = os.path.join(ROOT, "table_embedding_bag_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    names, todo = [], [KERNEL_FILE[kernel]]
+    while todo:
+        f = todo.pop(0)
+        if f in names or not os.path.exists(os.path.join(csrc, f)):
+            continue
+        names.append(f)
+        for line in open(os.path.join(csrc, f)):
+            if line.startswith('#include "'):
+                todo.append(line.split('"')[1])
+    h = hashlib.sha256()
+    for f in names:
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -213,7 +235,7 @@ def committed_counter(kernel, tag, key="hbm_bytes_per_launch"):
         if not os.path.exists(path):
             continue
         kv = _summary(path)
-        if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        if kv.get("kernel_source_sha256_16") != kernel_source_hash(k):
             return None
         try:
             return float(kv[key])

@@ -55,6 +55,7 @@ FRONT = ("init_workspace", "linearize_kernel", "radix_pass", "bucket_sort_rle", 
 SEG = ("queue_runs", "table_run_starts", "seg_fused", "seg_finalize")
 FWD = ("fwd_gather_pool", "fwd_linearize", "fwd_histogram", "hist_transpose",
        "fwd_split_segments", "fwd_split_combine")
+COUNT_BWD = ("cb_product", "cb_update", "cb_runs")
 
 
 def parse():
@@ -190,6 +191,8 @@ KERNEL_FILE = {
     "fwd_gather_pool": "forward.hip", "fwd_linearize": "forward.hip", "psw_grad": "forward.hip",
     "fwd_split_segments": "forward.hip", "fwd_split_combine": "forward.hip",
     "fwd_histogram": "histogram.hip", "hist_transpose": "histogram.hip",
+    "cb_product": "count_backward.hip", "cb_update": "count_backward.hip",
+    "cb_runs": "count_backward.hip",
     "init_workspace": "sort.hip", "linearize_kernel": "sort.hip", "radix_pass": "sort.hip",
     "radix_pass_wide": "sort.hip", "bucket_sort_rle": "sort.hip", "rle_kernel": "sort.hip",
     "queue_runs": "segment.hip", "table_run_starts": "segment.hip", "seg_fused": "segment.hip",
@@ -256,7 +259,7 @@ class Workload:
     """One workload resident on the GPU: tables, state, handle, 4 rotated batches, upstream
     gradients, output and workspace."""
 
-    def __init__(self, n, forward="gather"):
+    def __init__(self, n, forward="gather", extra_flags=0):
         import torch
         import table_embedding_bag_amd as tbe
         import workloads
@@ -268,7 +271,7 @@ class Workload:
         self.state = torch.zeros(spec.sum_rows, dtype=torch.float32, device=dev) \
             if spec.optimizer == "rowwise_adagrad" else None
         flags = {"gather": 0, "routed": tbe.FLAG_HISTOGRAM,
-                 "histogram": tbe.FLAG_FORCE_HISTOGRAM}[forward]
+                 "histogram": tbe.FLAG_FORCE_HISTOGRAM}[forward] | extra_flags
         self.forward_mode = forward
         self.op = tbe.TBE(spec.rows, spec.dims, self.W, self.state, pooling=spec.pooling,
                           optimizer=spec.optimizer, flags=flags)
@@ -349,8 +352,8 @@ def stage_split(us, per_call):
     def total(names):
         return sum(us[k] * per_call[k] for k in names if k in us)
     return {"t_fwd_us": round(total(FWD), 2), "t_bwd_front_us": round(total(FRONT), 2),
-            "t_bwd_seg_us": round(total(SEG), 2),
-            "t_bwd_us": round(total(FRONT) + total(SEG), 2)}
+            "t_bwd_seg_us": round(total(SEG) + total(COUNT_BWD), 2),
+            "t_bwd_us": round(total(FRONT) + total(SEG) + total(COUNT_BWD), 2)}
 
 
 def mean_alg_bytes(wl, gather_tables=None):
@@ -494,6 +497,34 @@ def histogram_forward(args, steps, warmup):
                 "pct_of_mfma_peak": None if tf is None else round(100 * tf / MFMA16_PEAK_TFLOPS, 1),
                 "alg_GBps": round(gbps(alg["fwd_histogram"], t), 1) if t else None,
                 "mfma_busy_pct": committed_counter("fwd_histogram", "workload5", "mfma_busy_pct")}
+    finally:
+        wl.close()
+
+
+def count_backward(args, steps, warmup):
+    """The many-small-tables workload with the count-matrix backward (no sort): step time,
+    backward time and the product's rate against the dense bf16 MFMA peak."""
+    import table_embedding_bag_amd as tbe
+    wl = Workload(5, extra_flags=tbe.FLAG_COUNT_BACKWARD)
+    try:
+        for i in range(warmup):
+            wl.pair(i)
+        el, look = wl.timed(wl.pair, warmup, steps)
+        kt = wl.kernel_times(wl.pair, warmup, steps)
+        us, per_call = avg_us(kt, steps)
+        spec = wl.spec
+        # three bf16 parts of G times the count matrix: 3 x 2 B E_t D_t per table
+        flops = float(sum(3 * 2 * spec.B * e * d for e, d in zip(spec.rows, spec.dims)))
+        t = us.get("cb_product")
+        tf = flops / (t * 1e-6) / 1e12 if t else None
+        bwd = sum(us[k] * per_call[k] for k in ("cb_product", "cb_update", "cb_runs") if k in us)
+        return {"ms_per_step": round(1e3 * el / steps, 4), "lookups_per_s": round(look / el, 1),
+                "t_bwd_us": round(bwd, 2),
+                "kernel_avg_us": {k: round(v, 2) for k, v in us.items()},
+                "product_alg_flops": flops,
+                "product_TFLOPs": None if tf is None else round(tf, 1),
+                "product_pct_of_mfma_peak": None if tf is None else round(100 * tf / MFMA16_PEAK_TFLOPS, 1),
+                "mfma_busy_pct": committed_counter("cb_product", "workload5", "mfma_busy_pct")}
     finally:
         wl.close()
 
@@ -671,6 +702,7 @@ def main():
             w.close()
             if n == 5:
                 others["workload5"]["count_matrix_forward"] = histogram_forward(args, steps_x, 3)
+                others["workload5"]["count_matrix_backward"] = count_backward(args, steps_x, 3)
         except Exception as e:  # report, keep the headline line
             others[f"workload{n}"] = {"error": f"{type(e).__name__}: {e}"}
     out["workloads"] = others

@@ -120,7 +120,22 @@ enum {
    * creation (about 64 MB); a call whose lookups could need more segments
    * than it holds pools its bags unsplit.  Source: kimbodo.com/?p=28372,
    * "Kimbodo Engineering Perspective" (load imbalance across lookups). */
-  TBE_FLAG_SPLIT_BAGS = 16u
+  TBE_FLAG_SPLIT_BAGS = 16u,
+  /* Count-matrix backward (off by default): for every bag b of table t, its
+   * gradient row is added to each row r its lookups hit, as the dense product
+   * Gamma_t = C_t^T G_t on the matrix cores (C_t the bag-by-row count
+   * matrix, G_t the table's columns of grad_output, scaled by 1/L for mean
+   * pooling), with G split exactly into three bf16 parts so the products are
+   * exact and the sums fp32 in a fixed order; then one optimizer update per
+   * row that a lookup touched.  No sort: the counts replace the grouping.
+   * Every table must have at most 1024 rows and a dim that is a multiple of
+   * 16 up to 256, else tbe_create fails with TBE_ERR_UNSUPPORTED; calls with
+   * per-sample weights take the sort path.  tbe_forward_group then only pools
+   * (there is no grouping to make) and records the batch for
+   * tbe_backward_update_grouped.  Extends kimbodo.com/?p=28372, "What
+   * Happened" (a histogram and tensor-core path for small tables, shown there
+   * for the forward) to the backward. */
+  TBE_FLAG_COUNT_BACKWARD = 32u
 };
 
 typedef struct {

@@ -24,7 +24,7 @@ __all__ = [
     "tbe_backward_update_no_alloc", "STATIC_SCRATCH_BYTES", "TBE",
     "F32", "F16", "BF16", "POOL_SUM", "POOL_MEAN", "OPT_SGD", "OPT_ROWWISE_ADAGRAD",
     "FLAG_VALIDATE", "FLAG_NO_HISTOGRAM", "FLAG_FORCE_HISTOGRAM", "FLAG_HISTOGRAM",
-    "FLAG_SPLIT_BAGS",
+    "FLAG_SPLIT_BAGS", "FLAG_COUNT_BACKWARD",
     "OPTION_LONG_RUN_THRESHOLD", "OPTION_PROFILE", "OPTION_SORT", "OPTION_SPIN_LIMIT",
     "EXPORTED_SYMBOLS",
 ]
@@ -35,6 +35,7 @@ POOL_SUM, POOL_MEAN = 0, 1
 OPT_SGD, OPT_ROWWISE_ADAGRAD = 0, 1
 FLAG_VALIDATE, FLAG_NO_HISTOGRAM, FLAG_FORCE_HISTOGRAM, FLAG_HISTOGRAM = 1, 2, 4, 8
 FLAG_SPLIT_BAGS = 16
+FLAG_COUNT_BACKWARD = 32
 OPTION_LONG_RUN_THRESHOLD, OPTION_PROFILE, OPTION_SORT, OPTION_SPIN_LIMIT = 1, 2, 3, 4
 STATIC_SCRATCH_BYTES = 64 << 20   # TBE_STATIC_SCRATCH_BYTES
 

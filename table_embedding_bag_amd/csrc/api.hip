@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "common.hpp"
+#include "count_backward.hpp"
 #include "tbe.h"
 
 using namespace tbe;
@@ -35,6 +36,7 @@ struct GroupRecord {
   int64_t long_threshold;  // the handle's option when the grouping was made
   bool bucket_sort;
   bool queued;             // its run-length encoding queued the longer runs
+  bool count_matrix;       // the call takes the count-matrix backward (no grouping made)
 };
 
 struct tbe_handle {
@@ -67,6 +69,12 @@ struct tbe_handle {
   uint16_t* wt = nullptr;
   int32_t hist_etiles = 0, hist_dtiles = 0;
   int64_t wt_elems = 0;
+  // count-matrix backward (TBE_FLAG_COUNT_BACKWARD): (table, 64-column slice)
+  // units (device list) and the row groups they hold
+  std::vector<CountUnit> cb_host;
+  CountUnit* cb_units = nullptr;
+  int64_t cb_groups = 0;
+  int64_t weight_elems = 0;  // sum of rows * dims
   int64_t long_threshold = 256;
   bool bucket_sort = true;  // TBE_OPTION_SORT
   // TBE_FLAG_SPLIT_BAGS scratch: counters, segment list, split-bag list and
@@ -247,6 +255,20 @@ struct BwdPlan {
   size_t bytes = 0;
 };
 
+// Bag slices of the count-matrix backward: about 2048 busy workgroups, at
+// least one 32-bag step per slice.
+int count_slices(const tbe_handle* h, int32_t B) {
+  const int64_t g = std::max<int64_t>(1, h->cb_groups);
+  int64_t s = (2048 + g - 1) / g;
+  s = std::min<int64_t>(s, std::max<int64_t>(1, B / 32));
+  return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(s, 64)));
+}
+
+// Whether a backward call of this handle takes the count-matrix path.
+bool uses_count_backward(const tbe_handle* h, const float* psw) {
+  return !h->cb_host.empty() && psw == nullptr;
+}
+
 bool plan_backward(const tbe_handle* h, int64_t n, bool vec, int64_t long_threshold, BwdPlan* p) {
   p->n = n;
   p->vec = vec;
@@ -386,6 +408,13 @@ hipError_t launch_front(const BackwardLaunch& a, hipStream_t s, const KernelTime
   return launch_sort_encode(a, s, kt);
 }
 
+// The count-matrix backward of a call (every table small, no per-sample
+// weights): the product, the update of touched rows, the runs if asked.
+tbe_status count_backward_impl(tbe_handle* h, int32_t B, const void* indices, const void* offsets,
+                               int32_t index_dtype, int64_t n, const float* grad_output, float lr,
+                               float eps, void* workspace, size_t workspace_bytes,
+                               const tbe_runs* runs, hipStream_t s, bool with_front, bool timed);
+
 // Reads and clears the handle's error mark once the stream's work is done.
 tbe_status check_error_mark(tbe_handle* h, hipStream_t s) {
   uint32_t mark = 0;
@@ -399,6 +428,60 @@ tbe_status check_error_mark(tbe_handle* h, hipStream_t s) {
 }
 
 constexpr size_t kMaxGroupRecords = 64;
+
+tbe_status count_backward_impl(tbe_handle* h, int32_t B, const void* indices, const void* offsets,
+                               int32_t index_dtype, int64_t n, const float* grad_output, float lr,
+                               float eps, void* workspace, size_t workspace_bytes,
+                               const tbe_runs* runs, hipStream_t s, bool with_front, bool timed) {
+  auto rec = std::find_if(h->groups.begin(), h->groups.end(),
+                          [&](const GroupRecord& g) { return g.workspace == workspace; });
+  if (!with_front &&
+      (rec == h->groups.end() || !rec->count_matrix || rec->indices != indices ||
+       rec->offsets != offsets || rec->psw != nullptr || rec->B != B || rec->n != n ||
+       rec->index_dtype != index_dtype))
+    return TBE_ERR_INVALID_ARGUMENT;
+  const int slices = count_slices(h, B);
+  const size_t need = count_backward_bytes(h->weight_elems, h->sum_rows, slices);
+  if (workspace_bytes < need) return TBE_ERR_WORKSPACE_TOO_SMALL;
+  if (h->flags & TBE_FLAG_VALIDATE) {
+    const tbe_status st = run_validation(h, B, indices, offsets, index_dtype, n, s);
+    if (st != TBE_OK) return st;
+  }
+  if (rec != h->groups.end()) h->groups.erase(rec);
+  KernelTimer timer{h, take_events};
+  const KernelTimer* kt = (h->profile && timed) ? &timer : nullptr;
+  CountLaunch c{};
+  c.indices = indices;
+  c.offsets = offsets;
+  c.grad = grad_output;
+  c.weights = h->weights;
+  c.state = h->state;
+  c.meta = h->meta;
+  c.units = h->cb_units;
+  c.nunits = static_cast<int32_t>(h->cb_host.size());
+  c.T = h->T;
+  c.B = B;
+  c.sum_dims = h->sum_dims;
+  c.slices = slices;
+  c.mean = h->pooling == TBE_POOL_MEAN;
+  c.index64 = index_dtype == TBE_I64;
+  c.dtype = h->dtype;
+  c.adagrad = h->optimizer == TBE_OPT_ROWWISE_ADAGRAD;
+  c.lr = lr;
+  c.eps = eps;
+  c.sum_rows = h->sum_rows;
+  char* w = static_cast<char*>(workspace);
+  auto up = [](size_t x) { return (x + kAlign - 1) / kAlign * kAlign; };
+  c.partial = reinterpret_cast<float*>(w);
+  c.counts = reinterpret_cast<uint32_t*>(w + up(4 * static_cast<size_t>(h->weight_elems) * slices));
+  c.scan = c.counts + up(4 * static_cast<size_t>(h->sum_rows) * slices) / 4;
+  if (runs) {
+    c.out_unique = runs->unique_ids;
+    c.out_lengths = runs->run_lengths;
+    c.out_num = runs->num_unique;
+  }
+  return from_hip(launch_count_backward(c, s, kt));
+}
 
 std::vector<GroupRecord>::iterator find_group(tbe_handle* h, const void* workspace) {
   return std::find_if(h->groups.begin(), h->groups.end(),
@@ -427,6 +510,9 @@ tbe_status backward_impl(tbe_handle* h, int32_t B, const void* indices, const vo
     }
     const bool vec = h->bwd_vec && aligned(grad_output, 16);
     if (!workspace || !aligned(workspace, kAlign)) return TBE_ERR_INVALID_ARGUMENT;
+    if (uses_count_backward(h, psw))
+      return count_backward_impl(h, B, indices, offsets, index_dtype, n, grad_output, lr, eps,
+                                 workspace, workspace_bytes, runs, s, with_front, timed);
     // the grouped variant takes the grouping that tbe_forward_group made of this
     // very batch in this workspace, with the options in force at that time
     int64_t threshold = h->long_threshold;
@@ -500,7 +586,7 @@ tbe_status tbe_create(const tbe_config* cfg, void* weights, float* optim_state, 
   if (cfg->optimizer != TBE_OPT_SGD && cfg->optimizer != TBE_OPT_ROWWISE_ADAGRAD)
     return TBE_ERR_INVALID_ARGUMENT;
   if (cfg->optimizer == TBE_OPT_ROWWISE_ADAGRAD && !optim_state) return TBE_ERR_INVALID_ARGUMENT;
-  if (cfg->flags & ~31u) return TBE_ERR_INVALID_ARGUMENT;
+  if (cfg->flags & ~63u) return TBE_ERR_INVALID_ARGUMENT;
   if ((cfg->flags & TBE_FLAG_NO_HISTOGRAM) &&
       (cfg->flags & (TBE_FLAG_FORCE_HISTOGRAM | TBE_FLAG_HISTOGRAM)))
     return TBE_ERR_INVALID_ARGUMENT;
@@ -584,6 +670,22 @@ tbe_status tbe_create(const tbe_config* cfg, void* weights, float* optim_state, 
       h->hist_dtiles = std::max(h->hist_dtiles, (m.dim + 63) / 64);
     }
     h->wt_elems = wt_off;
+    h->weight_elems = woff;
+    // count-matrix backward: every table at most kCbMaxRows rows, dims in
+    // 16-column MFMA tiles up to kCbMaxDim
+    if (h->flags & TBE_FLAG_COUNT_BACKWARD) {
+      for (int t = 0; t < h->T; ++t) {
+        const TableMeta& m = h->meta_host[t];
+        if (m.rows > kCbMaxRows || m.dim % 16 != 0 || m.dim > kCbMaxDim) {
+          delete h;
+          return TBE_ERR_UNSUPPORTED;
+        }
+        for (int c0 = 0; c0 < m.dim; c0 += kCbCols) {
+          h->cb_host.push_back(CountUnit{t, c0});
+          h->cb_groups += (m.rows + kCbGroupRows - 1) / kCbGroupRows;
+        }
+      }
+    }
   } catch (...) {
     delete h;
     return TBE_ERR_OUT_OF_MEMORY;
@@ -605,8 +707,11 @@ tbe_status tbe_create(const tbe_config* cfg, void* weights, float* optim_state, 
   const size_t hist_bytes = sizeof(HistTable) * h->hist_host.size();
   const size_t gather_off = hist_off + up(hist_bytes);
   const size_t gather_bytes = sizeof(int32_t) * h->gather_host.size();
+  const size_t cb_off = gather_off + up(gather_bytes);
+  const size_t cb_bytes = sizeof(CountUnit) * h->cb_host.size();
+  const size_t block_bytes = cb_off + up(cb_bytes);
   void* block = nullptr;
-  if (hipMalloc(&block, gather_off + up(gather_bytes)) != hipSuccess) {
+  if (hipMalloc(&block, block_bytes) != hipSuccess) {
     delete h;
     return TBE_ERR_OUT_OF_MEMORY;
   }
@@ -616,7 +721,8 @@ tbe_status tbe_create(const tbe_config* cfg, void* weights, float* optim_state, 
   h->error_mark = reinterpret_cast<uint32_t*>(base + flag_off + 128);
   h->hist = hist_bytes ? reinterpret_cast<HistTable*>(base + hist_off) : nullptr;
   h->gather_list = gather_bytes ? reinterpret_cast<int32_t*>(base + gather_off) : nullptr;
-  bool ok = hipMemset(block, 0, gather_off + up(gather_bytes)) == hipSuccess;
+  h->cb_units = cb_bytes ? reinterpret_cast<CountUnit*>(base + cb_off) : nullptr;
+  bool ok = hipMemset(block, 0, block_bytes) == hipSuccess;
   if (ok)
     ok = hipMemcpy(h->meta, h->meta_host.data(), meta_bytes, hipMemcpyHostToDevice) == hipSuccess;
   if (ok && hist_bytes)
@@ -624,6 +730,8 @@ tbe_status tbe_create(const tbe_config* cfg, void* weights, float* optim_state, 
   if (ok && gather_bytes)
     ok = hipMemcpy(h->gather_list, h->gather_host.data(), gather_bytes, hipMemcpyHostToDevice) ==
          hipSuccess;
+  if (ok && cb_bytes)
+    ok = hipMemcpy(h->cb_units, h->cb_host.data(), cb_bytes, hipMemcpyHostToDevice) == hipSuccess;
   if (!ok) {
     (void)hipFree(block);
     delete h;
@@ -868,6 +976,11 @@ tbe_status tbe_backward_workspace_size(const tbe_handle* h, int32_t B, int64_t n
   BwdPlan p;
   if (!plan_backward(h, n, h->bwd_vec, h->long_threshold, &p)) return TBE_ERR_UNSUPPORTED;
   *bytes = p.bytes;
+  // with the count-matrix backward, room for it too (calls with per-sample
+  // weights take the sort path)
+  if (!h->cb_host.empty())
+    *bytes = std::max(*bytes, count_backward_bytes(h->weight_elems, h->sum_rows,
+                                                   count_slices(h, B)));
   return TBE_OK;
 }
 
@@ -913,6 +1026,27 @@ tbe_status tbe_forward_group(tbe_handle* h, int32_t B, const void* indices, cons
   if (psw && (h->flags & TBE_FLAG_FORCE_HISTOGRAM)) return TBE_ERR_UNSUPPORTED;
   if (n == 0) return tbe_forward(h, B, indices, offsets, index_dtype, n, psw, output, stream);
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (uses_count_backward(h, psw)) {
+    // the count-matrix backward needs no grouping: the pooled lookup alone,
+    // and a record that its backward may use this workspace
+    if (!workspace || !aligned(workspace, kAlign)) return TBE_ERR_INVALID_ARGUMENT;
+    size_t need = 0;
+    st = tbe_backward_workspace_size(h, B, n, &need);
+    if (st != TBE_OK) return st;
+    if (workspace_bytes < need) return TBE_ERR_WORKSPACE_TOO_SMALL;
+    st = forward_impl(h, B, indices, offsets, index_dtype, n, psw, output, s, true);
+    if (st != TBE_OK) return st;
+    try {
+      auto old = find_group(h, workspace);
+      if (old != h->groups.end()) h->groups.erase(old);
+      if (h->groups.size() >= kMaxGroupRecords) h->groups.erase(h->groups.begin());
+      h->groups.push_back(GroupRecord{workspace, indices, offsets, psw, B, index_dtype, n,
+                                      h->long_threshold, h->bucket_sort, false, true});
+    } catch (...) {
+      return TBE_ERR_OUT_OF_MEMORY;
+    }
+    return TBE_OK;
+  }
   try {
     BwdPlan p;
     if (!plan_backward(h, n, h->bwd_vec, h->long_threshold, &p)) return TBE_ERR_UNSUPPORTED;
@@ -943,7 +1077,8 @@ tbe_status tbe_forward_group(tbe_handle* h, int32_t B, const void* indices, cons
     if (launch_sort_encode(a, s, kt) != hipSuccess) return TBE_ERR_HIP;
     if (h->groups.size() >= kMaxGroupRecords) h->groups.erase(h->groups.begin());
     h->groups.push_back(GroupRecord{workspace, indices, offsets, psw, B, index_dtype, n,
-                                    h->long_threshold, h->bucket_sort, uses_bucket_sort(a)});
+                                    h->long_threshold, h->bucket_sort, uses_bucket_sort(a),
+                                    false});
     return TBE_OK;
   } catch (...) {
     return TBE_ERR_OUT_OF_MEMORY;

@@ -78,9 +78,9 @@ def test_create_rejects_bad_configs_on_host(case):
     elif case == "adagrad_without_state":
         kw["opt"] = 1
     elif case == "unknown_flag":
-        kw["flags"] = 64
+        kw["flags"] = 256
     elif case == "lowest_unknown_flag":
-        kw["flags"] = tbe.FLAG_SPLIT_BAGS << 1
+        kw["flags"] = tbe.FLAG_COUNT_BACKWARD << 1
     elif case == "conflicting_flags":
         kw["flags"] = 6
     elif case == "misaligned_weights":
@@ -121,3 +121,16 @@ def test_null_handle_calls_are_rejected():
     assert lib.tbe_backward_update_no_alloc(None, 4, None, None, 1, 0, None, None, 0.1, 0.0,
                                             None, None) == 1
     lib.tbe_destroy(None)
+
+
+@pytest.mark.parametrize("rows,dims", [([10, 2000], [16, 16]),   # a table over 1024 rows
+                                       ([10, 20], [16, 24]),     # a dim not in 16-column tiles
+                                       ([10, 20], [16, 512])])   # a dim over 256
+def test_count_backward_on_an_ineligible_table_is_unsupported(rows, dims):
+    """The count-matrix backward takes only handles whose every table is small; otherwise
+    tbe_create fails before any device call."""
+    lib = tbe.load()
+    cfg, keep = _cfg(rows, dims, dtype=0, flags=tbe.FLAG_COUNT_BACKWARD)
+    out = ctypes.c_void_p(123)
+    assert lib.tbe_create(ctypes.byref(cfg), 4096, None, ctypes.byref(out)) == 2
+    assert out.value is None

@@ -30,7 +30,10 @@
 //    eight consecutive bags of one column -- is one 16-byte read), the
 //    step's lookups are counted into each wave's [64 rows][32 bags] count
 //    tile with packed bf16 LDS atomic adds, each wave reads its A operands,
-//    clears its tile and issues 3 x 16 MFMAs.  C never exists in HBM.  The
+//    clears its tile and issues 3 x 16 MFMAs.  The next step's gradient
+//    values and ids (and the offsets of the one after) are loaded into
+//    registers before the current step's barrier and products, so global
+//    latency overlaps them (two barriers per step).  C never exists in HBM.  The
 //    slice's partial Gamma (fp32) and the rows' lookup counts are written to
 //    the workspace.  Workgroups are numbered so that the row groups of one
 //    bag slice, which stage the same gradient columns, are neighbours on one
@@ -57,6 +60,7 @@ constexpr int kRowsPerWave = 64;
 constexpr int kTS = kK + 8;          // LDS row stride (16-bit elements) of the tiles
 constexpr int kParts = 3;            // g = hi + mid + lo
 constexpr int kCountCap = 256;       // every count 0..256 is exact in bf16
+enum { kFast = 0, kAtomic = 1, kPasses = 2 };  // counting modes of a step
 static_assert(kWaves * kRowsPerWave == kCbGroupRows, "row group");
 
 template <typename IT>
@@ -69,14 +73,28 @@ __device__ __forceinline__ f32x4 mma(const uint4& a, const uint4& b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float bf16_value(uint32_t bits) { return __uint_as_float(bits << 16); }
+// Two values rounded to a packed bf16 pair (first in the low half):
+// v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t cvt_pair(float x, float y) {
+  return __builtin_bit_cast(uint32_t, bf16x2{static_cast<__bf16>(x), static_cast<__bf16>(y)});
+}
 
-// g = hi + mid + lo exactly, each part a bf16 (bit patterns in the low 16 bits).
-__device__ __forceinline__ void split3(float g, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
-  hi = f32_to_bf16_bits(g);
-  const float r1 = g - bf16_value(hi);    // exact: g and hi share an exponent range
-  mid = f32_to_bf16_bits(r1);
-  lo = f32_to_bf16_bits(r1 - bf16_value(mid));  // exact: at most 8 significant bits remain
+// Eight values split into packed bf16 parts with g = hi + mid + lo exactly:
+// hi rounds g; g - hi is exact in fp32 and fits 17 significant bits; mid rounds
+// that, and the rest (at most 8 significant bits) is exactly a bf16.
+__device__ __forceinline__ void split8(const float (&g)[8], uint4& hi, uint4& mid, uint4& lo) {
+  uint32_t h[4], m[4], l[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    h[q] = cvt_pair(g[2 * q], g[2 * q + 1]);
+    const float r0 = g[2 * q] - __uint_as_float(h[q] << 16);
+    const float r1 = g[2 * q + 1] - __uint_as_float(h[q] & 0xFFFF0000u);
+    m[q] = cvt_pair(r0, r1);
+    l[q] = cvt_pair(r0 - __uint_as_float(m[q] << 16), r1 - __uint_as_float(m[q] & 0xFFFF0000u));
+  }
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  mid = make_uint4(m[0], m[1], m[2], m[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
 // +1 to the bf16 count at element el of a tile (packed 16-bit LDS atomic).
@@ -92,9 +110,9 @@ template <typename IT, bool MEAN>
 __global__ __launch_bounds__(kThreads) void cb_product(CountLaunch a) {
   __shared__ __align__(16) uint16_t s_cnt[kWaves][kRowsPerWave * kTS];  // count tiles
   __shared__ __align__(16) uint16_t s_g[kParts][kCbCols * kTS];         // G parts, transposed
-  __shared__ int64_t s_off[kK + 1];          // the step's bag bounds
+  __shared__ int64_t s_off[2][kK + 1];       // bag bounds of two steps
+  __shared__ int s_mode[2];                  // counting mode of the step (kFast, kAtomic, kPasses)
   __shared__ uint32_t s_rowcnt[kCbGroupRows];
-  __shared__ int s_maxlen;
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   // logical block -> (unit, bag slice, row group), row group fastest
@@ -116,6 +134,7 @@ __global__ __launch_bounds__(kThreads) void cb_product(CountLaunch a) {
   const int per_slice = ((a.B + a.slices - 1) / a.slices + kK - 1) / kK * kK;
   const int b_begin = min(a.B, slice * per_slice);
   const int b_end = min(a.B, b_begin + per_slice);
+  const int nsteps = (b_end - b_begin + kK - 1) / kK;
   const int64_t kbase = static_cast<int64_t>(unit.table) * a.B;
   const float* gbase = a.grad + m.doff + col0;
 
@@ -128,89 +147,202 @@ __global__ __launch_bounds__(kThreads) void cb_product(CountLaunch a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int gcol = tid & 63, gbag = (tid >> 6) * 8;  // G staging: one column, 8 bags
-  for (int c0 = b_begin; c0 < b_end; c0 += kK) {
-    const int nb = min(kK, b_end - c0);
-    __syncthreads();  // the previous step's readers of s_g, s_off and the tiles are done
-    // this step's gradient columns (loads in flight across the barrier below)
-    float g[8];
+  // thread roles: G staging takes one column of 8 bags; the ids are taken bag
+  // by bag, 8 adjacent lanes per bag (bag tid / 8, in-bag positions tid % 8 + 8k)
+  const int gcol = tid & 63, gbag = (tid >> 6) * 8;
+  const int ibag = tid >> 3, ij = tid & 7;
+  const bool want_counts = a.out_num != nullptr;  // exact counts per row only for the runs
+  auto step_bags = [&](int step) { return min(kK, b_end - (b_begin + step * kK)); };
+  // The prefetch loads below are issued unconditionally, from clamped (always
+  // valid) addresses, and zeroed or marked when out of range: their number
+  // is then fixed, so a wait for the oldest leaves the younger ones in flight.
+  auto load_offsets = [&](int step) -> int64_t {
+    const int st = min(step, nsteps - 1);
+    const int nb = step_bags(st);
+    const int b = tid <= kK ? min(tid, nb) : 0;
+    return ld_index<IT>(a.offsets, kbase + b_begin + st * kK + b);
+  };
+  auto store_offsets = [&](int buf, int step, int64_t v) {
+    if (tid <= kK) s_off[buf][tid] = v;
+    if (wave == 0) {  // threads 0..32 are lanes of wave 0
+      const int64_t next = __shfl_down(v, 1, kWave);
+      const int64_t len = lane < step_bags(step) ? next - v : 0;
+      const bool over8 = __ballot(len > 8) != 0u, over_cap = __ballot(len > kCountCap) != 0u;
+      if (lane == 0) s_mode[buf] = over_cap ? kPasses : (over8 ? kAtomic : kFast);
+    }
+  };
+  auto load_g = [&](int step, float (&g)[8]) {
+    const int st = min(step, nsteps - 1);
+    const int nb = step_bags(st), c0 = b_begin + st * kK;
+    const bool col_ok = gcol < NT * 16 && step < nsteps;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int b = gbag + j;
-      g[j] = (b < nb && gcol < NT * 16) ? gbase[static_cast<int64_t>(c0 + b) * a.sum_dims + gcol]
-                                        : 0.0f;
+      const bool ok = col_ok && b < nb;
+      const float v = gbase[static_cast<int64_t>(c0 + min(b, nb - 1)) * a.sum_dims +
+                            (col_ok ? gcol : 0)];
+      g[j] = ok ? v : 0.0f;
     }
-    if (tid <= kK) s_off[tid] = ld_index<IT>(a.offsets, kbase + c0 + min(tid, nb));
-    if (tid == 0) s_maxlen = 0;
+  };
+  auto load_ids = [&](int buf, int step, int64_t (&x)[2]) {
+    const bool in_step = step < nsteps && ibag < step_bags(min(step, nsteps - 1));
+    const int64_t s0 = s_off[buf][ibag], s1 = s_off[buf][ibag + 1];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int64_t p = s0 + ij + 8 * r;
+      const bool ok = in_step && p < s1;
+      const int64_t v = ld_index<IT>(a.indices, ok ? p : 0);  // position 0 exists (n > 0)
+      x[r] = ok ? v : -1;
+    }
+  };
+  auto add = [&](int64_t x, int bag) {
+    const int64_t r = x - row0;
+    if (r >= 0 && r < kCbGroupRows) {
+      count_add(s_cnt[r >> 6], static_cast<int>(r & 63) * kTS + bag);
+      if (want_counts) atomicAdd(&s_rowcnt[r], 1u); else s_rowcnt[r] = 1u;
+    }
+  };
+  // one wave's products of a counted step; the wave's tile is cleared again.
+  // All four column tiles are multiplied whatever the dim (columns past it
+  // hold zeros and are not written), so the products need no branch; a
+  // part's four B operands are read before its sixteen MFMAs.
+  auto multiply = [&]() {
+    if (!active) return;
+    uint4 af[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+      af[mt] = *reinterpret_cast<const uint4*>(s_cnt[wave] + (mt * 16 + (lane & 15)) * kTS +
+                                               (lane >> 4) * 8);
+    uint4 bf[2][4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+      bf[0][nt] = *reinterpret_cast<const uint4*>(s_g[0] + (nt * 16 + (lane & 15)) * kTS +
+                                                  (lane >> 4) * 8);
+    uint4* t4 = reinterpret_cast<uint4*>(s_cnt[wave]);  // a wave's LDS operations complete in order
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave * kTS / 8 / kWave; ++i)
+      t4[i * kWave + lane] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int part = 0; part < kParts; ++part) {
+      if (part + 1 < kParts) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          bf[(part + 1) & 1][nt] = *reinterpret_cast<const uint4*>(
+              s_g[part + 1] + (nt * 16 + (lane & 15)) * kTS + (lane >> 4) * 8);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[mt][nt] = mma(af[mt], bf[part & 1][nt], acc[mt][nt]);
+    }
+  };
+
+  if (nsteps > 0) {
+    // prologue: offsets of steps 0 and 1 stored, of step 2 in a register; G
+    // values and ids of step 0 in registers
+    store_offsets(0, 0, load_offsets(0));
+    int64_t off_a = load_offsets(1);   // offsets of step c + 2 at iteration c
     __syncthreads();
-    if (tid < nb) atomicMax(&s_maxlen, static_cast<int>(s_off[tid + 1] - s_off[tid]));
-    {
-      uint32_t hi[8], mid[8], lo[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float v = g[j];
-        if constexpr (MEAN) {
-          const int b = gbag + j;
-          const int64_t len = b < nb ? s_off[b + 1] - s_off[b] : 0;
-          v = len > 0 ? v * (1.0f / static_cast<float>(len)) : 0.0f;
-        }
-        split3(v, hi[j], mid[j], lo[j]);
-      }
-      uint4* dst0 = reinterpret_cast<uint4*>(s_g[0] + gcol * kTS + gbag);
-      uint4* dst1 = reinterpret_cast<uint4*>(s_g[1] + gcol * kTS + gbag);
-      uint4* dst2 = reinterpret_cast<uint4*>(s_g[2] + gcol * kTS + gbag);
-      *dst0 = make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16),
-                         hi[6] | (hi[7] << 16));
-      *dst1 = make_uint4(mid[0] | (mid[1] << 16), mid[2] | (mid[3] << 16),
-                         mid[4] | (mid[5] << 16), mid[6] | (mid[7] << 16));
-      *dst2 = make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16),
-                         lo[6] | (lo[7] << 16));
-    }
-    __syncthreads();  // s_maxlen
-    const int64_t p0 = s_off[0], p1 = s_off[nb];
-    const int passes = max(1, (s_maxlen + kCountCap - 1) / kCountCap);
-    for (int pass = 0; pass < passes; ++pass) {
-      if (pass > 0) __syncthreads();  // the previous pass's tiles were read and cleared
-      // this pass's lookups of the step (positions [pass*256, pass*256 + 256) of each bag)
-      for (int64_t p = p0 + tid; p < p1; p += kThreads) {
-        const int64_t x = ld_index<IT>(a.indices, p);
-        int lo = 0, hi = nb;  // the bag: s_off[lo] <= p < s_off[hi]
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (s_off[mid] <= p) lo = mid; else hi = mid;
-        }
-        if ((p - s_off[lo]) / kCountCap != pass) continue;
-        const int64_t r = x - row0;
-        if (r >= 0 && r < kCbGroupRows) {
-          count_add(s_cnt[r >> 6], static_cast<int>(r & 63) * kTS + lo);
-          atomicAdd(&s_rowcnt[r], 1u);
-        }
-      }
+    float g_cur[8];
+    int64_t x_cur[2];
+    load_g(0, g_cur);
+    load_ids(0, 0, x_cur);
+    store_offsets(1, 1, off_a);
+    off_a = load_offsets(2);
+
+    for (int c = 0; c < nsteps; ++c) {
+      const int buf = c & 1, nb = step_bags(c);
+      // the previous step's products are done (tiles cleared, s_g free) and the
+      // offsets of step c + 1 are visible
       __syncthreads();
-      if (active) {
-        uint4 af[4];
+      {
+        if constexpr (MEAN) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          af[mt] = *reinterpret_cast<const uint4*>(s_cnt[wave] + (mt * 16 + (lane & 15)) * kTS +
-                                                   (lane >> 4) * 8);
-        // clear the tile for the next step (a wave's LDS operations complete in order)
-        uint4* t4 = reinterpret_cast<uint4*>(s_cnt[wave]);
-#pragma unroll
-        for (int i = 0; i < kRowsPerWave * kTS / 8 / kWave; ++i)
-          t4[i * kWave + lane] = make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-        for (int part = 0; part < kParts; ++part) {
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt) {
-            if (nt < NT) {
-              const uint4 bf = *reinterpret_cast<const uint4*>(
-                  s_g[part] + (nt * 16 + (lane & 15)) * kTS + (lane >> 4) * 8);
-#pragma unroll
-              for (int mt = 0; mt < 4; ++mt) acc[mt][nt] = mma(af[mt], bf, acc[mt][nt]);
-            }
+          for (int j = 0; j < 8; ++j) {
+            const int b = gbag + j;
+            const int64_t len = b < nb ? s_off[buf][b + 1] - s_off[buf][b] : 0;
+            g_cur[j] = len > 0 ? g_cur[j] * (1.0f / static_cast<float>(len)) : 0.0f;
           }
         }
+        uint4 hi, mid, lo;
+        split8(g_cur, hi, mid, lo);
+        *reinterpret_cast<uint4*>(s_g[0] + gcol * kTS + gbag) = hi;
+        *reinterpret_cast<uint4*>(s_g[1] + gcol * kTS + gbag) = mid;
+        *reinterpret_cast<uint4*>(s_g[2] + gcol * kTS + gbag) = lo;
       }
+      // count a pass of the step.  kFast (no bag over 8 lookups): the 8 lanes
+      // of a bag compare their ids by shuffles and the first lane holding an
+      // id stores its count with a plain LDS write (each (row, bag) cell has
+      // one writer).  kAtomic (no bag over kCountCap): every lookup adds 1
+      // with an LDS atomic.  kPasses: the same over in-bag positions
+      // [q * kCountCap, (q + 1) * kCountCap), so no count exceeds what bf16
+      // holds exactly.
+      const int mode = s_mode[buf];
+      const bool long_step = mode == kPasses;
+      auto count_pass = [&](int q) -> bool {
+        bool added = false;
+        if (mode == kFast) {  // the same on every lane of the wave
+          const int x = static_cast<int>(x_cur[0]);  // a row (< kCbMaxRows), or -1
+          int same = 0;
+          bool first = true;
+#pragma unroll
+          for (int o = 1; o < 8; ++o) {
+            const int y = __shfl_xor(x, o, kWave);
+            same += y == x ? 1 : 0;
+            first &= !(y == x && (ij ^ o) < ij);
+          }
+          const int r = x - row0;
+          if (x >= 0 && first && r >= 0 && r < kCbGroupRows) {
+            s_cnt[r >> 6][(r & 63) * kTS + ibag] =
+                static_cast<uint16_t>(__float_as_uint(static_cast<float>(same + 1)) >> 16);
+            if (want_counts) atomicAdd(&s_rowcnt[r], static_cast<uint32_t>(same + 1));
+            else s_rowcnt[r] = 1u;
+          }
+          return true;
+        }
+        if (ibag >= nb) return false;
+        const int64_t s0 = s_off[buf][ibag], s1 = s_off[buf][ibag + 1];
+        if (!long_step) {
+#pragma unroll
+          for (int r = 0; r < 2; ++r)
+            if (x_cur[r] >= 0) add(x_cur[r], ibag);
+          for (int64_t p = s0 + ij + 16; p < s1; p += 8) add(ld_index<IT>(a.indices, p), ibag);
+          return true;
+        }
+        const int64_t lo = s0 + static_cast<int64_t>(q) * kCountCap;
+        const int64_t hi = min(s1, lo + kCountCap);
+        for (int64_t p = lo + ij; p < hi; p += 8) {
+          add(ld_index<IT>(a.indices, p), ibag);
+          added = true;
+        }
+        return added;
+      };
+      bool added = count_pass(0);
+      // prefetch: G values and ids of step c + 1, offsets of step c + 3
+      float g_nxt[8];
+      int64_t x_nxt[2];
+      load_g(c + 1, g_nxt);
+      load_ids(buf ^ 1, c + 1, x_nxt);
+      const int64_t off_b = load_offsets(c + 3);
+      for (int q = 0;; ++q) {
+        if (long_step) {
+          if (!__syncthreads_or(added)) break;
+        } else {
+          __syncthreads();
+        }
+        multiply();
+        if (!long_step) break;
+        __syncthreads();  // every tile cleared before the next pass counts
+        added = count_pass(q + 1);
+      }
+      // the offsets of step c are read no more: the buffer takes step c + 2's
+      // (loaded one iteration ago)
+      if (c + 2 < nsteps) store_offsets(buf, c + 2, off_a);
+      off_a = off_b;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) g_cur[j] = g_nxt[j];
+      x_cur[0] = x_nxt[0];
+      x_cur[1] = x_nxt[1];
     }
   }
 

@@ -250,7 +250,8 @@ struct BwdPlan {
   int passes = 1, slots = 256;
   int64_t zero_words = 0;
   size_t o_keys[2], o_vals[2], o_rec, o_zero, o_uniq, o_start, o_first, o_longs, o_long_keys,
-      o_items1, o_p1, o_truns;
+      o_items1, o_p1, o_truns, o_rows;
+  int64_t row_words = 0;
   bool per_table = false;
   size_t bytes = 0;
 };
@@ -269,7 +270,8 @@ bool uses_count_backward(const tbe_handle* h, const float* psw) {
   return !h->cb_host.empty() && psw == nullptr;
 }
 
-bool plan_backward(const tbe_handle* h, int64_t n, bool vec, int64_t long_threshold, BwdPlan* p) {
+bool plan_backward(const tbe_handle* h, int32_t B, int64_t n, bool vec, int64_t long_threshold,
+                   BwdPlan* p) {
   p->n = n;
   p->vec = vec;
   const int ve = vec ? 4 : 1;
@@ -291,6 +293,9 @@ bool plan_backward(const tbe_handle* h, int64_t n, bool vec, int64_t long_thresh
   p->pstride = static_cast<int32_t>((h->dmax + 3) / 4 * 4);
   const int64_t sort_tile = sort_tile_keys(n, h->key_bits);
   p->sort_tiles = static_cast<int>((n + sort_tile - 1) / sort_tile);
+  // segment bounds of a linearize step that sorts each tile by the high digit
+  const int64_t lin_tiles = (static_cast<int64_t>(h->T) * B + kLinBags - 1) / kLinBags;
+  p->row_words = lin_tiles <= kTileBucketMaxTiles ? lin_tiles * kTileRowWords : 0;
   // look-back status words of the RLE kernel, or those of the bucket-local
   // sort's windows followed by the windows' 4-word range records
   p->rle_tiles = 5 * static_cast<int>((n + kBucketWindow - 1) / kBucketWindow) + 4;
@@ -323,6 +328,7 @@ bool plan_backward(const tbe_handle* h, int64_t n, bool vec, int64_t long_thresh
   p->o_items1 = cv.take(8 * static_cast<size_t>(p->items1_ub));
   p->o_p1 = cv.take(4 * static_cast<size_t>(p->pstride) * p->chunks_ub);
   p->o_truns = cv.take(4 * static_cast<size_t>(h->T + 1));
+  p->o_rows = cv.take(4 * static_cast<size_t>(p->row_words));
   // short runs in lane groups of each table's own width, when some table's
   // rows are narrower than the widest (metadata staged in LDS)
   if (h->T <= kSegLdsTables)
@@ -398,6 +404,7 @@ void fill_backward(const tbe_handle* h, int32_t B, const void* indices, const vo
   b.items1 = reinterpret_cast<uint2*>(w + p.o_items1);
   b.partial1 = reinterpret_cast<float*>(w + p.o_p1);
   b.table_runs = reinterpret_cast<uint32_t*>(w + p.o_truns);
+  b.tile_rows = reinterpret_cast<uint32_t*>(w + p.o_rows);
 }
 
 // The grouping (linearize, sort, run-length encoding) of a backward call.
@@ -527,7 +534,7 @@ tbe_status backward_impl(tbe_handle* h, int32_t B, const void* indices, const vo
       queued = rec->queued;
     }
     BwdPlan p;
-    if (!plan_backward(h, n, vec, threshold, &p)) return TBE_ERR_UNSUPPORTED;
+    if (!plan_backward(h, B, n, vec, threshold, &p)) return TBE_ERR_UNSUPPORTED;
     if (workspace_bytes < p.bytes) return TBE_ERR_WORKSPACE_TOO_SMALL;
     if (h->flags & TBE_FLAG_VALIDATE) {
       st = run_validation(h, B, indices, offsets, index_dtype, n, s);
@@ -974,7 +981,7 @@ tbe_status tbe_psw_grad(tbe_handle* h, int32_t B, const void* indices, const voi
 tbe_status tbe_backward_workspace_size(const tbe_handle* h, int32_t B, int64_t n, size_t* bytes) {
   if (!h || !bytes || B < 0 || n < 0) return TBE_ERR_INVALID_ARGUMENT;
   BwdPlan p;
-  if (!plan_backward(h, n, h->bwd_vec, h->long_threshold, &p)) return TBE_ERR_UNSUPPORTED;
+  if (!plan_backward(h, B, n, h->bwd_vec, h->long_threshold, &p)) return TBE_ERR_UNSUPPORTED;
   *bytes = p.bytes;
   // with the count-matrix backward, room for it too (calls with per-sample
   // weights take the sort path)
@@ -1049,7 +1056,7 @@ tbe_status tbe_forward_group(tbe_handle* h, int32_t B, const void* indices, cons
   }
   try {
     BwdPlan p;
-    if (!plan_backward(h, n, h->bwd_vec, h->long_threshold, &p)) return TBE_ERR_UNSUPPORTED;
+    if (!plan_backward(h, B, n, h->bwd_vec, h->long_threshold, &p)) return TBE_ERR_UNSUPPORTED;
     if (!workspace || !aligned(workspace, kAlign)) return TBE_ERR_INVALID_ARGUMENT;
     if (workspace_bytes < p.bytes) return TBE_ERR_WORKSPACE_TOO_SMALL;
     BackwardLaunch a{};

@@ -279,6 +279,7 @@ struct BackwardBuffers {
   uint32_t* run_start;      // [N + 1]
   uint32_t* run_first;      // [N]: sorted value of each run's first lookup
   uint32_t* table_runs;     // [T + 1]: first run id of each table (per-table lane groups)
+  uint32_t* tile_rows;      // [linearize tiles][kTileRowWords] segment bounds (linearize_bucket)
   uint2* items1;            // workgroup items: {first position, medium flag | length}
                             // or {long run, chunk}
   uint4* longs;             // {first position, length, first chunk partial, chunk count}
@@ -401,6 +402,14 @@ hipError_t launch_sort_encode(const BackwardLaunch& a, hipStream_t stream, const
 // True when the grouping of this launch's batch takes the bucket-local sort
 // (whose run-length encoding also queues the longer runs).
 bool uses_bucket_sort(const BackwardLaunch& a);
+constexpr int kLinBags = 128;  // bags per linearize tile
+// Batches of at most this many linearize tiles: the linearize step also
+// sorts each tile's lookups by the high digit (linearize_bucket) and the
+// bucket-local sort gathers its buckets from the tiles' segments, so no radix
+// pass runs (the gather keeps one segment per tile in LDS).
+constexpr int kTileBucketMaxTiles = 256;
+bool uses_tile_buckets(const BackwardLaunch& a);
+
 hipError_t launch_segment_reduce_update(const BackwardLaunch& a, const uint32_t* sorted_keys,
                                         const uint32_t* sorted_vals, hipStream_t stream,
                                         const KernelTimer* kt);
@@ -421,6 +430,14 @@ constexpr int kRleTile = 8192;
 // Sorted positions per window of the bucket-local sort: a window takes the
 // buckets of the high digit that start inside it.
 constexpr int kBucketWindow = 2048;
+// The windows' look-back status words come first in the RLE status region
+// (rounded up to 4 words), then their 16-byte range records.
+__host__ __device__ inline int64_t bucket_windows(int64_t n) {
+  return (n + kBucketWindow - 1) / kBucketWindow;
+}
+__host__ __device__ inline uint32_t* bucket_window_table(uint32_t* rle_status, int64_t n) {
+  return rle_status + ((bucket_windows(n) + 3) & ~int64_t{3});
+}
 
 // LSD radix sort plan for n keys of key_bits bits: the fewest passes of
 // digits of at most kMaxRadixBits bits, the bits split evenly over the
@@ -434,6 +451,9 @@ constexpr int kBucketWindow = 2048;
 // status words) has radix_slots(bits) entries.
 constexpr int kMaxRadixBits = 10;
 constexpr int kMaxRadixPasses = 4;  // ids of up to 31 bits: at most 4 passes
+// Words per tile row of linearize_bucket: segment bounds of the 2^kMaxRadixBits
+// high digits and the tile's end.
+constexpr int kTileRowWords = (1 << kMaxRadixBits) + 1;
 constexpr int64_t kWideRadixMaxKeys = int64_t{1} << 20;
 __host__ __device__ inline int radix_passes(int key_bits, int64_t n) {
   const int w = n <= kWideRadixMaxKeys ? kMaxRadixBits : 8;

@@ -49,8 +49,7 @@ struct CountLaunch {
 
 // Workspace bytes of the count-matrix backward for `slices` bag slices.
 inline size_t count_backward_bytes(int64_t weights_elems, int64_t sum_rows, int slices) {
-  const size_t a = 256;
-  auto up = [a](size_t x) { return (x + a - 1) / a * a; };
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   return up(4 * static_cast<size_t>(weights_elems) * slices) +
          up(4 * static_cast<size_t>(sum_rows) * slices) +
          up(4 * (2 + static_cast<size_t>((sum_rows + 1023) / 1024)));

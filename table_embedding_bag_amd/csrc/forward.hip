@@ -302,12 +302,17 @@ constexpr int kFusedThreads = 512;
 constexpr int kFusedK = 2;
 constexpr int64_t kFusedLinCap = 1024;
 
-template <int ST, typename IT, bool VEC, bool PSW>
+template <int ST, typename IT, bool VEC, bool PSW, bool BUCKET>
 __global__ __launch_bounds__(kFusedThreads) void fwd_linearize(ForwardLaunch f, BackwardLaunch b,
                                                                int lin_blocks) {
   const int bid = static_cast<int>(blockIdx.x);
   if (bid < lin_blocks) {
-    linearize_tiles<IT, kFusedThreads, kFusedK>(b, bid, lin_blocks);
+    if constexpr (BUCKET) {
+      if (bid < (b.num_bags + kLinBags - 1) / kLinBags)
+        linearize_bucket<IT, kFusedThreads, kFusedK>(b, bid);
+    } else {
+      linearize_tiles<IT, kFusedThreads, kFusedK>(b, bid, lin_blocks);
+    }
     return;
   }
   constexpr int kPer = kFusedThreads / kBlock;
@@ -465,21 +470,30 @@ hipError_t dispatch_index(const ForwardLaunch& a, hipStream_t s, dim3 grid,
                    : dispatch_vec_psw<ST, int32_t>(a, s, grid, kt);
 }
 
-template <int ST, typename IT>
-hipError_t launch_fused(const ForwardLaunch& f, const BackwardLaunch& b, int lin, hipStream_t s,
-                        dim3 grid, const KernelTimer* kt) {
+template <int ST, typename IT, bool SC>
+void launch_fused_sc(const ForwardLaunch& f, const BackwardLaunch& b, int lin, hipStream_t s,
+                     dim3 grid, const KernelTimer* kt) {
   const dim3 block(kFusedThreads);
   if (f.vec) {
     if (f.psw)
-      launch_timed(kt, "fwd_linearize", fwd_linearize<ST, IT, true, true>, grid, block, 0, s, f, b, lin);
+      launch_timed(kt, "fwd_linearize", fwd_linearize<ST, IT, true, true, SC>, grid, block, 0, s, f, b, lin);
     else
-      launch_timed(kt, "fwd_linearize", fwd_linearize<ST, IT, true, false>, grid, block, 0, s, f, b, lin);
+      launch_timed(kt, "fwd_linearize", fwd_linearize<ST, IT, true, false, SC>, grid, block, 0, s, f, b, lin);
   } else {
     if (f.psw)
-      launch_timed(kt, "fwd_linearize", fwd_linearize<ST, IT, false, true>, grid, block, 0, s, f, b, lin);
+      launch_timed(kt, "fwd_linearize", fwd_linearize<ST, IT, false, true, SC>, grid, block, 0, s, f, b, lin);
     else
-      launch_timed(kt, "fwd_linearize", fwd_linearize<ST, IT, false, false>, grid, block, 0, s, f, b, lin);
+      launch_timed(kt, "fwd_linearize", fwd_linearize<ST, IT, false, false, SC>, grid, block, 0, s, f, b, lin);
   }
+}
+
+template <int ST, typename IT>
+hipError_t launch_fused(const ForwardLaunch& f, const BackwardLaunch& b, int lin, hipStream_t s,
+                        dim3 grid, const KernelTimer* kt) {
+  if (uses_tile_buckets(b))
+    launch_fused_sc<ST, IT, true>(f, b, lin, s, grid, kt);
+  else
+    launch_fused_sc<ST, IT, false>(f, b, lin, s, grid, kt);
   return hipGetLastError();
 }
 

@@ -12,10 +12,10 @@
 #pragma once
 
 #include "common.hpp"
+#include "lookback.hpp"
 
 namespace tbe {
 
-constexpr int kLinBags = 128;               // bags per linearize tile
 // Bags per tile of the stand-alone linearize kernel when a batch has more
 // tiles of kLinBags than its grid holds: fewer, longer tiles then amortise
 // each tile's offset staging (16.8 M lookups in bags of 8: 141 -> 121 us).
@@ -34,6 +34,41 @@ inline int64_t linearize_blocks(int64_t num_bags, int bags = kLinBags) {
 template <typename IT>
 __device__ __forceinline__ int64_t lin_index(const void* p, int64_t i) {
   return static_cast<int64_t>(static_cast<const IT*>(p)[i]);
+}
+
+// Bag slot s of a tile with s_off[s] <= p < s_off[s + 1] (s_off: the tile's
+// nb + 1 offsets in LDS).  A tile whose lookups are nb times its first bag's
+// length most likely has equally long bags: there the slot interpolated from
+// the position (per = nb / lookups) is exact -- it is checked before it is
+// used -- and the binary search is skipped.  Bags of 8 lookups: 121 -> 107 us
+// on 16.8 M lookups; trying it on every tile cost 4 us on 5.2 M lookups of
+// Poisson lengths.
+__device__ __forceinline__ int tile_bag_slot(const int64_t* s_off, int nb, int64_t p, int64_t p0,
+                                             bool even, float per) {
+  int g = static_cast<int>(static_cast<float>(p - p0) * per);
+  g = g < 0 ? 0 : (g > nb - 1 ? nb - 1 : g);
+  if (even && s_off[g] <= p && p < s_off[g + 1]) return g;
+  int lo = 0, hi = nb;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_off[mid] <= p)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+
+// Lanes among `active` whose digit d (of `bits` bits) equals this lane's: one
+// ballot per digit bit.  Call with the whole wave.
+__device__ __forceinline__ uint64_t match_bits(uint64_t active, uint32_t d, int bits) {
+  uint64_t peers = active;
+  for (int bit = 0; bit < bits; ++bit) {
+    const bool set = (d >> bit) & 1u;
+    const uint64_t bal = __ballot(set);
+    peers &= set ? bal : ~bal;
+  }
+  return peers;
 }
 
 // A workgroup of NT threads takes tiles first, first + stride, ... of
@@ -79,11 +114,6 @@ __device__ __forceinline__ void linearize_tiles(const BackwardLaunch& a, int64_t
     __syncthreads();
 
     const int64_t p0 = s_off[0], p1 = s_off[nb];
-    // A tile whose lookups are nb times its first bag's length most likely
-    // has equally long bags: there the slot interpolated from the position is
-    // exact (it is checked before it is used) and the binary search is
-    // skipped.  Bags of 8 lookups: 121 -> 107 us on 16.8 M lookups; trying it
-    // on every tile cost 4 us on 5.2 M lookups of Poisson lengths.
     const bool even = p1 - p0 == static_cast<int64_t>(nb) * (s_off[1] - p0);
     const float per = even && p1 > p0 ? static_cast<float>(nb) / static_cast<float>(p1 - p0) : 0.0f;
     for (int64_t base = p0; base < p1; base += static_cast<int64_t>(NT) * K) {
@@ -95,22 +125,7 @@ __device__ __forceinline__ void linearize_tiles(const BackwardLaunch& a, int64_t
       for (int k = 0; k < K; ++k) {
         const int64_t p = base + tid + static_cast<int64_t>(NT) * k;
         ok[k] = p < p1;
-        // bag slot s with s_off[s] <= p < s_off[s + 1]
-        int g = static_cast<int>(static_cast<float>(p - p0) * per);
-        g = g < 0 ? 0 : (g > nb - 1 ? nb - 1 : g);
-        if (even && s_off[g] <= p && p < s_off[g + 1]) {
-          slot[k] = g;
-        } else {
-          int lo = 0, hi = nb;
-          while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (s_off[mid] <= p)
-              lo = mid;
-            else
-              hi = mid;
-          }
-          slot[k] = lo;
-        }
+        slot[k] = tile_bag_slot(s_off, nb, p, p0, even, per);
       }
       // every load of the batch is issued before any is used (positions past
       // the tile read its last lookup instead)
@@ -142,12 +157,7 @@ __device__ __forceinline__ void linearize_tiles(const BackwardLaunch& a, int64_t
         if (active == 0) continue;
         for (int q = 0; q < passes; ++q) {
           const uint32_t d = (key >> (q * bits)) & dmask;
-          uint64_t peers = active;
-          for (int bit = 0; bit < bits; ++bit) {
-            const bool set = (d >> bit) & 1u;
-            const uint64_t bal = __ballot(set);
-            peers &= set ? bal : ~bal;
-          }
+          const uint64_t peers = match_bits(active, d, bits);
           if (ok[k] && popc_below(peers) == 0) atomicAdd(&s_hist[q * slots + d], __popcll(peers));
         }
       }
@@ -156,6 +166,178 @@ __device__ __forceinline__ void linearize_tiles(const BackwardLaunch& a, int64_t
   __syncthreads();
   for (int i = tid; i < passes * slots; i += NT)
     if (s_hist[i]) atomicAdd(&a.buf.digit_hist[i], s_hist[i]);
+}
+
+// The linearize step for batches whose grouping takes the bucket-local sort
+// (ids of two digits; the high digit is key >> lbits), with the tile's lookups
+// also sorted by the high digit inside the tile's own positions.  Tile `tile`
+// of kLinBags bags, lookups [p0, p1):
+//   1. count: keys are computed and their high digits counted in LDS (lanes
+//      with equal digits matched by ballots, one LDS add each);
+//   2. the tile's row of segment bounds goes out: row[d] = p0 + the number of
+//      the tile's keys with a high digit below d (row[2^kMaxRadixBits] = p1),
+//      and the counts are added to the global counts of the high digit;
+//   3. the lookups are walked again in rounds of NT * K positions (each wave on
+//      consecutive positions); a round is ranked in LDS with per-wave digit
+//      counters, which keeps lookup order within a digit, and written to
+//      buf.keys[1] / buf.vals[1] at row[d] + the digit's rank in the tile.
+//      The counters are double buffered by round: two barriers per round.
+// No workgroup waits for another: the bucket-local sort gathers a bucket's
+// keys from the tiles' segments [row_i[d], row_i[d + 1]) in tile order, which
+// is lookup order.
+template <typename IT, int NT, int K>
+__device__ __forceinline__ void linearize_bucket(const BackwardLaunch& a, int tile) {
+  constexpr int NW = NT / kWave;
+  constexpr int DIG = 1 << kMaxRadixBits;
+  constexpr int DPT = DIG / NT;  // digits owned per thread
+  static_assert(DPT >= 1 && DPT * NT == DIG, "threads own whole digits");
+  __shared__ int64_t s_off[kLinBags + 1];
+  __shared__ uint32_t s_roff[kLinBags];
+  __shared__ float s_scale[kLinBags];
+  __shared__ uint32_t s_cnt[DIG];  // the tile's digit counts; later each round's digit bases
+  __shared__ __align__(16) uint16_t s_wc[2][NW][DIG];  // per-wave digit counts, by round parity
+  __shared__ uint32_t scratch[NW];
+
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int lbits = radix_digit_bits(a.key_bits, a.num_indices);
+  const int hbits = a.key_bits - lbits;
+  const uint32_t hmask = (1u << hbits) - 1u;
+  const int slots = radix_slots(lbits);
+  const int64_t k0 = static_cast<int64_t>(tile) * kLinBags;
+  const int nb = static_cast<int>(min(static_cast<int64_t>(kLinBags), a.num_bags - k0));
+  if (tid < nb) {
+    const int64_t k = k0 + tid;
+    const int64_t lo = lin_index<IT>(a.offsets, k);
+    const int64_t hi = lin_index<IT>(a.offsets, k + 1);
+    s_off[tid] = lo;
+    if (tid == nb - 1) s_off[nb] = hi;
+    const int t = static_cast<int>(k / a.B);
+    s_roff[tid] = static_cast<uint32_t>(a.meta[t].roff);
+    s_scale[tid] = a.mean ? ((hi > lo) ? 1.0f / static_cast<float>(hi - lo) : 0.0f) : 1.0f;
+  }
+  for (int i = tid; i < DIG; i += NT) s_cnt[i] = 0u;
+  {
+    uint4* z = reinterpret_cast<uint4*>(&s_wc[0][0][0]);
+    constexpr int NZ = static_cast<int>(sizeof(s_wc) / sizeof(uint4));
+    for (int i = tid; i < NZ; i += NT) z[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  __syncthreads();
+  const int64_t p0 = s_off[0], p1 = s_off[nb];
+  const bool even = p1 - p0 == static_cast<int64_t>(nb) * (s_off[1] - p0);
+  const float per = even && p1 > p0 ? static_cast<float>(nb) / static_cast<float>(p1 - p0) : 0.0f;
+  const int qoff = wave * (kWave * K) + lane;  // position of (round base, k = 0)
+
+  // 1. count
+  for (int64_t base = p0; base < p1; base += NT * K) {
+    int slot[K];
+    bool ok[K];
+    int64_t x[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int64_t p = base + qoff + k * kWave;
+      ok[k] = p < p1;
+      slot[k] = ok[k] ? tile_bag_slot(s_off, nb, p, p0, even, per) : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      x[k] = lin_index<IT>(a.indices, ok[k] ? base + qoff + k * kWave : p1 - 1);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const uint32_t d = ((s_roff[slot[k]] + static_cast<uint32_t>(x[k])) >> lbits) & hmask;
+      const uint64_t peers = match_bits(__ballot(ok[k]), d, hbits);
+      if (ok[k] && popc_below(peers) == 0) atomicAdd(&s_cnt[d], __popcll(peers));
+    }
+  }
+  __syncthreads();
+
+  // 2. the tile's row of segment bounds, and the global counts
+  const int d0 = tid * DPT;
+  uint32_t cnt[DPT], csum = 0;
+#pragma unroll
+  for (int q = 0; q < DPT; ++q) {
+    cnt[q] = s_cnt[d0 + q];
+    csum += cnt[q];
+  }
+  uint32_t all;
+  uint32_t run[DPT];  // next position of each owned digit
+  {
+    uint32_t st = static_cast<uint32_t>(p0) + block_excl_n<NW>(csum, scratch, &all);
+    uint32_t* const row = a.buf.tile_rows + static_cast<int64_t>(tile) * kTileRowWords;
+    uint32_t* const htot = a.buf.digit_hist + slots;  // the high digit's counts
+#pragma unroll
+    for (int q = 0; q < DPT; ++q) {
+      row[d0 + q] = st;
+      run[q] = st;
+      if (cnt[q]) atomicAdd(htot + d0 + q, cnt[q]);
+      st += cnt[q];
+    }
+    if (tid == 0) row[DIG] = static_cast<uint32_t>(p1);
+  }
+
+  // 3. place
+  uint32_t* const kout = a.buf.keys[1];
+  uint32_t* const vout = a.buf.vals[1];
+  int par = 0;
+  for (int64_t base = p0; base < p1; base += NT * K, par ^= 1) {
+    uint16_t(*const wc)[DIG] = s_wc[par];
+    int slot[K];
+    bool ok[K];
+    int64_t x[K];
+    float pw[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int64_t p = base + qoff + k * kWave;
+      ok[k] = p < p1;
+      slot[k] = ok[k] ? tile_bag_slot(s_off, nb, p, p0, even, per) : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int64_t p = ok[k] ? base + qoff + k * kWave : p1 - 1;
+      x[k] = lin_index<IT>(a.indices, p);
+      pw[k] = a.psw ? a.psw[p] : 1.0f;
+    }
+    uint32_t key[K], d[K], rank[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      key[k] = s_roff[slot[k]] + static_cast<uint32_t>(x[k]);
+      d[k] = (key[k] >> lbits) & hmask;
+      const uint64_t peers = match_bits(__ballot(ok[k]), d[k], hbits);
+      const uint32_t below = popc_below(peers);
+      const uint32_t pre = ok[k] ? static_cast<uint32_t>(wc[wave][d[k]]) : 0u;
+      rank[k] = pre + below;
+      if (ok[k] && below == 0) wc[wave][d[k]] = static_cast<uint16_t>(pre + __popcll(peers));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < DPT; ++q) {
+      const int dd = d0 + q;
+      if (dd > static_cast<int>(hmask)) break;
+      uint32_t c[NW];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) c[w] = wc[w][dd];
+      uint32_t acc = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        wc[w][dd] = static_cast<uint16_t>(acc);
+        acc += c[w];
+        s_wc[par ^ 1][w][dd] = 0;  // last read in the round before this one
+      }
+      s_cnt[dd] = run[q];
+      run[q] += acc;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      if (!ok[k]) continue;
+      const int64_t p = base + qoff + k * kWave;
+      const uint32_t bag = static_cast<uint32_t>(k0 + slot[k]);
+      // pos lies in [p0, p1) (the ranks of a digit never pass its count)
+      const uint32_t pos = s_cnt[d[k]] + wc[wave][d[k]] + rank[k];
+      if (a.use_rec) a.buf.rec[p] = make_uint2(bag, __float_as_uint(pw[k] * s_scale[slot[k]]));
+      kout[pos] = key[k];
+      vout[pos] = a.use_rec ? static_cast<uint32_t>(p) : bag;
+    }
+  }
 }
 
 }  // namespace tbe

@@ -38,25 +38,16 @@
 // kernels then update nothing and the handle is marked.
 #include "common.hpp"
 #include "linearize.hpp"
+#include "lookback.hpp"
 
 namespace tbe {
 namespace {
 
-constexpr uint32_t kFlagAgg = 1u << 30;     // status word: this tile's own count
-constexpr uint32_t kFlagIncl = 2u << 30;    // status word: count up to and including this tile
-constexpr uint32_t kValueMask = (1u << 30) - 1u;
 constexpr int kResidentTiles = 256;         // grids this small are resident all at once
 
 template <typename IT>
 __device__ __forceinline__ int64_t ld_index(const void* p, int64_t i) {
   return static_cast<int64_t>(static_cast<const IT*>(p)[i]);
-}
-
-__device__ __forceinline__ uint32_t ld_status(uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_status(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // 16-byte stores: the zeroed region starts 256-byte aligned and its carve is
@@ -74,63 +65,10 @@ __global__ __launch_bounds__(kLinThreads) void linearize_kernel(BackwardLaunch a
   linearize_tiles<IT, kLinThreads, K, BAGS>(a, blockIdx.x, gridDim.x);
 }
 
-// Counts of digits d0 .. d0 + DPT - 1 in all tiles before `tile` (decoupled
-// look-back; every digit keeps DEPTH status words in flight per round).
-// status rows have `slots` words per tile.  A wait that gives up leaves excl
-// at most the true count, so every position derived from it stays in range.
-template <int DPT, int DEPTH>
-__device__ void lookback_digits(uint32_t* status, int slots, int tile, int d0, WaitCtl wait,
-                                uint32_t (&excl)[DPT]) {
-  int j[DPT];
-  bool done[DPT];
-#pragma unroll
-  for (int q = 0; q < DPT; ++q) excl[q] = 0u, j[q] = tile - 1, done[q] = false;
-  if (wait.limit == 0u) {
-    atomicOr(wait.err, 1u);
-    return;
-  }
-  uint32_t spins = 0;
-  while (true) {
-    uint32_t w[DPT][DEPTH];
-#pragma unroll
-    for (int q = 0; q < DPT; ++q)
-#pragma unroll
-      for (int k = 0; k < DEPTH; ++k)
-        w[q][k] = (!done[q] && j[q] - k >= 0)
-                      ? ld_status(status + static_cast<int64_t>(j[q] - k) * slots + d0 + q)
-                      : kFlagIncl;
-    bool all_done = true, moved = false;
-#pragma unroll
-    for (int q = 0; q < DPT; ++q) {
-      if (done[q]) continue;
-      bool stop = false;
-      int used = 0;
-#pragma unroll
-      for (int k = 0; k < DEPTH; ++k) {
-        if (!stop) {
-          const uint32_t f = w[q][k] & ~kValueMask;
-          if (f == 0) {
-            stop = true;  // not published yet: poll again from here
-          } else {
-            excl[q] += w[q][k] & kValueMask;
-            ++used;
-            if (f == kFlagIncl) stop = done[q] = true;
-          }
-        }
-      }
-      j[q] -= used;
-      moved |= used > 0;
-      all_done &= done[q];
-    }
-    if (all_done) return;
-    if (!moved) {
-      if (++spins > wait.limit) {
-        atomicOr(wait.err, 1u);
-        return;
-      }
-      __builtin_amdgcn_s_sleep(2);
-    }
-  }
+// The same with each tile's lookups sorted by the high digit: one workgroup per tile.
+template <typename IT, int K>
+__global__ __launch_bounds__(kLinThreads) void linearize_bucket_kernel(BackwardLaunch a) {
+  linearize_bucket<IT, kLinThreads, K>(a, blockIdx.x);
 }
 
 // Lanes of the wave (among those with ok) whose digit d equals this lane's.
@@ -175,20 +113,6 @@ __device__ __forceinline__ uint64_t match_digit(uint64_t* s_slots, uint32_t d, b
     peers &= set ? bal : ~bal;
   }
   return same ? m0 : peers;
-}
-
-// Window range records of the bucket-local sort: bucket d of the high digit
-// (sorted positions [start, start + count)) belongs to window start /
-// kBucketWindow.  A record is {~first start, end, ~first bucket, last bucket +
-// 1}, built with atomic maxima on a zeroed record, so 0 in the last word
-// means the window starts no bucket.
-__device__ __forceinline__ void record_window(uint32_t* wtable, uint32_t start, uint32_t count,
-                                              uint32_t d) {
-  uint32_t* w = wtable + 4 * (start / kBucketWindow);
-  atomicMax(w + 0, ~start);
-  atomicMax(w + 1, start + count);
-  atomicMax(w + 2, ~d);
-  atomicMax(w + 3, d + 1u);
 }
 
 // One LSD pass on the digit (key >> shift) & (2^bits - 1), bits <= RB.  A
@@ -323,25 +247,6 @@ __global__ __launch_bounds__(kBlock) void radix_pass(
       vout[gp] = s_v[i];
     }
   }
-}
-
-// Exclusive prefix sum over a block of NW waves; *total receives the sum.
-template <int NW>
-__device__ __forceinline__ uint32_t block_excl_n(uint32_t x, uint32_t* scratch, uint32_t* total) {
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
-  const uint32_t incl = wave_inclusive_sum(x);
-  if (lane == kWave - 1) scratch[wave] = incl;
-  __syncthreads();
-  uint32_t base = 0, sum = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const uint32_t s = scratch[w];
-    base += (w < wave) ? s : 0u;
-    sum += s;
-  }
-  __syncthreads();
-  *total = sum;
-  return base + incl - x;
 }
 
 // A pass on digits wider than 8 bits: 1024 threads, one digit per thread
@@ -683,15 +588,87 @@ __device__ __forceinline__ void queue_run(const RunQueue& q, uint32_t* counters,
   }
 }
 
+// Keys sorted by the high digit inside each linearize tile (linearize_bucket)
+// are read through a segment table: for the buckets [b0, b1), tile i's keys
+// lie at [rows_i[b0], rows_i[b1]); concatenated in tile order they are in
+// lookup order within each bucket.  s_segoff[i] is the first element of
+// segment i in the concatenation, s_seglo[i] its first position in the keys.
+// Contains barriers: call from the whole workgroup.
+__device__ __forceinline__ void build_segments(const uint32_t* rows, int nseg, uint32_t b0,
+                                               uint32_t b1, uint32_t* s_seglo,
+                                               uint32_t* s_segoff, uint32_t* scratch) {
+  const int tid = threadIdx.x;
+  uint32_t len = 0;
+  if (tid < nseg) {
+    const uint32_t lo = rows[static_cast<int64_t>(tid) * kTileRowWords + b0];
+    const uint32_t hi = rows[static_cast<int64_t>(tid) * kTileRowWords + b1];
+    s_seglo[tid] = lo;
+    len = hi - lo;
+  }
+  uint32_t total;
+  const uint32_t off = block_excl_n<kBucketWaves>(len, scratch, &total);
+  if (tid < nseg) s_segoff[tid] = off;
+  __syncthreads();
+}
+
+// Position in the keys of element e of the concatenated segments (the last
+// segment i with s_segoff[i] <= e; an empty segment shares its offset with the
+// next one, so the one found holds element e).
+__device__ __forceinline__ uint32_t seg_position(const uint32_t* s_seglo, const uint32_t* s_segoff,
+                                                 int nseg, uint32_t e) {
+  int lo = 0, hi = nseg;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_segoff[mid] <= e)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return s_seglo[lo] + (e - s_segoff[lo]);
+}
+
+// Elements [e0, e0 + len) of the concatenated segments (len <= kBucketCap)
+// into registers in the layout of lds_counting_pass; every load is issued
+// before any is used, and positions past n read nothing.
+__device__ __forceinline__ void gather_range(const uint32_t* kin, const uint32_t* vin, int64_t n,
+                                             const uint32_t* s_seglo, const uint32_t* s_segoff,
+                                             int nseg, uint32_t e0, int len, int rr,
+                                             uint32_t (&key)[kBucketKpt],
+                                             uint32_t (&val)[kBucketKpt]) {
+  const int wseg = (threadIdx.x >> 6) * kWave * rr;
+  uint32_t pos[kBucketKpt];
+#pragma unroll
+  for (int r = 0; r < kBucketKpt; ++r) {
+    const int e = wseg + r * kWave + lane_id();
+    pos[r] = (r < rr && e < len) ? seg_position(s_seglo, s_segoff, nseg, e0 + e) : 0xFFFFFFFFu;
+  }
+#pragma unroll
+  for (int r = 0; r < kBucketKpt; ++r) {
+    const bool ok = pos[r] < static_cast<uint64_t>(n);
+    key[r] = ok ? kin[pos[r]] : 0u;
+    val[r] = ok ? vin[pos[r]] : 0u;
+  }
+}
+
+// SEG: the keys come sorted by the high digit inside each linearize tile
+// (rows: the tiles' segment bounds, nseg tiles); each window finds its range
+// from the high digit's counts and gathers it from the segments.  Otherwise
+// they come from the pass on the high digit (globally bucketed) with the
+// windows' range records in wtable.
+template <bool SEG>
 __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
     const uint32_t* __restrict__ kin, const uint32_t* __restrict__ vin, uint32_t* kout,
     uint32_t* vout, int64_t n, int lbits, int nbuckets, const uint32_t* __restrict__ htotals,
     const uint32_t* __restrict__ wtable, int ntiles, uint32_t* status, uint32_t* ticket,
     uint32_t* counters, uint32_t* unique_keys, uint32_t* run_start, uint32_t* run_first,
-    RunQueue q, uint32_t spin_limit) {
+    RunQueue q, uint32_t spin_limit, const uint32_t* __restrict__ rows, int nseg) {
   constexpr int NT = kBucketThreads, NW = kBucketWaves, CAP = kBucketCap;
+  constexpr int SEGS = SEG ? kTileBucketMaxTiles : 1;
   __shared__ uint32_t s_k[CAP];
   __shared__ uint32_t s_v[CAP];
+  __shared__ uint32_t s_seglo[SEGS];
+  __shared__ uint32_t s_segoff[SEGS];
+  __shared__ uint32_t s_hrange[2];
   __shared__ uint16_t s_cnt[NW][NT];
   __shared__ uint64_t s_slots[NW][256];
   __shared__ uint32_t s_bstart[NT + 1];  // long ranges: bucket starts in the sorted order
@@ -713,21 +690,49 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
   // together; a range starts inside the window, so it usually lies within
   // them.  Wave w loads positions w0 + [w*64*KPT, (w+1)*64*KPT).
   const int64_t w0 = static_cast<int64_t>(tile) * kBucketWindow;
-  const uint4 rec = *reinterpret_cast<const uint4*>(wtable + 4 * static_cast<int64_t>(tile));
   uint32_t key[kBucketKpt], val[kBucketKpt];
+  int64_t start, len64;
+  uint32_t hf, hl;
+  if constexpr (SEG) {
+    // bucket starts from the high digit's counts; the window takes the buckets
+    // whose start lies in [w0, w0 + kBucketWindow) (empty buckets included:
+    // they hold nothing).  s_bstart[NT] = n; w0 < n always.
+    const uint32_t my_count = tid < nbuckets ? htotals[tid] : 0u;
 #pragma unroll
-  for (int r = 0; r < kBucketKpt; ++r) {
-    const int64_t p = w0 + wave * kWave * kBucketKpt + r * kWave + lane_id();
-    key[r] = p < n ? kin[p] : 0u;
-    val[r] = p < n ? vin[p] : 0u;
+    for (int w = 0; w < NW; ++w) s_cnt[w][tid] = 0;
+    for (int i = tid; i < NW * 256; i += NT) (&s_slots[0][0])[i] = 0u;
+    if (tid == 0) s_hrange[0] = s_hrange[1] = NT;
+    uint32_t tot;
+    s_bstart[tid] = block_excl_n<NW>(my_count, scratch, &tot);
+    if (tid == 0) s_bstart[NT] = tot;
+    __syncthreads();
+    const uint32_t lo = static_cast<uint32_t>(w0), hi = lo + kBucketWindow;
+    const uint32_t sb = s_bstart[tid], sp = tid > 0 ? s_bstart[tid - 1] : 0u;
+    if (sb >= lo && (tid == 0 || sp < lo)) s_hrange[0] = tid;
+    if (sb >= hi && (tid == 0 || sp < hi)) s_hrange[1] = tid;
+    __syncthreads();
+    hf = s_hrange[0];
+    const uint32_t h1 = s_hrange[1];
+    hl = h1 - 1u;
+    start = s_bstart[hf];
+    len64 = static_cast<int64_t>(s_bstart[h1]) - start;
+  } else {
+    const uint4 rec = *reinterpret_cast<const uint4*>(wtable + 4 * static_cast<int64_t>(tile));
+#pragma unroll
+    for (int r = 0; r < kBucketKpt; ++r) {
+      const int64_t p = w0 + wave * kWave * kBucketKpt + r * kWave + lane_id();
+      key[r] = p < n ? kin[p] : 0u;
+      val[r] = p < n ? vin[p] : 0u;
+    }
+#pragma unroll
+    for (int w = 0; w < NW; ++w) s_cnt[w][tid] = 0;
+    for (int i = tid; i < NW * 256; i += NT) (&s_slots[0][0])[i] = 0u;
+    const bool empty = rec.w == 0u;
+    start = empty ? 0 : static_cast<int64_t>(~rec.x);
+    len64 = empty ? 0 : static_cast<int64_t>(rec.y) - start;
+    hf = ~rec.z;
+    hl = rec.w - 1u;
   }
-#pragma unroll
-  for (int w = 0; w < NW; ++w) s_cnt[w][tid] = 0;
-  for (int i = tid; i < NW * 256; i += NT) (&s_slots[0][0])[i] = 0u;
-  const bool empty = rec.w == 0u;
-  const int64_t start = empty ? 0 : static_cast<int64_t>(~rec.x);
-  const int64_t len64 = empty ? 0 : static_cast<int64_t>(rec.y) - start;
-  const uint32_t hf = ~rec.z, hl = rec.w - 1u;
   const uint32_t lmask = (1u << lbits) - 1u;
   const auto low = [lmask](uint32_t k) { return k & lmask; };
 
@@ -737,7 +742,10 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
     const int len = static_cast<int>(len64);
     rr = (len + NT - 1) / NT;
     if (len > 0) {
-      if (start + len <= w0 + CAP) {
+      if constexpr (SEG) {
+        build_segments(rows, nseg, hf, hl + 1u, s_seglo, s_segoff, scratch);
+        gather_range(kin, vin, n, s_seglo, s_segoff, nseg, 0u, len, rr, key, val);
+      } else if (start + len <= w0 + CAP) {
         // the range's positions go to LDS in order, then back in the layout
         // of lds_counting_pass
 #pragma unroll
@@ -798,7 +806,7 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
     }
   } else {
     // long range: bucket by bucket, chunks of CAP positions in order
-    {
+    if constexpr (!SEG) {
       const uint32_t my_count = tid < nbuckets ? htotals[tid] : 0u;
       uint32_t tot;
       s_bstart[tid] = block_excl_n<NW>(my_count, scratch, &tot);
@@ -809,9 +817,19 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
       const uint32_t bs = s_bstart[h];
       const uint32_t bn = s_bstart[h + 1] - bs;
       if (bn == 0) continue;
+      if constexpr (SEG) build_segments(rows, nseg, h, h + 1u, s_seglo, s_segoff, scratch);
       s_dbase[tid] = 0u;
       __syncthreads();
-      for (uint32_t i = tid; i < bn; i += NT) atomicAdd(&s_dbase[kin[bs + i] & lmask], 1u);
+      for (uint32_t i = tid; i < bn; i += NT) {
+        uint32_t kk;
+        if constexpr (SEG) {
+          const uint32_t pp = seg_position(s_seglo, s_segoff, nseg, i);
+          kk = pp < static_cast<uint64_t>(n) ? kin[pp] : 0u;
+        } else {
+          kk = kin[bs + i];
+        }
+        atomicAdd(&s_dbase[kk & lmask], 1u);
+      }
       __syncthreads();
       const uint32_t hc = s_dbase[tid];
       uint32_t t2;
@@ -822,7 +840,10 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
       for (uint32_t c0 = 0; c0 < bn; c0 += CAP) {
         const int clen = static_cast<int>(min(static_cast<uint32_t>(CAP), bn - c0));
         const int crr = (clen + NT - 1) / NT;
-        load_range(kin, vin, static_cast<int64_t>(bs) + c0, clen, crr, key, val);
+        if constexpr (SEG)
+          gather_range(kin, vin, n, s_seglo, s_segoff, nseg, c0, clen, crr, key, val);
+        else
+          load_range(kin, vin, static_cast<int64_t>(bs) + c0, clen, crr, key, val);
         lds_counting_pass(key, val, crr, 0, clen, low, s_k, s_v, s_cnt, s_slots, s_dstart,
                           scratch);
         for (int i = tid; i < clen; i += NT) {
@@ -1039,6 +1060,27 @@ hipError_t launch_linearize_bags(const BackwardLaunch& a, hipStream_t stream,
 hipError_t launch_linearize_kernel(const BackwardLaunch& a, hipStream_t stream,
                                    const KernelTimer* kt) {
   if (a.num_bags <= 0) return hipSuccess;
+  if (uses_tile_buckets(a)) {
+    const int64_t tiles = (a.num_bags + kLinBags - 1) / kLinBags;
+    const dim3 grid(static_cast<unsigned>(tiles));
+    const bool deep = a.num_indices > tiles * kLinThreads;
+    if (a.index64) {
+      if (deep)
+        launch_timed(kt, "linearize_kernel", linearize_bucket_kernel<int64_t, 2>, grid,
+                     dim3(kLinThreads), 0, stream, a);
+      else
+        launch_timed(kt, "linearize_kernel", linearize_bucket_kernel<int64_t, 1>, grid,
+                     dim3(kLinThreads), 0, stream, a);
+    } else {
+      if (deep)
+        launch_timed(kt, "linearize_kernel", linearize_bucket_kernel<int32_t, 2>, grid,
+                     dim3(kLinThreads), 0, stream, a);
+      else
+        launch_timed(kt, "linearize_kernel", linearize_bucket_kernel<int32_t, 1>, grid,
+                     dim3(kLinThreads), 0, stream, a);
+    }
+    return hipGetLastError();
+  }
   return a.num_bags > int64_t{kLinBags} * kLinMaxBlocks
              ? launch_linearize_bags<kLinBagsLarge>(a, stream, kt)
              : launch_linearize_bags<kLinBags>(a, stream, kt);
@@ -1103,6 +1145,11 @@ bool uses_bucket_sort(const BackwardLaunch& a) {
          (n >> (a.key_bits - bits)) <= kBucketMeanMax;
 }
 
+bool uses_tile_buckets(const BackwardLaunch& a) {
+  return uses_bucket_sort(a) && a.num_bags > 0 &&
+         (a.num_bags + kLinBags - 1) / kLinBags <= kTileBucketMaxTiles;
+}
+
 hipError_t launch_sort_encode(const BackwardLaunch& a, hipStream_t stream, const KernelTimer* kt) {
   const int64_t n = a.num_indices;
   if (n <= 0) return hipSuccess;
@@ -1115,20 +1162,25 @@ hipError_t launch_sort_encode(const BackwardLaunch& a, hipStream_t stream, const
   const int bits = radix_digit_bits(a.key_bits, n);
   const uint32_t* htotals = a.buf.digit_hist + radix_slots(bits);  // counts of the high digit
   // look-back status words of the windows, then their range records
-  const int windows = static_cast<int>((n + kBucketWindow - 1) / kBucketWindow);
+  const int windows = static_cast<int>(bucket_windows(n));
   uint32_t* wstatus = a.buf.rle_status;
-  uint32_t* wtable = a.buf.rle_status + ((windows + 3) & ~3);  // 16-byte records
-  hipError_t e = launch_pass(a, 0, bits, htotals, a.buf.keys[0], a.buf.vals[0], a.buf.keys[1],
-                             a.buf.vals[1], wtable, stream, kt);
-  if (e != hipSuccess) return e;
-  launch_timed(kt, "bucket_sort_rle", bucket_sort_rle, dim3(windows), dim3(kBucketThreads), 0,
-               stream, a.buf.keys[1], a.buf.vals[1], a.buf.keys[0], a.buf.vals[0], n, bits,
-               1 << bits, htotals, wtable, windows, wstatus,
-               windows <= kResidentTiles ? nullptr : a.buf.tickets + kMaxRadixPasses,
+  uint32_t* wtable = bucket_window_table(a.buf.rle_status, n);  // 16-byte records
+  // the pass on the high digit, unless the linearize step sorted each tile
+  const bool seg = uses_tile_buckets(a);
+  if (!seg) {
+    const hipError_t e = launch_pass(a, 0, bits, htotals, a.buf.keys[0], a.buf.vals[0],
+                                     a.buf.keys[1], a.buf.vals[1], wtable, stream, kt);
+    if (e != hipSuccess) return e;
+  }
+  const int nseg = seg ? static_cast<int>((a.num_bags + kLinBags - 1) / kLinBags) : 0;
+  launch_timed(kt, "bucket_sort_rle", seg ? bucket_sort_rle<true> : bucket_sort_rle<false>,
+               dim3(windows), dim3(kBucketThreads), 0, stream, a.buf.keys[1], a.buf.vals[1],
+               a.buf.keys[0], a.buf.vals[0], n, bits, 1 << bits, htotals, wtable, windows,
+               wstatus, windows <= kResidentTiles ? nullptr : a.buf.tickets + kMaxRadixPasses,
                a.buf.counters, a.buf.unique_keys, a.buf.run_start, a.buf.run_first,
                RunQueue{a.buf.items1, a.buf.longs, a.buf.long_keys, a.short_max,
                         a.long_threshold, a.chunk},
-               a.spin_limit);
+               a.spin_limit, static_cast<const uint32_t*>(a.buf.tile_rows), nseg);
   return hipGetLastError();
 }
 

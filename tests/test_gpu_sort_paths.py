@@ -8,7 +8,13 @@
 
 Both must leave the lookups in the same order (stable on the id), so unique ids, run
 lengths, weights and state are bit-identical between them; the default path is also
-checked against the CPU reference (runs bit-exact, updates within tolerance)."""
+checked against the CPU reference (runs bit-exact, updates within tolerance).
+
+When a batch has at most 256 linearize tiles (128 bags each), the pass on the high digit is
+done by the linearize step itself (in the stand-alone linearize kernel, or in the launch that
+also pools the forward when the grouping runs with the forward); with more tiles it is a
+radix pass of its own.  Cases on both sides of that limit, plain and grouped, check that
+every variant leaves the same order."""
 import numpy as np
 import pytest
 import torch
@@ -54,6 +60,18 @@ def _cases():
         ("many-tables", workloads.custom(np.random.default_rng(232).integers(3, 60, 300),
                                          [8] * 300, "f32", B=7, lengths=("uniform_int", 0, 6),
                                          key=232), None),
+        # 2 x 16384 bags: 256 linearize tiles (the linearize step scatters)
+        ("256-tiles", workloads.custom([100_000, 50_000], [32, 32], "f32", B=16384,
+                                       lengths=("uniform_int", 0, 6), index_dist=("zipf", 1.1),
+                                       optimizer="rowwise_adagrad", key=233), None),
+        # 3 x 10923 bags: 257 tiles (a radix pass of its own)
+        ("257-tiles", workloads.custom([100_000, 50_000, 3_000], [32, 16, 32], "bf16", B=10923,
+                                       lengths=("uniform_int", 0, 6), index_dist=("zipf", 1.1),
+                                       pooling="mean", psw=True, key=234), None),
+        # one tile of 100 bags
+        ("one-tile", workloads.custom([5_000], [64], "f32", B=100, lengths=("uniform_int", 0, 40),
+                                      index_dist=("zipf", 1.3), optimizer="rowwise_adagrad",
+                                      key=235), None),
     ]
 
 
@@ -64,26 +82,42 @@ def _stages(op):
     return {name for name, _ in op.stage_times()}
 
 
+def _linearize_tiles(spec):
+    return (spec.T * spec.B + 127) // 128
+
+
+def _update(pb, spec, idx, off, psw, G, runs, grouped):
+    if grouped:
+        pb.op.forward_group(spec.B, idx, off, psw)
+        pb.op.backward_update_grouped(spec.B, idx, off, psw, G, spec.lr, spec.eps, runs)
+    else:
+        pb.op.backward_update(spec.B, idx, off, psw, G, spec.lr, spec.eps, runs)
+
+
+@pytest.mark.parametrize("grouped", [False, True], ids=["plain", "grouped"])
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_bucket_and_lsd_paths_bit_identical(case):
+def test_bucket_and_lsd_paths_bit_identical(case, grouped):
     name, spec, batches = case
-    _say(f"[sort paths] {name}")
-    a = make_problem(spec, seed=7, batch=None if batches is None else batches[0])
-    b = make_problem(spec, seed=7, batch=None if batches is None else batches[0])
+    _say(f"[sort paths] {name} grouped={grouped}")
+    idt = torch.int32 if name in ("256-tiles", "one-tile") else torch.int64
+    a = make_problem(spec, seed=7, batch=None if batches is None else batches[0], index_dtype=idt)
+    b = make_problem(spec, seed=7, batch=None if batches is None else batches[0], index_dtype=idt)
     b.op.set_option(tbe.OPTION_SORT, 1)
     a.op.set_option(tbe.OPTION_PROFILE, 1)
     for step in range(2):
         batch = batches[0] if batches is not None else workloads.batch(spec, seed=7, step=step)
-        idx, off, psw = to_device(batch)
+        idx, off, psw = to_device(batch, index_dtype=idt)
         G = workloads.grad_output(spec, seed=7, step=step, device="cuda")
         ra, rb = gpu_runs(a, batch.N), gpu_runs(b, batch.N)
-        a.op.backward_update(spec.B, idx, off, psw, G, spec.lr, spec.eps, ra)
-        b.op.backward_update(spec.B, idx, off, psw, G, spec.lr, spec.eps, rb)
+        _update(a, spec, idx, off, psw, G, ra, grouped)
+        _update(b, spec, idx, off, psw, G, rb, grouped)
         torch.cuda.synchronize()
         if step == 0:
             used = _stages(a.op)
             assert "bucket_sort_rle" in used, f"{name}: bucket path not taken ({used})"
             assert "rle_kernel" not in used
+            scatter = _linearize_tiles(spec) <= 256
+            assert ("radix_pass" in used) == (not scatter), f"{name}: {used}"
         U = int(ra[2].item())
         assert U == int(rb[2].item()) and U > 0
         assert torch.equal(ra[0][:U], rb[0][:U]), f"step {step}: unique ids"

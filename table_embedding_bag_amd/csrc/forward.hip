@@ -309,7 +309,7 @@ __global__ __launch_bounds__(kFusedThreads) void fwd_linearize(ForwardLaunch f, 
   if (bid < lin_blocks) {
     if constexpr (BUCKET) {
       if (bid < (b.num_bags + kLinBags - 1) / kLinBags)
-        linearize_bucket<IT, kFusedThreads, kFusedK>(b, bid);
+        linearize_bucket<IT, kFusedThreads>(b, bid);
     } else {
       linearize_tiles<IT, kFusedThreads, kFusedK>(b, bid, lin_blocks);
     }

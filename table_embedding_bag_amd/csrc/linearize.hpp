@@ -171,31 +171,34 @@ __device__ __forceinline__ void linearize_tiles(const BackwardLaunch& a, int64_t
 // The linearize step for batches whose grouping takes the bucket-local sort
 // (ids of two digits; the high digit is key >> lbits), with the tile's lookups
 // also sorted by the high digit inside the tile's own positions.  Tile `tile`
-// of kLinBags bags, lookups [p0, p1):
-//   1. count: keys are computed and their high digits counted in LDS (lanes
-//      with equal digits matched by ballots, one LDS add each);
+// of kLinBags bags, lookups [p0, p1); wave w owns the consecutive positions
+// [p0 + w*C, p0 + (w+1)*C) (C a multiple of 64), walked in steps of 64:
+//   1. count: keys are computed (the first kStash steps' keys stay in
+//      registers, their loads all issued at once) and each wave counts the
+//      high digits of its positions in its own LDS counters (lanes with equal
+//      digits matched by ballots, the lowest adds their number);
 //   2. the tile's row of segment bounds goes out: row[d] = p0 + the number of
-//      the tile's keys with a high digit below d (row[2^kMaxRadixBits] = p1),
-//      and the counts are added to the global counts of the high digit;
-//   3. the lookups are walked again in rounds of NT * K positions (each wave on
-//      consecutive positions); a round is ranked in LDS with per-wave digit
-//      counters, which keeps lookup order within a digit, and written to
-//      buf.keys[1] / buf.vals[1] at row[d] + the digit's rank in the tile.
-//      The counters are double buffered by round: two barriers per round.
-// No workgroup waits for another: the bucket-local sort gathers a bucket's
-// keys from the tiles' segments [row_i[d], row_i[d + 1]) in tile order, which
-// is lookup order.
-template <typename IT, int NT, int K>
+//      the tile's keys with a high digit below d (row[2^kMaxRadixBits] = p1);
+//      the counts are added to the global counts of the high digit, and every
+//      wave's counter becomes its first position for that digit (digits in
+//      order, waves in order within a digit);
+//   3. place: each wave walks its positions again and writes every key to
+//      buf.keys[1] / buf.vals[1] at its counter plus its rank among equal
+//      digits in the step, which keeps lookup order within a digit.
+// Two barriers per tile; no workgroup waits for another.  The bucket-local
+// sort gathers a bucket's keys from the tiles' segments [row_i[d], row_i[d+1])
+// in tile order, which is lookup order.
+template <typename IT, int NT>
 __device__ __forceinline__ void linearize_bucket(const BackwardLaunch& a, int tile) {
   constexpr int NW = NT / kWave;
   constexpr int DIG = 1 << kMaxRadixBits;
   constexpr int DPT = DIG / NT;  // digits owned per thread
+  constexpr int kStash = 8;      // steps whose keys stay in registers
   static_assert(DPT >= 1 && DPT * NT == DIG, "threads own whole digits");
   __shared__ int64_t s_off[kLinBags + 1];
   __shared__ uint32_t s_roff[kLinBags];
   __shared__ float s_scale[kLinBags];
-  __shared__ uint32_t s_cnt[DIG];  // the tile's digit counts; later each round's digit bases
-  __shared__ __align__(16) uint16_t s_wc[2][NW][DIG];  // per-wave digit counts, by round parity
+  __shared__ __align__(16) uint32_t s_wc[NW][DIG];  // per-wave digit counts, then next positions
   __shared__ uint32_t scratch[NW];
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
@@ -215,9 +218,8 @@ __device__ __forceinline__ void linearize_bucket(const BackwardLaunch& a, int ti
     s_roff[tid] = static_cast<uint32_t>(a.meta[t].roff);
     s_scale[tid] = a.mean ? ((hi > lo) ? 1.0f / static_cast<float>(hi - lo) : 0.0f) : 1.0f;
   }
-  for (int i = tid; i < DIG; i += NT) s_cnt[i] = 0u;
   {
-    uint4* z = reinterpret_cast<uint4*>(&s_wc[0][0][0]);
+    uint4* z = reinterpret_cast<uint4*>(&s_wc[0][0]);
     constexpr int NZ = static_cast<int>(sizeof(s_wc) / sizeof(uint4));
     for (int i = tid; i < NZ; i += NT) z[i] = make_uint4(0u, 0u, 0u, 0u);
   }
@@ -225,118 +227,117 @@ __device__ __forceinline__ void linearize_bucket(const BackwardLaunch& a, int ti
   const int64_t p0 = s_off[0], p1 = s_off[nb];
   const bool even = p1 - p0 == static_cast<int64_t>(nb) * (s_off[1] - p0);
   const float per = even && p1 > p0 ? static_cast<float>(nb) / static_cast<float>(p1 - p0) : 0.0f;
-  const int qoff = wave * (kWave * K) + lane;  // position of (round base, k = 0)
+  const int64_t C = ((p1 - p0 + NW - 1) / NW + kWave - 1) / kWave * kWave;
+  const int64_t c0 = p0 + wave * C;                   // this wave's positions [c0, c1)
+  const int64_t c1 = c0 + C < p1 ? c0 + C : p1;
+  const int steps = c1 > c0 ? static_cast<int>((c1 - c0 + kWave - 1) / kWave) : 0;
+  uint32_t* const wc = s_wc[wave];
 
-  // 1. count
-  for (int64_t base = p0; base < p1; base += NT * K) {
-    int slot[K];
-    bool ok[K];
-    int64_t x[K];
+  // key, bag slot and (with side records) the record of the lookup at p
+  const auto lookup = [&](int64_t p, bool ok, uint32_t* key, int* slot) {
+    *slot = ok ? tile_bag_slot(s_off, nb, p, p0, even, per) : 0;
+    const int64_t x = ok ? lin_index<IT>(a.indices, p) : 0;
+    *key = s_roff[*slot] + static_cast<uint32_t>(x);
+  };
+  const auto record = [&](int64_t p, int slot) {
+    const float pw = a.psw ? a.psw[p] : 1.0f;
+    a.buf.rec[p] = make_uint2(static_cast<uint32_t>(k0 + slot),
+                              __float_as_uint(pw * s_scale[slot]));
+  };
+  const auto count = [&](uint32_t key, bool ok) {
+    const uint32_t d = (key >> lbits) & hmask;
+    const uint64_t peers = match_bits(__ballot(ok), d, hbits);
+    if (ok && popc_below(peers) == 0) wc[d] += __popcll(peers);
+  };
+
+  // 1. count (steps past kStash are read again when placed)
+  uint32_t key[kStash];
+  int slot[kStash];
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int64_t p = base + qoff + k * kWave;
-      ok[k] = p < p1;
-      slot[k] = ok[k] ? tile_bag_slot(s_off, nb, p, p0, even, per) : 0;
-    }
+  for (int s = 0; s < kStash; ++s) {
+    const int64_t p = c0 + s * kWave + lane;
+    lookup(p, s < steps && p < c1, &key[s], &slot[s]);
+  }
 #pragma unroll
-    for (int k = 0; k < K; ++k)
-      x[k] = lin_index<IT>(a.indices, ok[k] ? base + qoff + k * kWave : p1 - 1);
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const uint32_t d = ((s_roff[slot[k]] + static_cast<uint32_t>(x[k])) >> lbits) & hmask;
-      const uint64_t peers = match_bits(__ballot(ok[k]), d, hbits);
-      if (ok[k] && popc_below(peers) == 0) atomicAdd(&s_cnt[d], __popcll(peers));
-    }
+  for (int s = 0; s < kStash; ++s) {
+    if (s >= steps) break;
+    const int64_t p = c0 + s * kWave + lane;
+    const bool ok = p < c1;
+    if (a.use_rec && ok) record(p, slot[s]);
+    count(key[s], ok);
+  }
+  for (int s = kStash; s < steps; ++s) {
+    const int64_t p = c0 + s * kWave + lane;
+    const bool ok = p < c1;
+    uint32_t kk;
+    int sl;
+    lookup(p, ok, &kk, &sl);
+    if (a.use_rec && ok) record(p, sl);
+    count(kk, ok);
   }
   __syncthreads();
 
-  // 2. the tile's row of segment bounds, and the global counts
+  // 2. the tile's row of segment bounds, the global counts, each wave's first
+  // position per digit
   const int d0 = tid * DPT;
-  uint32_t cnt[DPT], csum = 0;
+  uint32_t c[DPT][NW], tot[DPT], tsum = 0;
 #pragma unroll
   for (int q = 0; q < DPT; ++q) {
-    cnt[q] = s_cnt[d0 + q];
-    csum += cnt[q];
+    tot[q] = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      c[q][w] = s_wc[w][d0 + q];
+      tot[q] += c[q][w];
+    }
+    tsum += tot[q];
   }
-  uint32_t all;
-  uint32_t run[DPT];  // next position of each owned digit
   {
-    uint32_t st = static_cast<uint32_t>(p0) + block_excl_n<NW>(csum, scratch, &all);
+    uint32_t all;
+    uint32_t st = static_cast<uint32_t>(p0) + block_excl_n<NW>(tsum, scratch, &all);
     uint32_t* const row = a.buf.tile_rows + static_cast<int64_t>(tile) * kTileRowWords;
     uint32_t* const htot = a.buf.digit_hist + slots;  // the high digit's counts
 #pragma unroll
     for (int q = 0; q < DPT; ++q) {
       row[d0 + q] = st;
-      run[q] = st;
-      if (cnt[q]) atomicAdd(htot + d0 + q, cnt[q]);
-      st += cnt[q];
+      if (tot[q]) atomicAdd(htot + d0 + q, tot[q]);
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        s_wc[w][d0 + q] = st;
+        st += c[q][w];
+      }
     }
     if (tid == 0) row[DIG] = static_cast<uint32_t>(p1);
   }
+  __syncthreads();
 
   // 3. place
   uint32_t* const kout = a.buf.keys[1];
   uint32_t* const vout = a.buf.vals[1];
-  int par = 0;
-  for (int64_t base = p0; base < p1; base += NT * K, par ^= 1) {
-    uint16_t(*const wc)[DIG] = s_wc[par];
-    int slot[K];
-    bool ok[K];
-    int64_t x[K];
-    float pw[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int64_t p = base + qoff + k * kWave;
-      ok[k] = p < p1;
-      slot[k] = ok[k] ? tile_bag_slot(s_off, nb, p, p0, even, per) : 0;
+  const auto place = [&](int64_t p, bool ok, uint32_t k, int sl) {
+    const uint32_t d = (k >> lbits) & hmask;
+    const uint64_t peers = match_bits(__ballot(ok), d, hbits);
+    const uint32_t below = popc_below(peers);
+    const uint32_t pre = ok ? wc[d] : 0u;
+    if (ok && below == 0) wc[d] = pre + __popcll(peers);
+    if (ok) {
+      // pre + below lies in [p0, p1): a digit's positions never pass its count
+      kout[pre + below] = k;
+      vout[pre + below] = a.use_rec ? static_cast<uint32_t>(p) : static_cast<uint32_t>(k0 + sl);
     }
+  };
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int64_t p = ok[k] ? base + qoff + k * kWave : p1 - 1;
-      x[k] = lin_index<IT>(a.indices, p);
-      pw[k] = a.psw ? a.psw[p] : 1.0f;
-    }
-    uint32_t key[K], d[K], rank[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      key[k] = s_roff[slot[k]] + static_cast<uint32_t>(x[k]);
-      d[k] = (key[k] >> lbits) & hmask;
-      const uint64_t peers = match_bits(__ballot(ok[k]), d[k], hbits);
-      const uint32_t below = popc_below(peers);
-      const uint32_t pre = ok[k] ? static_cast<uint32_t>(wc[wave][d[k]]) : 0u;
-      rank[k] = pre + below;
-      if (ok[k] && below == 0) wc[wave][d[k]] = static_cast<uint16_t>(pre + __popcll(peers));
-    }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < DPT; ++q) {
-      const int dd = d0 + q;
-      if (dd > static_cast<int>(hmask)) break;
-      uint32_t c[NW];
-#pragma unroll
-      for (int w = 0; w < NW; ++w) c[w] = wc[w][dd];
-      uint32_t acc = 0;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        wc[w][dd] = static_cast<uint16_t>(acc);
-        acc += c[w];
-        s_wc[par ^ 1][w][dd] = 0;  // last read in the round before this one
-      }
-      s_cnt[dd] = run[q];
-      run[q] += acc;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      if (!ok[k]) continue;
-      const int64_t p = base + qoff + k * kWave;
-      const uint32_t bag = static_cast<uint32_t>(k0 + slot[k]);
-      // pos lies in [p0, p1) (the ranks of a digit never pass its count)
-      const uint32_t pos = s_cnt[d[k]] + wc[wave][d[k]] + rank[k];
-      if (a.use_rec) a.buf.rec[p] = make_uint2(bag, __float_as_uint(pw[k] * s_scale[slot[k]]));
-      kout[pos] = key[k];
-      vout[pos] = a.use_rec ? static_cast<uint32_t>(p) : bag;
-    }
+  for (int s = 0; s < kStash; ++s) {
+    if (s >= steps) break;
+    const int64_t p = c0 + s * kWave + lane;
+    place(p, p < c1, key[s], slot[s]);
+  }
+  for (int s = kStash; s < steps; ++s) {
+    const int64_t p = c0 + s * kWave + lane;
+    const bool ok = p < c1;
+    uint32_t kk;
+    int sl;
+    lookup(p, ok, &kk, &sl);
+    place(p, ok, kk, sl);
   }
 }
 

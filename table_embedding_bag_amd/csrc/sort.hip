@@ -66,9 +66,9 @@ __global__ __launch_bounds__(kLinThreads) void linearize_kernel(BackwardLaunch a
 }
 
 // The same with each tile's lookups sorted by the high digit: one workgroup per tile.
-template <typename IT, int K>
+template <typename IT>
 __global__ __launch_bounds__(kLinThreads) void linearize_bucket_kernel(BackwardLaunch a) {
-  linearize_bucket<IT, kLinThreads, K>(a, blockIdx.x);
+  linearize_bucket<IT, kLinThreads>(a, blockIdx.x);
 }
 
 // Lanes of the wave (among those with ok) whose digit d equals this lane's.
@@ -1061,24 +1061,13 @@ hipError_t launch_linearize_kernel(const BackwardLaunch& a, hipStream_t stream,
                                    const KernelTimer* kt) {
   if (a.num_bags <= 0) return hipSuccess;
   if (uses_tile_buckets(a)) {
-    const int64_t tiles = (a.num_bags + kLinBags - 1) / kLinBags;
-    const dim3 grid(static_cast<unsigned>(tiles));
-    const bool deep = a.num_indices > tiles * kLinThreads;
-    if (a.index64) {
-      if (deep)
-        launch_timed(kt, "linearize_kernel", linearize_bucket_kernel<int64_t, 2>, grid,
-                     dim3(kLinThreads), 0, stream, a);
-      else
-        launch_timed(kt, "linearize_kernel", linearize_bucket_kernel<int64_t, 1>, grid,
-                     dim3(kLinThreads), 0, stream, a);
-    } else {
-      if (deep)
-        launch_timed(kt, "linearize_kernel", linearize_bucket_kernel<int32_t, 2>, grid,
-                     dim3(kLinThreads), 0, stream, a);
-      else
-        launch_timed(kt, "linearize_kernel", linearize_bucket_kernel<int32_t, 1>, grid,
-                     dim3(kLinThreads), 0, stream, a);
-    }
+    const dim3 grid(static_cast<unsigned>((a.num_bags + kLinBags - 1) / kLinBags));
+    if (a.index64)
+      launch_timed(kt, "linearize_kernel", linearize_bucket_kernel<int64_t>, grid,
+                   dim3(kLinThreads), 0, stream, a);
+    else
+      launch_timed(kt, "linearize_kernel", linearize_bucket_kernel<int32_t>, grid,
+                   dim3(kLinThreads), 0, stream, a);
     return hipGetLastError();
   }
   return a.num_bags > int64_t{kLinBags} * kLinMaxBlocks

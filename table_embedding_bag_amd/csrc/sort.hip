@@ -553,6 +553,58 @@ __device__ __forceinline__ void lds_counting_pass(const uint32_t (&key)[kBucketK
     if (w < nwa) s_cnt[w][tid] = 0;
 }
 
+// Stable partition of the elements held in registers (the layout of
+// lds_counting_pass, positions [0, len)) by their bucket b = bucket(key) < nb
+// <= 64, into s_k / s_v, bucket b starting at bstart(b).  Each wave counts
+// its elements per bucket (lanes with equal buckets matched by ballots); lane
+// b of a wave then adds the counts of the earlier waves to bstart(b), and
+// every element takes that base plus its rank.  Two barriers, against five
+// for a counting pass over 1024 digits.  s_pc must be zero on entry (the
+// caller clears it before a barrier); the caller's elements must all have
+// been read out of s_k / s_v before the call.
+template <typename Bucket, typename Start>
+__device__ __forceinline__ void bucket_partition(const uint32_t (&key)[kBucketKpt],
+                                                 const uint32_t (&val)[kBucketKpt], int rr,
+                                                 int len, int nb, Bucket bucket, Start bstart,
+                                                 uint32_t* s_k, uint32_t* s_v,
+                                                 uint32_t (*s_pc)[64]) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int wseg = wave * kWave * rr;
+  const int bits = nb <= 1 ? 0 : 32 - __clz(nb - 1);
+  uint32_t rank[kBucketKpt], bk[kBucketKpt];
+#pragma unroll
+  for (int r = 0; r < kBucketKpt; ++r) {
+    rank[r] = 0u;
+    bk[r] = 0u;
+    if (r < rr) {
+      const bool ok = wseg + r * kWave + lane < len;
+      bk[r] = ok ? bucket(key[r]) : 0u;
+      const uint64_t peers = match_bits(__ballot(ok), bk[r], bits);
+      const uint32_t below = popc_below(peers);
+      const uint32_t pre = ok ? s_pc[wave][bk[r]] : 0u;
+      rank[r] = pre + below;
+      if (ok && below == 0) s_pc[wave][bk[r]] = pre + __popcll(peers);
+    }
+  }
+  __syncthreads();
+  uint32_t base = 0;
+  if (lane < nb) {
+    base = bstart(lane);
+    for (int w = 0; w < wave; ++w) base += s_pc[w][lane];
+  }
+#pragma unroll
+  for (int r = 0; r < kBucketKpt; ++r) {
+    if (r < rr) {
+      const uint32_t pos = __shfl(base, static_cast<int>(bk[r]), kWave) + rank[r];
+      if (wseg + r * kWave + lane < len) {
+        s_k[pos] = key[r];
+        s_v[pos] = val[r];
+      }
+    }
+  }
+  __syncthreads();
+}
+
 // Load positions [start, start + len) (len <= kBucketCap) into registers in
 // the layout of lds_counting_pass.
 __device__ __forceinline__ void load_range(const uint32_t* kin, const uint32_t* vin, int64_t start,
@@ -669,6 +721,7 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
   __shared__ uint32_t s_seglo[SEGS];
   __shared__ uint32_t s_segoff[SEGS];
   __shared__ uint32_t s_hrange[2];
+  __shared__ uint32_t s_pc[SEG ? NW : 1][64];  // bucket_partition's per-wave counts
   __shared__ uint16_t s_cnt[NW][NT];
   __shared__ uint64_t s_slots[NW][256];
   __shared__ uint32_t s_bstart[NT + 1];  // long ranges: bucket starts in the sorted order
@@ -781,17 +834,28 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
             val[r] = s_v[p];
           }
         }
+        const uint32_t hspan = hl - hf;
+        const bool few = SEG && hspan < 64u;  // the same on every thread
+        if (few)
+          for (int i = tid; i < (SEG ? NW : 1) * 64; i += NT) (&s_pc[0][0])[i] = 0u;
         __syncthreads();
         // a key's bucket lies in [hf, hl]; the clamp only matters for a batch
         // whose pass on the high digit gave up a wait (its output then holds
         // stale positions), and keeps the LDS counters in range
         const uint32_t hmask = static_cast<uint32_t>(nbuckets) - 1u;
-        const uint32_t hspan = hl - hf;
         const auto bucket = [lbits, hf, hmask, hspan](uint32_t k) {
           return min(((k >> lbits) & hmask) - hf, hspan);
         };
-        lds_counting_pass(key, val, rr, 0, len, bucket, s_k, s_v, s_cnt, s_slots, s_dstart,
-                          scratch);
+        if (few) {
+          // bucket starts inside the range are known (s_bstart)
+          const uint32_t s0 = static_cast<uint32_t>(start);
+          const auto bstart = [hf, s0](int b) { return s_bstart[hf + b] - s0; };
+          bucket_partition(key, val, rr, len, static_cast<int>(hspan) + 1, bucket, bstart, s_k,
+                           s_v, s_pc);
+        } else {
+          lds_counting_pass(key, val, rr, 0, len, bucket, s_k, s_v, s_cnt, s_slots, s_dstart,
+                            scratch);
+        }
       }
       // the sorted range goes out before the look-back (it does not depend on it)
       for (int i = tid; i < len; i += NT) {

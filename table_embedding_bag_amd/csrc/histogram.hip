@@ -39,7 +39,9 @@ namespace {
 constexpr int kHB = 256;              // bags per workgroup (64 per wave)
 constexpr int kDB = 64;               // output columns per workgroup
 constexpr int kCS = kHistKc + 8;      // LDS row stride in 16-bit elements (bank spread)
-constexpr int kRegIds = 8;            // row ids of a bag held in registers
+constexpr int kRegIds = 8;            // row ids of a bag held in registers (bags of at most 8)
+constexpr int kEntCap = 512;          // listed lookups per wave and batch
+constexpr int kListSteps = kEntCap / kWave;
 constexpr float kNoBag = -1.0f, kLongBag = -2.0f;
 constexpr int kMaxChunks = kHistMaxRows / kHistKc;
 
@@ -144,34 +146,28 @@ __global__ __launch_bounds__(kBlock) void hist_transpose(HistLaunch a) {
 }
 
 // Adds v (+1 or -1) to the count rows of a wave's bags for the lookups that
-// fall in one chunk: entries {bag slot in wave << 8 | row in chunk}, listed
-// by chunk once per tile.
+// fall in one chunk: entries {bag slot in wave << 6 | row in chunk}, listed
+// by chunk.
 template <typename M>
-__device__ __forceinline__ void add_listed(uint32_t* cw, const uint32_t* ent, int n, int row0,
+__device__ __forceinline__ void add_listed(uint32_t* cw, const uint16_t* ent, int n, int row0,
                                            float v) {
   for (int e = lane_id(); e < n; e += kWave) {
     const uint32_t q = ent[e];
-    const int el = (row0 + static_cast<int>(q >> 8)) * kCS + static_cast<int>(q & 0xFFu);
+    const int el = (row0 + static_cast<int>(q >> 6)) * kCS + static_cast<int>(q & 63u);
     M::lds_add(cw + (el >> 1), el & 1, v);
   }
 }
 
-// The same for the ids of this thread's bag beyond the first kRegIds (bags
-// longer than kRegIds only): they are re-read for every chunk.
-template <typename M, typename IT>
-__device__ __forceinline__ bool add_rest(const HistLaunch& a, uint32_t* cw, int row_base, int len,
-                                         int64_t p0, int k0, float v) {
-  bool any = false;
-  for (int j = kRegIds; j < len; ++j) {
-    const int64_t xj = ld_index<IT>(a.indices, p0 + j);
-    const uint64_t off = static_cast<uint64_t>(xj - k0);
-    if (off < static_cast<uint64_t>(kHistKc)) {
-      const int el = row_base + static_cast<int>(off);
-      M::lds_add(cw + (el >> 1), el & 1, v);
-      any = true;
-    }
+// Lanes among `active` whose value c (of `bits` bits) equals this lane's: one
+// ballot per bit.  Call with the whole wave.
+__device__ __forceinline__ uint64_t match_value(uint64_t active, uint32_t c, int bits) {
+  uint64_t peers = active;
+  for (int bit = 0; bit < bits; ++bit) {
+    const bool set = (c >> bit) & 1u;
+    const uint64_t bal = __ballot(set);
+    peers &= set ? bal : ~bal;
   }
-  return any;
+  return peers;
 }
 
 template <int ST, typename IT>
@@ -179,7 +175,8 @@ __global__ __launch_bounds__(kBlock) void fwd_histogram(HistLaunch a) {
   using M = Mma<ST>;
   __shared__ __align__(16) uint16_t s_c[kHB * kCS];  // count rows [bag][row in chunk]
   __shared__ float s_scale[kHB];  // output scale per bag; kNoBag: no bag, kLongBag: gathered
-  __shared__ uint32_t s_ent[kWavesPerBlock][kWave * kRegIds];  // per wave, by chunk
+  __shared__ uint16_t s_ent[kWavesPerBlock][kEntCap];  // per wave and batch, by chunk
+  __shared__ uint32_t s_boff[kWavesPerBlock][kWave + 1];  // the wave's bag starts, from its first lookup
   __shared__ uint32_t s_cnt[kWavesPerBlock][kMaxChunks];
   __shared__ uint32_t s_fill[kWavesPerBlock][kMaxChunks];
   __shared__ uint32_t s_start[kWavesPerBlock][kMaxChunks + 1];
@@ -211,13 +208,6 @@ __global__ __launch_bounds__(kBlock) void fwd_histogram(HistLaunch a) {
     len = static_cast<int>(ld_index<IT>(a.offsets, k + 1) - p0);
   }
   const bool fallback = len > M::kCountCap;  // pooled by the gather loop below
-  int32_t x[kRegIds];
-#pragma unroll
-  for (int j = 0; j < kRegIds; ++j) {
-    int64_t v = -1;
-    if (j < len && !fallback) v = ld_index<IT>(a.indices, p0 + j);
-    x[j] = (v >= 0 && v < ht.epad) ? static_cast<int32_t>(v) : -kHistKc - 1;
-  }
   const int my_len = fallback ? 0 : len;
   s_scale[tid] = tid >= nb ? kNoBag
                  : fallback ? kLongBag
@@ -228,29 +218,51 @@ __global__ __launch_bounds__(kBlock) void fwd_histogram(HistLaunch a) {
 #pragma unroll
     for (int i = 0; i < kCS / 8; ++i) c4[i] = make_uint4(0u, 0u, 0u, 0u);
   }
-
-  // list the wave's registered lookups by chunk: counts, offsets, then entries
-  if (lane < kMaxChunks) s_cnt[wave][lane] = 0u, s_fill[wave][lane] = 0u;
+  // The wave's bags are consecutive, so its lookups are the positions
+  // [P0, P1).  Waves whose bags all have at most kRegIds lookups keep their
+  // ids in registers (one load round); the others list all their lookups with
+  // the whole wave on consecutive positions, kEntCap at a time.
+  const int64_t P0 = __shfl(p0, 0, kWave);
+  int64_t P1 = tid < nb ? p0 + len : 0;
 #pragma unroll
-  for (int j = 0; j < kRegIds; ++j)
-    if (j < my_len && x[j] >= 0) atomicAdd(&s_cnt[wave][x[j] / kHistKc], 1u);
-  {
-    const uint32_t cnt = lane < kMaxChunks ? s_cnt[wave][lane] : 0u;
-    uint32_t tot;
-    const uint32_t st = wave_excl(cnt, &tot);
-    if (lane < kMaxChunks) s_start[wave][lane] = st;
-    if (lane == 0) s_start[wave][kMaxChunks] = tot;
+  for (int o = kWave >> 1; o >= 1; o >>= 1) {
+    const int64_t y = __shfl_xor(P1, o, kWave);
+    P1 = y > P1 ? y : P1;
   }
+  if (P1 < P0) P1 = P0;  // a wave without bags
+  s_boff[wave][lane] = static_cast<uint32_t>((tid < nb ? p0 : P1) - P0);
+  if (lane == 0) s_boff[wave][kWave] = static_cast<uint32_t>(P1 - P0);
+  const bool rest = __any(my_len > kRegIds);  // some bag of the wave is longer than kRegIds
+  int32_t x[kRegIds];
 #pragma unroll
-  for (int j = 0; j < kRegIds; ++j)
-    if (j < my_len && x[j] >= 0) {
-      const int c = x[j] / kHistKc;
-      s_ent[wave][s_start[wave][c] + atomicAdd(&s_fill[wave][c], 1u)] =
-          (static_cast<uint32_t>(lane) << 8) | static_cast<uint32_t>(x[j] & (kHistKc - 1));
+  for (int j = 0; j < kRegIds; ++j) {
+    int64_t v = -1;
+    if (!rest && j < my_len) v = ld_index<IT>(a.indices, p0 + j);
+    x[j] = (v >= 0 && v < ht.epad) ? static_cast<int32_t>(v) : -kHistKc - 1;
+  }
+  const int cbits = nchunks <= 1 ? 0 : 32 - __clz(nchunks - 1);
+  // the bag of a listed position: bags of 16 or more lookups on average are
+  // followed lane by lane (positions only grow), shorter ones binary searched
+  const bool follow = P1 - P0 >= int64_t{16} * kWave;
+  int cur = 0;
+  const auto bag_of = [&](uint32_t rel) {
+    if (follow) {
+      while (cur < kWave - 1 && s_boff[wave][cur + 1] <= rel) ++cur;
+      return cur;
     }
-  const bool rest = __any(my_len > kRegIds);  // some bag of the wave has ids beyond registers
+    int lo = 0, hi = kWave;  // the last slot starting at or before rel
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_boff[wave][mid] <= rel)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    return lo;
+  };
+  const int nbatch = rest ? static_cast<int>((P1 - P0 + kEntCap - 1) / kEntCap) : 1;
 
-  // B operands (W^T) straight from L2 into registers, one chunk ahead:
+  // B operands (W^T) straight from L2 into registers:
   // lane holds column n0 + (lane & 15), rows k0 + ks*32 + (lane >> 4)*8 .. +8
   const uint16_t* wcol =
       a.wt + ht.wt_off + static_cast<int64_t>(d0 + (lane & 15)) * ht.epad + (lane >> 4) * 8;
@@ -260,42 +272,135 @@ __global__ __launch_bounds__(kBlock) void fwd_histogram(HistLaunch a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int row_base = tid * kCS;
+  // Lookups are listed by chunk (entries {bag slot << 6 | row in chunk}):
+  // counts, offsets, then entries.  LDS operations of one wave complete in
+  // order, so the wave's lists need no barrier.
+  const auto offsets_by_chunk = [&]() {
+    const uint32_t cnt = lane < kMaxChunks ? s_cnt[wave][lane] : 0u;
+    uint32_t tot;
+    const uint32_t st = wave_excl(cnt, &tot);
+    if (lane < kMaxChunks) s_start[wave][lane] = st;
+    if (lane == 0) s_start[wave][kMaxChunks] = tot;
+  };
+  if (!rest) {  // the registered ids, once
+    if (lane < kMaxChunks) s_cnt[wave][lane] = 0u, s_fill[wave][lane] = 0u;
+#pragma unroll
+    for (int j = 0; j < kRegIds; ++j)
+      if (j < my_len && x[j] >= 0) atomicAdd(&s_cnt[wave][x[j] / kHistKc], 1u);
+    offsets_by_chunk();
+#pragma unroll
+    for (int j = 0; j < kRegIds; ++j)
+      if (j < my_len && x[j] >= 0) {
+        const int c = x[j] / kHistKc;
+        s_ent[wave][s_start[wave][c] + atomicAdd(&s_fill[wave][c], 1u)] =
+            static_cast<uint16_t>((lane << 6) | (x[j] & (kHistKc - 1)));
+      }
+  }
   __syncthreads();  // s_scale
-  for (int c = 0; c < nchunks; ++c) {
-    const int k0 = c * kHistKc;
-    uint4 bf[2][4];
+  for (int bt = 0; bt < nbatch; ++bt) {
+    const int64_t q0 = P0 + static_cast<int64_t>(bt) * kEntCap;
+    const int64_t q1 = q0 + kEntCap < P1 ? q0 + kEntCap : P1;
+    // a table of one row chunk: the batch's lookups go straight into the
+    // count tile, which is multiplied once and then cleared (no lists)
+    const bool direct = rest && nchunks == 1;
+    if (direct) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        bf[ks][nt] = nt < NT ? *reinterpret_cast<const uint4*>(
-                                   wcol + static_cast<int64_t>(nt * 16) * ht.epad + k0 + ks * 32)
-                             : make_uint4(0u, 0u, 0u, 0u);
-    // the wave's count rows for chunk c (LDS operations of one wave complete
-    // in order, so no barrier is needed before the reads below)
-    const int es = static_cast<int>(s_start[wave][c]);
-    const int en = static_cast<int>(s_start[wave][c + 1]) - es;
-    add_listed<M>(cw, s_ent[wave] + es, en, wave * 64, 1.0f);
-    bool extra = false;
-    if (rest) extra = __any(add_rest<M, IT>(a, cw, row_base, my_len, p0, k0, 1.0f));
-    if (en == 0 && !extra) continue;  // no lookup of this wave's bags in this chunk
-#pragma unroll
-    for (int ks = 0; ks < kHistKc / 32; ++ks) {
-      const int col = ks * 32 + (lane >> 4) * 8;
-      uint4 af[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        af[mt] = *reinterpret_cast<const uint4*>(s_c + (wave * 64 + mt * 16 + (lane & 15)) * kCS + col);
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        if (nt < NT) {
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt) acc[mt][nt] = M::mma(af[mt], bf[ks][nt], acc[mt][nt]);
+      for (int u = 0; u < kListSteps; ++u) {
+        const int64_t p = q0 + u * kWave + lane;
+        int lo = 0;
+        int64_t v = -1;
+        if (q0 + u * kWave < q1 && p < q1) {
+          lo = bag_of(static_cast<uint32_t>(p - P0));
+          v = ld_index<IT>(a.indices, p);
         }
+        if (v >= 0 && v < ht.epad && s_scale[wave * kWave + lo] >= 0.0f) {
+          const int el = (wave * kWave + lo) * kCS + static_cast<int>(v);
+          M::lds_add(cw + (el >> 1), el & 1, 1.0f);
+        }
+      }
     }
-    add_listed<M>(cw, s_ent[wave] + es, en, wave * 64, -1.0f);
-    if (extra) add_rest<M, IT>(a, cw, row_base, my_len, p0, k0, -1.0f);
+    if (rest && !direct) {
+      // the batch's positions, listed by the whole wave: the kListSteps steps
+      // of 64 positions issue their id loads together, and each lookup's entry
+      // stays in a register from the count to the fill
+      if (lane < kMaxChunks) s_cnt[wave][lane] = 0u, s_fill[wave][lane] = 0u;
+      int64_t v[kListSteps];
+      int slot[kListSteps];
+#pragma unroll
+      for (int u = 0; u < kListSteps; ++u) {
+        const int64_t p = q0 + u * kWave + lane;
+        v[u] = -1;
+        slot[u] = 0;
+        if (q0 + u * kWave < q1 && p < q1) {
+          slot[u] = bag_of(static_cast<uint32_t>(p - P0));
+          v[u] = ld_index<IT>(a.indices, p);
+        }
+      }
+      uint32_t ent[kListSteps];  // chunk << 16 | entry, or ~0 for no lookup
+#pragma unroll
+      for (int u = 0; u < kListSteps; ++u) {
+        if (q0 + u * kWave >= q1) break;
+        const bool valid = v[u] >= 0 && v[u] < ht.epad && s_scale[wave * kWave + slot[u]] >= 0.0f;
+        const uint32_t c = valid ? static_cast<uint32_t>(v[u] / kHistKc) : 0u;
+        ent[u] = valid ? (c << 16) | static_cast<uint32_t>((slot[u] << 6) |
+                                                           static_cast<int>(v[u] & (kHistKc - 1)))
+                       : ~0u;
+        const uint64_t peers = match_value(__ballot(valid), c, cbits);
+        if (valid && popc_below(peers) == 0) s_cnt[wave][c] += __popcll(peers);
+      }
+      offsets_by_chunk();
+#pragma unroll
+      for (int u = 0; u < kListSteps; ++u) {
+        if (q0 + u * kWave >= q1) break;
+        const bool valid = ent[u] != ~0u;
+        const uint32_t c = valid ? ent[u] >> 16 : 0u;
+        const uint64_t peers = match_value(__ballot(valid), c, cbits);
+        const uint32_t below = popc_below(peers);
+        const uint32_t pre = valid ? s_fill[wave][c] : 0u;
+        if (valid) s_ent[wave][s_start[wave][c] + pre + below] = static_cast<uint16_t>(ent[u] & 0xFFFFu);
+        if (valid && below == 0) s_fill[wave][c] = pre + __popcll(peers);
+      }
+    }
+
+    for (int c = 0; c < nchunks; ++c) {
+      const int k0 = c * kHistKc;
+      uint4 bf[2][4];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          bf[ks][nt] = nt < NT ? *reinterpret_cast<const uint4*>(
+                                     wcol + static_cast<int64_t>(nt * 16) * ht.epad + k0 + ks * 32)
+                               : make_uint4(0u, 0u, 0u, 0u);
+      // the wave's count rows for chunk c
+      const int es = direct ? 0 : static_cast<int>(s_start[wave][c]);
+      const int en = direct ? 0 : static_cast<int>(s_start[wave][c + 1]) - es;
+      if (!direct) {
+        if (en == 0) continue;  // no lookup of this wave's bags in this chunk
+        add_listed<M>(cw, s_ent[wave] + es, en, wave * 64, 1.0f);
+      }
+#pragma unroll
+      for (int ks = 0; ks < kHistKc / 32; ++ks) {
+        const int col = ks * 32 + (lane >> 4) * 8;
+        uint4 af[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          af[mt] = *reinterpret_cast<const uint4*>(s_c + (wave * 64 + mt * 16 + (lane & 15)) * kCS + col);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          if (nt < NT) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) acc[mt][nt] = M::mma(af[mt], bf[ks][nt], acc[mt][nt]);
+          }
+      }
+      if (direct) {  // this lane's count row back to zero
+        uint4* c4 = reinterpret_cast<uint4*>(s_c + tid * kCS);
+#pragma unroll
+        for (int i = 0; i < kCS / 8; ++i) c4[i] = make_uint4(0u, 0u, 0u, 0u);
+      } else {
+        add_listed<M>(cw, s_ent[wave] + es, en, wave * 64, -1.0f);
+      }
+    }
   }
 
   // results: lane holds rows 4*(lane/16) + r of each 16 x 16 tile, column lane % 16

@@ -35,6 +35,10 @@ HIST = [
     # fp16 counts are exact up to 2048
     workloads.custom([100], [32], "f16", B=6, lengths=("uniform_int", 2040, 2056),
                      index_dist=("zipf", 1.5), pooling="mean", key=305),
+    # bags longer than the ids a lane keeps in registers: the wave lists its lookups in
+    # batches of 512 (up to 15 per wave here), 16 row chunks, a wave with only short bags
+    workloads.custom([1024, 64, 300], [64, 32, 16], "bf16", B=300,
+                     lengths=("uniform_int", 9, 120), index_dist=("zipf", 1.1), key=307),
 ]
 
 

@@ -79,7 +79,45 @@ def parse():
                         "(for counter collection of one kind of call)")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain device copy of known size (counter calibration)")
+    p.add_argument("--histogram-sweep", action="store_true",
+                   help="only compare the count-matrix forward with the gather forward over "
+                        "table rows E and bag length L (16 bf16 tables, D=64, B=16384, uniform "
+                        "ids): one JSON line per (E, L)")
     return p.parse_args()
+
+
+def histogram_sweep():
+    """Crossover of the count-matrix forward against the gather: kernel times (HIP events,
+    10 calls after 3 warm-up calls) over E in {64 .. 1024} and L in {4 .. 128}."""
+    import torch
+    import table_embedding_bag_amd as tbe
+    import workloads
+    T, D, B = 16, 64, 16384
+    for E in (64, 128, 256, 512, 1024):
+        for L in (4, 8, 16, 32, 64, 128):
+            spec = workloads.custom([E] * T, [D] * T, "bf16", B=B, lengths=("fixed", L), key=900)
+            W = workloads.weights(spec, 0, "cuda")
+            hb = workloads.batch(spec, 0)
+            idx = torch.from_numpy(hb.indices).cuda()
+            off = torch.from_numpy(hb.offsets).cuda()
+            row = {"E": E, "L": L, "T": T, "D": D, "B": B}
+            for mode, flags in (("gather", 0), ("histogram", tbe.FLAG_FORCE_HISTOGRAM)):
+                op = tbe.TBE(spec.rows, spec.dims, W, None, pooling="sum", optimizer="sgd",
+                             flags=flags)
+                for _ in range(3):
+                    op.forward(B, idx, off)
+                torch.cuda.synchronize()
+                op.set_option(tbe.OPTION_PROFILE, 1)
+                tbe.tbe_stage_times(op.handle)
+                for _ in range(10):
+                    op.forward(B, idx, off)
+                us = sum(ms for _, ms in tbe.tbe_stage_times(op.handle)) / 10 * 1e3
+                row[mode + "_us"] = round(us, 2)
+                op.close()
+            row["histogram_speedup"] = round(row["gather_us"] / row["histogram_us"], 3)
+            print(json.dumps(row), flush=True)
+            del W, idx, off
+            torch.cuda.empty_cache()
 
 
 def copy_probe():
@@ -622,6 +660,9 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.histogram_sweep:
+        histogram_sweep()
         return
 
     import torch

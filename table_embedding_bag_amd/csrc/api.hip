@@ -252,6 +252,7 @@ struct BwdPlan {
   size_t o_keys[2], o_vals[2], o_rec, o_zero, o_uniq, o_start, o_first, o_longs, o_long_keys,
       o_items1, o_p1, o_truns, o_rows;
   int64_t row_words = 0;
+  int32_t first_stride = 1;
   bool per_table = false;
   size_t bytes = 0;
 };
@@ -322,7 +323,8 @@ bool plan_backward(const tbe_handle* h, int32_t B, int64_t n, bool vec, int64_t 
   p->o_zero = cv.take(4 * static_cast<size_t>(p->zero_words));
   p->o_uniq = cv.take(4 * static_cast<size_t>(n));
   p->o_start = cv.take(4 * static_cast<size_t>(n + 1));
-  p->o_first = cv.take(4 * static_cast<size_t>(n));
+  p->first_stride = n <= kWideRadixMaxKeys ? 4 : 1;
+  p->o_first = cv.take(4 * static_cast<size_t>(n) * p->first_stride);
   p->o_longs = cv.take(16 * static_cast<size_t>(p->long_ub));
   p->o_long_keys = cv.take(4 * static_cast<size_t>(p->long_ub));
   p->o_items1 = cv.take(8 * static_cast<size_t>(p->items1_ub));
@@ -399,6 +401,7 @@ void fill_backward(const tbe_handle* h, int32_t B, const void* indices, const vo
   b.unique_keys = reinterpret_cast<uint32_t*>(w + p.o_uniq);
   b.run_start = reinterpret_cast<uint32_t*>(w + p.o_start);
   b.run_first = reinterpret_cast<uint32_t*>(w + p.o_first);
+  b.first_stride = p.first_stride;
   b.longs = reinterpret_cast<uint4*>(w + p.o_longs);
   b.long_keys = reinterpret_cast<uint32_t*>(w + p.o_long_keys);
   b.items1 = reinterpret_cast<uint2*>(w + p.o_items1);

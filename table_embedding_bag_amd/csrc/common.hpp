@@ -277,7 +277,8 @@ struct BackwardBuffers {
   int64_t zero_words;       // size of the zeroed region, in 32-bit words
   uint32_t* unique_keys;    // [N]
   uint32_t* run_start;      // [N + 1]
-  uint32_t* run_first;      // [N]: sorted value of each run's first lookup
+  uint32_t* run_first;      // [N][first_stride]: sorted values of each run's first lookups
+  int32_t first_stride;     // 4 for batches of at most 2^20 lookups (the first four), else 1
   uint32_t* table_runs;     // [T + 1]: first run id of each table (per-table lane groups)
   uint32_t* tile_rows;      // [linearize tiles][kTileRowWords] segment bounds (linearize_bucket)
   uint2* items1;            // workgroup items: {first position, medium flag | length}

@@ -302,11 +302,12 @@ __device__ __forceinline__ void short_run(const BackwardLaunch& a, const uint32_
                                           int t_known, int Gs, int gl, int leader, int Gq) {
   int64_t s = 0, e = 0;
   uint32_t key = 0, first = 0;
+  const int fs = a.buf.first_stride;
   if (valid) {
     s = a.buf.run_start[r];
     e = a.buf.run_start[r + 1];
     key = a.buf.unique_keys[r];
-    first = a.buf.run_first[r];
+    if (gl < fs) first = a.buf.run_first[static_cast<int64_t>(r) * fs + gl];
   }
   const int len = valid ? static_cast<int>(e - s) : 0;
   if (valid && a.out_unique && gl == 0) {
@@ -316,9 +317,9 @@ __device__ __forceinline__ void short_run(const BackwardLaunch& a, const uint32_
   if (!valid || len > Gq) return;
   uint32_t my_bag = 0;
   float my_coef = 0.0f;
-  // the run's first lookup came with its bounds, so a run of one lookup
-  // reads no sorted value
-  if (gl < len) lookup_of<REC>(a, gl == 0 ? first : sorted_vals[s + gl], &my_bag, &my_coef);
+  // the run's first lookups (one, or four for batches of at most 2^20) came
+  // with its bounds, so a run of that many reads no sorted value
+  if (gl < len) lookup_of<REC>(a, gl < fs ? first : sorted_vals[s + gl], &my_bag, &my_coef);
   const int t = t_known >= 0 ? t_known : table_of_key(a, s_meta, key);
   const TableMeta m = meta_of(a, s_meta, t);
   const int64_t tb = static_cast<int64_t>(t) * a.B;

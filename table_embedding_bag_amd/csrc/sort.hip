@@ -398,7 +398,7 @@ __global__ __launch_bounds__(1024) void rle_kernel(const uint32_t* __restrict__ 
                                                      int ntiles, uint32_t* status, uint32_t* ticket,
                                                      uint32_t* counters, uint32_t* unique_keys,
                                                      uint32_t* run_start, uint32_t* run_first,
-                                                     uint32_t spin_limit) {
+                                                     int fstride, uint32_t spin_limit) {
   constexpr int NT = 1024;
   constexpr int PER = kRleTile / NT;
   __shared__ uint32_t s_k[kRleTile + 1];
@@ -457,7 +457,8 @@ __global__ __launch_bounds__(1024) void rle_kernel(const uint32_t* __restrict__ 
       if (r < static_cast<uint64_t>(n)) {
         unique_keys[r] = s_k[i + 1];
         run_start[r] = static_cast<uint32_t>(p);
-        run_first[r] = vals[p];
+        for (int q = 0; q < fstride; ++q)
+          run_first[static_cast<int64_t>(r) * fstride + q] = p + q < n ? vals[p + q] : 0u;
       }
       ++r;
     }
@@ -713,7 +714,7 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
     uint32_t* vout, int64_t n, int lbits, int nbuckets, const uint32_t* __restrict__ htotals,
     const uint32_t* __restrict__ wtable, int ntiles, uint32_t* status, uint32_t* ticket,
     uint32_t* counters, uint32_t* unique_keys, uint32_t* run_start, uint32_t* run_first,
-    RunQueue q, uint32_t spin_limit, const uint32_t* __restrict__ rows, int nseg) {
+    int fstride, RunQueue q, uint32_t spin_limit, const uint32_t* __restrict__ rows, int nseg) {
   constexpr int NT = kBucketThreads, NW = kBucketWaves, CAP = kBucketCap;
   constexpr int SEGS = SEG ? kTileBucketMaxTiles : 1;
   __shared__ uint32_t s_k[CAP];
@@ -1012,7 +1013,16 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
         if (r < static_cast<uint64_t>(n)) {
           unique_keys[r] = s_k[i];
           run_start[r] = ps;
-          run_first[r] = s_v[i];
+          if (fstride == 4) {  // 16-byte aligned: the region starts 256-byte aligned
+            uint4 f4;
+            f4.x = s_v[i];
+            f4.y = i + 1 < len_l ? s_v[i + 1] : 0u;
+            f4.z = i + 2 < len_l ? s_v[i + 2] : 0u;
+            f4.w = i + 3 < len_l ? s_v[i + 3] : 0u;
+            reinterpret_cast<uint4*>(run_first)[r] = f4;
+          } else {
+            run_first[r] = s_v[i];
+          }
         }
         if (q.short_max > 0 && rl > static_cast<uint32_t>(q.short_max)) {
           if (rl >= static_cast<uint32_t>(q.long_threshold)) {
@@ -1046,7 +1056,9 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
       if (head && r0 + ex < static_cast<uint64_t>(n)) {
         unique_keys[r0 + ex] = k;
         run_start[r0 + ex] = static_cast<uint32_t>(start + i);
-        run_first[r0 + ex] = vout[start + i];
+        for (int f = 0; f < fstride; ++f)
+          run_first[static_cast<int64_t>(r0 + ex) * fstride + f] =
+              i + f < len64 ? vout[start + i + f] : 0u;
       }
       r0 += t3;
     }
@@ -1231,6 +1243,7 @@ hipError_t launch_sort_encode(const BackwardLaunch& a, hipStream_t stream, const
                a.buf.keys[0], a.buf.vals[0], n, bits, 1 << bits, htotals, wtable, windows,
                wstatus, windows <= kResidentTiles ? nullptr : a.buf.tickets + kMaxRadixPasses,
                a.buf.counters, a.buf.unique_keys, a.buf.run_start, a.buf.run_first,
+               a.buf.first_stride,
                RunQueue{a.buf.items1, a.buf.longs, a.buf.long_keys, a.short_max,
                         a.long_threshold, a.chunk},
                a.spin_limit, static_cast<const uint32_t*>(a.buf.tile_rows), nseg);
@@ -1245,7 +1258,8 @@ hipError_t launch_run_length_encode(const BackwardLaunch& a, const uint32_t* sor
   launch_timed(kt, "rle_kernel", rle_kernel, dim3(ntiles), dim3(1024), 0, stream, sorted_keys,
                sorted_vals, n, ntiles, a.buf.rle_status,
                ntiles <= kResidentTiles ? nullptr : a.buf.tickets + kMaxRadixPasses,
-               a.buf.counters, a.buf.unique_keys, a.buf.run_start, a.buf.run_first, a.spin_limit);
+               a.buf.counters, a.buf.unique_keys, a.buf.run_start, a.buf.run_first,
+               a.buf.first_stride, a.spin_limit);
   return hipGetLastError();
 }
 

@@ -394,9 +394,11 @@ void fill_backward(const tbe_handle* h, int32_t B, const void* indices, const vo
   b.counters = reinterpret_cast<uint32_t*>(w + p.o_zero);
   b.tickets = b.counters + kNumCounters;
   b.digit_hist = b.tickets + kNumTickets;
-  b.sort_status = b.digit_hist + p.passes * p.slots;
-  b.rle_status = b.sort_status + static_cast<int64_t>(p.passes) * p.sort_tiles * p.slots;
+  b.rle_status = b.digit_hist + p.passes * p.slots;
   b.piece_tickets = b.rle_status + p.rle_tiles;
+  // last, so that a call whose linearize step sorts the tiles (no radix pass)
+  // clears only what comes before
+  b.sort_status = b.piece_tickets + p.chunks_ub / kFinPiece + 1;
   b.zero_words = p.zero_words;
   b.unique_keys = reinterpret_cast<uint32_t*>(w + p.o_uniq);
   b.run_start = reinterpret_cast<uint32_t*>(w + p.o_start);

@@ -264,8 +264,8 @@ struct BackwardBuffers {
   uint2* rec;               // per lookup {bag, coefficient bits} when needed, else null
   // One contiguous region zeroed at the start of every backward call:
   //   counters [kNumCounters], tickets [kNumTickets], digit_hist [passes][slots],
-  //   sort_status [passes][sort tiles][slots], rle_status [rle tiles],
-  //   piece_tickets [chunks cap / kFinPiece + 1]
+  //   rle_status [rle tiles], piece_tickets [chunks cap / kFinPiece + 1],
+  //   sort_status [passes][sort tiles][slots] (not cleared when no radix pass runs)
   // (slots = radix_slots(digit bits))
   uint32_t* counters;
   uint32_t* tickets;        // tile tickets: one per radix pass, then the RLE's

@@ -1094,7 +1094,12 @@ int sort_tile_keys(int64_t n, int key_bits) {
 hipError_t launch_init_workspace(const BackwardLaunch& a, hipStream_t stream,
                                  const KernelTimer* kt) {
   // the counters, histograms and look-back status words the later kernels chain through
-  const int64_t nvec = (a.buf.zero_words + 3) / 4;
+  // the radix passes' status words come last and are not needed when the
+  // linearize step sorts each tile by the high digit
+  const int64_t words =
+      uses_tile_buckets(a) ? static_cast<int64_t>(a.buf.sort_status - a.buf.counters)
+                           : a.buf.zero_words;
+  const int64_t nvec = (words + 3) / 4;
   int64_t zblocks = (nvec + kBlock - 1) / kBlock;
   if (zblocks > 1024) zblocks = 1024;
   launch_timed(kt, "init_workspace", init_workspace,

@@ -410,9 +410,8 @@ def measure(wl, args, steps, warmup, headline):
     torch = wl.torch
     out = {}
     phase = args.phase if headline else "all"
-    for i in range(warmup):
-        wl.pair(i, args.plain)
-    torch.cuda.synchronize()
+    # host-side statistics first, so that the warm-up steps run right before the timed
+    # ones (a GPU left idle between them starts the timed steps at lower clocks)
     routed = [] if wl.forward_mode == "gather" else hist_tables(wl.spec)
     gather = [t for t in range(wl.spec.T) if t not in routed]
     alg, mean_stats, stats0 = mean_alg_bytes(wl, gather)
@@ -422,6 +421,9 @@ def measure(wl, args, steps, warmup, headline):
                     "batch0": {"lookups": stats0["N"], "unique_rows": stats0["U"],
                                "long_run_share": round(stats0["long_run_share"], 3),
                                "max_run": stats0["max_run"]}}
+    for i in range(warmup):
+        wl.pair(i, args.plain)
+    torch.cuda.synchronize()
     if phase in ("all", "hot"):
         el, lookups = wl.timed(lambda i: wl.pair(i, args.plain), warmup, steps)
         out["elapsed"], out["lookups"] = el, lookups

@@ -299,7 +299,8 @@ bool plan_backward(const tbe_handle* h, int32_t B, int64_t n, bool vec, int64_t 
   p->row_words = lin_tiles <= kTileBucketMaxTiles ? lin_tiles * kTileRowWords : 0;
   // look-back status words of the RLE kernel, or those of the bucket-local
   // sort's windows followed by the windows' 4-word range records
-  p->rle_tiles = 5 * static_cast<int>((n + kBucketWindow - 1) / kBucketWindow) + 4;
+  p->rle_tiles = std::max(5 * static_cast<int>((n + kBucketWindow - 1) / kBucketWindow) + 4,
+                          2 * kBucketMaxWindows);
   p->passes = radix_passes(h->key_bits, n);
   p->slots = radix_slots(radix_digit_bits(h->key_bits, n));
   {
@@ -1080,7 +1081,9 @@ tbe_status tbe_forward_group(tbe_handle* h, int32_t B, const void* indices, cons
     // a grouping this workspace held before is overwritten from here on
     auto old = find_group(h, workspace);
     if (old != h->groups.end()) h->groups.erase(old);
-    if (launch_init_workspace(a, s, kt) != hipSuccess) return TBE_ERR_HIP;
+    // (a linearize step that sorts the tiles clears the workspace itself)
+    if (!uses_tile_buckets(a) && launch_init_workspace(a, s, kt) != hipSuccess)
+      return TBE_ERR_HIP;
     const bool fused = n <= kFusedMaxLookups;
     st = forward_impl(h, B, indices, offsets, index_dtype, n, psw, output, s, false,
                       fused ? &a : nullptr);

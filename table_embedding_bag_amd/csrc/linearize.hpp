@@ -178,16 +178,16 @@ __device__ __forceinline__ void linearize_tiles(const BackwardLaunch& a, int64_t
 //      high digits of its positions in its own LDS counters (lanes with equal
 //      digits matched by ballots, the lowest adds their number);
 //   2. the tile's row of segment bounds goes out: row[d] = p0 + the number of
-//      the tile's keys with a high digit below d (row[2^kMaxRadixBits] = p1);
-//      the counts are added to the global counts of the high digit, and every
-//      wave's counter becomes its first position for that digit (digits in
-//      order, waves in order within a digit);
+//      the tile's keys with a high digit below d (row[2^kMaxRadixBits] = p1),
+//      and every wave's counter becomes its first position for that digit
+//      (digits in order, waves in order within a digit);
 //   3. place: each wave walks its positions again and writes every key to
 //      buf.keys[1] / buf.vals[1] at its counter plus its rank among equal
 //      digits in the step, which keeps lookup order within a digit.
-// Two barriers per tile; no workgroup waits for another.  The bucket-local
-// sort gathers a bucket's keys from the tiles' segments [row_i[d], row_i[d+1])
-// in tile order, which is lookup order.
+// Two barriers per tile; no workgroup waits for another, and nothing here
+// needs cleared memory: tile 0 clears the counters and status words of the
+// kernels that follow.  The bucket-local sort gathers a bucket's keys from the
+// tiles' segments [row_i[d], row_i[d+1]) in tile order, which is lookup order.
 template <typename IT, int NT>
 __device__ __forceinline__ void linearize_bucket(const BackwardLaunch& a, int tile) {
   constexpr int NW = NT / kWave;
@@ -205,8 +205,14 @@ __device__ __forceinline__ void linearize_bucket(const BackwardLaunch& a, int ti
   const int lbits = radix_digit_bits(a.key_bits, a.num_indices);
   const int hbits = a.key_bits - lbits;
   const uint32_t hmask = (1u << hbits) - 1u;
-  const int slots = radix_slots(lbits);
   const int64_t k0 = static_cast<int64_t>(tile) * kLinBags;
+  if (tile == 0) {
+    // the counters and look-back status words of the later kernels (this
+    // launch uses none of them, so no separate clearing launch is needed)
+    const int64_t nvec = (static_cast<int64_t>(a.buf.sort_status - a.buf.counters) + 3) / 4;
+    uint4* const z = reinterpret_cast<uint4*>(a.buf.counters);
+    for (int64_t i = tid; i < nvec; i += NT) z[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
   const int nb = static_cast<int>(min(static_cast<int64_t>(kLinBags), a.num_bags - k0));
   if (tid < nb) {
     const int64_t k = k0 + tid;
@@ -295,11 +301,9 @@ __device__ __forceinline__ void linearize_bucket(const BackwardLaunch& a, int ti
     uint32_t all;
     uint32_t st = static_cast<uint32_t>(p0) + block_excl_n<NW>(tsum, scratch, &all);
     uint32_t* const row = a.buf.tile_rows + static_cast<int64_t>(tile) * kTileRowWords;
-    uint32_t* const htot = a.buf.digit_hist + slots;  // the high digit's counts
 #pragma unroll
     for (int q = 0; q < DPT; ++q) {
       row[d0 + q] = st;
-      if (tot[q]) atomicAdd(htot + d0 + q, tot[q]);
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         s_wc[w][d0 + q] = st;

@@ -714,14 +714,17 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
     uint32_t* vout, int64_t n, int lbits, int nbuckets, const uint32_t* __restrict__ htotals,
     const uint32_t* __restrict__ wtable, int ntiles, uint32_t* status, uint32_t* ticket,
     uint32_t* counters, uint32_t* unique_keys, uint32_t* run_start, uint32_t* run_first,
-    int fstride, RunQueue q, uint32_t spin_limit, const uint32_t* __restrict__ rows, int nseg) {
+    int fstride, RunQueue q, uint32_t spin_limit, const uint32_t* __restrict__ rows, int nseg,
+    int bpw, int nbk, uint32_t* estatus) {
   constexpr int NT = kBucketThreads, NW = kBucketWaves, CAP = kBucketCap;
   constexpr int SEGS = SEG ? kTileBucketMaxTiles : 1;
   __shared__ uint32_t s_k[CAP];
   __shared__ uint32_t s_v[CAP];
   __shared__ uint32_t s_seglo[SEGS];
   __shared__ uint32_t s_segoff[SEGS];
-  __shared__ uint32_t s_hrange[2];
+  __shared__ uint32_t s_segend[SEGS];
+  __shared__ uint32_t s_colsum[SEG ? kBucketMaxPerWindow + 1 : 1];
+  __shared__ uint32_t s_start;
   __shared__ uint32_t s_pc[SEG ? NW : 1][64];  // bucket_partition's per-wave counts
   __shared__ uint16_t s_cnt[NW][NT];
   __shared__ uint64_t s_slots[NW][256];
@@ -748,28 +751,53 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
   int64_t start, len64;
   uint32_t hf, hl;
   if constexpr (SEG) {
-    // bucket starts from the high digit's counts; the window takes the buckets
-    // whose start lies in [w0, w0 + kBucketWindow) (empty buckets included:
-    // they hold nothing).  s_bstart[NT] = n; w0 < n always.
-    const uint32_t my_count = tid < nbuckets ? htotals[tid] : 0u;
+    // window `tile`: the high-digit buckets [hf, h1), bpw of them (fewer at
+    // the end).  Every tile's segment bounds at hf .. h1 come in one round
+    // trip: the window's segment table (tile i: [row_i[hf], row_i[h1])) and
+    // column sums, whose differences are the buckets' sizes, so bucket starts
+    // inside the window need no scan.  The window's place in the sorted
+    // order comes from a look-back over the earlier windows' sizes, which
+    // are published at once.
+    hf = static_cast<uint32_t>(tile) * static_cast<uint32_t>(bpw);
+    const uint32_t h1 = min(hf + static_cast<uint32_t>(bpw), static_cast<uint32_t>(nbk));
+    hl = h1 - 1u;
+    const int nbw = static_cast<int>(h1 - hf);
 #pragma unroll
     for (int w = 0; w < NW; ++w) s_cnt[w][tid] = 0;
     for (int i = tid; i < NW * 256; i += NT) (&s_slots[0][0])[i] = 0u;
-    if (tid == 0) s_hrange[0] = s_hrange[1] = NT;
+    if (tid <= nbw) s_colsum[tid] = 0u;
+    __syncthreads();
+    // thread (k, i) reads tile i's bound k; each wave adds its values per
+    // bound (waves span at most two bounds when nseg >= 64) before one LDS
+    // atomic per bound
+    for (int base = 0; base < (nbw + 1) * nseg; base += NT) {
+      const int idx = base + tid;
+      const bool ok = idx < (nbw + 1) * nseg;
+      const int k = ok ? idx / nseg : 0, i = idx - k * nseg;
+      const uint32_t v = ok ? rows[static_cast<int64_t>(i) * kTileRowWords + hf + k] : 0u;
+      if (ok && k == 0) s_seglo[i] = v;
+      if (ok && k == nbw) s_segend[i] = v;
+      const uint64_t peers = match_bits(__ballot(ok), static_cast<uint32_t>(k), 7);
+      uint32_t sum = v;  // sum over the lanes with this k (they are contiguous)
+      const int lane = lane_id();
+      const int first = __builtin_ctzll(peers ? peers : 1ull);
+      const int last = 63 - __builtin_clzll(peers ? peers : 1ull);
+      for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t y = __shfl_down(sum, o, kWave);
+        if (lane + o <= last) sum += y;
+      }
+      if (ok && lane == first) atomicAdd(&s_colsum[k], sum);
+    }
+    __syncthreads();
+    const uint32_t sl = tid < nseg ? s_segend[tid] - s_seglo[tid] : 0u;
     uint32_t tot;
-    s_bstart[tid] = block_excl_n<NW>(my_count, scratch, &tot);
-    if (tid == 0) s_bstart[NT] = tot;
+    const uint32_t off = block_excl_n<NW>(sl, scratch, &tot);
+    if (tid < nseg) s_segoff[tid] = off;
+    if (tid <= nbw) s_bstart[tid] = s_colsum[tid] - s_colsum[0];  // inside the window
+    if (tid == 0) st_status(estatus + tile, (tile == 0 ? kFlagIncl : kFlagAgg) | tot);
     __syncthreads();
-    const uint32_t lo = static_cast<uint32_t>(w0), hi = lo + kBucketWindow;
-    const uint32_t sb = s_bstart[tid], sp = tid > 0 ? s_bstart[tid - 1] : 0u;
-    if (sb >= lo && (tid == 0 || sp < lo)) s_hrange[0] = tid;
-    if (sb >= hi && (tid == 0 || sp < hi)) s_hrange[1] = tid;
-    __syncthreads();
-    hf = s_hrange[0];
-    const uint32_t h1 = s_hrange[1];
-    hl = h1 - 1u;
-    start = s_bstart[hf];
-    len64 = static_cast<int64_t>(s_bstart[h1]) - start;
+    start = 0;  // known after the look-back
+    len64 = tot;
   } else {
     const uint4 rec = *reinterpret_cast<const uint4*>(wtable + 4 * static_cast<int64_t>(tile));
 #pragma unroll
@@ -797,7 +825,6 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
     rr = (len + NT - 1) / NT;
     if (len > 0) {
       if constexpr (SEG) {
-        build_segments(rows, nseg, hf, hl + 1u, s_seglo, s_segoff, scratch);
         gather_range(kin, vin, n, s_seglo, s_segoff, nseg, 0u, len, rr, key, val);
       } else if (start + len <= w0 + CAP) {
         // the range's positions go to LDS in order, then back in the layout
@@ -848,9 +875,8 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
           return min(((k >> lbits) & hmask) - hf, hspan);
         };
         if (few) {
-          // bucket starts inside the range are known (s_bstart)
-          const uint32_t s0 = static_cast<uint32_t>(start);
-          const auto bstart = [hf, s0](int b) { return s_bstart[hf + b] - s0; };
+          // bucket starts inside the window are known (s_bstart)
+          const auto bstart = [](int b) { return s_bstart[b]; };
           bucket_partition(key, val, rr, len, static_cast<int>(hspan) + 1, bucket, bstart, s_k,
                            s_v, s_pc);
         } else {
@@ -858,10 +884,12 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
                             scratch);
         }
       }
-      // the sorted range goes out before the look-back (it does not depend on it)
-      for (int i = tid; i < len; i += NT) {
-        kout[start + i] = s_k[i];
-        vout[start + i] = s_v[i];
+      // the sorted range goes out before the look-back when its place is known
+      if constexpr (!SEG) {
+        for (int i = tid; i < len; i += NT) {
+          kout[start + i] = s_k[i];
+          vout[start + i] = s_v[i];
+        }
       }
       // a range starts a bucket, so its first position is always a run head
       for (int j = 0; j < rr; ++j) {
@@ -877,10 +905,23 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
       s_bstart[tid] = block_excl_n<NW>(my_count, scratch, &tot);
       if (tid == 0) s_bstart[NT] = tot;
       __syncthreads();
+    } else {
+      // the buckets are written as they are sorted: the window's place first
+      if (tid < kWave) {
+        const uint32_t before =
+            tile > 0 ? lookback_wave(estatus, tile, WaitCtl{counters + kCntError, spin_limit}) : 0u;
+        if (tid == 0) {
+          if (tile > 0)
+            st_status(estatus + tile, kFlagIncl | ((before + static_cast<uint32_t>(len64)) & kValueMask));
+          s_start = before;
+        }
+      }
+      __syncthreads();
+      start = s_start;
     }
     for (uint32_t h = hf; h <= hl; ++h) {
-      const uint32_t bs = s_bstart[h];
-      const uint32_t bn = s_bstart[h + 1] - bs;
+      const uint32_t bs = SEG ? static_cast<uint32_t>(start) + s_bstart[h - hf] : s_bstart[h];
+      const uint32_t bn = SEG ? s_bstart[h - hf + 1] - s_bstart[h - hf] : s_bstart[h + 1] - s_bstart[h];
       if (bn == 0) continue;
       if constexpr (SEG) build_segments(rows, nseg, h, h + 1u, s_seglo, s_segoff, scratch);
       s_dbase[tid] = 0u;
@@ -992,7 +1033,17 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
         run_start[U] = static_cast<uint32_t>(n);
       }
     }
-  } else if (tid == kWave && (t_items | t_lc) != 0u) {
+  } else if (SEG && len64 <= CAP && tid < 2 * kWave) {
+    // the window's place in the sorted order, beside the run-id look-back
+    // (the sizes were published at the start, so it rarely waits)
+    const uint32_t before =
+        tile > 0 ? lookback_wave(estatus, tile, WaitCtl{counters + kCntError, spin_limit}) : 0u;
+    if (tid == kWave) {
+      if (tile > 0)
+        st_status(estatus + tile, kFlagIncl | ((before + static_cast<uint32_t>(len64)) & kValueMask));
+      s_start = before;
+    }
+  } else if (tid == 2 * kWave && (t_items | t_lc) != 0u) {
     // the window's queue slots, reserved while wave 0 looks back
     s_qbase[0] = t_items ? atomicAdd(&counters[kCntItems1], t_items) : 0u;
     s_qbase[1] = (t_lc >> 16) ? atomicAdd(&counters[kCntLong], t_lc >> 16) : 0u;
@@ -1000,6 +1051,13 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
   }
   __syncthreads();
   if (len64 <= CAP) {
+    if constexpr (SEG) {
+      start = s_start;
+      for (int i = tid; i < len_l; i += NT) {
+        kout[start + i] = s_k[i];
+        vout[start + i] = s_v[i];
+      }
+    }
     uint32_t lr = hex;
     uint32_t it = s_qbase[0] + x_items;
     uint32_t li = s_qbase[1] + (x_lc >> 16);
@@ -1109,8 +1167,11 @@ hipError_t launch_init_workspace(const BackwardLaunch& a, hipStream_t stream,
 }
 
 hipError_t launch_linearize(const BackwardLaunch& a, hipStream_t stream, const KernelTimer* kt) {
-  const hipError_t e = launch_init_workspace(a, stream, kt);
-  if (e != hipSuccess) return e;
+  // a linearize step that sorts the tiles clears the workspace itself
+  if (!uses_tile_buckets(a)) {
+    const hipError_t e = launch_init_workspace(a, stream, kt);
+    if (e != hipSuccess) return e;
+  }
   return launch_linearize_kernel(a, stream, kt);
 }
 
@@ -1243,15 +1304,19 @@ hipError_t launch_sort_encode(const BackwardLaunch& a, hipStream_t stream, const
     if (e != hipSuccess) return e;
   }
   const int nseg = seg ? static_cast<int>((a.num_bags + kLinBags - 1) / kLinBags) : 0;
+  const int nbk = 1 << (a.key_bits - bits);        // buckets of the high digit
+  const int bpw = seg ? buckets_per_window(n, nbk) : 0;
+  const int nwin = seg ? (nbk + bpw - 1) / bpw : windows;
   launch_timed(kt, "bucket_sort_rle", seg ? bucket_sort_rle<true> : bucket_sort_rle<false>,
-               dim3(windows), dim3(kBucketThreads), 0, stream, a.buf.keys[1], a.buf.vals[1],
-               a.buf.keys[0], a.buf.vals[0], n, bits, 1 << bits, htotals, wtable, windows,
-               wstatus, windows <= kResidentTiles ? nullptr : a.buf.tickets + kMaxRadixPasses,
+               dim3(nwin), dim3(kBucketThreads), 0, stream, a.buf.keys[1], a.buf.vals[1],
+               a.buf.keys[0], a.buf.vals[0], n, bits, 1 << bits, htotals, wtable, nwin,
+               wstatus, nwin <= kResidentTiles ? nullptr : a.buf.tickets + kMaxRadixPasses,
                a.buf.counters, a.buf.unique_keys, a.buf.run_start, a.buf.run_first,
                a.buf.first_stride,
                RunQueue{a.buf.items1, a.buf.longs, a.buf.long_keys, a.short_max,
                         a.long_threshold, a.chunk},
-               a.spin_limit, static_cast<const uint32_t*>(a.buf.tile_rows), nseg);
+               a.spin_limit, static_cast<const uint32_t*>(a.buf.tile_rows), nseg, bpw, nbk,
+               wstatus + kBucketMaxWindows);
   return hipGetLastError();
 }
 

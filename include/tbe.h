@@ -55,6 +55,13 @@
  * preconditions (ids in range, offsets monotone and ending at num_indices) are
  * not checked unless TBE_FLAG_VALIDATE is set; violating them is undefined.
  *
+ * Graph capture: without TBE_FLAG_VALIDATE and TBE_OPTION_PROFILE, the compute
+ * calls only enqueue kernels (no host synchronisation, no allocation, no
+ * memset), so they may be captured into a HIP graph on a capturing stream and
+ * replayed; a replay gives the same results as the calls made eagerly, bit
+ * for bit.  A captured tbe_forward_group and its tbe_backward_update_grouped
+ * belong in the same graph (the pairing is checked on the host at capture).
+ *
  * Threading: a handle may be used by one host thread at a time.  Two
  * backward_update calls in flight on one handle race on the weights; with
  * TBE_FLAG_SPLIT_BAGS, two forward calls in flight on one handle (on

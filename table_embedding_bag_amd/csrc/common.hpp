@@ -321,7 +321,7 @@ struct RunQueue {
 };
 constexpr int kNumTickets = 8;           // kMaxRadixPasses radix passes + the RLE
 
-// Keys per thread of a radix tile for a batch of n lookups (8 or 32).
+// Keys per thread of a radix tile for a batch of n lookups (8, or 16 above 2^20).
 int sort_keys_per_thread(int64_t n);
 // Keys per radix tile for a batch of n lookups sorted on key_bits bits.
 int sort_tile_keys(int64_t n, int key_bits);
@@ -485,5 +485,9 @@ __host__ __device__ inline int radix_digit_bits(int key_bits, int64_t n) {
 __host__ __device__ inline int radix_slots(int digit_bits) {
   return digit_bits > 8 ? 1024 : 256;  // the wide pass has 1024 digit slots
 }
+// Batches of more than 2^20 lookups (8-bit digits) sort with counted passes:
+// each pass counts every tile's digits, scans the counts over the tiles and
+// then places the tiles, with no look-back between tiles.
+__host__ __device__ inline bool counted_passes(int64_t n) { return n > kWideRadixMaxKeys; }
 
 }  // namespace tbe

@@ -76,11 +76,11 @@ __device__ __forceinline__ uint64_t match_bits(uint64_t active, uint32_t d, int 
 // workgroup then walks the tile's lookups NT * K at a time, each thread
 // taking K positions (consecutive threads on consecutive lookups): the bags
 // are found by binary search in LDS and all K row ids are loaded before any
-// is used, so a thread keeps K loads in flight.  Digit counts are kept in LDS
-// across the workgroup's tiles and added to the global counts once at the end
-// (a bounded grid keeps those global atomics, all on the same few hundred
-// words, few).  The global digit counts must be zero before the first
-// workgroup starts.
+// is used, so a thread keeps K loads in flight.  On batches of up to 2^20
+// lookups the radix digits are counted too: the counts are kept in LDS across
+// the workgroup's tiles and added to the global counts once at the end (a
+// bounded grid keeps those global atomics, all on the same few hundred words,
+// few), which must be zero before the first workgroup starts.
 template <typename IT, int NT, int K, int BAGS = kLinBags>
 __device__ __forceinline__ void linearize_tiles(const BackwardLaunch& a, int64_t first,
                                                 int64_t stride) {
@@ -91,7 +91,8 @@ __device__ __forceinline__ void linearize_tiles(const BackwardLaunch& a, int64_t
   __shared__ uint32_t s_hist[kMaxRadixPasses << kMaxRadixBits];
 
   const int tid = threadIdx.x;
-  const int passes = radix_passes(a.key_bits, a.num_indices);
+  // (counted passes take their digit counts themselves)
+  const int passes = counted_passes(a.num_indices) ? 0 : radix_passes(a.key_bits, a.num_indices);
   const int bits = radix_digit_bits(a.key_bits, a.num_indices);
   const int slots = radix_slots(bits);
   const uint32_t dmask = (1u << bits) - 1u;

@@ -241,20 +241,6 @@ __device__ __forceinline__ TableMeta meta_of(const BackwardLaunch& a, const Tabl
   return a.T <= kLdsTables ? s_meta[t] : a.meta[t];
 }
 
-// Exclusive prefix sum over the 64 lanes of a wave (all lanes active); the
-// wave's total goes to *total.
-__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t* total) {
-  const int lane = lane_id();
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
-  *total = __shfl(x, kWave - 1, kWave);
-  return x - v;
-}
-
 // Short runs (at most Gs lookups): one lane group per run, grid-stride over
 // runs.  Most runs have one to three lookups and the kernel is bound by the
 // latency of its dependent loads (run bounds -> lookup -> gradient rows), so

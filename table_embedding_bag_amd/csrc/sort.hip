@@ -10,10 +10,10 @@
 //               words the passes below chain through.
 //   linearize   key_i = roff_t + x_i (one 32-bit id space over all tables),
 //               value_i = bag id k (plain sums) or lookup id i with a side
-//               record {k, p_i * s_k} when lookups carry a coefficient.  It
-//               also counts the digits of every radix pass (these counts do not
-//               depend on the order of the keys), so no pass needs a counting
-//               kernel of its own.
+//               record {k, p_i * s_k} when lookups carry a coefficient.  On
+//               batches of up to 2^20 lookups it also counts the digits of
+//               every radix pass (these counts do not depend on the order of
+//               the keys), so no look-back pass needs a counting kernel.
 //   radix pass  one kernel per digit of a stable LSD radix sort on
 //               ceil(log2(sum E_t)) bits, split evenly into the fewest digits
 //               of at most 10 bits (20-bit ids: two 10-bit passes).  A tile
@@ -24,7 +24,10 @@
 //               tiles before it; the tile is then written bucket by bucket so
 //               global stores are coalesced.  Up to 8-bit digits: 256 threads
 //               per tile; 9-10 bits: 1024 threads, so that every thread still
-//               looks back for one digit.
+//               looks back for one digit.  Batches of more than 2^20 lookups
+//               take counted passes instead: a kernel counts every tile's
+//               digits, a second scans the counts over the tiles, and the pass
+//               places each tile at its scanned offsets without a look-back.
 //   RLE         one kernel: run heads of an 8192-key tile, a look-back over
 //               the head counts of earlier tiles, then unique ids and run
 //               starts.  The number of runs U stays on the device.
@@ -44,6 +47,9 @@ namespace tbe {
 namespace {
 
 constexpr int kResidentTiles = 256;         // grids this small are resident all at once
+// keys per thread of a counted pass: 4096-key tiles, 36 KB of LDS, four
+// workgroups per CU (8192-key tiles fit two per CU: passes 15-40% slower)
+constexpr int kCountedKpt = 16;
 
 template <typename IT>
 __device__ __forceinline__ int64_t ld_index(const void* p, int64_t i) {
@@ -118,7 +124,11 @@ __device__ __forceinline__ uint64_t match_digit(uint64_t* s_slots, uint32_t d, b
 // One LSD pass on the digit (key >> shift) & (2^bits - 1), bits <= RB.  A
 // tile of 256*KPT keys; thread tid owns the DPT = 2^RB / 256 consecutive
 // digits tid*DPT .. tid*DPT + DPT - 1 for counting, look-back and offsets.
-template <int KPT, int RB>
+// COUNTED: the tile's offset inside every digit bucket is read from
+// status[d * ntiles + tile] (the exclusive prefix over earlier tiles that
+// radix_count and radix_scan left there) instead of being found by a
+// look-back, so no tile waits for another.
+template <int KPT, int RB, bool COUNTED = false>
 __global__ __launch_bounds__(kBlock) void radix_pass(
     const uint32_t* __restrict__ kin, const uint32_t* __restrict__ vin, uint32_t* __restrict__ kout,
     uint32_t* __restrict__ vout, int64_t n, int shift, int bits, const uint32_t* __restrict__ totals,
@@ -139,10 +149,15 @@ __global__ __launch_bounds__(kBlock) void radix_pass(
   // and a failed call is reported by the kernels after the sort)
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int d0 = tid * DPT;
-  uint32_t my_total[DPT];  // issued with the key loads below
+  const int ntiles = static_cast<int>((n + TS - 1) / TS);
+  uint32_t my_total[DPT], before[DPT];  // issued with the key loads below
 #pragma unroll
-  for (int q = 0; q < DPT; ++q) my_total[q] = totals[d0 + q];
-  if (tid == 0) s_tile = ticket ? atomicAdd(ticket, 1u) : blockIdx.x;
+  for (int q = 0; q < DPT; ++q) {
+    my_total[q] = totals[d0 + q];
+    before[q] = 0u;
+    if constexpr (COUNTED) before[q] = status[static_cast<int64_t>(d0 + q) * ntiles + blockIdx.x];
+  }
+  if (tid == 0) s_tile = (ticket && !COUNTED) ? atomicAdd(ticket, 1u) : blockIdx.x;
   for (int i = tid; i < kWavesPerBlock * RMAX; i += kBlock) (&s_cnt[0][0])[i] = 0u;
   __syncthreads();
   const int tile = static_cast<int>(s_tile);
@@ -200,12 +215,9 @@ __global__ __launch_bounds__(kBlock) void radix_pass(
 #pragma unroll
   for (int q = 0; q < DPT; ++q) {
     s_dstart[d0 + q] = tbase + loc[q];
-    st_status(my_status + q, (tile == 0 ? kFlagIncl : kFlagAgg) | mine[q]);
+    if constexpr (!COUNTED) st_status(my_status + q, (tile == 0 ? kFlagIncl : kFlagAgg) | mine[q]);
   }
-  uint32_t before[DPT];
-#pragma unroll
-  for (int q = 0; q < DPT; ++q) before[q] = 0u;
-  if (tile > 0) {
+  if (!COUNTED && tile > 0) {
     lookback_digits<DPT, DEPTH>(status, RMAX, tile, d0, wait, before);
 #pragma unroll
     for (int q = 0; q < DPT; ++q)
@@ -218,7 +230,6 @@ __global__ __launch_bounds__(kBlock) void radix_pass(
 #pragma unroll
   for (int q = 0; q < DPT; ++q) s_gbase[d0 + q] = gbase + gloc[q] + before[q];
   if (wtable) {  // every tile knows all bucket starts; digit d is recorded by tile d % tiles
-    const int ntiles = static_cast<int>((n + TS - 1) / TS);
 #pragma unroll
     for (int q = 0; q < DPT; ++q)
       if (my_total[q] > 0 && (d0 + q) % ntiles == tile)
@@ -247,6 +258,81 @@ __global__ __launch_bounds__(kBlock) void radix_pass(
       vout[gp] = s_v[i];
     }
   }
+}
+
+// Counted passes (batches of more than 2^20 lookups, digits of at most 8
+// bits): every tile's digit counts are taken by radix_count, scanned over the
+// tiles by radix_scan, and radix_pass<.., COUNTED> then places each tile at
+// its scanned offsets.  The counts cost one more read of the keys (4 bytes a
+// lookup); in exchange no tile waits for the tiles before it (with 512 tiles
+// resident at once, the look-back's chain of status words took a third of a
+// tile's time).
+//
+// radix_count: tile `tile` (kBlock*KPT keys, the tiles of radix_pass) counts
+// the digits of its keys into cnt[d * ntiles + tile].  Lanes holding the
+// first active lane's digit add their number once (a hot row fills whole
+// rounds with one digit); the others add one each.  Workgroups are renumbered
+// XCD by XCD so that the counts of neighbouring tiles are written from one L2.
+template <int KPT>
+__global__ __launch_bounds__(kBlock) void radix_count(const uint32_t* __restrict__ kin, int64_t n,
+                                                      int shift, int bits,
+                                                      uint32_t* __restrict__ cnt, int ntiles) {
+  __shared__ uint32_t s_c[kBlock];
+  const int tid = threadIdx.x;
+  const int tile = xcd_contiguous_block(blockIdx.x, gridDim.x);
+  s_c[tid] = 0u;
+  const int64_t base = static_cast<int64_t>(tile) * (kBlock * KPT);
+  const uint32_t dmask = (1u << bits) - 1u;
+  uint32_t key[KPT];
+#pragma unroll
+  for (int r = 0; r < KPT; ++r) {
+    const int64_t p = base + r * kBlock + tid;
+    key[r] = p < n ? kin[p] : 0u;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < KPT; ++r) {
+    const bool ok = base + r * kBlock + tid < n;
+    const uint32_t d = (key[r] >> shift) & dmask;
+    const uint64_t act = __ballot(ok);
+    if (act == 0) continue;  // the same on the whole wave
+    const uint32_t dl = static_cast<uint32_t>(
+        __builtin_amdgcn_readlane(static_cast<int>(d), __builtin_ctzll(act)));
+    const bool same = ok && d == dl;
+    const uint64_t m = __ballot(same);
+    if (same && popc_below(m) == 0) atomicAdd(&s_c[dl], static_cast<uint32_t>(__popcll(m)));
+    if (ok && !same) atomicAdd(&s_c[d], 1u);
+  }
+  __syncthreads();
+  cnt[static_cast<int64_t>(tid) * ntiles + tile] = s_c[tid];
+}
+
+// radix_scan: workgroup d turns cnt[d * ntiles + t] into the exclusive prefix
+// over tiles t' < t and writes the digit's total to totals[d].
+__global__ __launch_bounds__(kBlock) void radix_scan(uint32_t* __restrict__ cnt, int ntiles,
+                                                     uint32_t* __restrict__ totals) {
+  __shared__ uint32_t scratch[kWavesPerBlock];
+  uint32_t* col = cnt + static_cast<int64_t>(blockIdx.x) * ntiles;
+  uint32_t carry = 0;
+  for (int t0 = 0; t0 < ntiles; t0 += kBlock * 4) {
+    uint32_t c[4], s = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = t0 + threadIdx.x * 4 + j;
+      c[j] = t < ntiles ? col[t] : 0u;
+      s += c[j];
+    }
+    uint32_t total;
+    uint32_t run = carry + block_exclusive_sum(s, scratch, &total);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = t0 + threadIdx.x * 4 + j;
+      if (t < ntiles) col[t] = run;
+      run += c[j];
+    }
+    carry += total;
+  }
+  if (threadIdx.x == 0) totals[blockIdx.x] = carry;
 }
 
 // A pass on digits wider than 8 bits: 1024 threads, one digit per thread
@@ -1144,7 +1230,7 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_rle(
 // lines (16-key tiles left half lines shared with the next tile, usually on
 // another XCD: the first pass over 16.8 M uniform 16-bit ids took 323 us
 // against 138 us).
-int sort_keys_per_thread(int64_t n) { return n <= (int64_t{1} << 20) ? 8 : 32; }
+int sort_keys_per_thread(int64_t n) { return n <= (int64_t{1} << 20) ? 8 : kCountedKpt; }
 int sort_tile_keys(int64_t n, int key_bits) {
   return radix_digit_bits(key_bits, n) > 8 ? 4096 : kBlock * sort_keys_per_thread(n);
 }
@@ -1154,9 +1240,9 @@ hipError_t launch_init_workspace(const BackwardLaunch& a, hipStream_t stream,
   // the counters, histograms and look-back status words the later kernels chain through
   // the radix passes' status words come last and are not needed when the
   // linearize step sorts each tile by the high digit
-  const int64_t words =
-      uses_tile_buckets(a) ? static_cast<int64_t>(a.buf.sort_status - a.buf.counters)
-                           : a.buf.zero_words;
+  const int64_t words = (uses_tile_buckets(a) || counted_passes(a.num_indices))
+                            ? static_cast<int64_t>(a.buf.sort_status - a.buf.counters)
+                            : a.buf.zero_words;
   const int64_t nvec = (words + 3) / 4;
   int64_t zblocks = (nvec + kBlock - 1) / kBlock;
   if (zblocks > 1024) zblocks = 1024;
@@ -1217,31 +1303,42 @@ hipError_t launch_linearize_kernel(const BackwardLaunch& a, hipStream_t stream,
              : launch_linearize_bags<kLinBags>(a, stream, kt);
 }
 
-// One look-back pass over keys/values (kin, vin) -> (kout, vout) on the digit
-// (key >> shift) & (2^bits - 1), whose counts are `totals`; `pass` selects the
-// pass's status words and ticket.  With wtable, the pass also records the
-// window ranges of the bucket-local sort.
-hipError_t launch_pass(const BackwardLaunch& a, int pass, int shift, const uint32_t* totals,
+// One pass over keys/values (kin, vin) -> (kout, vout) on the digit
+// (key >> shift) & (2^bits - 1).  Batches of up to 2^20 lookups: one look-back
+// kernel on the digit counts `totals` (from the linearize step); `pass`
+// selects the pass's status words and ticket, and with wtable the pass also
+// records the window ranges of the bucket-local sort.  Larger batches: the
+// counted pass (count, scan, place), whose scan writes `totals`.
+hipError_t launch_pass(const BackwardLaunch& a, int pass, int shift, uint32_t* totals,
                        const uint32_t* kin, const uint32_t* vin, uint32_t* kout, uint32_t* vout,
                        uint32_t* wtable, hipStream_t stream, const KernelTimer* kt) {
   const int64_t n = a.num_indices;
-  const int kpt = sort_keys_per_thread(n);
   const int64_t ts = sort_tile_keys(n, a.key_bits);
   const int ntiles = static_cast<int>((n + ts - 1) / ts);
   const int bits = radix_digit_bits(a.key_bits, n);
   const int slots = radix_slots(bits);
   uint32_t* status = a.buf.sort_status + static_cast<int64_t>(pass) * ntiles * slots;
   uint32_t* ticket = ntiles <= kResidentTiles ? nullptr : a.buf.tickets + pass;
+  if (counted_passes(n)) {
+    // counts of this pass's tiles (every pass reuses the first pass's words),
+    // then the digit totals, written by the scan
+    uint32_t* cnt = a.buf.sort_status;
+    const WaitCtl none{a.buf.counters + kCntError, a.spin_limit};
+    launch_timed(kt, "radix_count", radix_count<kCountedKpt>, dim3(ntiles), dim3(kBlock), 0,
+                 stream, kin, n, shift, bits, cnt, ntiles);
+    launch_timed(kt, "radix_scan", radix_scan, dim3(slots), dim3(kBlock), 0, stream, cnt, ntiles,
+                 totals);
+    launch_timed(kt, "radix_pass", radix_pass<kCountedKpt, 8, true>, dim3(ntiles), dim3(kBlock),
+                 0, stream, kin, vin, kout, vout, n, shift, bits, totals, cnt, nullptr, none,
+                 nullptr);
+    return hipGetLastError();
+  }
   if (bits > 8)
     launch_timed(kt, "radix_pass", radix_pass_wide<4, 10>, dim3(ntiles), dim3(1024), 0, stream,
                  kin, vin, kout, vout, n, shift, bits, totals, status, ticket,
                  WaitCtl{a.buf.counters + kCntError, a.spin_limit}, wtable);
-  else if (kpt == 8)
-    launch_timed(kt, "radix_pass", radix_pass<8, 8>, dim3(ntiles), dim3(kBlock), 0, stream, kin,
-                 vin, kout, vout, n, shift, bits, totals, status, ticket,
-                 WaitCtl{a.buf.counters + kCntError, a.spin_limit}, wtable);
   else
-    launch_timed(kt, "radix_pass", radix_pass<32, 8>, dim3(ntiles), dim3(kBlock), 0, stream, kin,
+    launch_timed(kt, "radix_pass", radix_pass<8, 8>, dim3(ntiles), dim3(kBlock), 0, stream, kin,
                  vin, kout, vout, n, shift, bits, totals, status, ticket,
                  WaitCtl{a.buf.counters + kCntError, a.spin_limit}, wtable);
   return hipGetLastError();
@@ -1291,7 +1388,7 @@ hipError_t launch_sort_encode(const BackwardLaunch& a, hipStream_t stream, const
     return launch_run_length_encode(a, a.buf.keys[sorted], a.buf.vals[sorted], stream, kt);
   }
   const int bits = radix_digit_bits(a.key_bits, n);
-  const uint32_t* htotals = a.buf.digit_hist + radix_slots(bits);  // counts of the high digit
+  uint32_t* htotals = a.buf.digit_hist + radix_slots(bits);  // counts of the high digit
   // look-back status words of the windows, then their range records
   const int windows = static_cast<int>(bucket_windows(n));
   uint32_t* wstatus = a.buf.rle_status;

@@ -191,8 +191,8 @@ def _uniform_batch(E, B, n, seed):
                                  ((1 << 20) + 1, 1 << 19)],
                          ids=["20bit-2^20-lookups", "20bit-2^20+1-lookups", "21bit-ids"])
 def test_path_boundaries(E, n):
-    """Both sides of the bucket path's limits: 2^20 lookups (bucket path) and one more (LSD
-    passes and the RLE kernel); ids of 20 bits (two digits) and of 21 bits (three LSD
+    """Both sides of the bucket path's limits: 2^20 lookups (bucket path) and one more (counted
+    LSD passes and the RLE kernel); ids of 20 bits (two digits) and of 21 bits (three LSD
     passes).  Runs bit-exact and sampled updates against the reference."""
     spec = workloads.custom([E], [16], "f32", B=4096, optimizer="rowwise_adagrad", key=250)
     batch = _uniform_batch(E, 4096, n, 51)
@@ -206,5 +206,8 @@ def test_path_boundaries(E, n):
     bucket = E == (1 << 20) and n <= (1 << 20)
     assert ("bucket_sort_rle" in used) == bucket, used
     assert ("rle_kernel" in used) == (not bucket), used
+    # more than 2^20 lookups: counted passes (count, scan, place), no look-back
+    counted = n > (1 << 20)
+    assert ("radix_count" in used) == counted and ("radix_scan" in used) == counted, used
     pb.op.close()
     parity(spec, seed=12, steps=1, batches=[batch], bag_sample=500, row_sample=2000)

@@ -54,7 +54,7 @@ FLUSH_BYTES = 1 << 30        # written between calls to empty L2 and the 256 MB 
 FRONT = ("init_workspace", "linearize_kernel", "radix_count", "radix_scan", "radix_pass",
          "bucket_sort_rle", "rle_kernel")
 SEG = ("queue_runs", "table_run_starts", "seg_fused", "seg_finalize")
-FWD = ("fwd_gather_pool", "fwd_linearize", "fwd_histogram", "hist_transpose",
+FWD = ("fwd_gather_pool", "fwd_lds_pool", "fwd_linearize", "fwd_histogram", "hist_transpose",
        "fwd_split_segments", "fwd_split_combine")
 COUNT_BWD = ("cb_product", "cb_update", "cb_runs")
 
@@ -217,7 +217,10 @@ def algorithmic_bytes(spec, batch, gather_tables=None, long_threshold=256, chunk
                                         + s16 * spec.rows[t] * spec.dims[t] for t in hist))
     hist_flops = float(sum(2 * spec.B * spec.rows[t] * spec.dims[t] for t in hist))
     hist_t = float(sum(2 * s16 * spec.rows[t] * spec.dims[t] for t in hist))
-    return {"fwd_gather_pool": fwd, "fwd_linearize": fwd + front["linearize_kernel"],
+    # the LDS-pooled small tables: the same work per lookup (rows read from LDS), so the
+    # same algorithmic bytes as the gather of all tables (a call takes one or the other)
+    return {"fwd_gather_pool": fwd, "fwd_lds_pool": fwd,
+            "fwd_linearize": fwd + front["linearize_kernel"],
             "fwd_histogram": hist_bytes, "hist_transpose": hist_t,
             "fwd_histogram_flops": hist_flops, "seg_short": seg_short, "seg_wg": seg_wg,
             "seg_fused": seg_short + seg_wg,
@@ -228,7 +231,8 @@ def algorithmic_bytes(spec, batch, gather_tables=None, long_threshold=256, chunk
 
 # source file of every kernel (the launch shapes are set next to the kernels)
 KERNEL_FILE = {
-    "fwd_gather_pool": "forward.hip", "fwd_linearize": "forward.hip", "psw_grad": "forward.hip",
+    "fwd_gather_pool": "forward.hip", "fwd_lds_pool": "forward.hip",
+    "fwd_linearize": "forward.hip", "psw_grad": "forward.hip",
     "fwd_split_segments": "forward.hip", "fwd_split_combine": "forward.hip",
     "fwd_histogram": "histogram.hip", "hist_transpose": "histogram.hip",
     "cb_product": "count_backward.hip", "cb_update": "count_backward.hip",

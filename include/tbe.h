@@ -189,7 +189,19 @@ typedef enum {
    * weight and no state, reports num_unique = -1 in its runs, and marks the
    * handle (tbe_check_device_status).  0 makes every such wait give up at
    * once, which only serves to test that path. */
-  TBE_OPTION_SPIN_LIMIT = 4
+  TBE_OPTION_SPIN_LIMIT = 4,
+  /* The pooled lookup of small tables ("What Happened": the same gather and
+   * pooling, with the rows read from the CU's local memory).
+   * 1 (default): when some tables qualify (fp16/bf16 storage, rows of 3 to 8
+   *    16-byte chunks, at most 128 KB with rows padded to 4 or 8 chunks) and a
+   *    call without TBE_FLAG_SPLIT_BAGS has at least 16 x the largest such E_t
+   *    lookups per table and short enough bags (a mean of at most 16 lookups;
+   *    8 with per-sample weights and rows of 5 to 8 chunks), every workgroup
+   *    of those tables stages its table in LDS once and pools its bags from
+   *    there; the other tables take the gather kernel.
+   * 0: every table takes the gather kernel.
+   * Both give the same bits.  Other values: TBE_ERR_INVALID_ARGUMENT. */
+  TBE_OPTION_LDS_FORWARD = 5
 } tbe_option;
 
 /* Create a handle.  Validates the configuration (host only; nothing is

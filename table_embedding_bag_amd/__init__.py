@@ -26,6 +26,7 @@ __all__ = [
     "FLAG_VALIDATE", "FLAG_NO_HISTOGRAM", "FLAG_FORCE_HISTOGRAM", "FLAG_HISTOGRAM",
     "FLAG_SPLIT_BAGS", "FLAG_COUNT_BACKWARD",
     "OPTION_LONG_RUN_THRESHOLD", "OPTION_PROFILE", "OPTION_SORT", "OPTION_SPIN_LIMIT",
+    "OPTION_LDS_FORWARD",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -37,6 +38,7 @@ FLAG_VALIDATE, FLAG_NO_HISTOGRAM, FLAG_FORCE_HISTOGRAM, FLAG_HISTOGRAM = 1, 2, 4
 FLAG_SPLIT_BAGS = 16
 FLAG_COUNT_BACKWARD = 32
 OPTION_LONG_RUN_THRESHOLD, OPTION_PROFILE, OPTION_SORT, OPTION_SPIN_LIMIT = 1, 2, 3, 4
+OPTION_LDS_FORWARD = 5
 STATIC_SCRATCH_BYTES = 64 << 20   # TBE_STATIC_SCRATCH_BYTES
 
 STATUS = {

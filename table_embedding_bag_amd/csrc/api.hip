@@ -74,6 +74,16 @@ struct tbe_handle {
   std::vector<CountUnit> cb_host;
   CountUnit* cb_units = nullptr;
   int64_t cb_groups = 0;
+  // small tables pooled from LDS (TBE_OPTION_LDS_FORWARD): those tables
+  // (device list, all with rows of 2^lds_gshift chunks), the other tables
+  // (device list for the gather kernel), the largest such table's rows
+  std::vector<int32_t> lds_host, lds_rest_host;
+  int32_t* lds_list = nullptr;
+  int32_t* lds_rest = nullptr;
+  int32_t lds_gshift = 0;
+  int64_t lds_max_rows = 0;
+  bool lds_forward = true;
+  int32_t num_cus = 256;
   int64_t weight_elems = 0;  // sum of rows * dims
   int64_t long_threshold = 256;
   bool bucket_sort = true;  // TBE_OPTION_SORT
@@ -684,6 +694,32 @@ tbe_status tbe_create(const tbe_config* cfg, void* weights, float* optim_state, 
     }
     h->wt_elems = wt_off;
     h->weight_elems = woff;
+    // LDS-pooled small tables (not with the count-matrix forward): those of
+    // the most common row width among the qualifying ones
+    if (!use_hist && h->fwd_vec && h->dtype != TBE_F32) {
+      auto fits = [&](int t) {
+        const TableMeta& m = h->meta_host[t];
+        return m.fwd_gshift >= kLdsFwdMinGshift && m.fwd_gshift <= kLdsFwdMaxGshift &&
+               (h->rows[t] << m.fwd_gshift) * 16 <= kLdsFwdBytes;
+      };
+      int count[kLdsFwdMaxGshift + 1] = {};
+      for (int t = 0; t < h->T; ++t)
+        if (fits(t)) ++count[h->meta_host[t].fwd_gshift];
+      int best = kLdsFwdMaxGshift;
+      for (int g = kLdsFwdMaxGshift; g >= kLdsFwdMinGshift; --g)
+        if (count[g] > count[best]) best = g;
+      if (count[best] > 0) {
+        h->lds_gshift = best;
+        for (int t = 0; t < h->T; ++t) {
+          if (fits(t) && h->meta_host[t].fwd_gshift == best) {
+            h->lds_host.push_back(t);
+            h->lds_max_rows = std::max(h->lds_max_rows, h->rows[t]);
+          } else {
+            h->lds_rest_host.push_back(t);
+          }
+        }
+      }
+    }
     // count-matrix backward: every table at most kCbMaxRows rows, dims in
     // 16-column MFMA tiles up to kCbMaxDim
     if (h->flags & TBE_FLAG_COUNT_BACKWARD) {
@@ -722,7 +758,11 @@ tbe_status tbe_create(const tbe_config* cfg, void* weights, float* optim_state, 
   const size_t gather_bytes = sizeof(int32_t) * h->gather_host.size();
   const size_t cb_off = gather_off + up(gather_bytes);
   const size_t cb_bytes = sizeof(CountUnit) * h->cb_host.size();
-  const size_t block_bytes = cb_off + up(cb_bytes);
+  const size_t lds_off = cb_off + up(cb_bytes);
+  const size_t lds_bytes = sizeof(int32_t) * h->lds_host.size();
+  const size_t rest_off = lds_off + up(lds_bytes);
+  const size_t rest_bytes = sizeof(int32_t) * h->lds_rest_host.size();
+  const size_t block_bytes = rest_off + up(rest_bytes);
   void* block = nullptr;
   if (hipMalloc(&block, block_bytes) != hipSuccess) {
     delete h;
@@ -735,6 +775,8 @@ tbe_status tbe_create(const tbe_config* cfg, void* weights, float* optim_state, 
   h->hist = hist_bytes ? reinterpret_cast<HistTable*>(base + hist_off) : nullptr;
   h->gather_list = gather_bytes ? reinterpret_cast<int32_t*>(base + gather_off) : nullptr;
   h->cb_units = cb_bytes ? reinterpret_cast<CountUnit*>(base + cb_off) : nullptr;
+  h->lds_list = lds_bytes ? reinterpret_cast<int32_t*>(base + lds_off) : nullptr;
+  h->lds_rest = rest_bytes ? reinterpret_cast<int32_t*>(base + rest_off) : nullptr;
   bool ok = hipMemset(block, 0, block_bytes) == hipSuccess;
   if (ok)
     ok = hipMemcpy(h->meta, h->meta_host.data(), meta_bytes, hipMemcpyHostToDevice) == hipSuccess;
@@ -745,6 +787,18 @@ tbe_status tbe_create(const tbe_config* cfg, void* weights, float* optim_state, 
          hipSuccess;
   if (ok && cb_bytes)
     ok = hipMemcpy(h->cb_units, h->cb_host.data(), cb_bytes, hipMemcpyHostToDevice) == hipSuccess;
+  if (ok && lds_bytes)
+    ok = hipMemcpy(h->lds_list, h->lds_host.data(), lds_bytes, hipMemcpyHostToDevice) == hipSuccess;
+  if (ok && rest_bytes)
+    ok = hipMemcpy(h->lds_rest, h->lds_rest_host.data(), rest_bytes, hipMemcpyHostToDevice) ==
+         hipSuccess;
+  if (ok) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device) ==
+            hipSuccess &&
+        cus > 0)
+      h->num_cus = cus;
+  }
   if (!ok) {
     (void)hipFree(block);
     delete h;
@@ -799,6 +853,10 @@ tbe_status tbe_set_option(tbe_handle* h, int32_t option, int64_t value) {
     case TBE_OPTION_SPIN_LIMIT:
       if (value < 0 || value > 0x7FFFFFFF) return TBE_ERR_INVALID_ARGUMENT;
       h->spin_limit = static_cast<uint32_t>(value);
+      return TBE_OK;
+    case TBE_OPTION_LDS_FORWARD:
+      if (value != 0 && value != 1) return TBE_ERR_INVALID_ARGUMENT;
+      h->lds_forward = value == 1;
       return TBE_OK;
   }
   return TBE_ERR_INVALID_ARGUMENT;
@@ -909,6 +967,25 @@ tbe_status forward_impl(tbe_handle* h, int32_t B, const void* indices, const voi
     // bags split only when every possible segment fits the scratch (at most
     // n / kSplitLen segments after the first ones)
     const bool split = h->split && n > kSplitLen && n / kSplitLen + 1 <= h->split_cap;
+    // small tables from LDS when each workgroup's staging is small next to
+    // its lookups and the bag's partial sums fit the LDS kernel
+    if (!hist && !fuse && !split && h->lds_forward && !h->lds_host.empty() &&
+        n / h->T >= 16 * h->lds_max_rows &&
+        (1 << std::min(6 - h->lds_gshift, lshift)) <= lds_forward_max_r(h->lds_gshift, psw)) {
+      ForwardLaunch l = a;
+      l.table_list = h->lds_list;
+      l.T = static_cast<int32_t>(h->lds_host.size());
+      const int64_t nblk = (static_cast<int64_t>(B) + kWave - 1) / kWave;
+      const int64_t wgs =
+          std::max<int64_t>(1, std::min<int64_t>(nblk, (h->num_cus + l.T - 1) / l.T));
+      hipError_t e = launch_forward_lds(l, h->lds_gshift, static_cast<int>(wgs), s, kt);
+      if (e == hipSuccess && !h->lds_rest_host.empty()) {
+        a.table_list = h->lds_rest;
+        a.T = static_cast<int32_t>(h->lds_rest_host.size());
+        e = launch_forward_gather(a, s, kt);
+      }
+      return from_hip(e);
+    }
     if (split) {
       a.split_len = kSplitLen;
       a.split_ctr = reinterpret_cast<uint32_t*>(h->split);

@@ -2,6 +2,8 @@
 // TBE library.  Everything here is internal; the public interface is tbe.h.
 #pragma once
 
+#include <algorithm>
+
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -147,6 +149,23 @@ __device__ __forceinline__ void load_widen(const void* base, int64_t e, float* o
   }
 }
 
+// Widen one 16-byte chunk of stored elements (4 fp32 or 8 fp16/bf16) to fp32,
+// as load_widen does with VE * bytes = 16.
+template <int ST>
+__device__ __forceinline__ void widen_chunk(const uint4& v, float* out) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  if constexpr (ST == kF32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(w[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = (ST == kBF16) ? bf16_lo(w[i]) : f16_lo(w[i]);
+      out[2 * i + 1] = (ST == kBF16) ? bf16_hi(w[i]) : f16_hi(w[i]);
+    }
+  }
+}
+
 // Narrow VE fp32 values to the storage dtype and store them at element e.
 template <int ST, int VE>
 __device__ __forceinline__ void narrow_store(void* base, int64_t e, const float* v) {
@@ -224,6 +243,22 @@ hipError_t launch_forward_split(const ForwardLaunch& a, int64_t num_indices, hip
                                 const KernelTimer* kt);
 hipError_t launch_forward_gather(const ForwardLaunch& a, hipStream_t stream,
                                  const KernelTimer* kt);
+// Small tables pooled from LDS (a.table_list: the tables, a.T of them), the
+// same bits as launch_forward_gather with the same lshift.  Every listed table
+// has rows * 2^gshift 16-byte chunk slots (rows padded to 2^gshift chunks) of
+// at most kLdsFwdBytes, rows of at most 2^gshift 16-byte chunks with
+// gshift in [kLdsFwdMinGshift, kLdsFwdMaxGshift], and R = 2^min(6 - gshift,
+// lshift) <= lds_forward_max_r(gshift, per-sample weights); no split bags.
+constexpr int kLdsFwdThreads = 1024;
+constexpr int kLdsFwdBytes = 128 * 1024;
+constexpr int kLdsFwdMinGshift = 2;
+constexpr int kLdsFwdMaxGshift = 3;
+constexpr int kLdsFwdMaxR = 4;  // partial sums per bag (more would spill registers)
+inline int lds_forward_max_r(int gshift, bool psw) {
+  return std::min(1 << gshift, (psw && gshift == 3) ? 2 : kLdsFwdMaxR);
+}
+hipError_t launch_forward_lds(const ForwardLaunch& a, int gshift, int wgs_per_table,
+                              hipStream_t stream, const KernelTimer* kt);
 // dL/dp_i for every lookup (a.table_list must be null: all tables).
 hipError_t launch_psw_grad(const ForwardLaunch& a, const float* grad, float* gpsw,
                            hipStream_t stream, const KernelTimer* kt);

@@ -163,6 +163,191 @@ __global__ __launch_bounds__(kBlock) void fwd_gather_pool(ForwardLaunch a) {
   fwd_tile<ST, IT, VEC, PSW>(a, xcd_contiguous_block(blockIdx.x, gridDim.x), threadIdx.x >> 6);
 }
 
+// Pooled lookup of small tables from LDS.  A workgroup stages one table in
+// LDS once (row r at chunk slots r*GS .. r*GS + C - 1, then a row of zeros)
+// and its waves pool blocks of 64 consecutive bags of that table: a block's
+// offsets are one load per lane, then every bag's first GS ids are loaded (one
+// per lane), and the rows are read from LDS.  A wave's blocks are pipelined:
+// the next block's ids and the offsets of the block after it are loaded before
+// a block is pooled.  Within a block, steps of NB = 64 / GS bags give each bag
+// one lane group of GS lanes (lane gl holds chunk gl of a row).  A round reads
+// the rows of GS lookups at once, those past the bag's end from the zero row;
+// adding those zeros changes no sum, as in the gather kernel.  A bag keeps the
+// gather kernel's R partial sums (rows j = g mod R, in lookup order) and folds
+// them in the same tree, so both kernels give the same bits.  Requires
+// R <= min(GS, kLdsFwdMaxR) and rows of at most GS chunks; no split bags.
+template <int ST, typename IT, bool PSW, int GSH, int R>
+__global__ __launch_bounds__(kLdsFwdThreads) void fwd_lds_pool(ForwardLaunch a,
+                                                               int wgs_per_table) {
+  constexpr int SB = StorageTraits<ST>::bytes;
+  constexpr int VE = 16 / SB;
+  constexpr int GS = 1 << GSH;
+  constexpr int NB = kWave / GS;
+  constexpr int NW = kLdsFwdThreads / kWave;
+  constexpr int kStage = 8;  // staging loads in flight per thread
+  // lookups whose rows are read at once (half a round with weights and rows of
+  // 8 chunks, which would otherwise spill registers)
+  constexpr int PART = (PSW && GSH == 3) ? GS / 2 : GS;
+  static_assert(PART % R == 0, "partial sums stay aligned to the reads");
+  static_assert(R <= GS && R <= kLdsFwdMaxR, "a bag's partial sums fit a round of GS lookups");
+  __shared__ uint4 s_tab[kLdsFwdBytes / 16 + (1 << kLdsFwdMaxGshift)];
+
+  const int wg = xcd_contiguous_block(blockIdx.x, gridDim.x);
+  const int listed = wg / wgs_per_table, part = wg - listed * wgs_per_table;
+  const int t = a.table_list ? a.table_list[listed] : listed;
+  const TableMeta m = a.meta[t];
+  const int C = m.dim / VE;  // chunks per row (at most GS, host-checked)
+  const int zrow = m.rows;   // the row of zeros
+  {
+    const uint4* src =
+        reinterpret_cast<const uint4*>(static_cast<const char*>(a.weights) + m.woff * SB);
+    const int nslot = (m.rows + 1) << GSH;
+    for (int i0 = 0; i0 < nslot; i0 += kLdsFwdThreads * kStage) {
+      uint4 v[kStage];
+#pragma unroll
+      for (int q = 0; q < kStage; ++q) {
+        const int i = i0 + q * kLdsFwdThreads + static_cast<int>(threadIdx.x);
+        const int r = i >> GSH, c = i & (GS - 1);
+        v[q] = make_uint4(0u, 0u, 0u, 0u);
+        if (r < m.rows && c < C) v[q] = src[r * C + c];
+      }
+#pragma unroll
+      for (int q = 0; q < kStage; ++q) {
+        const int i = i0 + q * kLdsFwdThreads + static_cast<int>(threadIdx.x);
+        if (i < nslot) s_tab[i] = v[q];
+      }
+    }
+  }
+  __syncthreads();
+
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int g = lane >> GSH, gl = lane & (GS - 1);
+  const int nblk = (a.B + kWave - 1) / kWave;
+  const int64_t k0 = static_cast<int64_t>(t) * a.B;
+  const int bstride = wgs_per_table * NW;
+  // software pipeline over the wave's blocks: while one block is pooled, the
+  // next block's first ids and the offsets of the block after it are in flight
+  // Loads and stores below take no branch that depends on the lane: absent
+  // bags past B repeat bag B - 1 and lanes past a row's chunks repeat chunk 0,
+  // storing the same values to the same places, and ids past a bag's end read
+  // an id of the batch and take the zero row instead.  (With lane-dependent
+  // branches the compiler made every block wait for all of its stores.)
+  const int cg = gl < C ? gl : 0;
+  auto load_offsets = [&](int blk, int64_t& lo, int64_t& hi) {
+    const int b = min(min(blk, nblk - 1) * kWave + lane, a.B - 1);
+    lo = ld_index<IT>(a.offsets, k0 + b);
+    hi = ld_index<IT>(a.offsets, k0 + b + 1);
+  };
+  // ids r0 + gl of the bag [st, st + len) (the zero row past its end)
+  auto load_id = [&](int64_t st, int len, int r0, int& x, float& pw) {
+    const bool in = r0 + gl < len;
+    const int64_t p = in ? st + r0 + gl : (len > 0 ? st : 0);  // (n > 0 here)
+    const int v = static_cast<int>(ld_index<IT>(a.indices, p));
+    x = in ? v : zrow;
+    pw = 1.0f;
+    if constexpr (PSW) {
+      const float q = a.psw[p];
+      pw = in ? q : 1.0f;
+    }
+  };
+  auto load_ids = [&](int64_t lo, int64_t hi, int (&x)[GS], float (&pw)[GS]) {
+#pragma unroll
+    for (int s = 0; s < GS; ++s) {
+      const int64_t st = __shfl(lo, s * NB + g, kWave);
+      const int len = static_cast<int>(__shfl(hi, s * NB + g, kWave) - st);
+      load_id(st, len, 0, x[s], pw[s]);
+    }
+  };
+  int blk = part * NW + wave;
+  int64_t lo, hi, lo_n, hi_n;
+  int x[GS], x_n[GS];
+  float pw[GS], pw_n[GS];
+  load_offsets(blk, lo, hi);
+  load_ids(lo, hi, x, pw);
+  load_offsets(blk + bstride, lo_n, hi_n);
+  for (; blk < nblk; blk += bstride) {
+    const int b0 = blk * kWave;
+    load_ids(lo_n, hi_n, x_n, pw_n);
+    int64_t lo_nn, hi_nn;
+    load_offsets(blk + 2 * bstride, lo_nn, hi_nn);
+#pragma unroll
+    for (int s = 0; s < GS; ++s) {
+      const int b = min(b0 + s * NB + g, a.B - 1);
+      // (the bag's start and length again: cheaper than keeping them in registers)
+      const int64_t st = __shfl(lo, s * NB + g, kWave);
+      const int len = static_cast<int>(__shfl(hi, s * NB + g, kWave) - st);
+      float acc[R][VE];
+#pragma unroll
+      for (int u = 0; u < R; ++u)
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc[u][e] = 0.0f;
+      // one round: the rows of ids r0 .. r0 + GS - 1 of every bag of the step,
+      // read PART lookups at a time (all GS unless the weights' registers are
+      // needed too)
+      auto round = [&](int xr, float pr) {
+#pragma unroll
+        for (int h0 = 0; h0 < GS; h0 += PART) {
+          uint4 w[PART];
+          float p[PART];
+#pragma unroll
+          for (int j = 0; j < PART; ++j) {
+            const int row = __shfl(xr, (g << GSH) + h0 + j, kWave);
+            p[j] = PSW ? __shfl(pr, (g << GSH) + h0 + j, kWave) : 1.0f;
+            w[j] = s_tab[(row << GSH) + cg];
+          }
+#pragma unroll
+          for (int j0 = 0; j0 < PART; j0 += R) {
+#pragma unroll
+            for (int u = 0; u < R; ++u) {
+              float v[VE];
+              widen_chunk<ST>(w[j0 + u], v);
+#pragma unroll
+              for (int e = 0; e < VE; ++e) {
+                if constexpr (PSW)
+                  acc[u][e] = fmaf(p[j0 + u], v[e], acc[u][e]);
+                else
+                  acc[u][e] += v[e];
+              }
+            }
+          }
+        }
+      };
+      round(x[s], pw[s]);
+      // ids past the first GS of the longer bags: loaded when needed (kept
+      // out of the first round, whose ids were loaded a block ahead)
+      if (__any(GS < len)) {
+        for (int r0 = GS;; r0 += GS) {
+          int xr;
+          float pr;
+          load_id(st, len, r0, xr, pr);
+          round(xr, pr);
+          if (!__any(r0 + GS < len)) break;
+        }
+      }
+      // fold the R partial sums as the gather kernel's lane groups do
+#pragma unroll
+      for (int h = R >> 1; h >= 1; h >>= 1)
+#pragma unroll
+        for (int u = 0; u < h; ++u)
+#pragma unroll
+          for (int e = 0; e < VE; ++e) acc[u][e] += acc[u + h][e];
+      float scale = 1.0f;
+      if (a.mean) scale = len > 0 ? 1.0f / static_cast<float>(len) : 0.0f;
+      float* dst = a.out + static_cast<int64_t>(b) * a.sum_dims + m.doff + cg * VE;
+#pragma unroll
+      for (int e = 0; e < VE; e += 4)
+        *reinterpret_cast<float4*>(dst + e) = make_float4(acc[0][e] * scale, acc[0][e + 1] * scale,
+                                                          acc[0][e + 2] * scale, acc[0][e + 3] * scale);
+    }
+    lo = lo_n;
+    hi = hi_n;
+    lo_n = lo_nn;
+    hi_n = hi_nn;
+#pragma unroll
+    for (int s = 0; s < GS; ++s) x[s] = x_n[s], pw[s] = pw_n[s];
+  }
+}
+
 // Segments of split bags (skew balancing: kimbodo.com/?p=28372, "Kimbodo
 // Engineering Perspective", names load imbalance across lookups as a risk):
 // one wave per queued segment pools its up to split_len lookups with lane
@@ -558,12 +743,63 @@ void launch_split_segments(const ForwardLaunch& a, hipStream_t s, dim3 grid,
   }
 }
 
+template <int ST, typename IT, bool PSW, int GSH>
+hipError_t launch_lds_r(const ForwardLaunch& a, int R, dim3 grid, int wgs, hipStream_t s,
+                        const KernelTimer* kt) {
+  const dim3 block(kLdsFwdThreads);
+  switch (R) {
+    case 1: launch_timed(kt, "fwd_lds_pool", fwd_lds_pool<ST, IT, PSW, GSH, 1>, grid, block, 0, s, a, wgs); break;
+    case 2: launch_timed(kt, "fwd_lds_pool", fwd_lds_pool<ST, IT, PSW, GSH, 2>, grid, block, 0, s, a, wgs); break;
+    case 4:
+      if constexpr (!(PSW && GSH == 3)) {  // (that one would spill registers)
+        launch_timed(kt, "fwd_lds_pool", fwd_lds_pool<ST, IT, PSW, GSH, 4>, grid, block, 0, s, a, wgs);
+        break;
+      }
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;  // (8 partial sums would spill registers)
+  }
+  return hipGetLastError();
+}
+
+template <int ST, typename IT, bool PSW>
+hipError_t launch_lds_g(const ForwardLaunch& a, int gshift, int R, dim3 grid, int wgs,
+                        hipStream_t s, const KernelTimer* kt) {
+  static_assert(kLdsFwdMinGshift == 2 && kLdsFwdMaxGshift == 3, "instantiated gshifts");
+  if (gshift == 2) return launch_lds_r<ST, IT, PSW, 2>(a, R, grid, wgs, s, kt);
+  if (gshift == 3) return launch_lds_r<ST, IT, PSW, 3>(a, R, grid, wgs, s, kt);
+  return hipErrorInvalidValue;
+}
+
+template <int ST>
+hipError_t launch_lds_st(const ForwardLaunch& a, int gshift, int R, dim3 grid, int wgs,
+                         hipStream_t s, const KernelTimer* kt) {
+  if (a.index64)
+    return a.psw ? launch_lds_g<ST, int64_t, true>(a, gshift, R, grid, wgs, s, kt)
+                 : launch_lds_g<ST, int64_t, false>(a, gshift, R, grid, wgs, s, kt);
+  return a.psw ? launch_lds_g<ST, int32_t, true>(a, gshift, R, grid, wgs, s, kt)
+               : launch_lds_g<ST, int32_t, false>(a, gshift, R, grid, wgs, s, kt);
+}
+
 template <int ST>
 void launch_split_index(const ForwardLaunch& a, hipStream_t s, dim3 grid, const KernelTimer* kt) {
   if (a.index64)
     launch_split_segments<ST, int64_t>(a, s, grid, kt);
   else
     launch_split_segments<ST, int32_t>(a, s, grid, kt);
+}
+
+hipError_t launch_forward_lds(const ForwardLaunch& a, int gshift, int wgs_per_table,
+                              hipStream_t stream, const KernelTimer* kt) {
+  const int64_t blocks = static_cast<int64_t>(a.T) * wgs_per_table;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7FFFFFFF || a.split_len > 0) return hipErrorInvalidConfiguration;
+  const int R = 1 << std::min(6 - gshift, static_cast<int>(a.lshift));
+  const dim3 grid(static_cast<unsigned>(blocks));
+  switch (a.dtype) {
+    case kF16: return launch_lds_st<kF16>(a, gshift, R, grid, wgs_per_table, stream, kt);
+    case kBF16: return launch_lds_st<kBF16>(a, gshift, R, grid, wgs_per_table, stream, kt);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_forward_split(const ForwardLaunch& a, int64_t num_indices, hipStream_t stream,

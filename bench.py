@@ -52,7 +52,7 @@ MFMA16_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16 matrix-core peak of the MI355X
 METRIC = "TBE fwd+bwd lookups/sec and achieved HBM GB/s (% of peak) at 1 MI355X"
 FLUSH_BYTES = 1 << 30        # written between calls to empty L2 and the 256 MB MALL
 FRONT = ("init_workspace", "linearize_kernel", "radix_count", "radix_scan", "radix_pass",
-         "bucket_sort_rle", "rle_kernel")
+         "bucket_sort_rle", "rle_count", "rle_kernel")
 SEG = ("queue_runs", "table_run_starts", "seg_fused", "seg_finalize")
 FWD = ("fwd_gather_pool", "fwd_lds_pool", "fwd_linearize", "fwd_histogram", "hist_transpose",
        "fwd_split_segments", "fwd_split_combine")
@@ -203,7 +203,7 @@ def algorithmic_bytes(spec, batch, gather_tables=None, long_threshold=256, chunk
     seg_final = float((nch[long_] * 4 * D[long_] + per_row[long_]).sum())
     N, U, nbags = int(lens.sum()), int(cnt.size), spec.T * spec.B
     front = {"linearize_kernel": float(N * (8 + 8 + rec) + 8 * nbags),
-             "radix_pass": float(16 * N), "radix_count": float(4 * N),
+             "radix_pass": float(16 * N), "radix_count": float(4 * N), "rle_count": float(4 * N),
              "rle_kernel": float(4 * N + 16 * U),
              "bucket_sort_rle": float(16 * N + 12 * U),
              "queue_runs": float(8 * U)}
@@ -238,7 +238,7 @@ KERNEL_FILE = {
     "cb_product": "count_backward.hip", "cb_update": "count_backward.hip",
     "cb_runs": "count_backward.hip",
     "init_workspace": "sort.hip", "linearize_kernel": "sort.hip", "radix_pass": "sort.hip",
-    "radix_count": "sort.hip", "radix_scan": "sort.hip",
+    "radix_count": "sort.hip", "radix_scan": "sort.hip", "rle_count": "sort.hip",
     "radix_pass_wide": "sort.hip", "bucket_sort_rle": "sort.hip", "rle_kernel": "sort.hip",
     "queue_runs": "segment.hip", "table_run_starts": "segment.hip", "seg_fused": "segment.hip",
     "seg_finalize": "segment.hip",

@@ -476,9 +476,46 @@ __device__ uint32_t lookback_wave(uint32_t* status, int tile, WaitCtl wait) {
   }
 }
 
+// Counted run-length encoding (batches of more than 2^20 lookups): the run
+// heads of every 8192-key tile are counted first (rle_count), the counts are
+// scanned over the tiles (radix_scan on one column), and rle_kernel<true>
+// then writes each tile's runs at its scanned run id, with no look-back.
+//
+// rle_count: heads of tile blockIdx.x (p == 0 or keys[p] != keys[p - 1]);
+// each thread owns 8 consecutive positions.
+__global__ __launch_bounds__(1024) void rle_count(const uint32_t* __restrict__ keys, int64_t n,
+                                                  uint32_t* __restrict__ cnt) {
+  constexpr int NT = 1024;
+  constexpr int PER = kRleTile / NT;
+  __shared__ uint32_t scratch[NT / kWave];
+  const int tid = threadIdx.x;
+  const int64_t p0 = static_cast<int64_t>(blockIdx.x) * kRleTile + tid * PER;
+  uint32_t k[PER + 1];
+  k[0] = (p0 > 0 && p0 - 1 < n) ? keys[p0 - 1] : 0u;
+  if (p0 + PER <= n) {
+    const uint4 a = *reinterpret_cast<const uint4*>(keys + p0);
+    const uint4 b = *reinterpret_cast<const uint4*>(keys + p0 + 4);
+    k[1] = a.x, k[2] = a.y, k[3] = a.z, k[4] = a.w, k[5] = b.x, k[6] = b.y, k[7] = b.z, k[8] = b.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) k[j + 1] = p0 + j < n ? keys[p0 + j] : 0u;
+  }
+  uint32_t c = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int64_t p = p0 + j;
+    if (p < n && (p == 0 || k[j + 1] != k[j])) ++c;
+  }
+  uint32_t total;
+  (void)block_excl_n<NT / kWave>(c, scratch, &total);
+  if (tid == 0) cnt[blockIdx.x] = total;
+}
+
 // Run heads of an 8192-key tile (staged in LDS with the key before it), 1024
 // threads per tile; each thread owns 8 consecutive positions so run ids
-// follow position order.
+// follow position order.  The tile's first run id comes from a look-back over
+// the earlier tiles' head counts, or (COUNTED) from cnt[tile], their scan.
+template <bool COUNTED>
 __global__ __launch_bounds__(1024) void rle_kernel(const uint32_t* __restrict__ keys,
                                                      const uint32_t* __restrict__ vals, int64_t n,
                                                      int ntiles, uint32_t* status, uint32_t* ticket,
@@ -491,7 +528,7 @@ __global__ __launch_bounds__(1024) void rle_kernel(const uint32_t* __restrict__ 
   __shared__ uint32_t scratch[NT / kWave];
   __shared__ uint32_t s_tile, s_base;
   const int tid = threadIdx.x;  // every write below is clamped in range
-  if (tid == 0) s_tile = ticket ? atomicAdd(ticket, 1u) : blockIdx.x;
+  if (tid == 0) s_tile = (ticket && !COUNTED) ? atomicAdd(ticket, 1u) : blockIdx.x;
   __syncthreads();
   const int tile = static_cast<int>(s_tile);
   const int64_t base = static_cast<int64_t>(tile) * kRleTile;
@@ -519,11 +556,15 @@ __global__ __launch_bounds__(1024) void rle_kernel(const uint32_t* __restrict__ 
   uint32_t total;
   uint32_t r = block_excl_n<NT / kWave>(c, scratch, &total);
   if (tid < kWave) {
-    if (tid == 0) st_status(status + tile, (tile == 0 ? kFlagIncl : kFlagAgg) | total);
     uint32_t before = 0;
-    if (tile > 0) before = lookback_wave(status, tile, WaitCtl{counters + kCntError, spin_limit});
+    if constexpr (COUNTED) {
+      before = status[tile];
+    } else {
+      if (tid == 0) st_status(status + tile, (tile == 0 ? kFlagIncl : kFlagAgg) | total);
+      if (tile > 0) before = lookback_wave(status, tile, WaitCtl{counters + kCntError, spin_limit});
+    }
     if (tid == 0) {
-      if (tile > 0) st_status(status + tile, kFlagIncl | ((before + total) & kValueMask));
+      if (!COUNTED && tile > 0) st_status(status + tile, kFlagIncl | ((before + total) & kValueMask));
       s_base = before;
       if (tile == ntiles - 1) {
         // U <= n always, unless a look-back gave up; keep every index in range regardless
@@ -1422,8 +1463,22 @@ hipError_t launch_run_length_encode(const BackwardLaunch& a, const uint32_t* sor
                                     const KernelTimer* kt) {
   const int64_t n = a.num_indices;
   const int ntiles = static_cast<int>((n + kRleTile - 1) / kRleTile);
-  launch_timed(kt, "rle_kernel", rle_kernel, dim3(ntiles), dim3(1024), 0, stream, sorted_keys,
-               sorted_vals, n, ntiles, a.buf.rle_status,
+  if (counted_passes(n)) {
+    // head counts of the tiles, then their scan (the radix passes' count words
+    // are free again; the scan's total goes to the word after them)
+    uint32_t* cnt = a.buf.sort_status;
+    launch_timed(kt, "rle_count", rle_count, dim3(ntiles), dim3(1024), 0, stream, sorted_keys, n,
+                 cnt);
+    launch_timed(kt, "radix_scan", radix_scan, dim3(1), dim3(kBlock), 0, stream, cnt, ntiles,
+                 cnt + ntiles);
+    launch_timed(kt, "rle_kernel", rle_kernel<true>, dim3(ntiles), dim3(1024), 0, stream,
+                 sorted_keys, sorted_vals, n, ntiles, cnt, nullptr, a.buf.counters,
+                 a.buf.unique_keys, a.buf.run_start, a.buf.run_first, a.buf.first_stride,
+                 a.spin_limit);
+    return hipGetLastError();
+  }
+  launch_timed(kt, "rle_kernel", rle_kernel<false>, dim3(ntiles), dim3(1024), 0, stream,
+               sorted_keys, sorted_vals, n, ntiles, a.buf.rle_status,
                ntiles <= kResidentTiles ? nullptr : a.buf.tickets + kMaxRadixPasses,
                a.buf.counters, a.buf.unique_keys, a.buf.run_start, a.buf.run_first,
                a.buf.first_stride, a.spin_limit);

@@ -206,8 +206,10 @@ def test_path_boundaries(E, n):
     bucket = E == (1 << 20) and n <= (1 << 20)
     assert ("bucket_sort_rle" in used) == bucket, used
     assert ("rle_kernel" in used) == (not bucket), used
-    # more than 2^20 lookups: counted passes (count, scan, place), no look-back
+    # more than 2^20 lookups: counted passes (count, scan, place) and a counted
+    # run-length encoding, no look-back
     counted = n > (1 << 20)
     assert ("radix_count" in used) == counted and ("radix_scan" in used) == counted, used
+    assert ("rle_count" in used) == counted, used
     pb.op.close()
     parity(spec, seed=12, steps=1, batches=[batch], bag_sample=500, row_sample=2000)

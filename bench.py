@@ -70,9 +70,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU baseline")
     p.add_argument("--forward", choices=("gather", "routed", "histogram"), default="gather",
-                   help="gather: the gather forward (the library default); routed: count-matrix "
-                        "forward for the tables that qualify; histogram: count-matrix forward "
-                        "for every table (all must qualify)")
+                   help="gather: the library default (the gather kernel, small tables pooled "
+                        "from LDS when a call qualifies); routed: count-matrix forward for the "
+                        "tables that qualify; histogram: count-matrix forward for every table "
+                        "(all must qualify)")
     p.add_argument("--plain", action="store_true",
                    help="time tbe_forward + tbe_backward_update instead of the grouped pair")
     p.add_argument("--phase", choices=("all", "hot", "flushed"), default="all",

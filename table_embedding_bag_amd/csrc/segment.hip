@@ -936,86 +936,105 @@ __global__ __launch_bounds__(kBlock) void seg_finalize(BackwardLaunch a) {
       }
     }
   }
-  for (uint32_t li = blockIdx.x; li < n; li += gridDim.x) {
-    const uint4 L = a.buf.longs[li];  // {first position, length, first partial, chunks}
-    // finished above (the same on every thread)
-    if (L.w <= kFinGroupChunks || L.w >= kFinPieceMin) continue;
-    const uint32_t key = a.buf.long_keys[li];
-    const TableMeta m = meta_of(a, s_meta, table_of_key(a, s_meta, key));
-    const int D = m.dim, C = D / VE;
-    const int64_t row0 = m.woff + static_cast<int64_t>(key - static_cast<uint32_t>(m.roff)) * D;
-    float w[kElemsPerThread];
-#pragma unroll
-    for (int k = 0; k < kElemsPerThread; ++k) {
-      const int d = tid + k * kBlock;
-      w[k] = 0.0f;
-      if (d < D) load_widen<ST, 1>(a.weights, row0 + d, &w[k]);
+  // The runs this workgroup finishes as a whole (more than kFinGroupChunks and
+  // fewer than kFinPieceMin chunks) among its share li = blockIdx.x + k *
+  // gridDim.x: every thread tests one of them, so the share costs one round
+  // trip instead of one per run; the runs are then finished one by one (each
+  // on its own: the order does not change any result).
+  __shared__ uint32_t s_whole[kBlock];
+  __shared__ uint32_t s_nwhole;
+  const uint32_t span = gridDim.x * static_cast<uint32_t>(kBlock);
+  for (uint32_t l0 = blockIdx.x; l0 < n; l0 += span) {
+    if (tid == 0) s_nwhole = 0u;
+    __syncthreads();
+    const uint32_t lt = l0 + static_cast<uint32_t>(tid) * gridDim.x;
+    if (lt < n) {
+      const uint32_t w = a.buf.longs[lt].w;
+      if (w > kFinGroupChunks && w < kFinPieceMin) s_whole[atomicAdd(&s_nwhole, 1u)] = lt;
     }
-    const float m_old = a.adagrad ? a.state[key] : 0.0f;
-    Acc<VE, NCH> acc;
-    acc.zero();
-    for (uint32_t c0 = g; c0 < L.w; c0 += static_cast<uint32_t>(ngroups * kU)) {
-      float v[kU][NCH][VE];
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const uint32_t c = c0 + static_cast<uint32_t>(u * ngroups);
-        const float* row = a.buf.partial1 + static_cast<int64_t>(L.z + c) * a.pstride;
-#pragma unroll
-        for (int q = 0; q < NCH; ++q) {
-          const int chunk = q * Gs + gl;
-          if (c < L.w && chunk < C) {
-            if constexpr (VE == 4) {
-              const float4 x = *reinterpret_cast<const float4*>(row + chunk * 4);
-              v[u][q][0] = x.x; v[u][q][1] = x.y; v[u][q][2] = x.z; v[u][q][3] = x.w;
+    __syncthreads();
+    const uint32_t nwhole = s_nwhole;
+    for (uint32_t q = 0; q < nwhole; ++q) {
+      const uint32_t li = s_whole[q];
+      const uint4 L = a.buf.longs[li];  // {first position, length, first partial, chunks}
+      const uint32_t key = a.buf.long_keys[li];
+      const TableMeta m = meta_of(a, s_meta, table_of_key(a, s_meta, key));
+      const int D = m.dim, C = D / VE;
+      const int64_t row0 = m.woff + static_cast<int64_t>(key - static_cast<uint32_t>(m.roff)) * D;
+      float w[kElemsPerThread];
+  #pragma unroll
+      for (int k = 0; k < kElemsPerThread; ++k) {
+        const int d = tid + k * kBlock;
+        w[k] = 0.0f;
+        if (d < D) load_widen<ST, 1>(a.weights, row0 + d, &w[k]);
+      }
+      const float m_old = a.adagrad ? a.state[key] : 0.0f;
+      Acc<VE, NCH> acc;
+      acc.zero();
+      for (uint32_t c0 = g; c0 < L.w; c0 += static_cast<uint32_t>(ngroups * kU)) {
+        float v[kU][NCH][VE];
+  #pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const uint32_t c = c0 + static_cast<uint32_t>(u * ngroups);
+          const float* row = a.buf.partial1 + static_cast<int64_t>(L.z + c) * a.pstride;
+  #pragma unroll
+          for (int q = 0; q < NCH; ++q) {
+            const int chunk = q * Gs + gl;
+            if (c < L.w && chunk < C) {
+              if constexpr (VE == 4) {
+                const float4 x = *reinterpret_cast<const float4*>(row + chunk * 4);
+                v[u][q][0] = x.x; v[u][q][1] = x.y; v[u][q][2] = x.z; v[u][q][3] = x.w;
+              } else {
+  #pragma unroll
+                for (int e = 0; e < VE; ++e) v[u][q][e] = row[chunk * VE + e];
+              }
             } else {
-#pragma unroll
-              for (int e = 0; e < VE; ++e) v[u][q][e] = row[chunk * VE + e];
+  #pragma unroll
+              for (int e = 0; e < VE; ++e) v[u][q][e] = 0.0f;
             }
-          } else {
-#pragma unroll
-            for (int e = 0; e < VE; ++e) v[u][q][e] = 0.0f;
           }
         }
+  #pragma unroll
+        for (int u = 0; u < kU; ++u)
+  #pragma unroll
+          for (int q = 0; q < NCH; ++q)
+  #pragma unroll
+            for (int e = 0; e < VE; ++e) acc.v[q][e] += static_cast<double>(v[u][q][e]);
       }
-#pragma unroll
-      for (int u = 0; u < kU; ++u)
-#pragma unroll
-        for (int q = 0; q < NCH; ++q)
-#pragma unroll
-          for (int e = 0; e < VE; ++e) acc.v[q][e] += static_cast<double>(v[u][q][e]);
-    }
-#pragma unroll
-    for (int q = 0; q < NCH; ++q)
-#pragma unroll
-      for (int e = 0; e < VE; ++e) s_red[g * row_elems + (q * Gs + gl) * VE + e] = acc.v[q][e];
-    __syncthreads();
-    double gam[kElemsPerThread];
-    double ss = 0.0;
-#pragma unroll
-    for (int k = 0; k < kElemsPerThread; ++k) {
-      const int d = tid + k * kBlock;
-      double x = 0.0;
-      if (d < D)
-        for (int gg = 0; gg < ngroups; ++gg) x += s_red[gg * row_elems + d];
-      gam[k] = x;
-      ss = fma(x, x, ss);
-    }
-    float step = a.lr;
-    if (a.adagrad) {
-      ss = block_sum(ss, s_scratch);
-      const float mnew = static_cast<float>(static_cast<double>(m_old) + ss / D);
-      if (tid == 0) a.state[key] = mnew;
-      step = a.lr / (sqrtf(mnew) + a.eps);
-    }
-#pragma unroll
-    for (int k = 0; k < kElemsPerThread; ++k) {
-      const int d = tid + k * kBlock;
-      if (d < D) {
-        float x = fmaf(-step, static_cast<float>(gam[k]), w[k]);
-        narrow_store<ST, 1>(a.weights, row0 + d, &x);
+  #pragma unroll
+      for (int q = 0; q < NCH; ++q)
+  #pragma unroll
+        for (int e = 0; e < VE; ++e) s_red[g * row_elems + (q * Gs + gl) * VE + e] = acc.v[q][e];
+      __syncthreads();
+      double gam[kElemsPerThread];
+      double ss = 0.0;
+  #pragma unroll
+      for (int k = 0; k < kElemsPerThread; ++k) {
+        const int d = tid + k * kBlock;
+        double x = 0.0;
+        if (d < D)
+          for (int gg = 0; gg < ngroups; ++gg) x += s_red[gg * row_elems + d];
+        gam[k] = x;
+        ss = fma(x, x, ss);
       }
+      float step = a.lr;
+      if (a.adagrad) {
+        ss = block_sum(ss, s_scratch);
+        const float mnew = static_cast<float>(static_cast<double>(m_old) + ss / D);
+        if (tid == 0) a.state[key] = mnew;
+        step = a.lr / (sqrtf(mnew) + a.eps);
+      }
+  #pragma unroll
+      for (int k = 0; k < kElemsPerThread; ++k) {
+        const int d = tid + k * kBlock;
+        if (d < D) {
+          float x = fmaf(-step, static_cast<float>(gam[k]), w[k]);
+          narrow_store<ST, 1>(a.weights, row0 + d, &x);
+        }
+      }
+      __syncthreads();  // s_red is reused by the next run
     }
-    __syncthreads();  // s_red is reused by the next run
+    __syncthreads();  // s_whole and s_nwhole are reused
   }
 }
 

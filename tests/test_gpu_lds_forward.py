@@ -33,6 +33,9 @@ CASES = [
     # bags of 0..30 lookups: four partial sums, rows of 8 chunks
     ("bf16-ragged-4-sums", workloads.custom([300, 1000], [64, 64], "bf16", B=2048,
                                             lengths=("uniform_int", 0, 30), key=274), torch.int64),
+    # tables of 1, 2 and 3 rows (every id is one of a few rows) with bags up to 30 long
+    ("bf16-tiny-tables", workloads.custom([1, 2, 3], [64, 64, 64], "bf16", B=2048,
+                                          lengths=("uniform_int", 0, 30), key=276), torch.int64),
     # rows of 4 chunks with weights and four partial sums
     ("bf16-dim32-psw-4-sums", workloads.custom([500, 200], [32, 32], "bf16", B=2048,
                                                lengths=("uniform_int", 0, 30), psw=True,

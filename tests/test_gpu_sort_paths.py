@@ -213,3 +213,23 @@ def test_path_boundaries(E, n):
     assert ("rle_count" in used) == counted, used
     pb.op.close()
     parity(spec, seed=12, steps=1, batches=[batch], bag_sample=500, row_sample=2000)
+
+
+def test_counted_single_pass_with_records():
+    """More than 2^20 lookups on 7-bit ids (one counted pass), mean pooling with per-sample
+    weights (sorted values are lookup ids with side records): runs bit-exact and sampled
+    updates against the reference."""
+    spec = workloads.custom([100, 20], [16, 32], "f32", B=40000, lengths=("uniform_int", 20, 35),
+                            index_dist=("zipf", 1.2), pooling="mean", psw=True,
+                            optimizer="rowwise_adagrad", key=252)
+    pb = make_problem(spec, seed=13)
+    assert pb.batch.indices.size > (1 << 20)
+    pb.op.set_option(tbe.OPTION_PROFILE, 1)
+    G = workloads.grad_output(spec, seed=13, step=0, device="cuda")
+    runs = gpu_runs(pb, pb.batch.indices.size)
+    pb.op.backward_update(spec.B, pb.idx, pb.off, pb.psw, G, spec.lr, spec.eps, runs)
+    torch.cuda.synchronize()
+    used = [name for name, _ in pb.op.stage_times()]
+    assert used.count("radix_count") == 1 and "rle_count" in used, used
+    pb.op.close()
+    parity(spec, seed=13, steps=2, bag_sample=3000)

@@ -74,6 +74,22 @@ __device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t x, uint32_t* sc
   return base + incl - x;
 }
 
+// Lanes among `active` whose value v (its low `bits` bits) equals this lane's:
+// one ballot per bit.  Each bit is taken as a mask of all ones or all zeros
+// (its sign-extended copy), so a lane keeps the ballot's lanes whose bit equals
+// its own with one xor and and per half (two selects and two ands per bit
+// otherwise; the radix passes' ranking is bound by this VALU work).  Call with
+// the whole wave.
+__device__ __forceinline__ uint64_t match_low_bits(uint64_t active, uint32_t v, int bits) {
+  uint64_t peers = active;
+  for (int bit = 0; bit < bits; ++bit) {
+    const uint32_t m = static_cast<uint32_t>(static_cast<int32_t>(v << (31 - bit)) >> 31);
+    const uint64_t bal = __ballot(m != 0u);
+    peers &= ~(bal ^ ((static_cast<uint64_t>(m) << 32) | m));
+  }
+  return peers;
+}
+
 // Workgroups are handed to the 8 XCDs of the chip round robin.  Renumber them
 // so that each XCD works on one contiguous range of logical work items (and so
 // keeps that range's data in its own L2).

@@ -161,13 +161,7 @@ __device__ __forceinline__ void add_listed(uint32_t* cw, const uint16_t* ent, in
 // Lanes among `active` whose value c (of `bits` bits) equals this lane's: one
 // ballot per bit.  Call with the whole wave.
 __device__ __forceinline__ uint64_t match_value(uint64_t active, uint32_t c, int bits) {
-  uint64_t peers = active;
-  for (int bit = 0; bit < bits; ++bit) {
-    const bool set = (c >> bit) & 1u;
-    const uint64_t bal = __ballot(set);
-    peers &= set ? bal : ~bal;
-  }
-  return peers;
+  return match_low_bits(active, c, bits);
 }
 
 template <int ST, typename IT>

@@ -62,13 +62,7 @@ __device__ __forceinline__ int tile_bag_slot(const int64_t* s_off, int nb, int64
 // Lanes among `active` whose digit d (of `bits` bits) equals this lane's: one
 // ballot per digit bit.  Call with the whole wave.
 __device__ __forceinline__ uint64_t match_bits(uint64_t active, uint32_t d, int bits) {
-  uint64_t peers = active;
-  for (int bit = 0; bit < bits; ++bit) {
-    const bool set = (d >> bit) & 1u;
-    const uint64_t bal = __ballot(set);
-    peers &= set ? bal : ~bal;
-  }
-  return peers;
+  return match_low_bits(active, d, bits);
 }
 
 // A workgroup of NT threads takes tiles first, first + stride, ... of

@@ -112,12 +112,7 @@ __device__ __forceinline__ uint64_t match_digit(uint64_t* s_slots, uint32_t d, b
   uint64_t peers = rest ? __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT) : 0u;
   wave_lds_sync();
   if (rest) __hip_atomic_store(slot, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
-#pragma unroll
-  for (int bit = 8; bit < RB; ++bit) {
-    const bool set = (d >> bit) & 1u;
-    const uint64_t bal = __ballot(set);
-    peers &= set ? bal : ~bal;
-  }
+  if constexpr (RB > 8) peers = match_low_bits(peers, d >> 8, RB - 8);
   return same ? m0 : peers;
 }
 
@@ -179,13 +174,8 @@ __global__ __launch_bounds__(kBlock) void radix_pass(
   for (int r = 0; r < KPT; ++r) {
     const bool ok = (seg + r * kWave + lane) < n;
     const uint32_t d = (key[r] >> shift) & dmask;
-    uint64_t peers = __ballot(ok);
-#pragma unroll
-    for (int bit = 0; bit < RB; ++bit) {  // bits above `bits` are 0 everywhere: no effect
-      const bool set = (d >> bit) & 1u;
-      const uint64_t bal = __ballot(set);
-      peers &= set ? bal : ~bal;
-    }
+    // (bits above `bits` are 0 everywhere: matching them changes nothing)
+    const uint64_t peers = match_low_bits(__ballot(ok), d, RB);
     const uint32_t below = popc_below(peers);
     const uint32_t cnt = __popcll(peers);
     const uint32_t pre = ok ? s_cnt[wave][d] : 0u;

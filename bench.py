@@ -54,6 +54,8 @@ FLUSH_BYTES = 1 << 30        # written between calls to empty L2 and the 256 MB 
 FRONT = ("init_workspace", "linearize_kernel", "radix_count", "radix_scan", "radix_pass",
          "bucket_sort_rle", "rle_count", "rle_kernel")
 SEG = ("queue_runs", "table_run_starts", "seg_fused", "seg_finalize")
+# batches of at most this many lookups have their long runs finished inside seg_fused
+FINISH_IN_ITEMS_MAX = 1 << 20
 FWD = ("fwd_gather_pool", "fwd_lds_pool", "fwd_linearize", "fwd_histogram", "hist_transpose",
        "fwd_split_segments", "fwd_split_combine")
 COUNT_BWD = ("cb_product", "cb_update", "cb_runs")
@@ -170,8 +172,10 @@ def algorithmic_bytes(spec, batch, gather_tables=None, long_threshold=256, chunk
       seg_fused           short runs (at most Gs lookups, one lane group each) and the
                           queued items: longer runs below the long-run threshold, and the
                           lookups of long runs (+ one 4*D partial write per 256-lookup
-                          chunk), in one launch
-      seg_finalize        per long run: its chunk partials read, the row terms
+                          chunk), in one launch; in batches of at most 2^20 lookups also
+                          the long runs' finish (below)
+      seg_finalize        per long run: its chunk partials read, the row terms (a launch
+                          of its own in batches of more than 2^20 lookups)
     grouping front: linearize, radix passes (key+value read and scatter 16 per lookup),
     bucket_sort_rle (key+value read and final write 16 per lookup; unique id, start and
     first value 12 per run), rle_kernel (keys 4 per lookup; per run 12 written, first
@@ -203,6 +207,8 @@ def algorithmic_bytes(spec, batch, gather_tables=None, long_threshold=256, chunk
                    + (cnt[long_] * per_look[long_] + nch[long_] * 4 * D[long_]).sum())
     seg_final = float((nch[long_] * 4 * D[long_] + per_row[long_]).sum())
     N, U, nbags = int(lens.sum()), int(cnt.size), spec.T * spec.B
+    if N <= FINISH_IN_ITEMS_MAX:  # the segment kernel finishes the long runs itself
+        seg_wg, seg_final = seg_wg + seg_final, 0.0
     front = {"linearize_kernel": float(N * (8 + 8 + rec) + 8 * nbags),
              "radix_pass": float(16 * N), "radix_count": float(4 * N), "rle_count": float(4 * N),
              "rle_kernel": float(4 * N + 16 * U),
@@ -697,8 +703,9 @@ def main():
     gates = {
         "forward_gather_pool": gate_entry(("fwd_gather_pool",), m["alg"], m["fwd_only_us"],
                                           m.get("flushed_us"), tag),
-        "segment_reduce_update": gate_entry(("seg_fused", "seg_finalize"), m["alg"],
-                                            m["avg_us"], m.get("flushed_us"), tag),
+        "segment_reduce_update": gate_entry(
+            tuple(k for k in ("seg_fused", "seg_finalize") if k in m["avg_us"]), m["alg"],
+            m["avg_us"], m.get("flushed_us"), tag),
         "threshold_pct": 60,
         "note": "alg = the method's own bytes (one row read per lookup); counter = "
                 "rocprofv3 FETCH_SIZE + WRITE_SIZE per launch (committed summaries, same "

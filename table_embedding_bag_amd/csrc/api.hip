@@ -324,7 +324,7 @@ bool plan_backward(const tbe_handle* h, int32_t B, int64_t n, bool vec, int64_t 
   p->items1_ub = ub.items1;
   p->zero_words = kNumCounters + kNumTickets + int64_t{p->passes} * p->slots +
                   int64_t{p->passes} * p->sort_tiles * p->slots + p->rle_tiles +
-                  p->chunks_ub / kFinPiece + 1;
+                  p->chunks_ub / kFinPiece + 1 + p->long_ub;
   Carve cv;
   for (int i = 0; i < 2; ++i) {
     p->o_keys[i] = cv.take(4 * static_cast<size_t>(n));
@@ -385,6 +385,7 @@ void fill_backward(const tbe_handle* h, int32_t B, const void* indices, const vo
   a.per_table = p.per_table ? 1 : 0;
   a.pstride = p.pstride;
   a.long_threshold = static_cast<int32_t>(std::min<int64_t>(long_threshold, 0x7FFFFFFF));
+  a.finish_in_items = n <= kFinishInItemsMaxKeys ? 1 : 0;
   a.bucket_sort = bucket_sort ? 1 : 0;
   a.spin_limit = h->spin_limit;
   a.error_mark = h->error_mark;
@@ -407,9 +408,10 @@ void fill_backward(const tbe_handle* h, int32_t B, const void* indices, const vo
   b.digit_hist = b.tickets + kNumTickets;
   b.rle_status = b.digit_hist + p.passes * p.slots;
   b.piece_tickets = b.rle_status + p.rle_tiles;
+  b.run_tickets = b.piece_tickets + p.chunks_ub / kFinPiece + 1;
   // last, so that a call whose linearize step sorts the tiles (no radix pass)
   // clears only what comes before
-  b.sort_status = b.piece_tickets + p.chunks_ub / kFinPiece + 1;
+  b.sort_status = b.run_tickets + p.long_ub;
   b.zero_words = p.zero_words;
   b.unique_keys = reinterpret_cast<uint32_t*>(w + p.o_uniq);
   b.run_start = reinterpret_cast<uint32_t*>(w + p.o_start);

@@ -316,6 +316,7 @@ struct BackwardBuffers {
   // One contiguous region zeroed at the start of every backward call:
   //   counters [kNumCounters], tickets [kNumTickets], digit_hist [passes][slots],
   //   rle_status [rle tiles], piece_tickets [chunks cap / kFinPiece + 1],
+  //   run_tickets [long runs cap],
   //   sort_status [passes][sort tiles][slots] (not cleared when no radix pass runs)
   // (slots = radix_slots(digit bits))
   uint32_t* counters;
@@ -324,7 +325,8 @@ struct BackwardBuffers {
   uint32_t* sort_status;    // look-back status words of the radix passes
   uint32_t* rle_status;     // look-back status words of the RLE
   uint32_t* piece_tickets;  // finished chunks of each piece of a very long run, by the piece's
-                            // first partial slot / kFinPiece (reset by the piece's last chunk)
+                            // first partial slot / kFinPiece (long runs finished by seg_fused)
+  uint32_t* run_tickets;    // finished chunks (or pieces) of each long run
   int64_t zero_words;       // size of the zeroed region, in 32-bit words
   uint32_t* unique_keys;    // [N]
   uint32_t* run_start;      // [N + 1]
@@ -354,6 +356,12 @@ enum { kCntUnique = 0, kCntLong = 32, kCntItems1 = 64, kCntChunks = 96, kCntErro
 // apart, and first slot / kFinPiece numbers them.
 constexpr uint32_t kFinPiece = 64;
 constexpr uint32_t kFinPieceMin = 2 * kFinPiece;
+// Batches of at most this many lookups have their long runs finished inside
+// the segment kernel by the workgroup that stores a run's last chunk partial
+// (a ticket per run), which saves a launch; larger ones, whose many long runs
+// would each add a ticket round trip to a workgroup item, take a separate
+// finishing kernel.
+constexpr int64_t kFinishInItemsMaxKeys = int64_t{1} << 20;
 
 // Workgroup items of the segment kernels: {first position, kMediumItem | length}
 // for a medium run, {long run, chunk} for a 256-lookup chunk of a long run.
@@ -411,6 +419,7 @@ struct BackwardLaunch {
   int32_t per_table;        // short runs use each table's own lane-group width
   int32_t short_max;        // runs of at most this many lookups are short (a lane group's)
   int32_t front_queued;     // the run-length encoder queued the longer runs
+  int32_t finish_in_items;  // seg_fused finishes the long runs (else seg_finalize does)
   int32_t pstride;          // floats per partial row
   int32_t long_threshold;   // runs at least this long use split accumulation
   int32_t chunk;            // lookups per level-1 partial

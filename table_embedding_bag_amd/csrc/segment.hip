@@ -27,24 +27,26 @@
 //                 or a 256-lookup chunk of a long run (split accumulation: an
 //                 fp32 partial sum per chunk).  The workgroup stages 256 lookups
 //                 in LDS and its 256/Gs lane groups keep 4 rows each in flight;
-//                 the groups' sums are added in LDS in a fixed order.
+//                 the groups' sums are added in LDS in a fixed order.  In a
+//                 batch of at most 2^20 lookups the workgroup that stores a
+//                 run's last partial (a ticket per run) adds the run's
+//                 partials in chunk order and updates the row.
 //     short runs  one lane group (Gs lanes = one gradient row of 16-byte
 //                 chunks; per table when tables differ in width) per run: every
 //                 lane prefetches one lookup, the group gathers the run's
 //                 gradient rows with 2 or 4 in flight (matched to the run's
 //                 length), sums them in fp32 and updates the row.  Most runs
 //                 are this short.
-//   seg_finalize  one workgroup per long run: its partials summed in a fixed
-//                 order, then the update.
+//   seg_finalize  larger batches: the long runs' partials added in the same
+//                 order and the rows updated, in a launch of their own.
 // Summation order never depends on scheduling (no float atomics), so results
 // are reproducible bit for bit.  Sums inside workgroup items are kept in fp64:
 // a run may add the same gradient row many times over (a hot row hit
 // repeatedly inside one bag), and fp32 rounding errors of such correlated sums
-// grow linearly; products c_i * g are exact in fp64.  Every stage is its own
-// kernel: no workgroup waits for another.  (Finishing a long run in the chunk
-// workgroup that completes it last would need a device-scope release per
-// chunk, which writes back the whole L2 of its XCD and costs far more than
-// one more small kernel.)
+// grow linearly; products c_i * g are exact in fp64.  No workgroup waits for
+// another: a ticket only decides which one finishes a run.  The partials go
+// through agent-scope atomic stores and loads, which other XCDs see without
+// the writeback of the whole L2 that a device-scope release fence costs.
 #include "common.hpp"
 
 namespace tbe {
@@ -475,6 +477,240 @@ __device__ __forceinline__ double block_sum(double x, double* scratch) {
   return s;
 }
 
+// Data one workgroup hands to another inside a kernel is stored and loaded
+// with relaxed agent-scope atomics: those go to the device's point of
+// coherence rather than stopping in the XCD's own L2, so a workgroup on any
+// XCD sees them without the L2 writeback a release fence would cost.  The
+// writer waits until its stores are performed (wait_stores) before it takes a
+// ticket; the workgroup whose ticket completes the set then reads the data.
+template <typename T>
+__device__ __forceinline__ void st_agent(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_agent(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// s_waitcnt vmcnt(0): every load and store this wave issued is performed.
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Takes one of `total` tickets at *ticket for the whole workgroup, once every
+// thread's earlier stores are performed, and tells every thread whether it
+// was the last one.  Call from the whole workgroup.
+__device__ __forceinline__ bool last_ticket(uint32_t* ticket, uint32_t total, uint32_t* s_flag) {
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *s_flag = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                      total - 1u
+                  ? 1u
+                  : 0u;
+  __syncthreads();
+  return *s_flag != 0u;
+}
+
+// Finish of a long run of fewer than kFinPieceMin chunks by a workgroup: lane
+// group g adds the chunk partials g, g + ngroups, ... in chunk order (fp64),
+// the groups' sums are added in group order, and the row is updated.  The row
+// and its state are loaded while the partials are in flight (KU per group).
+// AGENT: the partials were stored in this kernel (agent-scope loads), else in
+// an earlier one.
+template <int ST, int VE, int NCH, bool AGENT, int KU>
+__device__ __forceinline__ void finish_run(const BackwardLaunch& a, const uint4& L,
+                                           const TableMeta& m, uint32_t key, double* s_red,
+                                           double* s_scratch) {
+  constexpr int NV = VE * NCH;
+  constexpr int kElemsPerThread = kMaxDim / kBlock;
+  constexpr int kU = KU;
+  const int tid = threadIdx.x;
+  const int Gs = 1 << a.gshift;
+  const int ngroups = kBlock >> a.gshift;
+  const int g = tid >> a.gshift, gl = tid & (Gs - 1);
+  const int row_elems = Gs * NV;
+  const int D = m.dim, C = D / VE;
+  const int64_t row0 = m.woff + static_cast<int64_t>(key - static_cast<uint32_t>(m.roff)) * D;
+  float w[kElemsPerThread];
+#pragma unroll
+  for (int k = 0; k < kElemsPerThread; ++k) {
+    const int d = tid + k * kBlock;
+    w[k] = 0.0f;
+    if (d < D) load_widen<ST, 1>(a.weights, row0 + d, &w[k]);
+  }
+  const float m_old = a.adagrad ? a.state[key] : 0.0f;
+  Acc<VE, NCH> acc;
+  acc.zero();
+  for (uint32_t c0 = g; c0 < L.w; c0 += static_cast<uint32_t>(ngroups * kU)) {
+    float v[kU][NCH][VE];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const uint32_t c = c0 + static_cast<uint32_t>(u * ngroups);
+      const float* row = a.buf.partial1 + static_cast<int64_t>(L.z + c) * a.pstride;
+#pragma unroll
+      for (int q = 0; q < NCH; ++q) {
+        const int chunk = q * Gs + gl;
+        const bool ok = c < L.w && chunk < C;
+        if constexpr (AGENT) {
+#pragma unroll
+          for (int e = 0; e < VE; ++e) v[u][q][e] = ok ? ld_agent(row + chunk * VE + e) : 0.0f;
+        } else if (ok) {
+          if constexpr (VE == 4) {
+            const float4 x = *reinterpret_cast<const float4*>(row + chunk * 4);
+            v[u][q][0] = x.x; v[u][q][1] = x.y; v[u][q][2] = x.z; v[u][q][3] = x.w;
+          } else {
+#pragma unroll
+            for (int e = 0; e < VE; ++e) v[u][q][e] = row[chunk * VE + e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < VE; ++e) v[u][q][e] = 0.0f;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int q = 0; q < NCH; ++q)
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc.v[q][e] += static_cast<double>(v[u][q][e]);
+  }
+#pragma unroll
+  for (int q = 0; q < NCH; ++q)
+#pragma unroll
+    for (int e = 0; e < VE; ++e) s_red[g * row_elems + (q * Gs + gl) * VE + e] = acc.v[q][e];
+  __syncthreads();
+  double gam[kElemsPerThread];
+  double ss = 0.0;
+#pragma unroll
+  for (int k = 0; k < kElemsPerThread; ++k) {
+    const int d = tid + k * kBlock;
+    double x = 0.0;
+    if (d < D)
+      for (int gg = 0; gg < ngroups; ++gg) x += s_red[gg * row_elems + d];
+    gam[k] = x;
+    ss = fma(x, x, ss);
+  }
+  float step = a.lr;
+  if (a.adagrad) {
+    ss = block_sum(ss, s_scratch);
+    step = step_size(a, key, m_old, ss, D, tid == 0);
+  }
+#pragma unroll
+  for (int k = 0; k < kElemsPerThread; ++k) {
+    const int d = tid + k * kBlock;
+    if (d < D) {
+      float x = fmaf(-step, static_cast<float>(gam[k]), w[k]);
+      narrow_store<ST, 1>(a.weights, row0 + d, &x);
+    }
+  }
+}
+
+// Piece j of a long run of at least kFinPieceMin chunks (cnt chunk partials
+// from slot L.z + j * kFinPiece): with H thread sets (all threads when
+// D < kBlock), set h adds chunks h, h + H, ... in order (fp64), the sets'
+// sums are added in set order and left, as doubles, over the piece's first
+// two slots.  So a row hit hundreds of thousands of times is not finished by
+// one workgroup reading every partial.
+__device__ __forceinline__ void sum_piece(const BackwardLaunch& a, const uint4& L, uint32_t j,
+                                          uint32_t cnt, int D, double* s_sum) {
+  constexpr int kBatch = 8;  // partial loads in flight per thread
+  const int tid = threadIdx.x;
+  const int64_t ps = a.pstride;
+  float* first = a.buf.partial1 + static_cast<int64_t>(L.z + j * kFinPiece) * ps;
+  const int H = D < kBlock ? kBlock / D : 1;
+  for (int e = tid; e < H * D; e += kBlock) {
+    const int h = e / D, d = e - h * D;
+    double x = 0.0;
+    uint32_t q = static_cast<uint32_t>(h);
+    for (; q + (kBatch - 1) * H < cnt; q += kBatch * H) {
+      float v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) v[u] = ld_agent(first + static_cast<int64_t>(q + u * H) * ps + d);
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) x += static_cast<double>(v[u]);
+    }
+    for (; q < cnt; q += H) x += static_cast<double>(ld_agent(first + static_cast<int64_t>(q) * ps + d));
+    s_sum[e] = x;
+  }
+  __syncthreads();  // every read of the first two slots is done
+  for (int d = tid; d < D; d += kBlock) {
+    double x = 0.0;
+    for (int h = 0; h < H; ++h) x += s_sum[h * D + d];
+    st_agent(reinterpret_cast<double*>(first) + d, x);
+  }
+}
+
+// Finish of a long run from its np piece sums, added in piece order.
+template <int ST>
+__device__ __forceinline__ void finish_run_pieces(const BackwardLaunch& a, const uint4& L,
+                                                  const TableMeta& m, uint32_t key,
+                                                  double* s_sum, double* s_scratch) {
+  constexpr int kBatch = 8;
+  const int tid = threadIdx.x;
+  const int D = m.dim;
+  const uint32_t np = L.w / kFinPiece;
+  // read by every thread before block_sum's barriers (thread 0 writes the new
+  // state after them)
+  const float m_old = a.adagrad ? a.state[key] : 0.0f;
+  const int64_t row0 = m.woff + static_cast<int64_t>(key - static_cast<uint32_t>(m.roff)) * D;
+  const int64_t dstep = static_cast<int64_t>(kFinPiece) * a.pstride / 2;  // doubles per piece
+  const double* p0 = reinterpret_cast<const double*>(a.buf.partial1 +
+                                                     static_cast<int64_t>(L.z) * a.pstride);
+  double ss = 0.0;
+  for (int d = tid; d < D; d += kBlock) {
+    double x = 0.0;
+    uint32_t p = 0;
+    for (; p + kBatch <= np; p += kBatch) {
+      double v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) v[u] = ld_agent(p0 + (p + u) * dstep + d);
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) x += v[u];
+    }
+    for (; p < np; ++p) x += ld_agent(p0 + p * dstep + d);
+    s_sum[d] = x;
+    ss = fma(x, x, ss);
+  }
+  float step = a.lr;
+  if (a.adagrad) {
+    ss = block_sum(ss, s_scratch);
+    step = step_size(a, key, m_old, ss, D, tid == 0);
+  }
+  for (int d = tid; d < D; d += kBlock) {
+    float w;
+    load_widen<ST, 1>(a.weights, row0 + d, &w);
+    w = fmaf(-step, static_cast<float>(s_sum[d]), w);
+    narrow_store<ST, 1>(a.weights, row0 + d, &w);
+  }
+}
+
+// After chunk c of long run li has stored its partial: the workgroup that
+// completes the run (a ticket per run) finishes it; a run of at least
+// kFinPieceMin chunks first has each piece summed by the workgroup that
+// completes the piece (a ticket per piece), and the one that completes the
+// last piece finishes the run.  The sums follow chunk and piece order
+// whichever workgroup does them, so results do not depend on scheduling.
+template <int ST, int VE, int NCH>
+__device__ __forceinline__ void finish_after_chunk(const BackwardLaunch& a, uint32_t li,
+                                                   uint32_t c, const uint4& L, const TableMeta& m,
+                                                   uint32_t key, double* s_red,
+                                                   double* s_scratch, uint32_t* s_flag) {
+  uint32_t* run_ticket = a.buf.run_tickets + li;
+  if (L.w < kFinPieceMin) {
+    // two partials in flight per group (one for wide rows) cover most runs in
+    // one round and leave the item loop's registers as they were
+    if (last_ticket(run_ticket, L.w, s_flag))
+      finish_run<ST, VE, NCH, true, VE * NCH <= 4 ? 2 : 1>(a, L, m, key, s_red, s_scratch);
+    return;
+  }
+  const uint32_t np = L.w / kFinPiece;
+  const uint32_t j = min(c / kFinPiece, np - 1u);
+  const uint32_t cnt = j == np - 1u ? L.w - j * kFinPiece : kFinPiece;
+  if (!last_ticket(a.buf.piece_tickets + (L.z + j * kFinPiece) / kFinPiece, cnt, s_flag)) return;
+  sum_piece(a, L, j, cnt, m.dim, s_red);
+  if (last_ticket(run_ticket, np, s_flag))
+    finish_run_pieces<ST>(a, L, m, key, s_red, s_scratch);
+}
+
 template <int ST, int VE, int NCH, bool REC>
 __device__ __forceinline__ void wg_items(const BackwardLaunch& a, const uint32_t* __restrict__ keys,
                                          const uint32_t* __restrict__ sorted_vals, uint32_t bid,
@@ -486,6 +722,7 @@ __device__ __forceinline__ void wg_items(const BackwardLaunch& a, const uint32_t
   __shared__ float s_coef[kBlock];
   __shared__ double s_red[kBlock * NV];        // [group][row element]
   __shared__ double s_scratch[kWavesPerBlock];
+  __shared__ uint32_t s_flag;
 
   const int tid = threadIdx.x;
   const uint32_t n = a.buf.counters[kCntItems1];
@@ -495,11 +732,12 @@ __device__ __forceinline__ void wg_items(const BackwardLaunch& a, const uint32_t
     const bool medium = (it.y & kMediumItem) != 0;
     uint32_t slot = 0;
     int64_t s, e;
+    uint4 L = make_uint4(0u, 0u, 0u, 0u);
     if (medium) {  // {first position, medium flag | length}
       s = it.x;
       e = s + (it.y & ~kMediumItem);
     } else {       // {long run, chunk}
-      const uint4 L = a.buf.longs[it.x];
+      L = a.buf.longs[it.x];
       s = static_cast<int64_t>(L.x) + static_cast<int64_t>(it.y) * a.chunk;
       e = min(static_cast<int64_t>(L.x) + L.y, s + a.chunk);
       slot = L.z + it.y;
@@ -575,10 +813,19 @@ __device__ __forceinline__ void wg_items(const BackwardLaunch& a, const uint32_t
       }
     } else {
       float* dst = a.buf.partial1 + static_cast<int64_t>(slot) * a.pstride;
+      if (a.finish_in_items) {
 #pragma unroll
-      for (int k = 0; k < kElemsPerThread; ++k) {
-        const int d = tid + k * kBlock;
-        if (d < D) dst[d] = static_cast<float>(gam[k]);
+        for (int k = 0; k < kElemsPerThread; ++k) {
+          const int d = tid + k * kBlock;
+          if (d < D) st_agent(dst + d, static_cast<float>(gam[k]));
+        }
+        finish_after_chunk<ST, VE, NCH>(a, it.x, it.y, L, m, keys[s], s_red, s_scratch, &s_flag);
+      } else {
+#pragma unroll
+        for (int k = 0; k < kElemsPerThread; ++k) {
+          const int d = tid + k * kBlock;
+          if (d < D) dst[d] = static_cast<float>(gam[k]);
+        }
       }
     }
   }
@@ -776,118 +1023,24 @@ __device__ __forceinline__ void finish_long_in_group(const BackwardLaunch& a,
   }
 }
 
-// A long run of at least kFinPieceMin chunks is finished in pieces of
-// kFinPiece chunk partials (the last piece takes the remainder) by as many
-// workgroups: each adds its piece's partials in chunk order (fp64) and leaves
-// the sum, as doubles, over the piece's first two slots; the workgroup that
-// finishes the run's last piece (a ticket per run) adds the piece sums in
-// piece order and updates the row.  So a row hit hundreds of thousands of
-// times is not finished by one workgroup reading every partial, and the result
-// does not depend on which workgroup came last.  piece = {long run, piece}.
-template <int ST>
-__device__ __forceinline__ void finish_piece(const BackwardLaunch& a, const TableMeta* s_meta,
-                                             uint2 piece, double* s_sum, double* s_scratch,
-                                             uint32_t* s_last) {
-  constexpr int kBatch = 8;  // partial loads in flight per thread
-  const int tid = threadIdx.x;
-  const uint4 L = a.buf.longs[piece.x];
-  const uint32_t key = a.buf.long_keys[piece.x];
-  const TableMeta m = meta_of(a, s_meta, table_of_key(a, s_meta, key));
-  const int D = m.dim;
-  const int64_t ps = a.pstride;
-  const uint32_t np = L.w / kFinPiece;
-  const uint32_t j = piece.y;
-  const uint32_t cnt = j == np - 1 ? L.w - j * kFinPiece : kFinPiece;
-  float* first = a.buf.partial1 + static_cast<int64_t>(L.z + j * kFinPiece) * ps;
-  // H thread sets (all threads when D < kBlock): set h adds chunks h, h + H, ...
-  // in order; the sets' sums are then added in set order
-  const int H = D < kBlock ? kBlock / D : 1;
-  for (int e = tid; e < H * D; e += kBlock) {
-    const int h = e / D, d = e - h * D;
-    double x = 0.0;
-    uint32_t q = static_cast<uint32_t>(h);
-    for (; q + (kBatch - 1) * H < cnt; q += kBatch * H) {
-      float v[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) v[u] = first[static_cast<int64_t>(q + u * H) * ps + d];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) x += static_cast<double>(v[u]);
-    }
-    for (; q < cnt; q += H) x += static_cast<double>(first[static_cast<int64_t>(q) * ps + d]);
-    s_sum[e] = x;
-  }
-  __syncthreads();  // every read of the first two slots is done
-  for (int d = tid; d < D; d += kBlock) {
-    double x = 0.0;
-    for (int h = 0; h < H; ++h) x += s_sum[h * D + d];
-    reinterpret_cast<double*>(first)[d] = x;
-  }
-  __threadfence();  // the piece sum is visible to the other workgroups
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t* ticket = a.buf.piece_tickets + L.z / kFinPiece;
-    const bool last = atomicAdd(ticket, 1u) == np - 1;
-    if (last) atomicExch(ticket, 0u);  // ready for the next call on this workspace
-    *s_last = last ? 1u : 0u;
-  }
-  __syncthreads();
-  if (*s_last == 0u) return;  // the same on every thread
-  __threadfence();            // the other pieces' sums are seen
-  // read by every thread before block_sum's barriers (thread 0 writes the new
-  // state after them)
-  const float m_old = a.adagrad ? a.state[key] : 0.0f;
-  const int64_t row0 = m.woff + static_cast<int64_t>(key - static_cast<uint32_t>(m.roff)) * D;
-  const int64_t pstep = static_cast<int64_t>(kFinPiece) * ps;
-  const double* p0 = reinterpret_cast<const double*>(a.buf.partial1 + static_cast<int64_t>(L.z) * ps);
-  double ss = 0.0;
-  for (int d = tid; d < D; d += kBlock) {
-    double x = 0.0;
-    uint32_t p = 0;
-    for (; p + kBatch <= np; p += kBatch) {
-      double v[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) v[u] = p0[(p + u) * (pstep / 2) + d];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) x += v[u];
-    }
-    for (; p < np; ++p) x += p0[p * (pstep / 2) + d];
-    s_sum[d] = x;
-    ss = fma(x, x, ss);
-  }
-  float step = a.lr;
-  if (a.adagrad) {
-    ss = block_sum(ss, s_scratch);
-    step = step_size(a, key, m_old, ss, D, tid == 0);
-  }
-  for (int d = tid; d < D; d += kBlock) {
-    float w;
-    load_widen<ST, 1>(a.weights, row0 + d, &w);
-    w = fmaf(-step, static_cast<float>(s_sum[d]), w);
-    narrow_store<ST, 1>(a.weights, row0 + d, &w);
-  }
-}
-
-// Long runs of more chunks: one workgroup per long run: its chunk partials
-// are added up and the row is updated.  The workgroup's 256/Gs lane groups take the partials in a
-// fixed interleaving (group j: chunks j, j + 256/Gs, ...), each summing in
-// fp64 in chunk order, and the groups' sums are then added in group order, so
-// the result does not depend on scheduling.  The row to update and its state
-// are loaded while the partials are in flight.
+// The long runs of a batch whose workgroup items only stored their chunk
+// partials (batches of more than kFinishInItemsMaxKeys lookups, with many
+// long runs: there a separate launch costs less than the ticket round trip
+// per chunk): runs of at most kFinGroupChunks chunks by one lane group each,
+// longer ones by a workgroup each (finish_run), and runs of at least
+// kFinPieceMin chunks piece by piece (sum_piece), the workgroup that sums a
+// run's last piece finishing the run.  Either way a run's partials are added
+// in the order seg_fused's own finish uses (only the squared norm of a run of
+// at most kFinGroupChunks chunks is reduced in another order).
 template <int ST, int VE, int NCH, bool REC>
 __global__ __launch_bounds__(kBlock) void seg_finalize(BackwardLaunch a) {
   if (a.buf.counters[kCntError] != 0u) return;  // a look-back wait gave up earlier
   constexpr int NV = VE * NCH;
-  constexpr int kElemsPerThread = kMaxDim / kBlock;
-  constexpr int kU = group_unroll<VE, NCH>();
   __shared__ TableMeta s_meta[kLdsTables];
   __shared__ double s_red[kBlock * NV];        // [group][row element]
   __shared__ double s_scratch[kWavesPerBlock];
   stage_meta(a, s_meta);
   const int tid = threadIdx.x;
-  const int Gs = 1 << a.gshift;
-  const int ngroups = kBlock >> a.gshift;
-  const int g = tid >> a.gshift, gl = tid & (Gs - 1);
-  const int row_elems = Gs * NV;
   const uint32_t n = a.buf.counters[kCntLong];
   if (a.buf.counters[kCntPieced] != 0u) {
     // the pieces of runs of at least kFinPieceMin chunks: the workgroups scan
@@ -914,7 +1067,16 @@ __global__ __launch_bounds__(kBlock) void seg_finalize(BackwardLaunch a) {
       __syncthreads();
       const uint32_t np = s_np;
       for (uint32_t q = 0; q < np; ++q) {
-        finish_piece<ST>(a, s_meta, s_piece[q], s_red, s_scratch, &s_last);
+        // piece j of run li, then the run by the workgroup that sums its last piece
+        const uint32_t li = s_piece[q].x, j = s_piece[q].y;
+        const uint4 L = a.buf.longs[li];
+        const uint32_t key = a.buf.long_keys[li];
+        const TableMeta m = meta_of(a, s_meta, table_of_key(a, s_meta, key));
+        const uint32_t npc = L.w / kFinPiece;
+        const uint32_t cnt = j == npc - 1u ? L.w - j * kFinPiece : kFinPiece;
+        sum_piece(a, L, j, cnt, m.dim, s_red);
+        if (last_ticket(a.buf.run_tickets + li, npc, &s_last))
+          finish_run_pieces<ST>(a, L, m, key, s_red, s_scratch);
         __syncthreads();  // s_red, s_scratch and s_last are reused
       }
     }
@@ -959,79 +1121,7 @@ __global__ __launch_bounds__(kBlock) void seg_finalize(BackwardLaunch a) {
       const uint4 L = a.buf.longs[li];  // {first position, length, first partial, chunks}
       const uint32_t key = a.buf.long_keys[li];
       const TableMeta m = meta_of(a, s_meta, table_of_key(a, s_meta, key));
-      const int D = m.dim, C = D / VE;
-      const int64_t row0 = m.woff + static_cast<int64_t>(key - static_cast<uint32_t>(m.roff)) * D;
-      float w[kElemsPerThread];
-  #pragma unroll
-      for (int k = 0; k < kElemsPerThread; ++k) {
-        const int d = tid + k * kBlock;
-        w[k] = 0.0f;
-        if (d < D) load_widen<ST, 1>(a.weights, row0 + d, &w[k]);
-      }
-      const float m_old = a.adagrad ? a.state[key] : 0.0f;
-      Acc<VE, NCH> acc;
-      acc.zero();
-      for (uint32_t c0 = g; c0 < L.w; c0 += static_cast<uint32_t>(ngroups * kU)) {
-        float v[kU][NCH][VE];
-  #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          const uint32_t c = c0 + static_cast<uint32_t>(u * ngroups);
-          const float* row = a.buf.partial1 + static_cast<int64_t>(L.z + c) * a.pstride;
-  #pragma unroll
-          for (int q = 0; q < NCH; ++q) {
-            const int chunk = q * Gs + gl;
-            if (c < L.w && chunk < C) {
-              if constexpr (VE == 4) {
-                const float4 x = *reinterpret_cast<const float4*>(row + chunk * 4);
-                v[u][q][0] = x.x; v[u][q][1] = x.y; v[u][q][2] = x.z; v[u][q][3] = x.w;
-              } else {
-  #pragma unroll
-                for (int e = 0; e < VE; ++e) v[u][q][e] = row[chunk * VE + e];
-              }
-            } else {
-  #pragma unroll
-              for (int e = 0; e < VE; ++e) v[u][q][e] = 0.0f;
-            }
-          }
-        }
-  #pragma unroll
-        for (int u = 0; u < kU; ++u)
-  #pragma unroll
-          for (int q = 0; q < NCH; ++q)
-  #pragma unroll
-            for (int e = 0; e < VE; ++e) acc.v[q][e] += static_cast<double>(v[u][q][e]);
-      }
-  #pragma unroll
-      for (int q = 0; q < NCH; ++q)
-  #pragma unroll
-        for (int e = 0; e < VE; ++e) s_red[g * row_elems + (q * Gs + gl) * VE + e] = acc.v[q][e];
-      __syncthreads();
-      double gam[kElemsPerThread];
-      double ss = 0.0;
-  #pragma unroll
-      for (int k = 0; k < kElemsPerThread; ++k) {
-        const int d = tid + k * kBlock;
-        double x = 0.0;
-        if (d < D)
-          for (int gg = 0; gg < ngroups; ++gg) x += s_red[gg * row_elems + d];
-        gam[k] = x;
-        ss = fma(x, x, ss);
-      }
-      float step = a.lr;
-      if (a.adagrad) {
-        ss = block_sum(ss, s_scratch);
-        const float mnew = static_cast<float>(static_cast<double>(m_old) + ss / D);
-        if (tid == 0) a.state[key] = mnew;
-        step = a.lr / (sqrtf(mnew) + a.eps);
-      }
-  #pragma unroll
-      for (int k = 0; k < kElemsPerThread; ++k) {
-        const int d = tid + k * kBlock;
-        if (d < D) {
-          float x = fmaf(-step, static_cast<float>(gam[k]), w[k]);
-          narrow_store<ST, 1>(a.weights, row0 + d, &x);
-        }
-      }
+      finish_run<ST, VE, NCH, false, group_unroll<VE, NCH>()>(a, L, m, key, s_red, s_scratch);
       __syncthreads();  // s_red is reused by the next run
     }
     __syncthreads();  // s_whole and s_nwhole are reused
@@ -1078,9 +1168,11 @@ hipError_t run_segments(const BackwardLaunch& a, const uint32_t* keys, const uin
   else
     launch_timed(kt, "seg_fused", seg_fused<ST, VE, NCH, REC, false>, dim3(blocks), dim3(kBlock),
                  0, s, a, keys, sorted_vals);
-  const int64_t fin = ub.longs < kMaxFinBlocks ? ub.longs : kMaxFinBlocks;
-  launch_timed(kt, "seg_finalize", seg_finalize<ST, VE, NCH, REC>, dim3(fin), dim3(kBlock), 0, s,
-               a);
+  if (!a.finish_in_items) {
+    const int64_t fin = ub.longs < kMaxFinBlocks ? ub.longs : kMaxFinBlocks;
+    launch_timed(kt, "seg_finalize", seg_finalize<ST, VE, NCH, REC>, dim3(fin), dim3(kBlock), 0,
+                 s, a);
+  }
   return hipGetLastError();
 }
 

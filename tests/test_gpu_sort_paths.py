@@ -211,6 +211,8 @@ def test_path_boundaries(E, n):
     counted = n > (1 << 20)
     assert ("radix_count" in used) == counted and ("radix_scan" in used) == counted, used
     assert ("rle_count" in used) == counted, used
+    # up to 2^20 lookups the segment kernel finishes the long runs itself
+    assert ("seg_finalize" in used) == counted, used
     pb.op.close()
     parity(spec, seed=12, steps=1, batches=[batch], bag_sample=500, row_sample=2000)
 

@@ -45,8 +45,9 @@
  *
  * Ownership: every buffer is allocated and owned by the caller.  The weights
  * and state pointers given to tbe_create are kept (not copied) and must
- * outlive the handle.  The library allocates only a small per-handle device
- * metadata block (in tbe_create) and frees it in tbe_destroy.
+ * outlive the handle; so must a forward scratch attached with
+ * tbe_set_forward_scratch.  The library allocates only a small per-handle
+ * device metadata block (in tbe_create) and frees it in tbe_destroy.
  *
  * Asynchrony: tbe_forward and tbe_backward_update enqueue work on the given
  * HIP stream (a hipStream_t passed as void*, NULL = the null stream) and
@@ -64,8 +65,8 @@
  *
  * Threading: a handle may be used by one host thread at a time.  Two
  * backward_update calls in flight on one handle race on the weights; with
- * TBE_FLAG_SPLIT_BAGS, two forward calls in flight on one handle (on
- * different streams) race on the handle's segment-sum scratch.
+ * TBE_FLAG_SPLIT_BAGS or the count-matrix forward, two forward calls in
+ * flight on one handle (on different streams) race on its forward scratch.
  *
  * No C++ exception crosses this interface.  Every function returns a
  * tbe_status; tbe_status_string gives a static description.
@@ -80,7 +81,7 @@
 extern "C" {
 #endif
 
-#define TBE_ABI_VERSION 1
+#define TBE_ABI_VERSION 2
 
 typedef struct tbe_handle tbe_handle;
 
@@ -123,9 +124,9 @@ enum {
    * first 128 in the forward's own pass and its other 128-lookup segments
    * in parallel waves, whose sums are then added to the bag's output in
    * segment order (deterministic; the fp32 rounding order differs from the
-   * unsplit sum).  The handle allocates a scratch for the segment sums at
-   * creation (about 64 MB); a call whose lookups could need more segments
-   * than it holds pools its bags unsplit.  Source: kimbodo.com/?p=28372,
+   * unsplit sum).  The segment sums go to the caller's forward scratch
+   * (tbe_set_forward_scratch, about 64 MB); a call whose lookups could need
+   * more segments than it holds pools its bags unsplit.  Source: kimbodo.com/?p=28372,
    * "Kimbodo Engineering Perspective" (load imbalance across lookups). */
   TBE_FLAG_SPLIT_BAGS = 16u,
   /* Count-matrix backward (off by default): for every bag b of table t, its
@@ -215,6 +216,23 @@ tbe_status tbe_create(const tbe_config* config, void* weights, float* optim_stat
 /* Release the handle's metadata.  Waits for nothing; the caller must not
  * destroy a handle whose work is still running.  NULL is a no-op. */
 void tbe_destroy(tbe_handle* handle);
+
+/* Device scratch of the forward's opt-in paths, which the caller provides:
+ * the count-matrix forward's transposed copy of its tables (TBE_FLAG_HISTOGRAM,
+ * TBE_FLAG_FORCE_HISTOGRAM; rewritten by every forward call that takes that
+ * path) and the split bags' segment sums (TBE_FLAG_SPLIT_BAGS).  *bytes = 0
+ * when the handle uses neither path: its forward calls need no scratch. */
+tbe_status tbe_forward_scratch_size(const tbe_handle* handle, size_t* bytes);
+
+/* Attach a caller-owned device buffer of at least tbe_forward_scratch_size
+ * bytes, 256-byte aligned, for the later forward calls on the handle (kept,
+ * not copied: it must stay valid until it is replaced, detached with NULL and
+ * 0, or the handle destroyed).  Its contents need no initialisation and are
+ * undefined after a call.  While a handle that needs scratch has none, its
+ * forward calls return TBE_ERR_WORKSPACE_TOO_SMALL and enqueue nothing.
+ * Errors: TBE_ERR_INVALID_ARGUMENT (null handle, misaligned buffer, NULL with
+ * bytes != 0), TBE_ERR_WORKSPACE_TOO_SMALL (bytes below the size). */
+tbe_status tbe_set_forward_scratch(tbe_handle* handle, void* scratch, size_t bytes);
 
 /* Pooled forward.  B >= 0 bags per table; num_indices >= 0.  B == 0 is a
  * no-op; bags without ids produce zeros (also under mean pooling). */

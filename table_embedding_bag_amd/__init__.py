@@ -21,7 +21,8 @@ __all__ = [
     "tbe_backward_workspace_size", "tbe_backward_update", "tbe_forward_group",
     "tbe_backward_update_grouped", "tbe_psw_grad", "tbe_set_option", "tbe_stage_times",
     "tbe_status_string", "tbe_abi_version", "tbe_check_device_status",
-    "tbe_backward_update_no_alloc", "STATIC_SCRATCH_BYTES", "TBE",
+    "tbe_backward_update_no_alloc", "tbe_forward_scratch_size", "tbe_set_forward_scratch",
+    "STATIC_SCRATCH_BYTES", "TBE",
     "F32", "F16", "BF16", "POOL_SUM", "POOL_MEAN", "OPT_SGD", "OPT_ROWWISE_ADAGRAD",
     "FLAG_VALIDATE", "FLAG_NO_HISTOGRAM", "FLAG_FORCE_HISTOGRAM", "FLAG_HISTOGRAM",
     "FLAG_SPLIT_BAGS", "FLAG_COUNT_BACKWARD",
@@ -51,7 +52,8 @@ EXPORTED_SYMBOLS = (
     "tbe_create", "tbe_destroy", "tbe_forward", "tbe_backward_workspace_size",
     "tbe_backward_update", "tbe_forward_group", "tbe_backward_update_grouped", "tbe_psw_grad",
     "tbe_set_option", "tbe_stage_times", "tbe_status_string", "tbe_abi_version",
-    "tbe_check_device_status", "tbe_backward_update_no_alloc",
+    "tbe_check_device_status", "tbe_backward_update_no_alloc", "tbe_forward_scratch_size",
+    "tbe_set_forward_scratch",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -110,12 +112,15 @@ def load():
                                     ctypes.POINTER(i32)]
     lib.tbe_status_string.argtypes = [ctypes.c_int]
     lib.tbe_status_string.restype = ctypes.c_char_p
+    lib.tbe_forward_scratch_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+    lib.tbe_set_forward_scratch.argtypes = [P, P, ctypes.c_size_t]
     lib.tbe_abi_version.argtypes = []
     lib.tbe_abi_version.restype = i32
     for name in ("tbe_create", "tbe_forward", "tbe_backward_workspace_size", "tbe_backward_update",
                  "tbe_forward_group", "tbe_backward_update_grouped", "tbe_psw_grad",
                  "tbe_set_option", "tbe_stage_times", "tbe_check_device_status",
-                 "tbe_backward_update_no_alloc"):
+                 "tbe_backward_update_no_alloc", "tbe_forward_scratch_size",
+                 "tbe_set_forward_scratch"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -187,6 +192,17 @@ def tbe_create(rows: Sequence[int], dims: Sequence[int], weight_dtype: int, pool
 def tbe_destroy(handle) -> None:
     if handle:
         load().tbe_destroy(handle)
+
+
+def tbe_forward_scratch_size(handle) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().tbe_forward_scratch_size(handle, ctypes.byref(n)), "tbe_forward_scratch_size")
+    return int(n.value)
+
+
+def tbe_set_forward_scratch(handle, scratch, nbytes: int) -> None:
+    _check(load().tbe_set_forward_scratch(handle, _ptr(scratch), int(nbytes)),
+           "tbe_set_forward_scratch")
 
 
 def tbe_forward(handle, B: int, indices, offsets, per_sample_weights, output, stream=None) -> None:
@@ -303,6 +319,13 @@ class TBE:
                                  {"sgd": OPT_SGD, "rowwise_adagrad": OPT_ROWWISE_ADAGRAD}[optimizer],
                                  weights, state, flags)
         self._ws = None
+        # the forward's opt-in paths (count-matrix forward, split bags) take
+        # their scratch from the caller
+        self._fscratch = None
+        need = tbe_forward_scratch_size(self.handle)
+        if need:
+            self._fscratch = torch.empty(need, dtype=torch.uint8, device=weights.device)
+            tbe_set_forward_scratch(self.handle, self._fscratch, need)
 
     def forward(self, B, indices, offsets, per_sample_weights=None, out=None):
         import torch

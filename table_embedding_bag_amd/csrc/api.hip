@@ -92,6 +92,12 @@ struct tbe_handle {
   char* split = nullptr;
   int64_t split_cap = 0;
   int32_t split_pstride = 0;
+  // the caller's forward scratch (tbe_set_forward_scratch): the transposed
+  // tables (wt) first, then the split-bag scratch; fscratch_bytes is what the
+  // handle's paths need (0: none)
+  size_t fscratch_bytes = 0;
+  size_t fscratch_split_off = 0;
+  bool fscratch_set = false;
   // groupings made by tbe_forward_group and not yet used, by workspace
   std::vector<GroupRecord> groups;
   // profiling: pairs of events handed to timed kernel launches (start and end
@@ -806,25 +812,18 @@ tbe_status tbe_create(const tbe_config* cfg, void* weights, float* optim_state, 
     delete h;
     return TBE_ERR_HIP;
   }
-  if (h->wt_elems > 0 &&
-      hipMalloc(reinterpret_cast<void**>(&h->wt), sizeof(uint16_t) * h->wt_elems) != hipSuccess) {
-    (void)hipFree(block);
-    delete h;
-    return TBE_ERR_OUT_OF_MEMORY;
-  }
+  // the forward's opt-in paths take their scratch from the caller
+  // (tbe_set_forward_scratch): the transposed tables, then the split-bag sums
   if (h->flags & TBE_FLAG_SPLIT_BAGS) {
     h->split_pstride = (h->dmax + 3) / 4 * 4;
     h->split_cap = std::min<int64_t>(kSplitMaxSegments,
                                      kSplitScratchBytes / (4 * int64_t{h->split_pstride})) /
                    16 * 16;  // keeps the 16-byte split-bag records aligned
-    if (hipMalloc(reinterpret_cast<void**>(&h->split), split_bytes(h->split_cap, h->split_pstride)) !=
-        hipSuccess) {
-      if (h->wt) (void)hipFree(h->wt);
-      (void)hipFree(block);
-      delete h;
-      return TBE_ERR_OUT_OF_MEMORY;
-    }
   }
+  h->fscratch_split_off = up(sizeof(uint16_t) * static_cast<size_t>(h->wt_elems));
+  h->fscratch_bytes =
+      h->fscratch_split_off +
+      ((h->flags & TBE_FLAG_SPLIT_BAGS) ? up(split_bytes(h->split_cap, h->split_pstride)) : 0);
   *out = h;
   return TBE_OK;
 }
@@ -833,9 +832,31 @@ void tbe_destroy(tbe_handle* h) {
   if (!h) return;
   for (auto& e : h->pool) (void)hipEventDestroy(e);
   if (h->meta) (void)hipFree(h->meta);
-  if (h->wt) (void)hipFree(h->wt);
-  if (h->split) (void)hipFree(h->split);
   delete h;
+}
+
+tbe_status tbe_forward_scratch_size(const tbe_handle* h, size_t* bytes) {
+  if (!h || !bytes) return TBE_ERR_INVALID_ARGUMENT;
+  *bytes = h->fscratch_bytes;
+  return TBE_OK;
+}
+
+tbe_status tbe_set_forward_scratch(tbe_handle* h, void* scratch, size_t bytes) {
+  if (!h) return TBE_ERR_INVALID_ARGUMENT;
+  if (!scratch) {  // detach
+    if (bytes != 0) return TBE_ERR_INVALID_ARGUMENT;
+    h->wt = nullptr;
+    h->split = nullptr;
+    h->fscratch_set = false;
+    return TBE_OK;
+  }
+  if (!aligned(scratch, kAlign)) return TBE_ERR_INVALID_ARGUMENT;
+  if (bytes < h->fscratch_bytes) return TBE_ERR_WORKSPACE_TOO_SMALL;
+  char* base = static_cast<char*>(scratch);
+  h->wt = h->wt_elems > 0 ? reinterpret_cast<uint16_t*>(base) : nullptr;
+  h->split = (h->flags & TBE_FLAG_SPLIT_BAGS) ? base + h->fscratch_split_off : nullptr;
+  h->fscratch_set = true;
+  return TBE_OK;
 }
 
 tbe_status tbe_set_option(tbe_handle* h, int32_t option, int64_t value) {
@@ -906,6 +927,8 @@ tbe_status forward_impl(tbe_handle* h, int32_t B, const void* indices, const voi
   if (psw && !aligned(psw, 4)) return TBE_ERR_INVALID_ARGUMENT;
   // per-sample weights rule out the count-matrix forward
   if (psw && (h->flags & TBE_FLAG_FORCE_HISTOGRAM)) return TBE_ERR_UNSUPPORTED;
+  // the opt-in paths' scratch comes from the caller
+  if (h->fscratch_bytes > 0 && !h->fscratch_set) return TBE_ERR_WORKSPACE_TOO_SMALL;
   try {
     // Sub-wave size: enough lane groups per bag that one round of row loads
     // covers a mean-length bag.

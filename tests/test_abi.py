@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert tbe.tbe_abi_version() == 1
+    assert tbe.tbe_abi_version() == 2
     for s in range(8):
         assert tbe.tbe_status_string(s)
     assert tbe.tbe_status_string(0) == "ok"
@@ -120,6 +120,8 @@ def test_null_handle_calls_are_rejected():
     assert lib.tbe_check_device_status(None, None) == 1
     assert lib.tbe_backward_update_no_alloc(None, 4, None, None, 1, 0, None, None, 0.1, 0.0,
                                             None, None) == 1
+    assert lib.tbe_forward_scratch_size(None, ctypes.byref(n)) == 1
+    assert lib.tbe_set_forward_scratch(None, None, 0) == 1
     lib.tbe_destroy(None)
 
 

@@ -236,6 +236,36 @@ def test_very_long_runs_finish_in_pieces(dtype, D):
     b.op.close()
 
 
+@pytest.mark.parametrize("extra", [0, 320_000], ids=["finished-in-items", "finalize-launch"])
+def test_many_long_runs_finish_once_each(extra):
+    # 250 rows hit 256 to 12 000 times (1 to 47 chunk partials) and two rows hit 33 000 and
+    # 40 000 times (pieces of 64 chunks), among uniform lookups: about 770k lookups, so the
+    # workgroup that stores a run's last partial finishes it inside the segment kernel; with
+    # 320k more uniform lookups the batch passes 2^20 and a separate launch finishes the runs.
+    # Both against the reference (every row updated once), and three handles bit-identical.
+    E, D, B = 3000, 64, 2048
+    rng = np.random.default_rng(17)
+    counts = np.exp(rng.uniform(np.log(256), np.log(12000), 250)).astype(np.int64)
+    hot = rng.choice(E, 252, replace=False)
+    hits = np.concatenate([np.repeat(hot[:250], counts), np.repeat(hot[250], 33000),
+                           np.repeat(hot[251], 40000), rng.integers(0, E, 20000 + extra)])
+    hits = rng.permutation(hits)
+    assert (len(hits) <= (1 << 20)) == (extra == 0)
+    batch = _hand_batch(1, B, [[list(b) for b in np.array_split(hits, B)]])
+    spec = workloads.custom([E], [D], "f32", B=B, optimizer="rowwise_adagrad", key=226)
+    parity(spec, seed=9, steps=1, batches=[batch])
+    outs = []
+    G = workloads.grad_output(spec, seed=9, step=0, device="cuda")
+    for _ in range(3):
+        pb = make_problem(spec, seed=9, batch=batch)
+        pb.op.backward_update(B, pb.idx, pb.off, None, G, spec.lr, spec.eps)
+        torch.cuda.synchronize()
+        outs.append((pb.W.clone(), pb.state.clone()))
+        pb.op.close()
+    for W, st in outs[1:]:
+        assert torch.equal(W, outs[0][0]) and torch.equal(st, outs[0][1])
+
+
 @pytest.mark.parametrize("cycle", [(2, 0, 4, 2), (2, 1, 3, 2), (8,)], ids=["with-empty", "uneven", "even"])
 def test_linearize_tiles_whose_lengths_sum_evenly(cycle):
     # Bag lengths cycling (2, 0, 4, 2) or (2, 1, 3, 2) make every tile of 128 bags hold

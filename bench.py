@@ -136,6 +136,29 @@ def copy_probe():
                       "launches": 5}))
 
 
+def copy_peak():
+    """Context for the HBM figures: a plain device copy (torch copy_ of 512 MiB, read plus
+    write), timed with events on torch's stream over 10 launches after 3 untimed ones."""
+    import torch
+    n = 1 << 27
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(10):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / 10
+    gbps_ = 2 * 4 * n / us / 1e3
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"kernel": "torch copy_ (512 MiB read + 512 MiB written)", "avg_us": round(us, 1),
+            "GBps": round(gbps_, 1), "pct_of_peak": pct(gbps_, HBM_PEAK_GBPS)}
+
+
 def row_stats(spec, batch):
     """Runs of equal (table, row) ids: their lengths, from the batch itself."""
     import numpy as np
@@ -740,6 +763,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "gates": gates,
+        "copy_kernel": copy_peak(),
         "times": m["times"],
         "kernels": kernel_table(m),
         "profiled_ms_per_step": round(m["profiled_ms_per_step"], 4),

@@ -392,6 +392,7 @@ void fill_backward(const tbe_handle* h, int32_t B, const void* indices, const vo
   a.pstride = p.pstride;
   a.long_threshold = static_cast<int32_t>(std::min<int64_t>(long_threshold, 0x7FFFFFFF));
   a.finish_in_items = n <= kFinishInItemsMaxKeys ? 1 : 0;
+  a.xcd_runs = int64_t{4} * B * h->sum_dims <= 8 * kXcdL2Bytes ? 1 : 0;
   a.bucket_sort = bucket_sort ? 1 : 0;
   a.spin_limit = h->spin_limit;
   a.error_mark = h->error_mark;

@@ -362,6 +362,9 @@ constexpr uint32_t kFinPieceMin = 2 * kFinPiece;
 // would each add a ticket round trip to a workgroup item, take a separate
 // finishing kernel.
 constexpr int64_t kFinishInItemsMaxKeys = int64_t{1} << 20;
+// L2 of one XCD: the short runs are split into one range per XCD when an
+// eighth of the upstream gradient fits in it.
+constexpr int64_t kXcdL2Bytes = int64_t{4} << 20;
 
 // Workgroup items of the segment kernels: {first position, kMediumItem | length}
 // for a medium run, {long run, chunk} for a 256-lookup chunk of a long run.
@@ -420,6 +423,7 @@ struct BackwardLaunch {
   int32_t short_max;        // runs of at most this many lookups are short (a lane group's)
   int32_t front_queued;     // the run-length encoder queued the longer runs
   int32_t finish_in_items;  // seg_fused finishes the long runs (else seg_finalize does)
+  int32_t xcd_runs;         // short runs in one contiguous range per XCD
   int32_t pstride;          // floats per partial row
   int32_t long_threshold;   // runs at least this long use split accumulation
   int32_t chunk;            // lookups per level-1 partial

@@ -390,14 +390,24 @@ __device__ __forceinline__ void short_runs(const BackwardLaunch& a, const uint32
   const int Gq = a.short_max;
   const int lane = lane_id();
   if constexpr (!PT) {
-    const GroupIds id = group_ids(a, bid, nblk);
+    // With xcd_runs the runs are split into G = min(8, workgroups) contiguous
+    // ranges, range g taken by workgroups b = g mod G.  Workgroups go to the 8
+    // XCDs round robin and sorted runs are table-major, so each XCD gathers
+    // the gradient rows of its own stretch of tables, which then stay in its
+    // L2 (the host sets xcd_runs when an eighth of the upstream gradient fits
+    // one).  Otherwise one range.
+    const uint32_t G = a.xcd_runs ? (nblk < 8u ? nblk : 8u) : 1u;
+    const uint32_t g = bid % G;
+    const uint32_t r_lo = static_cast<uint32_t>(static_cast<uint64_t>(U) * g / G);
+    const uint32_t r_hi = static_cast<uint32_t>(static_cast<uint64_t>(U) * (g + 1u) / G);
+    const GroupIds id = group_ids(a, bid / G, (nblk - g + G - 1u) / G);
     const int Gs = 1 << a.gshift;  // >= Gq
     const int leader = lane & ~(Gs - 1);
-    const uint32_t wave_first = id.gid - static_cast<uint32_t>(lane >> a.gshift);
+    const uint32_t wave_first = r_lo + id.gid - static_cast<uint32_t>(lane >> a.gshift);
     const uint32_t ng = id.ngroups;
-    uint32_t r = id.gid;
-    for (uint32_t rb = wave_first; rb < U; rb += ng, r += ng)
-      short_run<ST, VE, NCH, REC, false>(a, sorted_vals, s_meta, r, r < U, -1, Gs, id.g.gl,
+    uint32_t r = r_lo + id.gid;
+    for (uint32_t rb = wave_first; rb < r_hi; rb += ng, r += ng)
+      short_run<ST, VE, NCH, REC, false>(a, sorted_vals, s_meta, r, r < r_hi, -1, Gs, id.g.gl,
                                          leader, Gq);
     return;
   }

@@ -54,6 +54,8 @@ FLUSH_BYTES = 1 << 30        # written between calls to empty L2 and the 256 MB 
 FRONT = ("init_workspace", "linearize_kernel", "radix_count", "radix_scan", "radix_pass",
          "bucket_sort_rle", "rle_count", "rle_kernel")
 SEG = ("queue_runs", "table_run_starts", "seg_fused", "seg_finalize")
+# calls in each per-kernel and forward-alone pass (at least; more when --steps is larger)
+KERNEL_PASS_STEPS = 200
 # batches of at most this many lookups have their long runs finished inside seg_fused
 FINISH_IN_ITEMS_MAX = 1 << 20
 FWD = ("fwd_gather_pool", "fwd_lds_pool", "fwd_linearize", "fwd_histogram", "hist_transpose",
@@ -458,6 +460,25 @@ def measure(wl, args, steps, warmup, headline):
                     "batch0": {"lookups": stats0["N"], "unique_rows": stats0["U"],
                                "long_run_share": round(stats0["long_run_share"], 3),
                                "max_run": stats0["max_run"]}}
+    if phase in ("all", "hot"):
+        # The per-kernel pass and the forward alone come first, over at least
+        # KERNEL_PASS_STEPS calls each (finer averages).  They also keep the GPU busy for
+        # a few tens of ms before the timed steps: after idling it raises its clocks over
+        # about 10 ms of work (workload 2, per 10-step block: 85, 81, 80, ... 77.5 us a
+        # step), so a short timed run started cold would measure the ramp.
+        ks = max(steps, KERNEL_PASS_STEPS)
+        kt = wl.kernel_times(lambda i: wl.pair(i, args.plain), warmup, ks)
+        us, per_call = avg_us(kt, ks)
+        out["avg_us"], out["per_call"] = us, per_call
+        out["profiled_ms_per_step"] = sum(sum(v) for v in kt.values()) / ks
+        out["times"] = stage_split(us, per_call)
+        # forward alone (tbe_forward): its lookups/s and the plain gather kernel
+        el_f, look_f = wl.timed(wl.forward, warmup, ks)
+        out["times"]["lookups_per_s_fwd"] = round(look_f / el_f, 1)
+        out["times"]["t_fwd_call_us"] = round(1e6 * el_f / ks, 2)
+        kf = wl.kernel_times(wl.forward, warmup, ks)
+        out["fwd_only_us"], _ = avg_us(kf, ks)
+    # the warm-up steps, then the timed ones
     for i in range(warmup):
         wl.pair(i, args.plain)
     torch.cuda.synchronize()
@@ -466,17 +487,6 @@ def measure(wl, args, steps, warmup, headline):
         out["elapsed"], out["lookups"] = el, lookups
         print(f"[bench] workload {wl.n}: {steps} steps in {el * 1e3:.2f} ms", file=sys.stderr,
               flush=True)
-        kt = wl.kernel_times(lambda i: wl.pair(i, args.plain), warmup, steps)
-        us, per_call = avg_us(kt, steps)
-        out["avg_us"], out["per_call"] = us, per_call
-        out["profiled_ms_per_step"] = sum(sum(v) for v in kt.values()) / steps
-        out["times"] = stage_split(us, per_call)
-        # forward alone (tbe_forward): its lookups/s and the plain gather kernel
-        el_f, look_f = wl.timed(wl.forward, warmup, steps)
-        out["times"]["lookups_per_s_fwd"] = round(look_f / el_f, 1)
-        out["times"]["t_fwd_call_us"] = round(1e6 * el_f / steps, 2)
-        kf = wl.kernel_times(wl.forward, warmup, steps)
-        out["fwd_only_us"], _ = avg_us(kf, steps)
     if headline and phase in ("all", "flushed"):
         # every call starts with caches emptied by a 1 GiB write: a plain forward, then the
         # grouped pair with a second flush before its backward (its segment kernels then read

@@ -418,9 +418,14 @@ class Workload:
         self.torch.cuda.empty_cache()
 
 
-def avg_us(times, k):
-    """Average launch time (us) and launches per call, per kernel."""
-    return ({name: 1e3 * sum(v) / len(v) for name, v in times.items()},
+def avg_us(times, k, skip_half=False):
+    """Average launch time (us) and launches per call, per kernel; skip_half: average over
+    the second half of the launches only (the first half of a pass that starts the GPU's
+    clock ramp)."""
+    def mean(v):
+        w = v[len(v) // 2:] if skip_half and len(v) > 1 else v
+        return 1e3 * sum(w) / len(w)
+    return ({name: mean(v) for name, v in times.items()},
             {name: len(v) / k for name, v in times.items()})
 
 
@@ -468,9 +473,10 @@ def measure(wl, args, steps, warmup, headline):
         # step), so a short timed run started cold would measure the ramp.
         ks = max(steps, KERNEL_PASS_STEPS)
         kt = wl.kernel_times(lambda i: wl.pair(i, args.plain), warmup, ks)
-        us, per_call = avg_us(kt, ks)
+        # averages over the pass's second half, past the ramp
+        us, per_call = avg_us(kt, ks, skip_half=True)
         out["avg_us"], out["per_call"] = us, per_call
-        out["profiled_ms_per_step"] = sum(sum(v) for v in kt.values()) / ks
+        out["profiled_ms_per_step"] = sum(us[k] * per_call[k] for k in us) / 1e3
         out["times"] = stage_split(us, per_call)
         # forward alone (tbe_forward): its lookups/s and the plain gather kernel
         el_f, look_f = wl.timed(wl.forward, warmup, ks)

@@ -178,7 +178,9 @@ __device__ __forceinline__ void linearize_tiles(const BackwardLaunch& a, int64_t
 //      (digits in order, waves in order within a digit);
 //   3. place: each wave walks its positions again and writes every key to
 //      buf.keys[1] / buf.vals[1] at its counter plus its rank among equal
-//      digits in the step, which keeps lookup order within a digit.
+//      digits in the step, which keeps lookup order within a digit (the
+//      stashed steps keep their ranks from the count, so only later steps
+//      match their digits again).
 // Two barriers per tile; no workgroup waits for another, and nothing here
 // needs cleared memory: tile 0 clears the counters and status words of the
 // kernels that follow.  The bucket-local sort gathers a bucket's keys from the
@@ -245,27 +247,34 @@ __device__ __forceinline__ void linearize_bucket(const BackwardLaunch& a, int ti
     a.buf.rec[p] = make_uint2(static_cast<uint32_t>(k0 + slot),
                               __float_as_uint(pw * s_scale[slot]));
   };
+  // returns the lane's rank among equal digits in the step and their number
+  // (rank | number << 8), which the place step of a stashed key reuses
   const auto count = [&](uint32_t key, bool ok) {
     const uint32_t d = (key >> lbits) & hmask;
     const uint64_t peers = match_bits(__ballot(ok), d, hbits);
-    if (ok && popc_below(peers) == 0) wc[d] += __popcll(peers);
+    const uint32_t below = popc_below(peers), n = __popcll(peers);
+    if (ok && below == 0) wc[d] += n;
+    return below | (n << 8);
   };
 
   // 1. count (steps past kStash are read again when placed)
-  uint32_t key[kStash];
-  int slot[kStash];
+  // stashed steps: the key, and the bag slot (< kLinBags, bits 0-7) packed
+  // with the rank and number that count returns (bits 8-23)
+  uint32_t key[kStash], sr[kStash];
 #pragma unroll
   for (int s = 0; s < kStash; ++s) {
     const int64_t p = c0 + s * kWave + lane;
-    lookup(p, s < steps && p < c1, &key[s], &slot[s]);
+    int sl;
+    lookup(p, s < steps && p < c1, &key[s], &sl);
+    sr[s] = static_cast<uint32_t>(sl);
   }
 #pragma unroll
   for (int s = 0; s < kStash; ++s) {
     if (s >= steps) break;
     const int64_t p = c0 + s * kWave + lane;
     const bool ok = p < c1;
-    if (a.use_rec && ok) record(p, slot[s]);
-    count(key[s], ok);
+    if (a.use_rec && ok) record(p, static_cast<int>(sr[s]));
+    sr[s] |= count(key[s], ok) << 8;
   }
   for (int s = kStash; s < steps; ++s) {
     const int64_t p = c0 + s * kWave + lane;
@@ -312,12 +321,13 @@ __device__ __forceinline__ void linearize_bucket(const BackwardLaunch& a, int ti
   // 3. place
   uint32_t* const kout = a.buf.keys[1];
   uint32_t* const vout = a.buf.vals[1];
-  const auto place = [&](int64_t p, bool ok, uint32_t k, int sl) {
+  // r: the lane's rank among equal digits in the step and their number, as
+  // count returns them
+  const auto place = [&](int64_t p, bool ok, uint32_t k, int sl, uint32_t r) {
     const uint32_t d = (k >> lbits) & hmask;
-    const uint64_t peers = match_bits(__ballot(ok), d, hbits);
-    const uint32_t below = popc_below(peers);
+    const uint32_t below = r & 0xFFu;
     const uint32_t pre = ok ? wc[d] : 0u;
-    if (ok && below == 0) wc[d] = pre + __popcll(peers);
+    if (ok && below == 0) wc[d] = pre + (r >> 8);
     if (ok) {
       // pre + below lies in [p0, p1): a digit's positions never pass its count
       kout[pre + below] = k;
@@ -328,7 +338,7 @@ __device__ __forceinline__ void linearize_bucket(const BackwardLaunch& a, int ti
   for (int s = 0; s < kStash; ++s) {
     if (s >= steps) break;
     const int64_t p = c0 + s * kWave + lane;
-    place(p, p < c1, key[s], slot[s]);
+    place(p, p < c1, key[s], static_cast<int>(sr[s] & 0xFFu), sr[s] >> 8);
   }
   for (int s = kStash; s < steps; ++s) {
     const int64_t p = c0 + s * kWave + lane;
@@ -336,7 +346,9 @@ __device__ __forceinline__ void linearize_bucket(const BackwardLaunch& a, int ti
     uint32_t kk;
     int sl;
     lookup(p, ok, &kk, &sl);
-    place(p, ok, kk, sl);
+    const uint32_t d = (kk >> lbits) & hmask;
+    const uint64_t peers = match_bits(__ballot(ok), d, hbits);
+    place(p, ok, kk, sl, popc_below(peers) | (static_cast<uint32_t>(__popcll(peers)) << 8));
   }
 }
 

@@ -710,8 +710,8 @@ def workload_line(wl, m, steps):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
-              "multi-GPU path", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the library has no "
+              "multi-GPU path (tables are not sharded across GPUs)", file=sys.stderr)
         sys.exit(2)
     if args.copy_probe:
         copy_probe()

@@ -88,7 +88,7 @@ typedef struct tbe_handle tbe_handle;
 typedef enum {
   TBE_OK = 0,
   TBE_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size or enum, misaligned buffer */
-  TBE_ERR_UNSUPPORTED = 2,        /* valid request this build does not handle */
+  TBE_ERR_UNSUPPORTED = 2,        /* valid request the library does not handle */
   TBE_ERR_INDEX_OUT_OF_RANGE = 3, /* TBE_FLAG_VALIDATE found a bad id or offsets array */
   TBE_ERR_WORKSPACE_TOO_SMALL = 4,
   TBE_ERR_HIP = 5,                /* a HIP runtime call or kernel launch failed */

@@ -36,7 +36,9 @@
 //                 lane prefetches one lookup, the group gathers the run's
 //                 gradient rows with 2 or 4 in flight (matched to the run's
 //                 length), sums them in fp32 and updates the row.  Most runs
-//                 are this short.
+//                 are this short.  When an eighth of the upstream gradient
+//                 fits one XCD's L2, each XCD takes one contiguous range of
+//                 runs (so of tables) and keeps their gradient rows there.
 //   seg_finalize  larger batches: the long runs' partials added in the same
 //                 order and the rows updated, in a launch of their own.
 // Summation order never depends on scheduling (no float atomics), so results

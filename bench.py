@@ -78,6 +78,9 @@ def parse():
                         "from LDS when a call qualifies); routed: count-matrix forward for the "
                         "tables that qualify; histogram: count-matrix forward for every table "
                         "(all must qualify)")
+    p.add_argument("--count-backward", action="store_true",
+                   help="the headline workload's handle takes the count-matrix backward "
+                        "(every table at most 1024 rows; for its counter collection)")
     p.add_argument("--plain", action="store_true",
                    help="time tbe_forward + tbe_backward_update instead of the grouped pair")
     p.add_argument("--phase", choices=("all", "hot", "flushed"), default="all",
@@ -725,7 +728,9 @@ def main():
 
     torch.cuda.set_device(0)
     t_gen = time.perf_counter()
-    wl = Workload(args.workload, args.forward)
+    import table_embedding_bag_amd as tbe
+    wl = Workload(args.workload, args.forward,
+                  tbe.FLAG_COUNT_BACKWARD if args.count_backward else 0)
     W_host = workloads.storage_numpy(wl.W).copy() \
         if not args.no_cpu_baseline and args.phase == "all" else None
     print(f"[bench] workload {args.workload} ready in {time.perf_counter() - t_gen:.1f}s",

@@ -273,11 +273,12 @@ struct BwdPlan {
   size_t bytes = 0;
 };
 
-// Bag slices of the count-matrix backward: about 2048 busy workgroups, at
-// least one 32-bag step per slice.
+// Bag slices of the count-matrix backward: about 1024 workgroups (one per
+// CU four times over; every slice adds a pass over the weights' partial sums
+// in the update), at least one 32-bag step per slice.
 int count_slices(const tbe_handle* h, int32_t B) {
   const int64_t g = std::max<int64_t>(1, h->cb_groups);
-  int64_t s = (2048 + g - 1) / g;
+  int64_t s = (1024 + g - 1) / g;
   s = std::min<int64_t>(s, std::max<int64_t>(1, B / 32));
   return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(s, 64)));
 }

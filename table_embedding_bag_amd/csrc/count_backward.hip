@@ -22,22 +22,23 @@
 // fixed order: the accuracy of an fp32 segment sum, reproducible bit for bit.
 //
 // Mapping onto CDNA4:
-//  * cb_product: a workgroup of 4 waves owns 256 rows (64 per wave: four
-//    16-row tiles) x 64 columns (four 16-column tiles) of one table and one
-//    slice of its bags, and walks the slice in steps of 32 bags (the K of
-//    v_mfma_f32_16x16x32_bf16).  Per step: the 32 bags' gradient columns are
-//    staged in LDS transposed ([part][column][bag], so a lane's B operand --
-//    eight consecutive bags of one column -- is one 16-byte read), the
+//  * cb_product: a workgroup of 16 waves owns all rows of one table (up to
+//    1024; 64 per wave: four 16-row tiles) x 64 columns (four 16-column
+//    tiles) and one slice of its bags, and walks the slice in steps of 32
+//    bags (the K of v_mfma_f32_16x16x32_bf16).  Per step: the 32 bags'
+//    gradient columns are split and staged in LDS transposed
+//    ([part][column][bag], so a lane's B operand -- eight consecutive bags of
+//    one column -- is one 16-byte read; each thread splits two values), the
 //    step's lookups are counted into each wave's [64 rows][32 bags] count
-//    tile with packed bf16 LDS atomic adds, each wave reads its A operands,
-//    clears its tile and issues 3 x 16 MFMAs.  The next step's gradient
-//    values and ids (and the offsets of the one after) are loaded into
-//    registers before the current step's barrier and products, so global
-//    latency overlaps them (two barriers per step).  C never exists in HBM.  The
-//    slice's partial Gamma (fp32) and the rows' lookup counts are written to
-//    the workspace.  Workgroups are numbered so that the row groups of one
-//    bag slice, which stage the same gradient columns, are neighbours on one
-//    XCD (the second and later reads come from its L2).
+//    tile, each wave with rows reads its A operands, clears its tile and
+//    issues 3 x 16 MFMAs.  The next step's gradient values and ids (and the
+//    offsets of the one after) are loaded into registers before the current
+//    step's barrier and products, so global latency overlaps them (two
+//    barriers per step).  C never exists in HBM.  The slice's partial Gamma
+//    (fp32) and the rows' lookup counts are written to the workspace.  One
+//    workgroup per table (rather than one per 256 rows) splits and counts
+//    each step once for the whole table, and over 1024 threads: that per-step
+//    work, not the matrix cores, sets the time.
 //  * cb_update: one 16-lane group per table row; rows with no lookup are
 //    skipped (their weights and state stay bit-identical); the slices'
 //    partials are added in slice order in fp64, then the SGD or row-wise
@@ -54,14 +55,16 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 constexpr int kK = 32;               // bags per MFMA step
-constexpr int kWaves = 4;
+constexpr int kWaves = 16;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kRowsPerWave = 64;
 constexpr int kTS = kK + 8;          // LDS row stride (16-bit elements) of the tiles
 constexpr int kParts = 3;            // g = hi + mid + lo
 constexpr int kCountCap = 256;       // every count 0..256 is exact in bf16
+constexpr int kGB = kK * kCbCols / kThreads;  // bags of one column a thread stages per step
 enum { kFast = 0, kAtomic = 1, kPasses = 2 };  // counting modes of a step
-static_assert(kWaves * kRowsPerWave == kCbGroupRows, "row group");
+static_assert(kWaves * kRowsPerWave == kCbGroupRows && kCbGroupRows == kCbMaxRows,
+              "one workgroup holds every row of a table");
 
 template <typename IT>
 __device__ __forceinline__ int64_t ld_index(const void* p, int64_t i) {
@@ -79,22 +82,16 @@ __device__ __forceinline__ uint32_t cvt_pair(float x, float y) {
   return __builtin_bit_cast(uint32_t, bf16x2{static_cast<__bf16>(x), static_cast<__bf16>(y)});
 }
 
-// Eight values split into packed bf16 parts with g = hi + mid + lo exactly:
-// hi rounds g; g - hi is exact in fp32 and fits 17 significant bits; mid rounds
+// Two values split into packed bf16 parts with g = hi + mid + lo exactly: hi
+// rounds g; g - hi is exact in fp32 and fits 17 significant bits; mid rounds
 // that, and the rest (at most 8 significant bits) is exactly a bf16.
-__device__ __forceinline__ void split8(const float (&g)[8], uint4& hi, uint4& mid, uint4& lo) {
-  uint32_t h[4], m[4], l[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    h[q] = cvt_pair(g[2 * q], g[2 * q + 1]);
-    const float r0 = g[2 * q] - __uint_as_float(h[q] << 16);
-    const float r1 = g[2 * q + 1] - __uint_as_float(h[q] & 0xFFFF0000u);
-    m[q] = cvt_pair(r0, r1);
-    l[q] = cvt_pair(r0 - __uint_as_float(m[q] << 16), r1 - __uint_as_float(m[q] & 0xFFFF0000u));
-  }
-  hi = make_uint4(h[0], h[1], h[2], h[3]);
-  mid = make_uint4(m[0], m[1], m[2], m[3]);
-  lo = make_uint4(l[0], l[1], l[2], l[3]);
+__device__ __forceinline__ void split_pair(float g0, float g1, uint32_t& hi, uint32_t& mid,
+                                           uint32_t& lo) {
+  hi = cvt_pair(g0, g1);
+  const float r0 = g0 - __uint_as_float(hi << 16);
+  const float r1 = g1 - __uint_as_float(hi & 0xFFFF0000u);
+  mid = cvt_pair(r0, r1);
+  lo = cvt_pair(r0 - __uint_as_float(mid << 16), r1 - __uint_as_float(mid & 0xFFFF0000u));
 }
 
 // +1 to the bf16 count at element el of a tile (packed 16-bit LDS atomic).
@@ -115,20 +112,19 @@ __global__ __launch_bounds__(kThreads) void cb_product(CountLaunch a) {
   __shared__ uint32_t s_rowcnt[kCbGroupRows];
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  // logical block -> (unit, bag slice, row group), row group fastest
+  // logical block -> (unit, bag slice), slice fastest; the workgroup holds
+  // every row of the table.  Logical blocks are contiguous per XCD, so one
+  // XCD takes the units of a band of adjacent tables, whose gradient columns
+  // are neighbours in every row of G (measured 3.5% faster than round robin,
+  // which puts all units of a slice on one XCD).
   const int logical = xcd_contiguous_block(blockIdx.x, gridDim.x);
-  const int per_unit = a.slices * kCbGroupsPerTable;
-  const int u = logical / per_unit;
-  const int rem = logical - u * per_unit;
-  const int slice = rem / kCbGroupsPerTable;
-  const int rg = rem - slice * kCbGroupsPerTable;
+  const int u = logical / a.slices;
+  const int slice = logical - u * a.slices;
   const CountUnit unit = a.units[u];
   const TableMeta m = a.meta[unit.table];
-  const int row0 = rg * kCbGroupRows;
-  if (row0 >= m.rows) return;                // the whole workgroup: no rows here
   const int col0 = unit.col0;
   const int NT = min(kCbCols, m.dim - col0) >> 4;  // 16-column tiles (dims are multiples of 16)
-  const int wrow0 = row0 + wave * kRowsPerWave;
+  const int wrow0 = wave * kRowsPerWave;
   const bool active = wrow0 < m.rows;
   // bag slice, whole 32-bag steps except the last
   const int per_slice = ((a.B + a.slices - 1) / a.slices + kK - 1) / kK * kK;
@@ -149,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void cb_product(CountLaunch a) {
 
   // thread roles: G staging takes one column of 8 bags; the ids are taken bag
   // by bag, 8 adjacent lanes per bag (bag tid / 8, in-bag positions tid % 8 + 8k)
-  const int gcol = tid & 63, gbag = (tid >> 6) * 8;
+  const int gcol = tid & 63, gbag = (tid >> 6) * kGB;
   const int ibag = tid >> 3, ij = tid & 7;
   const bool want_counts = a.out_num != nullptr;  // exact counts per row only for the runs
   auto step_bags = [&](int step) { return min(kK, b_end - (b_begin + step * kK)); };
@@ -171,12 +167,12 @@ __global__ __launch_bounds__(kThreads) void cb_product(CountLaunch a) {
       if (lane == 0) s_mode[buf] = over_cap ? kPasses : (over8 ? kAtomic : kFast);
     }
   };
-  auto load_g = [&](int step, float (&g)[8]) {
+  auto load_g = [&](int step, float (&g)[kGB]) {
     const int st = min(step, nsteps - 1);
     const int nb = step_bags(st), c0 = b_begin + st * kK;
     const bool col_ok = gcol < NT * 16 && step < nsteps;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < kGB; ++j) {
       const int b = gbag + j;
       const bool ok = col_ok && b < nb;
       const float v = gbase[static_cast<int64_t>(c0 + min(b, nb - 1)) * a.sum_dims +
@@ -186,7 +182,8 @@ __global__ __launch_bounds__(kThreads) void cb_product(CountLaunch a) {
   };
   auto load_ids = [&](int buf, int step, int64_t (&x)[2]) {
     const bool in_step = step < nsteps && ibag < step_bags(min(step, nsteps - 1));
-    const int64_t s0 = s_off[buf][ibag], s1 = s_off[buf][ibag + 1];
+    const int cb = min(ibag, kK - 1);  // threads past the step's bags hold no ids
+    const int64_t s0 = s_off[buf][cb], s1 = s_off[buf][cb + 1];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int64_t p = s0 + ij + 8 * r;
@@ -196,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void cb_product(CountLaunch a) {
     }
   };
   auto add = [&](int64_t x, int bag) {
-    const int64_t r = x - row0;
+    const int64_t r = x;
     if (r >= 0 && r < kCbGroupRows) {
       count_add(s_cnt[r >> 6], static_cast<int>(r & 63) * kTS + bag);
       if (want_counts) atomicAdd(&s_rowcnt[r], 1u); else s_rowcnt[r] = 1u;
@@ -243,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void cb_product(CountLaunch a) {
     store_offsets(0, 0, load_offsets(0));
     int64_t off_a = load_offsets(1);   // offsets of step c + 2 at iteration c
     __syncthreads();
-    float g_cur[8];
+    float g_cur[kGB];
     int64_t x_cur[2];
     load_g(0, g_cur);
     load_ids(0, 0, x_cur);
@@ -258,17 +255,18 @@ __global__ __launch_bounds__(kThreads) void cb_product(CountLaunch a) {
       {
         if constexpr (MEAN) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
+          for (int j = 0; j < kGB; ++j) {
             const int b = gbag + j;
             const int64_t len = b < nb ? s_off[buf][b + 1] - s_off[buf][b] : 0;
             g_cur[j] = len > 0 ? g_cur[j] * (1.0f / static_cast<float>(len)) : 0.0f;
           }
         }
-        uint4 hi, mid, lo;
-        split8(g_cur, hi, mid, lo);
-        *reinterpret_cast<uint4*>(s_g[0] + gcol * kTS + gbag) = hi;
-        *reinterpret_cast<uint4*>(s_g[1] + gcol * kTS + gbag) = mid;
-        *reinterpret_cast<uint4*>(s_g[2] + gcol * kTS + gbag) = lo;
+        static_assert(kGB == 2, "one packed pair per part and thread");
+        uint32_t hi, mid, lo;
+        split_pair(g_cur[0], g_cur[1], hi, mid, lo);
+        *reinterpret_cast<uint32_t*>(s_g[0] + gcol * kTS + gbag) = hi;
+        *reinterpret_cast<uint32_t*>(s_g[1] + gcol * kTS + gbag) = mid;
+        *reinterpret_cast<uint32_t*>(s_g[2] + gcol * kTS + gbag) = lo;
       }
       // count a pass of the step.  kFast (no bag over 8 lookups): the 8 lanes
       // of a bag compare their ids by shuffles and the first lane holding an
@@ -291,7 +289,7 @@ __global__ __launch_bounds__(kThreads) void cb_product(CountLaunch a) {
             same += y == x ? 1 : 0;
             first &= !(y == x && (ij ^ o) < ij);
           }
-          const int r = x - row0;
+          const int r = x;
           if (x >= 0 && first && r >= 0 && r < kCbGroupRows) {
             s_cnt[r >> 6][(r & 63) * kTS + ibag] =
                 static_cast<uint16_t>(__float_as_uint(static_cast<float>(same + 1)) >> 16);
@@ -319,7 +317,7 @@ __global__ __launch_bounds__(kThreads) void cb_product(CountLaunch a) {
       };
       bool added = count_pass(0);
       // prefetch: G values and ids of step c + 1, offsets of step c + 3
-      float g_nxt[8];
+      float g_nxt[kGB];
       int64_t x_nxt[2];
       load_g(c + 1, g_nxt);
       load_ids(buf ^ 1, c + 1, x_nxt);
@@ -340,7 +338,7 @@ __global__ __launch_bounds__(kThreads) void cb_product(CountLaunch a) {
       if (c + 2 < nsteps) store_offsets(buf, c + 2, off_a);
       off_a = off_b;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) g_cur[j] = g_nxt[j];
+      for (int j = 0; j < kGB; ++j) g_cur[j] = g_nxt[j];
       x_cur[0] = x_nxt[0];
       x_cur[1] = x_nxt[1];
     }
@@ -364,9 +362,9 @@ __global__ __launch_bounds__(kThreads) void cb_product(CountLaunch a) {
       }
   }
   __syncthreads();  // s_rowcnt
-  if (col0 == 0 && row0 + tid < m.rows)
+  if (col0 == 0 && tid < m.rows)
     a.counts[static_cast<int64_t>(a.slices) * m.roff + static_cast<int64_t>(slice) * m.rows +
-             row0 + tid] = s_rowcnt[tid];
+             tid] = s_rowcnt[tid];
 }
 
 // Table of linear row id r: the last t with roff_t <= r.
@@ -383,7 +381,15 @@ __device__ __forceinline__ uint32_t row_count(const CountLaunch& a, const TableM
                                               int64_t rr) {
   uint32_t c = 0;
   const uint32_t* cp = a.counts + static_cast<int64_t>(a.slices) * m.roff + rr;
-  for (int s = 0; s < a.slices; ++s) c += cp[static_cast<int64_t>(s) * m.rows];
+  int s = 0;
+  for (; s + 8 <= a.slices; s += 8) {  // eight loads in flight
+    uint32_t v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = cp[static_cast<int64_t>(s + k) * m.rows];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) c += v[k];
+  }
+  for (; s < a.slices; ++s) c += cp[static_cast<int64_t>(s) * m.rows];
   return c;
 }
 
@@ -411,8 +417,20 @@ __global__ __launch_bounds__(kBlock) void cb_update(CountLaunch a) {
       const int d = j * kG * 4 + gl * 4;
       if (d < m.dim) {
         load_widen<ST, 4>(a.weights, row_e + d, w[j]);
+        // slice order; eight slices' loads in flight at a time
         double x[4] = {0.0, 0.0, 0.0, 0.0};
-        for (int s = 0; s < a.slices; ++s) {
+        int s = 0;
+        for (; s + 8 <= a.slices; s += 8) {
+          float4 v[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            v[k] = *reinterpret_cast<const float4*>(p + (s + k) * sstride + d);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            x[0] += v[k].x; x[1] += v[k].y; x[2] += v[k].z; x[3] += v[k].w;
+          }
+        }
+        for (; s < a.slices; ++s) {
           const float4 v = *reinterpret_cast<const float4*>(p + s * sstride + d);
           x[0] += v.x; x[1] += v.y; x[2] += v.z; x[3] += v.w;
         }
@@ -491,7 +509,7 @@ void launch_product(const CountLaunch& a, dim3 grid, hipStream_t s, const Kernel
 
 hipError_t launch_count_backward(const CountLaunch& a, hipStream_t stream, const KernelTimer* kt) {
   if (a.B <= 0 || a.nunits <= 0) return hipSuccess;
-  const int64_t blocks = static_cast<int64_t>(a.nunits) * a.slices * kCbGroupsPerTable;
+  const int64_t blocks = static_cast<int64_t>(a.nunits) * a.slices;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   if (a.index64)
     launch_product<int64_t>(a, dim3(static_cast<unsigned>(blocks)), stream, kt);

@@ -11,13 +11,11 @@ namespace tbe {
 // with per-sample weights use the sort path instead.
 constexpr int kCbMaxRows = 1024;
 constexpr int kCbMaxDim = 256;
-constexpr int kCbGroupRows = 256;   // table rows per workgroup (4 waves x 64 rows)
+constexpr int kCbGroupRows = 1024;  // table rows per workgroup (16 waves x 64 rows)
 constexpr int kCbCols = 64;         // columns per workgroup (4 MFMA column tiles)
-constexpr int kCbGroupsPerTable = kCbMaxRows / kCbGroupRows;
 
-// One (table, 64-column slice) of the product.  Its kCbGroupsPerTable row
-// groups (256 rows each; those past the table's end exit at once) and its bag
-// slices make the workgroups.
+// One (table, 64-column slice) of the product.  Its bag slices make the
+// workgroups (one row group of kCbGroupRows rows holds the whole table).
 struct CountUnit {
   int32_t table;
   int32_t col0;

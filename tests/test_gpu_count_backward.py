@@ -34,6 +34,10 @@ SMALL = [
     # bags longer than 256 lookups with hot rows: counts above 256 in one bag
     workloads.custom([200], [64], "bf16", B=20, lengths=("uniform_int", 250, 700),
                      index_dist=("zipf", 1.3), key=705),
+    # degenerate and edge row counts: a one-row table (every lookup on row 0), one row
+    # short of and one past a wave's 64 rows, one row short of the 1024-row limit
+    workloads.custom([1, 63, 65, 1023], [16, 32, 48, 64], "f32", B=97,
+                     lengths=("uniform_int", 0, 16), optimizer="rowwise_adagrad", key=708),
 ]
 
 

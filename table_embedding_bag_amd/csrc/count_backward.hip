@@ -63,6 +63,12 @@ constexpr int kParts = 3;            // g = hi + mid + lo
 constexpr int kCountCap = 256;       // every count 0..256 is exact in bf16
 constexpr int kGB = kK * kCbCols / kThreads;  // bags of one column a thread stages per step
 enum { kFast = 0, kAtomic = 1, kPasses = 2 };  // counting modes of a step
+// DPP lane selects (gfx9 encoding): quad permutations lane ^ 1, ^ 2, ^ 3 within
+// each group of 4 lanes, and the half-row mirror lane ^ 7 within each group of 8
+constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2, 3, 0, 1]
+constexpr int kDppQuadXor3 = 0x1B;   // quad_perm [3, 2, 1, 0]
+constexpr int kDppHalfMirror = 0x141;
 static_assert(kWaves * kRowsPerWave == kCbGroupRows && kCbGroupRows == kCbMaxRows,
               "one workgroup holds every row of a table");
 
@@ -282,13 +288,24 @@ __global__ __launch_bounds__(kThreads) void cb_product(CountLaunch a) {
         bool added = false;
         if (mode == kFast) {  // the same on every lane of the wave
           const int x = static_cast<int>(x_cur[0]);  // a row (< kCbMaxRows), or -1
+          // the ids of the 7 other lanes of the bag's 8-lane group, lane ij ^ o at
+          // y[o - 1], by DPP moves (no LDS round trips): the quad permutations give
+          // o = 1, 2, 3; the half-row mirror gives o = 7, and the quad permutations
+          // of the mirrored ids give o = 6, 5, 4
+          const int m7 = __builtin_amdgcn_mov_dpp(x, kDppHalfMirror, 0xF, 0xF, false);
+          const int y[7] = {__builtin_amdgcn_mov_dpp(x, kDppQuadXor1, 0xF, 0xF, false),
+                            __builtin_amdgcn_mov_dpp(x, kDppQuadXor2, 0xF, 0xF, false),
+                            __builtin_amdgcn_mov_dpp(x, kDppQuadXor3, 0xF, 0xF, false),
+                            __builtin_amdgcn_mov_dpp(m7, kDppQuadXor3, 0xF, 0xF, false),
+                            __builtin_amdgcn_mov_dpp(m7, kDppQuadXor2, 0xF, 0xF, false),
+                            __builtin_amdgcn_mov_dpp(m7, kDppQuadXor1, 0xF, 0xF, false),
+                            m7};
           int same = 0;
           bool first = true;
 #pragma unroll
           for (int o = 1; o < 8; ++o) {
-            const int y = __shfl_xor(x, o, kWave);
-            same += y == x ? 1 : 0;
-            first &= !(y == x && (ij ^ o) < ij);
+            same += y[o - 1] == x ? 1 : 0;
+            first &= !(y[o - 1] == x && (ij ^ o) < ij);
           }
           const int r = x;
           if (x >= 0 && first && r >= 0 && r < kCbGroupRows) {

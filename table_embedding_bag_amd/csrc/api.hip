@@ -991,6 +991,7 @@ tbe_status forward_impl(tbe_handle* h, int32_t B, const void* indices, const voi
     a.dtype = h->dtype;
     a.index64 = index_dtype == TBE_I64;
     a.vec = h->fwd_vec;
+    a.uncond_loads = n > kFusedMaxLookups ? 1 : 0;
     // bags split only when every possible segment fits the scratch (at most
     // n / kSplitLen segments after the first ones)
     const bool split = h->split && n > kSplitLen && n / kSplitLen + 1 <= h->split_cap;

@@ -242,6 +242,8 @@ struct ForwardLaunch {
   int32_t dtype;            // storage dtype code
   int32_t index64;          // indices/offsets are int64
   int32_t vec;              // 16-byte row chunks (else one element per lane)
+  int32_t uncond_loads;     // row loads issued unconditionally (batches above
+                            // kFusedMaxLookups lookups)
   const int32_t* table_list;  // tables to cover (T entries), or null for tables 0..T-1
   // Bags longer than split_len lookups (0: none) pool only their first
   // split_len lookups here; the rest is queued as segments of split_len for
